@@ -1,0 +1,144 @@
+"""CPU oracle for the Q4_0 dequantize-and-multiply path (binary64, plain loops).
+
+TEST INFRASTRUCTURE ONLY.  Imported by ``tests/``, by ``__graft_entry__.smoke()``
+and by the CPU-baseline leg of ``bench.py``; the product package never imports
+it and shares no code with it.  The arithmetic lives in ``q4_oracle.c`` (the
+definition it follows is written out in that file's header); this module only
+compiles it with gcc and marshals numpy arrays.
+
+Pinned by ``tests/test_oracle_pins.py`` (hand-computed blocks in
+``tests/golden/``, exhaustive binary16 decode against numpy, closed forms,
+exact integer products, brute force on tiny shapes, argmax invariants).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+import time
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "q4_oracle.c")
+_LIB = os.path.join(_HERE, "libq4oracle.so")
+_lock = threading.Lock()
+_default = None
+
+# Per-output tolerance factor: |y_gpu - y| <= TOL * a, a = sum |w_k x_k|.
+TOL = 1e-3
+
+
+def build(force: bool = False) -> str:
+    """Compile q4_oracle.c (gcc -O2, OpenMP over outputs, no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-fno-fast-math",
+                               "-ffp-contract=off", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class Oracle:
+    """The oracle's entry points over one compiled copy of q4_oracle.c."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        vp, i64 = ctypes.c_void_p, ctypes.c_int64
+        lib.q4o_f16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.q4o_f16_to_f64.restype = ctypes.c_double
+        lib.q4o_f16_to_f64_array.argtypes = [vp, i64, vp]
+        lib.q4o_dequant_row.argtypes = [vp, i64, vp]
+        lib.q4o_gemm_rows.argtypes = [vp, i64, i64, vp, i64, vp, vp]
+        lib.q4o_argmax.argtypes = [vp, i64]
+        lib.q4o_argmax.restype = i64
+        self.lib = lib
+        self.path = path
+
+    def f16_to_f64(self, bits) -> np.ndarray:
+        """Exact binary16 -> binary64 of uint16 bit patterns."""
+        b = _f16bits(np.asarray(bits))
+        out = np.empty(b.shape, dtype=np.float64)
+        self.lib.q4o_f16_to_f64_array(b.ctypes.data, b.size, out.ctypes.data)
+        return out
+
+    def dequant_rows(self, w_rows: np.ndarray, k: int) -> np.ndarray:
+        """The binary64 weights of packed rows uint8[n, K/32*18] -> float64[n, K]."""
+        w = _u8(w_rows).reshape(-1, k // 32 * 18)
+        out = np.empty((w.shape[0], k), dtype=np.float64)
+        for i in range(w.shape[0]):
+            self.lib.q4o_dequant_row(w[i].ctypes.data, k, out[i].ctypes.data)
+        return out
+
+    def gemm_rows(self, w_rows: np.ndarray, k: int, x) -> tuple[np.ndarray, np.ndarray]:
+        """(y, a) for packed rows uint8[n, K/32*18] and f16 activations [M, K] (or [K]).
+
+        y[m, i] = sum_k w[i, k] x[m, k] and a[m, i] = sum_k |w[i, k] x[m, k]|, binary64,
+        shapes [M, n] (or [n] for a 1-D x).
+        """
+        assert k % 32 == 0
+        w = _u8(w_rows).reshape(-1, k // 32 * 18)
+        xb = _f16bits(np.asarray(x))
+        one_d = xb.ndim == 1
+        xb = np.ascontiguousarray(xb.reshape(-1, k))
+        m, n = xb.shape[0], w.shape[0]
+        y = np.empty((m, n), dtype=np.float64)
+        a = np.empty((m, n), dtype=np.float64)
+        self.lib.q4o_gemm_rows(w.ctypes.data, n, k, xb.ctypes.data, m, y.ctypes.data, a.ctypes.data)
+        if one_d:
+            return y[0], a[0]
+        return y, a
+
+    def argmax(self, y) -> int:
+        """Lowest index among the maxima of a binary64 vector."""
+        v = np.ascontiguousarray(np.asarray(y, dtype=np.float64)).ravel()
+        assert v.size >= 1
+        return int(self.lib.q4o_argmax(v.ctypes.data, v.size))
+
+
+def default() -> Oracle:
+    global _default
+    with _lock:
+        if _default is None:
+            if not os.path.exists(_LIB):
+                build()
+            _default = Oracle(_LIB)
+    return _default
+
+
+def f16_to_f64(bits) -> np.ndarray:
+    return default().f16_to_f64(bits)
+
+
+def dequant_rows(w_rows: np.ndarray, k: int) -> np.ndarray:
+    return default().dequant_rows(w_rows, k)
+
+
+def gemm_rows(w_rows: np.ndarray, k: int, x) -> tuple[np.ndarray, np.ndarray]:
+    return default().gemm_rows(w_rows, k, x)
+
+
+def argmax(y) -> int:
+    return default().argmax(y)
+
+
+def _u8(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    assert a.dtype == np.uint8
+    return a
+
+
+def _f16bits(x) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float16:
+        x = x.view(np.uint16)
+    assert x.dtype == np.uint16
+    return x
+
+
+def time_gemm_rows(w_rows: np.ndarray, k: int, x) -> float:
+    """Wall-clock seconds of one gemm_rows call (used by the CPU baseline)."""
+    t0 = time.perf_counter()
+    gemm_rows(w_rows, k, x)
+    return time.perf_counter() - t0

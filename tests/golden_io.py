@@ -1,0 +1,61 @@
+"""Readers for the hand-computed fixtures under tests/golden/."""
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _cases(name):
+    case = None
+    with open(os.path.join(GOLDEN, name)) as f:
+        for raw in f:
+            line = raw.split("#", 1)[0].strip()
+            if not line:
+                continue
+            key, _, rest = line.partition(" ")
+            if key == "case":
+                case = {"name": rest.strip(), "rows": [], "y": [], "a": []}
+            elif key == "end":
+                yield case
+                case = None
+            else:
+                case.setdefault("_lines", []).append((key, rest.split()))
+                if key == "row":
+                    case["rows"].append(bytes(int(t, 16) for t in rest.split()))
+                elif key == "k":
+                    case["k"] = int(rest)
+                elif key == "x":
+                    case["x"] = rest.split()
+                elif key in ("y", "a"):
+                    case[key].extend(float(t) for t in rest.split())
+                elif key == "r":
+                    case["r"] = int(rest)
+
+
+def q4_0_block_cases():
+    """Hand-computed Q4_0 cases: dict(name, k, w uint8[n, k/32*18], x float16[k], y, a)."""
+    out = []
+    for c in _cases("q4_0_blocks.txt"):
+        k = c["k"]
+        rb = k // 32 * 18
+        for r in c["rows"]:
+            assert len(r) == rb, (c["name"], len(r), rb)
+        w = np.frombuffer(b"".join(c["rows"]), dtype=np.uint8).reshape(len(c["rows"]), rb).copy()
+        if c["x"] == ["iota"]:
+            x = np.arange(1, k + 1, dtype=np.float64)
+        else:
+            x = np.array([float(t) for t in c["x"]], dtype=np.float64)
+        assert x.size == k, c["name"]
+        x16 = x.astype(np.float16)
+        assert np.array_equal(x16.astype(np.float64), x), "fixture x must be exact in f16"
+        out.append(dict(name=c["name"], k=k, w=w, x=x16, y=np.array(c["y"]), a=np.array(c["a"])))
+    return out
+
+
+def argmax_cases():
+    out = []
+    for c in _cases("argmax.txt"):
+        ys = [v for key, v in c["_lines"] if key == "y"][0]
+        out.append(dict(name=c["name"], y=np.array([float(t) for t in ys]), r=c["r"]))
+    return out

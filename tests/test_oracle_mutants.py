@@ -1,0 +1,52 @@
+"""Plant plausible mistakes into copies of the oracle's source; the pins must catch each one.
+
+A mutant is the oracle's C source with one textual substitution, compiled with
+gcc into a temporary directory.  Nothing here runs on a GPU.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import oracle_pin_suite as suite
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "q4_oracle.c")
+
+MUTANTS = {
+    "offset_7_not_8": ("(double)(code - 8)", "(double)(code - 7)"),
+    "sign_flipped": ("(double)(code - 8)", "(double)(8 - code)"),
+    "nibbles_swapped": ("(k < 16) ? (byte & 0x0F) : (byte >> 4)", "(k < 16) ? (byte >> 4) : (byte & 0x0F)"),
+    "sequential_nibbles": ("blk[2 + (k & 15)]", "blk[2 + (k >> 1)]"),
+    "scale_big_endian": ("blk[0] | ((uint16_t)blk[1] << 8)", "blk[1] | ((uint16_t)blk[0] << 8)"),
+    "magnitude_without_abs": ("mag += fabs(p);", "mag += p;"),
+    "f16_bias_off_by_one": ("e - 25", "e - 24"),
+    "f16_subnormal_scale": ("ldexp((double)f, -24)", "ldexp((double)f, -25)"),
+    "block_stride_16": ("(i / 32) * 18", "(i / 32) * 16"),
+    "output_transposed": ("y[mm * nrows + n] = acc;", "y[n * m + mm] = acc;"),
+    "argmax_last_tie": ("if (y[i] > y[best])", "if (y[i] >= y[best])"),
+    "scale_dropped": ("return (double)(code - 8) * d;", "return (double)(code - 8);"),
+    "x_ignored_sign": ("* q4o_f16_to_f64(xr[i]);", "* fabs(q4o_f16_to_f64(xr[i]));"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert old in src, "mutation site vanished from the oracle: " + old
+    mutated = src.replace(old, new)
+    c = tmp_path / "mutant.c"
+    so = tmp_path / "libmutant.so"
+    c.write_text(mutated)
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+                           "-o", str(so), str(c), "-lm"])
+    bad = suite.failures(oracle.Oracle(str(so)))
+    assert bad, "mutant %s passed every pin" % name
+
+
+def test_unmutated_copy_passes(tmp_path):
+    so = tmp_path / "libcopy.so"
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+                           "-o", str(so), SRC, "-lm"])
+    assert suite.failures(oracle.Oracle(str(so))) == []
