@@ -1,0 +1,292 @@
+"""Benchmark of the Q4_0 dequantize-and-multiply path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sweep|gemv|lmhead|smallm|prefill]
+
+Default workload ("sweep"): the 27B-shaped decode weight sweep, 64 layers x
+(q, k, v, o 5120x5120; gate, up 17408x5120; down 5120x17408) = 448 Q4_0 GEMVs
+and 13,400,801,280 bytes of packed weights, each GEMV with its own f16 input
+(synthetic, seeded).  One step = one sweep = one launch of the batch kernel
+(q4_0_gemv_batch).  Inputs are resident in HBM before timing starts; K steps
+are bracketed by HIP events on the launch stream.
+
+Prints ONE JSON line: metric/value/unit (algorithmic GB/s of the sweep), the
+roofline of the dominant kernel and a CPU baseline (the binary64 oracle timed
+on a bounded sample of the same workload on this host's cores).
+
+Other workloads print the same kind of line for the single 5120x5120 GEMV
+(rotating weight copies so the 256 MB last-level cache does not serve them),
+the LM head with argmax, small-M (--m) and prefill (--m) over the sweep.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Q4_0 GEMV HBM GB/s (% of 8 TB/s) and 27B-shape decode weight-sweeps/sec"
+PEAK_HBM_GBS = 8000.0
+PEAK_F16_TFLOPS = 2500.0
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "q4_dequant_gemv_block_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None when
+    there are none or the kernel sources changed since they were taken."""
+    path = os.path.join(PROFILE_DIR, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        table = json.load(f)
+    e = table.get(workload)
+    if not e or e.get("kernel") != kernel or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def load_q4():
+    import q4_dequant_gemv_block_amd as q4
+    if not os.path.exists(q4.LIB_PATH):
+        from q4_dequant_gemv_block_amd import build
+        build.build()
+    q4.load_library()
+    return q4
+
+
+def cpu_cores() -> int:
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit():
+        return int(env)
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(items, budget_s: float = 12.0) -> dict:
+    """Time the oracle over the sweep's GEMVs in order until about budget_s of
+    CPU work; report algorithmic GB/s (and the sweeps/s it implies)."""
+    import oracle
+    import synth
+    done_bytes, done, t_total = 0, 0, 0.0
+    for (sw, sx, n, k) in items:
+        w = synth.q4_0(SEED, sw, n, k)
+        x = synth.f16_normal(SEED, sx, k)
+        t0 = time.perf_counter()
+        oracle.gemm_rows(w, k, x)
+        t_total += time.perf_counter() - t0
+        done_bytes += w.nbytes + k * 2 + n * 4
+        done += 1
+        if t_total >= budget_s:
+            break
+    gbs = done_bytes / t_total / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": cpu_cores(), "kind": "oracle",
+            "sample": "first %d of the sweep's GEMVs (%.2f GB of weights), binary64, %.1f s" % (
+                done, done_bytes / 1e9, t_total),
+            "sweeps_per_s": round(gbs * 1e9 / SWEEP_BYTES, 6)}
+
+
+SEED = 0x51A40000
+SWEEP_BYTES = 13_422_428_160  # weights 13,400,801,280 + x 6,160,384 + y 15,466,496
+
+
+def time_steps(fn, steps: int, warmup: int):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms
+
+
+def sweep_inputs(q4, workload_id: int, m: int = 1):
+    """Upload the 448 GEMVs' weights and inputs; returns device tensors and stream ids."""
+    import torch
+    import synth
+    dev = torch.device("cuda:0")
+    ws, xs, ys, ids = [], [], [], []
+    for (layer, proj, n, k) in synth.decode_sweep():
+        sw = synth.stream_id(1, layer, proj, synth.T_W)  # the same weights for every workload
+        sx = synth.stream_id(workload_id, layer, proj, synth.T_X)
+        w = torch.from_numpy(synth.q4_0(SEED, sw, n, k)).to(dev)
+        x = torch.from_numpy(synth.f16_normal(SEED, sx, m * k).reshape(m, k) if m > 1
+                             else synth.f16_normal(SEED, sx, k)).to(dev)
+        ws.append(w)
+        xs.append(x)
+        ys.append(torch.empty((m, n) if m > 1 else (n,), dtype=torch.float32, device=dev))
+        ids.append((sw, sx, n, k))
+    torch.cuda.synchronize()
+    return ws, xs, ys, ids
+
+
+def bench_sweep(args):
+    import torch
+    q4 = load_q4()
+    log("uploading the 64-layer sweep ...")
+    t0 = time.time()
+    ws, xs, ys, ids = sweep_inputs(q4, 1)
+    log("  %.1f s" % (time.time() - t0))
+    batch = q4.GemvBatch(list(zip(ws, xs, ys)))
+    ms = time_steps(batch, args.steps, args.warmup)
+    gbs = SWEEP_BYTES / (ms * 1e-3) / 1e9
+    # LM head (151,936 x 5,120 + argmax) for the implied tokens/s
+    import synth
+    wl = torch.from_numpy(synth.q4_0(SEED, synth.stream_id(2, 0, 0, synth.T_W), synth.VOCAB, synth.HIDDEN)).cuda()
+    hl = torch.from_numpy(synth.f16_normal(SEED, synth.stream_id(2, 0, 0, synth.T_X), synth.HIDDEN)).cuda()
+    lg = torch.empty(synth.VOCAB, dtype=torch.float32, device="cuda")
+    tok = torch.empty(1, dtype=torch.int32, device="cuda")
+    wsp = torch.empty(q4.workspace_bytes(q4.Q4_OP_LM_HEAD_ARGMAX, 1, synth.VOCAB, synth.HIDDEN), dtype=torch.uint8, device="cuda")
+    lm_ms = time_steps(lambda: q4.lm_head_argmax(wl, hl, lg, tok, wsp), max(args.steps, 20), args.warmup)
+    out = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16->f32", "data": "synthetic",
+        "config": {"workload": "27B-shape decode weight sweep: 64 layers x (q,k,v,o 5120x5120; "
+                               "gate,up 17408x5120; down 5120x17408), 448 Q4_0 GEMVs, M=1, one launch",
+                   "weight_bytes": 13_400_801_280, "algorithmic_bytes_per_step": SWEEP_BYTES,
+                   "seed": SEED},
+        "sweeps_per_s": round(1000.0 / ms, 2),
+        "pct_of_8TBps": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "lm_head_argmax_us": round(lm_ms * 1000.0, 2),
+        "implied_tok_s": round(1000.0 / (ms + lm_ms), 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": counter_traffic("k_gemv_batch", "sweep"),
+                     "kernel": "q4::k_gemv_batch<2,4>", "launches_per_step": 1},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(ids)
+    return out
+
+
+def bench_gemv(args):
+    """Single 5120x5120 GEMV, cycling through enough weight copies to exceed the last-level cache."""
+    import torch
+    import synth
+    q4 = load_q4()
+    n = k = 5120
+    copies = 48  # 48 x 14.7 MB = 708 MB > 256 MB
+    w0 = synth.q4_0(SEED, synth.stream_id(0, 0, 0, synth.T_W), n, k)
+    ws = [torch.from_numpy(w0).cuda() for _ in range(copies)]
+    x = torch.from_numpy(synth.f16_normal(SEED, synth.stream_id(0, 0, 0, synth.T_X), k)).cuda()
+    y = torch.empty(n, dtype=torch.float32, device="cuda")
+    it = [0]
+
+    def step():
+        q4.q4_0_gemv(ws[it[0] % copies], x, y)
+        it[0] += 1
+    steps = max(args.steps, 1) * copies
+    ms = time_steps(step, steps, args.warmup * copies)
+    hot_ms = time_steps(lambda: q4.q4_0_gemv(ws[0], x, y), steps, args.warmup)
+    bytes_ = n * k // 32 * 18 + k * 2 + n * 4
+    gbs = bytes_ / (ms * 1e-3) / 1e9
+    return {"metric": "Q4_0 GEMV HBM GB/s (single 5120x5120 GEMV, cold weights)", "value": round(gbs, 2),
+            "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16->f32",
+            "data": "synthetic", "config": {"workload": "single Q4_0 GEMV 5120x5120, 48 rotating weight copies"},
+            "hot_cache_GBps": round(bytes_ / (hot_ms * 1e-3) / 1e9, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counter_traffic("k_gemv", "gemv"),
+                         "kernel": "q4::k_gemv"}}
+
+
+def bench_lmhead(args):
+    import torch
+    import synth
+    q4 = load_q4()
+    n, k = synth.VOCAB, synth.HIDDEN
+    w = torch.from_numpy(synth.q4_0(SEED, synth.stream_id(2, 0, 0, synth.T_W), n, k)).cuda()
+    h = torch.from_numpy(synth.f16_normal(SEED, synth.stream_id(2, 0, 0, synth.T_X), k)).cuda()
+    lg = torch.empty(n, dtype=torch.float32, device="cuda")
+    tok = torch.empty(1, dtype=torch.int32, device="cuda")
+    wsp = torch.empty(q4.workspace_bytes(q4.Q4_OP_LM_HEAD_ARGMAX, 1, n, k), dtype=torch.uint8, device="cuda")
+    ms = time_steps(lambda: q4.lm_head_argmax(w, h, lg, tok, wsp), args.steps * 10, args.warmup)
+    bytes_ = n * k // 32 * 18 + k * 2 + n * 4 + 4
+    gbs = bytes_ / (ms * 1e-3) / 1e9
+    return {"metric": "LM head + greedy argmax HBM GB/s (151936x5120 Q4_0)", "value": round(gbs, 2), "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps * 10, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16->f32",
+            "data": "synthetic", "config": {"workload": "LM head 151936x5120 + argmax"},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counter_traffic("k_gemv", "lmhead"),
+                         "kernel": "q4::k_gemv<ARGMAX> + q4::k_argmax_final"}}
+
+
+def bench_gemm(args, prefill: bool):
+    import torch
+    q4 = load_q4()
+    m = args.m or (169 if prefill else 16)
+    ws, xs, ys, ids = sweep_inputs(q4, 4 if prefill else 3, m=m)
+    fn = q4.q4_0_gemm_prefill if prefill else q4.q4_0_gemm_smallm
+
+    def step():
+        for w, x, y in zip(ws, xs, ys):
+            fn(w, x, y)
+    ms = time_steps(step, args.steps, args.warmup)
+    wbytes = 13_400_801_280
+    io = m * (6_160_384 + 15_466_496)
+    flops = 2.0 * m * 23_823_646_720
+    gbs = (wbytes + io) / (ms * 1e-3) / 1e9
+    tf = flops / (ms * 1e-3) / 1e12
+    name = "prefill" if prefill else "small-M"
+    rl = ({"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+           "frac": round(tf / PEAK_F16_TFLOPS, 4)} if prefill else
+          {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+           "frac": round(gbs / PEAK_HBM_GBS, 4)})
+    rl["traffic"] = counter_traffic(name, name)
+    return {"metric": "%s Q4_0 GEMM over the 64-layer sweep (M=%d)" % (name, m),
+            "value": round(tf if prefill else gbs, 3), "unit": "TFLOP/s" if prefill else "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16->f32",
+            "data": "synthetic", "config": {"workload": "%s M=%d x 448 sweep GEMMs, 448 launches" % (name, m)},
+            "tflops": round(tf, 3), "GBps": round(gbs, 2), "roofline": rl}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="sweep", choices=["sweep", "gemv", "lmhead", "smallm", "prefill"])
+    ap.add_argument("--m", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fn = {"sweep": bench_sweep, "gemv": bench_gemv, "lmhead": bench_lmhead,
+          "smallm": lambda a: bench_gemm(a, False), "prefill": lambda a: bench_gemm(a, True)}[args.workload]
+    out = fn(args)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

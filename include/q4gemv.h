@@ -1,0 +1,196 @@
+/*
+ * q4gemv.h - C ABI of the Q4_0 dequantize-and-multiply library for MI355X (gfx950).
+ *
+ * The operation: the decode engine's matrix-vector product over 4-bit block
+ * quantized weights, where decode streams every layer's weights once per
+ * token, expands the 4-bit values in registers and reduces the row products
+ * on chip ("Every Device Brings a Slice: How SwarmLLM Runs a 27B Model Across
+ * Browser Tabs", originshq.com, section "The Engine: ~50 WGSL Kernels Written
+ * From Scratch").  The weight format is the one the pages call "GGUF Q4_0"
+ * (taozi.news, section "支持模型与限制"):
+ *
+ *   - a weight row of K columns (K % 32 == 0) is K/32 blocks of 18 bytes,
+ *     blocks consecutive along K, rows consecutive (row stride K/32*18 bytes);
+ *   - block bytes 0..1: scale d, IEEE binary16, little-endian;
+ *   - block bytes 2..17: byte j holds code j in its low nibble and code j+16
+ *     in its high nibble;
+ *   - weight = (code - 8) * d.
+ *
+ * Activations are IEEE binary16, outputs IEEE binary32.  For every output the
+ * result lies within 1e-3 * sum_k |w_k x_k| of the exact sum.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees or keeps them; nothing is retained after
+ *     the call returns.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *     void*; NULL means the null stream).  No call synchronizes the host,
+ *     except q4_0_gemv_batch_plan (see there).
+ *   - Outputs are overwritten.  Outputs must not overlap any input.
+ *   - Arguments are validated on the host before anything is enqueued; on an
+ *     error nothing has been launched and the output is untouched.
+ *   - Thread safety: calls may come from several host threads.  The only
+ *     library state is the per-thread text returned by q4_last_error().
+ *   - Alignment: w and x (h) must be 16-byte aligned, outputs 4-byte aligned
+ *     (fresh torch / hipMalloc allocations are 256-byte aligned).
+ */
+#ifndef Q4GEMV_H
+#define Q4GEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define Q4_API __attribute__((visibility("default")))
+#else
+#define Q4_API
+#endif
+
+#define Q4_ABI_VERSION 1
+
+typedef int q4_status;
+#define Q4_OK 0
+#define Q4_ERR_INVALID_ARG -1 /* null pointer, size <= 0, K % 32 != 0, M outside the entry point's range */
+#define Q4_ERR_MISALIGNED -2  /* w or x not 16-byte aligned, or an output not 4-byte aligned */
+#define Q4_ERR_WORKSPACE -3   /* workspace missing or smaller than q4_workspace_bytes() */
+#define Q4_ERR_HIP -4         /* the HIP runtime refused a launch or copy; text in q4_last_error() */
+
+/* Operation ids for q4_workspace_bytes(). */
+#define Q4_OP_GEMV 0
+#define Q4_OP_GEMM_SMALLM 1
+#define Q4_OP_GEMM_PREFILL 2
+#define Q4_OP_LM_HEAD_ARGMAX 3
+
+/* Version of this interface (Q4_ABI_VERSION of the library that was built). */
+Q4_API int q4_abi_version(void);
+
+/* Text of the last error on the calling thread ("" if none); valid until the
+ * next call into the library on the same thread. */
+Q4_API const char* q4_last_error(void);
+
+/* Bytes of device workspace an entry point needs for the given shape (0 when
+ * it needs none).  Returns 0 for an unknown op. */
+Q4_API size_t q4_workspace_bytes(int op, int64_t m, int64_t n, int64_t k);
+
+/*
+ * y[n] = sum_k w[n][k] * x[k]                         (one Q4_0 GEMV, M = 1)
+ *
+ * The per-token product of the decode engine (originshq.com page, section
+ * "The Engine: ~50 WGSL Kernels Written From Scratch").
+ *   w : n rows of k/32 Q4_0 blocks (n * k/32 * 18 bytes)
+ *   x : k binary16 values
+ *   y : n binary32 values (written)
+ *   n >= 1, k >= 32, k % 32 == 0.  k % 64 == 0 takes the fast path; other
+ *   multiples of 32 take a slower path with the same results bound.
+ * Deterministic: identical inputs give bit-identical outputs, and two rows
+ * with identical bytes give bit-identical outputs wherever they sit.
+ */
+Q4_API q4_status q4_0_gemv(const void* w, const void* x, float* y, int64_t n, int64_t k, void* stream);
+
+/*
+ * Y[m][n] = sum_k w[n][k] * X[m][k]                   (small-M batched GEMM)
+ *
+ * The batched pass that verifies speculative drafts and carries 16-token
+ * prefill chunks (aipolix.com en-us page, section "Speculation is used to
+ * amortize network round trips"; taozi.news, section "技术架构").  Each
+ * weight is read from memory once for all M rows.
+ *   w : n rows of k/32 Q4_0 blocks
+ *   x : m x k binary16, row-major
+ *   y : m x n binary32, row-major (written)
+ *   1 <= m <= 16, n >= 1, k >= 32, k % 32 == 0.
+ * Row m of the result satisfies the same bound as q4_0_gemv on X[m].
+ */
+Q4_API q4_status q4_0_gemm_smallm(const void* w, const void* x, float* y,
+                           int64_t m, int64_t n, int64_t k, void* stream);
+
+/*
+ * Y[m][n] = sum_k w[n][k] * X[m][k]                   (prefill GEMM, matrix cores)
+ *
+ * The prompt-processing matrix product (taozi.news, section "基准成绩";
+ * originshq.com page, section "The Engine ...").  Weight tiles are expanded
+ * to binary16 ((code - 8) * d rounded to nearest) on chip and multiplied on
+ * the matrix cores with binary32 accumulation.
+ *   w : n rows of k/32 Q4_0 blocks
+ *   x : m x k binary16, row-major
+ *   y : m x n binary32, row-major (written)
+ *   m >= 1, n >= 1, k >= 32, k % 32 == 0.
+ *   workspace : q4_workspace_bytes(Q4_OP_GEMM_PREFILL, m, n, k) bytes of
+ *               device memory (may be NULL when that is 0).
+ */
+Q4_API q4_status q4_0_gemm_prefill(const void* w, const void* x, float* y,
+                            int64_t m, int64_t n, int64_t k,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * logits[n] = sum_k w[n][k] * h[k];  token = lowest n with the largest logit
+ *
+ * The host's LM-head projection followed by the greedy pick (originshq.com
+ * page, section "The Architecture: Layers Distributed, Activations in
+ * Flight"; greedy decoding: taozi.news, section "基准成绩").  -0 and +0
+ * compare equal.
+ *   w      : n_vocab rows of k/32 Q4_0 blocks
+ *   h      : k binary16 values
+ *   logits : n_vocab binary32 values (written)
+ *   token  : one int32 in device memory (written)
+ *   workspace : q4_workspace_bytes(Q4_OP_LM_HEAD_ARGMAX, 1, n_vocab, k) bytes
+ *               of device memory; its contents on entry do not matter.
+ *   n_vocab >= 1, k >= 32, k % 32 == 0.  Inputs must be finite.
+ */
+Q4_API q4_status lm_head_argmax(const void* w, const void* h, float* logits, int32_t* token,
+                         int64_t n_vocab, int64_t k,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * A list of independent GEMVs run as ONE launch ("one command submit per
+ * token": originshq.com page, section "The Engine ...").  A whole decode
+ * weight sweep (every layer's projections) streams through a single
+ * persistent kernel instead of hundreds of launches.
+ *
+ * Each descriptor is one y = W x as in q4_0_gemv (k % 64 == 0 here).  The
+ * GEMVs must be independent: no y may overlap any w, x or other y of the
+ * list.
+ */
+typedef struct q4_gemv_desc {
+    const void* w;  /* n rows of k/32 Q4_0 blocks, 16-byte aligned */
+    const void* x;  /* k binary16, 16-byte aligned */
+    float* y;       /* n binary32, written */
+    int64_t n;
+    int64_t k;
+} q4_gemv_desc;
+
+/* Host-side handle of a batch plan: where its descriptors live on the device
+ * and the launch parameters derived from them.  Filled by
+ * q4_0_gemv_batch_plan; plain data, may be copied. */
+typedef struct q4_gemv_plan {
+    void* device;        /* the caller's device buffer holding the descriptors */
+    int count;           /* number of GEMVs */
+    int max_k;           /* largest k in the list */
+    int64_t total_cost;  /* work measure used to split the list across workgroups */
+} q4_gemv_plan;
+
+/* Device bytes q4_0_gemv_batch_plan needs for `count` descriptors. */
+Q4_API size_t q4_0_gemv_batch_plan_bytes(int count);
+
+/*
+ * Validate `count` host-side descriptors, write their device form into the
+ * caller's device buffer `plan_buf` (q4_0_gemv_batch_plan_bytes(count) bytes)
+ * and fill `*plan`.  The copy is enqueued on `stream` and has completed when
+ * this call returns (it synchronizes `stream`), so `descs` may be freed
+ * afterwards.  The plan stays valid as long as `plan_buf` and the tensors it
+ * names do.  1 <= count <= 1<<20; every k % 64 == 0 and k <= 32768.
+ */
+Q4_API q4_status q4_0_gemv_batch_plan(const q4_gemv_desc* descs, int count, void* plan_buf,
+                               size_t plan_bytes, q4_gemv_plan* plan, void* stream);
+
+/* Run every GEMV of a plan in one launch on `stream`. */
+Q4_API q4_status q4_0_gemv_batch(const q4_gemv_plan* plan, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4GEMV_H */

@@ -1,0 +1,247 @@
+// C ABI of the Q4_0 library: argument validation, error text, dispatch to the
+// kernel launchers.  Every check runs on the host before anything is enqueued.
+#include "../../include/q4gemv.h"
+#include "q4_launch.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <utility>
+#include <vector>
+
+namespace {
+
+thread_local char g_err[512];
+
+q4_status fail(q4_status code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+q4_status ok() {
+    g_err[0] = '\0';
+    return Q4_OK;
+}
+
+q4_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(Q4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range(const void* p, size_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + bytes};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+int64_t row_bytes(int64_t k) { return k / 32 * 18; }
+
+// Largest sizes accepted anywhere: keeps every byte offset far inside int64
+// and every row index inside the 32-bit fields the kernels use for it.
+constexpr int64_t kMaxN = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxK = int64_t(1) << 24;
+
+q4_status check_shape(const char* fn, int64_t m, int64_t m_max, int64_t n, int64_t k) {
+    if (m < 1 || m > m_max) return fail(Q4_ERR_INVALID_ARG, "%s: m = %lld outside [1, %lld]", fn, (long long)m, (long long)m_max);
+    if (n < 1 || n > kMaxN) return fail(Q4_ERR_INVALID_ARG, "%s: n = %lld outside [1, %lld]", fn, (long long)n, (long long)kMaxN);
+    if (k < 32 || k > kMaxK || k % 32 != 0)
+        return fail(Q4_ERR_INVALID_ARG, "%s: k = %lld must be a multiple of 32 in [32, %lld]", fn, (long long)k, (long long)kMaxK);
+    return Q4_OK;
+}
+
+q4_status check_tensors(const char* fn, const void* w, const void* x, const void* y, int64_t m,
+                        int64_t n, int64_t k, size_t y_bytes) {
+    if (!w || !x || !y) return fail(Q4_ERR_INVALID_ARG, "%s: null tensor pointer", fn);
+    if (!aligned(w, 16) || !aligned(x, 16)) return fail(Q4_ERR_MISALIGNED, "%s: w and x must be 16-byte aligned", fn);
+    if (!aligned(y, 4)) return fail(Q4_ERR_MISALIGNED, "%s: output must be 4-byte aligned", fn);
+    const Range rw = range(w, (size_t)(n * row_bytes(k)));
+    const Range rx = range(x, (size_t)(m * k * 2));
+    const Range ry = range(y, y_bytes);
+    if (overlap(ry, rw) || overlap(ry, rx)) return fail(Q4_ERR_INVALID_ARG, "%s: output overlaps an input", fn);
+    return Q4_OK;
+}
+
+bool fast_path(const void* w, int64_t k) { return k % 64 == 0 && k <= q4::kFastMaxK && aligned(w, 4); }
+
+}  // namespace
+
+extern "C" {
+
+int q4_abi_version(void) { return Q4_ABI_VERSION; }
+
+const char* q4_last_error(void) { return g_err; }
+
+size_t q4_workspace_bytes(int op, int64_t m, int64_t n, int64_t k) {
+    (void)m;
+    switch (op) {
+        case Q4_OP_GEMV:
+        case Q4_OP_GEMM_SMALLM:
+        case Q4_OP_GEMM_PREFILL:
+            return 0;
+        case Q4_OP_LM_HEAD_ARGMAX:
+            if (n < 1 || k < 32) return 0;
+            return (size_t)q4::argmax_blocks(n, k) * sizeof(uint64_t);
+        default:
+            return 0;
+    }
+}
+
+q4_status q4_0_gemv(const void* w, const void* x, float* y, int64_t n, int64_t k, void* stream) {
+    q4_status st = check_shape("q4_0_gemv", 1, 1, n, k);
+    if (st) return st;
+    st = check_tensors("q4_0_gemv", w, x, y, 1, n, k, (size_t)n * 4);
+    if (st) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (fast_path(w, k))
+        e = q4::launch_gemv(static_cast<const uint8_t*>(w), static_cast<const uint16_t*>(x), y, n, k, s);
+    else
+        e = q4::launch_gemm_generic(static_cast<const uint8_t*>(w), static_cast<const uint16_t*>(x), y, 1, n, k, s);
+    return hip_status(e, "q4_0_gemv launch");
+}
+
+q4_status q4_0_gemm_smallm(const void* w, const void* x, float* y, int64_t m, int64_t n, int64_t k,
+                           void* stream) {
+    q4_status st = check_shape("q4_0_gemm_smallm", m, 16, n, k);
+    if (st) return st;
+    st = check_tensors("q4_0_gemm_smallm", w, x, y, m, n, k, (size_t)(m * n) * 4);
+    if (st) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = q4::launch_gemm_generic(static_cast<const uint8_t*>(w), static_cast<const uint16_t*>(x), y, m, n, k, s);
+    return hip_status(e, "q4_0_gemm_smallm launch");
+}
+
+q4_status q4_0_gemm_prefill(const void* w, const void* x, float* y, int64_t m, int64_t n, int64_t k,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    q4_status st = check_shape("q4_0_gemm_prefill", m, kMaxN, n, k);
+    if (st) return st;
+    if (m * n > (int64_t(1) << 40)) return fail(Q4_ERR_INVALID_ARG, "q4_0_gemm_prefill: m*n too large");
+    st = check_tensors("q4_0_gemm_prefill", w, x, y, m, n, k, (size_t)(m * n) * 4);
+    if (st) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint8_t* wb = static_cast<const uint8_t*>(w);
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    for (int64_t m0 = 0; m0 < m; m0 += 16) {
+        const int64_t mm = std::min<int64_t>(16, m - m0);
+        const hipError_t e = q4::launch_gemm_generic(wb, xb + m0 * k, y + m0 * n, mm, n, k, s);
+        if (e != hipSuccess) return hip_status(e, "q4_0_gemm_prefill launch");
+    }
+    return ok();
+}
+
+q4_status lm_head_argmax(const void* w, const void* h, float* logits, int32_t* token, int64_t n_vocab,
+                         int64_t k, void* workspace, size_t workspace_bytes, void* stream) {
+    q4_status st = check_shape("lm_head_argmax", 1, 1, n_vocab, k);
+    if (st) return st;
+    st = check_tensors("lm_head_argmax", w, h, logits, 1, n_vocab, k, (size_t)n_vocab * 4);
+    if (st) return st;
+    if (!token) return fail(Q4_ERR_INVALID_ARG, "lm_head_argmax: null token pointer");
+    if (!aligned(token, 4)) return fail(Q4_ERR_MISALIGNED, "lm_head_argmax: token must be 4-byte aligned");
+    if (!fast_path(w, k))
+        return fail(Q4_ERR_INVALID_ARG, "lm_head_argmax: needs k %% 64 == 0 and k <= %lld", (long long)q4::kFastMaxK);
+    const size_t need = q4_workspace_bytes(Q4_OP_LM_HEAD_ARGMAX, 1, n_vocab, k);
+    if (!workspace || workspace_bytes < need)
+        return fail(Q4_ERR_WORKSPACE, "lm_head_argmax: workspace of %zu bytes needed", need);
+    if (!aligned(workspace, 8)) return fail(Q4_ERR_MISALIGNED, "lm_head_argmax: workspace must be 8-byte aligned");
+    const Range rws = range(workspace, need), rt = range(token, 4), rl = range(logits, (size_t)n_vocab * 4);
+    if (overlap(rws, range(w, (size_t)(n_vocab * row_bytes(k)))) || overlap(rws, range(h, (size_t)k * 2)) ||
+        overlap(rws, rl) || overlap(rws, rt) || overlap(rt, rl) ||
+        overlap(rt, range(w, (size_t)(n_vocab * row_bytes(k)))) || overlap(rt, range(h, (size_t)k * 2)))
+        return fail(Q4_ERR_INVALID_ARG, "lm_head_argmax: token, workspace and tensors must not overlap");
+    const hipError_t e = q4::launch_lm_head(static_cast<const uint8_t*>(w), static_cast<const uint16_t*>(h), logits,
+                                            token, n_vocab, k, static_cast<uint64_t*>(workspace),
+                                            static_cast<hipStream_t>(stream));
+    return hip_status(e, "lm_head_argmax launch");
+}
+
+size_t q4_0_gemv_batch_plan_bytes(int count) {
+    if (count < 1 || count > (1 << 20)) return 0;
+    return (size_t)count * sizeof(q4::PlanDesc);
+}
+
+q4_status q4_0_gemv_batch_plan(const q4_gemv_desc* descs, int count, void* plan_buf, size_t plan_bytes,
+                               q4_gemv_plan* plan, void* stream) {
+    const char* fn = "q4_0_gemv_batch_plan";
+    if (!descs || !plan || !plan_buf) return fail(Q4_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (count < 1 || count > (1 << 20)) return fail(Q4_ERR_INVALID_ARG, "%s: count = %d outside [1, 1<<20]", fn, count);
+    if (plan_bytes < q4_0_gemv_batch_plan_bytes(count))
+        return fail(Q4_ERR_WORKSPACE, "%s: plan buffer of %zu bytes needed", fn, q4_0_gemv_batch_plan_bytes(count));
+    if (!aligned(plan_buf, 16)) return fail(Q4_ERR_MISALIGNED, "%s: plan buffer must be 16-byte aligned", fn);
+    std::vector<q4::PlanDesc> dev(count);
+    std::vector<Range> outs, ins;
+    outs.reserve(count);
+    ins.reserve(2 * (size_t)count);
+    const int64_t rows_step = q4::batch_rows_per_step();
+    int64_t cost = 0;
+    int max_k = 0;
+    for (int i = 0; i < count; ++i) {
+        const q4_gemv_desc& d = descs[i];
+        q4_status st = check_shape(fn, 1, 1, d.n, d.k);
+        if (st) return fail(st, "%s: descriptor %d: %s", fn, i, std::string(g_err).c_str());
+        if (d.k % 64 != 0 || d.k > q4::kFastMaxK)
+            return fail(Q4_ERR_INVALID_ARG, "%s: descriptor %d: k must be a multiple of 64 up to %lld", fn, i, (long long)q4::kFastMaxK);
+        st = check_tensors(fn, d.w, d.x, d.y, 1, d.n, d.k, (size_t)d.n * 4);
+        if (st) return fail(st, "%s: descriptor %d: %s", fn, i, std::string(g_err).c_str());
+        q4::PlanDesc& p = dev[i];
+        p.w = static_cast<const uint8_t*>(d.w);
+        p.x = static_cast<const uint16_t*>(d.x);
+        p.y = d.y;
+        p.n = d.n;
+        p.k = (int32_t)d.k;
+        p.npl = (int32_t)(((d.k / 64) + 15) / 16);
+        p.steps = (d.n + rows_step - 1) / rows_step;
+        p.cost_begin = cost;
+        cost += p.steps * p.npl;
+        max_k = std::max<int>(max_k, (int)d.k);
+        outs.push_back(range(d.y, (size_t)d.n * 4));
+        ins.push_back(range(d.w, (size_t)(d.n * row_bytes(d.k))));
+        ins.push_back(range(d.x, (size_t)d.k * 2));
+    }
+    std::sort(outs.begin(), outs.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+    for (size_t i = 1; i < outs.size(); ++i)
+        if (outs[i].lo < outs[i - 1].hi) return fail(Q4_ERR_INVALID_ARG, "%s: two outputs overlap", fn);
+    for (const Range& r : ins) {
+        auto it = std::upper_bound(outs.begin(), outs.end(), r.lo, [](uintptr_t v, const Range& o) { return v < o.lo; });
+        if (it != outs.end() && overlap(*it, r)) return fail(Q4_ERR_INVALID_ARG, "%s: an output overlaps an input", fn);
+        if (it != outs.begin() && overlap(*(it - 1), r)) return fail(Q4_ERR_INVALID_ARG, "%s: an output overlaps an input", fn);
+    }
+    const Range rp = range(plan_buf, q4_0_gemv_batch_plan_bytes(count));
+    for (const Range& r : outs)
+        if (overlap(r, rp)) return fail(Q4_ERR_INVALID_ARG, "%s: plan buffer overlaps an output", fn);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(plan_buf, dev.data(), dev.size() * sizeof(q4::PlanDesc), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_status(e, "q4_0_gemv_batch_plan copy");
+    plan->device = plan_buf;
+    plan->count = count;
+    plan->max_k = max_k;
+    plan->total_cost = cost;
+    return ok();
+}
+
+q4_status q4_0_gemv_batch(const q4_gemv_plan* plan, void* stream) {
+    if (!plan || !plan->device) return fail(Q4_ERR_INVALID_ARG, "q4_0_gemv_batch: null plan");
+    if (plan->count < 1 || plan->max_k < 64 || plan->max_k > q4::kFastMaxK || plan->total_cost < 1)
+        return fail(Q4_ERR_INVALID_ARG, "q4_0_gemv_batch: plan was not filled by q4_0_gemv_batch_plan");
+    const hipError_t e = q4::launch_gemv_batch(static_cast<const q4::PlanDesc*>(plan->device), plan->count,
+                                               plan->total_cost, plan->max_k, static_cast<hipStream_t>(stream));
+    return hip_status(e, "q4_0_gemv_batch launch");
+}
+
+}  // extern "C"

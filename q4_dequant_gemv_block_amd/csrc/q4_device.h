@@ -1,0 +1,159 @@
+// Device-side building blocks for the Q4_0 kernels (gfx950, wave64).
+//
+// Q4_0 block (the format the pages call "GGUF Q4_0"; taozi.news, section
+// "支持模型与限制"): 18 bytes = f16 scale d, then 16 code bytes, byte j holding
+// code j (low nibble) and code j+16 (high nibble); weight = (code - 8) * d.
+//
+// Two consecutive blocks ("a pair", 36 bytes) start on a 4-byte boundary
+// whenever the row stride is a multiple of 4 (K % 64 == 0), so a lane reads a
+// pair as nine dwords D0..D8:
+//   D0 = [d0 lo, d0 hi, c0, c1]      block 0 scale and code bytes 0-1
+//   D1..D3 = block 0 code bytes 2..13
+//   D4 = [c14, c15, d1 lo, d1 hi]    block 0 code bytes 14-15, block 1 scale
+//   D5..D8 = block 1 code bytes 0..15
+// Block 0's code bytes are re-aligned with one byte permute:
+//   E0 = [c14, c15, c0, c1] = perm(D0, D4), E1..E3 = D1..D3.
+//
+// A code dword V with bytes (codes a, b, c, e in the low nibbles and a+16,
+// b+16, c+16, e+16 in the high nibbles) expands to four f16 pairs with exact
+// values code - 8:
+//   (a, c)        : (V      & 0x000F000F) | 0x6400 6400 -> 1024 + q, minus 1032
+//   (a+16, c+16)  : (V      & 0x00F000F0) | 0x5400 5400 -> 64 + q,   minus 72
+//   (b, e)        : (V >> 8 & 0x000F000F) | 0x6400 6400
+//   (b+16, e+16)  : (V >> 8 & 0x00F000F0) | 0x5400 5400
+// (0x6400 is 1024.0 with unit spacing, 0x5400 is 64.0 with spacing 1/16, so a
+// nibble OR-ed into bits 0-3 or 4-7 adds exactly q).  Each pair then meets the
+// matching pair of activations in one v_dot2 (f16 x f16 products are exact in
+// f32; sums round in f32), and the block sum is scaled once by d.
+//
+// The activations are therefore stored, per code dword, as the four f16
+// pairs (x_a, x_c), (x_a+16, x_c+16), (x_b, x_e), (x_b+16, x_e+16): one 16-byte
+// "chunk".  A pair of blocks has 8 chunks; in LDS chunk c of pair p lives at
+// index c * npp + p (npp = pairs rounded up to a multiple of 16), so the 16
+// lanes that share a row read 16 consecutive chunks (no bank conflicts).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4 {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u2a4 __attribute__((ext_vector_type(2), aligned(4)));
+
+constexpr int kWave = 64;
+constexpr int kLanesPerRow = 16;   // one DPP row of lanes shares a weight row
+constexpr int kPairBytes = 36;
+constexpr int kBlockBytes = 18;
+constexpr int kChunksPerPair = 8;
+
+__device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
+__device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// (v & mask) | bias as one v_and_or_b32; gfx9 VOP3 takes no literal, so the
+// mask rides in an SGPR and the bias in a VGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t mask, uint32_t bias) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "s"(mask), "v"(bias));
+    return r;
+}
+
+// Block 0 of a pair: code bytes 14,15 (low half of D4) then 0,1 (high half of D0).
+__device__ __forceinline__ uint32_t realign_block0(uint32_t d0, uint32_t d4) {
+    return __builtin_amdgcn_perm(d0, d4, 0x07060100u);
+}
+
+// Four exact (code - 8) f16 pairs of one code dword, in chunk order.
+struct Codes4 {
+    h2 q0, q1, q2, q3;
+};
+
+__device__ __forceinline__ Codes4 expand(uint32_t v) {
+    const uint32_t u = v >> 8;
+    const h2 c1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const h2 c72 = {(_Float16)72.0f, (_Float16)72.0f};
+    Codes4 r;
+    r.q0 = as_h2(and_or(v, 0x000F000Fu, 0x64006400u)) - c1032;
+    r.q1 = as_h2(and_or(v, 0x00F000F0u, 0x54005400u)) - c72;
+    r.q2 = as_h2(and_or(u, 0x000F000Fu, 0x64006400u)) - c1032;
+    r.q3 = as_h2(and_or(u, 0x00F000F0u, 0x54005400u)) - c72;
+    return r;
+}
+
+__device__ __forceinline__ float dot_chunk(const Codes4& q, u4 x, float s) {
+    s = __builtin_amdgcn_fdot2(q.q0, as_h2(x.x), s, false);
+    s = __builtin_amdgcn_fdot2(q.q1, as_h2(x.y), s, false);
+    s = __builtin_amdgcn_fdot2(q.q2, as_h2(x.z), s, false);
+    s = __builtin_amdgcn_fdot2(q.q3, as_h2(x.w), s, false);
+    return s;
+}
+
+__device__ __forceinline__ float f16_lo(uint32_t v) { return (float)as_h2(v).x; }
+__device__ __forceinline__ float f16_hi(uint32_t v) { return (float)as_h2(v).y; }
+
+// acc + d0 * S0 + d1 * S1 for one pair of blocks held in D[0..8], with the
+// eight activation chunks X[0..7] of that pair.
+__device__ __forceinline__ float pair_dot(const uint32_t (&D)[9], const u4 (&X)[8], float acc) {
+    float s0 = 0.0f, s1 = 0.0f;
+    s0 = dot_chunk(expand(realign_block0(D[0], D[4])), X[0], s0);
+    s0 = dot_chunk(expand(D[1]), X[1], s0);
+    s0 = dot_chunk(expand(D[2]), X[2], s0);
+    s0 = dot_chunk(expand(D[3]), X[3], s0);
+    s1 = dot_chunk(expand(D[5]), X[4], s1);
+    s1 = dot_chunk(expand(D[6]), X[5], s1);
+    s1 = dot_chunk(expand(D[7]), X[6], s1);
+    s1 = dot_chunk(expand(D[8]), X[7], s1);
+    acc = __builtin_fmaf(f16_lo(D[0]), s0, acc);
+    acc = __builtin_fmaf(f16_hi(D[4]), s1, acc);
+    return acc;
+}
+
+// Streaming (non-temporal) load of one pair of blocks at a 4-byte aligned address.
+__device__ __forceinline__ void load_pair(const uint8_t* p, uint32_t (&D)[9]) {
+    const u4a4 a = __builtin_nontemporal_load(reinterpret_cast<const u4a4*>(p));
+    const u4a4 b = __builtin_nontemporal_load(reinterpret_cast<const u4a4*>(p + 16));
+    const uint32_t c = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p + 32));
+    D[0] = a.x; D[1] = a.y; D[2] = a.z; D[3] = a.w;
+    D[4] = b.x; D[5] = b.y; D[6] = b.z; D[7] = b.w;
+    D[8] = c;
+}
+
+__device__ __forceinline__ void zero_pair(uint32_t (&D)[9]) {
+#pragma unroll
+    for (int i = 0; i < 9; ++i) D[i] = 0u;  // scale +0: contributes exactly 0
+}
+
+// Sum over the 16 lanes of a DPP row, in a fixed order; every lane gets a
+// value, lane 0 of the row holds ((v0+v1)+(v2+v3)) + ... in the same order for
+// every row, so equal rows give equal sums wherever they sit.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_mov<0x124>(v);  // row_ror:4
+    v += dpp_mov<0x128>(v);  // row_ror:8
+    return v;
+}
+
+// Activation chunk c (0..7) of pair p from 64 f16 values x[0..63] of that pair.
+// Code-dword byte positions (low-nibble codes a, b, c, e):
+//   chunk 0: 14, 15, 0, 1 (re-aligned block 0); chunks 1..3: 4c-2 .. 4c+1;
+//   chunks 4..7: block 1, positions 4(c-4) .. 4(c-4)+3, offset 32.
+__host__ __device__ inline void chunk_positions(int c, int (&pos)[4]) {
+    if (c == 0) {
+        pos[0] = 14; pos[1] = 15; pos[2] = 0; pos[3] = 1;
+    } else if (c < 4) {
+        pos[0] = 4 * c - 2; pos[1] = 4 * c - 1; pos[2] = 4 * c; pos[3] = 4 * c + 1;
+    } else {
+        const int b = 32 + 4 * (c - 4);
+        pos[0] = b; pos[1] = b + 1; pos[2] = b + 2; pos[3] = b + 3;
+    }
+}
+
+}  // namespace q4

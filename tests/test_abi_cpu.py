@@ -1,0 +1,121 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host (no GPU is touched: every call here fails validation
+before anything would be enqueued)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import q4_dequant_gemv_block_amd as q4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4gemv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(q4.LIB_PATH):
+        from q4_dequant_gemv_block_amd import build
+        build.build()
+    return q4.load_library()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"Q4_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_symbols()
+    for required in ("q4_0_gemv", "q4_0_gemm_smallm", "q4_0_gemm_prefill", "lm_head_argmax"):
+        assert required in names
+    assert sorted(q4.EXPORTS) == names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.check_output(["nm", "-D", "--defined-only", q4.LIB_PATH]).decode()
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_symbols():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+    # nothing else of ours leaks out with default visibility
+    ours = {n for n in exported if n.startswith(("q4", "lm_head"))}
+    assert ours == set(declared_symbols())
+
+
+def test_abi_version(lib):
+    assert lib.q4_abi_version() == 1
+
+
+def test_workspace_bytes(lib):
+    assert lib.q4_workspace_bytes(q4.Q4_OP_GEMV, 1, 5120, 5120) == 0
+    assert lib.q4_workspace_bytes(q4.Q4_OP_GEMM_SMALLM, 16, 5120, 5120) == 0
+    ws = lib.q4_workspace_bytes(q4.Q4_OP_LM_HEAD_ARGMAX, 1, 151936, 5120)
+    assert ws >= 8 and ws % 8 == 0
+    assert lib.q4_workspace_bytes(99, 1, 1, 32) == 0
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("args, code", [
+    ((0, FAKE, FAKE * 4, 8, 64), q4.Q4_ERR_INVALID_ARG),           # null w
+    ((FAKE, FAKE * 2, FAKE * 4, 0, 64), q4.Q4_ERR_INVALID_ARG),     # n = 0
+    ((FAKE, FAKE * 2, FAKE * 4, 8, 48), q4.Q4_ERR_INVALID_ARG),     # k % 32
+    ((FAKE, FAKE * 2, FAKE * 4, 8, 0), q4.Q4_ERR_INVALID_ARG),      # k = 0
+    ((FAKE + 4, FAKE * 2, FAKE * 4, 8, 64), q4.Q4_ERR_MISALIGNED),  # w not 16-aligned
+    ((FAKE, FAKE * 2 + 8, FAKE * 4, 8, 64), q4.Q4_ERR_MISALIGNED),  # x not 16-aligned
+    ((FAKE, FAKE * 2, FAKE * 4 + 2, 8, 64), q4.Q4_ERR_MISALIGNED),  # y not 4-aligned
+    ((FAKE, FAKE * 2, FAKE + 16, 8, 64), q4.Q4_ERR_INVALID_ARG),    # y overlaps w
+])
+def test_gemv_validation(lib, args, code):
+    assert lib.q4_0_gemv(*args, None) == code
+    assert lib.q4_last_error()
+
+
+def test_smallm_validation(lib):
+    assert lib.q4_0_gemm_smallm(FAKE, FAKE * 2, FAKE * 8, 17, 8, 64, None) == q4.Q4_ERR_INVALID_ARG
+    assert lib.q4_0_gemm_smallm(FAKE, FAKE * 2, FAKE * 8, 0, 8, 64, None) == q4.Q4_ERR_INVALID_ARG
+    assert b"m = 17" in lib.q4_last_error() or b"m = 0" in lib.q4_last_error()
+
+
+def test_prefill_validation(lib):
+    assert lib.q4_0_gemm_prefill(FAKE, FAKE * 2, FAKE * 8, 0, 8, 64, None, 0, None) == q4.Q4_ERR_INVALID_ARG
+    assert lib.q4_0_gemm_prefill(FAKE, FAKE * 2, FAKE * 8, 4, 8, 40, None, 0, None) == q4.Q4_ERR_INVALID_ARG
+
+
+def test_lm_head_validation(lib):
+    w, h, lg, tok = FAKE, FAKE * 2, FAKE * 4, FAKE * 8
+    need = lib.q4_workspace_bytes(q4.Q4_OP_LM_HEAD_ARGMAX, 1, 1000, 64)
+    assert lib.lm_head_argmax(w, h, lg, tok, 1000, 64, None, 0, None) == q4.Q4_ERR_WORKSPACE
+    assert lib.lm_head_argmax(w, h, lg, tok, 1000, 64, FAKE * 16, need - 8, None) == q4.Q4_ERR_WORKSPACE
+    assert lib.lm_head_argmax(w, h, lg, 0, 1000, 64, FAKE * 16, need, None) == q4.Q4_ERR_INVALID_ARG
+    assert lib.lm_head_argmax(w, h, lg, tok + 2, 1000, 64, FAKE * 16, need, None) == q4.Q4_ERR_MISALIGNED
+    # token inside the logits
+    assert lib.lm_head_argmax(w, h, lg, lg + 8, 1000, 64, FAKE * 16, need, None) == q4.Q4_ERR_INVALID_ARG
+    # k % 64 != 0 is not supported here
+    assert lib.lm_head_argmax(w, h, lg, tok, 1000, 96, FAKE * 16, need, None) == q4.Q4_ERR_INVALID_ARG
+
+
+def test_batch_plan_validation(lib):
+    D = q4.GemvDesc
+    plan = q4.GemvPlan()
+    buf = FAKE * 64
+    arr = (D * 2)(D(FAKE, FAKE * 2, FAKE * 4, 8, 64), D(FAKE * 8, FAKE * 2, FAKE * 4 + 16, 8, 64))
+    nbytes = lib.q4_0_gemv_batch_plan_bytes(2)
+    assert nbytes > 0
+    # the two outputs overlap
+    assert lib.q4_0_gemv_batch_plan(arr, 2, buf, nbytes, ctypes.byref(plan), None) == q4.Q4_ERR_INVALID_ARG
+    # k not a multiple of 64
+    arr = (D * 1)(D(FAKE, FAKE * 2, FAKE * 4, 8, 96))
+    assert lib.q4_0_gemv_batch_plan(arr, 1, buf, nbytes, ctypes.byref(plan), None) == q4.Q4_ERR_INVALID_ARG
+    # plan buffer too small, count 0, output overlapping another descriptor's input
+    arr = (D * 1)(D(FAKE, FAKE * 2, FAKE * 4, 8, 64))
+    assert lib.q4_0_gemv_batch_plan(arr, 1, buf, 1, ctypes.byref(plan), None) == q4.Q4_ERR_WORKSPACE
+    assert lib.q4_0_gemv_batch_plan(arr, 0, buf, nbytes, ctypes.byref(plan), None) == q4.Q4_ERR_INVALID_ARG
+    arr = (D * 2)(D(FAKE, FAKE * 2, FAKE * 4, 8, 64), D(FAKE * 8, FAKE * 4, FAKE * 6, 8, 64))
+    assert lib.q4_0_gemv_batch_plan(arr, 2, buf, nbytes, ctypes.byref(plan), None) == q4.Q4_ERR_INVALID_ARG
+    # an unfilled plan is refused
+    assert lib.q4_0_gemv_batch(ctypes.byref(q4.GemvPlan()), None) == q4.Q4_ERR_INVALID_ARG
