@@ -175,8 +175,8 @@ def bench_sweep(args):
         "implied_tok_s": round(1000.0 / (ms + lm_ms), 2),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4),
-                     "traffic": counter_traffic("k_gemv_batch", "sweep"),
-                     "kernel": "q4::k_gemv_batch<2,4>", "launches_per_step": 1},
+                     "traffic": counter_traffic("k_sweep", "sweep"),
+                     "kernel": "q4::k_sweep<PairLoads<2,2>> (batch)", "launches_per_step": 1},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(ids)
@@ -210,8 +210,8 @@ def bench_gemv(args):
             "data": "synthetic", "config": {"workload": "single Q4_0 GEMV 5120x5120, 48 rotating weight copies"},
             "hot_cache_GBps": round(bytes_ / (hot_ms * 1e-3) / 1e9, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counter_traffic("k_gemv", "gemv"),
-                         "kernel": "q4::k_gemv"}}
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counter_traffic("k_sweep", "gemv"),
+                         "kernel": "q4::k_sweep<PairLoads<2,2>>"}}
 
 
 def bench_lmhead(args):
@@ -232,8 +232,8 @@ def bench_lmhead(args):
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16->f32",
             "data": "synthetic", "config": {"workload": "LM head 151936x5120 + argmax"},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counter_traffic("k_gemv", "lmhead"),
-                         "kernel": "q4::k_gemv<ARGMAX> + q4::k_argmax_final"}}
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counter_traffic("k_sweep", "lmhead"),
+                         "kernel": "q4::k_sweep<PairLoads<2,1>,ARGMAX> + q4::k_argmax_final"}}
 
 
 def bench_gemm(args, prefill: bool):

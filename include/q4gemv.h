@@ -169,6 +169,7 @@ typedef struct q4_gemv_plan {
     void* device;        /* the caller's device buffer holding the descriptors */
     int count;           /* number of GEMVs */
     int max_k;           /* largest k in the list */
+    int flags;           /* launch path chosen at planning time (internal) */
     int64_t total_cost;  /* work measure used to split the list across workgroups */
 } q4_gemv_plan;
 

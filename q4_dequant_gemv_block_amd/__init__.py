@@ -53,7 +53,7 @@ class GemvDesc(ctypes.Structure):
 
 class GemvPlan(ctypes.Structure):
     _fields_ = [("device", ctypes.c_void_p), ("count", ctypes.c_int), ("max_k", ctypes.c_int),
-                ("total_cost", ctypes.c_int64)]
+                ("flags", ctypes.c_int), ("total_cost", ctypes.c_int64)]
 
 
 _lib = None

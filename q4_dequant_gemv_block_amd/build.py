@@ -36,13 +36,14 @@ def hipcc():
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, defines=()) -> str:
+    """Compile every source and link libq4gemv.so; `defines` are extra -D flags."""
     objs = []
     build_dir = os.path.join(HERE, "_build")
     os.makedirs(build_dir, exist_ok=True)
     for src in SOURCES:
         obj = os.path.join(build_dir, src + ".o")
-        cmd = [hipcc()] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc()] + FLAGS + ["-D" + d for d in defines] + ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.check_call(cmd)

@@ -1,6 +1,6 @@
 // C ABI of the Q4_0 library: argument validation, error text, dispatch to the
 // kernel launchers.  Every check runs on the host before anything is enqueued.
-#include "../../include/q4gemv.h"
+#include "q4gemv.h"
 #include "q4_launch.h"
 
 #include <hip/hip_runtime.h>
@@ -190,6 +190,7 @@ q4_status q4_0_gemv_batch_plan(const q4_gemv_desc* descs, int count, void* plan_
     const int64_t rows_step = q4::batch_rows_per_step();
     int64_t cost = 0;
     int max_k = 0;
+    bool all_k1024 = true;
     for (int i = 0; i < count; ++i) {
         const q4_gemv_desc& d = descs[i];
         q4_status st = check_shape(fn, 1, 1, d.n, d.k);
@@ -209,6 +210,7 @@ q4_status q4_0_gemv_batch_plan(const q4_gemv_desc* descs, int count, void* plan_
         p.cost_begin = cost;
         cost += p.steps * p.npl;
         max_k = std::max<int>(max_k, (int)d.k);
+        all_k1024 = all_k1024 && d.k % 1024 == 0;
         outs.push_back(range(d.y, (size_t)d.n * 4));
         ins.push_back(range(d.w, (size_t)(d.n * row_bytes(d.k))));
         ins.push_back(range(d.x, (size_t)d.k * 2));
@@ -231,6 +233,7 @@ q4_status q4_0_gemv_batch_plan(const q4_gemv_desc* descs, int count, void* plan_
     plan->device = plan_buf;
     plan->count = count;
     plan->max_k = max_k;
+    plan->flags = all_k1024 ? 1 : 0;
     plan->total_cost = cost;
     return ok();
 }
@@ -240,7 +243,8 @@ q4_status q4_0_gemv_batch(const q4_gemv_plan* plan, void* stream) {
     if (plan->count < 1 || plan->max_k < 64 || plan->max_k > q4::kFastMaxK || plan->total_cost < 1)
         return fail(Q4_ERR_INVALID_ARG, "q4_0_gemv_batch: plan was not filled by q4_0_gemv_batch_plan");
     const hipError_t e = q4::launch_gemv_batch(static_cast<const q4::PlanDesc*>(plan->device), plan->count,
-                                               plan->total_cost, plan->max_k, static_cast<hipStream_t>(stream));
+                                               plan->total_cost, plan->max_k, (plan->flags & 1) != 0,
+                                               static_cast<hipStream_t>(stream));
     return hip_status(e, "q4_0_gemv_batch launch");
 }
 

@@ -1,25 +1,39 @@
-// Q4_0 matrix-vector kernels for gfx950: single GEMV, the one-launch batch of
-// GEMVs (a whole decode weight sweep), the LM head with greedy argmax, and a
-// generic kernel for shapes the fast path does not take.
+// Q4_0 matrix-vector kernels for gfx950: a single GEMV, a list of GEMVs in
+// one launch (a whole decode weight sweep), the LM head with greedy argmax,
+// and a generic kernel for shapes the fast path does not take.
 //
 // Decode reads every weight once per token and is bound by memory bandwidth
 // ("Every Device Brings a Slice: How SwarmLLM Runs a 27B Model Across Browser
 // Tabs", originshq.com, section "The Engine: ~50 WGSL Kernels Written From
-// Scratch").  The kernels here keep that structure but are laid out for CDNA4:
+// Scratch").  The kernels keep that structure, laid out for CDNA4:
 //
 //  * 16 lanes (one DPP row) own one weight row; lane l takes block pairs
 //    l, l+16, l+32, ... so the 16 lanes of a row read 576 contiguous bytes per
-//    step, and the 4 rows of a wave are R rows apart.  Each lane keeps R rows
-//    in flight at the same pair positions, so one read of the activation
-//    chunks from LDS serves R rows.
-//  * Weights are read with non-temporal dwordx4/dword loads (36-byte pairs at
-//    4-byte alignment); the 4-bit codes become exact (code - 8) f16 pairs with
-//    one v_and_or_b32 and one v_pk_add_f16 per pair and meet the activations
-//    in v_dot2_f32_f16; the block scale is applied once per block in f32.
-//  * The activation vector is staged once per workgroup into LDS in the
-//    chunk order of q4_device.h, conflict-free for the 16-lane row reads.
+//    step.  Each lane group carries R consecutive rows at the same pair
+//    positions, so one read of the activation chunks from LDS serves R rows.
+//  * Weights are read with global dwordx4/dword loads (36-byte pairs at
+//    4-byte alignment); 4-bit codes become exact (code - 8) f16 pairs
+//    with one v_and_or_b32 and one v_pk_add_f16 per pair and meet the
+//    activations in v_dot2_f32_f16; the block scale is applied once per block
+//    in f32 (v_fma_mix).
+//  * The activation vector is staged once per workgroup and GEMV into LDS in
+//    the chunk order of q4_device.h (conflict-free for the 16-lane reads).
+//  * Every wave walks a sequence of units (a group of 4R rows x JB pairs per
+//    lane) and issues the loads of the next unit before computing the current
+//    one, also across row groups and GEMV boundaries, so the memory pipe never
+//    drains inside a workgroup's range.
+//  * Out-of-range rows and pairs load from clamped in-range addresses instead
+//    of branching: padding pairs meet zero activation chunks and add exactly
+//    0, padding rows are never stored.
 //  * The row sum is a fixed-order DPP tree inside the 16-lane row, so results
 //    are deterministic and independent of where a row sits.
+//
+// Work split: a work item is (GEMV d, row step s of 16R rows); it starts at
+// cost cost_begin[d] + s * npl[d], npl (pairs per lane) being proportional to
+// its bytes.  Workgroup g takes every item starting in [T*g/G, T*(g+1)/G):
+// contiguous, byte-balanced ranges, so a workgroup stages few activation
+// vectors.  The single-GEMV and LM-head entry points run the same kernel on a
+// one-descriptor list passed by value.
 #include "q4_device.h"
 #include "q4_launch.h"
 
@@ -28,22 +42,73 @@
 
 namespace q4 {
 
-constexpr int kThreads = 256;  // 4 waves
-constexpr int kBatchR = 2;     // rows per lane group in the batch kernel
-constexpr int kBatchJB = 4;    // pairs per lane loaded before compute
+// Build-time shape of the engine (defaults measured best on MI355X).
+#ifndef Q4_SWEEP_R
+#define Q4_SWEEP_R 2
+#endif
+#ifndef Q4_SWEEP_JB
+#define Q4_SWEEP_JB 2
+#endif
+#ifndef Q4_SWEEP_WG_PER_CU
+#define Q4_SWEEP_WG_PER_CU 2
+#endif
+#ifndef Q4_SWEEP_THREADS
+#define Q4_SWEEP_THREADS 512
+#endif
+#ifndef Q4_SWEEP_WPE
+#define Q4_SWEEP_WPE 4
+#endif
+#ifndef Q4_SWEEP_COALESCED
+#define Q4_SWEEP_COALESCED 0
+#endif
+#ifndef Q4_SWEEP_NB_PAIR
+#define Q4_SWEEP_NB_PAIR 2
+#endif
+#ifndef Q4_SWEEP_NB_COAL
+#define Q4_SWEEP_NB_COAL 2
+#endif
 
-int batch_rows_per_step() { return 16 * kBatchR; }
+constexpr int kThreads = Q4_SWEEP_THREADS;  // the waves of a workgroup share one staged activation vector
+constexpr int kWavesPerEu = Q4_SWEEP_WPE;   // register budget: waves per SIMD the sweep kernel must fit
+constexpr int kWaves = kThreads / 64;
+constexpr int kR = Q4_SWEEP_R;         // rows per 16-lane group
+constexpr int kJB = Q4_SWEEP_JB;       // pairs per lane per unit
+constexpr int kWgPerCu = Q4_SWEEP_WG_PER_CU;
+constexpr int kNBP = Q4_SWEEP_NB_PAIR;  // unit buffers in the ring, per-lane pair loads
+constexpr int kNBC = Q4_SWEEP_NB_COAL;  // unit buffers in the ring, coalesced loads
+
+int batch_rows_per_step() { return kWaves * 4 * kR; }
+
+typedef __attribute__((address_space(1))) float g_f32;
 
 // ---------------------------------------------------------------------------
 // Activation staging: the 8 chunks of every block pair, chunk c of pair p at
 // xs[c * npp + p]; pairs >= k/64 (padding up to npp) are zero.
 // ---------------------------------------------------------------------------
+template <int HALF>
+__device__ __forceinline__ void stage_block(const uint32_t (&v)[16], int p, int npp, u4* __restrict__ xs) {
+    auto xe = [&](int j) -> uint32_t { return (v[j >> 1] >> (16 * (j & 1))) & 0xFFFFu; };
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+        int pos[4];
+        chunk_positions(4 * HALF + cc, pos);
+        const int off = 32 * HALF;
+        const int a = pos[0] - off, b = pos[1] - off, c = pos[2] - off, e = pos[3] - off;
+        u4 ent;
+        ent.x = xe(a) | (xe(c) << 16);
+        ent.y = xe(a + 16) | (xe(c + 16) << 16);
+        ent.z = xe(b) | (xe(e) << 16);
+        ent.w = xe(b + 16) | (xe(e + 16) << 16);
+        xs[(4 * HALF + cc) * npp + p] = ent;
+    }
+}
+
 __device__ void stage_x(const uint16_t* __restrict__ x, int nblocks, int npp, u4* __restrict__ xs) {
     const int nb_pad = 2 * npp;
     for (int b = threadIdx.x; b < nb_pad; b += blockDim.x) {
-        uint32_t v[16];  // 32 f16 values of block b, two per dword
+        uint32_t v[16];  // the 32 f16 values of block b, two per dword
         if (b < nblocks) {
-            const u4* src = reinterpret_cast<const u4*>(x + 32 * (int64_t)b);
+            g_u4* src = (g_u4*)(x + 32 * (int64_t)b);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const u4 t = src[i];
@@ -53,72 +118,11 @@ __device__ void stage_x(const uint16_t* __restrict__ x, int nblocks, int npp, u4
 #pragma unroll
             for (int i = 0; i < 16; ++i) v[i] = 0u;
         }
-        auto xe = [&](int j) -> uint32_t { return (v[j >> 1] >> (16 * (j & 1))) & 0xFFFFu; };
-        const int p = b >> 1;
-        const int base = (b & 1) ? 4 : 0;
-        const int off = (b & 1) ? 32 : 0;
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-            int pos[4];
-            chunk_positions(base + cc, pos);
-            const int a = pos[0] - off, bb = pos[1] - off, c = pos[2] - off, e = pos[3] - off;
-            u4 ent;
-            ent.x = xe(a) | (xe(c) << 16);
-            ent.y = xe(a + 16) | (xe(c + 16) << 16);
-            ent.z = xe(bb) | (xe(e) << 16);
-            ent.w = xe(bb + 16) | (xe(e + 16) << 16);
-            xs[(base + cc) * npp + p] = ent;
-        }
+        if (b & 1)
+            stage_block<1>(v, b >> 1, npp, xs);
+        else
+            stage_block<0>(v, b >> 1, npp, xs);
     }
-}
-
-// ---------------------------------------------------------------------------
-// One wave, 4*R rows: rows row0 + 4*i + q (q = lane / 16) for i < R... laid out
-// as lane group q taking rows row0 + q*R + i.  Returns the 16-lane sums.
-// ---------------------------------------------------------------------------
-template <int R, int JB>
-__device__ __forceinline__ void rows_dot(const uint8_t* __restrict__ w, int64_t rb, int64_t n,
-                                         int np, int npl, const u4* __restrict__ xs, int npp,
-                                         int64_t row0, float (&out)[R]) {
-    const int lane = threadIdx.x & 63;
-    const int l = lane & 15;
-    const int64_t rbase = row0 + (lane >> 4) * R;
-    float acc[R];
-#pragma unroll
-    for (int i = 0; i < R; ++i) acc[i] = 0.0f;
-
-    for (int jb = 0; jb < npl; jb += JB) {
-        uint32_t D[JB][R][9];
-#pragma unroll
-        for (int t = 0; t < JB; ++t) {
-            const int j = jb + t;
-            if (j < npl) {
-                const int p = l + 16 * j;
-#pragma unroll
-                for (int i = 0; i < R; ++i) {
-                    const int64_t r = rbase + i;
-                    if (r < n && p < np)
-                        load_pair(w + r * rb + (int64_t)p * kPairBytes, D[t][i]);
-                    else
-                        zero_pair(D[t][i]);
-                }
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < JB; ++t) {
-            const int j = jb + t;
-            if (j < npl) {
-                const int p = l + 16 * j;
-                u4 X[8];
-#pragma unroll
-                for (int c = 0; c < 8; ++c) X[c] = xs[c * npp + p];
-#pragma unroll
-                for (int i = 0; i < R; ++i) acc[i] = pair_dot(D[t][i], X, acc[i]);
-            }
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < R; ++i) out[i] = row16_sum(acc[i]);
 }
 
 // Order-preserving key: larger logit first, then lower index; -0 counts as +0.
@@ -133,48 +137,277 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* sh) {
     sh[threadIdx.x] = v;
     __syncthreads();
     for (int s = kThreads / 2; s > 0; s >>= 1) {
-        if ((int)threadIdx.x < s) sh[threadIdx.x] = sh[threadIdx.x] > sh[threadIdx.x + s] ? sh[threadIdx.x] : sh[threadIdx.x + s];
+        if ((int)threadIdx.x < s) {
+            const uint64_t o = sh[threadIdx.x + s];
+            if (o > sh[threadIdx.x]) sh[threadIdx.x] = o;
+        }
         __syncthreads();
     }
     return sh[0];
 }
 
 // ---------------------------------------------------------------------------
-// Single GEMV (optionally with per-workgroup argmax keys).
+// The GEMV engine.  A wave's unit is 4R consecutive rows x JB pairs per lane
+// (pairs [16*jb, 16*(jb+JB)) of each row); lane group q = lane / 16 owns rows
+// q*R .. q*R+R-1 of the unit, lane l = lane % 16 owns pairs l + 16*(jb+t).
+// Two ways to bring a unit's bytes in (the "policies"):
+//   PairLoads:      every lane loads its own 36-byte pairs (any k % 64 == 0).
+//   CoalescedLoads: the wave loads the unit's rows as consecutive 16-byte
+//                   pieces (fully coalesced, non-temporal), parks them in a
+//                   wave-private LDS window and every lane reads its pairs
+//                   back; needs k % 1024 == 0 so each row is whole 16-pair
+//                   segments.  Measured on a load-only copy: 6.85 TB/s for
+//                   this pattern against 6.2 TB/s for per-lane pair loads.
 // ---------------------------------------------------------------------------
-template <int R, int JB, bool ARGMAX>
-__global__ void __launch_bounds__(kThreads) k_gemv(const uint8_t* __restrict__ w,
-                                                   const uint16_t* __restrict__ x,
-                                                   float* __restrict__ y, int64_t n, int k,
-                                                   uint64_t* __restrict__ keys) {
-    extern __shared__ u4 xs[];
-    const int np = k / 64;
-    const int npp = (np + 15) & ~15;
-    const int npl = npp / 16;
-    const int64_t rb = (int64_t)np * kPairBytes;
-    stage_x(x, k / 32, npp, xs);
-    __syncthreads();
+struct Cursor {
+    int d;       // descriptor
+    int64_t s;   // row step within the descriptor
+    int jb;      // first pair-per-lane index of the unit
+};
 
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int64_t rows_per_step = 16 * R;
-    uint64_t best = 0;
-    for (int64_t step = blockIdx.x; step * rows_per_step < n; step += gridDim.x) {
-        const int64_t row0 = step * rows_per_step + (int64_t)wave * 4 * R;
-        float out[R];
-        rows_dot<R, JB>(w, rb, n, np, npl, xs, npp, row0, out);
-        if ((lane & 15) == 0) {
-            const int64_t rbase = row0 + (lane >> 4) * R;
+struct Ctx {
+    int wave, lane;
+    __device__ __forceinline__ int64_t wave_row0(const Cursor& c, int R) const {
+        return c.s * (kWaves * 4 * R) + (int64_t)wave * 4 * R;
+    }
+};
+
+template <int R, int JB>
+struct PairLoads {
+    struct Buf {
+        uint32_t d[JB][R][9];
+    };
+    static constexpr int kWaveLds = 0;
+    static constexpr bool kCoalesced = false;
+
+    __device__ __forceinline__ static void issue(const Ctx& x, const PlanDesc& D, const Cursor& c, Buf& b) {
+        const int np = D.k >> 6;
+        const int64_t rb = (int64_t)np * kPairBytes;
+        const int64_t r0 = x.wave_row0(c, R) + (x.lane >> 4) * R;
+        const int l = x.lane & 15;
 #pragma unroll
-            for (int i = 0; i < R; ++i) {
-                const int64_t r = rbase + i;
-                if (r < n) {
-                    y[r] = out[i];
-                    if (ARGMAX) {
-                        const uint64_t kk = argmax_key(out[i], r);
-                        best = kk > best ? kk : best;
+        for (int t = 0; t < JB; ++t) {
+            const int j = c.jb + t;
+            if (j < D.npl) {  // uniform
+                const int p = min(l + 16 * j, np - 1);
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    const int64_t r = min(r0 + i, D.n - 1);
+                    load_pair(D.w + r * rb + (int64_t)p * kPairBytes, b.d[t][i]);
+                }
+            }
+        }
+    }
+
+    __device__ __forceinline__ static void compute(const Ctx& x, const PlanDesc& D, const Cursor& c,
+                                                   const u4* __restrict__ xs, uint8_t* __restrict__ wl,
+                                                   const Buf& b, float (&acc)[R]) {
+        (void)wl;
+        const int npp = D.npl * 16;
+        const int l = x.lane & 15;
+#pragma unroll
+        for (int t = 0; t < JB; ++t) {
+            const int j = c.jb + t;
+            if (j < D.npl) {
+                const int p = l + 16 * j;
+                u4 X[8];
+#pragma unroll
+                for (int ch = 0; ch < 8; ++ch) X[ch] = xs[ch * npp + p];
+#pragma unroll
+                for (int i = 0; i < R; ++i) acc[i] = pair_dot(b.d[t][i], X, acc[i]);
+            }
+        }
+    }
+};
+
+template <int R, int JB>
+struct CoalescedLoads {
+    static constexpr int kSegBytes = 576 * JB;          // one row's part of a unit
+    static constexpr int kSegStride = kSegBytes + 32;   // padding staggers LDS banks between lane groups
+    static constexpr int kPieces = 36 * JB * 4 * R;     // 16-byte pieces per unit
+    static_assert(kPieces % 32 == 0, "R*JB must be even");
+    static constexpr int kPerLane = (kPieces + 63) / 64;  // the last slot may cover half the lanes
+    static constexpr int kWaveLds = 4 * R * kSegStride;
+    static constexpr bool kCoalesced = true;
+    struct Buf {
+        u4 v[kPerLane];
+    };
+
+    __device__ __forceinline__ static void issue(const Ctx& x, const PlanDesc& D, const Cursor& c, Buf& b) {
+        const int64_t rb = (int64_t)(D.k >> 6) * kPairBytes;  // a multiple of 576
+        const int64_t r0 = x.wave_row0(c, R);
+#pragma unroll
+        for (int k = 0; k < kPerLane; ++k) {
+            const int P = 64 * k + x.lane;
+            const int g = P / (36 * JB);
+            const int rem = P - g * (36 * JB);
+            const int t = rem / 36;
+            const int64_t r = min(r0 + g, D.n - 1);
+            const int64_t off = r * rb + 576 * (int64_t)c.jb + 16 * rem;
+            // pieces of a pair index past the row (only in a row's last unit) are not loaded
+            if (P < kPieces && c.jb + t < D.npl) b.v[k] = __builtin_nontemporal_load((g_u4*)(D.w + off));
+        }
+    }
+
+    __device__ __forceinline__ static void compute(const Ctx& x, const PlanDesc& D, const Cursor& c,
+                                                   const u4* __restrict__ xs, uint8_t* __restrict__ wl,
+                                                   const Buf& b, float (&acc)[R]) {
+#pragma unroll
+        for (int k = 0; k < kPerLane; ++k) {
+            const int P = 64 * k + x.lane;
+            const int g = P / (36 * JB);
+            if (P < kPieces) *(u4*)(wl + g * kSegStride + 16 * (P - g * 36 * JB)) = b.v[k];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int npp = D.npl * 16;
+        const int l = x.lane & 15;
+        const int q = x.lane >> 4;
+#pragma unroll
+        for (int t = 0; t < JB; ++t) {
+            const int j = c.jb + t;
+            if (j < D.npl) {
+                const int p = l + 16 * j;
+                u4 X[8];
+#pragma unroll
+                for (int ch = 0; ch < 8; ++ch) X[ch] = xs[ch * npp + p];
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    const uint32_t* src = (const uint32_t*)(wl + (q * R + i) * kSegStride + 576 * t + kPairBytes * l);
+                    uint32_t Dw[9];
+#pragma unroll
+                    for (int e = 0; e < 9; ++e) Dw[e] = src[e];
+                    acc[i] = pair_dot(Dw, X, acc[i]);
+                }
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+};
+
+__device__ __forceinline__ Cursor next_unit(const PlanDesc& D, Cursor c, int JB) {
+    c.jb += JB;
+    if (c.jb >= D.npl) {
+        c.jb = 0;
+        if (++c.s == D.steps) {
+            ++c.d;
+            c.s = 0;
+        }
+    }
+    return c;
+}
+
+template <class Policy, int R, int JB, int NB, bool ARGMAX>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEu))) k_sweep(const PlanDesc* __restrict__ descs, int count, PlanDesc one,
+                                                    int64_t total, int xs_bytes, uint64_t* __restrict__ keys) {
+    extern __shared__ u4 xs[];
+    Ctx x;
+    x.wave = threadIdx.x >> 6;
+    x.lane = threadIdx.x & 63;
+    uint8_t* wl = reinterpret_cast<uint8_t*>(xs) + xs_bytes + x.wave * Policy::kWaveLds;
+    const int n_desc = descs ? count : 1;
+    auto get = [&](int d) -> PlanDesc { return descs ? descs[d] : one; };
+    const int64_t G = gridDim.x;
+    const int64_t c_lo = (total / G) * blockIdx.x + ((total % G) * blockIdx.x) / G;
+    const int64_t c_hi = (total / G) * (blockIdx.x + 1) + ((total % G) * ((int64_t)blockIdx.x + 1)) / G;
+    auto owned = [&](const PlanDesc& D, const Cursor& c) { return D.cost_begin + c.s * D.npl < c_hi; };
+
+    uint64_t best = 0;
+    Cursor cur;
+    bool have = c_lo < c_hi;
+    PlanDesc D;
+    if (have) {
+        int lo = 0, hi = n_desc - 1;  // last descriptor starting at or before c_lo
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (get(mid).cost_begin <= c_lo) lo = mid; else hi = mid - 1;
+        }
+        cur.d = lo;
+        D = get(lo);
+        cur.s = (c_lo - D.cost_begin + D.npl - 1) / D.npl;
+        cur.jb = 0;
+        if (cur.s >= D.steps) {
+            cur.d++;
+            cur.s = 0;
+            have = cur.d < n_desc;
+            if (have) D = get(cur.d);
+        }
+        have = have && owned(D, cur);
+    }
+
+    if (have) {
+        // A ring of NB unit buffers: unit u is loaded NB-1 steps before it is
+        // computed, so every wave keeps NB-1 units of loads in flight.
+        typename Policy::Buf A, B, C;
+        float acc[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) acc[i] = 0.0f;
+        int staged = -1;
+        Cursor cl = cur;  // next unit to load
+        PlanDesc Dl = D;
+        bool have_l = true;
+        auto advance_l = [&]() {
+            Cursor c2 = next_unit(Dl, cl, JB);
+            if (c2.d != cl.d && c2.d < n_desc) Dl = get(c2.d);
+            have_l = c2.d < n_desc && owned(Dl, c2);
+            cl = c2;
+        };
+        Policy::issue(x, Dl, cl, A);
+        advance_l();
+        if (NB == 3 && have_l) {
+            Policy::issue(x, Dl, cl, B);
+            advance_l();
+        }
+
+        // One step: load the next unit into `into` (the buffer computed in the
+        // previous step), compute the unit in `now`, finish the row group when
+        // its last unit is done.  Returns false after the last unit.
+        auto step = [&](typename Policy::Buf& now, typename Policy::Buf& into) -> bool {
+            if (have_l) {
+                Policy::issue(x, Dl, cl, into);
+                advance_l();
+            }
+            if (staged != cur.d) {
+                __syncthreads();
+                stage_x(D.x, D.k >> 5, D.npl * 16, xs);
+                __syncthreads();
+                staged = cur.d;
+            }
+            Policy::compute(x, D, cur, xs, wl, now, acc);
+            if (cur.jb + JB >= D.npl) {  // last unit of this row group
+                const int64_t r0 = x.wave_row0(cur, R) + (x.lane >> 4) * R;
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    const float v = row16_sum(acc[i]);
+                    acc[i] = 0.0f;
+                    if ((x.lane & 15) == 0 && r0 + i < D.n) {
+                        ((g_f32*)D.y)[r0 + i] = v;
+                        if (ARGMAX) {
+                            const uint64_t kk = argmax_key(v, r0 + i);
+                            best = kk > best ? kk : best;
+                        }
                     }
                 }
+            }
+            Cursor c2 = next_unit(D, cur, JB);
+            if (c2.d != cur.d && c2.d < n_desc) D = get(c2.d);
+            const bool more = c2.d < n_desc && owned(D, c2);
+            cur = c2;
+            return more;
+        };
+        if (NB == 3) {
+            for (;;) {
+                if (!step(A, C)) break;
+                if (!step(B, A)) break;
+                if (!step(C, B)) break;
+            }
+        } else {
+            for (;;) {
+                if (!step(A, B)) break;
+                if (!step(B, A)) break;
             }
         }
     }
@@ -195,69 +428,15 @@ __global__ void __launch_bounds__(kThreads) k_argmax_final(const uint64_t* __res
 }
 
 // ---------------------------------------------------------------------------
-// Batch of independent GEMVs in one persistent launch.  Work item = (desc,
-// row step of 16*R rows); item (d, s) "starts" at cost cost_begin[d] + s*npl[d]
-// (npl is proportional to the bytes of one step).  Workgroup g takes every item
-// that starts in [total*g/G, total*(g+1)/G): contiguous, byte-balanced ranges,
-// so consecutive items of one workgroup share the staged activations.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int64_t split_point(int64_t total, int64_t g, int64_t G) {
-    return (total / G) * g + ((total % G) * g) / G;
-}
-
-template <int R, int JB>
-__global__ void __launch_bounds__(kThreads) k_gemv_batch(const PlanDesc* __restrict__ descs,
-                                                         int count, int64_t total) {
-    extern __shared__ u4 xs[];
-    const int64_t G = gridDim.x;
-    const int64_t c_lo = split_point(total, blockIdx.x, G);
-    const int64_t c_hi = split_point(total, (int64_t)blockIdx.x + 1, G);
-    if (c_lo >= c_hi) return;  // whole workgroup leaves together
-
-    int lo = 0, hi = count - 1;  // last descriptor whose range starts at or before c_lo
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (descs[mid].cost_begin <= c_lo) lo = mid; else hi = mid - 1;
-    }
-    int d = lo;
-    int64_t s = (c_lo - descs[d].cost_begin + descs[d].npl - 1) / descs[d].npl;
-    if (s >= descs[d].steps) { ++d; s = 0; }
-
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    int staged = -1;
-    while (d < count) {
-        const PlanDesc D = descs[d];
-        if (D.cost_begin + s * D.npl >= c_hi) break;
-        const int np = D.k / 64;
-        const int npp = D.npl * 16;
-        if (staged != d) {
-            __syncthreads();
-            stage_x(D.x, D.k / 32, npp, xs);
-            __syncthreads();
-            staged = d;
-        }
-        const int64_t row0 = s * (16 * R) + (int64_t)wave * 4 * R;
-        float out[R];
-        rows_dot<R, JB>(D.w, (int64_t)np * kPairBytes, D.n, np, D.npl, xs, npp, row0, out);
-        if ((lane & 15) == 0) {
-            const int64_t rbase = row0 + (lane >> 4) * R;
-#pragma unroll
-            for (int i = 0; i < R; ++i)
-                if (rbase + i < D.n) D.y[rbase + i] = out[i];
-        }
-        if (++s == D.steps) { ++d; s = 0; }
-    }
-}
-
-// ---------------------------------------------------------------------------
 // Generic path: any k % 32 == 0, rows at 2-byte alignment, 1 <= m <= 16.
 // One wave per weight row, lanes stride over blocks, activations from global
 // memory; used for shapes the fast kernels do not take.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 
-__global__ void __launch_bounds__(kThreads) k_gemm_generic(const uint8_t* __restrict__ w,
+constexpr int kGenThreads = 256;  // generic kernel: 4 waves, one row each
+
+__global__ void __launch_bounds__(kGenThreads) k_gemm_generic(const uint8_t* __restrict__ w,
                                                            const uint16_t* __restrict__ x,
                                                            float* __restrict__ y, int m, int64_t n,
                                                            int64_t k) {
@@ -315,44 +494,89 @@ int device_cu_count() {
     return cus;
 }
 
-static size_t x_lds_bytes(int64_t k) {
-    const int64_t np = k / 64;
-    const int64_t npp = (np + 15) & ~int64_t(15);
-    return (size_t)npp * kChunksPerPair * sizeof(u4);
+static int npl_of(int64_t k) { return (int)(((k / 64) + 15) / 16); }
+
+static size_t x_lds_bytes(int64_t k) { return (size_t)npl_of(k) * 16 * kChunksPerPair * sizeof(u4); }
+
+static PlanDesc single_desc(const uint8_t* w, const uint16_t* x, float* y, int64_t n, int64_t k) {
+    PlanDesc d;
+    d.w = w;
+    d.x = x;
+    d.y = y;
+    d.n = n;
+    d.k = (int32_t)k;
+    d.npl = npl_of(k);
+    d.steps = (n + batch_rows_per_step() - 1) / batch_rows_per_step();
+    d.cost_begin = 0;
+    return d;
 }
+
+static int device_lds_per_cu() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 65536;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int b = 0;
+    if (hipDeviceGetAttribute(&b, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess || b <= 0)
+        b = 65536;
+    cache[dev].store(b, std::memory_order_relaxed);
+    return b;
+}
+
+#ifndef Q4_SWEEP_CJB
+#define Q4_SWEEP_CJB 1
+#endif
+constexpr int kCJB = Q4_SWEEP_CJB;  // pairs per lane in a coalesced unit (R * JB even)
+using PairP = PairLoads<kR, kJB>;
+using PairP1 = PairLoads<kR, 1>;  // LM head: the argmax epilogue needs the registers of one pair
+using CoalP = CoalescedLoads<kR, kCJB>;
+
+template <class P, int JB, bool AM>
+static hipError_t launch_sweep(const PlanDesc* descs, int count, const PlanDesc& one, int64_t total,
+                               int64_t max_k, int64_t max_steps, uint64_t* keys, int grid_cap,
+                               int* grid_out, hipStream_t s) {
+    const size_t xsb = x_lds_bytes(max_k);
+    const size_t lds = xsb + kWaves * (size_t)P::kWaveLds;
+    auto kern = k_sweep<P, kR, JB, (P::kCoalesced ? kNBC : kNBP), AM>;
+    if (lds > 65536) {
+        const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    const int per_cu = std::max(1, std::min<int>(kWgPerCu, (int)(device_lds_per_cu() / std::max<size_t>(lds, 1))));
+    int grid = (int)std::max<int64_t>(1, std::min<int64_t>(max_steps, (int64_t)device_cu_count() * per_cu));
+    grid = std::min(grid, grid_cap);
+    if (grid_out) *grid_out = grid;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, s, descs, count, one, total, (int)xsb, keys);
+    return hipGetLastError();
+}
+
+static bool coalesced_ok(int64_t k) { return Q4_SWEEP_COALESCED && k % 1024 == 0; }
 
 hipError_t launch_gemv(const uint8_t* w, const uint16_t* x, float* y, int64_t n, int64_t k,
                        hipStream_t s) {
-    const size_t lds = x_lds_bytes(k);
-    const int cus = device_cu_count();
-    // Small matrices: one row per lane group so more workgroups share the rows.
-    if (n <= (int64_t)cus * 64) {
-        const int64_t steps = (n + 15) / 16;
-        const int grid = (int)std::min<int64_t>(steps, (int64_t)cus * 8);
-        hipLaunchKernelGGL((k_gemv<1, 4, false>), dim3(grid), dim3(kThreads), lds, s, w, x, y, n,
-                           (int)k, nullptr);
-    } else {
-        const int64_t steps = (n + 31) / 32;
-        const int grid = (int)std::min<int64_t>(steps, (int64_t)cus * 4);
-        hipLaunchKernelGGL((k_gemv<2, 4, false>), dim3(grid), dim3(kThreads), lds, s, w, x, y, n,
-                           (int)k, nullptr);
+    const PlanDesc d = single_desc(w, x, y, n, k);
+    const int64_t total = d.steps * d.npl;
+    if constexpr (Q4_SWEEP_COALESCED) {
+        if (coalesced_ok(k))
+            return launch_sweep<CoalP, kCJB, false>(nullptr, 1, d, total, k, d.steps, nullptr, INT32_MAX, nullptr, s);
     }
-    return hipGetLastError();
+    return launch_sweep<PairP, kJB, false>(nullptr, 1, d, total, k, d.steps, nullptr, INT32_MAX, nullptr, s);
 }
 
 int argmax_blocks(int64_t n, int64_t k) {
     (void)k;
-    const int64_t steps = (n + 31) / 32;
+    const int64_t steps = (n + batch_rows_per_step() - 1) / batch_rows_per_step();
     return (int)std::min<int64_t>(steps, kArgmaxMaxBlocks);
 }
 
 hipError_t launch_lm_head(const uint8_t* w, const uint16_t* h, float* logits, int32_t* token,
                           int64_t n, int64_t k, uint64_t* keys, hipStream_t s) {
-    const size_t lds = x_lds_bytes(k);
-    const int grid = std::min(argmax_blocks(n, k), device_cu_count() * 4);
-    hipLaunchKernelGGL((k_gemv<2, 4, true>), dim3(grid), dim3(kThreads), lds, s, w, h, logits, n,
-                       (int)k, keys);
-    hipError_t e = hipGetLastError();
+    const PlanDesc d = single_desc(w, h, logits, n, k);
+    const int64_t total = d.steps * d.npl;
+    int grid = 0;
+    const int cap = argmax_blocks(n, k);
+    hipError_t e = launch_sweep<PairP1, 1, true>(nullptr, 1, d, total, k, d.steps, keys, cap, &grid, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_argmax_final, dim3(1), dim3(kThreads), 0, s, keys, grid, token);
     return hipGetLastError();
@@ -361,18 +585,21 @@ hipError_t launch_lm_head(const uint8_t* w, const uint16_t* h, float* logits, in
 hipError_t launch_gemm_generic(const uint8_t* w, const uint16_t* x, float* y, int64_t m,
                                int64_t n, int64_t k, hipStream_t s) {
     const int64_t grid = (n + 3) / 4;
-    hipLaunchKernelGGL(k_gemm_generic, dim3((unsigned)grid), dim3(kThreads), 0, s, w, x, y, (int)m,
+    hipLaunchKernelGGL(k_gemm_generic, dim3((unsigned)grid), dim3(kGenThreads), 0, s, w, x, y, (int)m,
                        n, k);
     return hipGetLastError();
 }
 
 hipError_t launch_gemv_batch(const PlanDesc* descs, int count, int64_t total_cost, int max_k,
-                             hipStream_t s) {
-    const size_t lds = x_lds_bytes(max_k);
-    const int grid = device_cu_count() * 4;
-    hipLaunchKernelGGL((k_gemv_batch<kBatchR, kBatchJB>), dim3(grid), dim3(kThreads), lds, s,
-                       descs, count, total_cost);
-    return hipGetLastError();
+                             bool all_k1024, hipStream_t s) {
+    PlanDesc none = {};
+    if constexpr (Q4_SWEEP_COALESCED) {
+        if (all_k1024)
+            return launch_sweep<CoalP, kCJB, false>(descs, count, none, total_cost, max_k, INT64_MAX, nullptr,
+                                                    INT32_MAX, nullptr, s);
+    }
+    return launch_sweep<PairP, kJB, false>(descs, count, none, total_cost, max_k, INT64_MAX, nullptr,
+                                           INT32_MAX, nullptr, s);
 }
 
 }  // namespace q4

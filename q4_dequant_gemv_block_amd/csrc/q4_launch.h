@@ -39,6 +39,6 @@ int argmax_blocks(int64_t n, int64_t k);
 hipError_t launch_lm_head(const uint8_t* w, const uint16_t* h, float* logits, int32_t* token,
                           int64_t n, int64_t k, uint64_t* keys, hipStream_t s);
 hipError_t launch_gemv_batch(const PlanDesc* descs, int count, int64_t total_cost, int max_k,
-                             hipStream_t s);
+                             bool all_k1024, hipStream_t s);
 
 }  // namespace q4
