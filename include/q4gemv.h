@@ -97,15 +97,23 @@ Q4_API q4_status q4_0_gemv(const void* w, const void* x, float* y, int64_t n, in
  * The batched pass that verifies speculative drafts and carries 16-token
  * prefill chunks (aipolix.com en-us page, section "Speculation is used to
  * amortize network round trips"; taozi.news, section "技术架构").  Each
- * weight is read from memory once for all M rows.
+ * weight is read from memory and expanded once for all M rows.  For m >= 2
+ * the products run on the matrix cores with (code - 8) * d rounded once to
+ * binary16 (relative error <= 2^-11 per weight); m == 1 is q4_0_gemv.
  *   w : n rows of k/32 Q4_0 blocks
  *   x : m x k binary16, row-major
  *   y : m x n binary32, row-major (written)
- *   1 <= m <= 16, n >= 1, k >= 32, k % 32 == 0.
+ *   1 <= m <= 16, n >= 1, k >= 32, k % 32 == 0.  |d| <= 8188 (so that
+ *   (code - 8) * d is finite in binary16).
+ *   workspace : q4_workspace_bytes(Q4_OP_GEMM_SMALLM, m, n, k) bytes of
+ *               device memory (may be NULL when that is 0); contents on entry
+ *               do not matter.
  * Row m of the result satisfies the same bound as q4_0_gemv on X[m].
+ * Deterministic for a given shape.
  */
 Q4_API q4_status q4_0_gemm_smallm(const void* w, const void* x, float* y,
-                           int64_t m, int64_t n, int64_t k, void* stream);
+                                  int64_t m, int64_t n, int64_t k,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Y[m][n] = sum_k w[n][k] * X[m][k]                   (prefill GEMM, matrix cores)
@@ -117,7 +125,7 @@ Q4_API q4_status q4_0_gemm_smallm(const void* w, const void* x, float* y,
  *   w : n rows of k/32 Q4_0 blocks
  *   x : m x k binary16, row-major
  *   y : m x n binary32, row-major (written)
- *   m >= 1, n >= 1, k >= 32, k % 32 == 0.
+ *   m >= 1, n >= 1, k >= 32, k % 32 == 0.  |d| <= 8188.
  *   workspace : q4_workspace_bytes(Q4_OP_GEMM_PREFILL, m, n, k) bytes of
  *               device memory (may be NULL when that is 0).
  */

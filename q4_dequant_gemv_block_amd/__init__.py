@@ -77,7 +77,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.q4_0_gemv.restype = st
     lib.q4_0_gemv.argtypes = [vp, vp, vp, i64, i64, vp]
     lib.q4_0_gemm_smallm.restype = st
-    lib.q4_0_gemm_smallm.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+    lib.q4_0_gemm_smallm.argtypes = [vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t, vp]
     lib.q4_0_gemm_prefill.restype = st
     lib.q4_0_gemm_prefill.argtypes = [vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t, vp]
     lib.lm_head_argmax.restype = st
@@ -158,7 +158,8 @@ def q4_0_gemv(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
     return out
 
 
-def q4_0_gemm_smallm(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+def q4_0_gemm_smallm(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Y = X W^T for X float16 [M, K] with 1 <= M <= 16; Y float32 [M, N]."""
     if x.dim() != 2:
         raise ValueError("x must be float16 [M, K]")
@@ -168,8 +169,13 @@ def q4_0_gemm_smallm(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None 
         out = torch.empty((m, n), dtype=torch.float32, device=x.device)
     elif out.numel() != m * n:
         raise ValueError("out must hold M*N floats")
+    need = workspace_bytes(Q4_OP_GEMM_SMALLM, m, n, k)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wp = _ptr(workspace, torch.uint8, "workspace") if workspace is not None else None
+    wb = workspace.numel() if workspace is not None else 0
     _check(load_library().q4_0_gemm_smallm(_ptr(w, torch.uint8, "w"), _ptr(x, torch.float16, "x"),
-                                           _ptr(out, torch.float32, "out"), m, n, k, _stream(stream)))
+                                           _ptr(out, torch.float32, "out"), m, n, k, wp, wb, _stream(stream)))
     return out
 
 

@@ -86,12 +86,14 @@ int q4_abi_version(void) { return Q4_ABI_VERSION; }
 const char* q4_last_error(void) { return g_err; }
 
 size_t q4_workspace_bytes(int op, int64_t m, int64_t n, int64_t k) {
-    (void)m;
     switch (op) {
         case Q4_OP_GEMV:
-        case Q4_OP_GEMM_SMALLM:
         case Q4_OP_GEMM_PREFILL:
             return 0;
+        case Q4_OP_GEMM_SMALLM:
+            // only the matrix-core path (2 <= m <= 16, k % 64 == 0) splits K
+            if (m < 2 || m > 16 || n < 1 || k < 64 || k % 64 != 0 || k > kMaxK || n > kMaxN) return 0;
+            return q4::smallm_workspace_bytes(m, n, k);
         case Q4_OP_LM_HEAD_ARGMAX:
             if (n < 1 || k < 32) return 0;
             return (size_t)q4::argmax_blocks(n, k) * sizeof(uint64_t);
@@ -115,13 +117,31 @@ q4_status q4_0_gemv(const void* w, const void* x, float* y, int64_t n, int64_t k
 }
 
 q4_status q4_0_gemm_smallm(const void* w, const void* x, float* y, int64_t m, int64_t n, int64_t k,
-                           void* stream) {
-    q4_status st = check_shape("q4_0_gemm_smallm", m, 16, n, k);
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "q4_0_gemm_smallm";
+    q4_status st = check_shape(fn, m, 16, n, k);
     if (st) return st;
-    st = check_tensors("q4_0_gemm_smallm", w, x, y, m, n, k, (size_t)(m * n) * 4);
+    st = check_tensors(fn, w, x, y, m, n, k, (size_t)(m * n) * 4);
     if (st) return st;
+    const size_t need = q4_workspace_bytes(Q4_OP_GEMM_SMALLM, m, n, k);
+    if (need) {
+        if (!workspace || workspace_bytes < need) return fail(Q4_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
+        if (!aligned(workspace, 16)) return fail(Q4_ERR_MISALIGNED, "%s: workspace must be 16-byte aligned", fn);
+        const Range rws = range(workspace, need);
+        if (overlap(rws, range(w, (size_t)(n * row_bytes(k)))) || overlap(rws, range(x, (size_t)(m * k * 2))) ||
+            overlap(rws, range(y, (size_t)(m * n) * 4)))
+            return fail(Q4_ERR_INVALID_ARG, "%s: workspace overlaps a tensor", fn);
+    }
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t e = q4::launch_gemm_generic(static_cast<const uint8_t*>(w), static_cast<const uint16_t*>(x), y, m, n, k, s);
+    const uint8_t* wb = static_cast<const uint8_t*>(w);
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    hipError_t e;
+    if (!fast_path(w, k))
+        e = q4::launch_gemm_generic(wb, xb, y, m, n, k, s);
+    else if (m == 1)
+        e = q4::launch_gemv(wb, xb, y, n, k, s);
+    else
+        e = q4::launch_gemm_smallm(wb, xb, y, m, n, k, static_cast<float*>(workspace), s);
     return hip_status(e, "q4_0_gemm_smallm launch");
 }
 
@@ -137,6 +157,8 @@ q4_status q4_0_gemm_prefill(const void* w, const void* x, float* y, int64_t m, i
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const uint8_t* wb = static_cast<const uint8_t*>(w);
     const uint16_t* xb = static_cast<const uint16_t*>(x);
+    if (k % 64 == 0 && aligned(w, 4) && m <= (int64_t(1) << 30) && n <= (int64_t(1) << 30))
+        return hip_status(q4::launch_gemm_prefill(wb, xb, y, m, n, k, s), "q4_0_gemm_prefill launch");
     for (int64_t m0 = 0; m0 < m; m0 += 16) {
         const int64_t mm = std::min<int64_t>(16, m - m0);
         const hipError_t e = q4::launch_gemm_generic(wb, xb + m0 * k, y + m0 * n, mm, n, k, s);

@@ -35,6 +35,12 @@ hipError_t launch_gemv(const uint8_t* w, const uint16_t* x, float* y, int64_t n,
                        hipStream_t s);
 hipError_t launch_gemm_generic(const uint8_t* w, const uint16_t* x, float* y, int64_t m,
                                int64_t n, int64_t k, hipStream_t s);
+void smallm_split(int64_t n, int64_t k, int* splits, int* cps);
+size_t smallm_workspace_bytes(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemm_smallm(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
+                              int64_t k, float* workspace, hipStream_t s);
+hipError_t launch_gemm_prefill(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
+                               int64_t k, hipStream_t s);
 int argmax_blocks(int64_t n, int64_t k);
 hipError_t launch_lm_head(const uint8_t* w, const uint16_t* h, float* logits, int32_t* token,
                           int64_t n, int64_t k, uint64_t* keys, hipStream_t s);

@@ -51,7 +51,8 @@ def test_abi_version(lib):
 
 def test_workspace_bytes(lib):
     assert lib.q4_workspace_bytes(q4.Q4_OP_GEMV, 1, 5120, 5120) == 0
-    assert lib.q4_workspace_bytes(q4.Q4_OP_GEMM_SMALLM, 16, 5120, 5120) == 0
+    assert lib.q4_workspace_bytes(q4.Q4_OP_GEMM_SMALLM, 1, 5120, 5120) == 0
+    assert lib.q4_workspace_bytes(q4.Q4_OP_GEMM_SMALLM, 16, 5120, 5120) > 0
     ws = lib.q4_workspace_bytes(q4.Q4_OP_LM_HEAD_ARGMAX, 1, 151936, 5120)
     assert ws >= 8 and ws % 8 == 0
     assert lib.q4_workspace_bytes(99, 1, 1, 32) == 0
@@ -76,9 +77,16 @@ def test_gemv_validation(lib, args, code):
 
 
 def test_smallm_validation(lib):
-    assert lib.q4_0_gemm_smallm(FAKE, FAKE * 2, FAKE * 8, 17, 8, 64, None) == q4.Q4_ERR_INVALID_ARG
-    assert lib.q4_0_gemm_smallm(FAKE, FAKE * 2, FAKE * 8, 0, 8, 64, None) == q4.Q4_ERR_INVALID_ARG
-    assert b"m = 17" in lib.q4_last_error() or b"m = 0" in lib.q4_last_error()
+    assert lib.q4_0_gemm_smallm(FAKE, FAKE * 2, FAKE * 8, 17, 8, 64, None, 0, None) == q4.Q4_ERR_INVALID_ARG
+    assert b"m = 17" in lib.q4_last_error()
+    assert lib.q4_0_gemm_smallm(FAKE, FAKE * 2, FAKE * 8, 0, 8, 64, None, 0, None) == q4.Q4_ERR_INVALID_ARG
+    need = lib.q4_workspace_bytes(q4.Q4_OP_GEMM_SMALLM, 16, 5120, 5120)
+    assert need > 0 and need % 4 == 0
+    w, x, y = FAKE * 64, FAKE * 4096, FAKE * 8192
+    assert lib.q4_0_gemm_smallm(w, x, y, 16, 5120, 5120, None, 0, None) == q4.Q4_ERR_WORKSPACE
+    assert lib.q4_0_gemm_smallm(w, x, y, 16, 5120, 5120, FAKE * 16384, need - 4, None) == q4.Q4_ERR_WORKSPACE
+    # workspace overlapping the output
+    assert lib.q4_0_gemm_smallm(w, x, y, 16, 5120, 5120, y + 64, need, None) == q4.Q4_ERR_INVALID_ARG
 
 
 def test_prefill_validation(lib):
