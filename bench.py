@@ -50,16 +50,17 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def counter_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, or None when
-    there are none or the kernel sources changed since they were taken."""
+def counter_traffic(workload: str):
+    """HBM bytes per launch of the workload's dominant kernel from committed
+    rocprofv3 counter runs (profiles/traffic.json), or None when there are none
+    or the kernel sources changed since they were taken."""
     path = os.path.join(PROFILE_DIR, "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         table = json.load(f)
     e = table.get(workload)
-    if not e or e.get("kernel") != kernel or e.get("source_hash") != kernel_source_hash():
+    if not e or e.get("source_hash") != kernel_source_hash():
         return None
     return e.get("bytes_per_launch")
 
@@ -175,7 +176,7 @@ def bench_sweep(args):
         "implied_tok_s": round(1000.0 / (ms + lm_ms), 2),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4),
-                     "traffic": counter_traffic("k_sweep", "sweep"),
+                     "traffic": counter_traffic("sweep"),
                      "kernel": "q4::k_sweep<PairLoads<2,2>> (batch)", "launches_per_step": 1},
     }
     if not args.no_cpu_baseline:
@@ -210,7 +211,7 @@ def bench_gemv(args):
             "data": "synthetic", "config": {"workload": "single Q4_0 GEMV 5120x5120, 48 rotating weight copies"},
             "hot_cache_GBps": round(bytes_ / (hot_ms * 1e-3) / 1e9, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counter_traffic("k_sweep", "gemv"),
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counter_traffic("gemv"),
                          "kernel": "q4::k_sweep<PairLoads<2,2>>"}}
 
 
@@ -232,7 +233,7 @@ def bench_lmhead(args):
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16->f32",
             "data": "synthetic", "config": {"workload": "LM head 151936x5120 + argmax"},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counter_traffic("k_sweep", "lmhead"),
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counter_traffic("lmhead"),
                          "kernel": "q4::k_sweep<PairLoads<2,1>,ARGMAX> + q4::k_argmax_final"}}
 
 
@@ -270,7 +271,7 @@ def bench_gemm(args, prefill: bool):
            "frac": round(tf / PEAK_F16_TFLOPS, 4)} if prefill else
           {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
            "frac": round(gbs / PEAK_HBM_GBS, 4)})
-    rl["traffic"] = counter_traffic(name, name)
+    rl["traffic"] = counter_traffic("prefill_m%d" % m if prefill else "smallm_m%d" % m)
     return {"metric": "%s Q4_0 GEMM over the 64-layer sweep (M=%d)" % (name, m),
             "value": round(tf if prefill else gbs, 3), "unit": "TFLOP/s" if prefill else "GB/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -279,15 +280,70 @@ def bench_gemm(args, prefill: bool):
             "tflops": round(tf, 3), "GBps": round(gbs, 2), "eager_ms_per_step": round(eager_ms, 4), "roofline": rl}
 
 
+COPY_BYTES = 1 << 30
+
+
+def bench_copy(args):
+    """A plain device-to-device copy of 1 GiB: the known-size kernel that
+    calibrates the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    ms = time_steps(lambda: b.copy_(a), args.steps, args.warmup)
+    return {"metric": "device copy GB/s (counter calibration)", "value": round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 2),
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "copy of %d bytes" % COPY_BYTES}}
+
+
+def _counter_mean(csv_path: str, kernel_substr: str, counter: str) -> float:
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+            if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    if not vals:
+        raise SystemExit("no %s samples for kernels matching %r in %s" % (counter, kernel_substr, csv_path))
+    return sum(vals) / len(vals)
+
+
+def record_traffic(workload: str, kernel: str, fetch_csv: str, write_csv: str, copy_fetch_csv: str,
+                   copy_write_csv: str) -> dict:
+    """HBM bytes per launch of `kernel` from rocprofv3 FETCH_SIZE and WRITE_SIZE
+    runs (KiB per dispatch), each scaled by what the same counter reads for the
+    1 GiB copy, written into profiles/traffic.json under `workload`."""
+    copy_kernel = "copy"
+    f_copy = _counter_mean(copy_fetch_csv, copy_kernel, "FETCH_SIZE")
+    w_copy = _counter_mean(copy_write_csv, copy_kernel, "WRITE_SIZE")
+    f_scale = COPY_BYTES / (f_copy * 1024.0)
+    w_scale = COPY_BYTES / (w_copy * 1024.0)
+    fetch = _counter_mean(fetch_csv, kernel, "FETCH_SIZE") * 1024.0 * f_scale
+    write = _counter_mean(write_csv, kernel, "WRITE_SIZE") * 1024.0 * w_scale
+    path = os.path.join(PROFILE_DIR, "traffic.json")
+    table = json.load(open(path)) if os.path.exists(path) else {}
+    table[workload] = {"kernel": kernel, "source_hash": kernel_source_hash(),
+                       "bytes_per_launch": int(round(fetch + write)),
+                       "fetch_bytes": int(round(fetch)), "write_bytes": int(round(write)),
+                       "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}
+    os.makedirs(PROFILE_DIR, exist_ok=True)
+    with open(path, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+    return table[workload]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="sweep", choices=["sweep", "gemv", "lmhead", "smallm", "prefill"])
+    ap.add_argument("--workload", default="sweep", choices=["sweep", "gemv", "lmhead", "smallm", "prefill", "copy"])
     ap.add_argument("--m", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--record-traffic", nargs=6, metavar=("WORKLOAD", "KERNEL", "FETCH_CSV", "WRITE_CSV",
+                                                          "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write profiles/traffic.json from rocprofv3 counter CSVs and exit (no GPU needed)")
     args = ap.parse_args()
+    if args.record_traffic:
+        print(json.dumps(record_traffic(*args.record_traffic)))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
@@ -295,7 +351,7 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    fn = {"sweep": bench_sweep, "gemv": bench_gemv, "lmhead": bench_lmhead,
+    fn = {"sweep": bench_sweep, "gemv": bench_gemv, "lmhead": bench_lmhead, "copy": bench_copy,
           "smallm": lambda a: bench_gemm(a, False), "prefill": lambda a: bench_gemm(a, True)}[args.workload]
     out = fn(args)
     print(json.dumps(out), flush=True)

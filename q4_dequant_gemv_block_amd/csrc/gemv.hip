@@ -551,7 +551,7 @@ static hipError_t launch_sweep(const PlanDesc* descs, int count, const PlanDesc&
     return hipGetLastError();
 }
 
-static bool coalesced_ok(int64_t k) { return Q4_SWEEP_COALESCED && k % 1024 == 0; }
+[[maybe_unused]] static bool coalesced_ok(int64_t k) { return Q4_SWEEP_COALESCED && k % 1024 == 0; }
 
 hipError_t launch_gemv(const uint8_t* w, const uint16_t* x, float* y, int64_t n, int64_t k,
                        hipStream_t s) {
