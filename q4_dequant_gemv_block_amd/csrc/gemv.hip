@@ -11,26 +11,29 @@
 //    l, l+16, l+32, ... so the 16 lanes of a row read 576 contiguous bytes per
 //    step.  Each lane group carries R consecutive rows at the same pair
 //    positions, so one read of the activation chunks from LDS serves R rows.
-//  * Weights are read with global dwordx4/dword loads (36-byte pairs at
-//    4-byte alignment); 4-bit codes become exact (code - 8) f16 pairs
-//    with one v_and_or_b32 and one v_pk_add_f16 per pair and meet the
-//    activations in v_dot2_f32_f16; the block scale is applied once per block
-//    in f32 (v_fma_mix).
+//  * Weights are read with cached global dwordx4/dword loads (36-byte pairs
+//    at 4-byte alignment).  The unit's base address is uniform (scalar
+//    registers) and every lane adds a fixed 32-bit offset, so issuing loads
+//    costs one multiply-add per row and no 64-bit vector arithmetic.
+//  * 4-bit codes become exact (code - 8) f16 pairs with one v_and_or_b32 and
+//    one v_pk_add_f16 per pair and meet the activations in v_dot2_f32_f16; the
+//    block scale is applied once per block in f32 (v_fma_mix).
 //  * The activation vector is staged once per workgroup and GEMV into LDS in
-//    the chunk order of q4_device.h (conflict-free for the 16-lane reads).
-//  * Every wave walks a sequence of units (a group of 4R rows x JB pairs per
-//    lane) and issues the loads of the next unit before computing the current
-//    one, also across row groups and GEMV boundaries, so the memory pipe never
-//    drains inside a workgroup's range.
-//  * Out-of-range rows and pairs load from clamped in-range addresses instead
-//    of branching: padding pairs meet zero activation chunks and add exactly
-//    0, padding rows are never stored.
+//    the chunk order of q4_device.h, at a fixed chunk stride so every LDS read
+//    is one base register plus an immediate offset.
+//  * Every wave walks a sequence of units (4R rows x JB pairs per lane) and
+//    issues the loads of the next unit before computing the current one, also
+//    across row groups and GEMV boundaries.
+//  * Units at the end of a matrix (rows past N, or K not a multiple of 1024)
+//    load from clamped in-range addresses instead of branching per lane:
+//    padding pairs meet zero activation chunks and add exactly 0, padding
+//    rows are never stored.
 //  * The row sum is a fixed-order DPP tree inside the 16-lane row, so results
 //    are deterministic and independent of where a row sits.
 //
-// Work split: a work item is (GEMV d, row step s of 16R rows); it starts at
-// cost cost_begin[d] + s * npl[d], npl (pairs per lane) being proportional to
-// its bytes.  Workgroup g takes every item starting in [T*g/G, T*(g+1)/G):
+// Work split: a work item is (GEMV d, row step s); it starts at cost
+// cost_begin[d] + s * npl[d], npl (pairs per lane) being proportional to its
+// bytes.  Workgroup g takes every item starting in [T*g/G, T*(g+1)/G):
 // contiguous, byte-balanced ranges, so a workgroup stages few activation
 // vectors.  The single-GEMV and LM-head entry points run the same kernel on a
 // one-descriptor list passed by value.
@@ -39,6 +42,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 namespace q4 {
 
@@ -47,7 +51,7 @@ namespace q4 {
 #define Q4_SWEEP_R 2
 #endif
 #ifndef Q4_SWEEP_JB
-#define Q4_SWEEP_JB 2
+#define Q4_SWEEP_JB 1
 #endif
 #ifndef Q4_SWEEP_WG_PER_CU
 #define Q4_SWEEP_WG_PER_CU 2
@@ -58,35 +62,30 @@ namespace q4 {
 #ifndef Q4_SWEEP_WPE
 #define Q4_SWEEP_WPE 4
 #endif
-#ifndef Q4_SWEEP_COALESCED
-#define Q4_SWEEP_COALESCED 0
-#endif
-#ifndef Q4_SWEEP_NB_PAIR
-#define Q4_SWEEP_NB_PAIR 2
-#endif
-#ifndef Q4_SWEEP_NB_COAL
-#define Q4_SWEEP_NB_COAL 2
+#ifndef Q4_SWEEP_NB
+#define Q4_SWEEP_NB 2
 #endif
 
 constexpr int kThreads = Q4_SWEEP_THREADS;  // the waves of a workgroup share one staged activation vector
-constexpr int kWavesPerEu = Q4_SWEEP_WPE;   // register budget: waves per SIMD the sweep kernel must fit
 constexpr int kWaves = kThreads / 64;
-constexpr int kR = Q4_SWEEP_R;         // rows per 16-lane group
-constexpr int kJB = Q4_SWEEP_JB;       // pairs per lane per unit
+constexpr int kWavesPerEu = Q4_SWEEP_WPE;   // register budget: waves per SIMD the sweep kernel must fit
+constexpr int kR = Q4_SWEEP_R;              // rows per 16-lane group
+constexpr int kJB = Q4_SWEEP_JB;            // pairs per lane per unit
+constexpr int kNB = Q4_SWEEP_NB;            // unit buffers in the prefetch ring (2 or 3)
 constexpr int kWgPerCu = Q4_SWEEP_WG_PER_CU;
-constexpr int kNBP = Q4_SWEEP_NB_PAIR;  // unit buffers in the ring, per-lane pair loads
-constexpr int kNBC = Q4_SWEEP_NB_COAL;  // unit buffers in the ring, coalesced loads
+constexpr int kRowsPerStep = kWaves * 4 * kR;
+constexpr int kXStride = 288;               // activation chunk stride in pairs: k <= 18432 (36 KiB of LDS)
 
-int batch_rows_per_step() { return kWaves * 4 * kR; }
+int batch_rows_per_step() { return kRowsPerStep; }
 
 typedef __attribute__((address_space(1))) float g_f32;
 
 // ---------------------------------------------------------------------------
 // Activation staging: the 8 chunks of every block pair, chunk c of pair p at
-// xs[c * npp + p]; pairs >= k/64 (padding up to npp) are zero.
+// xs[c * stride + p]; pairs >= k/64 up to npl*16 are zero.
 // ---------------------------------------------------------------------------
 template <int HALF>
-__device__ __forceinline__ void stage_block(const uint32_t (&v)[16], int p, int npp, u4* __restrict__ xs) {
+__device__ __forceinline__ void stage_block(const uint32_t (&v)[16], int p, int stride, u4* __restrict__ xs) {
     auto xe = [&](int j) -> uint32_t { return (v[j >> 1] >> (16 * (j & 1))) & 0xFFFFu; };
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
@@ -99,12 +98,13 @@ __device__ __forceinline__ void stage_block(const uint32_t (&v)[16], int p, int 
         ent.y = xe(a + 16) | (xe(c + 16) << 16);
         ent.z = xe(b) | (xe(e) << 16);
         ent.w = xe(b + 16) | (xe(e + 16) << 16);
-        xs[(4 * HALF + cc) * npp + p] = ent;
+        xs[(4 * HALF + cc) * stride + p] = ent;
     }
 }
 
-__device__ void stage_x(const uint16_t* __restrict__ x, int nblocks, int npp, u4* __restrict__ xs) {
-    const int nb_pad = 2 * npp;
+__device__ void stage_x(const uint16_t* __restrict__ x, int nblocks, int npairs_pad, int stride,
+                        u4* __restrict__ xs) {
+    const int nb_pad = 2 * npairs_pad;
     for (int b = threadIdx.x; b < nb_pad; b += blockDim.x) {
         uint32_t v[16];  // the 32 f16 values of block b, two per dword
         if (b < nblocks) {
@@ -119,9 +119,9 @@ __device__ void stage_x(const uint16_t* __restrict__ x, int nblocks, int npp, u4
             for (int i = 0; i < 16; ++i) v[i] = 0u;
         }
         if (b & 1)
-            stage_block<1>(v, b >> 1, npp, xs);
+            stage_block<1>(v, b >> 1, stride, xs);
         else
-            stage_block<0>(v, b >> 1, npp, xs);
+            stage_block<0>(v, b >> 1, stride, xs);
     }
 }
 
@@ -150,135 +150,238 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* sh) {
 // The GEMV engine.  A wave's unit is 4R consecutive rows x JB pairs per lane
 // (pairs [16*jb, 16*(jb+JB)) of each row); lane group q = lane / 16 owns rows
 // q*R .. q*R+R-1 of the unit, lane l = lane % 16 owns pairs l + 16*(jb+t).
-// Two ways to bring a unit's bytes in (the "policies"):
-//   PairLoads:      every lane loads its own 36-byte pairs (any k % 64 == 0).
-//   CoalescedLoads: the wave loads the unit's rows as consecutive 16-byte
-//                   pieces (fully coalesced, non-temporal), parks them in a
-//                   wave-private LDS window and every lane reads its pairs
-//                   back; needs k % 1024 == 0 so each row is whole 16-pair
-//                   segments.  Measured on a load-only copy: 6.85 TB/s for
-//                   this pattern against 6.2 TB/s for per-lane pair loads.
 // ---------------------------------------------------------------------------
+// A wave-uniform 64-bit value moved to scalar registers (64-bit divisions run
+// on the vector unit, and a uniform value left in vector registers costs
+// registers and, when spilled, a scratch reload that waits on every load).
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 struct Cursor {
     int d;       // descriptor
     int64_t s;   // row step within the descriptor
     int jb;      // first pair-per-lane index of the unit
 };
 
-struct Ctx {
-    int wave, lane;
-    __device__ __forceinline__ int64_t wave_row0(const Cursor& c, int R) const {
-        return c.s * (kWaves * 4 * R) + (int64_t)wave * 4 * R;
-    }
-};
-
-template <int R, int JB>
-struct PairLoads {
+template <int R, int JB, int XS>
+struct Engine {
+    static constexpr int kR = R;
+    static constexpr int kJB = JB;
+    static constexpr int kWaveLds = 0;
     struct Buf {
         uint32_t d[JB][R][9];
     };
-    static constexpr int kWaveLds = 0;
-    static constexpr bool kCoalesced = false;
+    int lane, l16;
+    uint32_t rr0;  // row of this lane's first row within a step (its R rows are rr0 .. rr0+R-1)
+    uint32_t l36;  // this lane's byte offset within a 16-pair segment
 
-    __device__ __forceinline__ static void issue(const Ctx& x, const PlanDesc& D, const Cursor& c, Buf& b) {
+    __device__ __forceinline__ void init(uint8_t* wl) {
+        (void)wl;
+        lane = threadIdx.x & 63;
+        l16 = lane & 15;
+        const int wave = threadIdx.x >> 6;
+        rr0 = (uint32_t)(wave * 4 * R + (lane >> 4) * R);
+        l36 = (uint32_t)(l16 * kPairBytes);
+    }
+
+    __device__ __forceinline__ void issue(const PlanDesc& D, const Cursor& c, Buf& b) const {
         const int np = D.k >> 6;
-        const int64_t rb = (int64_t)np * kPairBytes;
-        const int64_t r0 = x.wave_row0(c, R) + (x.lane >> 4) * R;
-        const int l = x.lane & 15;
+        const uint32_t rb = (uint32_t)np * kPairBytes;
+        const int64_t row0 = c.s * (int64_t)(kWaves * 4 * R);
+        const bool interior = row0 + kWaves * 4 * R <= D.n && (np & 15) == 0;  // uniform
+        if (interior) {
+            const uint8_t* base = D.w + row0 * rb + (int64_t)c.jb * (16 * kPairBytes);
 #pragma unroll
-        for (int t = 0; t < JB; ++t) {
-            const int j = c.jb + t;
-            if (j < D.npl) {  // uniform
-                const int p = min(l + 16 * j, np - 1);
+            for (int t = 0; t < JB; ++t) {
+                if (c.jb + t < D.npl) {  // uniform
 #pragma unroll
-                for (int i = 0; i < R; ++i) {
-                    const int64_t r = min(r0 + i, D.n - 1);
-                    load_pair(D.w + r * rb + (int64_t)p * kPairBytes, b.d[t][i]);
+                    for (int i = 0; i < R; ++i)
+                        load_pair(base + ((rr0 + i) * rb + l36 + (uint32_t)t * (16 * kPairBytes)), b.d[t][i]);
+                }
+            }
+        } else {
+            // rows and pairs fit 31 bits (the boundary checks n and k)
+            const int last_row = (int)(D.n - 1);
+            const int r0 = (int)row0 + (int)rr0;
+#pragma unroll
+            for (int t = 0; t < JB; ++t) {
+                const int j = c.jb + t;
+                if (j < D.npl) {
+                    const uint32_t p = (uint32_t)min(l16 + 16 * j, np - 1);
+#pragma unroll
+                    for (int i = 0; i < R; ++i) {
+                        const uint32_t r = (uint32_t)min(r0 + i, last_row);
+                        load_pair(D.w + (uint64_t)r * rb + p * kPairBytes, b.d[t][i]);
+                    }
                 }
             }
         }
     }
 
-    __device__ __forceinline__ static void compute(const Ctx& x, const PlanDesc& D, const Cursor& c,
-                                                   const u4* __restrict__ xs, uint8_t* __restrict__ wl,
-                                                   const Buf& b, float (&acc)[R]) {
-        (void)wl;
-        const int npp = D.npl * 16;
-        const int l = x.lane & 15;
+    __device__ __forceinline__ void compute(const PlanDesc& D, const Cursor& c, const u4* __restrict__ xs,
+                                            const Buf& b, float (&acc)[R]) const {
+        const int stride = XS > 0 ? XS : D.npl * 16;
+        const u4* xb = xs + (l16 + 16 * c.jb);
 #pragma unroll
         for (int t = 0; t < JB; ++t) {
-            const int j = c.jb + t;
-            if (j < D.npl) {
-                const int p = l + 16 * j;
-                u4 X[8];
+            if (c.jb + t < D.npl) {
+                // chunk-outer, row-inner: one activation chunk is live at a time
+                float s0[R], s1[R];
 #pragma unroll
-                for (int ch = 0; ch < 8; ++ch) X[ch] = xs[ch * npp + p];
+                for (int i = 0; i < R; ++i) s0[i] = s1[i] = 0.0f;
 #pragma unroll
-                for (int i = 0; i < R; ++i) acc[i] = pair_dot(b.d[t][i], X, acc[i]);
+                for (int ch = 0; ch < 8; ++ch) {
+                    const u4 X = xb[ch * stride + 16 * t];
+#pragma unroll
+                    for (int i = 0; i < R; ++i) {
+                        const uint32_t* Dw = b.d[t][i];
+                        const uint32_t code = ch == 0 ? realign_block0(Dw[0], Dw[4]) : Dw[ch < 4 ? ch : ch + 1];
+                        if (ch < 4)
+                            s0[i] = dot_chunk(expand(code), X, s0[i]);
+                        else
+                            s1[i] = dot_chunk(expand(code), X, s1[i]);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    acc[i] = __builtin_fmaf(f16_lo(b.d[t][i][0]), s0[i], acc[i]);
+                    acc[i] = __builtin_fmaf(f16_hi(b.d[t][i][4]), s1[i], acc[i]);
+                }
             }
         }
     }
 };
 
-template <int R, int JB>
-struct CoalescedLoads {
-    static constexpr int kSegBytes = 576 * JB;          // one row's part of a unit
-    static constexpr int kSegStride = kSegBytes + 32;   // padding staggers LDS banks between lane groups
-    static constexpr int kPieces = 36 * JB * 4 * R;     // 16-byte pieces per unit
-    static_assert(kPieces % 32 == 0, "R*JB must be even");
-    static constexpr int kPerLane = (kPieces + 63) / 64;  // the last slot may cover half the lanes
+// The same units loaded as fully coalesced 16-byte pieces with the
+// non-temporal hint (each 128-byte line is requested once), parked in a
+// wave-private LDS window and read back as 36-byte pairs.  On a load-only
+// copy this access pattern streams at 6.6-6.8 TB/s against about 6.15 TB/s
+// for per-lane pair loads (which cannot take the non-temporal hint: their
+// lines are touched by three instructions and would be refetched).
+template <int R, int JB, int XS>
+struct CoalEngine {
+    static constexpr int kR = R;
+    static constexpr int kJB = JB;
+    static constexpr int kSegBytes = 16 * kPairBytes * JB;  // one row's part of a unit
+    static constexpr int kSegStride = kSegBytes + 32;        // padding staggers LDS banks between rows
+    static constexpr int kPieces = kSegBytes / 16 * 4 * R;   // 16-byte pieces per wave unit
+    static_assert(kPieces % 32 == 0, "R * JB must be even");
+    static constexpr int kPerLane = (kPieces + 63) / 64;     // the last slot may cover half the lanes
     static constexpr int kWaveLds = 4 * R * kSegStride;
-    static constexpr bool kCoalesced = true;
     struct Buf {
         u4 v[kPerLane];
     };
+    int lane, l16;
+    uint32_t rr0;           // row of this lane's first row within a step
+    uint32_t wrow0;         // first row of this wave within a step (wave-uniform)
+    uint8_t* wl;            // this wave's LDS window
+    uint32_t pg[kPerLane];  // row (0 .. 4R-1) of each of this lane's pieces
+    uint32_t po[kPerLane];  // byte offset of each piece within its row's segment
 
-    __device__ __forceinline__ static void issue(const Ctx& x, const PlanDesc& D, const Cursor& c, Buf& b) {
-        const int64_t rb = (int64_t)(D.k >> 6) * kPairBytes;  // a multiple of 576
-        const int64_t r0 = x.wave_row0(c, R);
+    __device__ __forceinline__ void init(uint8_t* window) {
+        lane = threadIdx.x & 63;
+        l16 = lane & 15;
+        const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+        wrow0 = (uint32_t)(wave * 4 * R);
+        rr0 = wrow0 + (uint32_t)((lane >> 4) * R);
+        wl = window;
 #pragma unroll
         for (int k = 0; k < kPerLane; ++k) {
-            const int P = 64 * k + x.lane;
-            const int g = P / (36 * JB);
-            const int rem = P - g * (36 * JB);
-            const int t = rem / 36;
-            const int64_t r = min(r0 + g, D.n - 1);
-            const int64_t off = r * rb + 576 * (int64_t)c.jb + 16 * rem;
-            // pieces of a pair index past the row (only in a row's last unit) are not loaded
-            if (P < kPieces && c.jb + t < D.npl) b.v[k] = __builtin_nontemporal_load((g_u4*)(D.w + off));
+            const int P = 64 * k + lane;
+            const int g = P / (kSegBytes / 16);
+            pg[k] = (uint32_t)g;
+            po[k] = (uint32_t)(16 * (P - g * (kSegBytes / 16)));
         }
     }
 
-    __device__ __forceinline__ static void compute(const Ctx& x, const PlanDesc& D, const Cursor& c,
-                                                   const u4* __restrict__ xs, uint8_t* __restrict__ wl,
-                                                   const Buf& b, float (&acc)[R]) {
+    __device__ __forceinline__ bool valid_piece(int k) const { return 64 * k + lane < kPieces; }
+
+    __device__ __forceinline__ void issue(const PlanDesc& D, const Cursor& c, Buf& b) const {
+        const int np = D.k >> 6;
+        const uint32_t rb = (uint32_t)np * kPairBytes;
+        const int64_t row0 = c.s * (int64_t)(kWaves * 4 * R);
+        const bool interior = row0 + kWaves * 4 * R <= D.n && (np & 15) == 0;  // uniform
+        const int64_t seg0 = (int64_t)c.jb * (16 * kPairBytes);
+        if (interior) {
+            const uint8_t* base = D.w + (row0 + wrow0) * rb + seg0;
 #pragma unroll
-        for (int k = 0; k < kPerLane; ++k) {
-            const int P = 64 * k + x.lane;
-            const int g = P / (36 * JB);
-            if (P < kPieces) *(u4*)(wl + g * kSegStride + 16 * (P - g * 36 * JB)) = b.v[k];
+            for (int k = 0; k < kPerLane; ++k) {
+                const int t = (int)(po[k] / (16 * kPairBytes));
+                if (valid_piece(k) && c.jb + t < D.npl)
+                    b.v[k] = __builtin_nontemporal_load((g_u4*)(base + (pg[k] * rb + po[k])));
+            }
+        } else {
+            // Rows past N read the last row (never stored).  With k % 1024 != 0 a
+            // segment runs past the row end: load dword by dword (a row is a
+            // multiple of 4 bytes, so no dword straddles its end) and leave the
+            // dwords past it zero; their pairs get zero scales in compute().
+            const int last_row = (int)(D.n - 1);
+#pragma unroll
+            for (int k = 0; k < kPerLane; ++k) {
+                const int t = (int)(po[k] / (16 * kPairBytes));
+                if (valid_piece(k) && c.jb + t < D.npl) {
+                    const uint32_t r = (uint32_t)min((int)(row0 + wrow0 + pg[k]), last_row);
+                    const uint32_t off = (uint32_t)seg0 + po[k];
+                    const uint8_t* row = D.w + (uint64_t)r * rb;
+                    uint32_t dw[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        dw[e] = off + 4u * e < rb ? *(g_u32*)(row + off + 4u * e) : 0u;
+                    b.v[k] = u4{dw[0], dw[1], dw[2], dw[3]};
+                }
+            }
         }
+    }
+
+    __device__ __forceinline__ void compute(const PlanDesc& D, const Cursor& c, const u4* __restrict__ xs,
+                                            const Buf& b, float (&acc)[R]) const {
+#pragma unroll
+        for (int k = 0; k < kPerLane; ++k)
+            if (valid_piece(k)) *(u4*)(wl + pg[k] * kSegStride + po[k]) = b.v[k];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int npp = D.npl * 16;
-        const int l = x.lane & 15;
-        const int q = x.lane >> 4;
+        const int stride = XS > 0 ? XS : D.npl * 16;
+        const u4* xb = xs + (l16 + 16 * c.jb);
+        const uint8_t* mine = wl + (lane >> 4) * R * kSegStride + l16 * kPairBytes;
+        const int np = D.k >> 6;
 #pragma unroll
         for (int t = 0; t < JB; ++t) {
-            const int j = c.jb + t;
-            if (j < D.npl) {
-                const int p = l + 16 * j;
-                u4 X[8];
-#pragma unroll
-                for (int ch = 0; ch < 8; ++ch) X[ch] = xs[ch * npp + p];
+            if (c.jb + t < D.npl) {
+                uint32_t Dw[R][9];
 #pragma unroll
                 for (int i = 0; i < R; ++i) {
-                    const uint32_t* src = (const uint32_t*)(wl + (q * R + i) * kSegStride + 576 * t + kPairBytes * l);
-                    uint32_t Dw[9];
+                    const uint32_t* src = (const uint32_t*)(mine + i * kSegStride + t * 16 * kPairBytes);
 #pragma unroll
-                    for (int e = 0; e < 9; ++e) Dw[e] = src[e];
-                    acc[i] = pair_dot(Dw, X, acc[i]);
+                    for (int e = 0; e < 9; ++e) Dw[i][e] = src[e];
+                    // a pair past the row end (k % 1024 != 0) holds other bytes: zero its scales
+                    if (l16 + 16 * (c.jb + t) >= np) {
+                        Dw[i][0] &= 0xFFFF0000u;
+                        Dw[i][4] &= 0x0000FFFFu;
+                    }
+                }
+                float s0[R], s1[R];
+#pragma unroll
+                for (int i = 0; i < R; ++i) s0[i] = s1[i] = 0.0f;
+#pragma unroll
+                for (int ch = 0; ch < 8; ++ch) {
+                    const u4 X = xb[ch * stride + 16 * t];
+#pragma unroll
+                    for (int i = 0; i < R; ++i) {
+                        const uint32_t code = ch == 0 ? realign_block0(Dw[i][0], Dw[i][4]) : Dw[i][ch < 4 ? ch : ch + 1];
+                        if (ch < 4)
+                            s0[i] = dot_chunk(expand(code), X, s0[i]);
+                        else
+                            s1[i] = dot_chunk(expand(code), X, s1[i]);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    acc[i] = __builtin_fmaf(f16_lo(Dw[i][0]), s0[i], acc[i]);
+                    acc[i] = __builtin_fmaf(f16_hi(Dw[i][4]), s1[i], acc[i]);
                 }
             }
         }
@@ -300,19 +403,20 @@ __device__ __forceinline__ Cursor next_unit(const PlanDesc& D, Cursor c, int JB)
     return c;
 }
 
-template <class Policy, int R, int JB, int NB, bool ARGMAX>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEu))) k_sweep(const PlanDesc* __restrict__ descs, int count, PlanDesc one,
-                                                    int64_t total, int xs_bytes, uint64_t* __restrict__ keys) {
+template <class E, int NB, int XS, bool ARGMAX>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
+k_sweep(const PlanDesc* __restrict__ descs, int count, PlanDesc one, int64_t total, int xs_bytes,
+        uint64_t* __restrict__ keys) {
     extern __shared__ u4 xs[];
-    Ctx x;
-    x.wave = threadIdx.x >> 6;
-    x.lane = threadIdx.x & 63;
-    uint8_t* wl = reinterpret_cast<uint8_t*>(xs) + xs_bytes + x.wave * Policy::kWaveLds;
+    constexpr int R = E::kR;
+    constexpr int JB = E::kJB;
+    E eng;
+    eng.init(reinterpret_cast<uint8_t*>(xs) + xs_bytes + (threadIdx.x >> 6) * E::kWaveLds);
     const int n_desc = descs ? count : 1;
     auto get = [&](int d) -> PlanDesc { return descs ? descs[d] : one; };
     const int64_t G = gridDim.x;
-    const int64_t c_lo = (total / G) * blockIdx.x + ((total % G) * blockIdx.x) / G;
-    const int64_t c_hi = (total / G) * (blockIdx.x + 1) + ((total % G) * ((int64_t)blockIdx.x + 1)) / G;
+    const int64_t c_lo = uniform64((total / G) * blockIdx.x + ((total % G) * blockIdx.x) / G);
+    const int64_t c_hi = uniform64((total / G) * (blockIdx.x + 1) + ((total % G) * ((int64_t)blockIdx.x + 1)) / G);
     auto owned = [&](const PlanDesc& D, const Cursor& c) { return D.cost_begin + c.s * D.npl < c_hi; };
 
     uint64_t best = 0;
@@ -327,7 +431,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
         }
         cur.d = lo;
         D = get(lo);
-        cur.s = (c_lo - D.cost_begin + D.npl - 1) / D.npl;
+        cur.s = uniform64((c_lo - D.cost_begin + D.npl - 1) / D.npl);
         cur.jb = 0;
         if (cur.s >= D.steps) {
             cur.d++;
@@ -341,7 +445,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
     if (have) {
         // A ring of NB unit buffers: unit u is loaded NB-1 steps before it is
         // computed, so every wave keeps NB-1 units of loads in flight.
-        typename Policy::Buf A, B, C;
+        typename E::Buf A, B, C;
         float acc[R];
 #pragma unroll
         for (int i = 0; i < R; ++i) acc[i] = 0.0f;
@@ -355,35 +459,35 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
             have_l = c2.d < n_desc && owned(Dl, c2);
             cl = c2;
         };
-        Policy::issue(x, Dl, cl, A);
+        eng.issue(Dl, cl, A);
         advance_l();
         if (NB == 3 && have_l) {
-            Policy::issue(x, Dl, cl, B);
+            eng.issue(Dl, cl, B);
             advance_l();
         }
 
         // One step: load the next unit into `into` (the buffer computed in the
         // previous step), compute the unit in `now`, finish the row group when
         // its last unit is done.  Returns false after the last unit.
-        auto step = [&](typename Policy::Buf& now, typename Policy::Buf& into) -> bool {
+        auto step = [&](typename E::Buf& now, typename E::Buf& into) -> bool {
             if (have_l) {
-                Policy::issue(x, Dl, cl, into);
+                eng.issue(Dl, cl, into);
                 advance_l();
             }
             if (staged != cur.d) {
                 __syncthreads();
-                stage_x(D.x, D.k >> 5, D.npl * 16, xs);
+                stage_x(D.x, D.k >> 5, D.npl * 16, XS > 0 ? XS : D.npl * 16, xs);
                 __syncthreads();
                 staged = cur.d;
             }
-            Policy::compute(x, D, cur, xs, wl, now, acc);
+            eng.compute(D, cur, xs, now, acc);
             if (cur.jb + JB >= D.npl) {  // last unit of this row group
-                const int64_t r0 = x.wave_row0(cur, R) + (x.lane >> 4) * R;
+                const int64_t r0 = cur.s * (int64_t)(kWaves * 4 * R) + eng.rr0;
 #pragma unroll
                 for (int i = 0; i < R; ++i) {
                     const float v = row16_sum(acc[i]);
                     acc[i] = 0.0f;
-                    if ((x.lane & 15) == 0 && r0 + i < D.n) {
+                    if (eng.l16 == 0 && r0 + i < D.n) {
                         ((g_f32*)D.y)[r0 + i] = v;
                         if (ARGMAX) {
                             const uint64_t kk = argmax_key(v, r0 + i);
@@ -496,7 +600,12 @@ int device_cu_count() {
 
 static int npl_of(int64_t k) { return (int)(((k / 64) + 15) / 16); }
 
-static size_t x_lds_bytes(int64_t k) { return (size_t)npl_of(k) * 16 * kChunksPerPair * sizeof(u4); }
+// LDS of the staged activations: the fixed stride when k fits it, else k's own padding.
+static bool fixed_stride(int64_t max_k) { return npl_of(max_k) * 16 <= kXStride; }
+static size_t x_lds_bytes(int64_t max_k) {
+    const int pairs = fixed_stride(max_k) ? kXStride : npl_of(max_k) * 16;
+    return (size_t)pairs * kChunksPerPair * sizeof(u4);
+}
 
 static PlanDesc single_desc(const uint8_t* w, const uint16_t* x, float* y, int64_t n, int64_t k) {
     PlanDesc d;
@@ -506,77 +615,62 @@ static PlanDesc single_desc(const uint8_t* w, const uint16_t* x, float* y, int64
     d.n = n;
     d.k = (int32_t)k;
     d.npl = npl_of(k);
-    d.steps = (n + batch_rows_per_step() - 1) / batch_rows_per_step();
+    d.steps = (n + kRowsPerStep - 1) / kRowsPerStep;
     d.cost_begin = 0;
     return d;
 }
 
-static int device_lds_per_cu() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 65536;
-    int v = cache[dev].load(std::memory_order_relaxed);
-    if (v > 0) return v;
-    int b = 0;
-    if (hipDeviceGetAttribute(&b, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess || b <= 0)
-        b = 65536;
-    cache[dev].store(b, std::memory_order_relaxed);
-    return b;
-}
-
-#ifndef Q4_SWEEP_CJB
-#define Q4_SWEEP_CJB 1
+#ifndef Q4_SWEEP_COAL
+#define Q4_SWEEP_COAL 0
 #endif
-constexpr int kCJB = Q4_SWEEP_CJB;  // pairs per lane in a coalesced unit (R * JB even)
-using PairP = PairLoads<kR, kJB>;
-using PairP1 = PairLoads<kR, 1>;  // LM head: the argmax epilogue needs the registers of one pair
-using CoalP = CoalescedLoads<kR, kCJB>;
+template <int XS>
+using SweepEngine = typename std::conditional<Q4_SWEEP_COAL != 0, CoalEngine<kR, kJB, XS>, Engine<kR, kJB, XS>>::type;
 
-template <class P, int JB, bool AM>
+template <int XS, bool AM>
 static hipError_t launch_sweep(const PlanDesc* descs, int count, const PlanDesc& one, int64_t total,
                                int64_t max_k, int64_t max_steps, uint64_t* keys, int grid_cap,
                                int* grid_out, hipStream_t s) {
+    using E = SweepEngine<XS>;
     const size_t xsb = x_lds_bytes(max_k);
-    const size_t lds = xsb + kWaves * (size_t)P::kWaveLds;
-    auto kern = k_sweep<P, kR, JB, (P::kCoalesced ? kNBC : kNBP), AM>;
+    const size_t lds = xsb + kWaves * (size_t)E::kWaveLds;
+    auto kern = k_sweep<E, kNB, XS, AM>;
     if (lds > 65536) {
         const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    const int per_cu = std::max(1, std::min<int>(kWgPerCu, (int)(device_lds_per_cu() / std::max<size_t>(lds, 1))));
-    int grid = (int)std::max<int64_t>(1, std::min<int64_t>(max_steps, (int64_t)device_cu_count() * per_cu));
+    int grid = (int)std::max<int64_t>(1, std::min<int64_t>(max_steps, (int64_t)device_cu_count() * kWgPerCu));
     grid = std::min(grid, grid_cap);
     if (grid_out) *grid_out = grid;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, s, descs, count, one, total, (int)xsb, keys);
     return hipGetLastError();
 }
 
-[[maybe_unused]] static bool coalesced_ok(int64_t k) { return Q4_SWEEP_COALESCED && k % 1024 == 0; }
+template <bool AM>
+static hipError_t launch_any(const PlanDesc* descs, int count, const PlanDesc& one, int64_t total,
+                             int64_t max_k, int64_t max_steps, uint64_t* keys, int grid_cap, int* grid_out,
+                             hipStream_t s) {
+    if (fixed_stride(max_k))
+        return launch_sweep<kXStride, AM>(descs, count, one, total, max_k, max_steps, keys, grid_cap, grid_out, s);
+    return launch_sweep<0, AM>(descs, count, one, total, max_k, max_steps, keys, grid_cap, grid_out, s);
+}
 
 hipError_t launch_gemv(const uint8_t* w, const uint16_t* x, float* y, int64_t n, int64_t k,
                        hipStream_t s) {
     const PlanDesc d = single_desc(w, x, y, n, k);
-    const int64_t total = d.steps * d.npl;
-    if constexpr (Q4_SWEEP_COALESCED) {
-        if (coalesced_ok(k))
-            return launch_sweep<CoalP, kCJB, false>(nullptr, 1, d, total, k, d.steps, nullptr, INT32_MAX, nullptr, s);
-    }
-    return launch_sweep<PairP, kJB, false>(nullptr, 1, d, total, k, d.steps, nullptr, INT32_MAX, nullptr, s);
+    return launch_any<false>(nullptr, 1, d, d.steps * d.npl, k, d.steps, nullptr, INT32_MAX, nullptr, s);
 }
 
 int argmax_blocks(int64_t n, int64_t k) {
     (void)k;
-    const int64_t steps = (n + batch_rows_per_step() - 1) / batch_rows_per_step();
+    const int64_t steps = (n + kRowsPerStep - 1) / kRowsPerStep;
     return (int)std::min<int64_t>(steps, kArgmaxMaxBlocks);
 }
 
 hipError_t launch_lm_head(const uint8_t* w, const uint16_t* h, float* logits, int32_t* token,
                           int64_t n, int64_t k, uint64_t* keys, hipStream_t s) {
     const PlanDesc d = single_desc(w, h, logits, n, k);
-    const int64_t total = d.steps * d.npl;
     int grid = 0;
-    const int cap = argmax_blocks(n, k);
-    hipError_t e = launch_sweep<PairP1, 1, true>(nullptr, 1, d, total, k, d.steps, keys, cap, &grid, s);
+    hipError_t e = launch_any<true>(nullptr, 1, d, d.steps * d.npl, k, d.steps, keys, argmax_blocks(n, k), &grid, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_argmax_final, dim3(1), dim3(kThreads), 0, s, keys, grid, token);
     return hipGetLastError();
@@ -592,14 +686,9 @@ hipError_t launch_gemm_generic(const uint8_t* w, const uint16_t* x, float* y, in
 
 hipError_t launch_gemv_batch(const PlanDesc* descs, int count, int64_t total_cost, int max_k,
                              bool all_k1024, hipStream_t s) {
+    (void)all_k1024;
     PlanDesc none = {};
-    if constexpr (Q4_SWEEP_COALESCED) {
-        if (all_k1024)
-            return launch_sweep<CoalP, kCJB, false>(descs, count, none, total_cost, max_k, INT64_MAX, nullptr,
-                                                    INT32_MAX, nullptr, s);
-    }
-    return launch_sweep<PairP, kJB, false>(descs, count, none, total_cost, max_k, INT64_MAX, nullptr,
-                                           INT32_MAX, nullptr, s);
+    return launch_any<false>(descs, count, none, total_cost, max_k, INT64_MAX, nullptr, INT32_MAX, nullptr, s);
 }
 
 }  // namespace q4
