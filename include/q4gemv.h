@@ -170,32 +170,41 @@ typedef struct q4_gemv_desc {
     int64_t k;
 } q4_gemv_desc;
 
-/* Host-side handle of a batch plan: where its descriptors live on the device
- * and the launch parameters derived from them.  Filled by
- * q4_0_gemv_batch_plan; plain data, may be copied. */
+/* Host-side handle of a batch plan.  Filled by q4_0_gemv_batch_plan; plain
+ * data, may be copied. */
 typedef struct q4_gemv_plan {
-    void* device;        /* the caller's device buffer holding the descriptors */
-    int count;           /* number of GEMVs */
-    int max_k;           /* largest k in the list */
-    int flags;           /* launch path chosen at planning time (internal) */
-    int64_t total_cost;  /* work measure used to split the list across workgroups */
+    void* device;  /* the caller's device buffer holding the plan */
+    int count;     /* number of GEMVs */
+    int max_k;     /* largest k in the list */
+    int grid;      /* workgroups of one launch */
+    int nchunks;   /* pieces of work in the plan's schedule */
 } q4_gemv_plan;
 
-/* Device bytes q4_0_gemv_batch_plan needs for `count` descriptors. */
-Q4_API size_t q4_0_gemv_batch_plan_bytes(int count);
+/* Device bytes q4_0_gemv_batch_plan needs for this descriptor list (the size
+ * depends on the shapes and on the current device's compute-unit count).
+ * Returns 0, with q4_last_error() set, if the list is not valid. */
+Q4_API size_t q4_0_gemv_batch_plan_bytes(const q4_gemv_desc* descs, int count);
 
 /*
- * Validate `count` host-side descriptors, write their device form into the
- * caller's device buffer `plan_buf` (q4_0_gemv_batch_plan_bytes(count) bytes)
- * and fill `*plan`.  The copy is enqueued on `stream` and has completed when
+ * Validate `count` host-side descriptors and write the plan into the caller's
+ * device buffer `plan_buf` (at least q4_0_gemv_batch_plan_bytes(descs, count)
+ * bytes, 16-byte aligned), then fill `*plan`.  The plan holds the
+ * descriptors, a schedule that cuts the list's row steps into chunks (one per
+ * workgroup first, then smaller ones that workgroups take as they finish), and
+ * two counters the launch uses to hand the chunks out; the counters are zero
+ * between launches.  The copy is enqueued on `stream` and has completed when
  * this call returns (it synchronizes `stream`), so `descs` may be freed
  * afterwards.  The plan stays valid as long as `plan_buf` and the tensors it
- * names do.  1 <= count <= 1<<20; every k % 64 == 0 and k <= 32768.
+ * names do, on the device that was current when it was made.  1 <= count <=
+ * 1<<20; every k % 64 == 0 and k <= 32768; no output may overlap another
+ * output, an input or the plan.
  */
 Q4_API q4_status q4_0_gemv_batch_plan(const q4_gemv_desc* descs, int count, void* plan_buf,
                                size_t plan_bytes, q4_gemv_plan* plan, void* stream);
 
-/* Run every GEMV of a plan in one launch on `stream`. */
+/* Run every GEMV of a plan in one launch on `stream`.  Launches of the same
+ * plan must not overlap in time (they share its counters and outputs); the
+ * results do not depend on how the chunks were handed out. */
 Q4_API q4_status q4_0_gemv_batch(const q4_gemv_plan* plan, void* stream);
 
 #ifdef __cplusplus

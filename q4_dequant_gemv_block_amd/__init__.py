@@ -53,7 +53,7 @@ class GemvDesc(ctypes.Structure):
 
 class GemvPlan(ctypes.Structure):
     _fields_ = [("device", ctypes.c_void_p), ("count", ctypes.c_int), ("max_k", ctypes.c_int),
-                ("flags", ctypes.c_int), ("total_cost", ctypes.c_int64)]
+                ("grid", ctypes.c_int), ("nchunks", ctypes.c_int)]
 
 
 _lib = None
@@ -83,7 +83,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lm_head_argmax.restype = st
     lib.lm_head_argmax.argtypes = [vp, vp, vp, vp, i64, i64, vp, ctypes.c_size_t, vp]
     lib.q4_0_gemv_batch_plan_bytes.restype = ctypes.c_size_t
-    lib.q4_0_gemv_batch_plan_bytes.argtypes = [ctypes.c_int]
+    lib.q4_0_gemv_batch_plan_bytes.argtypes = [ctypes.POINTER(GemvDesc), ctypes.c_int]
     lib.q4_0_gemv_batch_plan.restype = st
     lib.q4_0_gemv_batch_plan.argtypes = [ctypes.POINTER(GemvDesc), ctypes.c_int, vp, ctypes.c_size_t,
                                          ctypes.POINTER(GemvPlan), vp]
@@ -238,12 +238,15 @@ class GemvBatch:
                                 _ptr(y, torch.float32, "y"), n, k)
             self._keep.append((w, x, y))
         lib = load_library()
-        nbytes = int(lib.q4_0_gemv_batch_plan_bytes(len(items)))
         dev = items[0][0].device if items else torch.device("cuda")
-        self.buffer = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
         self.plan = GemvPlan()
-        _check(lib.q4_0_gemv_batch_plan(descs, len(items), self.buffer.data_ptr(), self.buffer.numel(),
-                                        ctypes.byref(self.plan), _stream(stream)))
+        with torch.cuda.device(dev):  # the schedule is cut for this device
+            nbytes = int(lib.q4_0_gemv_batch_plan_bytes(descs, len(items)))
+            if nbytes == 0:
+                _check(Q4_ERR_INVALID_ARG)
+            self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+            _check(lib.q4_0_gemv_batch_plan(descs, len(items), self.buffer.data_ptr(), self.buffer.numel(),
+                                            ctypes.byref(self.plan), _stream(stream)))
 
     def __call__(self, stream=None):
         _check(load_library().q4_0_gemv_batch(ctypes.byref(self.plan), _stream(stream)))

@@ -25,6 +25,9 @@ FLAGS = [
     "-Wall",
     # packed fp32 forms are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # a work-queue atomic is issued by one lane and its result read much later;
+    # the wave-aggregating rewrite would wait for it (and every older load) at once
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-I" + os.path.join(ROOT, "include"),
 ]
 

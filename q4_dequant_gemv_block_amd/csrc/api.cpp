@@ -192,27 +192,21 @@ q4_status lm_head_argmax(const void* w, const void* h, float* logits, int32_t* t
     return hip_status(e, "lm_head_argmax launch");
 }
 
-size_t q4_0_gemv_batch_plan_bytes(int count) {
-    if (count < 1 || count > (1 << 20)) return 0;
-    return (size_t)count * sizeof(q4::PlanDesc);
-}
+}  // extern "C"
 
-q4_status q4_0_gemv_batch_plan(const q4_gemv_desc* descs, int count, void* plan_buf, size_t plan_bytes,
-                               q4_gemv_plan* plan, void* stream) {
-    const char* fn = "q4_0_gemv_batch_plan";
-    if (!descs || !plan || !plan_buf) return fail(Q4_ERR_INVALID_ARG, "%s: null pointer", fn);
+namespace {
+
+// Validates a descriptor list and lays out its plan: device descriptors,
+// chunk schedule and launch grid.
+q4_status plan_layout(const char* fn, const q4_gemv_desc* descs, int count, std::vector<q4::PlanDesc>* dev,
+                      std::vector<q4::SchedChunk>* chunks, int* grid, int* max_k_out) {
+    if (!descs) return fail(Q4_ERR_INVALID_ARG, "%s: null descriptor list", fn);
     if (count < 1 || count > (1 << 20)) return fail(Q4_ERR_INVALID_ARG, "%s: count = %d outside [1, 1<<20]", fn, count);
-    if (plan_bytes < q4_0_gemv_batch_plan_bytes(count))
-        return fail(Q4_ERR_WORKSPACE, "%s: plan buffer of %zu bytes needed", fn, q4_0_gemv_batch_plan_bytes(count));
-    if (!aligned(plan_buf, 16)) return fail(Q4_ERR_MISALIGNED, "%s: plan buffer must be 16-byte aligned", fn);
-    std::vector<q4::PlanDesc> dev(count);
+    dev->assign(count, q4::PlanDesc{});
     std::vector<Range> outs, ins;
     outs.reserve(count);
     ins.reserve(2 * (size_t)count);
-    const int64_t rows_step = q4::batch_rows_per_step();
-    int64_t cost = 0;
     int max_k = 0;
-    bool all_k1024 = true;
     for (int i = 0; i < count; ++i) {
         const q4_gemv_desc& d = descs[i];
         q4_status st = check_shape(fn, 1, 1, d.n, d.k);
@@ -221,18 +215,13 @@ q4_status q4_0_gemv_batch_plan(const q4_gemv_desc* descs, int count, void* plan_
             return fail(Q4_ERR_INVALID_ARG, "%s: descriptor %d: k must be a multiple of 64 up to %lld", fn, i, (long long)q4::kFastMaxK);
         st = check_tensors(fn, d.w, d.x, d.y, 1, d.n, d.k, (size_t)d.n * 4);
         if (st) return fail(st, "%s: descriptor %d: %s", fn, i, std::string(g_err).c_str());
-        q4::PlanDesc& p = dev[i];
+        q4::PlanDesc& p = (*dev)[i];
         p.w = static_cast<const uint8_t*>(d.w);
         p.x = static_cast<const uint16_t*>(d.x);
         p.y = d.y;
         p.n = d.n;
         p.k = (int32_t)d.k;
-        p.npl = (int32_t)(((d.k / 64) + 15) / 16);
-        p.steps = (d.n + rows_step - 1) / rows_step;
-        p.cost_begin = cost;
-        cost += p.steps * p.npl;
         max_k = std::max<int>(max_k, (int)d.k);
-        all_k1024 = all_k1024 && d.k % 1024 == 0;
         outs.push_back(range(d.y, (size_t)d.n * 4));
         ins.push_back(range(d.w, (size_t)(d.n * row_bytes(d.k))));
         ins.push_back(range(d.x, (size_t)d.k * 2));
@@ -245,27 +234,71 @@ q4_status q4_0_gemv_batch_plan(const q4_gemv_desc* descs, int count, void* plan_
         if (it != outs.end() && overlap(*it, r)) return fail(Q4_ERR_INVALID_ARG, "%s: an output overlaps an input", fn);
         if (it != outs.begin() && overlap(*(it - 1), r)) return fail(Q4_ERR_INVALID_ARG, "%s: an output overlaps an input", fn);
     }
-    const Range rp = range(plan_buf, q4_0_gemv_batch_plan_bytes(count));
-    for (const Range& r : outs)
-        if (overlap(r, rp)) return fail(Q4_ERR_INVALID_ARG, "%s: plan buffer overlaps an output", fn);
+    q4::build_schedule(dev->data(), count, chunks, grid);
+    *max_k_out = max_k;
+    return ok();
+}
+
+size_t plan_size(int count, size_t nchunks) {
+    return sizeof(q4::SchedHead) + (size_t)count * sizeof(q4::PlanDesc) + nchunks * sizeof(q4::SchedChunk);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t q4_0_gemv_batch_plan_bytes(const q4_gemv_desc* descs, int count) {
+    std::vector<q4::PlanDesc> dev;
+    std::vector<q4::SchedChunk> chunks;
+    int grid = 0, max_k = 0;
+    if (plan_layout("q4_0_gemv_batch_plan_bytes", descs, count, &dev, &chunks, &grid, &max_k)) return 0;
+    ok();
+    return plan_size(count, chunks.size());
+}
+
+q4_status q4_0_gemv_batch_plan(const q4_gemv_desc* descs, int count, void* plan_buf, size_t plan_bytes,
+                               q4_gemv_plan* plan, void* stream) {
+    const char* fn = "q4_0_gemv_batch_plan";
+    if (!plan || !plan_buf) return fail(Q4_ERR_INVALID_ARG, "%s: null pointer", fn);
+    std::vector<q4::PlanDesc> dev;
+    std::vector<q4::SchedChunk> chunks;
+    int grid = 0, max_k = 0;
+    const q4_status st = plan_layout(fn, descs, count, &dev, &chunks, &grid, &max_k);
+    if (st) return st;
+    const size_t need = plan_size(count, chunks.size());
+    if (plan_bytes < need) return fail(Q4_ERR_WORKSPACE, "%s: plan buffer of %zu bytes needed", fn, need);
+    if (!aligned(plan_buf, 16)) return fail(Q4_ERR_MISALIGNED, "%s: plan buffer must be 16-byte aligned", fn);
+    const Range rp = range(plan_buf, need);
+    for (int i = 0; i < count; ++i) {
+        const q4_gemv_desc& d = descs[i];
+        if (overlap(rp, range(d.y, (size_t)d.n * 4)) || overlap(rp, range(d.w, (size_t)(d.n * row_bytes(d.k)))) ||
+            overlap(rp, range(d.x, (size_t)d.k * 2)))
+            return fail(Q4_ERR_INVALID_ARG, "%s: plan buffer overlaps a tensor of descriptor %d", fn, i);
+    }
+    std::vector<uint8_t> host(need);
+    q4::SchedHead head = {0u, 0u, (int32_t)chunks.size(), (int32_t)grid};
+    std::memcpy(host.data(), &head, sizeof(head));
+    std::memcpy(host.data() + sizeof(head), dev.data(), dev.size() * sizeof(q4::PlanDesc));
+    std::memcpy(host.data() + sizeof(head) + dev.size() * sizeof(q4::PlanDesc), chunks.data(),
+                chunks.size() * sizeof(q4::SchedChunk));
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = hipMemcpyAsync(plan_buf, dev.data(), dev.size() * sizeof(q4::PlanDesc), hipMemcpyHostToDevice, s);
+    hipError_t e = hipMemcpyAsync(plan_buf, host.data(), need, hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return hip_status(e, "q4_0_gemv_batch_plan copy");
     plan->device = plan_buf;
     plan->count = count;
     plan->max_k = max_k;
-    plan->flags = all_k1024 ? 1 : 0;
-    plan->total_cost = cost;
+    plan->grid = grid;
+    plan->nchunks = (int)chunks.size();
     return ok();
 }
 
 q4_status q4_0_gemv_batch(const q4_gemv_plan* plan, void* stream) {
     if (!plan || !plan->device) return fail(Q4_ERR_INVALID_ARG, "q4_0_gemv_batch: null plan");
-    if (plan->count < 1 || plan->max_k < 64 || plan->max_k > q4::kFastMaxK || plan->total_cost < 1)
+    if (plan->count < 1 || plan->max_k < 64 || plan->max_k > q4::kFastMaxK || plan->grid < 1 ||
+        plan->nchunks < plan->grid)
         return fail(Q4_ERR_INVALID_ARG, "q4_0_gemv_batch: plan was not filled by q4_0_gemv_batch_plan");
-    const hipError_t e = q4::launch_gemv_batch(static_cast<const q4::PlanDesc*>(plan->device), plan->count,
-                                               plan->total_cost, plan->max_k, (plan->flags & 1) != 0,
+    const hipError_t e = q4::launch_gemv_batch(plan->device, plan->count, plan->nchunks, plan->grid, plan->max_k,
                                                static_cast<hipStream_t>(stream));
     return hip_status(e, "q4_0_gemv_batch launch");
 }

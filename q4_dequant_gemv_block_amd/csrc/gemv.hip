@@ -8,41 +8,37 @@
 // Scratch").  The kernels keep that structure, laid out for CDNA4:
 //
 //  * 16 lanes (one DPP row) own one weight row; lane l takes block pairs
-//    l, l+16, l+32, ... so the 16 lanes of a row read 576 contiguous bytes per
-//    step.  Each lane group carries R consecutive rows at the same pair
-//    positions, so one read of the activation chunks from LDS serves R rows.
-//  * Weights are read with cached global dwordx4/dword loads (36-byte pairs
-//    at 4-byte alignment).  The unit's base address is uniform (scalar
-//    registers) and every lane adds a fixed 32-bit offset, so issuing loads
-//    costs one multiply-add per row and no 64-bit vector arithmetic.
+//    l, l+16, l+32, ...; a wave's unit is 4 rows x one 576-byte segment
+//    (16 pairs) per row.
+//  * Weights move from HBM straight into LDS: one global_load_lds_dwordx4 per
+//    row segment, 36 lanes x 16 contiguous bytes with the non-temporal hint,
+//    so every 128-byte line is requested once and no registers hold loads in
+//    flight.  Each wave keeps a ring of units in its own LDS window and waits
+//    for a unit with an explicit vmcnt before reading its pairs back.
 //  * 4-bit codes become exact (code - 8) f16 pairs with one v_and_or_b32 and
 //    one v_pk_add_f16 per pair and meet the activations in v_dot2_f32_f16; the
 //    block scale is applied once per block in f32 (v_fma_mix).
 //  * The activation vector is staged once per workgroup and GEMV into LDS in
 //    the chunk order of q4_device.h, at a fixed chunk stride so every LDS read
 //    is one base register plus an immediate offset.
-//  * Every wave walks a sequence of units (4R rows x JB pairs per lane) and
-//    issues the loads of the next unit before computing the current one, also
-//    across row groups and GEMV boundaries.
 //  * Units at the end of a matrix (rows past N, or K not a multiple of 1024)
-//    load from clamped in-range addresses instead of branching per lane:
-//    padding pairs meet zero activation chunks and add exactly 0, padding
-//    rows are never stored.
+//    read clamped rows and only the bytes of the row; pairs past the row end
+//    get zero scales and meet zero activations, padding rows are never stored.
 //  * The row sum is a fixed-order DPP tree inside the 16-lane row, so results
-//    are deterministic and independent of where a row sits.
+//    are deterministic and independent of where a row sits or which
+//    workgroup computed it.
 //
-// Work split: a work item is (GEMV d, row step s); it starts at cost
-// cost_begin[d] + s * npl[d], npl (pairs per lane) being proportional to its
-// bytes.  Workgroup g takes every item starting in [T*g/G, T*(g+1)/G):
-// contiguous, byte-balanced ranges, so a workgroup stages few activation
-// vectors.  The single-GEMV and LM-head entry points run the same kernel on a
-// one-descriptor list passed by value.
+// Work split: a work item is a row step (64 rows) of one GEMV; its cost is
+// proportional to its bytes.  The single GEMV and the LM head split their
+// steps statically into byte-balanced contiguous ranges; a batch follows the
+// plan's schedule (a static first chunk per workgroup, then chunks taken from
+// a shared counter), so workgroups that stream faster take more work.
 #include "q4_device.h"
 #include "q4_launch.h"
 
 #include <algorithm>
 #include <atomic>
-#include <type_traits>
+#include <vector>
 
 namespace q4 {
 
@@ -50,14 +46,11 @@ namespace q4 {
 #ifndef Q4_SWEEP_R
 #define Q4_SWEEP_R 2
 #endif
-#ifndef Q4_SWEEP_JB
-#define Q4_SWEEP_JB 1
-#endif
 #ifndef Q4_SWEEP_WG_PER_CU
-#define Q4_SWEEP_WG_PER_CU 2
+#define Q4_SWEEP_WG_PER_CU 1
 #endif
 #ifndef Q4_SWEEP_THREADS
-#define Q4_SWEEP_THREADS 512
+#define Q4_SWEEP_THREADS 768
 #endif
 #ifndef Q4_SWEEP_WPE
 #define Q4_SWEEP_WPE 4
@@ -70,10 +63,9 @@ constexpr int kThreads = Q4_SWEEP_THREADS;  // the waves of a workgroup share on
 constexpr int kWaves = kThreads / 64;
 constexpr int kWavesPerEu = Q4_SWEEP_WPE;   // register budget: waves per SIMD the sweep kernel must fit
 constexpr int kR = Q4_SWEEP_R;              // rows per 16-lane group
-constexpr int kJB = Q4_SWEEP_JB;            // pairs per lane per unit
-constexpr int kNB = Q4_SWEEP_NB;            // unit buffers in the prefetch ring (2 or 3)
+constexpr int kNB = Q4_SWEEP_NB;            // units per wave in the LDS ring (2 or 3)
 constexpr int kWgPerCu = Q4_SWEEP_WG_PER_CU;
-constexpr int kRowsPerStep = kWaves * 4 * kR;
+constexpr int kRowsPerStep = kWaves * 4 * kR;  // rows of one workgroup step (4R per wave)
 constexpr int kXStride = 288;               // activation chunk stride in pairs: k <= 18432 (36 KiB of LDS)
 
 int batch_rows_per_step() { return kRowsPerStep; }
@@ -133,17 +125,25 @@ __device__ __forceinline__ uint64_t argmax_key(float v, int64_t idx) {
     return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
 }
 
-__device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* sh) {
-    sh[threadIdx.x] = v;
-    __syncthreads();
-    for (int s = kThreads / 2; s > 0; s >>= 1) {
-        if ((int)threadIdx.x < s) {
-            const uint64_t o = sh[threadIdx.x + s];
-            if (o > sh[threadIdx.x]) sh[threadIdx.x] = o;
-        }
-        __syncthreads();
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, o);
+        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), o);
+        const uint64_t t = ((uint64_t)hi << 32) | lo;
+        v = t > v ? t : v;
     }
-    return sh[0];
+    return v;
+}
+
+// Maximum over the workgroup; sh holds one entry per wave.
+__device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* sh) {
+    v = wave_max_u64(v);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+    __syncthreads();
+    uint64_t r = 0;
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) r = sh[i] > r ? sh[i] : r;
+    return r;
 }
 
 // ---------------------------------------------------------------------------
@@ -166,120 +166,77 @@ struct Cursor {
     int jb;      // first pair-per-lane index of the unit
 };
 
-template <int R, int JB, int XS>
-struct Engine {
-    static constexpr int kR = R;
-    static constexpr int kJB = JB;
-    static constexpr int kWaveLds = 0;
-    struct Buf {
-        uint32_t d[JB][R][9];
-    };
-    int lane, l16;
-    uint32_t rr0;  // row of this lane's first row within a step (its R rows are rr0 .. rr0+R-1)
-    uint32_t l36;  // this lane's byte offset within a 16-pair segment
-
-    __device__ __forceinline__ void init(uint8_t* wl) {
-        (void)wl;
-        lane = threadIdx.x & 63;
-        l16 = lane & 15;
-        const int wave = threadIdx.x >> 6;
-        rr0 = (uint32_t)(wave * 4 * R + (lane >> 4) * R);
-        l36 = (uint32_t)(l16 * kPairBytes);
-    }
-
-    __device__ __forceinline__ void issue(const PlanDesc& D, const Cursor& c, Buf& b) const {
-        const int np = D.k >> 6;
-        const uint32_t rb = (uint32_t)np * kPairBytes;
-        const int64_t row0 = c.s * (int64_t)(kWaves * 4 * R);
-        const bool interior = row0 + kWaves * 4 * R <= D.n && (np & 15) == 0;  // uniform
-        if (interior) {
-            const uint8_t* base = D.w + row0 * rb + (int64_t)c.jb * (16 * kPairBytes);
+// R rows' pairs (nine dwords each, D[i]) against the activation chunks at
+// xb[c * stride], accumulated into acc[i]: chunk-outer, row-inner, so one
+// activation chunk is live at a time; the block sums are scaled once each.
+template <int R>
+__device__ __forceinline__ void rows_dot(const uint32_t (&D)[R][9], const u4* __restrict__ xb, int stride,
+                                         float (&acc)[R]) {
+    float s0[R], s1[R];
 #pragma unroll
-            for (int t = 0; t < JB; ++t) {
-                if (c.jb + t < D.npl) {  // uniform
+    for (int i = 0; i < R; ++i) s0[i] = s1[i] = 0.0f;
 #pragma unroll
-                    for (int i = 0; i < R; ++i)
-                        load_pair(base + ((rr0 + i) * rb + l36 + (uint32_t)t * (16 * kPairBytes)), b.d[t][i]);
-                }
-            }
-        } else {
-            // rows and pairs fit 31 bits (the boundary checks n and k)
-            const int last_row = (int)(D.n - 1);
-            const int r0 = (int)row0 + (int)rr0;
+    for (int ch = 0; ch < 8; ++ch) {
+        const u4 X = xb[ch * stride];
 #pragma unroll
-            for (int t = 0; t < JB; ++t) {
-                const int j = c.jb + t;
-                if (j < D.npl) {
-                    const uint32_t p = (uint32_t)min(l16 + 16 * j, np - 1);
-#pragma unroll
-                    for (int i = 0; i < R; ++i) {
-                        const uint32_t r = (uint32_t)min(r0 + i, last_row);
-                        load_pair(D.w + (uint64_t)r * rb + p * kPairBytes, b.d[t][i]);
-                    }
-                }
-            }
+        for (int i = 0; i < R; ++i) {
+            const uint32_t code = ch == 0 ? realign_block0(D[i][0], D[i][4]) : D[i][ch < 4 ? ch : ch + 1];
+            if (ch < 4)
+                s0[i] = dot_chunk(expand(code), X, s0[i]);
+            else
+                s1[i] = dot_chunk(expand(code), X, s1[i]);
         }
     }
-
-    __device__ __forceinline__ void compute(const PlanDesc& D, const Cursor& c, const u4* __restrict__ xs,
-                                            const Buf& b, float (&acc)[R]) const {
-        const int stride = XS > 0 ? XS : D.npl * 16;
-        const u4* xb = xs + (l16 + 16 * c.jb);
 #pragma unroll
-        for (int t = 0; t < JB; ++t) {
-            if (c.jb + t < D.npl) {
-                // chunk-outer, row-inner: one activation chunk is live at a time
-                float s0[R], s1[R];
-#pragma unroll
-                for (int i = 0; i < R; ++i) s0[i] = s1[i] = 0.0f;
-#pragma unroll
-                for (int ch = 0; ch < 8; ++ch) {
-                    const u4 X = xb[ch * stride + 16 * t];
-#pragma unroll
-                    for (int i = 0; i < R; ++i) {
-                        const uint32_t* Dw = b.d[t][i];
-                        const uint32_t code = ch == 0 ? realign_block0(Dw[0], Dw[4]) : Dw[ch < 4 ? ch : ch + 1];
-                        if (ch < 4)
-                            s0[i] = dot_chunk(expand(code), X, s0[i]);
-                        else
-                            s1[i] = dot_chunk(expand(code), X, s1[i]);
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < R; ++i) {
-                    acc[i] = __builtin_fmaf(f16_lo(b.d[t][i][0]), s0[i], acc[i]);
-                    acc[i] = __builtin_fmaf(f16_hi(b.d[t][i][4]), s1[i], acc[i]);
-                }
-            }
-        }
+    for (int i = 0; i < R; ++i) {
+        acc[i] = __builtin_fmaf(f16_lo(D[i][0]), s0[i], acc[i]);
+        acc[i] = __builtin_fmaf(f16_hi(D[i][4]), s1[i], acc[i]);
     }
-};
+}
 
-// The same units loaded as fully coalesced 16-byte pieces with the
-// non-temporal hint (each 128-byte line is requested once), parked in a
-// wave-private LDS window and read back as 36-byte pairs.  On a load-only
-// copy this access pattern streams at 6.6-6.8 TB/s against about 6.15 TB/s
-// for per-lane pair loads (which cannot take the non-temporal hint: their
-// lines are touched by three instructions and would be refetched).
-template <int R, int JB, int XS>
-struct CoalEngine {
+// s_waitcnt vmcnt(n) with the other counters left free (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+typedef __attribute__((address_space(1))) void g_void;
+typedef __attribute__((address_space(3))) void l_void;
+
+// Direct-to-LDS engine.  A wave's unit is 4R consecutive rows x one segment
+// of 16 pairs (576 bytes) per row.  Each row's segment is fetched by one
+// global_load_lds_dwordx4 (36 lanes x 16 bytes, non-temporal) into the
+// wave's window in LDS: every 128-byte line is requested by one instruction
+// and no registers hold loads in flight.  The lanes then read their pair
+// (nine dwords) back from the window.  The wait before a unit is computed is
+// an explicit vmcnt: every unit issues at least 4R load instructions, so
+// "4R times the units issued since" bounds what may still be outstanding.
+// Segments that run past the row end (k % 1024 != 0) load only the row's
+// bytes (whole 16-byte pieces, then dwords); pairs past the row end have
+// their scales zeroed before use, and meet zero activations.
+template <int R, int NB, int XS>
+struct DmaEngine {
     static constexpr int kR = R;
-    static constexpr int kJB = JB;
-    static constexpr int kSegBytes = 16 * kPairBytes * JB;  // one row's part of a unit
-    static constexpr int kSegStride = kSegBytes + 32;        // padding staggers LDS banks between rows
-    static constexpr int kPieces = kSegBytes / 16 * 4 * R;   // 16-byte pieces per wave unit
-    static_assert(kPieces % 32 == 0, "R * JB must be even");
-    static constexpr int kPerLane = (kPieces + 63) / 64;     // the last slot may cover half the lanes
-    static constexpr int kWaveLds = 4 * R * kSegStride;
+    static constexpr int kJB = 1;
+    static constexpr int kSeg = 16 * kPairBytes;  // 576
+    // Row pitch 576 bytes = 144 dwords: lane l of a 16-lane group reads dword 9l + c
+    // of its row, and rows 144 dwords apart put the four groups of a wave on
+    // disjoint banks (9 is invertible modulo 32 and 64).
+    static constexpr int kPitch = kSeg;
+    static constexpr int kSlot = 4 * R * kPitch;
+    static constexpr int kWaveLds = NB * kSlot;
     struct Buf {
-        u4 v[kPerLane];
+        int slot;
+        uint32_t seq;  // issue order of the unit in the slot
+        bool edge;
     };
     int lane, l16;
-    uint32_t rr0;           // row of this lane's first row within a step
-    uint32_t wrow0;         // first row of this wave within a step (wave-uniform)
-    uint8_t* wl;            // this wave's LDS window
-    uint32_t pg[kPerLane];  // row (0 .. 4R-1) of each of this lane's pieces
-    uint32_t po[kPerLane];  // byte offset of each piece within its row's segment
+    uint32_t rr0;    // row of this lane's first row within a step
+    uint32_t wrow0;  // first row of this wave within a step
+    uint32_t seq;    // units issued so far
+    uint8_t* wl;     // this wave's window
 
     __device__ __forceinline__ void init(uint8_t* window) {
         lane = threadIdx.x & 63;
@@ -287,107 +244,78 @@ struct CoalEngine {
         const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
         wrow0 = (uint32_t)(wave * 4 * R);
         rr0 = wrow0 + (uint32_t)((lane >> 4) * R);
+        seq = 0;
         wl = window;
-#pragma unroll
-        for (int k = 0; k < kPerLane; ++k) {
-            const int P = 64 * k + lane;
-            const int g = P / (kSegBytes / 16);
-            pg[k] = (uint32_t)g;
-            po[k] = (uint32_t)(16 * (P - g * (kSegBytes / 16)));
-        }
+    }
+    __device__ __forceinline__ void init_buf(Buf& b, int slot) const {
+        b.slot = slot;
+        b.seq = 0;
+        b.edge = false;
     }
 
-    __device__ __forceinline__ bool valid_piece(int k) const { return 64 * k + lane < kPieces; }
-
-    __device__ __forceinline__ void issue(const PlanDesc& D, const Cursor& c, Buf& b) const {
+    __device__ __forceinline__ void issue(const PlanDesc& D, const Cursor& c, Buf& b) {
         const int np = D.k >> 6;
         const uint32_t rb = (uint32_t)np * kPairBytes;
-        const int64_t row0 = c.s * (int64_t)(kWaves * 4 * R);
-        const bool interior = row0 + kWaves * 4 * R <= D.n && (np & 15) == 0;  // uniform
-        const int64_t seg0 = (int64_t)c.jb * (16 * kPairBytes);
-        if (interior) {
-            const uint8_t* base = D.w + (row0 + wrow0) * rb + seg0;
+        const int64_t row0 = c.s * (int64_t)(kWaves * 4 * R) + wrow0;
+        const uint32_t seg = (uint32_t)c.jb * kSeg;
+        uint8_t* dst = wl + b.slot * kSlot;
+        b.seq = seq++;
+        b.edge = !(row0 + 4 * R <= D.n && (np & 15) == 0);  // uniform
+        if (!b.edge) {
+            const uint8_t* src = D.w + row0 * rb + seg + 16 * lane;
 #pragma unroll
-            for (int k = 0; k < kPerLane; ++k) {
-                const int t = (int)(po[k] / (16 * kPairBytes));
-                if (valid_piece(k) && c.jb + t < D.npl)
-                    b.v[k] = __builtin_nontemporal_load((g_u4*)(base + (pg[k] * rb + po[k])));
-            }
+            for (int r = 0; r < 4 * R; ++r)
+                if (lane < kSeg / 16)
+                    __builtin_amdgcn_global_load_lds((g_void*)(src + (uint32_t)r * rb), (l_void*)(dst + r * kPitch),
+                                                     16, 0, 2);
         } else {
-            // Rows past N read the last row (never stored).  With k % 1024 != 0 a
-            // segment runs past the row end: load dword by dword (a row is a
-            // multiple of 4 bytes, so no dword straddles its end) and leave the
-            // dwords past it zero; their pairs get zero scales in compute().
+            // rows past N read the last row (never stored)
+            const uint32_t avail = min((uint32_t)kSeg, rb - seg);
+            const uint32_t full = avail >> 4, rem = avail & 15;
             const int last_row = (int)(D.n - 1);
 #pragma unroll
-            for (int k = 0; k < kPerLane; ++k) {
-                const int t = (int)(po[k] / (16 * kPairBytes));
-                if (valid_piece(k) && c.jb + t < D.npl) {
-                    const uint32_t r = (uint32_t)min((int)(row0 + wrow0 + pg[k]), last_row);
-                    const uint32_t off = (uint32_t)seg0 + po[k];
-                    const uint8_t* row = D.w + (uint64_t)r * rb;
-                    uint32_t dw[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        dw[e] = off + 4u * e < rb ? *(g_u32*)(row + off + 4u * e) : 0u;
-                    b.v[k] = u4{dw[0], dw[1], dw[2], dw[3]};
-                }
+            for (int r = 0; r < 4 * R; ++r) {
+                const uint32_t rr = (uint32_t)min((int)row0 + r, last_row);
+                const uint8_t* row = D.w + (uint64_t)rr * rb + seg;
+                if ((uint32_t)lane < full)
+                    __builtin_amdgcn_global_load_lds((g_void*)(row + 16 * lane), (l_void*)(dst + r * kPitch), 16, 0,
+                                                     2);
+                if ((uint32_t)lane < (rem >> 2))
+                    __builtin_amdgcn_global_load_lds((g_void*)(row + 16 * full + 4 * lane),
+                                                     (l_void*)(dst + r * kPitch + 16 * full), 4, 0, 2);
             }
         }
     }
 
-    __device__ __forceinline__ void compute(const PlanDesc& D, const Cursor& c, const u4* __restrict__ xs,
-                                            const Buf& b, float (&acc)[R]) const {
+    // Wait for the unit in `b`, read this lane's pairs from the window into
+    // registers, and wait for those reads, so the slot may be refilled.
+    __device__ __forceinline__ void fetch(int k, int jb, const Buf& b, uint32_t (&D)[R][9]) const {
+        const uint32_t after = seq - 1u - b.seq;  // units issued after this one (uniform)
+        if (after >= 2u)
+            wait_vmcnt<8 * R>();
+        else if (after == 1u)
+            wait_vmcnt<4 * R>();
+        else
+            wait_vmcnt<0>();
+        const uint32_t* p = (const uint32_t*)(wl + b.slot * kSlot + (rr0 - wrow0) * kPitch + kPairBytes * l16);
 #pragma unroll
-        for (int k = 0; k < kPerLane; ++k)
-            if (valid_piece(k)) *(u4*)(wl + pg[k] * kSegStride + po[k]) = b.v[k];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int stride = XS > 0 ? XS : D.npl * 16;
-        const u4* xb = xs + (l16 + 16 * c.jb);
-        const uint8_t* mine = wl + (lane >> 4) * R * kSegStride + l16 * kPairBytes;
-        const int np = D.k >> 6;
+        for (int i = 0; i < R; ++i)
 #pragma unroll
-        for (int t = 0; t < JB; ++t) {
-            if (c.jb + t < D.npl) {
-                uint32_t Dw[R][9];
+            for (int c = 0; c < 9; ++c) D[i][c] = p[i * (kPitch / 4) + c];
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the reads are done before the slot is reloaded
+        if (b.edge && 16 * jb + l16 >= (k >> 6)) {
 #pragma unroll
-                for (int i = 0; i < R; ++i) {
-                    const uint32_t* src = (const uint32_t*)(mine + i * kSegStride + t * 16 * kPairBytes);
-#pragma unroll
-                    for (int e = 0; e < 9; ++e) Dw[i][e] = src[e];
-                    // a pair past the row end (k % 1024 != 0) holds other bytes: zero its scales
-                    if (l16 + 16 * (c.jb + t) >= np) {
-                        Dw[i][0] &= 0xFFFF0000u;
-                        Dw[i][4] &= 0x0000FFFFu;
-                    }
-                }
-                float s0[R], s1[R];
-#pragma unroll
-                for (int i = 0; i < R; ++i) s0[i] = s1[i] = 0.0f;
-#pragma unroll
-                for (int ch = 0; ch < 8; ++ch) {
-                    const u4 X = xb[ch * stride + 16 * t];
-#pragma unroll
-                    for (int i = 0; i < R; ++i) {
-                        const uint32_t code = ch == 0 ? realign_block0(Dw[i][0], Dw[i][4]) : Dw[i][ch < 4 ? ch : ch + 1];
-                        if (ch < 4)
-                            s0[i] = dot_chunk(expand(code), X, s0[i]);
-                        else
-                            s1[i] = dot_chunk(expand(code), X, s1[i]);
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < R; ++i) {
-                    acc[i] = __builtin_fmaf(f16_lo(Dw[i][0]), s0[i], acc[i]);
-                    acc[i] = __builtin_fmaf(f16_hi(Dw[i][4]), s1[i], acc[i]);
-                }
+            for (int i = 0; i < R; ++i) {
+                D[i][0] &= 0xFFFF0000u;  // d of block 0
+                D[i][4] &= 0x0000FFFFu;  // d of block 1
             }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+
+    __device__ __forceinline__ void math(int npl, int jb, const u4* __restrict__ xs, const uint32_t (&D)[R][9],
+                                         float (&acc)[R]) const {
+        const int stride = XS > 0 ? XS : npl * 16;
+        rows_dot<R>(D, xs + (l16 + 16 * jb), stride, acc);
     }
 };
 
@@ -403,92 +331,170 @@ __device__ __forceinline__ Cursor next_unit(const PlanDesc& D, Cursor c, int JB)
     return c;
 }
 
+// The sweep kernel.  A workgroup works through chunks; a chunk is the row
+// steps from (d0, s0) on, in list order, that start before cost c_end.
+//  * Single GEMV / LM head (head == nullptr): one chunk per workgroup, its
+//    byte-balanced share [T*g/G, T*(g+1)/G) of the one descriptor `one`.
+//  * Batch (head != nullptr): chunk g of the plan's schedule first, then
+//    further chunks taken from the shared counter head->next as the workgroup
+//    runs out of work, so workgroups that stream faster take more.  Chunk ids
+//    travel through two LDS slots: at its t-th chunk change the workgroup
+//    reads the id of chunk t+1 from q_next[(t+1)&1] and fetches that chunk's
+//    entry; in the following half-step lane 0 takes the id of chunk t+2 from
+//    the counter before that half-step's loads and stores it to q_next[t&1]
+//    after its compute, when the atomic has long returned.  The schedule
+//    gives every chunk but the list's last at least two units, so chunk
+//    changes are at least one half-step apart.  The last workgroup to finish
+//    resets the counters for the next launch.
+// Every wave walks the same unit sequence (its own rows of each step), so the
+// barriers of chunk changes and activation staging are reached by all.
 template <class E, int NB, int XS, bool ARGMAX>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
-k_sweep(const PlanDesc* __restrict__ descs, int count, PlanDesc one, int64_t total, int xs_bytes,
-        uint64_t* __restrict__ keys) {
+k_sweep(const PlanDesc* __restrict__ descs, int count, SchedHead* head, const SchedChunk* __restrict__ chunks,
+        PlanDesc one, int64_t total, int xs_bytes, uint64_t* __restrict__ keys) {
+    static_assert(NB == 2, "two slots per wave: the slot of the unit being computed is refilled once its pairs are read");
     extern __shared__ u4 xs[];
+    __shared__ int q_next[2];  // ids of this workgroup's coming chunks (batch schedule)
     constexpr int R = E::kR;
     constexpr int JB = E::kJB;
     E eng;
-    eng.init(reinterpret_cast<uint8_t*>(xs) + xs_bytes + (threadIdx.x >> 6) * E::kWaveLds);
+    eng.init(reinterpret_cast<uint8_t*>(xs) + xs_bytes +
+             __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) * E::kWaveLds);
+    const bool dyn = head != nullptr;  // uniform
     const int n_desc = descs ? count : 1;
     auto get = [&](int d) -> PlanDesc { return descs ? descs[d] : one; };
-    const int64_t G = gridDim.x;
-    const int64_t c_lo = uniform64((total / G) * blockIdx.x + ((total % G) * blockIdx.x) / G);
-    const int64_t c_hi = uniform64((total / G) * (blockIdx.x + 1) + ((total % G) * ((int64_t)blockIdx.x + 1)) / G);
-    auto owned = [&](const PlanDesc& D, const Cursor& c) { return D.cost_begin + c.s * D.npl < c_hi; };
 
-    uint64_t best = 0;
-    Cursor cur;
-    bool have = c_lo < c_hi;
-    PlanDesc D;
-    if (have) {
-        int lo = 0, hi = n_desc - 1;  // last descriptor starting at or before c_lo
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (get(mid).cost_begin <= c_lo) lo = mid; else hi = mid - 1;
+    // The workgroup's first chunk.
+    Cursor cl;       // next unit to load
+    int64_t hl;      // end (cost) of the chunk being loaded
+    bool have_l;
+    PlanDesc Dl;
+    if (dyn) {
+        const SchedChunk ch = chunks[blockIdx.x];
+        cl.d = ch.d0;
+        cl.s = ch.s0;
+        hl = ch.c_end;
+        have_l = true;
+    } else {
+        const int64_t G = gridDim.x;
+        const int64_t c_lo = uniform64((total / G) * blockIdx.x + ((total % G) * blockIdx.x) / G);
+        hl = uniform64((total / G) * (blockIdx.x + 1) + ((total % G) * ((int64_t)blockIdx.x + 1)) / G);
+        cl.d = 0;
+        cl.s = uniform64((c_lo + one.npl - 1) / one.npl);
+        have_l = cl.s < one.steps && cl.s * one.npl < hl;
+    }
+    cl.jb = 0;
+    if (have_l) Dl = get(cl.d);
+
+    const int n_static = gridDim.x;
+    const int n_chunks = dyn ? head->nchunks : 0;
+    SchedChunk nx;         // entry of the chunk after the one being loaded
+    bool nx_ok = false;
+    int trans = 0;         // chunk changes so far
+    bool grab = false;     // this half-step takes a chunk id from the counter
+    uint32_t pending = 0;  // lane 0: the id taken
+    if (dyn) {
+        if (threadIdx.x == 0) {
+            q_next[1] = n_static + (int)atomicAdd(&head->next, 1u);
+            q_next[0] = n_static + (int)atomicAdd(&head->next, 1u);
         }
-        cur.d = lo;
-        D = get(lo);
-        cur.s = uniform64((c_lo - D.cost_begin + D.npl - 1) / D.npl);
-        cur.jb = 0;
-        if (cur.s >= D.steps) {
-            cur.d++;
-            cur.s = 0;
-            have = cur.d < n_desc;
-            if (have) D = get(cur.d);
-        }
-        have = have && owned(D, cur);
+        __syncthreads();
+        const int id = __builtin_amdgcn_readfirstlane(q_next[1]);
+        nx_ok = id < n_chunks;
+        if (nx_ok) nx = chunks[id];
     }
 
-    if (have) {
-        // A ring of NB unit buffers: unit u is loaded NB-1 steps before it is
-        // computed, so every wave keeps NB-1 units of loads in flight.
-        typename E::Buf A, B, C;
+    // Move the load cursor one unit on; at the end of a chunk go to the next
+    // one (batch) or stop.
+    auto advance_l = [&]() {
+        Cursor c2 = next_unit(Dl, cl, JB);
+        if (c2.d < n_desc) {
+            if (c2.d != cl.d) Dl = get(c2.d);
+            if (Dl.cost_begin + c2.s * Dl.npl < hl) {
+                cl = c2;
+                return;
+            }
+        }
+        if (!nx_ok) {
+            have_l = false;
+            return;
+        }
+        cl.d = nx.d0;
+        cl.s = nx.s0;
+        cl.jb = 0;
+        hl = nx.c_end;
+        Dl = get(cl.d);
+        ++trans;
+        __syncthreads();  // q_next[(trans+1)&1] is written and q_next[trans&1] read by every wave
+        const int id = __builtin_amdgcn_readfirstlane(q_next[(trans + 1) & 1]);
+        nx_ok = id < n_chunks;
+        if (nx_ok) nx = chunks[id];
+        grab = true;
+    };
+
+    uint64_t best = 0;
+    if (have_l) {
+        // Unit ring: the next unit's loads are issued before the current one
+        // is computed, across row groups, GEMVs and chunks.
+        struct Rec {  // a loaded unit: descriptor, row step, pair-per-lane index
+            int32_t d;
+            int32_t jb;
+            int64_t s;
+            bool valid;
+        };
+        auto record = [&](Rec& r) {
+            r.d = cl.d;
+            r.jb = cl.jb;
+            r.s = cl.s;
+        };
+        typename E::Buf B0, B1;
+        eng.init_buf(B0, 0);
+        eng.init_buf(B1, 1);
+        Rec R0, R1;
         float acc[R];
 #pragma unroll
         for (int i = 0; i < R; ++i) acc[i] = 0.0f;
-        int staged = -1;
-        Cursor cl = cur;  // next unit to load
-        PlanDesc Dl = D;
-        bool have_l = true;
-        auto advance_l = [&]() {
-            Cursor c2 = next_unit(Dl, cl, JB);
-            if (c2.d != cl.d && c2.d < n_desc) Dl = get(c2.d);
-            have_l = c2.d < n_desc && owned(Dl, c2);
-            cl = c2;
-        };
-        eng.issue(Dl, cl, A);
-        advance_l();
-        if (NB == 3 && have_l) {
-            eng.issue(Dl, cl, B);
-            advance_l();
-        }
+        int dc = -1;      // descriptor held in Dc (compute side)
+        int staged = -1;  // descriptor whose activations are in LDS
+        PlanDesc Dc;
 
-        // One step: load the next unit into `into` (the buffer computed in the
-        // previous step), compute the unit in `now`, finish the row group when
-        // its last unit is done.  Returns false after the last unit.
-        auto step = [&](typename E::Buf& now, typename E::Buf& into) -> bool {
+        // One half-step on the unit in (r, b): take a chunk id if one is
+        // owed, stage the activations if the GEMV changed, read the unit's
+        // pairs, refill its slot with the next unit to load (so two units
+        // are in flight during the math), compute, store the taken id.
+        // Returns whether the unit after this one (r_next) is loaded.
+        auto half_step = [&](Rec& r, typename E::Buf& b, const Rec& r_next) -> bool {
+            const bool took = grab;
+            grab = false;
+            if (took && threadIdx.x == 0) pending = atomicAdd(&head->next, 1u);
+            const Rec u = r;
+            if (u.d != dc) {
+                Dc = get(u.d);
+                dc = u.d;
+            }
+            if (u.d != staged) {
+                __syncthreads();
+                stage_x(Dc.x, Dc.k >> 5, Dc.npl * 16, XS > 0 ? XS : Dc.npl * 16, xs);
+                __syncthreads();
+                staged = u.d;
+            }
+            uint32_t W[R][9];
+            eng.fetch(Dc.k, u.jb, b, W);
+            r.valid = have_l;
             if (have_l) {
-                eng.issue(Dl, cl, into);
+                record(r);
+                eng.issue(Dl, cl, b);
                 advance_l();
             }
-            if (staged != cur.d) {
-                __syncthreads();
-                stage_x(D.x, D.k >> 5, D.npl * 16, XS > 0 ? XS : D.npl * 16, xs);
-                __syncthreads();
-                staged = cur.d;
-            }
-            eng.compute(D, cur, xs, now, acc);
-            if (cur.jb + JB >= D.npl) {  // last unit of this row group
-                const int64_t r0 = cur.s * (int64_t)(kWaves * 4 * R) + eng.rr0;
+            eng.math(Dc.npl, u.jb, xs, W, acc);
+            if (u.jb + JB >= Dc.npl) {  // last unit of this row group
+                const int64_t r0 = u.s * (int64_t)(kWaves * 4 * R) + eng.rr0;
 #pragma unroll
                 for (int i = 0; i < R; ++i) {
                     const float v = row16_sum(acc[i]);
                     acc[i] = 0.0f;
-                    if (eng.l16 == 0 && r0 + i < D.n) {
-                        ((g_f32*)D.y)[r0 + i] = v;
+                    if (eng.l16 == 0 && r0 + i < Dc.n) {
+                        ((g_f32*)Dc.y)[r0 + i] = v;
                         if (ARGMAX) {
                             const uint64_t kk = argmax_key(v, r0 + i);
                             best = kk > best ? kk : best;
@@ -496,27 +502,33 @@ k_sweep(const PlanDesc* __restrict__ descs, int count, PlanDesc one, int64_t tot
                     }
                 }
             }
-            Cursor c2 = next_unit(D, cur, JB);
-            if (c2.d != cur.d && c2.d < n_desc) D = get(c2.d);
-            const bool more = c2.d < n_desc && owned(D, c2);
-            cur = c2;
-            return more;
+            if (took && threadIdx.x == 0) q_next[trans & 1] = n_static + (int)pending;
+            return r_next.valid;
         };
-        if (NB == 3) {
-            for (;;) {
-                if (!step(A, C)) break;
-                if (!step(B, A)) break;
-                if (!step(C, B)) break;
-            }
-        } else {
-            for (;;) {
-                if (!step(A, B)) break;
-                if (!step(B, A)) break;
-            }
+        R0.valid = true;
+        record(R0);
+        eng.issue(Dl, cl, B0);
+        advance_l();
+        R1.valid = have_l;
+        if (have_l) {
+            record(R1);
+            eng.issue(Dl, cl, B1);
+            advance_l();
+        }
+        for (;;) {
+            if (!half_step(R0, B0, R1)) break;
+            if (!half_step(R1, B1, R0)) break;
+        }
+    }
+    if (dyn && threadIdx.x == 0) {
+        __threadfence();  // this workgroup's grabs are complete
+        if (atomicAdd(&head->done, 1u) == gridDim.x - 1) {
+            atomicExch(&head->next, 0u);
+            atomicExch(&head->done, 0u);
         }
     }
     if (ARGMAX) {
-        __shared__ uint64_t sh[kThreads];
+        __shared__ uint64_t sh[kWaves];
         const uint64_t b = block_max_u64(best, sh);
         if (threadIdx.x == 0) keys[blockIdx.x] = b;
     }
@@ -524,7 +536,7 @@ k_sweep(const PlanDesc* __restrict__ descs, int count, PlanDesc one, int64_t tot
 
 __global__ void __launch_bounds__(kThreads) k_argmax_final(const uint64_t* __restrict__ keys,
                                                            int count, int32_t* __restrict__ token) {
-    __shared__ uint64_t sh[kThreads];
+    __shared__ uint64_t sh[kWaves];
     uint64_t best = 0;
     for (int i = threadIdx.x; i < count; i += kThreads) best = keys[i] > best ? keys[i] : best;
     const uint64_t b = block_max_u64(best, sh);
@@ -620,57 +632,58 @@ static PlanDesc single_desc(const uint8_t* w, const uint16_t* x, float* y, int64
     return d;
 }
 
-#ifndef Q4_SWEEP_COAL
-#define Q4_SWEEP_COAL 0
-#endif
+// The sweep engine for an activation stride.
 template <int XS>
-using SweepEngine = typename std::conditional<Q4_SWEEP_COAL != 0, CoalEngine<kR, kJB, XS>, Engine<kR, kJB, XS>>::type;
+using SweepEngine = DmaEngine<kR, kNB, XS>;
 
 template <int XS, bool AM>
-static hipError_t launch_sweep(const PlanDesc* descs, int count, const PlanDesc& one, int64_t total,
-                               int64_t max_k, int64_t max_steps, uint64_t* keys, int grid_cap,
-                               int* grid_out, hipStream_t s) {
+static hipError_t launch_sweep(const PlanDesc* descs, int count, SchedHead* head, const SchedChunk* chunks,
+                               const PlanDesc& one, int64_t total, int64_t max_k, int grid, uint64_t* keys,
+                               hipStream_t s) {
     using E = SweepEngine<XS>;
     const size_t xsb = x_lds_bytes(max_k);
-    const size_t lds = xsb + kWaves * (size_t)E::kWaveLds;
+    const size_t lds = xsb + (size_t)kWaves * E::kWaveLds;
     auto kern = k_sweep<E, kNB, XS, AM>;
     if (lds > 65536) {
         const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    int grid = (int)std::max<int64_t>(1, std::min<int64_t>(max_steps, (int64_t)device_cu_count() * kWgPerCu));
-    grid = std::min(grid, grid_cap);
-    if (grid_out) *grid_out = grid;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, s, descs, count, one, total, (int)xsb, keys);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, s, descs, count, head, chunks, one, total, (int)xsb,
+                       keys);
     return hipGetLastError();
 }
 
 template <bool AM>
-static hipError_t launch_any(const PlanDesc* descs, int count, const PlanDesc& one, int64_t total,
-                             int64_t max_k, int64_t max_steps, uint64_t* keys, int grid_cap, int* grid_out,
+static hipError_t launch_any(const PlanDesc* descs, int count, SchedHead* head, const SchedChunk* chunks,
+                             const PlanDesc& one, int64_t total, int64_t max_k, int grid, uint64_t* keys,
                              hipStream_t s) {
     if (fixed_stride(max_k))
-        return launch_sweep<kXStride, AM>(descs, count, one, total, max_k, max_steps, keys, grid_cap, grid_out, s);
-    return launch_sweep<0, AM>(descs, count, one, total, max_k, max_steps, keys, grid_cap, grid_out, s);
+        return launch_sweep<kXStride, AM>(descs, count, head, chunks, one, total, max_k, grid, keys, s);
+    return launch_sweep<0, AM>(descs, count, head, chunks, one, total, max_k, grid, keys, s);
+}
+
+// Workgroups for a static split of `steps` row steps.
+static int static_grid(int64_t steps, int cap) {
+    return (int)std::max<int64_t>(1, std::min<int64_t>({steps, (int64_t)device_cu_count() * kWgPerCu, (int64_t)cap}));
 }
 
 hipError_t launch_gemv(const uint8_t* w, const uint16_t* x, float* y, int64_t n, int64_t k,
                        hipStream_t s) {
     const PlanDesc d = single_desc(w, x, y, n, k);
-    return launch_any<false>(nullptr, 1, d, d.steps * d.npl, k, d.steps, nullptr, INT32_MAX, nullptr, s);
+    return launch_any<false>(nullptr, 1, nullptr, nullptr, d, d.steps * d.npl, k, static_grid(d.steps, INT32_MAX),
+                             nullptr, s);
 }
 
 int argmax_blocks(int64_t n, int64_t k) {
     (void)k;
-    const int64_t steps = (n + kRowsPerStep - 1) / kRowsPerStep;
-    return (int)std::min<int64_t>(steps, kArgmaxMaxBlocks);
+    return static_grid((n + kRowsPerStep - 1) / kRowsPerStep, kArgmaxMaxBlocks);
 }
 
 hipError_t launch_lm_head(const uint8_t* w, const uint16_t* h, float* logits, int32_t* token,
                           int64_t n, int64_t k, uint64_t* keys, hipStream_t s) {
     const PlanDesc d = single_desc(w, h, logits, n, k);
-    int grid = 0;
-    hipError_t e = launch_any<true>(nullptr, 1, d, d.steps * d.npl, k, d.steps, keys, argmax_blocks(n, k), &grid, s);
+    const int grid = argmax_blocks(n, k);
+    hipError_t e = launch_any<true>(nullptr, 1, nullptr, nullptr, d, d.steps * d.npl, k, grid, keys, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_argmax_final, dim3(1), dim3(kThreads), 0, s, keys, grid, token);
     return hipGetLastError();
@@ -684,11 +697,75 @@ hipError_t launch_gemm_generic(const uint8_t* w, const uint16_t* x, float* y, in
     return hipGetLastError();
 }
 
-hipError_t launch_gemv_batch(const PlanDesc* descs, int count, int64_t total_cost, int max_k,
-                             bool all_k1024, hipStream_t s) {
-    (void)all_k1024;
+// Schedule of a batch.  Row steps are taken in list order and grouped into
+// atoms of at least two units (a step of one unit, k <= 1024, is paired with
+// the next), so a chunk made of whole atoms has at least two units, as the
+// kernel's chunk-id hand-over requires.  The first `grid` chunks (one per
+// workgroup, assigned statically) cover about kStaticShare of the work in
+// equal parts; the rest is cut into chunks of about remaining / (3 * grid)
+// (guided self-scheduling), at least one atom each, which workgroups take
+// from the shared counter as they run out of work.  Depends only on the
+// shapes and the device's CU count.
+static constexpr double kStaticShare = 0.6;
+
+void build_schedule(PlanDesc* descs, int count, std::vector<SchedChunk>* out, int* grid_out) {
+    struct Atom {
+        int32_t d, s;
+        int64_t cost;  // start cost of its first step
+    };
+    std::vector<Atom> atoms;
+    int64_t total = 0;
+    int open_units = 2;  // units of the last atom
+    for (int i = 0; i < count; ++i) {
+        PlanDesc& p = descs[i];
+        p.npl = npl_of(p.k);
+        p.steps = (p.n + kRowsPerStep - 1) / kRowsPerStep;
+        p.cost_begin = total;
+        const int units = p.npl;  // one unit per 16 pairs of a row
+        for (int64_t st = 0; st < p.steps; ++st) {
+            if (open_units >= 2) {
+                atoms.push_back(Atom{i, (int32_t)st, total + st * p.npl});
+                open_units = 0;
+            }
+            open_units += units;
+        }
+        total += p.steps * p.npl;
+    }
+    if (open_units < 2 && atoms.size() > 1) atoms.pop_back();  // a lone one-unit step joins the atom before it
+    const int64_t n_atoms = (int64_t)atoms.size();
+    const int grid = static_grid(n_atoms, INT32_MAX);
+    out->clear();
+    int64_t a = 0;
+    auto cost_at = [&](int64_t i) { return i < n_atoms ? atoms[i].cost : total; };
+    for (int g = 0; g < grid; ++g) {
+        out->push_back(SchedChunk{atoms[a].d, atoms[a].s, 0});
+        const int64_t end = (int64_t)(kStaticShare * (double)total * (g + 1) / grid);
+        ++a;
+        while (n_atoms - a > grid - 1 - g && cost_at(a) < end) ++a;
+    }
+    while (a < n_atoms) {
+        out->push_back(SchedChunk{atoms[a].d, atoms[a].s, 0});
+        const int64_t size = std::max<int64_t>(1, (total - cost_at(a) + 3 * grid - 1) / (3 * grid));
+        const int64_t end = cost_at(a) + size;
+        ++a;
+        while (a < n_atoms && cost_at(a) < end) ++a;
+    }
+    for (size_t i = 0; i + 1 < out->size(); ++i) {
+        const SchedChunk& nx = (*out)[i + 1];
+        (*out)[i].c_end = descs[nx.d0].cost_begin + (int64_t)nx.s0 * descs[nx.d0].npl;
+    }
+    out->back().c_end = total;
+    *grid_out = grid;
+}
+
+hipError_t launch_gemv_batch(const void* plan, int count, int nchunks, int grid, int max_k, hipStream_t s) {
+    (void)nchunks;
+    const uint8_t* base = static_cast<const uint8_t*>(plan);
+    SchedHead* head = (SchedHead*)base;
+    const PlanDesc* descs = (const PlanDesc*)(base + sizeof(SchedHead));
+    const SchedChunk* chunks = (const SchedChunk*)(base + sizeof(SchedHead) + (size_t)count * sizeof(PlanDesc));
     PlanDesc none = {};
-    return launch_any<false>(descs, count, none, total_cost, max_k, INT64_MAX, nullptr, INT32_MAX, nullptr, s);
+    return launch_any<false>(descs, count, head, chunks, none, 0, max_k, grid, nullptr, s);
 }
 
 }  // namespace q4

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <vector>
+
 namespace q4 {
 
 // Device-resident descriptor of one GEMV inside a batch plan.
@@ -19,6 +21,30 @@ struct PlanDesc {
     int64_t steps;       // row steps of kBatchRows rows
     int64_t cost_begin;  // sum of steps*npl over the earlier descriptors
 };
+
+// Head of a batch plan's schedule (device memory, first bytes of the plan).
+// `next` and `done` are zero between launches: a launch hands out chunks
+// grid, grid+1, ... through `next`, counts finished workgroups in `done`, and
+// its last workgroup sets both back to zero.
+struct SchedHead {
+    uint32_t next;
+    uint32_t done;
+    int32_t nchunks;
+    int32_t grid;
+};
+
+// One chunk of a batch schedule: the row steps from step s0 of descriptor d0
+// on, in list order, that start before cost c_end.
+struct SchedChunk {
+    int32_t d0;
+    int32_t s0;
+    int64_t c_end;
+};
+
+// Fills npl, steps and cost_begin of descs[0..count) and cuts the list into
+// chunks for the current device; *grid is the launch's workgroup count (the
+// number of chunks assigned statically).
+void build_schedule(PlanDesc* descs, int count, std::vector<SchedChunk>* out, int* grid);
 
 // Rows one workgroup step covers in the batch kernel (4 waves x 4 rows x R).
 int batch_rows_per_step();
@@ -44,7 +70,7 @@ hipError_t launch_gemm_prefill(const uint8_t* w, const uint16_t* x, float* y, in
 int argmax_blocks(int64_t n, int64_t k);
 hipError_t launch_lm_head(const uint8_t* w, const uint16_t* h, float* logits, int32_t* token,
                           int64_t n, int64_t k, uint64_t* keys, hipStream_t s);
-hipError_t launch_gemv_batch(const PlanDesc* descs, int count, int64_t total_cost, int max_k,
-                             bool all_k1024, hipStream_t s);
+// `plan`: SchedHead, then `count` PlanDesc, then `nchunks` SchedChunk.
+hipError_t launch_gemv_batch(const void* plan, int count, int nchunks, int grid, int max_k, hipStream_t s);
 
 }  // namespace q4

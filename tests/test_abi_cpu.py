@@ -111,9 +111,13 @@ def test_batch_plan_validation(lib):
     D = q4.GemvDesc
     plan = q4.GemvPlan()
     buf = FAKE * 64
-    arr = (D * 2)(D(FAKE, FAKE * 2, FAKE * 4, 8, 64), D(FAKE * 8, FAKE * 2, FAKE * 4 + 16, 8, 64))
-    nbytes = lib.q4_0_gemv_batch_plan_bytes(2)
+    good = (D * 2)(D(FAKE, FAKE * 2, FAKE * 4, 8, 64), D(FAKE * 8, FAKE * 2, FAKE * 6, 8, 64))
+    nbytes = lib.q4_0_gemv_batch_plan_bytes(good, 2)
     assert nbytes > 0
+    # a list the plan would refuse has no size
+    arr = (D * 2)(D(FAKE, FAKE * 2, FAKE * 4, 8, 64), D(FAKE * 8, FAKE * 2, FAKE * 4 + 16, 8, 64))
+    assert lib.q4_0_gemv_batch_plan_bytes(arr, 2) == 0
+    assert lib.q4_0_gemv_batch_plan_bytes(None, 2) == 0
     # the two outputs overlap
     assert lib.q4_0_gemv_batch_plan(arr, 2, buf, nbytes, ctypes.byref(plan), None) == q4.Q4_ERR_INVALID_ARG
     # k not a multiple of 64
@@ -125,5 +129,7 @@ def test_batch_plan_validation(lib):
     assert lib.q4_0_gemv_batch_plan(arr, 0, buf, nbytes, ctypes.byref(plan), None) == q4.Q4_ERR_INVALID_ARG
     arr = (D * 2)(D(FAKE, FAKE * 2, FAKE * 4, 8, 64), D(FAKE * 8, FAKE * 4, FAKE * 6, 8, 64))
     assert lib.q4_0_gemv_batch_plan(arr, 2, buf, nbytes, ctypes.byref(plan), None) == q4.Q4_ERR_INVALID_ARG
+    # the plan buffer overlapping a tensor
+    assert lib.q4_0_gemv_batch_plan(good, 2, FAKE * 8, nbytes, ctypes.byref(plan), None) == q4.Q4_ERR_INVALID_ARG
     # an unfilled plan is refused
     assert lib.q4_0_gemv_batch(ctypes.byref(q4.GemvPlan()), None) == q4.Q4_ERR_INVALID_ARG

@@ -39,6 +39,70 @@ def test_mixed_list_matches_single_gemv_and_oracle():
         assert torch.equal(b, it[2])
 
 
+def _read_plan(batch):
+    """Head, descriptors and chunk schedule of a plan, read back from the device."""
+    raw = batch.buffer.cpu().numpy()
+    nxt, done, nchunks, grid = np.frombuffer(raw[:16].tobytes(), dtype=np.int32)
+    count = batch.plan.count
+    desc_t = np.dtype([("w", "<u8"), ("x", "<u8"), ("y", "<u8"), ("n", "<i8"), ("k", "<i4"), ("npl", "<i4"),
+                       ("steps", "<i8"), ("cost_begin", "<i8")])
+    chunk_t = np.dtype([("d0", "<i4"), ("s0", "<i4"), ("c_end", "<i8")])
+    descs = np.frombuffer(raw[16:16 + count * desc_t.itemsize].tobytes(), dtype=desc_t)
+    off = 16 + count * desc_t.itemsize
+    chunks = np.frombuffer(raw[off:off + nchunks * chunk_t.itemsize].tobytes(), dtype=chunk_t)
+    return int(nxt), int(done), int(nchunks), int(grid), descs, chunks
+
+
+def test_schedule_partitions_the_row_steps():
+    """The plan's chunks cover every row step once, in list order; every chunk
+    but the last holds at least two units (pairs-per-lane steps); the counters
+    are zero after planning and again after every launch."""
+    q4 = lib()
+    shapes = [(5, 64), (100, 5120), (33, 1088), (1, 17408), (257, 2048), (64, 1024), (31, 17408), (2000, 320),
+              (64, 64), (70, 1024), (1, 64)]
+    items = []
+    for i, (n, k) in enumerate(shapes):
+        items.append((dev_u8(synth.q4_0(SEED, 7000 + i, n, k)), dev_f16(synth.f16_normal(SEED, 7100 + i, k)),
+                      torch.empty(n, dtype=torch.float32, device=device())))
+    batch = q4.GemvBatch(items)
+    nxt, done, nchunks, grid, descs, chunks = _read_plan(batch)
+    assert (nxt, done) == (0, 0)
+    assert nchunks == batch.plan.nchunks and grid == batch.plan.grid and 1 <= grid <= nchunks
+    # the plan's row steps: every descriptor's step count fits one rows-per-step value
+    fits = [r for r in range(1, 2049)
+            if all(int(d["steps"]) == -(-n // r) for (n, _), d in zip(shapes, descs))]
+    assert fits, "no common rows-per-step"
+    starts, units = [], []
+    cost = 0
+    for (n, k), d in zip(shapes, descs):
+        npl = -(-(k // 64) // 16)
+        assert int(d["npl"]) == npl and int(d["cost_begin"]) == cost
+        for st in range(int(d["steps"])):
+            starts.append(cost + st * npl)
+            units.append(npl)
+        cost += int(d["steps"]) * npl
+    starts = np.array(starts)
+    units = np.array(units)
+    begin = [int(descs["cost_begin"][c["d0"]]) + int(c["s0"]) * int(descs["npl"][c["d0"]]) for c in chunks]
+    assert begin[0] == 0
+    ends = [int(c["c_end"]) for c in chunks]
+    assert ends[-1] == cost
+    for i in range(nchunks):
+        assert begin[i] < ends[i]
+        if i + 1 < nchunks:
+            assert ends[i] == begin[i + 1]
+        assert begin[i] in set(starts.tolist())
+        u = int(units[(starts >= begin[i]) & (starts < ends[i])].sum())
+        assert u >= 2 or i == nchunks - 1, (i, u)
+    for _ in range(3):
+        batch()
+    torch.cuda.synchronize()
+    nxt, done, *_ = _read_plan(batch)
+    assert (nxt, done) == (0, 0)
+    for (wd, xd, yd) in items:
+        assert torch.equal(yd, q4.q4_0_gemv(wd, xd))
+
+
 def test_full_decode_sweep_sampled():
     """All 448 GEMVs of the 64-layer sweep (13.4 GB of weights) in one launch;
     every GEMV checked on 6 sampled rows against the oracle."""
