@@ -207,6 +207,45 @@ Q4_API q4_status q4_0_gemv_batch_plan(const q4_gemv_desc* descs, int count, void
  * results do not depend on how the chunks were handed out. */
 Q4_API q4_status q4_0_gemv_batch(const q4_gemv_plan* plan, void* stream);
 
+/* Host-side handle of a small-M batch plan.  Filled by
+ * q4_0_gemm_smallm_batch_plan; plain data, may be copied. */
+typedef struct q4_gemm_plan {
+    void* device;            /* the caller's device buffer holding the descriptors */
+    int count;               /* number of GEMMs */
+    int m;                   /* activation rows of every GEMM */
+    int max_p;               /* internal: longest K-range in block pairs */
+    int flags;               /* internal: bit 0 = some GEMM splits K */
+    int64_t total_cost;      /* internal: work units of the list */
+    int64_t max_mn;          /* internal: largest m * n */
+    size_t workspace_bytes;  /* device workspace q4_0_gemm_smallm_batch needs (may be 0) */
+} q4_gemm_plan;
+
+/* Device bytes q4_0_gemm_smallm_batch_plan needs for `count` descriptors. */
+Q4_API size_t q4_0_gemm_smallm_batch_plan_bytes(int count);
+
+/*
+ * A list of small-M GEMMs with the same m, run as one launch: the verify pass
+ * of a speculative draft over a whole layer stack, one submit per token
+ * (aipolix.com en-us page, sections "Speculation is used to amortize network
+ * round trips" and "One submit per token").  Descriptor i names w (n rows of
+ * k/32 Q4_0 blocks, 4-byte aligned), x (m x k binary16, 16-byte aligned) and
+ * y (m x n binary32, written); every k % 64 == 0, 2 <= m <= 16, |d| <= 8188.
+ * Each GEMM's result is bit-identical to q4_0_gemm_smallm on the same
+ * operands.  Validates the list, writes its device form into `plan_buf`
+ * (q4_0_gemm_smallm_batch_plan_bytes(count) bytes, 16-byte aligned) and
+ * fills `*plan`; the copy has completed when this returns (it synchronizes
+ * `stream`).  No output may overlap another output, an input or the plan.
+ */
+Q4_API q4_status q4_0_gemm_smallm_batch_plan(const q4_gemv_desc* descs, int count, int64_t m, void* plan_buf,
+                                             size_t plan_bytes, q4_gemm_plan* plan, void* stream);
+
+/* Run every GEMM of a small-M plan on `stream`: one launch, plus one that
+ * adds K-range partial sums when plan->flags says some GEMM splits K.
+ * `workspace`: plan->workspace_bytes of device memory, 16-byte aligned, not
+ * overlapping the plan's tensors (NULL when that is 0). */
+Q4_API q4_status q4_0_gemm_smallm_batch(const q4_gemm_plan* plan, void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

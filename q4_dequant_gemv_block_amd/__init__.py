@@ -36,6 +36,7 @@ Q4_OP_LM_HEAD_ARGMAX = 3
 EXPORTS = (
     "q4_abi_version", "q4_last_error", "q4_workspace_bytes", "q4_0_gemv", "q4_0_gemm_smallm",
     "q4_0_gemm_prefill", "lm_head_argmax", "q4_0_gemv_batch_plan_bytes", "q4_0_gemv_batch_plan",
+    "q4_0_gemm_smallm_batch_plan_bytes", "q4_0_gemm_smallm_batch_plan", "q4_0_gemm_smallm_batch",
     "q4_0_gemv_batch",
 )
 
@@ -89,6 +90,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                          ctypes.POINTER(GemvPlan), vp]
     lib.q4_0_gemv_batch.restype = st
     lib.q4_0_gemv_batch.argtypes = [ctypes.POINTER(GemvPlan), vp]
+    lib.q4_0_gemm_smallm_batch_plan_bytes.restype = ctypes.c_size_t
+    lib.q4_0_gemm_smallm_batch_plan_bytes.argtypes = [ctypes.c_int]
+    lib.q4_0_gemm_smallm_batch_plan.restype = st
+    lib.q4_0_gemm_smallm_batch_plan.argtypes = [ctypes.POINTER(GemvDesc), ctypes.c_int, i64, vp, ctypes.c_size_t,
+                                                ctypes.POINTER(GemmPlan), vp]
+    lib.q4_0_gemm_smallm_batch.restype = st
+    lib.q4_0_gemm_smallm_batch.argtypes = [ctypes.POINTER(GemmPlan), vp, ctypes.c_size_t, vp]
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -222,6 +230,12 @@ def lm_head_argmax(w: torch.Tensor, h: torch.Tensor, logits: torch.Tensor | None
     return logits, token
 
 
+class GemmPlan(ctypes.Structure):
+    _fields_ = [("device", ctypes.c_void_p), ("count", ctypes.c_int), ("m", ctypes.c_int),
+                ("max_p", ctypes.c_int), ("flags", ctypes.c_int), ("total_cost", ctypes.c_int64),
+                ("max_mn", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
+
+
 class GemvBatch:
     """A list of independent GEMVs (w, x, y) planned once and run as one launch per call."""
 
@@ -250,6 +264,45 @@ class GemvBatch:
 
     def __call__(self, stream=None):
         _check(load_library().q4_0_gemv_batch(ctypes.byref(self.plan), _stream(stream)))
+
+
+class SmallMBatch:
+    """A list of small-M GEMMs (w, x, y) with x of shape (m, k) and y (m, n), the
+    same m for all, planned once and run as one launch (plus one reduction of
+    K-range partials when some GEMM splits K) per call."""
+
+    def __init__(self, items, stream=None):
+        items = list(items)
+        if not items:
+            raise ValueError("empty list")
+        m = items[0][1].shape[0] if items[0][1].dim() == 2 else 1
+        descs = (GemvDesc * len(items))()
+        self._keep = []
+        for i, (w, x, y) in enumerate(items):
+            if x.dim() != 2 or x.shape[0] != m:
+                raise ValueError("descriptor %d: x must be (m, k) with m = %d" % (i, m))
+            k = x.shape[1]
+            n = _weights(w, k)
+            if y.numel() != m * n:
+                raise ValueError("descriptor %d: y must hold m*N=%d floats" % (i, m * n))
+            descs[i] = GemvDesc(_ptr(w, torch.uint8, "w"), _ptr(x, torch.float16, "x"),
+                                _ptr(y, torch.float32, "y"), n, k)
+            self._keep.append((w, x, y))
+        lib = load_library()
+        dev = items[0][0].device
+        self.m = m
+        self.plan = GemmPlan()
+        with torch.cuda.device(dev):
+            nbytes = int(lib.q4_0_gemm_smallm_batch_plan_bytes(len(items)))
+            self.buffer = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+            _check(lib.q4_0_gemm_smallm_batch_plan(descs, len(items), m, self.buffer.data_ptr(),
+                                                   self.buffer.numel(), ctypes.byref(self.plan),
+                                                   _stream(stream)))
+            self.workspace = torch.empty(max(int(self.plan.workspace_bytes), 16), dtype=torch.uint8, device=dev)
+
+    def __call__(self, stream=None):
+        _check(load_library().q4_0_gemm_smallm_batch(ctypes.byref(self.plan), self.workspace.data_ptr(),
+                                                     self.workspace.numel(), _stream(stream)))
 
 
 # Short names.

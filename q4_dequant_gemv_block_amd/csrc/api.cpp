@@ -93,6 +93,7 @@ size_t q4_workspace_bytes(int op, int64_t m, int64_t n, int64_t k) {
         case Q4_OP_GEMM_SMALLM:
             // only the matrix-core path (2 <= m <= 16, k % 64 == 0) splits K
             if (m < 2 || m > 16 || n < 1 || k < 64 || k % 64 != 0 || k > kMaxK || n > kMaxN) return 0;
+            // (with w not 4-byte aligned the call takes the generic kernel and ignores the workspace)
             return q4::smallm_workspace_bytes(m, n, k);
         case Q4_OP_LM_HEAD_ARGMAX:
             if (n < 1 || k < 32) return 0;
@@ -136,12 +137,12 @@ q4_status q4_0_gemm_smallm(const void* w, const void* x, float* y, int64_t m, in
     const uint8_t* wb = static_cast<const uint8_t*>(w);
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     hipError_t e;
-    if (!fast_path(w, k))
-        e = q4::launch_gemm_generic(wb, xb, y, m, n, k, s);
-    else if (m == 1)
+    if (m == 1 && fast_path(w, k))
         e = q4::launch_gemv(wb, xb, y, n, k, s);
-    else
+    else if (m >= 2 && k % 64 == 0 && aligned(w, 4))
         e = q4::launch_gemm_smallm(wb, xb, y, m, n, k, static_cast<float*>(workspace), s);
+    else
+        e = q4::launch_gemm_generic(wb, xb, y, m, n, k, s);
     return hip_status(e, "q4_0_gemm_smallm launch");
 }
 
@@ -196,35 +197,29 @@ q4_status lm_head_argmax(const void* w, const void* h, float* logits, int32_t* t
 
 namespace {
 
-// Validates a descriptor list and lays out its plan: device descriptors,
-// chunk schedule and launch grid.
-q4_status plan_layout(const char* fn, const q4_gemv_desc* descs, int count, std::vector<q4::PlanDesc>* dev,
-                      std::vector<q4::SchedChunk>* chunks, int* grid, int* max_k_out) {
+// Validates a descriptor list whose x are m x k and y m x n: shapes,
+// alignment, k % 64 == 0 (and k <= k_max), no output overlapping another
+// output or any input.  *max_k_out: the largest k.
+q4_status check_list(const char* fn, const q4_gemv_desc* descs, int count, int64_t m, int64_t m_max, int64_t k_max,
+                     int* max_k_out) {
     if (!descs) return fail(Q4_ERR_INVALID_ARG, "%s: null descriptor list", fn);
     if (count < 1 || count > (1 << 20)) return fail(Q4_ERR_INVALID_ARG, "%s: count = %d outside [1, 1<<20]", fn, count);
-    dev->assign(count, q4::PlanDesc{});
     std::vector<Range> outs, ins;
     outs.reserve(count);
     ins.reserve(2 * (size_t)count);
     int max_k = 0;
     for (int i = 0; i < count; ++i) {
         const q4_gemv_desc& d = descs[i];
-        q4_status st = check_shape(fn, 1, 1, d.n, d.k);
+        q4_status st = check_shape(fn, m, m_max, d.n, d.k);
         if (st) return fail(st, "%s: descriptor %d: %s", fn, i, std::string(g_err).c_str());
-        if (d.k % 64 != 0 || d.k > q4::kFastMaxK)
-            return fail(Q4_ERR_INVALID_ARG, "%s: descriptor %d: k must be a multiple of 64 up to %lld", fn, i, (long long)q4::kFastMaxK);
-        st = check_tensors(fn, d.w, d.x, d.y, 1, d.n, d.k, (size_t)d.n * 4);
+        if (d.k % 64 != 0 || d.k > k_max)
+            return fail(Q4_ERR_INVALID_ARG, "%s: descriptor %d: k must be a multiple of 64 up to %lld", fn, i, (long long)k_max);
+        st = check_tensors(fn, d.w, d.x, d.y, m, d.n, d.k, (size_t)(m * d.n) * 4);
         if (st) return fail(st, "%s: descriptor %d: %s", fn, i, std::string(g_err).c_str());
-        q4::PlanDesc& p = (*dev)[i];
-        p.w = static_cast<const uint8_t*>(d.w);
-        p.x = static_cast<const uint16_t*>(d.x);
-        p.y = d.y;
-        p.n = d.n;
-        p.k = (int32_t)d.k;
         max_k = std::max<int>(max_k, (int)d.k);
-        outs.push_back(range(d.y, (size_t)d.n * 4));
+        outs.push_back(range(d.y, (size_t)(m * d.n) * 4));
         ins.push_back(range(d.w, (size_t)(d.n * row_bytes(d.k))));
-        ins.push_back(range(d.x, (size_t)d.k * 2));
+        ins.push_back(range(d.x, (size_t)(m * d.k) * 2));
     }
     std::sort(outs.begin(), outs.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
     for (size_t i = 1; i < outs.size(); ++i)
@@ -234,8 +229,39 @@ q4_status plan_layout(const char* fn, const q4_gemv_desc* descs, int count, std:
         if (it != outs.end() && overlap(*it, r)) return fail(Q4_ERR_INVALID_ARG, "%s: an output overlaps an input", fn);
         if (it != outs.begin() && overlap(*(it - 1), r)) return fail(Q4_ERR_INVALID_ARG, "%s: an output overlaps an input", fn);
     }
-    q4::build_schedule(dev->data(), count, chunks, grid);
     *max_k_out = max_k;
+    return ok();
+}
+
+// A device buffer that must not overlap any tensor of the list.
+q4_status check_buffer(const char* fn, const char* what, const void* buf, size_t bytes, const q4_gemv_desc* descs,
+                       int count, int64_t m) {
+    const Range rb = range(buf, bytes);
+    for (int i = 0; i < count; ++i) {
+        const q4_gemv_desc& d = descs[i];
+        if (overlap(rb, range(d.y, (size_t)(m * d.n) * 4)) || overlap(rb, range(d.w, (size_t)(d.n * row_bytes(d.k)))) ||
+            overlap(rb, range(d.x, (size_t)(m * d.k) * 2)))
+            return fail(Q4_ERR_INVALID_ARG, "%s: %s overlaps a tensor of descriptor %d", fn, what, i);
+    }
+    return Q4_OK;
+}
+
+// Validates a GEMV list and lays out its plan: device descriptors, chunk
+// schedule and launch grid.
+q4_status plan_layout(const char* fn, const q4_gemv_desc* descs, int count, std::vector<q4::PlanDesc>* dev,
+                      std::vector<q4::SchedChunk>* chunks, int* grid, int* max_k_out) {
+    const q4_status st = check_list(fn, descs, count, 1, 1, q4::kFastMaxK, max_k_out);
+    if (st) return st;
+    dev->assign(count, q4::PlanDesc{});
+    for (int i = 0; i < count; ++i) {
+        q4::PlanDesc& p = (*dev)[i];
+        p.w = static_cast<const uint8_t*>(descs[i].w);
+        p.x = static_cast<const uint16_t*>(descs[i].x);
+        p.y = descs[i].y;
+        p.n = descs[i].n;
+        p.k = (int32_t)descs[i].k;
+    }
+    q4::build_schedule(dev->data(), count, chunks, grid);
     return ok();
 }
 
@@ -268,13 +294,7 @@ q4_status q4_0_gemv_batch_plan(const q4_gemv_desc* descs, int count, void* plan_
     const size_t need = plan_size(count, chunks.size());
     if (plan_bytes < need) return fail(Q4_ERR_WORKSPACE, "%s: plan buffer of %zu bytes needed", fn, need);
     if (!aligned(plan_buf, 16)) return fail(Q4_ERR_MISALIGNED, "%s: plan buffer must be 16-byte aligned", fn);
-    const Range rp = range(plan_buf, need);
-    for (int i = 0; i < count; ++i) {
-        const q4_gemv_desc& d = descs[i];
-        if (overlap(rp, range(d.y, (size_t)d.n * 4)) || overlap(rp, range(d.w, (size_t)(d.n * row_bytes(d.k)))) ||
-            overlap(rp, range(d.x, (size_t)d.k * 2)))
-            return fail(Q4_ERR_INVALID_ARG, "%s: plan buffer overlaps a tensor of descriptor %d", fn, i);
-    }
+    if (check_buffer(fn, "plan buffer", plan_buf, need, descs, count, 1)) return Q4_ERR_INVALID_ARG;
     std::vector<uint8_t> host(need);
     q4::SchedHead head = {0u, 0u, (int32_t)chunks.size(), (int32_t)grid};
     std::memcpy(host.data(), &head, sizeof(head));
@@ -301,6 +321,73 @@ q4_status q4_0_gemv_batch(const q4_gemv_plan* plan, void* stream) {
     const hipError_t e = q4::launch_gemv_batch(plan->device, plan->count, plan->nchunks, plan->grid, plan->max_k,
                                                static_cast<hipStream_t>(stream));
     return hip_status(e, "q4_0_gemv_batch launch");
+}
+
+size_t q4_0_gemm_smallm_batch_plan_bytes(int count) {
+    if (count < 1 || count > (1 << 20)) return 0;
+    return (size_t)count * sizeof(q4::SmDesc);
+}
+
+q4_status q4_0_gemm_smallm_batch_plan(const q4_gemv_desc* descs, int count, int64_t m, void* plan_buf,
+                                      size_t plan_bytes, q4_gemm_plan* plan, void* stream) {
+    const char* fn = "q4_0_gemm_smallm_batch_plan";
+    if (!plan || !plan_buf) return fail(Q4_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (m < 2 || m > 16) return fail(Q4_ERR_INVALID_ARG, "%s: m = %lld outside [2, 16]", fn, (long long)m);
+    int max_k = 0;
+    q4_status st = check_list(fn, descs, count, m, 16, kMaxK, &max_k);
+    if (st) return st;
+    const size_t need = q4_0_gemm_smallm_batch_plan_bytes(count);
+    if (plan_bytes < need) return fail(Q4_ERR_WORKSPACE, "%s: plan buffer of %zu bytes needed", fn, need);
+    if (!aligned(plan_buf, 16)) return fail(Q4_ERR_MISALIGNED, "%s: plan buffer must be 16-byte aligned", fn);
+    if (check_buffer(fn, "plan buffer", plan_buf, need, descs, count, m)) return Q4_ERR_INVALID_ARG;
+    for (int i = 0; i < count; ++i)
+        if (!aligned(descs[i].w, 4)) return fail(Q4_ERR_MISALIGNED, "%s: descriptor %d: w must be 4-byte aligned", fn, i);
+    std::vector<q4::SmDesc> dev(count);
+    int64_t ws = 0, cost = 0, max_mn = 0;
+    int max_p = 0;
+    bool split = false;
+    for (int i = 0; i < count; ++i) {
+        q4::SmDesc& d = dev[i];
+        d.w = static_cast<const uint8_t*>(descs[i].w);
+        d.x = static_cast<const uint16_t*>(descs[i].x);
+        d.y = descs[i].y;
+        d.n = descs[i].n;
+        d.k = (int32_t)descs[i].k;
+        ws += q4::smallm_fill(&d, m, ws, cost);
+        cost += q4::smallm_cost(d);
+        max_p = std::max(max_p, (int)d.P);
+        max_mn = std::max(max_mn, m * d.n);
+        split = split || d.nranges > 1;
+    }
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(plan_buf, dev.data(), need, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_status(e, "q4_0_gemm_smallm_batch_plan copy");
+    plan->device = plan_buf;
+    plan->count = count;
+    plan->m = (int)m;
+    plan->max_p = max_p;
+    plan->flags = split ? 1 : 0;
+    plan->total_cost = cost;
+    plan->max_mn = max_mn;
+    plan->workspace_bytes = (size_t)ws * sizeof(float);
+    return ok();
+}
+
+q4_status q4_0_gemm_smallm_batch(const q4_gemm_plan* plan, void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "q4_0_gemm_smallm_batch";
+    if (!plan || !plan->device) return fail(Q4_ERR_INVALID_ARG, "%s: null plan", fn);
+    if (plan->count < 1 || plan->m < 2 || plan->m > 16 || plan->total_cost < 1 || plan->max_p < 16)
+        return fail(Q4_ERR_INVALID_ARG, "%s: plan was not filled by q4_0_gemm_smallm_batch_plan", fn);
+    if (plan->workspace_bytes) {
+        if (!workspace || workspace_bytes < plan->workspace_bytes)
+            return fail(Q4_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, plan->workspace_bytes);
+        if (!aligned(workspace, 16)) return fail(Q4_ERR_MISALIGNED, "%s: workspace must be 16-byte aligned", fn);
+    }
+    const hipError_t e = q4::launch_gemm_smallm_batch(
+        static_cast<const q4::SmDesc*>(plan->device), plan->count, plan->m, plan->total_cost, plan->max_p,
+        plan->max_mn, (plan->flags & 1) != 0, static_cast<float*>(workspace), static_cast<hipStream_t>(stream));
+    return hip_status(e, "q4_0_gemm_smallm_batch launch");
 }
 
 }  // extern "C"

@@ -61,10 +61,33 @@ hipError_t launch_gemv(const uint8_t* w, const uint16_t* x, float* y, int64_t n,
                        hipStream_t s);
 hipError_t launch_gemm_generic(const uint8_t* w, const uint16_t* x, float* y, int64_t m,
                                int64_t n, int64_t k, hipStream_t s);
-void smallm_split(int64_t n, int64_t k, int* splits, int* cps);
+// One GEMM of a small-M list (device memory, or by value for a single GEMM).
+// The fields after k are derived by smallm_fill.
+struct SmDesc {
+    const uint8_t* w;
+    const uint16_t* x;   // m x k
+    float* y;            // m x n
+    int64_t n;
+    int32_t k;
+    int32_t np;          // pairs per row (k / 64)
+    int32_t P;           // pairs per K-range (a multiple of 16)
+    int32_t nranges;     // K-ranges
+    int32_t tiles;       // tiles of 256 rows
+    int32_t pad;
+    int64_t ws_off;      // first partial-sum float in the workspace (nranges > 1)
+    int64_t cost_begin;  // units of the earlier descriptors
+};
+
+// Fills np, P, nranges, tiles, ws_off and cost_begin; returns the workspace
+// floats the descriptor's partial sums take (0 with a single K-range).
+int64_t smallm_fill(SmDesc* d, int64_t m, int64_t ws_off, int64_t cost_begin);
+int64_t smallm_cost(const SmDesc& d);
 size_t smallm_workspace_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm_smallm(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
                               int64_t k, float* workspace, hipStream_t s);
+// descs: `count` filled descriptors in device memory; total: sum of their costs.
+hipError_t launch_gemm_smallm_batch(const SmDesc* descs, int count, int64_t m, int64_t total, int max_p,
+                                    int64_t max_mn, bool any_split, float* workspace, hipStream_t s);
 hipError_t launch_gemm_prefill(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
                                int64_t k, hipStream_t s);
 int argmax_blocks(int64_t n, int64_t k);

@@ -1,4 +1,5 @@
-// Small-M Q4_0 GEMM: Y[m][n] = sum_k w[n][k] X[m][k] for 2 <= M <= 16.
+// Small-M Q4_0 GEMM: Y[m][n] = sum_k w[n][k] X[m][k] for 2 <= M <= 16, for
+// one GEMM or a list of GEMMs in one launch.
 //
 // The batched pass that verifies speculative drafts, and 16-token prefill
 // chunks ("SwarmLLM v0.2.0 ..." on aipolix.com, section "Speculation is used to
@@ -8,28 +9,33 @@
 //
 // With up to 16 activation rows this is a dense contraction, so the products
 // run on the matrix cores (v_mfma_f32_16x16x32_f16): the vector ALUs only
-// expand the weights, at the same cost per weight as the M = 1 kernel,
-// whatever M is.  (A vector-ALU version with one v_dot2 chain per activation
-// row was measured at 1.8 TB/s for M = 2 down to 0.4 TB/s for M = 16 on the
-// 64-layer sweep, bound by its LDS reads.)
+// expand and scale the weights, at the same cost per weight as the M = 1
+// kernel, whatever M is.  (A vector-ALU version with one v_dot2 chain per
+// activation row was measured at 1.8 TB/s for M = 2 down to 0.4 TB/s for
+// M = 16, bound by its LDS reads.)
 //
-// Work split: a workgroup owns 64 weight rows (16 per wave) and one K-range of
-// at most kMaxChunks chunks of 1024 columns.  It stages the activations of
-// that K-range for all 16 rows once into LDS (chunk order of q4_device.h,
-// zero beyond M), then streams its weight rows.  When K is split over S
-// ranges each range writes a partial product to the workspace and a second
-// kernel adds the S partials in a fixed order, so results are deterministic.
-// S is chosen from the shape alone so that the grid has enough workgroups.
+// Work: a workgroup of 16 waves owns a tile of 256 weight rows (16 per wave)
+// and one K-range of its GEMM; the K-range is the longest run of 16-pair
+// segments whose activations for all M rows fit kXBytes of LDS, so K is split
+// only for large M and K (M = 16: 4096 columns).  Items (GEMM, K-range, tile)
+// are ordered GEMM, K-range, tile, and every workgroup takes a byte-balanced
+// contiguous run of them, so the activations of a K-range are staged once and
+// serve many tiles.  When a GEMM has several K-ranges each range writes its
+// partial product to the workspace and a second kernel adds the partials in
+// range order, so results are deterministic.
 //
-// Lane (g, n) = (lane / 16, lane % 16) of a wave reads block pairs g, g+4,
-// g+8, g+12 of each 16-pair chunk of weight row n (4 lanes cover 144
-// contiguous bytes).  Each pair expands to 8 chunks of 8 halves ((code - 8) * d
-// rounded once to f16: error <= 2^-11 of each weight, inside the 1e-3 bound);
-// chunk c of lane (g, n) is the B operand for weight row n, and the A operand
-// of lane (g, m) is chunk c of the same pair of activation row m.  The 32 k of
-// one MFMA are 8 k from each of 4 pairs; both operands use the same
-// assignment, so the sum is the full dot product.  Rows beyond N and pairs
-// beyond K/64 read clamped in-range addresses and meet zero activations.
+// A wave's unit is its 16 rows x one 16-pair segment.  Lane (g, n) = (lane /
+// 16, lane % 16) loads pairs g, g+4, g+8, g+12 of the segment of weight row n
+// (the four lanes of a row cover its 576 contiguous bytes) into registers; the
+// loads of the next unit are issued before the current one is computed, also
+// across tiles, K-ranges and GEMMs.  Each pair expands to 8 chunks of 8 halves
+// ((code - 8) * d rounded once to f16: error <= 2^-11 of each weight, inside
+// the 1e-3 bound); chunk c of lane (g, n) is the B operand for weight row n,
+// and the A operand of lane (g, m) is chunk c of the same pair of activation
+// row m, read from LDS (rows m >= M are zero).  The 32 k of one MFMA are 8 k
+// from each of 4 pairs; both operands use the same assignment, so the sum is
+// the full dot product.  Rows beyond N and pairs beyond K/64 read clamped
+// in-range addresses and meet zero activations.
 #include "q4_device.h"
 #include "q4_launch.h"
 
@@ -43,24 +49,44 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) float g_f32;
 
-constexpr int kSmThreads = 256;        // 4 waves x 16 rows
-constexpr int kSmRows = 64;
-constexpr int kPC = 16;                // pairs per chunk (1024 columns)
-constexpr int kPairsPerLane = 4;       // pairs g, g+4, g+8, g+12 of a chunk
-constexpr int kChunkU4 = kPC * 8 * 16; // u4 entries of one chunk: [pair][chunk][m]
-constexpr int kMaxChunks = 2;          // chunks per K-range (64 KiB of activations)
+constexpr int kSmWaves = 16;
+constexpr int kSmThreads = kSmWaves * 64;
+constexpr int kTileRows = 16 * kSmWaves;  // 256
+constexpr int kPairsPerLane = 4;          // pairs g, g+4, g+8, g+12 of a segment
+constexpr int kXBytes = 144 * 1024;       // activations of one K-range, all M rows
 
-// Activation chunks of pairs [p0, p0 + npairs) of rows 0..15 into
-// buf[(pl * 8 + c) * 16 + m]; rows >= m_real and pairs >= np are zero.
-__device__ void stage_range(const uint16_t* __restrict__ x, int64_t k, int m_real, int np, int p0,
-                            int npairs, u4* __restrict__ buf) {
-    for (int it = threadIdx.x; it < 16 * 2 * npairs; it += kSmThreads) {
-        const int mm = it & 15;
-        const int b = it >> 4;  // block within the range
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Segments (16 pairs) of K-range c of a descriptor.
+__device__ __forceinline__ int segs_of(const SmDesc& D, int c) {
+    return (min(D.P, D.np - c * D.P) + 15) >> 4;
+}
+
+// First unit (cost) of item (c, t): ranges before c are full.
+__device__ __forceinline__ int64_t item_start(const SmDesc& D, int c, int t) {
+    return D.cost_begin + (int64_t)c * D.tiles * (D.P >> 4) + (int64_t)t * segs_of(D, c);
+}
+
+struct SmCursor {
+    int d, c, t, jb;
+};
+
+// Activations of pairs [c*P, c*P + 16*segs) of all M rows into
+// xs[(pl * 8 + chunk) * m + row]; pairs past K/64 are zero.
+__device__ void stage_range(const SmDesc& D, int c, int m, u4* __restrict__ xs) {
+    const int p0 = c * D.P;
+    const int npairs = 16 * segs_of(D, c);
+    for (int it = threadIdx.x; it < 2 * npairs * m; it += kSmThreads) {
+        const int mm = it % m;
+        const int b = it / m;  // block within the range
         const int p = p0 + (b >> 1);
         uint32_t v[16];
-        if (mm < m_real && p < np) {
-            const g_u4* src = (const g_u4*)(x + (int64_t)mm * k + 32 * (int64_t)(2 * p0 + b));
+        if (p < D.np) {
+            const g_u4* src = (const g_u4*)(D.x + (int64_t)mm * D.k + 32 * (int64_t)(2 * p0 + b));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const u4 t = src[i];
@@ -71,72 +97,128 @@ __device__ void stage_range(const uint16_t* __restrict__ x, int64_t k, int m_rea
             for (int i = 0; i < 16; ++i) v[i] = 0u;
         }
         auto xe = [&](int j) -> uint32_t { return (v[j >> 1] >> (16 * (j & 1))) & 0xFFFFu; };
-        auto put = [&](int half) {
+        const int half = b & 1;
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-                int pos[4];
-                chunk_positions(4 * half + cc, pos);
-                const int off = 32 * half;
-                const int a = pos[0] - off, bb = pos[1] - off, c = pos[2] - off, e = pos[3] - off;
-                u4 ent;
-                ent.x = xe(a) | (xe(c) << 16);
-                ent.y = xe(a + 16) | (xe(c + 16) << 16);
-                ent.z = xe(bb) | (xe(e) << 16);
-                ent.w = xe(bb + 16) | (xe(e + 16) << 16);
-                buf[((b >> 1) * 8 + 4 * half + cc) * 16 + mm] = ent;
-            }
-        };
-        if (b & 1) put(1); else put(0);
+        for (int cc = 0; cc < 4; ++cc) {
+            int pos[4];
+            chunk_positions(4 * half + cc, pos);
+            const int off = 32 * half;
+            const int a = pos[0] - off, bb = pos[1] - off, cq = pos[2] - off, e = pos[3] - off;
+            u4 ent;
+            ent.x = xe(a) | (xe(cq) << 16);
+            ent.y = xe(a + 16) | (xe(cq + 16) << 16);
+            ent.z = xe(bb) | (xe(e) << 16);
+            ent.w = xe(bb + 16) | (xe(e + 16) << 16);
+            xs[((b >> 1) * 8 + 4 * half + cc) * m + mm] = ent;
+        }
     }
 }
 
-struct SmArgs {
-    const uint8_t* w;
-    const uint16_t* x;
-    float* out;   // y (splits == 1) or the partials [split][m][n]
-    int64_t n;
-    int k;
-    int m;
-    int splits;
-    int cps;      // chunks per split
+struct SmBuf {
+    uint32_t d[kPairsPerLane][9];
 };
 
-__global__ void __launch_bounds__(kSmThreads) k_smallm(SmArgs a) {
-    extern __shared__ u4 xbuf[];
+__global__ void __launch_bounds__(kSmThreads) k_smallm(const SmDesc* __restrict__ descs, int count, SmDesc one,
+                                                       int m, int64_t total, float* __restrict__ ws) {
+    extern __shared__ u4 xs[];
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4;
     const int l16 = lane & 15;
-    const int wave = threadIdx.x >> 6;
-    const int np = a.k >> 6;
-    const int64_t rb = (int64_t)np * kPairBytes;
-    const int split = blockIdx.x % a.splits;
-    const int64_t tile = blockIdx.x / a.splits;
-    const int c0 = split * a.cps;
-    const int nchunks = (np + kPC - 1) / kPC;
-    const int c1 = min(c0 + a.cps, nchunks);
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int n_desc = descs ? count : 1;
+    auto get = [&](int d) -> SmDesc { return descs ? descs[d] : one; };
 
-    const int64_t row = tile * kSmRows + 16 * wave + l16;  // weight row of this lane
-    const uint8_t* wrow = a.w + min(row, a.n - 1) * rb;
+    const int64_t G = gridDim.x;
+    const int64_t c_lo = uniform64((total / G) * blockIdx.x + ((total % G) * blockIdx.x) / G);
+    const int64_t c_hi = uniform64((total / G) * (blockIdx.x + 1) + ((total % G) * ((int64_t)blockIdx.x + 1)) / G);
+    if (c_lo >= c_hi) return;  // whole workgroup leaves together
 
-    uint32_t A[kPairsPerLane][9], B[kPairsPerLane][9];
-    auto load_chunk = [&](int ch, uint32_t (&D)[kPairsPerLane][9]) {
+    // First item starting at or after c_lo.
+    int lo = 0, hi = n_desc - 1;  // last descriptor starting at or before c_lo
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (get(mid).cost_begin <= c_lo) lo = mid; else hi = mid - 1;
+    }
+    SmCursor cl;
+    cl.d = lo;
+    cl.jb = 0;
+    SmDesc Dl = get(lo);
+    {
+        const int64_t full = (int64_t)Dl.tiles * (Dl.P >> 4);  // units of a full K-range
+        const int64_t o = c_lo - Dl.cost_begin;
+        int c = (int)(o / full < Dl.nranges - 1 ? o / full : Dl.nranges - 1);
+        const int64_t r = o - c * full;
+        const int sg = segs_of(Dl, c);
+        int64_t t = (r + sg - 1) / sg;
+        if (t >= Dl.tiles) {
+            t = 0;
+            if (++c == Dl.nranges) {
+                c = 0;
+                if (++cl.d < n_desc) Dl = get(cl.d);
+            }
+        }
+        cl.c = c;
+        cl.t = (int)t;
+    }
+    bool have_l = cl.d < n_desc && item_start(Dl, cl.c, cl.t) < c_hi;
+    if (!have_l) return;
+
+    auto advance_l = [&]() {
+        if (++cl.jb < segs_of(Dl, cl.c)) return;
+        cl.jb = 0;
+        if (++cl.t == Dl.tiles) {
+            cl.t = 0;
+            if (++cl.c == Dl.nranges) {
+                cl.c = 0;
+                if (++cl.d >= n_desc) {
+                    have_l = false;
+                    return;
+                }
+                Dl = get(cl.d);
+            }
+        }
+        have_l = item_start(Dl, cl.c, cl.t) < c_hi;
+    };
+
+    auto issue = [&](SmBuf& b) {
+        const int64_t row = min((int64_t)cl.t * kTileRows + 16 * wave + l16, Dl.n - 1);
+        const uint8_t* wrow = Dl.w + row * (int64_t)Dl.np * kPairBytes;
+        const int p0 = cl.c * Dl.P + 16 * cl.jb + g;
 #pragma unroll
         for (int jj = 0; jj < kPairsPerLane; ++jj) {
-            const int p = min(ch * kPC + g + 4 * jj, np - 1);
-            load_pair(wrow + (int64_t)p * kPairBytes, D[jj]);
+            const int p = min(p0 + 4 * jj, Dl.np - 1);
+            load_pair(wrow + (int64_t)p * kPairBytes, b.d[jj]);
         }
     };
+
+    struct Rec {
+        int d, c, t, jb;
+    };
     f4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    auto mma_chunk = [&](int ch, const uint32_t (&D)[kPairsPerLane][9]) {
-        const u4* xc = xbuf + (ch - c0) * kChunkU4;
+    int dc = -1, staged_d = -1, staged_c = -1;
+    SmDesc Dc;
+
+    auto process = [&](const Rec& r, const SmBuf& b) {
+        if (r.d != dc) {
+            Dc = get(r.d);
+            dc = r.d;
+        }
+        if (r.d != staged_d || r.c != staged_c) {
+            __syncthreads();
+            stage_range(Dc, r.c, m, xs);
+            __syncthreads();
+            staged_d = r.d;
+            staged_c = r.c;
+        }
+        const bool arow = l16 < m;
 #pragma unroll
         for (int jj = 0; jj < kPairsPerLane; ++jj) {
-            const int pl = g + 4 * jj;
-            const _Float16 d0 = as_h2(D[jj][0]).x, d1 = as_h2(D[jj][4]).y;
+            const int pl = 16 * r.jb + g + 4 * jj;
+            const _Float16 d0 = as_h2(b.d[jj][0]).x, d1 = as_h2(b.d[jj][4]).y;
             const h2 s0 = {d0, d0}, s1 = {d1, d1};
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
-                const uint32_t code = (c == 0) ? realign_block0(D[jj][0], D[jj][4]) : D[jj][c < 4 ? c : c + 1];
+                const uint32_t code = (c == 0) ? realign_block0(b.d[jj][0], b.d[jj][4]) : b.d[jj][c < 4 ? c : c + 1];
                 const Codes4 q = expand(code);
                 const h2 s = c < 4 ? s0 : s1;
                 u4 bw;
@@ -144,91 +226,150 @@ __global__ void __launch_bounds__(kSmThreads) k_smallm(SmArgs a) {
                 bw.y = as_u32(q.q1 * s);
                 bw.z = as_u32(q.q2 * s);
                 bw.w = as_u32(q.q3 * s);
-                const u4 ax = xc[(pl * 8 + c) * 16 + l16];
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, ax),
-                                                             __builtin_bit_cast(h8, bw), acc, 0, 0, 0);
+                u4 ax = {0u, 0u, 0u, 0u};
+                if (arow) ax = xs[(pl * 8 + c) * m + l16];
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, ax), __builtin_bit_cast(h8, bw),
+                                                             acc, 0, 0, 0);
             }
+        }
+        if (r.jb + 1 == segs_of(Dc, r.c)) {  // last segment of the item: store the tile
+            // D layout of the 16x16 product: lane (g, l16), element e -> activation row 4g + e, weight row l16
+            const int64_t row = (int64_t)r.t * kTileRows + 16 * wave + l16;
+            if (row < Dc.n) {
+                float* out = Dc.nranges > 1 ? ws + Dc.ws_off + (int64_t)r.c * m * Dc.n : Dc.y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int mm = 4 * g + e;
+                    if (mm < m) ((g_f32*)out)[(int64_t)mm * Dc.n + row] = acc[e];
+                }
+            }
+            acc = f4v{0.0f, 0.0f, 0.0f, 0.0f};
         }
     };
 
-    load_chunk(c0, A);  // weight loads first: they do not depend on the staged activations
-    stage_range(a.x, a.k, a.m, np, c0 * kPC, (c1 - c0) * kPC, xbuf);
-    __syncthreads();
-    for (int ch = c0; ch < c1; ch += 2) {
-        if (ch + 1 < c1) load_chunk(ch + 1, B);
-        mma_chunk(ch, A);
-        if (ch + 1 >= c1) break;
-        if (ch + 2 < c1) load_chunk(ch + 2, A);
-        mma_chunk(ch + 1, B);
-    }
-
-    // D layout of the 16x16 product: lane (g, l16), element r -> activation row 4g + r, weight row l16
-    if (row < a.n) {
-        float* out = a.out + (int64_t)split * a.m * a.n;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int mm = 4 * g + r;
-            if (mm < a.m) ((g_f32*)out)[(int64_t)mm * a.n + row] = acc[r];
+    SmBuf A, B;
+    Rec ra, rb;
+    ra = Rec{cl.d, cl.c, cl.t, cl.jb};
+    issue(A);
+    advance_l();
+    for (;;) {
+        bool more = have_l;
+        if (more) {
+            rb = Rec{cl.d, cl.c, cl.t, cl.jb};
+            issue(B);
+            advance_l();
         }
+        process(ra, A);
+        if (!more) break;
+        more = have_l;
+        if (more) {
+            ra = Rec{cl.d, cl.c, cl.t, cl.jb};
+            issue(A);
+            advance_l();
+        }
+        process(rb, B);
+        if (!more) break;
     }
 }
 
-// y[i] = sum over s of part[s][i], s in increasing order.
-__global__ void __launch_bounds__(256) k_sum_splits(const float* __restrict__ part, float* __restrict__ y,
-                                                    int64_t count, int splits) {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256) {
-        float v = part[i];
-        for (int s = 1; s < splits; ++s) v += part[(int64_t)s * count + i];
-        y[i] = v;
+// y[mm][n] = sum over ranges c (in order) of the partials, for every
+// descriptor with more than one K-range (blockIdx.y).
+__global__ void __launch_bounds__(256) k_sum_ranges(const SmDesc* __restrict__ descs, int count, SmDesc one,
+                                                    int m, const float* __restrict__ ws) {
+    for (int d = blockIdx.y; d < count; d += gridDim.y) {
+        const SmDesc D = descs ? descs[d] : one;
+        if (D.nranges < 2) continue;
+        const int64_t n_out = (int64_t)m * D.n;
+        const float* part = ws + D.ws_off;
+        for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n_out; i += (int64_t)gridDim.x * 256) {
+            float v = part[i];
+            for (int c = 1; c < D.nranges; ++c) v += part[(int64_t)c * n_out + i];
+            ((g_f32*)D.y)[i] = v;
+        }
     }
 }
 
 }  // namespace
 
-// Split of K for a shape: enough workgroups to cover the device twice over,
-// at most kMaxChunks chunks of activations per workgroup.  Depends on the
-// shape only, so the workspace size is known before any launch.
-void smallm_split(int64_t n, int64_t k, int* splits, int* cps) {
-    const int64_t tiles = (n + kSmRows - 1) / kSmRows;
-    const int nchunks = (int)(((k / 64) + kPC - 1) / kPC);
-    int s = (int)std::min<int64_t>(nchunks, std::max<int64_t>(1, (512 + tiles - 1) / tiles));
-    int c = (nchunks + s - 1) / s;
-    if (c > kMaxChunks) {
-        c = kMaxChunks;
-        s = (nchunks + c - 1) / c;
-    }
-    s = (nchunks + c - 1) / c;
-    *splits = s;
-    *cps = c;
+// Pairs per K-range for m activation rows: the longest run of whole
+// 16-pair segments whose activations fit kXBytes.
+static int smallm_range_pairs(int64_t k, int64_t m) {
+    const int np = (int)(k / 64);
+    const int fit = std::max(16, (int)(kXBytes / (kChunksPerPair * 16 * m)) / 16 * 16);
+    return std::min(fit, (np + 15) / 16 * 16);
+}
+
+// Fills the derived fields of a descriptor; returns its workspace floats.
+int64_t smallm_fill(SmDesc* d, int64_t m, int64_t ws_off, int64_t cost_begin) {
+    d->np = (int32_t)(d->k / 64);
+    d->P = smallm_range_pairs(d->k, m);
+    d->nranges = (d->np + d->P - 1) / d->P;
+    d->tiles = (int32_t)((d->n + kTileRows - 1) / kTileRows);
+    d->cost_begin = cost_begin;
+    const int64_t floats = d->nranges > 1 ? (int64_t)d->nranges * m * d->n : 0;
+    d->ws_off = floats ? ws_off : 0;
+    return floats;
+}
+
+int64_t smallm_cost(const SmDesc& d) {
+    int64_t c = 0;
+    for (int r = 0; r < d.nranges; ++r) c += (int64_t)d.tiles * ((std::min(d.P, d.np - r * d.P) + 15) / 16);
+    return c;
 }
 
 size_t smallm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
-    int s, c;
-    smallm_split(n, k, &s, &c);
-    return s > 1 ? (size_t)s * (size_t)m * (size_t)n * sizeof(float) : 0;
+    SmDesc d = {};
+    d.n = n;
+    d.k = (int32_t)k;
+    return (size_t)smallm_fill(&d, m, 0, 0) * sizeof(float);
 }
 
-hipError_t launch_gemm_smallm(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
-                              int64_t k, float* workspace, hipStream_t s) {
-    int splits, cps;
-    smallm_split(n, k, &splits, &cps);
-    SmArgs a;
-    a.w = w;
-    a.x = x;
-    a.out = splits > 1 ? workspace : y;
-    a.n = n;
-    a.k = (int)k;
-    a.m = (int)m;
-    a.splits = splits;
-    a.cps = cps;
-    const int64_t tiles = (n + kSmRows - 1) / kSmRows;
-    const size_t lds = (size_t)cps * kChunkU4 * sizeof(u4);
-    hipLaunchKernelGGL(k_smallm, dim3((unsigned)(tiles * splits)), dim3(kSmThreads), lds, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || splits == 1) return e;
-    const int64_t count = m * n;
-    const int grid = (int)std::min<int64_t>((count + 255) / 256, (int64_t)device_cu_count() * 8);
-    hipLaunchKernelGGL(k_sum_splits, dim3(grid), dim3(256), 0, s, workspace, y, count, splits);
+static int smallm_grid(int64_t total) {
+    return (int)std::max<int64_t>(1, std::min<int64_t>(total, (int64_t)device_cu_count()));
+}
+
+static size_t smallm_lds(int64_t max_range_pairs, int64_t m) {
+    return (size_t)max_range_pairs * kChunksPerPair * m * sizeof(u4);
+}
+
+static hipError_t launch_sm(const SmDesc* descs, int count, const SmDesc& one, int64_t m, int64_t total,
+                            int max_p, float* ws, hipStream_t s) {
+    const size_t lds = smallm_lds(max_p, m);
+    if (lds > 65536) {
+        const hipError_t e =
+            hipFuncSetAttribute((const void*)k_smallm, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_smallm, dim3(smallm_grid(total)), dim3(kSmThreads), lds, s, descs, count, one, (int)m,
+                       total, ws);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_smallm(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n, int64_t k,
+                              float* workspace, hipStream_t s) {
+    SmDesc d = {};
+    d.w = w;
+    d.x = x;
+    d.y = y;
+    d.n = n;
+    d.k = (int32_t)k;
+    smallm_fill(&d, m, 0, 0);
+    const int64_t total = smallm_cost(d);
+    hipError_t e = launch_sm(nullptr, 1, d, m, total, d.P, workspace, s);
+    if (e != hipSuccess || d.nranges < 2) return e;
+    const int grid = (int)std::min<int64_t>((m * n + 255) / 256, (int64_t)device_cu_count() * 4);
+    hipLaunchKernelGGL(k_sum_ranges, dim3(grid, 1), dim3(256), 0, s, nullptr, 1, d, (int)m, workspace);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_smallm_batch(const SmDesc* descs, int count, int64_t m, int64_t total, int max_p,
+                                    int64_t max_mn, bool any_split, float* workspace, hipStream_t s) {
+    SmDesc none = {};
+    hipError_t e = launch_sm(descs, count, none, m, total, max_p, workspace, s);
+    if (e != hipSuccess || !any_split) return e;
+    const int gx = (int)std::max<int64_t>(1, std::min<int64_t>((max_mn + 255) / 256, 64));
+    const int gy = std::min(count, 65535);
+    hipLaunchKernelGGL(k_sum_ranges, dim3(gx, gy), dim3(256), 0, s, descs, count, none, (int)m, workspace);
     return hipGetLastError();
 }
 

@@ -133,3 +133,27 @@ def test_batch_plan_validation(lib):
     assert lib.q4_0_gemv_batch_plan(good, 2, FAKE * 8, nbytes, ctypes.byref(plan), None) == q4.Q4_ERR_INVALID_ARG
     # an unfilled plan is refused
     assert lib.q4_0_gemv_batch(ctypes.byref(q4.GemvPlan()), None) == q4.Q4_ERR_INVALID_ARG
+
+
+def test_smallm_batch_plan_validation(lib):
+    D = q4.GemvDesc
+    plan = q4.GemmPlan()
+    buf = FAKE * 64
+    nbytes = lib.q4_0_gemm_smallm_batch_plan_bytes(2)
+    assert nbytes > 0 and lib.q4_0_gemm_smallm_batch_plan_bytes(0) == 0
+    good = (D * 2)(D(FAKE, FAKE * 2, FAKE * 4, 8, 64), D(FAKE * 8, FAKE * 2, FAKE * 6, 8, 64))
+    # m outside [2, 16]
+    for m in (1, 17):
+        assert lib.q4_0_gemm_smallm_batch_plan(good, 2, m, buf, nbytes, ctypes.byref(plan), None) == q4.Q4_ERR_INVALID_ARG
+    # k not a multiple of 64
+    arr = (D * 1)(D(FAKE, FAKE * 2, FAKE * 4, 8, 96))
+    assert lib.q4_0_gemm_smallm_batch_plan(arr, 1, 2, buf, nbytes, ctypes.byref(plan), None) == q4.Q4_ERR_INVALID_ARG
+    # outputs of m x n floats overlapping (8 x 2 x 4 bytes from FAKE*4 reach FAKE*4 + 64)
+    arr = (D * 2)(D(FAKE, FAKE * 2, FAKE * 4, 8, 64), D(FAKE * 8, FAKE * 2, FAKE * 4 + 32, 8, 64))
+    assert lib.q4_0_gemm_smallm_batch_plan(arr, 2, 2, buf, nbytes, ctypes.byref(plan), None) == q4.Q4_ERR_INVALID_ARG
+    # plan buffer too small, misaligned, overlapping a tensor
+    assert lib.q4_0_gemm_smallm_batch_plan(good, 2, 2, buf, 8, ctypes.byref(plan), None) == q4.Q4_ERR_WORKSPACE
+    assert lib.q4_0_gemm_smallm_batch_plan(good, 2, 2, buf + 4, nbytes, ctypes.byref(plan), None) == q4.Q4_ERR_MISALIGNED
+    assert lib.q4_0_gemm_smallm_batch_plan(good, 2, 2, FAKE * 8, nbytes, ctypes.byref(plan), None) == q4.Q4_ERR_INVALID_ARG
+    # an unfilled plan is refused
+    assert lib.q4_0_gemm_smallm_batch(ctypes.byref(q4.GemmPlan()), None, 0, None) == q4.Q4_ERR_INVALID_ARG
