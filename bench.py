@@ -177,7 +177,7 @@ def bench_sweep(args):
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": counter_traffic("sweep"),
-                     "kernel": "q4::k_sweep<DmaEngine<1,2,288>> (batch)", "launches_per_step": 1},
+                     "kernel": "q4::k_sweep<DmaEngine<2,2,288>> (batch)", "launches_per_step": 1},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(ids)
@@ -212,7 +212,7 @@ def bench_gemv(args):
             "hot_cache_GBps": round(bytes_ / (hot_ms * 1e-3) / 1e9, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counter_traffic("gemv"),
-                         "kernel": "q4::k_sweep<DmaEngine<1,2,288>>"}}
+                         "kernel": "q4::k_sweep<DmaEngine<2,2,288>>"}}
 
 
 def bench_lmhead(args):
@@ -234,7 +234,7 @@ def bench_lmhead(args):
             "data": "synthetic", "config": {"workload": "LM head 151936x5120 + argmax"},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counter_traffic("lmhead"),
-                         "kernel": "q4::k_sweep<DmaEngine<1,2,288>,ARGMAX> + q4::k_argmax_final"}}
+                         "kernel": "q4::k_sweep<DmaEngine<2,2,288>,ARGMAX> + q4::k_argmax_final"}}
 
 
 def bench_gemm(args, prefill: bool):

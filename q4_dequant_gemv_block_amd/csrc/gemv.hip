@@ -59,16 +59,22 @@ namespace q4 {
 #define Q4_SWEEP_NB 2
 #endif
 
-constexpr int kThreads = Q4_SWEEP_THREADS;  // the waves of a workgroup share one staged activation vector
-constexpr int kWaves = kThreads / 64;
 constexpr int kWavesPerEu = Q4_SWEEP_WPE;   // register budget: waves per SIMD the sweep kernel must fit
-constexpr int kR = Q4_SWEEP_R;              // rows per 16-lane group
-constexpr int kNB = Q4_SWEEP_NB;            // units per wave in the LDS ring (2 or 3)
-constexpr int kWgPerCu = Q4_SWEEP_WG_PER_CU;
-constexpr int kRowsPerStep = kWaves * 4 * kR;  // rows of one workgroup step (4R per wave)
-constexpr int kXStride = 288;               // activation chunk stride in pairs: k <= 18432 (36 KiB of LDS)
+constexpr int kNB = Q4_SWEEP_NB;            // units per wave in the LDS ring (2)
 
-int batch_rows_per_step() { return kRowsPerStep; }
+// Workgroup shapes of the sweep kernel: waves per workgroup, rows per 16-lane
+// group, workgroups per CU.  The batch and the large single GEMVs (LM head)
+// use the wide shape; single GEMVs too small to give every CU two wide
+// workgroups use the narrow one (16 rows per step instead of 96).
+struct Shape {
+    int waves, r, wg_per_cu;
+    constexpr int rows_per_step() const { return waves * 4 * r; }
+};
+constexpr Shape kWide = {Q4_SWEEP_THREADS / 64, Q4_SWEEP_R, Q4_SWEEP_WG_PER_CU};
+constexpr Shape kNarrow = {4, 1, 2};
+constexpr int kXStride = 288;  // activation chunk stride in pairs: k <= 18432 (36 KiB of LDS)
+
+int batch_rows_per_step() { return kWide.rows_per_step(); }
 
 typedef __attribute__((address_space(1))) float g_f32;
 
@@ -216,8 +222,9 @@ typedef __attribute__((address_space(3))) void l_void;
 // Segments that run past the row end (k % 1024 != 0) load only the row's
 // bytes (whole 16-byte pieces, then dwords); pairs past the row end have
 // their scales zeroed before use, and meet zero activations.
-template <int R, int NB, int XS>
+template <int WAVES, int R, int NB, int XS>
 struct DmaEngine {
+    static constexpr int kWaves = WAVES;
     static constexpr int kR = R;
     static constexpr int kJB = 1;
     static constexpr int kSeg = 16 * kPairBytes;  // 576
@@ -256,7 +263,7 @@ struct DmaEngine {
     __device__ __forceinline__ void issue(const PlanDesc& D, const Cursor& c, Buf& b) {
         const int np = D.k >> 6;
         const uint32_t rb = (uint32_t)np * kPairBytes;
-        const int64_t row0 = c.s * (int64_t)(kWaves * 4 * R) + wrow0;
+        const int64_t row0 = c.s * (int64_t)(WAVES * 4 * R) + wrow0;
         const uint32_t seg = (uint32_t)c.jb * kSeg;
         uint8_t* dst = wl + b.slot * kSlot;
         b.seq = seq++;
@@ -349,7 +356,7 @@ __device__ __forceinline__ Cursor next_unit(const PlanDesc& D, Cursor c, int JB)
 // Every wave walks the same unit sequence (its own rows of each step), so the
 // barriers of chunk changes and activation staging are reached by all.
 template <class E, int NB, int XS, bool ARGMAX>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
+__global__ void __launch_bounds__(E::kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
 k_sweep(const PlanDesc* __restrict__ descs, int count, SchedHead* head, const SchedChunk* __restrict__ chunks,
         PlanDesc one, int64_t total, int xs_bytes, uint64_t* __restrict__ keys) {
     static_assert(NB == 2, "two slots per wave: the slot of the unit being computed is refilled once its pairs are read");
@@ -488,7 +495,7 @@ k_sweep(const PlanDesc* __restrict__ descs, int count, SchedHead* head, const Sc
             }
             eng.math(Dc.npl, u.jb, xs, W, acc);
             if (u.jb + JB >= Dc.npl) {  // last unit of this row group
-                const int64_t r0 = u.s * (int64_t)(kWaves * 4 * R) + eng.rr0;
+                const int64_t r0 = u.s * (int64_t)(E::kWaves * 4 * R) + eng.rr0;
 #pragma unroll
                 for (int i = 0; i < R; ++i) {
                     const float v = row16_sum(acc[i]);
@@ -528,17 +535,19 @@ k_sweep(const PlanDesc* __restrict__ descs, int count, SchedHead* head, const Sc
         }
     }
     if (ARGMAX) {
-        __shared__ uint64_t sh[kWaves];
+        __shared__ uint64_t sh[E::kWaves];
         const uint64_t b = block_max_u64(best, sh);
         if (threadIdx.x == 0) keys[blockIdx.x] = b;
     }
 }
 
-__global__ void __launch_bounds__(kThreads) k_argmax_final(const uint64_t* __restrict__ keys,
+constexpr int kFinalThreads = 256;
+
+__global__ void __launch_bounds__(kFinalThreads) k_argmax_final(const uint64_t* __restrict__ keys,
                                                            int count, int32_t* __restrict__ token) {
-    __shared__ uint64_t sh[kWaves];
+    __shared__ uint64_t sh[kFinalThreads / 64];
     uint64_t best = 0;
-    for (int i = threadIdx.x; i < count; i += kThreads) best = keys[i] > best ? keys[i] : best;
+    for (int i = threadIdx.x; i < count; i += kFinalThreads) best = keys[i] > best ? keys[i] : best;
     const uint64_t b = block_max_u64(best, sh);
     if (threadIdx.x == 0) token[0] = (int32_t)(0xFFFFFFFFu - (uint32_t)(b & 0xFFFFFFFFu));
 }
@@ -619,7 +628,7 @@ static size_t x_lds_bytes(int64_t max_k) {
     return (size_t)pairs * kChunksPerPair * sizeof(u4);
 }
 
-static PlanDesc single_desc(const uint8_t* w, const uint16_t* x, float* y, int64_t n, int64_t k) {
+static PlanDesc single_desc(const uint8_t* w, const uint16_t* x, float* y, int64_t n, int64_t k, const Shape& sh) {
     PlanDesc d;
     d.w = w;
     d.x = x;
@@ -627,65 +636,83 @@ static PlanDesc single_desc(const uint8_t* w, const uint16_t* x, float* y, int64
     d.n = n;
     d.k = (int32_t)k;
     d.npl = npl_of(k);
-    d.steps = (n + kRowsPerStep - 1) / kRowsPerStep;
+    d.steps = (n + sh.rows_per_step() - 1) / sh.rows_per_step();
     d.cost_begin = 0;
     return d;
 }
 
-// The sweep engine for an activation stride.
-template <int XS>
-using SweepEngine = DmaEngine<kR, kNB, XS>;
+// The sweep engine for a workgroup shape and an activation stride.
+template <int WAVES, int R, int XS>
+using SweepEngine = DmaEngine<WAVES, R, kNB, XS>;
 
-template <int XS, bool AM>
+template <int WAVES, int R, int XS, bool AM>
 static hipError_t launch_sweep(const PlanDesc* descs, int count, SchedHead* head, const SchedChunk* chunks,
                                const PlanDesc& one, int64_t total, int64_t max_k, int grid, uint64_t* keys,
                                hipStream_t s) {
-    using E = SweepEngine<XS>;
+    using E = SweepEngine<WAVES, R, XS>;
     const size_t xsb = x_lds_bytes(max_k);
-    const size_t lds = xsb + (size_t)kWaves * E::kWaveLds;
+    const size_t lds = xsb + (size_t)WAVES * E::kWaveLds;
     auto kern = k_sweep<E, kNB, XS, AM>;
     if (lds > 65536) {
         const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, s, descs, count, head, chunks, one, total, (int)xsb,
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVES * 64), lds, s, descs, count, head, chunks, one, total, (int)xsb,
                        keys);
     return hipGetLastError();
 }
 
 template <bool AM>
-static hipError_t launch_any(const PlanDesc* descs, int count, SchedHead* head, const SchedChunk* chunks,
-                             const PlanDesc& one, int64_t total, int64_t max_k, int grid, uint64_t* keys,
-                             hipStream_t s) {
-    if (fixed_stride(max_k))
-        return launch_sweep<kXStride, AM>(descs, count, head, chunks, one, total, max_k, grid, keys, s);
-    return launch_sweep<0, AM>(descs, count, head, chunks, one, total, max_k, grid, keys, s);
+static hipError_t launch_any(const Shape& sh, const PlanDesc* descs, int count, SchedHead* head,
+                             const SchedChunk* chunks, const PlanDesc& one, int64_t total, int64_t max_k, int grid,
+                             uint64_t* keys, hipStream_t s) {
+    const bool fixed = fixed_stride(max_k);
+    if (sh.waves == kNarrow.waves && sh.r == kNarrow.r)
+        return fixed ? launch_sweep<kNarrow.waves, kNarrow.r, kXStride, AM>(descs, count, head, chunks, one, total,
+                                                                            max_k, grid, keys, s)
+                     : launch_sweep<kNarrow.waves, kNarrow.r, 0, AM>(descs, count, head, chunks, one, total, max_k,
+                                                                      grid, keys, s);
+    return fixed ? launch_sweep<kWide.waves, kWide.r, kXStride, AM>(descs, count, head, chunks, one, total, max_k,
+                                                                    grid, keys, s)
+                 : launch_sweep<kWide.waves, kWide.r, 0, AM>(descs, count, head, chunks, one, total, max_k, grid,
+                                                              keys, s);
 }
 
 // Workgroups for a static split of `steps` row steps.
-static int static_grid(int64_t steps, int cap) {
-    return (int)std::max<int64_t>(1, std::min<int64_t>({steps, (int64_t)device_cu_count() * kWgPerCu, (int64_t)cap}));
+static int static_grid(int64_t steps, const Shape& sh, int cap) {
+    return (int)std::max<int64_t>(
+        1, std::min<int64_t>({steps, (int64_t)device_cu_count() * sh.wg_per_cu, (int64_t)cap}));
+}
+
+// Shape for a single GEMV of n rows: the wide one when it gives every CU two
+// workgroups of work, else the narrow one.
+static const Shape& single_shape(int64_t n) {
+    const int64_t wide_steps = (n + kWide.rows_per_step() - 1) / kWide.rows_per_step();
+    return wide_steps >= 2 * (int64_t)device_cu_count() ? kWide : kNarrow;
 }
 
 hipError_t launch_gemv(const uint8_t* w, const uint16_t* x, float* y, int64_t n, int64_t k,
                        hipStream_t s) {
-    const PlanDesc d = single_desc(w, x, y, n, k);
-    return launch_any<false>(nullptr, 1, nullptr, nullptr, d, d.steps * d.npl, k, static_grid(d.steps, INT32_MAX),
-                             nullptr, s);
+    const Shape& sh = single_shape(n);
+    const PlanDesc d = single_desc(w, x, y, n, k, sh);
+    return launch_any<false>(sh, nullptr, 1, nullptr, nullptr, d, d.steps * d.npl, k,
+                             static_grid(d.steps, sh, INT32_MAX), nullptr, s);
 }
 
 int argmax_blocks(int64_t n, int64_t k) {
     (void)k;
-    return static_grid((n + kRowsPerStep - 1) / kRowsPerStep, kArgmaxMaxBlocks);
+    const Shape& sh = single_shape(n);
+    return static_grid((n + sh.rows_per_step() - 1) / sh.rows_per_step(), sh, kArgmaxMaxBlocks);
 }
 
 hipError_t launch_lm_head(const uint8_t* w, const uint16_t* h, float* logits, int32_t* token,
                           int64_t n, int64_t k, uint64_t* keys, hipStream_t s) {
-    const PlanDesc d = single_desc(w, h, logits, n, k);
+    const Shape& sh = single_shape(n);
+    const PlanDesc d = single_desc(w, h, logits, n, k, sh);
     const int grid = argmax_blocks(n, k);
-    hipError_t e = launch_any<true>(nullptr, 1, nullptr, nullptr, d, d.steps * d.npl, k, grid, keys, s);
+    hipError_t e = launch_any<true>(sh, nullptr, 1, nullptr, nullptr, d, d.steps * d.npl, k, grid, keys, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_argmax_final, dim3(1), dim3(kThreads), 0, s, keys, grid, token);
+    hipLaunchKernelGGL(k_argmax_final, dim3(1), dim3(kFinalThreads), 0, s, keys, grid, token);
     return hipGetLastError();
 }
 
@@ -719,7 +746,7 @@ void build_schedule(PlanDesc* descs, int count, std::vector<SchedChunk>* out, in
     for (int i = 0; i < count; ++i) {
         PlanDesc& p = descs[i];
         p.npl = npl_of(p.k);
-        p.steps = (p.n + kRowsPerStep - 1) / kRowsPerStep;
+        p.steps = (p.n + kWide.rows_per_step() - 1) / kWide.rows_per_step();
         p.cost_begin = total;
         const int units = p.npl;  // one unit per 16 pairs of a row
         for (int64_t st = 0; st < p.steps; ++st) {
@@ -733,7 +760,7 @@ void build_schedule(PlanDesc* descs, int count, std::vector<SchedChunk>* out, in
     }
     if (open_units < 2 && atoms.size() > 1) atoms.pop_back();  // a lone one-unit step joins the atom before it
     const int64_t n_atoms = (int64_t)atoms.size();
-    const int grid = static_grid(n_atoms, INT32_MAX);
+    const int grid = static_grid(n_atoms, kWide, INT32_MAX);
     out->clear();
     int64_t a = 0;
     auto cost_at = [&](int64_t i) { return i < n_atoms ? atoms[i].cost : total; };
@@ -765,7 +792,7 @@ hipError_t launch_gemv_batch(const void* plan, int count, int nchunks, int grid,
     const PlanDesc* descs = (const PlanDesc*)(base + sizeof(SchedHead));
     const SchedChunk* chunks = (const SchedChunk*)(base + sizeof(SchedHead) + (size_t)count * sizeof(PlanDesc));
     PlanDesc none = {};
-    return launch_any<false>(descs, count, head, chunks, none, 0, max_k, grid, nullptr, s);
+    return launch_any<false>(kWide, descs, count, head, chunks, none, 0, max_k, grid, nullptr, s);
 }
 
 }  // namespace q4
