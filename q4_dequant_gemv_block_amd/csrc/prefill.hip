@@ -5,26 +5,35 @@
 // (taozi.news, section "基准成绩"; originshq.com page, section "The Engine:
 // ~50 WGSL Kernels Written From Scratch").  With M in the hundreds this is a
 // real dense contraction, so the weights are expanded on chip and fed to the
-// gfx950 matrix cores.
+// gfx950 matrix cores (v_mfma_f32_32x32x16_f16, f32 accumulation).
 //
-// Tiling: a workgroup of 4 waves owns a 128 (M) x 128 (N) output tile; wave
-// (wm, wn) owns the 64 x 64 quarter at (64 wm, 64 wn) as 2 x 2 tiles of
-// v_mfma_f32_32x32x16_f16 with f32 accumulators.  K advances 64 columns (one
-// Q4_0 block pair per weight row) per step:
-//   * threads 0..127 each expand one weight row's pair: exact (code - 8) f16
-//     pairs (v_and_or_b32 + v_pk_add_f16), times the block scale d in f16
-//     (one rounding: relative error <= 2^-11, inside the 1e-3 bound), written
-//     to LDS as 8 chunks of 8 halves;
-//   * threads 128..255 copy one activation row's 64 halves into the same chunk
-//     order (q4_device.h), so chunk c of an activation row meets chunk c of a
-//     weight row: the k order inside a pair is permuted identically on both
-//     sides and each chunk is exactly one 8-half MFMA operand.
-// Rows past M or N are zero in LDS and never stored.  Both tiles are double
-// buffered: the next step's global loads are issued before the current
-// step's matrix work.
+// Tiling: a workgroup of NW waves owns BM = 32 IT activation rows x BN = 64 NW
+// weight rows.  Wave w owns weight rows [64 w, 64 w + 64) of the tile as two
+// 32-column MFMA tiles (j) and all IT 32-row tiles (i) of the activations.
+// K advances 64 columns (one Q4_0 block pair per weight row) per step:
+//  * the activation tile [BM][64] (f16, natural k order) moves from HBM into
+//    LDS with global_load_lds_dwordx4, in a ring of three; the 16-byte chunk c of
+//    row i is stored at slot 8 i + (c ^ swz(i)), chosen through each lane's
+//    source address, so the MFMA operand reads of 32 rows spread over the
+//    banks;
+//  * the step's weight pairs (36 bytes per row) move into LDS the same way
+//    (dword pieces, row-major); lane (n, g) = (lane % 32, lane / 32) reads the
+//    pairs of its two weight rows and expands, for k-substep ks, the 8
+//    weights k = 16 ks + 8 g .. + 7
+//    of the pair in natural order (block ks / 2; low nibbles of code bytes
+//    8g .. 8g+7 for even ks, high nibbles for odd ks) straight into its B
+//    operand: (code - 8) exact in f16 (v_perm_b32 + v_and_or_b32 +
+//    v_pk_add_f16), times d rounded once (v_pk_mul_f16);
+//  * the A operand of lane (i, g) at substep ks is the chunk 2 ks + g of
+//    activation row i, so both operands cover the same 8 k.
+// One barrier per step: every wave waits for its own loads of the step, the
+// barrier makes all of them visible and frees the buffer of the step after
+// next, whose loads are then issued before this step's matrix work (three
+// steps in flight: a step's matrix work is shorter than a load's latency).
+// Rows past M or N read clamped in-range addresses and are never stored.
 // Grid order is XCD-aware: workgroup b runs on XCD b % 8, and all M-tiles of
-// one N-tile are given to consecutive workgroups of the same XCD, so a weight
-// tile is fetched from HBM once and served from that XCD's L2 to the others.
+// one N-tile go to consecutive workgroups of the same XCD, so a weight tile is
+// read from HBM once and served from that XCD's L2 to the others.
 #include "q4_device.h"
 #include "q4_launch.h"
 
@@ -37,13 +46,12 @@ namespace {
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f16v __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(1))) float g_f32;
+typedef __attribute__((address_space(1))) void g_void;
+typedef __attribute__((address_space(3))) void l_void;
 
-constexpr int kPfThreads = 256;
-constexpr int kBM = 128;
-constexpr int kBN = 128;
-constexpr int kRowBytes = 8 * 16 + 16;  // 8 chunks + 16 bytes of padding (bank stagger)
-constexpr int kTileBytes = 128 * kRowBytes;
 constexpr int kXcd = 8;
+constexpr int kRing = 3;  // steps in flight: activation tiles in LDS, weight pairs in registers
+constexpr int kStepBytes = 64 * 2;  // one activation row of one step (64 halves)
 
 struct PfArgs {
     const uint8_t* w;
@@ -51,47 +59,59 @@ struct PfArgs {
     float* y;
     int64_t m, n;
     int k;
+    int np;      // pairs per weight row
     int mt, nt;  // tiles along M and N
 };
 
-// One weight row's pair, expanded and scaled, as the 8 chunks of the pair.
-__device__ __forceinline__ void expand_pair_scaled(const uint32_t (&D)[9], u4 (&out)[8]) {
-    const _Float16 d0 = as_h2(D[0]).x;
-    const _Float16 d1 = as_h2(D[4]).y;
-    const h2 s0 = {d0, d0}, s1 = {d1, d1};
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const uint32_t code = (c == 0) ? realign_block0(D[0], D[4]) : D[c < 4 ? c : c + 1];
-        const Codes4 q = expand(code);
-        const h2 s = c < 4 ? s0 : s1;
-        out[c].x = as_u32(q.q0 * s);
-        out[c].y = as_u32(q.q1 * s);
-        out[c].z = as_u32(q.q2 * s);
-        out[c].w = as_u32(q.q3 * s);
-    }
+// The four f16 pairs of natural-order weights from 8 code bytes (two dwords,
+// byte j = codes j (low nibble) and j + 16 (high nibble) of the block):
+// HI selects the high nibbles.  Exact (code - 8), then times the scale.
+template <bool HI>
+__device__ __forceinline__ u4 expand8(const uint32_t (&P)[4], h2 s) {
+    const uint32_t mask = HI ? 0x00F000F0u : 0x000F000Fu;
+    const uint32_t bias = HI ? 0x54005400u : 0x64006400u;
+    const h2 off = HI ? h2{(_Float16)72.0f, (_Float16)72.0f} : h2{(_Float16)1032.0f, (_Float16)1032.0f};
+    u4 r;
+    r.x = as_u32((as_h2(and_or(P[0], mask, bias)) - off) * s);
+    r.y = as_u32((as_h2(and_or(P[1], mask, bias)) - off) * s);
+    r.z = as_u32((as_h2(and_or(P[2], mask, bias)) - off) * s);
+    r.w = as_u32((as_h2(and_or(P[3], mask, bias)) - off) * s);
+    return r;
 }
 
-// One activation row's 64 halves (two blocks) in chunk order.
-__device__ __forceinline__ void permute_x(const uint32_t (&v)[32], u4 (&out)[8]) {
-    auto xe = [&](int j) -> uint32_t { return (v[j >> 1] >> (16 * (j & 1))) & 0xFFFFu; };
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        int pos[4];
-        chunk_positions(c, pos);
-        const int a = pos[0], b = pos[1], cc = pos[2], e = pos[3];
-        out[c].x = xe(a) | (xe(cc) << 16);
-        out[c].y = xe(a + 16) | (xe(cc + 16) << 16);
-        out[c].z = xe(b) | (xe(e) << 16);
-        out[c].w = xe(b + 16) | (xe(e + 16) << 16);
-    }
+// Position of chunk c of activation row i within the row's 8 LDS slots is
+// c ^ swz(i).  Rows are 128 bytes apart; swz gives 8 consecutive rows 8
+// distinct slots (no conflict with 32 banks of 4 bytes) and 16 consecutive
+// rows distinct (row parity, slot) pairs (no conflict with 64 banks).
+__device__ __forceinline__ int swz(int i) { return (i & 7) ^ ((i >> 3) & 1); }
+
+// Code bytes 8g .. 8g+7 of a block as four dwords [b, 0, b', 0] (consecutive
+// byte pairs spread to the two halves), from the block's code dwords E0, E1.
+__device__ __forceinline__ void spread(uint32_t e0, uint32_t e1, uint32_t (&P)[4]) {
+    P[0] = __builtin_amdgcn_perm(e0, e0, 0x0C010C00u);
+    P[1] = __builtin_amdgcn_perm(e0, e0, 0x0C030C02u);
+    P[2] = __builtin_amdgcn_perm(e1, e1, 0x0C010C00u);
+    P[3] = __builtin_amdgcn_perm(e1, e1, 0x0C030C02u);
 }
 
-__global__ void __launch_bounds__(kPfThreads) k_prefill(PfArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kTileBytes];  // [buffer][X | W]
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
+template <int IT, int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) k_prefill(PfArgs a) {
+    constexpr int BM = 32 * IT;
+    constexpr int kTile = BM * kStepBytes;           // bytes of one activation tile
+    constexpr int kInstr = kTile / (64 * 16) / NW;   // DMA instructions per wave per tile
+    constexpr int kWTile = 64 * NW * kPairBytes;     // bytes of one step's weight pairs
+    static_assert(kInstr * NW * 64 * 16 == kTile, "tile split over the waves");
+    constexpr int kWInstr = kWTile / 4 / 64 / NW;    // dword DMA instructions per wave per step (9)
+    static_assert(kWInstr * NW * 64 * 4 == kWTile, "weight tile split over the waves");
+    constexpr int kPerStep = kInstr + kWInstr;       // load instructions per wave per step
+    static_assert(kPerStep < 32, "vmcnt encoding below");
+    __shared__ __attribute__((aligned(16))) uint8_t xs[kRing][kTile];
+    __shared__ __attribute__((aligned(16))) uint32_t wsh[kRing][kWTile / 4];
+
+    const int lane = threadIdx.x & 63;
+    const int li = lane & 31;
+    const int g = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 
     // XCD-aware tile order
     const int b = blockIdx.x;
@@ -100,110 +120,164 @@ __global__ void __launch_bounds__(kPfThreads) k_prefill(PfArgs a) {
     const int m_tile = local % a.mt;
     const int n_tile = (local / a.mt) * kXcd + xcd;
     if (n_tile >= a.nt) return;  // whole workgroup leaves together (grid padded to a multiple of 8 N-tiles)
-    const int64_t m0 = (int64_t)m_tile * kBM;
-    const int64_t n0 = (int64_t)n_tile * kBN;
+    const int64_t m0 = (int64_t)m_tile * BM;
+    const int64_t n0 = (int64_t)n_tile * (64 * NW);
 
-    const int np = a.k >> 6;
-    const int64_t rb = (int64_t)np * kPairBytes;
-    // loader role: weight row (tid < 128) or activation row (tid >= 128)
-    const bool is_w = tid < 128;
-    const int r = tid & 127;
-    const int64_t wrow = min(n0 + r, a.n - 1);
-    const bool x_ok = m0 + r < a.m;
-    const uint16_t* xrow = a.x + min(m0 + r, a.m - 1) * (int64_t)a.k;
-    const bool w_ok = n0 + r < a.n;
-
-    uint32_t Dw[9];
-    uint32_t Xv[32];
-    auto load_step = [&](int s) {
-        if (is_w) {
-            load_pair(a.w + wrow * rb + (int64_t)s * kPairBytes, Dw);
-        } else {
-            const g_u4* src = (const g_u4*)(xrow + 64 * (int64_t)s);
+    const int64_t rb = (int64_t)a.np * kPairBytes;
+    // Per-lane source offsets (bytes, 32-bit: a weight matrix or an
+    // activation tile is far below 4 GiB from its base) fixed for the whole
+    // K loop; the uniform bases advance by one pair / 64 halves per step.
+    //  * weights: dword G of the step's tile (row G / 9, dword G % 9; rows past
+    //    N read row N - 1) goes to LDS word G, a row-major tile with a 36-byte
+    //    pitch; instruction t of this wave covers G = 64 (9 wave + t) + lane.
+    //  * activations: slot S = 64 (kInstr wave + q) + lane holds chunk
+    //    (S % 8) ^ (row % 8) of row S / 8 (rows past M read row M - 1).
+    const uint8_t* wbase = a.w + n0 * rb;
+    const uint8_t* xbase = (const uint8_t*)(a.x + m0 * (int64_t)a.k);
+    const int64_t n_last = a.n - 1 - n0;  // last valid row of the tile
+    const int64_t m_last = a.m - 1 - m0;
+    uint32_t woff[kWInstr], xoff[kInstr];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const u4 t = src[i];
-                Xv[4 * i] = t.x; Xv[4 * i + 1] = t.y; Xv[4 * i + 2] = t.z; Xv[4 * i + 3] = t.w;
-            }
-        }
-    };
-    auto store_step = [&](int buf) {
-        u4 ch[8];
-        uint8_t* dst;
-        if (is_w) {
-            expand_pair_scaled(Dw, ch);
-            if (!w_ok) {
+    for (int t = 0; t < kWInstr; ++t) {
+        const int G = 64 * (kWInstr * wave + t) + lane;
+        const int64_t row = min((int64_t)(G / 9), n_last);
+        woff[t] = (uint32_t)(row * rb + 4 * (G % 9));
+    }
 #pragma unroll
-                for (int c = 0; c < 8; ++c) ch[c] = u4{0, 0, 0, 0};
-            }
-            dst = &lds[buf][1][r * kRowBytes];
-        } else {
-            permute_x(Xv, ch);
-            if (!x_ok) {
+    for (int q = 0; q < kInstr; ++q) {
+        const int slot = 64 * (wave * kInstr + q) + lane;
+        const int i = slot >> 3;
+        const int c = (slot & 7) ^ swz(i);
+        const int64_t row = min((int64_t)i, m_last);
+        xoff[q] = (uint32_t)((row * a.k + 8 * c) * 2);
+    }
+    auto issue = [&](int s, int buf) {
+        const uint8_t* xb = xbase + (int64_t)s * kStepBytes;
+        const uint8_t* wb = wbase + (int64_t)s * kPairBytes;
 #pragma unroll
-                for (int c = 0; c < 8; ++c) ch[c] = u4{0, 0, 0, 0};
-            }
-            dst = &lds[buf][0][r * kRowBytes];
-        }
+        for (int q = 0; q < kInstr; ++q)
+            __builtin_amdgcn_global_load_lds((g_void*)(xb + xoff[q]),
+                                             (l_void*)(&xs[buf][0] + 1024 * (wave * kInstr + q)), 16, 0, 0);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) *(u4*)(dst + 16 * c) = ch[c];
+        for (int t = 0; t < kWInstr; ++t)
+            __builtin_amdgcn_global_load_lds((g_void*)(wb + woff[t]),
+                                             (l_void*)(&wsh[buf][0] + 64 * (kWInstr * wave + t)), 4, 0, 0);
     };
 
-    f16v acc[2][2];
+    // LDS read offsets: the A chunk c = 2 ks + g of row 32 i + li sits at slot
+    // 256 i + 8 li + (c ^ swz(li)) (swz(32 i + li) = swz(li)); the weight pairs
+    // of rows 64 wave + 32 j + li.
+    uint32_t aoff[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int ks = 0; ks < 4; ++ks) aoff[ks] = 16u * (uint32_t)(8 * li + ((2 * ks + g) ^ swz(li)));
+    const uint32_t doff = 4u * (uint32_t)((64 * wave + li) * 9);
+
+    f16v acc[IT][2];
+#pragma unroll
+    for (int i = 0; i < IT; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    load_step(0);
-    store_step(0);
-    __syncthreads();
-    for (int s = 0; s < np; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < np) load_step(s + 1);
-        // matrix work on buffer `buf`
-        const uint8_t* xt = &lds[buf][0][0];
-        const uint8_t* wt = &lds[buf][1][0];
-        const int li = lane & 31, g = lane >> 5;
+    auto compute = [&](int buf) {
+        const uint8_t* xt = &xs[buf][0];
+        const uint8_t* wt = (const uint8_t*)&wsh[buf][0] + doff;
+        uint32_t D[2][9];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int c = 2 * ks + g;
-            h8 af[2], bf[2];
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                af[i] = *(const h8*)(xt + (64 * wm + 32 * i + li) * kRowBytes + 16 * c);
+            for (int c = 0; c < 9; ++c) D[j][c] = *(const uint32_t*)(wt + 32 * 36 * j + 4 * c);
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bf[j] = *(const h8*)(wt + (64 * wn + 32 * j + li) * kRowBytes + 16 * c);
+        for (int blk = 0; blk < 2; ++blk) {
+            uint32_t P[2][4];
+            h2 sc[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int j = 0; j < 2; ++j) {
+                uint32_t e0, e1;
+                if (blk == 0) {
+                    // block 0 codes start at byte 2 of the pair: bytes 8g .. 8g+7 of the codes
+                    // are bytes 2 .. 9 of dwords D[2g] .. D[2g+2]
+                    const uint32_t lo = g ? D[j][2] : D[j][0];
+                    const uint32_t mid = g ? D[j][3] : D[j][1];
+                    const uint32_t hi = g ? D[j][4] : D[j][2];
+                    e0 = __builtin_amdgcn_perm(mid, lo, 0x05040302u);
+                    e1 = __builtin_amdgcn_perm(hi, mid, 0x05040302u);
+                    const _Float16 d = as_h2(D[j][0]).x;
+                    sc[j] = h2{d, d};
+                } else {
+                    e0 = g ? D[j][7] : D[j][5];
+                    e1 = g ? D[j][8] : D[j][6];
+                    const _Float16 d = as_h2(D[j][4]).y;
+                    sc[j] = h2{d, d};
+                }
+                spread(e0, e1, P[j]);
+            }
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+            for (int hi = 0; hi < 2; ++hi) {
+                const int ks = 2 * blk + hi;
+                u4 bw[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) bw[j] = hi ? expand8<true>(P[j], sc[j]) : expand8<false>(P[j], sc[j]);
+#pragma unroll
+                for (int i = 0; i < IT; ++i) {
+                    const h8 av = *(const h8*)(xt + aoff[ks] + 4096 * i);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, __builtin_bit_cast(h8, bw[j]),
+                                                                           acc[i][j], 0, 0, 0);
+                }
+            }
         }
-        if (s + 1 < np) store_step(buf ^ 1);
-        __syncthreads();
+    };
+
+    // Ring of three steps: step s uses buffers s % 3; the loads of step s + 2
+    // are issued (after the barrier that frees their buffers) before step s is
+    // computed.
+    issue(0, 0);
+    if (a.np > 1) issue(1, 1);
+    int buf = 0;
+    for (int s = 0; s < a.np; ++s) {
+        // this wave's loads of step s have landed: at most the ones of step s + 1 are outstanding
+        if (s + 1 < a.np)
+            __builtin_amdgcn_s_waitcnt(kPerStep < 16 ? (0x0F70 | kPerStep) : (0x4F70 | (kPerStep - 16)));
+        else
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();  // everyone's loads of step s are visible; the buffers of step s + 2 are free
+        const int fill = buf == 0 ? 2 : buf - 1;
+        if (s + 2 < a.np) issue(s + 2, fill);
+        compute(buf);
+        buf = buf == kRing - 1 ? 0 : buf + 1;
     }
 
     // D layout of the 32x32 product: lane (li, g), element e -> row 8*(e/4) + 4*g + e%4, column li
-    const int li = lane & 31, g = lane >> 5;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < IT; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int64_t col = n0 + 64 * wn + 32 * j + li;
+            const int64_t col = n0 + 64 * wave + 32 * j + li;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t row = m0 + 64 * wm + 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
+                const int64_t row = m0 + 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
                 if (row < a.m && col < a.n) ((g_f32*)a.y)[row * a.n + col] = acc[i][j][e];
             }
         }
 }
 
+template <int IT, int NW>
+hipError_t launch(PfArgs a, hipStream_t s) {
+    a.mt = (int)((a.m + 32 * IT - 1) / (32 * IT));
+    a.nt = (int)((a.n + 64 * NW - 1) / (64 * NW));
+    const int64_t ngroups = (a.nt + kXcd - 1) / kXcd;
+    const int64_t grid = ngroups * kXcd * a.mt;
+    hipLaunchKernelGGL((k_prefill<IT, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, s, a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
+// Tile shape by size: the largest tile (activation rows 32 IT x weight rows
+// 64 NW) that still gives every CU a workgroup, else the smallest.
 hipError_t launch_gemm_prefill(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
                                int64_t k, hipStream_t s) {
     PfArgs a;
@@ -213,12 +287,13 @@ hipError_t launch_gemm_prefill(const uint8_t* w, const uint16_t* x, float* y, in
     a.m = m;
     a.n = n;
     a.k = (int)k;
-    a.mt = (int)((m + kBM - 1) / kBM);
-    a.nt = (int)((n + kBN - 1) / kBN);
-    const int64_t ngroups = (a.nt + kXcd - 1) / kXcd;
-    const int64_t grid = ngroups * kXcd * a.mt;
-    hipLaunchKernelGGL(k_prefill, dim3((unsigned)grid), dim3(kPfThreads), 0, s, a);
-    return hipGetLastError();
+    a.np = (int)(k / 64);
+    const int64_t cus = device_cu_count();
+    auto tiles = [&](int it, int nw) { return ((m + 32 * it - 1) / (32 * it)) * ((n + 64 * nw - 1) / (64 * nw)); };
+    if (m > 96 && tiles(4, 4) >= cus) return launch<4, 4>(a, s);
+    if (m > 96 && tiles(4, 2) >= cus) return launch<4, 2>(a, s);
+    if (tiles(2, 4) >= cus) return launch<2, 4>(a, s);
+    return launch<2, 2>(a, s);
 }
 
 }  // namespace q4
