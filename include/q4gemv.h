@@ -246,6 +246,40 @@ Q4_API q4_status q4_0_gemm_smallm_batch_plan(const q4_gemv_desc* descs, int coun
 Q4_API q4_status q4_0_gemm_smallm_batch(const q4_gemm_plan* plan, void* workspace, size_t workspace_bytes,
                                         void* stream);
 
+/* Host-side handle of a prefill batch plan.  Filled by
+ * q4_0_gemm_prefill_batch_plan; plain data, may be copied. */
+typedef struct q4_prefill_plan {
+    void* device;        /* the caller's device buffer holding the descriptors */
+    int count;           /* number of GEMMs */
+    int m;               /* token rows of every GEMM */
+    int tile_m;          /* internal: activation rows per tile (64 or 128) */
+    int reserved;
+    int64_t total_cost;  /* internal: 64-column steps of all tiles */
+} q4_prefill_plan;
+
+/* Device bytes q4_0_gemm_prefill_batch_plan needs for `count` descriptors. */
+Q4_API size_t q4_0_gemm_prefill_batch_plan_bytes(int count);
+
+/*
+ * A list of prefill GEMMs with the same m, run as one launch: the prompt
+ * matrices of independent projections (taozi.news, section "基准成绩";
+ * originshq.com page, section "The Engine ...") share the machine instead of
+ * each filling only part of it.  Descriptor i names w (n rows of k/32 Q4_0
+ * blocks, 16-byte aligned), x (m x k binary16, 16-byte aligned) and y (m x n
+ * binary32, written); every k % 64 == 0, m*n <= 2^40, |d| <= 8188.  Each
+ * result is that of q4_0_gemm_prefill on the same operands within the same
+ * bound (the tile shape may differ, so the f32 summation order may too).
+ * Validates the list, writes its device form into `plan_buf`
+ * (q4_0_gemm_prefill_batch_plan_bytes(count) bytes, 16-byte aligned) and
+ * fills `*plan`; the copy has completed when this returns.  No output may
+ * overlap another output, an input or the plan.
+ */
+Q4_API q4_status q4_0_gemm_prefill_batch_plan(const q4_gemv_desc* descs, int count, int64_t m, void* plan_buf,
+                                              size_t plan_bytes, q4_prefill_plan* plan, void* stream);
+
+/* Run every GEMM of a prefill plan on `stream` (one launch). */
+Q4_API q4_status q4_0_gemm_prefill_batch(const q4_prefill_plan* plan, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -37,6 +37,7 @@ EXPORTS = (
     "q4_abi_version", "q4_last_error", "q4_workspace_bytes", "q4_0_gemv", "q4_0_gemm_smallm",
     "q4_0_gemm_prefill", "lm_head_argmax", "q4_0_gemv_batch_plan_bytes", "q4_0_gemv_batch_plan",
     "q4_0_gemm_smallm_batch_plan_bytes", "q4_0_gemm_smallm_batch_plan", "q4_0_gemm_smallm_batch",
+    "q4_0_gemm_prefill_batch_plan_bytes", "q4_0_gemm_prefill_batch_plan", "q4_0_gemm_prefill_batch",
     "q4_0_gemv_batch",
 )
 
@@ -97,6 +98,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                 ctypes.POINTER(GemmPlan), vp]
     lib.q4_0_gemm_smallm_batch.restype = st
     lib.q4_0_gemm_smallm_batch.argtypes = [ctypes.POINTER(GemmPlan), vp, ctypes.c_size_t, vp]
+    lib.q4_0_gemm_prefill_batch_plan_bytes.restype = ctypes.c_size_t
+    lib.q4_0_gemm_prefill_batch_plan_bytes.argtypes = [ctypes.c_int]
+    lib.q4_0_gemm_prefill_batch_plan.restype = st
+    lib.q4_0_gemm_prefill_batch_plan.argtypes = [ctypes.POINTER(GemvDesc), ctypes.c_int, i64, vp, ctypes.c_size_t,
+                                                 ctypes.POINTER(PrefillPlan), vp]
+    lib.q4_0_gemm_prefill_batch.restype = st
+    lib.q4_0_gemm_prefill_batch.argtypes = [ctypes.POINTER(PrefillPlan), vp]
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -236,6 +244,11 @@ class GemmPlan(ctypes.Structure):
                 ("max_mn", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
 
 
+class PrefillPlan(ctypes.Structure):
+    _fields_ = [("device", ctypes.c_void_p), ("count", ctypes.c_int), ("m", ctypes.c_int),
+                ("tile_m", ctypes.c_int), ("reserved", ctypes.c_int), ("total_cost", ctypes.c_int64)]
+
+
 class GemvBatch:
     """A list of independent GEMVs (w, x, y) planned once and run as one launch per call."""
 
@@ -303,6 +316,42 @@ class SmallMBatch:
     def __call__(self, stream=None):
         _check(load_library().q4_0_gemm_smallm_batch(ctypes.byref(self.plan), self.workspace.data_ptr(),
                                                      self.workspace.numel(), _stream(stream)))
+
+
+class PrefillBatch:
+    """A list of prefill GEMMs (w, x, y) with x of shape (m, k) and y (m, n), the
+    same m for all, planned once and run as one launch per call."""
+
+    def __init__(self, items, stream=None):
+        items = list(items)
+        if not items:
+            raise ValueError("empty list")
+        m = items[0][1].shape[0]
+        descs = (GemvDesc * len(items))()
+        self._keep = []
+        for i, (w, x, y) in enumerate(items):
+            if x.dim() != 2 or x.shape[0] != m:
+                raise ValueError("descriptor %d: x must be (m, k) with m = %d" % (i, m))
+            k = x.shape[1]
+            n = _weights(w, k)
+            if y.numel() != m * n:
+                raise ValueError("descriptor %d: y must hold m*N=%d floats" % (i, m * n))
+            descs[i] = GemvDesc(_ptr(w, torch.uint8, "w"), _ptr(x, torch.float16, "x"),
+                                _ptr(y, torch.float32, "y"), n, k)
+            self._keep.append((w, x, y))
+        lib = load_library()
+        dev = items[0][0].device
+        self.m = m
+        self.plan = PrefillPlan()
+        with torch.cuda.device(dev):
+            nbytes = int(lib.q4_0_gemm_prefill_batch_plan_bytes(len(items)))
+            self.buffer = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+            _check(lib.q4_0_gemm_prefill_batch_plan(descs, len(items), m, self.buffer.data_ptr(),
+                                                    self.buffer.numel(), ctypes.byref(self.plan),
+                                                    _stream(stream)))
+
+    def __call__(self, stream=None):
+        _check(load_library().q4_0_gemm_prefill_batch(ctypes.byref(self.plan), _stream(stream)))
 
 
 # Short names.

@@ -390,4 +390,60 @@ q4_status q4_0_gemm_smallm_batch(const q4_gemm_plan* plan, void* workspace, size
     return hip_status(e, "q4_0_gemm_smallm_batch launch");
 }
 
+size_t q4_0_gemm_prefill_batch_plan_bytes(int count) {
+    if (count < 1 || count > (1 << 20)) return 0;
+    return (size_t)count * sizeof(q4::PfDesc);
+}
+
+q4_status q4_0_gemm_prefill_batch_plan(const q4_gemv_desc* descs, int count, int64_t m, void* plan_buf,
+                                       size_t plan_bytes, q4_prefill_plan* plan, void* stream) {
+    const char* fn = "q4_0_gemm_prefill_batch_plan";
+    if (!plan || !plan_buf) return fail(Q4_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (m < 1 || m > (int64_t(1) << 30)) return fail(Q4_ERR_INVALID_ARG, "%s: m = %lld outside [1, 2^30]", fn, (long long)m);
+    int max_k = 0;
+    q4_status st = check_list(fn, descs, count, m, int64_t(1) << 30, kMaxK, &max_k);
+    if (st) return st;
+    for (int i = 0; i < count; ++i)
+        if (m * descs[i].n > (int64_t(1) << 40) || descs[i].n > (int64_t(1) << 30))
+            return fail(Q4_ERR_INVALID_ARG, "%s: descriptor %d: m*n too large", fn, i);
+    const size_t need = q4_0_gemm_prefill_batch_plan_bytes(count);
+    if (plan_bytes < need) return fail(Q4_ERR_WORKSPACE, "%s: plan buffer of %zu bytes needed", fn, need);
+    if (!aligned(plan_buf, 16)) return fail(Q4_ERR_MISALIGNED, "%s: plan buffer must be 16-byte aligned", fn);
+    if (check_buffer(fn, "plan buffer", plan_buf, need, descs, count, m)) return Q4_ERR_INVALID_ARG;
+    const int tile_m = q4::prefill_batch_tile_m(m);
+    std::vector<q4::PfDesc> dev(count);
+    int64_t cost = 0;
+    for (int i = 0; i < count; ++i) {
+        q4::PfDesc& d = dev[i];
+        d.w = static_cast<const uint8_t*>(descs[i].w);
+        d.x = static_cast<const uint16_t*>(descs[i].x);
+        d.y = descs[i].y;
+        d.m = m;
+        d.n = descs[i].n;
+        d.k = (int)descs[i].k;
+        cost += q4::prefill_fill(&d, tile_m, cost);
+    }
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(plan_buf, dev.data(), need, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_status(e, "q4_0_gemm_prefill_batch_plan copy");
+    plan->device = plan_buf;
+    plan->count = count;
+    plan->m = (int)m;
+    plan->tile_m = tile_m;
+    plan->total_cost = cost;
+    return ok();
+}
+
+q4_status q4_0_gemm_prefill_batch(const q4_prefill_plan* plan, void* stream) {
+    const char* fn = "q4_0_gemm_prefill_batch";
+    if (!plan || !plan->device) return fail(Q4_ERR_INVALID_ARG, "%s: null plan", fn);
+    if (plan->count < 1 || plan->m < 1 || (plan->tile_m != 64 && plan->tile_m != 128) || plan->total_cost < 1)
+        return fail(Q4_ERR_INVALID_ARG, "%s: plan was not filled by q4_0_gemm_prefill_batch_plan", fn);
+    const hipError_t e = q4::launch_gemm_prefill_batch(static_cast<const q4::PfDesc*>(plan->device), plan->count,
+                                                       plan->tile_m, plan->total_cost,
+                                                       static_cast<hipStream_t>(stream));
+    return hip_status(e, "q4_0_gemm_prefill_batch launch");
+}
+
 }  // extern "C"

@@ -53,15 +53,13 @@ constexpr int kXcd = 8;
 constexpr int kRing = 3;  // steps in flight: activation tiles in LDS, weight pairs in registers
 constexpr int kStepBytes = 64 * 2;  // one activation row of one step (64 halves)
 
-struct PfArgs {
-    const uint8_t* w;
-    const uint16_t* x;
-    float* y;
-    int64_t m, n;
-    int k;
-    int np;      // pairs per weight row
-    int mt, nt;  // tiles along M and N
-};
+typedef PfDesc PfArgs;
+
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 // The four f16 pairs of natural-order weights from 8 code bytes (two dwords,
 // byte j = codes j (low nibble) and j + 16 (high nibble) of the block):
@@ -94,8 +92,9 @@ __device__ __forceinline__ void spread(uint32_t e0, uint32_t e1, uint32_t (&P)[4
     P[3] = __builtin_amdgcn_perm(e1, e1, 0x0C030C02u);
 }
 
-template <int IT, int NW>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) k_prefill(PfArgs a) {
+template <int IT, int NW, bool BATCH>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+k_prefill(PfArgs one, const PfDesc* __restrict__ descs, int count, int64_t total) {
     constexpr int BM = 32 * IT;
     constexpr int kTile = BM * kStepBytes;           // bytes of one activation tile
     constexpr int kInstr = kTile / (64 * 16) / NW;   // DMA instructions per wave per tile
@@ -113,16 +112,8 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)
     const int g = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 
-    // XCD-aware tile order
-    const int b = blockIdx.x;
-    const int xcd = b % kXcd;
-    const int local = b / kXcd;
-    const int m_tile = local % a.mt;
-    const int n_tile = (local / a.mt) * kXcd + xcd;
-    if (n_tile >= a.nt) return;  // whole workgroup leaves together (grid padded to a multiple of 8 N-tiles)
-    const int64_t m0 = (int64_t)m_tile * BM;
-    const int64_t n0 = (int64_t)n_tile * (64 * NW);
-
+    // One output tile: activation rows [m0, m0 + BM) x weight rows [n0, n0 + 64 NW).
+    auto tile = [&](const PfArgs& a, int64_t m0, int64_t n0) {
     const int64_t rb = (int64_t)a.np * kPairBytes;
     // Per-lane source offsets (bytes, 32-bit: a weight matrix or an
     // activation tile is far below 4 GiB from its base) fixed for the whole
@@ -262,22 +253,72 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)
                 if (row < a.m && col < a.n) ((g_f32*)a.y)[row * a.n + col] = acc[i][j][e];
             }
         }
+    };
+
+    if (!BATCH) {
+        // XCD-aware tile order
+        const int b = blockIdx.x;
+        const int xcd = b % kXcd;
+        const int local = b / kXcd;
+        const int m_tile = local % one.mt;
+        const int n_tile = (local / one.mt) * kXcd + xcd;
+        if (n_tile >= one.nt) return;  // whole workgroup leaves together (grid padded to a multiple of 8 N-tiles)
+        tile(one, (int64_t)m_tile * BM, (int64_t)n_tile * (64 * NW));
+        return;
+    }
+    // Batch: the tiles (GEMM, N-tile, M-tile; M-tile fastest, so consecutive
+    // tiles reuse a weight tile from L2) whose start cost (steps) lies in this
+    // workgroup's byte-balanced share [T g / G, T (g + 1) / G).
+    const int64_t G = gridDim.x;
+    const int64_t c_lo = uniform64((total / G) * blockIdx.x + ((total % G) * blockIdx.x) / G);
+    const int64_t c_hi = uniform64((total / G) * (blockIdx.x + 1) + ((total % G) * ((int64_t)blockIdx.x + 1)) / G);
+    if (c_lo >= c_hi) return;
+    int lo = 0, hi = count - 1;  // last descriptor starting at or before c_lo
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (descs[mid].cost_begin <= c_lo) lo = mid; else hi = mid - 1;
+    }
+    int d = lo;
+    PfDesc D = descs[d];
+    int64_t t = uniform64((c_lo - D.cost_begin + D.np - 1) / D.np);
+    for (;;) {
+        if (t >= (int64_t)D.mt * D.nt) {
+            if (++d >= count) break;
+            D = descs[d];
+            t = 0;
+        }
+        if (D.cost_begin + t * D.np >= c_hi) break;
+        __syncthreads();  // the previous tile's buffers are no longer read
+        tile(D, (t % D.mt) * BM, (t / D.mt) * (64 * NW));
+        ++t;
+    }
 }
 
 template <int IT, int NW>
 hipError_t launch(PfArgs a, hipStream_t s) {
     a.mt = (int)((a.m + 32 * IT - 1) / (32 * IT));
     a.nt = (int)((a.n + 64 * NW - 1) / (64 * NW));
+    a.cost_begin = 0;
     const int64_t ngroups = (a.nt + kXcd - 1) / kXcd;
     const int64_t grid = ngroups * kXcd * a.mt;
-    hipLaunchKernelGGL((k_prefill<IT, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, s, a);
+    hipLaunchKernelGGL((k_prefill<IT, NW, false>), dim3((unsigned)grid), dim3(NW * 64), 0, s, a, nullptr, 0,
+                       (int64_t)0);
+    return hipGetLastError();
+}
+
+template <int IT, int NW>
+hipError_t launch_batch(const PfDesc* descs, int count, int64_t total, hipStream_t s) {
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(total, 2 * (int64_t)device_cu_count()));
+    PfArgs none = {};
+    hipLaunchKernelGGL((k_prefill<IT, NW, true>), dim3(grid), dim3(NW * 64), 0, s, none, descs, count, total);
     return hipGetLastError();
 }
 
 }  // namespace
 
 // Tile shape by size: the largest tile (activation rows 32 IT x weight rows
-// 64 NW) that still gives every CU a workgroup, else the smallest.
+// 64 NW) that still gives every CU a workgroup, else the smallest.  (128 x
+// 128 is left out: it needs more than 256 registers, one wave per SIMD.)
 hipError_t launch_gemm_prefill(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
                                int64_t k, hipStream_t s) {
     PfArgs a;
@@ -291,9 +332,28 @@ hipError_t launch_gemm_prefill(const uint8_t* w, const uint16_t* x, float* y, in
     const int64_t cus = device_cu_count();
     auto tiles = [&](int it, int nw) { return ((m + 32 * it - 1) / (32 * it)) * ((n + 64 * nw - 1) / (64 * nw)); };
     if (m > 96 && tiles(4, 4) >= cus) return launch<4, 4>(a, s);
-    if (m > 96 && tiles(4, 2) >= cus) return launch<4, 2>(a, s);
     if (tiles(2, 4) >= cus) return launch<2, 4>(a, s);
     return launch<2, 2>(a, s);
+}
+
+// Tile rows for a batch of M-row GEMMs: 128 unless 64-row tiles pad M by
+// clearly less (M = 169: 192 rows against 256).
+int prefill_batch_tile_m(int64_t m) {
+    const int64_t p128 = (m + 127) / 128 * 128, p64 = (m + 63) / 64 * 64;
+    return (double)p128 <= 1.15 * (double)p64 ? 128 : 64;
+}
+
+// Fills mt, nt, np and cost_begin for the batch tile shape; returns the cost.
+int64_t prefill_fill(PfDesc* d, int tile_m, int64_t cost_begin) {
+    d->np = d->k / 64;
+    d->mt = (int)((d->m + tile_m - 1) / tile_m);
+    d->nt = (int)((d->n + 255) / 256);
+    d->cost_begin = cost_begin;
+    return (int64_t)d->mt * d->nt * d->np;
+}
+
+hipError_t launch_gemm_prefill_batch(const PfDesc* descs, int count, int tile_m, int64_t total, hipStream_t s) {
+    return tile_m == 128 ? launch_batch<4, 4>(descs, count, total, s) : launch_batch<2, 4>(descs, count, total, s);
 }
 
 }  // namespace q4

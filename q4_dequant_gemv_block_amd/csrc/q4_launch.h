@@ -90,6 +90,21 @@ hipError_t launch_gemm_smallm_batch(const SmDesc* descs, int count, int64_t m, i
                                     int64_t max_mn, bool any_split, float* workspace, hipStream_t s);
 hipError_t launch_gemm_prefill(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
                                int64_t k, hipStream_t s);
+// One GEMM of a prefill list (device memory); m, n, k, w, x, y set by the
+// caller, the rest by prefill_fill.
+struct PfDesc {
+    const uint8_t* w;
+    const uint16_t* x;  // m x k
+    float* y;           // m x n
+    int64_t m, n;
+    int k;
+    int np;             // pairs per weight row (k / 64)
+    int mt, nt;         // tiles along M and N
+    int64_t cost_begin; // steps of the earlier tiles of the list
+};
+int prefill_batch_tile_m(int64_t m);
+int64_t prefill_fill(PfDesc* d, int tile_m, int64_t cost_begin);
+hipError_t launch_gemm_prefill_batch(const PfDesc* descs, int count, int tile_m, int64_t total, hipStream_t s);
 int argmax_blocks(int64_t n, int64_t k);
 hipError_t launch_lm_head(const uint8_t* w, const uint16_t* h, float* logits, int32_t* token,
                           int64_t n, int64_t k, uint64_t* keys, hipStream_t s);

@@ -157,3 +157,18 @@ def test_smallm_batch_plan_validation(lib):
     assert lib.q4_0_gemm_smallm_batch_plan(good, 2, 2, FAKE * 8, nbytes, ctypes.byref(plan), None) == q4.Q4_ERR_INVALID_ARG
     # an unfilled plan is refused
     assert lib.q4_0_gemm_smallm_batch(ctypes.byref(q4.GemmPlan()), None, 0, None) == q4.Q4_ERR_INVALID_ARG
+
+
+def test_prefill_batch_plan_validation(lib):
+    D = q4.GemvDesc
+    plan = q4.PrefillPlan()
+    buf = FAKE * 64
+    nbytes = lib.q4_0_gemm_prefill_batch_plan_bytes(2)
+    assert nbytes > 0 and lib.q4_0_gemm_prefill_batch_plan_bytes(0) == 0
+    good = (D * 2)(D(FAKE, FAKE * 2, FAKE * 4, 8, 64), D(FAKE * 8, FAKE * 2, FAKE * 6, 8, 64))
+    assert lib.q4_0_gemm_prefill_batch_plan(good, 2, 0, buf, nbytes, ctypes.byref(plan), None) == q4.Q4_ERR_INVALID_ARG
+    arr = (D * 1)(D(FAKE, FAKE * 2, FAKE * 4, 8, 96))
+    assert lib.q4_0_gemm_prefill_batch_plan(arr, 1, 2, buf, nbytes, ctypes.byref(plan), None) == q4.Q4_ERR_INVALID_ARG
+    assert lib.q4_0_gemm_prefill_batch_plan(good, 2, 2, buf, 8, ctypes.byref(plan), None) == q4.Q4_ERR_WORKSPACE
+    assert lib.q4_0_gemm_prefill_batch_plan(good, 2, 2, FAKE * 8, nbytes, ctypes.byref(plan), None) == q4.Q4_ERR_INVALID_ARG
+    assert lib.q4_0_gemm_prefill_batch(ctypes.byref(q4.PrefillPlan()), None) == q4.Q4_ERR_INVALID_ARG
