@@ -74,7 +74,6 @@ constexpr Shape kWide = {Q4_SWEEP_THREADS / 64, Q4_SWEEP_R, Q4_SWEEP_WG_PER_CU};
 constexpr Shape kNarrow = {4, 1, 2};
 constexpr int kXStride = 288;  // activation chunk stride in pairs: k <= 18432 (36 KiB of LDS)
 
-int batch_rows_per_step() { return kWide.rows_per_step(); }
 
 typedef __attribute__((address_space(1))) float g_f32;
 

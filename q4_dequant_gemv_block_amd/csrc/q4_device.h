@@ -93,23 +93,6 @@ __device__ __forceinline__ float dot_chunk(const Codes4& q, u4 x, float s) {
 __device__ __forceinline__ float f16_lo(uint32_t v) { return (float)as_h2(v).x; }
 __device__ __forceinline__ float f16_hi(uint32_t v) { return (float)as_h2(v).y; }
 
-// acc + d0 * S0 + d1 * S1 for one pair of blocks held in D[0..8], with the
-// eight activation chunks X[0..7] of that pair.
-__device__ __forceinline__ float pair_dot(const uint32_t (&D)[9], const u4 (&X)[8], float acc) {
-    float s0 = 0.0f, s1 = 0.0f;
-    s0 = dot_chunk(expand(realign_block0(D[0], D[4])), X[0], s0);
-    s0 = dot_chunk(expand(D[1]), X[1], s0);
-    s0 = dot_chunk(expand(D[2]), X[2], s0);
-    s0 = dot_chunk(expand(D[3]), X[3], s0);
-    s1 = dot_chunk(expand(D[5]), X[4], s1);
-    s1 = dot_chunk(expand(D[6]), X[5], s1);
-    s1 = dot_chunk(expand(D[7]), X[6], s1);
-    s1 = dot_chunk(expand(D[8]), X[7], s1);
-    acc = __builtin_fmaf(f16_lo(D[0]), s0, acc);
-    acc = __builtin_fmaf(f16_hi(D[4]), s1, acc);
-    return acc;
-}
-
 typedef __attribute__((address_space(1))) const u4a4 g_u4a4;
 typedef __attribute__((address_space(1))) const uint32_t g_u32;
 typedef __attribute__((address_space(1))) const u4 g_u4;

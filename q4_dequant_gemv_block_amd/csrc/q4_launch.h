@@ -46,9 +46,6 @@ struct SchedChunk {
 // number of chunks assigned statically).
 void build_schedule(PlanDesc* descs, int count, std::vector<SchedChunk>* out, int* grid);
 
-// Rows one workgroup step covers in the batch kernel (4 waves x 4 rows x R).
-int batch_rows_per_step();
-
 // Largest k the LDS-staged fast path takes (activation chunks fit in 64 KiB).
 constexpr int64_t kFastMaxK = 32768;
 

@@ -58,6 +58,42 @@ def test_workspace_bytes(lib):
     assert lib.q4_workspace_bytes(99, 1, 1, 32) == 0
 
 
+def test_smallm_k_range_workspace_rule(lib):
+    # The activations of one K-range (all M rows) live in 144 KiB of LDS, in
+    # whole 16-pair segments: 128 bytes per pair and row.  A GEMM needs partial
+    # sums (nranges x M x N floats) only when its K does not fit one range.
+    def expect(m, n, k):
+        np_ = k // 64
+        fit = max(16, (144 * 1024 // (128 * m)) // 16 * 16)
+        p = min(fit, (np_ + 15) // 16 * 16)
+        nr = -(-np_ // p)
+        return nr * m * n * 4 if nr > 1 else 0
+
+    op = q4.Q4_OP_GEMM_SMALLM
+    assert lib.q4_workspace_bytes(op, 16, 5120, 5120) == 2 * 16 * 5120 * 4
+    assert lib.q4_workspace_bytes(op, 16, 5120, 4096) == 0
+    assert lib.q4_workspace_bytes(op, 8, 5120, 5120) == 0
+    assert lib.q4_workspace_bytes(op, 2, 5120, 5120) == 0
+    for m in (2, 3, 5, 8, 9, 12, 16):
+        for k in (64, 1024, 4096, 5120, 13824, 17408, 32768):
+            assert lib.q4_workspace_bytes(op, m, 4608, k) == expect(m, 4608, k), (m, k)
+
+
+def test_gemv_plan_bytes_layout(lib):
+    # head (16 bytes) + one 56-byte descriptor per GEMV + 16-byte chunks; the
+    # chunks partition the row steps, so there are at least one and at most
+    # as many as row steps.
+    D = q4.GemvDesc
+    for count, n, k in ((1, 8, 64), (3, 5120, 5120), (448, 5120, 5120), (7, 151936, 5120)):
+        span = 1 << 32  # larger than any tensor here, so the fake tensors never overlap
+        arr = (D * count)(*[D(span * (3 * i + 1), span * (3 * i + 2), span * (3 * i + 3), n, k)
+                            for i in range(count)])
+        nbytes = lib.q4_0_gemv_batch_plan_bytes(arr, count)
+        rest = nbytes - 16 - 56 * count
+        assert rest > 0 and rest % 16 == 0, (count, n, k, nbytes)
+        assert 1 <= rest // 16 <= count * n
+
+
 FAKE = 0x10000  # never dereferenced: every call below fails validation first
 
 
