@@ -178,6 +178,7 @@ typedef struct q4_gemv_plan {
     int max_k;     /* largest k in the list */
     int grid;      /* workgroups of one launch */
     int nchunks;   /* pieces of work in the plan's schedule */
+    int flags;     /* internal: the kernel layout the schedule was made for */
 } q4_gemv_plan;
 
 /* Device bytes q4_0_gemv_batch_plan needs for this descriptor list (the size

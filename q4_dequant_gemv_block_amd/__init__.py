@@ -55,7 +55,7 @@ class GemvDesc(ctypes.Structure):
 
 class GemvPlan(ctypes.Structure):
     _fields_ = [("device", ctypes.c_void_p), ("count", ctypes.c_int), ("max_k", ctypes.c_int),
-                ("grid", ctypes.c_int), ("nchunks", ctypes.c_int)]
+                ("grid", ctypes.c_int), ("nchunks", ctypes.c_int), ("flags", ctypes.c_int)]
 
 
 _lib = None

@@ -5,6 +5,7 @@
 Every call compiles: a stale library never survives a source change.
 """
 import os
+import re
 import subprocess
 import sys
 
@@ -28,8 +29,38 @@ FLAGS = [
     # a work-queue atomic is issued by one lane and its result read much later;
     # the wave-aggregating rewrite would wait for it (and every older load) at once
     "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
+    # keep per-case updates of named accumulators as branches: merging them
+    # into one store through a computed address would move the accumulators
+    # to scratch memory
+    "-mllvm", "-simplifycfg-sink-common=false",
+    # per-kernel register and scratch report, checked below
+    "-Rpass-analysis=kernel-resource-usage",
     "-I" + os.path.join(ROOT, "include"),
 ]
+
+_REMARK = re.compile(r"remark:\s+(Function Name|ScratchSize \[bytes/lane\]|VGPRs Spill|SGPRs Spill|VGPRs|AGPRs):\s+(\S+)")
+
+
+def check_resources(stderr: str, src: str) -> list:
+    """Per-kernel resource report from the compiler's remarks; raises if a
+    kernel of `src` uses scratch memory (private arrays or register spills)."""
+    kernels, cur = [], None
+    for line in stderr.splitlines():
+        m = _REMARK.search(line)
+        if not m:
+            continue
+        key, val = m.group(1), m.group(2)
+        if key == "Function Name":
+            cur = {"name": val}
+            kernels.append(cur)
+        elif cur is not None:
+            cur[key] = val
+    bad = [k for k in kernels if k.get("ScratchSize [bytes/lane]", "0") != "0" or k.get("VGPRs Spill", "0") != "0"]
+    if bad:
+        raise RuntimeError("%s: kernels using scratch memory: %s" % (
+            src, ", ".join("%s (scratch %s, vgpr spill %s)" % (k["name"], k.get("ScratchSize [bytes/lane]"),
+                                                                k.get("VGPRs Spill")) for k in bad)))
+    return kernels
 
 
 def hipcc():
@@ -49,7 +80,19 @@ def build(verbose: bool = False, defines=()) -> str:
         cmd = [hipcc()] + FLAGS + ["-D" + d for d in defines] + ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.check_call(cmd)
+        r = subprocess.run(cmd, stderr=subprocess.PIPE, text=True)
+        diag = "\n".join(l for l in r.stderr.splitlines()
+                         if "kernel-resource-usage" not in l and "packed-fp32-ops" not in l
+                         and not re.match(r"^\s*\d*\s*\|", l))
+        if diag.strip():
+            print(diag, file=sys.stderr, flush=True)
+        if r.returncode != 0:
+            raise subprocess.CalledProcessError(r.returncode, cmd)
+        if src.endswith(".hip"):
+            for k in check_resources(r.stderr, src):
+                if verbose:
+                    print("  %-100s vgpr %s agpr %s sgpr-spill %s" % (k["name"][:100], k.get("VGPRs"), k.get("AGPRs"),
+                                                                     k.get("SGPRs Spill")), flush=True)
         objs.append(obj)
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs

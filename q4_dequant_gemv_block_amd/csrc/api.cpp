@@ -249,7 +249,7 @@ q4_status check_buffer(const char* fn, const char* what, const void* buf, size_t
 // Validates a GEMV list and lays out its plan: device descriptors, chunk
 // schedule and launch grid.
 q4_status plan_layout(const char* fn, const q4_gemv_desc* descs, int count, std::vector<q4::PlanDesc>* dev,
-                      std::vector<q4::SchedChunk>* chunks, int* grid, int* max_k_out) {
+                      std::vector<q4::SchedChunk>* chunks, int* grid, int* flags, int* max_k_out) {
     const q4_status st = check_list(fn, descs, count, 1, 1, q4::kFastMaxK, max_k_out);
     if (st) return st;
     dev->assign(count, q4::PlanDesc{});
@@ -261,7 +261,7 @@ q4_status plan_layout(const char* fn, const q4_gemv_desc* descs, int count, std:
         p.n = descs[i].n;
         p.k = (int32_t)descs[i].k;
     }
-    q4::build_schedule(dev->data(), count, chunks, grid);
+    q4::build_schedule(dev->data(), count, chunks, grid, flags);
     return ok();
 }
 
@@ -276,8 +276,8 @@ extern "C" {
 size_t q4_0_gemv_batch_plan_bytes(const q4_gemv_desc* descs, int count) {
     std::vector<q4::PlanDesc> dev;
     std::vector<q4::SchedChunk> chunks;
-    int grid = 0, max_k = 0;
-    if (plan_layout("q4_0_gemv_batch_plan_bytes", descs, count, &dev, &chunks, &grid, &max_k)) return 0;
+    int grid = 0, flags = 0, max_k = 0;
+    if (plan_layout("q4_0_gemv_batch_plan_bytes", descs, count, &dev, &chunks, &grid, &flags, &max_k)) return 0;
     ok();
     return plan_size(count, chunks.size());
 }
@@ -288,8 +288,8 @@ q4_status q4_0_gemv_batch_plan(const q4_gemv_desc* descs, int count, void* plan_
     if (!plan || !plan_buf) return fail(Q4_ERR_INVALID_ARG, "%s: null pointer", fn);
     std::vector<q4::PlanDesc> dev;
     std::vector<q4::SchedChunk> chunks;
-    int grid = 0, max_k = 0;
-    const q4_status st = plan_layout(fn, descs, count, &dev, &chunks, &grid, &max_k);
+    int grid = 0, flags = 0, max_k = 0;
+    const q4_status st = plan_layout(fn, descs, count, &dev, &chunks, &grid, &flags, &max_k);
     if (st) return st;
     const size_t need = plan_size(count, chunks.size());
     if (plan_bytes < need) return fail(Q4_ERR_WORKSPACE, "%s: plan buffer of %zu bytes needed", fn, need);
@@ -310,16 +310,17 @@ q4_status q4_0_gemv_batch_plan(const q4_gemv_desc* descs, int count, void* plan_
     plan->max_k = max_k;
     plan->grid = grid;
     plan->nchunks = (int)chunks.size();
+    plan->flags = flags;
     return ok();
 }
 
 q4_status q4_0_gemv_batch(const q4_gemv_plan* plan, void* stream) {
     if (!plan || !plan->device) return fail(Q4_ERR_INVALID_ARG, "q4_0_gemv_batch: null plan");
     if (plan->count < 1 || plan->max_k < 64 || plan->max_k > q4::kFastMaxK || plan->grid < 1 ||
-        plan->nchunks < plan->grid)
+        plan->nchunks < plan->grid || (plan->flags & ~q4::kPlanQuad) != 0)
         return fail(Q4_ERR_INVALID_ARG, "q4_0_gemv_batch: plan was not filled by q4_0_gemv_batch_plan");
     const hipError_t e = q4::launch_gemv_batch(plan->device, plan->count, plan->nchunks, plan->grid, plan->max_k,
-                                               static_cast<hipStream_t>(stream));
+                                               plan->flags, static_cast<hipStream_t>(stream));
     return hip_status(e, "q4_0_gemv_batch launch");
 }
 

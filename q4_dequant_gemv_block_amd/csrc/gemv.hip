@@ -55,23 +55,35 @@ namespace q4 {
 #ifndef Q4_SWEEP_WPE
 #define Q4_SWEEP_WPE 4
 #endif
-#ifndef Q4_SWEEP_NB
-#define Q4_SWEEP_NB 2
-#endif
 
 constexpr int kWavesPerEu = Q4_SWEEP_WPE;   // register budget: waves per SIMD the sweep kernel must fit
-constexpr int kNB = Q4_SWEEP_NB;            // units per wave in the LDS ring (2)
 
 // Workgroup shapes of the sweep kernel: waves per workgroup, rows per 16-lane
-// group, workgroups per CU.  The batch and the large single GEMVs (LM head)
-// use the wide shape; single GEMVs too small to give every CU two wide
-// workgroups use the narrow one (16 rows per step instead of 96).
+// group (segment engine), workgroups per CU, and the engine.  A batch and the
+// large single GEMVs (LM head) use a wide shape; single GEMVs too small to
+// give every CU two wide workgroups use a narrow one.  The quad engine takes
+// every list whose k are multiples of 1024 from 4096 up, the segment engine
+// the rest.
+#ifndef Q4_QUAD_NB
+#define Q4_QUAD_NB 2
+#endif
+constexpr int kQuadNB = Q4_QUAD_NB;  // units per wave in the quad engine's LDS ring
+
 struct Shape {
     int waves, r, wg_per_cu;
+    bool quad;
     constexpr int rows_per_step() const { return waves * 4 * r; }
 };
-constexpr Shape kWide = {Q4_SWEEP_THREADS / 64, Q4_SWEEP_R, Q4_SWEEP_WG_PER_CU};
-constexpr Shape kNarrow = {4, 1, 2};
+constexpr Shape kWide = {Q4_SWEEP_THREADS / 64, Q4_SWEEP_R, Q4_SWEEP_WG_PER_CU, false};
+constexpr Shape kNarrow = {4, 1, 2, false};
+#ifndef Q4_QUAD_R
+#define Q4_QUAD_R 2
+#endif
+#ifndef Q4_QUAD_WAVES
+#define Q4_QUAD_WAVES 12
+#endif
+constexpr Shape kQuadWide = {Q4_QUAD_WAVES, Q4_QUAD_R, 1, true};
+constexpr Shape kQuadNarrow = {4, 1, 2, true};
 constexpr int kXStride = 288;  // activation chunk stride in pairs: k <= 18432 (36 KiB of LDS)
 
 
@@ -152,9 +164,12 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* sh) {
 }
 
 // ---------------------------------------------------------------------------
-// The GEMV engine.  A wave's unit is 4R consecutive rows x JB pairs per lane
-// (pairs [16*jb, 16*(jb+JB)) of each row); lane group q = lane / 16 owns rows
-// q*R .. q*R+R-1 of the unit, lane l = lane % 16 owns pairs l + 16*(jb+t).
+// GEMV engines.  Both keep one contract with the sweep kernel below: a row
+// step of a GEMV gives every wave kRowsPerWave consecutive rows, which the
+// wave works through in npl units (npl = k/1024 rounded up); `issue` starts
+// the loads of a unit into a slot of the wave's LDS ring, `fetch` waits for a
+// unit and moves this lane's part of it into registers, `math` accumulates it,
+// and `finish` (after the rows' last unit) sums the rows and hands them out.
 // ---------------------------------------------------------------------------
 // A wave-uniform 64-bit value moved to scalar registers (64-bit divisions run
 // on the vector unit, and a uniform value left in vector registers costs
@@ -165,19 +180,12 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-struct Cursor {
-    int d;       // descriptor
-    int64_t s;   // row step within the descriptor
-    int jb;      // first pair-per-lane index of the unit
-};
-
 // R rows' pairs (nine dwords each, D[i]) against the activation chunks at
-// xb[c * stride], accumulated into acc[i]: chunk-outer, row-inner, so one
-// activation chunk is live at a time; the block sums are scaled once each.
+// xb[c * stride]: the two block sums of each pair (s0[i], s1[i], unscaled),
+// chunk-outer and row-inner, so one activation chunk is live at a time.
 template <int R>
-__device__ __forceinline__ void rows_dot(const uint32_t (&D)[R][9], const u4* __restrict__ xb, int stride,
-                                         float (&acc)[R]) {
-    float s0[R], s1[R];
+__device__ __forceinline__ void block_sums(const uint32_t (&D)[R][9], const u4* __restrict__ xb, int stride,
+                                           float (&s0)[R], float (&s1)[R]) {
 #pragma unroll
     for (int i = 0; i < R; ++i) s0[i] = s1[i] = 0.0f;
 #pragma unroll
@@ -192,12 +200,18 @@ __device__ __forceinline__ void rows_dot(const uint32_t (&D)[R][9], const u4* __
                 s1[i] = dot_chunk(expand(code), X, s1[i]);
         }
     }
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-        acc[i] = __builtin_fmaf(f16_lo(D[i][0]), s0[i], acc[i]);
-        acc[i] = __builtin_fmaf(f16_hi(D[i][4]), s1[i], acc[i]);
-    }
 }
+
+// One pair into a row accumulator: a = d1 * s1 + (d0 * s0 + a), two roundings.
+__device__ __forceinline__ float pair_acc(float a, float d0, float s0, float d1, float s1) {
+    return __builtin_fmaf(d1, s1, __builtin_fmaf(d0, s0, a));
+}
+
+// Row sums in a fixed association that both engines share.  Pair p of a row
+// belongs to class c = (p / 16) % 4 of lane slot p % 16; a class is summed in
+// pair order by pair_acc, the four classes as (c0 + c2) + (c1 + c3), and the
+// 16 lane slots by row16_sum.  Every row's result thus depends only on its
+// own bytes and the activations, not on its position or on the engine.
 
 // s_waitcnt vmcnt(n) with the other counters left free (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14).
@@ -207,41 +221,72 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// Wait until a unit's loads are done, given the units issued after it (each
+// of at least L load instructions) in a ring of NB slots: at most that many
+// times L loads may still be outstanding.  Fewer is always safe.
+template <int L, int NB>
+__device__ __forceinline__ void wait_unit(uint32_t after) {
+    static_assert(NB >= 2 && NB <= 4, "ring depth");
+    if (NB > 3 && after >= 3u)
+        wait_vmcnt<(NB > 3 ? 3 * L : 0)>();
+    else if (NB > 2 && after >= 2u)
+        wait_vmcnt<(NB > 2 ? 2 * L : 0)>();
+    else if (after >= 1u)
+        wait_vmcnt<L>();
+    else
+        wait_vmcnt<0>();
+}
+
 typedef __attribute__((address_space(1))) void g_void;
 typedef __attribute__((address_space(3))) void l_void;
 
-// Direct-to-LDS engine.  A wave's unit is 4R consecutive rows x one segment
-// of 16 pairs (576 bytes) per row.  Each row's segment is fetched by one
-// global_load_lds_dwordx4 (36 lanes x 16 bytes, non-temporal) into the
-// wave's window in LDS: every 128-byte line is requested by one instruction
-// and no registers hold loads in flight.  The lanes then read their pair
-// (nine dwords) back from the window.  The wait before a unit is computed is
-// an explicit vmcnt: every unit issues at least 4R load instructions, so
-// "4R times the units issued since" bounds what may still be outstanding.
-// Segments that run past the row end (k % 1024 != 0) load only the row's
-// bytes (whole 16-byte pieces, then dwords); pairs past the row end have
-// their scales zeroed before use, and meet zero activations.
-template <int WAVES, int R, int NB, int XS>
+// Fourth dword of a raw buffer descriptor on gfx9 (32-bit data format, no
+// swizzle); loads past the descriptor's size return zero.
+constexpr int kBufferWord3 = 0x00020000;
+
+// 16 (4) bytes per lane from global memory straight into LDS (lane i's bytes
+// land at dst + 16 i (4 i)), non-temporal.  `dst` must be wave-uniform.
+__device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* dst) {
+    __builtin_amdgcn_global_load_lds((g_void*)src, (l_void*)dst, 16, 0, 2);
+}
+__device__ __forceinline__ void dma4(const uint8_t* src, uint8_t* dst) {
+    __builtin_amdgcn_global_load_lds((g_void*)src, (l_void*)dst, 4, 0, 2);
+}
+
+// Segment engine, for any k % 64 == 0.  A wave's unit is 4R consecutive rows
+// x one segment of 16 pairs (576 bytes) per row; lane group q = lane / 16
+// owns rows q*R .. q*R+R-1, lane l = lane % 16 owns pair l of the segment.
+// Each row's segment is fetched by one global_load_lds_dwordx4 (36 lanes x 16
+// bytes, non-temporal) into the wave's window in LDS, and the lanes read
+// their pair (nine dwords) back.  Segments that run past the row end
+// (k % 1024 != 0) load only the row's bytes (whole 16-byte pieces, then
+// dwords); pairs past the row end have their scales zeroed before use, and
+// meet zero activations.  A 128-byte line that straddles two segments of a
+// row is requested by both.
+template <int WAVES, int R, int XS>
 struct DmaEngine {
     static constexpr int kWaves = WAVES;
-    static constexpr int kR = R;
-    static constexpr int kJB = 1;
+    static constexpr int kNB = 2;
+    static constexpr int kRowsPerWave = 4 * R;
+    static constexpr int kLoads = 4 * R;          // load instructions per unit, at least
     static constexpr int kSeg = 16 * kPairBytes;  // 576
     // Row pitch 576 bytes = 144 dwords: lane l of a 16-lane group reads dword 9l + c
     // of its row, and rows 144 dwords apart put the four groups of a wave on
     // disjoint banks (9 is invertible modulo 32 and 64).
     static constexpr int kPitch = kSeg;
     static constexpr int kSlot = 4 * R * kPitch;
-    static constexpr int kWaveLds = NB * kSlot;
-    struct Buf {
-        int slot;
-        uint32_t seq;  // issue order of the unit in the slot
-        bool edge;
+    static constexpr int kWaveLds = kNB * kSlot;
+    struct Regs {
+        uint32_t d[R][9];
+    };
+    // Per row of the lane, one accumulator per pair class, as separate
+    // variables (a run-time class index would move them to memory).
+    struct Acc {
+        float c0[R], c1[R], c2[R], c3[R];
     };
     int lane, l16;
     uint32_t rr0;    // row of this lane's first row within a step
     uint32_t wrow0;  // first row of this wave within a step
-    uint32_t seq;    // units issued so far
     uint8_t* wl;     // this wave's window
 
     __device__ __forceinline__ void init(uint8_t* window) {
@@ -250,30 +295,31 @@ struct DmaEngine {
         const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
         wrow0 = (uint32_t)(wave * 4 * R);
         rr0 = wrow0 + (uint32_t)((lane >> 4) * R);
-        seq = 0;
         wl = window;
     }
-    __device__ __forceinline__ void init_buf(Buf& b, int slot) const {
-        b.slot = slot;
-        b.seq = 0;
-        b.edge = false;
+    __device__ __forceinline__ void init_acc(Acc& a) const {
+#pragma unroll
+        for (int i = 0; i < R; ++i) a.c0[i] = a.c1[i] = a.c2[i] = a.c3[i] = 0.0f;
     }
 
-    __device__ __forceinline__ void issue(const PlanDesc& D, const Cursor& c, Buf& b) {
+    // Whether the unit reads clamped rows or a short segment (uniform).
+    template <class DS>
+    __device__ __forceinline__ bool edge(const DS& D, int s) const {
+        return !((int64_t)s * (WAVES * 4 * R) + wrow0 + 4 * R <= D.n && ((D.k >> 6) & 15) == 0);
+    }
+
+    template <class DS>
+    __device__ __forceinline__ void issue(const DS& D, int s, int jb, int slot) {
         const int np = D.k >> 6;
         const uint32_t rb = (uint32_t)np * kPairBytes;
-        const int64_t row0 = c.s * (int64_t)(WAVES * 4 * R) + wrow0;
-        const uint32_t seg = (uint32_t)c.jb * kSeg;
-        uint8_t* dst = wl + b.slot * kSlot;
-        b.seq = seq++;
-        b.edge = !(row0 + 4 * R <= D.n && (np & 15) == 0);  // uniform
-        if (!b.edge) {
+        const int64_t row0 = (int64_t)s * (WAVES * 4 * R) + wrow0;
+        const uint32_t seg = (uint32_t)jb * kSeg;
+        uint8_t* dst = wl + slot * kSlot;
+        if (!edge(D, s)) {
             const uint8_t* src = D.w + row0 * rb + seg + 16 * lane;
 #pragma unroll
             for (int r = 0; r < 4 * R; ++r)
-                if (lane < kSeg / 16)
-                    __builtin_amdgcn_global_load_lds((g_void*)(src + (uint32_t)r * rb), (l_void*)(dst + r * kPitch),
-                                                     16, 0, 2);
+                if (lane < kSeg / 16) dma16(src + (uint32_t)r * rb, dst + r * kPitch);
         } else {
             // rows past N read the last row (never stored)
             const uint32_t avail = min((uint32_t)kSeg, rb - seg);
@@ -283,9 +329,7 @@ struct DmaEngine {
             for (int r = 0; r < 4 * R; ++r) {
                 const uint32_t rr = (uint32_t)min((int)row0 + r, last_row);
                 const uint8_t* row = D.w + (uint64_t)rr * rb + seg;
-                if ((uint32_t)lane < full)
-                    __builtin_amdgcn_global_load_lds((g_void*)(row + 16 * lane), (l_void*)(dst + r * kPitch), 16, 0,
-                                                     2);
+                if ((uint32_t)lane < full) dma16(row + 16 * lane, dst + r * kPitch);
                 if ((uint32_t)lane < (rem >> 2))
                     __builtin_amdgcn_global_load_lds((g_void*)(row + 16 * full + 4 * lane),
                                                      (l_void*)(dst + r * kPitch + 16 * full), 4, 0, 2);
@@ -293,113 +337,318 @@ struct DmaEngine {
         }
     }
 
-    // Wait for the unit in `b`, read this lane's pairs from the window into
-    // registers, and wait for those reads, so the slot may be refilled.
-    __device__ __forceinline__ void fetch(int k, int jb, const Buf& b, uint32_t (&D)[R][9]) const {
-        const uint32_t after = seq - 1u - b.seq;  // units issued after this one (uniform)
-        if (after >= 2u)
-            wait_vmcnt<8 * R>();
-        else if (after == 1u)
-            wait_vmcnt<4 * R>();
-        else
-            wait_vmcnt<0>();
-        const uint32_t* p = (const uint32_t*)(wl + b.slot * kSlot + (rr0 - wrow0) * kPitch + kPairBytes * l16);
+    // Wait for the unit in `slot` (`after` units were issued behind it), read
+    // this lane's pairs from the window into registers, and wait for those
+    // reads, so the slot may be refilled.
+    template <class DS>
+    __device__ __forceinline__ void fetch(const DS& Dp, int s, int jb, int slot, uint32_t after, Regs& W) const {
+        wait_unit<kLoads, kNB>(after);
+        const uint32_t* p = (const uint32_t*)(wl + slot * kSlot + (rr0 - wrow0) * kPitch + kPairBytes * l16);
 #pragma unroll
         for (int i = 0; i < R; ++i)
 #pragma unroll
-            for (int c = 0; c < 9; ++c) D[i][c] = p[i * (kPitch / 4) + c];
+            for (int c = 0; c < 9; ++c) W.d[i][c] = p[i * (kPitch / 4) + c];
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the reads are done before the slot is reloaded
-        if (b.edge && 16 * jb + l16 >= (k >> 6)) {
+        if (edge(Dp, s) && 16 * jb + l16 >= (Dp.k >> 6)) {
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                D[i][0] &= 0xFFFF0000u;  // d of block 0
-                D[i][4] &= 0x0000FFFFu;  // d of block 1
+                W.d[i][0] &= 0xFFFF0000u;  // d of block 0
+                W.d[i][4] &= 0x0000FFFFu;  // d of block 1
             }
         }
     }
 
-    __device__ __forceinline__ void math(int npl, int jb, const u4* __restrict__ xs, const uint32_t (&D)[R][9],
-                                         float (&acc)[R]) const {
-        const int stride = XS > 0 ? XS : npl * 16;
-        rows_dot<R>(D, xs + (l16 + 16 * jb), stride, acc);
+    template <class DS>
+    __device__ __forceinline__ void math(const DS& Dp, int jb, const u4* __restrict__ xs, const Regs& W,
+                                         Acc& acc) const {
+        const int stride = XS > 0 ? XS : Dp.npl * 16;
+        float s0[R], s1[R];
+        block_sums<R>(W.d, xs + (l16 + 16 * jb), stride, s0, s1);
+        float d0[R], d1[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            d0[i] = f16_lo(W.d[i][0]);
+            d1[i] = f16_hi(W.d[i][4]);
+        }
+        auto add = [&](float(&a)[R]) {
+#pragma unroll
+            for (int i = 0; i < R; ++i) a[i] = pair_acc(a[i], d0[i], s0[i], d1[i], s1[i]);
+        };
+        switch (jb & 3) {  // the pairs' class (uniform)
+            case 0: add(acc.c0); break;
+            case 1: add(acc.c1); break;
+            case 2: add(acc.c2); break;
+            default: add(acc.c3); break;
+        }
+    }
+
+    // After the last unit of row step s: row sums, in a fixed order.
+    template <class F>
+    __device__ __forceinline__ void finish(int s, Acc& acc, F&& store) const {
+        const int64_t r0 = (int64_t)s * (WAVES * 4 * R) + rr0;
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const float v = row16_sum((acc.c0[i] + acc.c2[i]) + (acc.c1[i] + acc.c3[i]));
+            acc.c0[i] = acc.c1[i] = acc.c2[i] = acc.c3[i] = 0.0f;
+            if (l16 == 0) store(r0 + i, v);
+        }
     }
 };
 
-__device__ __forceinline__ Cursor next_unit(const PlanDesc& D, Cursor c, int JB) {
-    c.jb += JB;
-    if (c.jb >= D.npl) {
-        c.jb = 0;
-        if (++c.s == D.steps) {
-            ++c.d;
-            c.s = 0;
+// Quad engine, for k % 1024 == 0 and k >= 4096 (np = k/64 pairs per row, a
+// multiple of 16 and at least 64).  Four consecutive rows are 4*np*36 bytes,
+// exactly np/16 slabs of 64 pairs (2304 bytes, 18 lines of 128 bytes).  A
+// wave's rows in a row step are R such quads (4R consecutive rows), taken
+// slab by slab: a unit is slab t of each of the R quads, three buffer loads
+// straight to LDS per slab (64 lanes x 16, 16 and 4 bytes, non-temporal).  Slabs start on 128-byte boundaries relative to the matrix
+// start, so no line is requested twice.  Lane j computes pair j of each slab;
+// slab t of every quad holds the same pairs of the same quad rows, so the R
+// pairs of a lane meet the same activations.  A pair's row is the quad row
+// that holds it (a slab meets at most two rows, as np >= 64), and the lane
+// adds the pair into its accumulator for that row.  After the quads' last
+// slab each quad's four accumulators are summed over the wave.
+template <int WAVES, int R, int NB, int XS>
+struct QuadEngine {
+    static constexpr int kWaves = WAVES;
+    static constexpr int kNB = NB;
+    static constexpr int kRowsPerWave = 4 * R;
+    static constexpr int kLoads = 3 * R;
+    static constexpr int kSlab = 64 * kPairBytes;  // 2304
+    static constexpr int kSlot = R * kSlab;
+    static constexpr int kWaveLds = NB * kSlot;
+    struct Regs {
+        uint32_t d[R][9];
+    };
+    // Per quad, one accumulator per quad row, as separate variables: every
+    // index is a compile-time constant (a run-time row index would move the
+    // accumulators to memory).
+    struct Acc {
+        float a0[R], a1[R], a2[R], a3[R];
+        int rc;  // quad row of the slab's first pair (uniform)
+        int nb;  // first pair of quad row rc + 1, from the quad start (uniform)
+    };
+    int lane;
+    uint32_t wrow0;  // first row of this wave within a step
+    uint8_t* wl;     // this wave's ring
+
+    __device__ __forceinline__ void init(uint8_t* window) {
+        lane = threadIdx.x & 63;
+        const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+        wrow0 = (uint32_t)(wave * 4 * R);
+        wl = window;
+    }
+    __device__ __forceinline__ void init_acc(Acc& a) const {
+#pragma unroll
+        for (int i = 0; i < R; ++i) a.a0[i] = a.a1[i] = a.a2[i] = a.a3[i] = 0.0f;
+        a.rc = 0;
+        a.nb = 0;
+    }
+
+    // A slab is two full-wave loads of 16 bytes per lane and one of 4 bytes
+    // per lane (1024 + 1024 + 256 bytes), buffer loads from a descriptor
+    // whose base is the slab and whose size ends at the matrix end: the
+    // hardware returns zeros past the end (rows past N, never stored), every
+    // lane is active, and the per-lane offsets are fixed.
+    template <class DS>
+    __device__ __forceinline__ void issue(const DS& D, int s, int jb, int slot) const {
+        const uint64_t rb = (uint32_t)(D.k >> 6) * kPairBytes;
+        const uint64_t row0 = (uint64_t)s * (WAVES * 4 * R) + wrow0;
+        const uint64_t end = (uint64_t)(uint32_t)D.n * rb;
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const uint64_t off = (row0 + 4 * i) * rb + (uint32_t)jb * kSlab;
+            // bytes left after `off`, clamped to [0, 2^32 - 1] with 32-bit compares
+            const int64_t left = (int64_t)(end - off);
+            const int32_t hi = (int32_t)((uint64_t)left >> 32);
+            const uint32_t nrec = hi < 0 ? 0u : (hi > 0 ? 0xFFFFFFFFu : (uint32_t)left);
+            const __amdgpu_buffer_rsrc_t rs =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(D.w + off), (short)0, (int)nrec, kBufferWord3);
+            // The piece offsets ride in the per-lane offset: an instruction
+            // offset would move the LDS destination as well.
+            uint8_t* dst = wl + slot * kSlot + i * kSlab;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (l_void*)dst, 16, 16 * lane, 0, 0, 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (l_void*)(dst + 1024), 16, 1024 + 16 * lane, 0, 0, 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (l_void*)(dst + 2048), 4, 2048 + 4 * lane, 0, 0, 2);
         }
     }
-    return c;
+
+    template <class DS>
+    __device__ __forceinline__ void fetch(const DS& Dp, int s, int jb, int slot, uint32_t after, Regs& W) const {
+        (void)Dp;
+        (void)s;
+        (void)jb;
+        wait_unit<kLoads, kNB>(after);
+        const uint32_t* p = (const uint32_t*)(wl + slot * kSlot + kPairBytes * lane);
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+            for (int c = 0; c < 9; ++c) W.d[i][c] = p[i * (kSlab / 4) + c];
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the reads are done before the slot is reloaded
+    }
+
+    template <class DS>
+    __device__ __forceinline__ void math(const DS& Dp, int jb, const u4* __restrict__ xs, const Regs& W,
+                                         Acc& acc) const {
+        const int np = Dp.k >> 6;
+        const int o = 64 * jb;  // first pair of the slab within the quad
+        if (jb == 0) {
+            acc.rc = 0;
+            acc.nb = np;
+        }
+        const int b = acc.nb - o;  // lanes >= b hold pairs of row rc + 1 (b >= 64: none)
+        const bool next = lane >= b;
+        const int p = o - (acc.nb - np) + lane - (next ? np : 0);  // pair within its row
+        const int stride = XS > 0 ? XS : Dp.npl * 16;
+        float s0[R], s1[R];
+        block_sums<R>(W.d, xs + p, stride, s0, s1);
+        // one row: A = pair_acc(A, ...) in place
+        auto one = [&](float(&A)[R]) {
+#pragma unroll
+            for (int i = 0; i < R; ++i) A[i] = pair_acc(A[i], f16_lo(W.d[i][0]), s0[i], f16_hi(W.d[i][4]), s1[i]);
+        };
+        // two rows: lanes < b into A, the others into B (a zero scale leaves
+        // the other accumulator as it is)
+        auto two = [&](float(&A)[R], float(&B)[R]) {
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                const float d0 = f16_lo(W.d[i][0]), d1 = f16_hi(W.d[i][4]);
+                A[i] = pair_acc(A[i], next ? 0.0f : d0, s0[i], next ? 0.0f : d1, s1[i]);
+                B[i] = pair_acc(B[i], next ? d0 : 0.0f, s0[i], next ? d1 : 0.0f, s1[i]);
+            }
+        };
+        if (b >= 64) {
+            switch (acc.rc) {
+                case 0: one(acc.a0); break;
+                case 1: one(acc.a1); break;
+                case 2: one(acc.a2); break;
+                default: one(acc.a3); break;
+            }
+        } else {
+            switch (acc.rc) {
+                case 0: two(acc.a0, acc.a1); break;
+                case 1: two(acc.a1, acc.a2); break;
+                default: two(acc.a2, acc.a3); break;
+            }
+        }
+        if (o + 64 >= acc.nb) {
+            ++acc.rc;
+            acc.nb += np;
+        }
+    }
+
+    // After the quads' last slab: each row's 64 lane partials summed in a
+    // fixed order.  Rows 0|1 and 2|3 are paired across the wave halves, then
+    // across 16-lane groups, then summed inside each group, so lane 0, 16, 32
+    // and 48 end with rows 0, 2, 1 and 3 of the quad.
+    template <class F>
+    __device__ __forceinline__ void finish(int s, Acc& acc, F&& store) const {
+        const bool h = (lane & 32) != 0;
+        const bool g = (lane & 16) != 0;
+        const int partner = (lane ^ 32) << 2;
+        auto bperm = [&](float v) {
+            return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(partner, __builtin_bit_cast(int, v)));
+        };
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const float b01 = (h ? acc.a1[i] : acc.a0[i]) + bperm(h ? acc.a0[i] : acc.a1[i]);
+            const float b23 = (h ? acc.a3[i] : acc.a2[i]) + bperm(h ? acc.a2[i] : acc.a3[i]);
+            const float t = g ? b01 : b23;
+            const float sw =
+                __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, t), 0x401F));
+            const float e = row16_sum((g ? b23 : b01) + sw);
+            acc.a0[i] = acc.a1[i] = acc.a2[i] = acc.a3[i] = 0.0f;
+            if ((lane & 15) == 0)
+                store((int64_t)s * (WAVES * 4 * R) + wrow0 + 4 * i + (g ? 2 : 0) + (h ? 1 : 0), e);
+        }
+    }
+};
+
+
+// The fields of a GEMV the sweep kernel keeps in scalar registers.
+struct Live {
+    const uint8_t* w;
+    const uint16_t* x;
+    float* y;
+    int32_t n, k, npl, steps;
+    int64_t cost_begin;
+};
+
+__device__ __forceinline__ Live live_of(const PlanDesc& p) {
+    Live l;
+    l.w = p.w;
+    l.x = p.x;
+    l.y = p.y;
+    l.n = (int32_t)p.n;
+    l.k = p.k;
+    l.npl = p.npl;
+    l.steps = (int32_t)p.steps;
+    l.cost_begin = p.cost_begin;
+    return l;
 }
 
 // The sweep kernel.  A workgroup works through chunks; a chunk is the row
 // steps from (d0, s0) on, in list order, that start before cost c_end.
-//  * Single GEMV / LM head (head == nullptr): one chunk per workgroup, its
+//  * Single GEMV / LM head (BATCH false): one chunk per workgroup, its
 //    byte-balanced share [T*g/G, T*(g+1)/G) of the one descriptor `one`.
-//  * Batch (head != nullptr): chunk g of the plan's schedule first, then
-//    further chunks taken from the shared counter head->next as the workgroup
-//    runs out of work, so workgroups that stream faster take more.  Chunk ids
-//    travel through two LDS slots: at its t-th chunk change the workgroup
-//    reads the id of chunk t+1 from q_next[(t+1)&1] and fetches that chunk's
-//    entry; in the following half-step lane 0 takes the id of chunk t+2 from
-//    the counter before that half-step's loads and stores it to q_next[t&1]
-//    after its compute, when the atomic has long returned.  The schedule
-//    gives every chunk but the list's last at least two units, so chunk
-//    changes are at least one half-step apart.  The last workgroup to finish
-//    resets the counters for the next launch.
-// Every wave walks the same unit sequence (its own rows of each step), so the
-// barriers of chunk changes and activation staging are reached by all.
-template <class E, int NB, int XS, bool ARGMAX>
+//  * Batch: chunk g of the plan's schedule first, then further chunks taken
+//    from the shared counter head->next as the workgroup runs out of work, so
+//    workgroups that stream faster take more.  Chunk ids travel through two
+//    LDS slots: at its t-th chunk change the workgroup reads the id of chunk
+//    t+1 from q_next[(t+1)&1] and fetches that chunk's entry; in the
+//    following step lane 0 takes the id of chunk t+2 from the counter before
+//    that step's loads and stores it to q_next[t&1] after its compute, when
+//    the atomic has long returned.  The schedule gives every chunk but the
+//    list's last at least two units, so chunk changes are at least one step
+//    apart.  The last workgroup to finish resets the counters for the next
+//    launch.
+// Every wave walks the same unit sequence (its own rows of each row step), so
+// the barriers of chunk changes and activation staging are reached by all.
+// The NB-slot ring of each wave: the slot of the unit being computed is
+// refilled once its pairs are read, so NB units are in flight during the math.
+template <class E, int XS, bool BATCH, bool ARGMAX>
 __global__ void __launch_bounds__(E::kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
 k_sweep(const PlanDesc* __restrict__ descs, int count, SchedHead* head, const SchedChunk* __restrict__ chunks,
-        PlanDesc one, int64_t total, int xs_bytes, uint64_t* __restrict__ keys) {
-    static_assert(NB == 2, "two slots per wave: the slot of the unit being computed is refilled once its pairs are read");
+        PlanDesc one, int xs_bytes, uint64_t* __restrict__ keys) {
+    constexpr int NB = E::kNB;
     extern __shared__ u4 xs[];
     __shared__ int q_next[2];  // ids of this workgroup's coming chunks (batch schedule)
-    constexpr int R = E::kR;
-    constexpr int JB = E::kJB;
     E eng;
     eng.init(reinterpret_cast<uint8_t*>(xs) + xs_bytes +
              __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) * E::kWaveLds);
-    const bool dyn = head != nullptr;  // uniform
-    const int n_desc = descs ? count : 1;
-    auto get = [&](int d) -> PlanDesc { return descs ? descs[d] : one; };
+    const int n_desc = BATCH ? count : 1;
+    auto get = [&](int d) -> Live { return live_of(BATCH ? descs[d] : one); };
 
     // The workgroup's first chunk.
-    Cursor cl;       // next unit to load
-    int64_t hl;      // end (cost) of the chunk being loaded
+    int cl_d, cl_s, cl_jb;  // next unit to load: descriptor, row step, unit within the step
+    int64_t hl;             // end (cost) of the chunk being loaded
     bool have_l;
-    PlanDesc Dl;
-    if (dyn) {
+    Live Dl;
+    if (BATCH) {
         const SchedChunk ch = chunks[blockIdx.x];
-        cl.d = ch.d0;
-        cl.s = ch.s0;
+        cl_d = ch.d0;
+        cl_s = ch.s0;
         hl = ch.c_end;
         have_l = true;
     } else {
+        const int64_t total = (int64_t)one.steps * one.npl;
         const int64_t G = gridDim.x;
         const int64_t c_lo = uniform64((total / G) * blockIdx.x + ((total % G) * blockIdx.x) / G);
         hl = uniform64((total / G) * (blockIdx.x + 1) + ((total % G) * ((int64_t)blockIdx.x + 1)) / G);
-        cl.d = 0;
-        cl.s = uniform64((c_lo + one.npl - 1) / one.npl);
-        have_l = cl.s < one.steps && cl.s * one.npl < hl;
+        cl_d = 0;
+        cl_s = (int)uniform64((c_lo + one.npl - 1) / one.npl);
+        have_l = cl_s < one.steps && (int64_t)cl_s * one.npl < hl;
     }
-    cl.jb = 0;
-    if (have_l) Dl = get(cl.d);
+    cl_jb = 0;
+    if (have_l) Dl = get(cl_d);
 
     const int n_static = gridDim.x;
-    const int n_chunks = dyn ? head->nchunks : 0;
+    const int n_chunks = BATCH ? head->nchunks : 0;
     SchedChunk nx;         // entry of the chunk after the one being loaded
     bool nx_ok = false;
     int trans = 0;         // chunk changes so far
-    bool grab = false;     // this half-step takes a chunk id from the counter
+    bool grab = false;     // this step takes a chunk id from the counter
     uint32_t pending = 0;  // lane 0: the id taken
-    if (dyn) {
+    if (BATCH) {
         if (threadIdx.x == 0) {
             q_next[1] = n_static + (int)atomicAdd(&head->next, 1u);
             q_next[0] = n_static + (int)atomicAdd(&head->next, 1u);
@@ -413,11 +662,20 @@ k_sweep(const PlanDesc* __restrict__ descs, int count, SchedHead* head, const Sc
     // Move the load cursor one unit on; at the end of a chunk go to the next
     // one (batch) or stop.
     auto advance_l = [&]() {
-        Cursor c2 = next_unit(Dl, cl, JB);
-        if (c2.d < n_desc) {
-            if (c2.d != cl.d) Dl = get(c2.d);
-            if (Dl.cost_begin + c2.s * Dl.npl < hl) {
-                cl = c2;
+        int d2 = cl_d, s2 = cl_s, jb2 = cl_jb + 1;
+        if (jb2 >= Dl.npl) {
+            jb2 = 0;
+            if (++s2 == Dl.steps) {
+                ++d2;
+                s2 = 0;
+            }
+        }
+        if (d2 < n_desc) {
+            if (d2 != cl_d) Dl = get(d2);
+            if (Dl.cost_begin + (int64_t)s2 * Dl.npl < hl) {
+                cl_d = d2;
+                cl_s = s2;
+                cl_jb = jb2;
                 return;
             }
         }
@@ -425,11 +683,11 @@ k_sweep(const PlanDesc* __restrict__ descs, int count, SchedHead* head, const Sc
             have_l = false;
             return;
         }
-        cl.d = nx.d0;
-        cl.s = nx.s0;
-        cl.jb = 0;
+        cl_d = nx.d0;
+        cl_s = nx.s0;
+        cl_jb = 0;
         hl = nx.c_end;
-        Dl = get(cl.d);
+        Dl = get(cl_d);
         ++trans;
         __syncthreads();  // q_next[(trans+1)&1] is written and q_next[trans&1] read by every wave
         const int id = __builtin_amdgcn_readfirstlane(q_next[(trans + 1) & 1]);
@@ -440,36 +698,30 @@ k_sweep(const PlanDesc* __restrict__ descs, int count, SchedHead* head, const Sc
 
     uint64_t best = 0;
     if (have_l) {
-        // Unit ring: the next unit's loads are issued before the current one
-        // is computed, across row groups, GEMVs and chunks.
-        struct Rec {  // a loaded unit: descriptor, row step, pair-per-lane index
-            int32_t d;
-            int32_t jb;
-            int64_t s;
-            bool valid;
+        struct Rec {  // a unit in a slot: descriptor (-1: none), row step, unit within the step
+            int32_t d, s, jb;
         };
-        auto record = [&](Rec& r) {
-            r.d = cl.d;
-            r.jb = cl.jb;
-            r.s = cl.s;
-        };
-        typename E::Buf B0, B1;
-        eng.init_buf(B0, 0);
-        eng.init_buf(B1, 1);
-        Rec R0, R1;
-        float acc[R];
-#pragma unroll
-        for (int i = 0; i < R; ++i) acc[i] = 0.0f;
+        Rec RR[NB];
+        typename E::Acc acc;
+        eng.init_acc(acc);
+        uint32_t n_issued = 0, n_done = 0;  // units issued, units computed
         int dc = -1;      // descriptor held in Dc (compute side)
         int staged = -1;  // descriptor whose activations are in LDS
-        PlanDesc Dc;
+        Live Dc;
 
-        // One half-step on the unit in (r, b): take a chunk id if one is
-        // owed, stage the activations if the GEMV changed, read the unit's
-        // pairs, refill its slot with the next unit to load (so two units
-        // are in flight during the math), compute, store the taken id.
-        // Returns whether the unit after this one (r_next) is loaded.
-        auto half_step = [&](Rec& r, typename E::Buf& b, const Rec& r_next) -> bool {
+        auto issue_next = [&](Rec& r, int slot) {
+            r.d = cl_d;
+            r.s = cl_s;
+            r.jb = cl_jb;
+            eng.issue(Dl, cl_s, cl_jb, slot);
+            ++n_issued;
+            advance_l();
+        };
+        // One step on the unit in (r, slot): take a chunk id if one is owed,
+        // stage the activations if the GEMV changed, read the unit's pairs,
+        // refill its slot with the next unit to load, compute, store the
+        // taken id.  Returns whether the unit after this one (r_next) is loaded.
+        auto step = [&](Rec& r, int slot, const Rec& r_next) -> bool {
             const bool took = grab;
             grab = false;
             if (took && threadIdx.x == 0) pending = atomicAdd(&head->next, 1u);
@@ -484,49 +736,43 @@ k_sweep(const PlanDesc* __restrict__ descs, int count, SchedHead* head, const Sc
                 __syncthreads();
                 staged = u.d;
             }
-            uint32_t W[R][9];
-            eng.fetch(Dc.k, u.jb, b, W);
-            r.valid = have_l;
-            if (have_l) {
-                record(r);
-                eng.issue(Dl, cl, b);
-                advance_l();
-            }
-            eng.math(Dc.npl, u.jb, xs, W, acc);
-            if (u.jb + JB >= Dc.npl) {  // last unit of this row group
-                const int64_t r0 = u.s * (int64_t)(E::kWaves * 4 * R) + eng.rr0;
-#pragma unroll
-                for (int i = 0; i < R; ++i) {
-                    const float v = row16_sum(acc[i]);
-                    acc[i] = 0.0f;
-                    if (eng.l16 == 0 && r0 + i < Dc.n) {
-                        ((g_f32*)Dc.y)[r0 + i] = v;
+            typename E::Regs W;
+            eng.fetch(Dc, u.s, u.jb, slot, n_issued - 1u - n_done, W);
+            ++n_done;
+            if (have_l)
+                issue_next(r, slot);
+            else
+                r.d = -1;
+            eng.math(Dc, u.jb, xs, W, acc);
+            if (u.jb + 1 >= Dc.npl) {  // last unit of the wave's rows in this step
+                eng.finish(u.s, acc, [&](int64_t row, float v) {
+                    if (row < Dc.n) {
+                        ((g_f32*)Dc.y)[row] = v;
                         if (ARGMAX) {
-                            const uint64_t kk = argmax_key(v, r0 + i);
+                            const uint64_t kk = argmax_key(v, row);
                             best = kk > best ? kk : best;
                         }
                     }
-                }
+                });
             }
             if (took && threadIdx.x == 0) q_next[trans & 1] = n_static + (int)pending;
-            return r_next.valid;
+            return r_next.d >= 0;
         };
-        R0.valid = true;
-        record(R0);
-        eng.issue(Dl, cl, B0);
-        advance_l();
-        R1.valid = have_l;
-        if (have_l) {
-            record(R1);
-            eng.issue(Dl, cl, B1);
-            advance_l();
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            if (have_l)
+                issue_next(RR[i], i);
+            else
+                RR[i].d = -1;
         }
-        for (;;) {
-            if (!half_step(R0, B0, R1)) break;
-            if (!half_step(R1, B1, R0)) break;
+        bool go = true;
+        while (go) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i)
+                if (go) go = step(RR[i], i, RR[(i + 1) % NB]);
         }
     }
-    if (dyn && threadIdx.x == 0) {
+    if (BATCH && threadIdx.x == 0) {
         __threadfence();  // this workgroup's grabs are complete
         if (atomicAdd(&head->done, 1u) == gridDim.x - 1) {
             atomicExch(&head->next, 0u);
@@ -640,41 +886,54 @@ static PlanDesc single_desc(const uint8_t* w, const uint16_t* x, float* y, int64
     return d;
 }
 
-// The sweep engine for a workgroup shape and an activation stride.
-template <int WAVES, int R, int XS>
-using SweepEngine = DmaEngine<WAVES, R, kNB, XS>;
+static bool quad_ok(int64_t k) { return k % 1024 == 0 && k >= 4096; }
 
-template <int WAVES, int R, int XS, bool AM>
+template <class E, int XS, bool BATCH, bool AM>
 static hipError_t launch_sweep(const PlanDesc* descs, int count, SchedHead* head, const SchedChunk* chunks,
-                               const PlanDesc& one, int64_t total, int64_t max_k, int grid, uint64_t* keys,
-                               hipStream_t s) {
-    using E = SweepEngine<WAVES, R, XS>;
+                               const PlanDesc& one, int64_t max_k, int grid, uint64_t* keys, hipStream_t s) {
     const size_t xsb = x_lds_bytes(max_k);
-    const size_t lds = xsb + (size_t)WAVES * E::kWaveLds;
-    auto kern = k_sweep<E, kNB, XS, AM>;
+    const size_t lds = xsb + (size_t)E::kWaves * E::kWaveLds;
+    auto kern = k_sweep<E, XS, BATCH, AM>;
     if (lds > 65536) {
         const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVES * 64), lds, s, descs, count, head, chunks, one, total, (int)xsb,
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(E::kWaves * 64), lds, s, descs, count, head, chunks, one, (int)xsb,
                        keys);
     return hipGetLastError();
 }
 
-template <bool AM>
+// The kernel of a shape, for the activation stride max_k needs.
+template <class E, class EV, bool BATCH, bool AM>
+static hipError_t launch_stride(const PlanDesc* descs, int count, SchedHead* head, const SchedChunk* chunks,
+                                const PlanDesc& one, int64_t max_k, int grid, uint64_t* keys, hipStream_t s) {
+    return fixed_stride(max_k)
+               ? launch_sweep<E, kXStride, BATCH, AM>(descs, count, head, chunks, one, max_k, grid, keys, s)
+               : launch_sweep<EV, 0, BATCH, AM>(descs, count, head, chunks, one, max_k, grid, keys, s);
+}
+
+// A batch (descs, head, chunks) runs on a wide shape; a single GEMV passes
+// its descriptor in `one`.
+template <bool BATCH, bool AM>
 static hipError_t launch_any(const Shape& sh, const PlanDesc* descs, int count, SchedHead* head,
-                             const SchedChunk* chunks, const PlanDesc& one, int64_t total, int64_t max_k, int grid,
-                             uint64_t* keys, hipStream_t s) {
-    const bool fixed = fixed_stride(max_k);
-    if (sh.waves == kNarrow.waves && sh.r == kNarrow.r)
-        return fixed ? launch_sweep<kNarrow.waves, kNarrow.r, kXStride, AM>(descs, count, head, chunks, one, total,
-                                                                            max_k, grid, keys, s)
-                     : launch_sweep<kNarrow.waves, kNarrow.r, 0, AM>(descs, count, head, chunks, one, total, max_k,
-                                                                      grid, keys, s);
-    return fixed ? launch_sweep<kWide.waves, kWide.r, kXStride, AM>(descs, count, head, chunks, one, total, max_k,
-                                                                    grid, keys, s)
-                 : launch_sweep<kWide.waves, kWide.r, 0, AM>(descs, count, head, chunks, one, total, max_k, grid,
-                                                              keys, s);
+                             const SchedChunk* chunks, const PlanDesc& one, int64_t max_k, int grid, uint64_t* keys,
+                             hipStream_t s) {
+    constexpr int W = kWide.waves, WN = kNarrow.waves, R = kWide.r;
+    if constexpr (!BATCH) {
+        if (sh.waves == WN && sh.quad)
+            return launch_stride<QuadEngine<WN, 1, 4, kXStride>, QuadEngine<WN, 1, 4, 0>, BATCH, AM>(
+                descs, count, head, chunks, one, max_k, grid, keys, s);
+        if (sh.waves == WN)
+            return launch_stride<DmaEngine<WN, kNarrow.r, kXStride>, DmaEngine<WN, kNarrow.r, 0>, BATCH, AM>(
+                descs, count, head, chunks, one, max_k, grid, keys, s);
+    }
+    if (sh.quad)
+        return launch_stride<QuadEngine<kQuadWide.waves, kQuadWide.r, kQuadNB, kXStride>,
+                             QuadEngine<kQuadWide.waves, kQuadWide.r, kQuadNB, 0>,
+                             BATCH, AM>(
+            descs, count, head, chunks, one, max_k, grid, keys, s);
+    return launch_stride<DmaEngine<W, R, kXStride>, DmaEngine<W, R, 0>, BATCH, AM>(descs, count, head, chunks, one,
+                                                                                  max_k, grid, keys, s);
 }
 
 // Workgroups for a static split of `steps` row steps.
@@ -685,31 +944,33 @@ static int static_grid(int64_t steps, const Shape& sh, int cap) {
 
 // Shape for a single GEMV of n rows: the wide one when it gives every CU two
 // workgroups of work, else the narrow one.
-static const Shape& single_shape(int64_t n) {
-    const int64_t wide_steps = (n + kWide.rows_per_step() - 1) / kWide.rows_per_step();
-    return wide_steps >= 2 * (int64_t)device_cu_count() ? kWide : kNarrow;
+static const Shape& single_shape(int64_t n, int64_t k) {
+    const bool quad = quad_ok(k);
+    const Shape& wide = quad ? kQuadWide : kWide;
+    const int64_t wide_steps = (n + wide.rows_per_step() - 1) / wide.rows_per_step();
+    if (wide_steps >= 2 * (int64_t)device_cu_count()) return wide;
+    return quad ? kQuadNarrow : kNarrow;
 }
 
 hipError_t launch_gemv(const uint8_t* w, const uint16_t* x, float* y, int64_t n, int64_t k,
                        hipStream_t s) {
-    const Shape& sh = single_shape(n);
+    const Shape& sh = single_shape(n, k);
     const PlanDesc d = single_desc(w, x, y, n, k, sh);
-    return launch_any<false>(sh, nullptr, 1, nullptr, nullptr, d, d.steps * d.npl, k,
-                             static_grid(d.steps, sh, INT32_MAX), nullptr, s);
+    return launch_any<false, false>(sh, nullptr, 1, nullptr, nullptr, d, k, static_grid(d.steps, sh, INT32_MAX),
+                                    nullptr, s);
 }
 
 int argmax_blocks(int64_t n, int64_t k) {
-    (void)k;
-    const Shape& sh = single_shape(n);
+    const Shape& sh = single_shape(n, k);
     return static_grid((n + sh.rows_per_step() - 1) / sh.rows_per_step(), sh, kArgmaxMaxBlocks);
 }
 
 hipError_t launch_lm_head(const uint8_t* w, const uint16_t* h, float* logits, int32_t* token,
                           int64_t n, int64_t k, uint64_t* keys, hipStream_t s) {
-    const Shape& sh = single_shape(n);
+    const Shape& sh = single_shape(n, k);
     const PlanDesc d = single_desc(w, h, logits, n, k, sh);
     const int grid = argmax_blocks(n, k);
-    hipError_t e = launch_any<true>(sh, nullptr, 1, nullptr, nullptr, d, d.steps * d.npl, k, grid, keys, s);
+    hipError_t e = launch_any<false, true>(sh, nullptr, 1, nullptr, nullptr, d, k, grid, keys, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_argmax_final, dim3(1), dim3(kFinalThreads), 0, s, keys, grid, token);
     return hipGetLastError();
@@ -734,7 +995,10 @@ hipError_t launch_gemm_generic(const uint8_t* w, const uint16_t* x, float* y, in
 // shapes and the device's CU count.
 static constexpr double kStaticShare = 0.6;
 
-void build_schedule(PlanDesc* descs, int count, std::vector<SchedChunk>* out, int* grid_out) {
+void build_schedule(PlanDesc* descs, int count, std::vector<SchedChunk>* out, int* grid_out, int* flags_out) {
+    bool quad = true;
+    for (int i = 0; i < count; ++i) quad = quad && quad_ok(descs[i].k);
+    const Shape& sh = quad ? kQuadWide : kWide;
     struct Atom {
         int32_t d, s;
         int64_t cost;  // start cost of its first step
@@ -745,7 +1009,7 @@ void build_schedule(PlanDesc* descs, int count, std::vector<SchedChunk>* out, in
     for (int i = 0; i < count; ++i) {
         PlanDesc& p = descs[i];
         p.npl = npl_of(p.k);
-        p.steps = (p.n + kWide.rows_per_step() - 1) / kWide.rows_per_step();
+        p.steps = (p.n + sh.rows_per_step() - 1) / sh.rows_per_step();
         p.cost_begin = total;
         const int units = p.npl;  // one unit per 16 pairs of a row
         for (int64_t st = 0; st < p.steps; ++st) {
@@ -759,7 +1023,7 @@ void build_schedule(PlanDesc* descs, int count, std::vector<SchedChunk>* out, in
     }
     if (open_units < 2 && atoms.size() > 1) atoms.pop_back();  // a lone one-unit step joins the atom before it
     const int64_t n_atoms = (int64_t)atoms.size();
-    const int grid = static_grid(n_atoms, kWide, INT32_MAX);
+    const int grid = static_grid(n_atoms, sh, INT32_MAX);
     out->clear();
     int64_t a = 0;
     auto cost_at = [&](int64_t i) { return i < n_atoms ? atoms[i].cost : total; };
@@ -782,16 +1046,19 @@ void build_schedule(PlanDesc* descs, int count, std::vector<SchedChunk>* out, in
     }
     out->back().c_end = total;
     *grid_out = grid;
+    *flags_out = quad ? kPlanQuad : 0;
 }
 
-hipError_t launch_gemv_batch(const void* plan, int count, int nchunks, int grid, int max_k, hipStream_t s) {
+hipError_t launch_gemv_batch(const void* plan, int count, int nchunks, int grid, int max_k, int flags,
+                             hipStream_t s) {
     (void)nchunks;
     const uint8_t* base = static_cast<const uint8_t*>(plan);
     SchedHead* head = (SchedHead*)base;
     const PlanDesc* descs = (const PlanDesc*)(base + sizeof(SchedHead));
     const SchedChunk* chunks = (const SchedChunk*)(base + sizeof(SchedHead) + (size_t)count * sizeof(PlanDesc));
     PlanDesc none = {};
-    return launch_any<false>(kWide, descs, count, head, chunks, none, 0, max_k, grid, nullptr, s);
+    return launch_any<true, false>((flags & kPlanQuad) ? kQuadWide : kWide, descs, count, head, chunks, none, max_k,
+                                   grid, nullptr, s);
 }
 
 }  // namespace q4

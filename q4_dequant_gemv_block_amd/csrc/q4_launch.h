@@ -18,7 +18,7 @@ struct PlanDesc {
     int64_t n;
     int32_t k;
     int32_t npl;         // pairs per lane: ceil(k/64 / 16)
-    int64_t steps;       // row steps of kBatchRows rows
+    int64_t steps;       // row steps of the engine's rows per step
     int64_t cost_begin;  // sum of steps*npl over the earlier descriptors
 };
 
@@ -41,10 +41,13 @@ struct SchedChunk {
     int64_t c_end;
 };
 
+// Plan flag: the list runs on the quad engine (every k a multiple of 1024, at least 4096).
+constexpr int kPlanQuad = 1;
+
 // Fills npl, steps and cost_begin of descs[0..count) and cuts the list into
 // chunks for the current device; *grid is the launch's workgroup count (the
-// number of chunks assigned statically).
-void build_schedule(PlanDesc* descs, int count, std::vector<SchedChunk>* out, int* grid);
+// number of chunks assigned statically), *flags the plan flags.
+void build_schedule(PlanDesc* descs, int count, std::vector<SchedChunk>* out, int* grid, int* flags);
 
 // Largest k the LDS-staged fast path takes (activation chunks fit in 64 KiB).
 constexpr int64_t kFastMaxK = 32768;
@@ -106,6 +109,7 @@ int argmax_blocks(int64_t n, int64_t k);
 hipError_t launch_lm_head(const uint8_t* w, const uint16_t* h, float* logits, int32_t* token,
                           int64_t n, int64_t k, uint64_t* keys, hipStream_t s);
 // `plan`: SchedHead, then `count` PlanDesc, then `nchunks` SchedChunk.
-hipError_t launch_gemv_batch(const void* plan, int count, int nchunks, int grid, int max_k, hipStream_t s);
+hipError_t launch_gemv_batch(const void* plan, int count, int nchunks, int grid, int max_k, int flags,
+                             hipStream_t s);
 
 }  // namespace q4
