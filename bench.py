@@ -177,7 +177,7 @@ def bench_sweep(args):
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": counter_traffic("sweep"),
-                     "kernel": "q4::k_sweep<DmaEngine<2,2,288>> (batch)", "launches_per_step": 1},
+                     "kernel": "q4::k_sweep<QuadEngine<12,2,2,288>> (batch)", "launches_per_step": 1},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(ids)
@@ -212,7 +212,7 @@ def bench_gemv(args):
             "hot_cache_GBps": round(bytes_ / (hot_ms * 1e-3) / 1e9, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counter_traffic("gemv"),
-                         "kernel": "q4::k_sweep<DmaEngine<2,2,288>>"}}
+                         "kernel": "q4::k_sweep<QuadEngine<4,1,4,288>>"}}
 
 
 def bench_lmhead(args):
@@ -234,7 +234,7 @@ def bench_lmhead(args):
             "data": "synthetic", "config": {"workload": "LM head 151936x5120 + argmax"},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counter_traffic("lmhead"),
-                         "kernel": "q4::k_sweep<DmaEngine<2,2,288>,ARGMAX> + q4::k_argmax_final"}}
+                         "kernel": "q4::k_sweep<QuadEngine<12,2,2,288>,ARGMAX> + q4::k_argmax_final"}}
 
 
 def bench_gemm(args, prefill: bool):
@@ -329,8 +329,10 @@ def record_traffic(workload: str, kernel: str, fetch_csv: str, write_csv: str, c
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=30)
+    # the first launches after the inputs are written run slower (about 40 %
+    # on the first one, settling within about ten launches of the sweep)
+    ap.add_argument("--warmup", type=int, default=25)
     ap.add_argument("--workload", default="sweep", choices=["sweep", "gemv", "lmhead", "smallm", "prefill", "copy"])
     ap.add_argument("--m", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")

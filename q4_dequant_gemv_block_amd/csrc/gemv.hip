@@ -7,32 +7,31 @@
 // Tabs", originshq.com, section "The Engine: ~50 WGSL Kernels Written From
 // Scratch").  The kernels keep that structure, laid out for CDNA4:
 //
-//  * 16 lanes (one DPP row) own one weight row; lane l takes block pairs
-//    l, l+16, l+32, ...; a wave's unit is 4 rows x one 576-byte segment
-//    (16 pairs) per row.
-//  * Weights move from HBM straight into LDS: one global_load_lds_dwordx4 per
-//    row segment, 36 lanes x 16 contiguous bytes with the non-temporal hint,
-//    so every 128-byte line is requested once and no registers hold loads in
-//    flight.  Each wave keeps a ring of units in its own LDS window and waits
-//    for a unit with an explicit vmcnt before reading its pairs back.
+//  * Weights move from HBM straight into LDS with the non-temporal hint, so
+//    no registers hold loads in flight.  For K a multiple of 1024 (the quad
+//    engine) four consecutive rows are a whole number of 2304-byte slabs, 18
+//    aligned 128-byte lines each, and every line is requested once; other K
+//    load 576-byte row segments (the segment engine).  Each wave keeps a ring
+//    of units in its own LDS window and waits for a unit with an explicit
+//    vmcnt before reading its pairs back.
 //  * 4-bit codes become exact (code - 8) f16 pairs with one v_and_or_b32 and
 //    one v_pk_add_f16 per pair and meet the activations in v_dot2_f32_f16; the
-//    block scale is applied once per block in f32 (v_fma_mix).
+//    block scale is applied once per block in f32.
 //  * The activation vector is staged once per workgroup and GEMV into LDS in
 //    the chunk order of q4_device.h, at a fixed chunk stride so every LDS read
 //    is one base register plus an immediate offset.
-//  * Units at the end of a matrix (rows past N, or K not a multiple of 1024)
-//    read clamped rows and only the bytes of the row; pairs past the row end
-//    get zero scales and meet zero activations, padding rows are never stored.
-//  * The row sum is a fixed-order DPP tree inside the 16-lane row, so results
-//    are deterministic and independent of where a row sits or which
-//    workgroup computed it.
+//  * Rows past N are never stored; their loads read zeros (quad engine) or
+//    clamped rows (segment engine), and pairs past a row's end get zero scales.
+//  * Every row is summed in one fixed association in both engines, so results
+//    are deterministic and independent of where a row sits, which engine ran
+//    it, or which workgroup computed it.
 //
-// Work split: a work item is a row step (64 rows) of one GEMV; its cost is
-// proportional to its bytes.  The single GEMV and the LM head split their
-// steps statically into byte-balanced contiguous ranges; a batch follows the
-// plan's schedule (a static first chunk per workgroup, then chunks taken from
-// a shared counter), so workgroups that stream faster take more work.
+// Work split: a work item is a row step (96 rows in the wide shapes) of one
+// GEMV; its cost is proportional to its bytes.  The single GEMV and the LM
+// head split their steps statically into byte-balanced contiguous ranges; a
+// batch follows the plan's schedule (a static first chunk per workgroup, then
+// chunks taken from a shared counter), so workgroups that stream faster take
+// more work.
 #include "q4_device.h"
 #include "q4_launch.h"
 
