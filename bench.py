@@ -42,11 +42,21 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources and build flags, comments and blank space
+    left out (so an edited comment does not invalidate a measurement)."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "q4_dequant_gemv_block_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+    files = [os.path.join(csrc, n) for n in sorted(os.listdir(csrc))]
+    files.append(os.path.join(ROOT, "q4_dequant_gemv_block_amd", "build.py"))
+    for path in files:
+        with open(path) as f:
+            text = f.read()
+        if not path.endswith(".py"):
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
+        text = " ".join(text.split())
+        h.update(os.path.basename(path).encode() + b"\0" + text.encode())
     return h.hexdigest()[:16]
 
 
