@@ -426,15 +426,23 @@ struct QuadEngine {
         int rc;  // quad row of the slab's first pair (uniform)
         int nb;  // first pair of quad row rc + 1, from the quad start (uniform)
     };
+    typedef const __attribute__((address_space(3))) uint32_t* lds_u32;
     int lane;
-    uint32_t wrow0;  // first row of this wave within a step
-    uint8_t* wl;     // this wave's ring
+    uint32_t lane16;  // 16 * lane: this lane's byte offset in a chunk row of the activations
+    uint32_t wrow0;   // first row of this wave within a step
+    uint8_t* wl;      // this wave's ring
+    lds_u32 rd[NB][R];  // this lane's pair in each slot and quad
 
     __device__ __forceinline__ void init(uint8_t* window) {
         lane = threadIdx.x & 63;
+        lane16 = (uint32_t)lane * 16u;
         const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
         wrow0 = (uint32_t)(wave * 4 * R);
         wl = window;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int i = 0; i < R; ++i) rd[b][i] = (lds_u32)(window + b * kSlot + i * kSlab + kPairBytes * lane);
     }
     __device__ __forceinline__ void init_acc(Acc& a) const {
 #pragma unroll
@@ -477,11 +485,10 @@ struct QuadEngine {
         (void)s;
         (void)jb;
         wait_unit<kLoads, kNB>(after);
-        const uint32_t* p = (const uint32_t*)(wl + slot * kSlot + kPairBytes * lane);
 #pragma unroll
         for (int i = 0; i < R; ++i)
 #pragma unroll
-            for (int c = 0; c < 9; ++c) W.d[i][c] = p[i * (kSlab / 4) + c];
+            for (int c = 0; c < 9; ++c) W.d[i][c] = rd[slot][i][c];
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the reads are done before the slot is reloaded
     }
 
@@ -496,11 +503,13 @@ struct QuadEngine {
         }
         const int b = acc.nb - o;  // lanes >= b hold pairs of row rc + 1 (b >= 64: none)
         const bool next = lane >= b;
-        const int p = o - (acc.nb - np) + lane - (next ? np : 0);  // pair within its row
+        // pair within its row, as a byte offset of its activation chunk row:
+        // 16 * (o - (nb - np) + lane - (next ? np : 0))
+        const uint32_t px = lane16 + (uint32_t)(16 * (o - acc.nb + np)) + (next ? (uint32_t)(-16 * np) : 0u);
         const int stride = XS > 0 ? XS : Dp.npl * 16;
         float s0[R], s1[R];
-        block_sums<R>(W.d, xs + p, stride, s0, s1);
-        // one row: A = pair_acc(A, ...) in place
+        block_sums<R>(W.d, (const u4*)((const uint8_t*)xs + px), stride, s0, s1);
+        // one row: A = pair_acc(A, ...) in place, the f16 scales read as they are
         auto one = [&](float(&A)[R]) {
 #pragma unroll
             for (int i = 0; i < R; ++i) A[i] = pair_acc(A[i], f16_lo(W.d[i][0]), s0[i], f16_hi(W.d[i][4]), s1[i]);
@@ -510,9 +519,10 @@ struct QuadEngine {
         auto two = [&](float(&A)[R], float(&B)[R]) {
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                const float d0 = f16_lo(W.d[i][0]), d1 = f16_hi(W.d[i][4]);
-                A[i] = pair_acc(A[i], next ? 0.0f : d0, s0[i], next ? 0.0f : d1, s1[i]);
-                B[i] = pair_acc(B[i], next ? d0 : 0.0f, s0[i], next ? d1 : 0.0f, s1[i]);
+                const uint32_t w0 = W.d[i][0], w4 = W.d[i][4];
+                const uint32_t z0 = w0 & 0xFFFF0000u, z4 = w4 & 0x0000FFFFu;  // scale zeroed
+                A[i] = pair_acc(A[i], f16_lo(next ? z0 : w0), s0[i], f16_hi(next ? z4 : w4), s1[i]);
+                B[i] = pair_acc(B[i], f16_lo(next ? w0 : z0), s0[i], f16_hi(next ? w4 : z4), s1[i]);
             }
         };
         if (b >= 64) {
@@ -983,7 +993,8 @@ hipError_t launch_gemm_generic(const uint8_t* w, const uint16_t* x, float* y, in
     return hipGetLastError();
 }
 
-// Schedule of a batch.  Row steps are taken in list order and grouped into
+// Schedule of a batch.  The list is reordered (larger row steps first, list
+// order kept otherwise); row steps are then taken in that order and grouped into
 // atoms of at least two units (a step of one unit, k <= 1024, is paired with
 // the next), so a chunk made of whole atoms has at least two units, as the
 // kernel's chunk-id hand-over requires.  The first `grid` chunks (one per
@@ -995,6 +1006,10 @@ hipError_t launch_gemm_generic(const uint8_t* w, const uint16_t* x, float* y, in
 static constexpr double kStaticShare = 0.6;
 
 void build_schedule(PlanDesc* descs, int count, std::vector<SchedChunk>* out, int* grid_out, int* flags_out) {
+    // GEMVs with more units per row step first: the chunks handed out last
+    // are then the shortest, and so is the wait for the last workgroup.
+    std::stable_sort(descs, descs + count,
+                     [](const PlanDesc& a, const PlanDesc& b) { return npl_of(a.k) > npl_of(b.k); });
     bool quad = true;
     for (int i = 0; i < count; ++i) quad = quad && quad_ok(descs[i].k);
     const Shape& sh = quad ? kQuadWide : kWide;

@@ -44,7 +44,8 @@ struct SchedChunk {
 // Plan flag: the list runs on the quad engine (every k a multiple of 1024, at least 4096).
 constexpr int kPlanQuad = 1;
 
-// Fills npl, steps and cost_begin of descs[0..count) and cuts the list into
+// Orders descs[0..count) by row-step size (largest first, stable), fills
+// npl, steps and cost_begin and cuts the list into
 // chunks for the current device; *grid is the launch's workgroup count (the
 // number of chunks assigned statically), *flags the plan flags.
 void build_schedule(PlanDesc* descs, int count, std::vector<SchedChunk>* out, int* grid, int* flags);

@@ -66,6 +66,9 @@ def test_schedule_partitions_the_row_steps():
                       torch.empty(n, dtype=torch.float32, device=device())))
     batch = q4.GemvBatch(items)
     nxt, done, nchunks, grid, descs, chunks = _read_plan(batch)
+    # the plan holds the list ordered by row-step size, largest first (stable)
+    shapes = [shapes[i] for i in sorted(range(len(shapes)), key=lambda i: (-(shapes[i][1] // 64)) // 16)]
+    assert [int(d["k"]) for d in descs] == [k for _, k in shapes]
     assert (nxt, done) == (0, 0)
     assert nchunks == batch.plan.nchunks and grid == batch.plan.grid and 1 <= grid <= nchunks
     # the plan's row steps: every descriptor's step count fits one rows-per-step value
