@@ -75,8 +75,12 @@ struct SmCursor {
     int d, c, t, jb;
 };
 
+// Row stride of the staged activations, in 16-byte chunks: odd, so the 16
+// activation rows that a wave reads at once fall on different LDS banks.
+__device__ __forceinline__ int x_stride(const SmDesc& D) { return 8 * D.P + 1; }
+
 // Activations of pairs [c*P, c*P + 16*segs) of all M rows into
-// xs[(pl * 8 + chunk) * m + row]; pairs past K/64 are zero.
+// xs[row * x_stride + pl * 8 + chunk]; pairs past K/64 are zero.
 __device__ void stage_range(const SmDesc& D, int c, int m, u4* __restrict__ xs) {
     const int p0 = c * D.P;
     const int npairs = 16 * segs_of(D, c);
@@ -109,7 +113,7 @@ __device__ void stage_range(const SmDesc& D, int c, int m, u4* __restrict__ xs) 
             ent.y = xe(a + 16) | (xe(cq + 16) << 16);
             ent.z = xe(bb) | (xe(e) << 16);
             ent.w = xe(bb + 16) | (xe(e + 16) << 16);
-            xs[((b >> 1) * 8 + 4 * half + cc) * m + mm] = ent;
+            xs[mm * x_stride(D) + (b >> 1) * 8 + 4 * half + cc] = ent;
         }
     }
 }
@@ -210,10 +214,11 @@ __global__ void __launch_bounds__(kSmThreads) k_smallm(const SmDesc* __restrict_
             staged_d = r.d;
             staged_c = r.c;
         }
-        const bool arow = l16 < m;
+        // A operand rows m >= M only produce product rows that are never
+        // stored, so those lanes read activation row M - 1 (an LDS broadcast).
+        const u4* xu = xs + min(l16, m - 1) * x_stride(Dc) + (16 * r.jb + g) * 8;
 #pragma unroll
         for (int jj = 0; jj < kPairsPerLane; ++jj) {
-            const int pl = 16 * r.jb + g + 4 * jj;
             const _Float16 d0 = as_h2(b.d[jj][0]).x, d1 = as_h2(b.d[jj][4]).y;
             const h2 s0 = {d0, d0}, s1 = {d1, d1};
 #pragma unroll
@@ -226,8 +231,7 @@ __global__ void __launch_bounds__(kSmThreads) k_smallm(const SmDesc* __restrict_
                 bw.y = as_u32(q.q1 * s);
                 bw.z = as_u32(q.q2 * s);
                 bw.w = as_u32(q.q3 * s);
-                u4 ax = {0u, 0u, 0u, 0u};
-                if (arow) ax = xs[(pl * 8 + c) * m + l16];
+                const u4 ax = xu[32 * jj + c];
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, ax), __builtin_bit_cast(h8, bw),
                                                              acc, 0, 0, 0);
             }
@@ -328,8 +332,10 @@ static int smallm_grid(int64_t total) {
     return (int)std::max<int64_t>(1, std::min<int64_t>(total, (int64_t)device_cu_count()));
 }
 
+// Staged activations: m rows of max_range_pairs * 8 chunks plus one chunk of
+// padding (at most 16 * 16 bytes beyond kXBytes).
 static size_t smallm_lds(int64_t max_range_pairs, int64_t m) {
-    return (size_t)max_range_pairs * kChunksPerPair * m * sizeof(u4);
+    return (size_t)(max_range_pairs * kChunksPerPair + 1) * m * sizeof(u4);
 }
 
 static hipError_t launch_sm(const SmDesc* descs, int count, const SmDesc& one, int64_t m, int64_t total,
