@@ -250,12 +250,13 @@ Q4_API q4_status q4_0_gemm_smallm_batch(const q4_gemm_plan* plan, void* workspac
 /* Host-side handle of a prefill batch plan.  Filled by
  * q4_0_gemm_prefill_batch_plan; plain data, may be copied. */
 typedef struct q4_prefill_plan {
-    void* device;        /* the caller's device buffer holding the descriptors */
-    int count;           /* number of GEMMs */
-    int m;               /* token rows of every GEMM */
-    int tile_m;          /* internal: activation rows per tile (64 or 128) */
-    int reserved;
-    int64_t total_cost;  /* internal: 64-column steps of all tiles */
+    void* device;          /* the caller's device buffer holding the descriptors */
+    int count;             /* number of GEMMs */
+    int m;                 /* token rows of every GEMM */
+    int tile_m;            /* internal: activation rows per tile (64 or 128) */
+    int count_chunked;     /* internal: GEMMs with k % 256 == 0 (first in the device list) */
+    int64_t tiles_chunked; /* internal: their tiles */
+    int64_t tiles_other;   /* internal: tiles of the other GEMMs */
 } q4_prefill_plan;
 
 /* Device bytes q4_0_gemm_prefill_batch_plan needs for `count` descriptors. */
@@ -273,12 +274,17 @@ Q4_API size_t q4_0_gemm_prefill_batch_plan_bytes(int count);
  * Validates the list, writes its device form into `plan_buf`
  * (q4_0_gemm_prefill_batch_plan_bytes(count) bytes, 16-byte aligned) and
  * fills `*plan`; the copy has completed when this returns.  No output may
- * overlap another output, an input or the plan.
+ * overlap another output, an input or the plan.  The plan buffer also holds
+ * the launch's work counter, which every launch returns to its initial state
+ * when it completes: run one launch of a plan at a time (launches on one
+ * stream are fine; the same plan on two streams at once is not).
  */
 Q4_API q4_status q4_0_gemm_prefill_batch_plan(const q4_gemv_desc* descs, int count, int64_t m, void* plan_buf,
                                               size_t plan_bytes, q4_prefill_plan* plan, void* stream);
 
-/* Run every GEMM of a prefill plan on `stream` (one launch). */
+/* Run every GEMM of a prefill plan on `stream`: one launch, or two when the
+ * list mixes k % 256 == 0 with other k (each GEMM runs in the kernel its own
+ * q4_0_gemm_prefill call uses, so the results are the same bit for bit). */
 Q4_API q4_status q4_0_gemm_prefill_batch(const q4_prefill_plan* plan, void* stream);
 
 #ifdef __cplusplus

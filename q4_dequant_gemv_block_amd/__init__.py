@@ -246,7 +246,8 @@ class GemmPlan(ctypes.Structure):
 
 class PrefillPlan(ctypes.Structure):
     _fields_ = [("device", ctypes.c_void_p), ("count", ctypes.c_int), ("m", ctypes.c_int),
-                ("tile_m", ctypes.c_int), ("reserved", ctypes.c_int), ("total_cost", ctypes.c_int64)]
+                ("tile_m", ctypes.c_int), ("count_chunked", ctypes.c_int), ("tiles_chunked", ctypes.c_int64),
+                ("tiles_other", ctypes.c_int64)]
 
 
 class GemvBatch:

@@ -393,7 +393,7 @@ q4_status q4_0_gemm_smallm_batch(const q4_gemm_plan* plan, void* workspace, size
 
 size_t q4_0_gemm_prefill_batch_plan_bytes(int count) {
     if (count < 1 || count > (1 << 20)) return 0;
-    return (size_t)count * sizeof(q4::PfDesc);
+    return 2 * sizeof(q4::PfHead) + (size_t)count * sizeof(q4::PfDesc);
 }
 
 q4_status q4_0_gemm_prefill_batch_plan(const q4_gemv_desc* descs, int count, int64_t m, void* plan_buf,
@@ -412,38 +412,53 @@ q4_status q4_0_gemm_prefill_batch_plan(const q4_gemv_desc* descs, int count, int
     if (!aligned(plan_buf, 16)) return fail(Q4_ERR_MISALIGNED, "%s: plan buffer must be 16-byte aligned", fn);
     if (check_buffer(fn, "plan buffer", plan_buf, need, descs, count, m)) return Q4_ERR_INVALID_ARG;
     const int tile_m = q4::prefill_batch_tile_m(m);
-    std::vector<q4::PfDesc> dev(count);
-    int64_t cost = 0;
-    for (int i = 0; i < count; ++i) {
-        q4::PfDesc& d = dev[i];
-        d.w = static_cast<const uint8_t*>(descs[i].w);
-        d.x = static_cast<const uint16_t*>(descs[i].x);
-        d.y = descs[i].y;
-        d.m = m;
-        d.n = descs[i].n;
-        d.k = (int)descs[i].k;
-        cost += q4::prefill_fill(&d, tile_m, cost);
-    }
+    // Two zeroed work counters, then the descriptors with k % 256 == 0 (run by
+    // the kernel that moves weights in 144-byte chunks), then the others, each
+    // part in list order and numbering its tiles from 0.
+    std::vector<uint8_t> host(need, 0);
+    q4::PfDesc* dev = reinterpret_cast<q4::PfDesc*>(host.data() + 2 * sizeof(q4::PfHead));
+    int64_t tiles[2] = {0, 0};
+    int placed = 0;
+    for (int part = 0; part < 2; ++part)
+        for (int i = 0; i < count; ++i) {
+            if ((descs[i].k % 256 == 0) != (part == 0)) continue;
+            q4::PfDesc d = {};
+            d.w = static_cast<const uint8_t*>(descs[i].w);
+            d.x = static_cast<const uint16_t*>(descs[i].x);
+            d.y = descs[i].y;
+            d.m = m;
+            d.n = descs[i].n;
+            d.k = (int)descs[i].k;
+            tiles[part] += q4::prefill_fill(&d, tile_m, tiles[part]);
+            if (tiles[part] >= (int64_t(1) << 31)) return fail(Q4_ERR_INVALID_ARG, "%s: more than 2^31 tiles", fn);
+            std::memcpy(&dev[placed++], &d, sizeof(d));
+        }
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = hipMemcpyAsync(plan_buf, dev.data(), need, hipMemcpyHostToDevice, s);
+    hipError_t e = hipMemcpyAsync(plan_buf, host.data(), need, hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return hip_status(e, "q4_0_gemm_prefill_batch_plan copy");
+    int n_chunked = 0;
+    for (int i = 0; i < count; ++i) n_chunked += descs[i].k % 256 == 0;
     plan->device = plan_buf;
     plan->count = count;
     plan->m = (int)m;
     plan->tile_m = tile_m;
-    plan->total_cost = cost;
+    plan->count_chunked = n_chunked;
+    plan->tiles_chunked = tiles[0];
+    plan->tiles_other = tiles[1];
     return ok();
 }
 
 q4_status q4_0_gemm_prefill_batch(const q4_prefill_plan* plan, void* stream) {
     const char* fn = "q4_0_gemm_prefill_batch";
     if (!plan || !plan->device) return fail(Q4_ERR_INVALID_ARG, "%s: null plan", fn);
-    if (plan->count < 1 || plan->m < 1 || (plan->tile_m != 64 && plan->tile_m != 128) || plan->total_cost < 1)
+    const int n_other = plan->count - plan->count_chunked;
+    if (plan->count < 1 || plan->m < 1 || (plan->tile_m != 64 && plan->tile_m != 128) || plan->count_chunked < 0 ||
+        n_other < 0 || (plan->count_chunked > 0) != (plan->tiles_chunked > 0) || (n_other > 0) != (plan->tiles_other > 0))
         return fail(Q4_ERR_INVALID_ARG, "%s: plan was not filled by q4_0_gemm_prefill_batch_plan", fn);
-    const hipError_t e = q4::launch_gemm_prefill_batch(static_cast<const q4::PfDesc*>(plan->device), plan->count,
-                                                       plan->tile_m, plan->total_cost,
-                                                       static_cast<hipStream_t>(stream));
+    const hipError_t e =
+        q4::launch_gemm_prefill_batch(plan->device, plan->count_chunked, plan->tiles_chunked, n_other,
+                                      plan->tiles_other, plan->tile_m, static_cast<hipStream_t>(stream));
     return hip_status(e, "q4_0_gemm_prefill_batch launch");
 }
 

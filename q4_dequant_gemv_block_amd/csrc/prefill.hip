@@ -7,6 +7,11 @@
 // real dense contraction, so the weights are expanded on chip and fed to the
 // gfx950 matrix cores (v_mfma_f32_32x32x16_f16, f32 accumulation).
 //
+// Two kernels.  k_prefill_q (k % 256 == 0, every shape of the 27B sweep)
+// moves a weight row's next four block pairs in one 144-byte chunk and splits
+// each block pair between two waves; it is described above its definition.
+// k_prefill (any k % 64 == 0) is the plain per-step form:
+//
 // Tiling: a workgroup of NW waves owns BM = 32 IT activation rows x BN = 64 NW
 // weight rows.  Wave w owns weight rows [64 w, 64 w + 64) of the tile as two
 // 32-column MFMA tiles (j) and all IT 32-row tiles (i) of the activations.
@@ -28,12 +33,21 @@
 //    activation row i, so both operands cover the same 8 k.
 // One barrier per step: every wave waits for its own loads of the step, the
 // barrier makes all of them visible and frees the buffer of the step after
-// next, whose loads are then issued before this step's matrix work (three
-// steps in flight: a step's matrix work is shorter than a load's latency).
+// next, whose loads are then issued before this step's matrix work.
 // Rows past M or N read clamped in-range addresses and are never stored.
-// Grid order is XCD-aware: workgroup b runs on XCD b % 8, and all M-tiles of
-// one N-tile go to consecutive workgroups of the same XCD, so a weight tile is
-// read from HBM once and served from that XCD's L2 to the others.
+//
+// Both kernels issue their direct-to-LDS loads through asm and wait for them
+// with explicit vmcnt counts, and use a barrier without a release fence (see
+// dma_x4 and step_barrier): the compiler's own waits would drain every
+// outstanding load at each step.
+//
+// A single GEMM runs an XCD-aware grid: workgroup b runs on XCD b % 8, and
+// all M-tiles of one N-tile go to consecutive workgroups of the same XCD, so
+// a weight tile is read from HBM once and served from that XCD's L2 to the
+// others.  A list of GEMMs (the batch entry point) numbers its tiles in list
+// order (GEMM, N-tile, M-tile) and hands them out one at a time from a
+// counter in the plan, so the workgroups running at once share a few GEMMs
+// and their weight and activation tiles are re-read from the caches, not HBM.
 #include "q4_device.h"
 #include "q4_launch.h"
 
@@ -54,12 +68,6 @@ constexpr int kRing = 3;  // steps in flight: activation tiles in LDS, weight pa
 constexpr int kStepBytes = 64 * 2;  // one activation row of one step (64 halves)
 
 typedef PfDesc PfArgs;
-
-__device__ __forceinline__ int64_t uniform64(int64_t v) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-}
 
 // The four f16 pairs of natural-order weights from 8 code bytes (two dwords,
 // byte j = codes j (low nibble) and j + 16 (high nibble) of the block):
@@ -92,9 +100,30 @@ __device__ __forceinline__ void spread(uint32_t e0, uint32_t e1, uint32_t (&P)[4
     P[3] = __builtin_amdgcn_perm(e1, e1, 0x0C030C02u);
 }
 
+// Direct-to-LDS loads (lane i's bytes land at M0 + size * i) issued through
+// asm, so the compiler does not track them: it cannot tell the ring slot being
+// filled from the one being read and would wait for every fill before the
+// first LDS read.  The kernel waits for them itself (explicit vmcnt before
+// each step's barrier).  They write no register.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void dma_x4(const void* src, uint32_t m0) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+__device__ __forceinline__ void dma_x1(const void* src, uint32_t m0) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+
+// Workgroup barrier without the release fence of __syncthreads: that fence
+// would wait for every outstanding load of this wave, the ones of the next
+// steps included.  The caller first waits (vmcnt) for its own loads of the
+// step; the asm is a compiler memory barrier, so no LDS access moves across.
+__device__ __forceinline__ void step_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 template <int IT, int NW, bool BATCH>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
-k_prefill(PfArgs one, const PfDesc* __restrict__ descs, int count, int64_t total) {
+k_prefill(PfArgs one, const PfDesc* __restrict__ descs, int count, int64_t total, PfHead* head) {
     constexpr int BM = 32 * IT;
     constexpr int kTile = BM * kStepBytes;           // bytes of one activation tile
     constexpr int kInstr = kTile / (64 * 16) / NW;   // DMA instructions per wave per tile
@@ -104,8 +133,11 @@ k_prefill(PfArgs one, const PfDesc* __restrict__ descs, int count, int64_t total
     static_assert(kWInstr * NW * 64 * 4 == kWTile, "weight tile split over the waves");
     constexpr int kPerStep = kInstr + kWInstr;       // load instructions per wave per step
     static_assert(kPerStep < 32, "vmcnt encoding below");
-    __shared__ __attribute__((aligned(16))) uint8_t xs[kRing][kTile];
-    __shared__ __attribute__((aligned(16))) uint32_t wsh[kRing][kWTile / 4];
+    // One array per ring slot; the step loop below is unrolled by the ring, so
+    // every slot address is a constant.
+    __shared__ __attribute__((aligned(16))) uint8_t xs0[kTile], xs1[kTile], xs2[kTile];
+    __shared__ __attribute__((aligned(16))) uint32_t ws0[kWTile / 4], ws1[kWTile / 4], ws2[kWTile / 4];
+    static_assert(kRing == 3, "three named slots");
 
     const int lane = threadIdx.x & 63;
     const int li = lane & 31;
@@ -142,17 +174,13 @@ k_prefill(PfArgs one, const PfDesc* __restrict__ descs, int count, int64_t total
         const int64_t row = min((int64_t)i, m_last);
         xoff[q] = (uint32_t)((row * a.k + 8 * c) * 2);
     }
-    auto issue = [&](int s, int buf) {
+    auto issue = [&](int s, uint8_t* xdst, uint32_t* wdst) {
         const uint8_t* xb = xbase + (int64_t)s * kStepBytes;
         const uint8_t* wb = wbase + (int64_t)s * kPairBytes;
 #pragma unroll
-        for (int q = 0; q < kInstr; ++q)
-            __builtin_amdgcn_global_load_lds((g_void*)(xb + xoff[q]),
-                                             (l_void*)(&xs[buf][0] + 1024 * (wave * kInstr + q)), 16, 0, 0);
+        for (int q = 0; q < kInstr; ++q) dma_x4(xb + xoff[q], lds_addr(xdst + 1024 * (wave * kInstr + q)));
 #pragma unroll
-        for (int t = 0; t < kWInstr; ++t)
-            __builtin_amdgcn_global_load_lds((g_void*)(wb + woff[t]),
-                                             (l_void*)(&wsh[buf][0] + 64 * (kWInstr * wave + t)), 4, 0, 0);
+        for (int t = 0; t < kWInstr; ++t) dma_x1(wb + woff[t], lds_addr(wdst + 64 * (kWInstr * wave + t)));
     };
 
     // LDS read offsets: the A chunk c = 2 ks + g of row 32 i + li sits at slot
@@ -171,14 +199,16 @@ k_prefill(PfArgs one, const PfDesc* __restrict__ descs, int count, int64_t total
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    auto compute = [&](int buf) {
-        const uint8_t* xt = &xs[buf][0];
-        const uint8_t* wt = (const uint8_t*)&wsh[buf][0] + doff;
+    auto compute = [&](const uint8_t* xt, const uint32_t* wsl) {
+        const uint8_t* wt = (const uint8_t*)wsl + doff;
         uint32_t D[2][9];
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int c = 0; c < 9; ++c) D[j][c] = *(const uint32_t*)(wt + 32 * 36 * j + 4 * c);
+        h8 av[2][IT];
+#pragma unroll
+        for (int i = 0; i < IT; ++i) av[0][i] = *(const h8*)(xt + aoff[0] + 4096 * i);
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             uint32_t P[2][4];
@@ -207,38 +237,44 @@ k_prefill(PfArgs one, const PfDesc* __restrict__ descs, int count, int64_t total
 #pragma unroll
             for (int hi = 0; hi < 2; ++hi) {
                 const int ks = 2 * blk + hi;
+                // A operands of the next substep are read before this substep's products
+                if (ks + 1 < 4) {
+#pragma unroll
+                    for (int i = 0; i < IT; ++i) av[(ks + 1) & 1][i] = *(const h8*)(xt + aoff[ks + 1] + 4096 * i);
+                }
                 u4 bw[2];
 #pragma unroll
                 for (int j = 0; j < 2; ++j) bw[j] = hi ? expand8<true>(P[j], sc[j]) : expand8<false>(P[j], sc[j]);
 #pragma unroll
-                for (int i = 0; i < IT; ++i) {
-                    const h8 av = *(const h8*)(xt + aoff[ks] + 4096 * i);
+                for (int i = 0; i < IT; ++i)
 #pragma unroll
                     for (int j = 0; j < 2; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, __builtin_bit_cast(h8, bw[j]),
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[ks & 1][i], __builtin_bit_cast(h8, bw[j]),
                                                                            acc[i][j], 0, 0, 0);
-                }
             }
         }
     };
 
-    // Ring of three steps: step s uses buffers s % 3; the loads of step s + 2
-    // are issued (after the barrier that frees their buffers) before step s is
-    // computed.
-    issue(0, 0);
-    if (a.np > 1) issue(1, 1);
-    int buf = 0;
-    for (int s = 0; s < a.np; ++s) {
+    // Ring of three steps: step s computes from slot s % 3; the loads of step
+    // s + 2 go to slot (s + 2) % 3 (freed by the barrier of step s) before
+    // step s is computed.  The loop is unrolled by the ring so every slot is
+    // named statically.
+    auto step = [&](int s, const uint8_t* xt, const uint32_t* wt, uint8_t* xf, uint32_t* wf) {
         // this wave's loads of step s have landed: at most the ones of step s + 1 are outstanding
         if (s + 1 < a.np)
             __builtin_amdgcn_s_waitcnt(kPerStep < 16 ? (0x0F70 | kPerStep) : (0x4F70 | (kPerStep - 16)));
         else
             __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();  // everyone's loads of step s are visible; the buffers of step s + 2 are free
-        const int fill = buf == 0 ? 2 : buf - 1;
-        if (s + 2 < a.np) issue(s + 2, fill);
-        compute(buf);
-        buf = buf == kRing - 1 ? 0 : buf + 1;
+        step_barrier();  // everyone's loads of step s are visible; the slot of step s + 2 is free
+        if (s + 2 < a.np) issue(s + 2, xf, wf);
+        compute(xt, wt);
+    };
+    issue(0, xs0, ws0);
+    if (a.np > 1) issue(1, xs1, ws1);
+    for (int s = 0; s < a.np; s += 3) {
+        step(s, xs0, ws0, xs2, ws2);
+        if (s + 1 < a.np) step(s + 1, xs1, ws1, xs0, ws0);
+        if (s + 2 < a.np) step(s + 2, xs2, ws2, xs1, ws1);
     }
 
     // D layout of the 32x32 product: lane (li, g), element e -> row 8*(e/4) + 4*g + e%4, column li
@@ -266,31 +302,349 @@ k_prefill(PfArgs one, const PfDesc* __restrict__ descs, int count, int64_t total
         tile(one, (int64_t)m_tile * BM, (int64_t)n_tile * (64 * NW));
         return;
     }
-    // Batch: the tiles (GEMM, N-tile, M-tile; M-tile fastest, so consecutive
-    // tiles reuse a weight tile from L2) whose start cost (steps) lies in this
-    // workgroup's byte-balanced share [T g / G, T (g + 1) / G).
-    const int64_t G = gridDim.x;
-    const int64_t c_lo = uniform64((total / G) * blockIdx.x + ((total % G) * blockIdx.x) / G);
-    const int64_t c_hi = uniform64((total / G) * (blockIdx.x + 1) + ((total % G) * ((int64_t)blockIdx.x + 1)) / G);
-    if (c_lo >= c_hi) return;
-    int lo = 0, hi = count - 1;  // last descriptor starting at or before c_lo
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (descs[mid].cost_begin <= c_lo) lo = mid; else hi = mid - 1;
+    // Batch: tiles are numbered in list order (GEMM, N-tile, M-tile; M-tile
+    // fastest) and handed out one at a time from the plan's counter, so the
+    // workgroups running at any moment share a few GEMMs: the M-tiles of an
+    // N-tile read the same weight rows close together in time, and an
+    // activation matrix is read by all N-tiles of its GEMM while it is hot in
+    // the caches.  The next number is fetched while the current tile runs.
+    __shared__ uint32_t ticket;
+    if (threadIdx.x == 0) ticket = atomicAdd(&head->next, 1u);
+    __syncthreads();
+    uint32_t t = __builtin_amdgcn_readfirstlane(ticket);
+    int d = 0;
+    while ((int64_t)t < total) {
+        while (d + 1 < count && descs[d + 1].tile_begin <= (int64_t)t) ++d;
+        const PfDesc D = descs[d];
+        const int64_t local = (int64_t)t - D.tile_begin;
+        uint32_t following = 0;
+        if (threadIdx.x == 0) following = atomicAdd(&head->next, 1u);
+        tile(D, (local % D.mt) * BM, (local / D.mt) * (64 * NW));
+        __syncthreads();  // every wave is done with this tile's buffers and has read `ticket`
+        if (threadIdx.x == 0) ticket = following;
+        __syncthreads();
+        t = __builtin_amdgcn_readfirstlane(ticket);
     }
-    int d = lo;
-    PfDesc D = descs[d];
-    int64_t t = uniform64((c_lo - D.cost_begin + D.np - 1) / D.np);
-    for (;;) {
-        if (t >= (int64_t)D.mt * D.nt) {
-            if (++d >= count) break;
-            D = descs[d];
-            t = 0;
+    if (threadIdx.x == 0) {
+        __threadfence();  // this workgroup's counter updates come first
+        if (atomicAdd(&head->done, 1u) == gridDim.x - 1) {  // last workgroup of the launch
+            atomicExch(&head->next, 0u);
+            atomicExch(&head->done, 0u);
         }
-        if (D.cost_begin + t * D.np >= c_hi) break;
-        __syncthreads();  // the previous tile's buffers are no longer read
-        tile(D, (t % D.mt) * BM, (t / D.mt) * (64 * NW));
-        ++t;
+    }
+}
+
+// Wait until at most `n` of this wave's loads are outstanding (n is one of
+// the few values the step schedule produces; the count is an immediate).
+template <int A, int B, int C>
+__device__ __forceinline__ void wait_vm_upto(int n) {
+    static_assert(A < 16 && B < 16 && C < 16, "vmcnt values below 16");
+    if (n == 0)
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+    else if (n == A)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | A);
+    else if (n == B)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | B);
+    else
+        __builtin_amdgcn_s_waitcnt(0x0F70 | C);
+}
+
+// Prefill for k % 256 == 0: weights move in 144-byte row chunks.
+//
+// The other kernel brings each step's 36 bytes per weight row into LDS; a
+// 128-byte line then serves three or four consecutive steps and is requested
+// from the caches once for each, and those requests (not the bytes) bound it.
+// Here a weight row's next four block pairs (144 bytes, nine 16-byte pieces,
+// about two lines) move in one go, every four steps, into a ring of two
+// slots, so each line is requested about once per tile.
+//
+// A workgroup of 2 NWN waves owns BM = 32 IT activation rows x BN = 64 NWN
+// weight rows.  Waves (h, s) = (wave / NWN, wave % NWN): slice s owns weight
+// rows [64 s, 64 s + 64) as two 32-column MFMA tiles and all IT 32-row
+// activation tiles, and of each step's block pair, wave h takes block h
+// (k 32 h .. 32 h + 31 of the step: two 16-wide k-substeps).  So the weights
+// are expanded once and the two waves of a slice hold partial sums of the
+// same outputs, which meet once per tile: in rounds of one activation tile,
+// each wave hands the partner the tile the partner stores, through LDS, and
+// adds what it receives (own + partner; the sum is the same either way).
+// Activation tiles move per step as in the other kernel (ring of three).
+template <int IT, int NWN, int XD, bool BATCH>
+__global__ void __launch_bounds__(128 * NWN) __attribute__((amdgpu_waves_per_eu(2)))
+k_prefill_q(PfArgs one, const PfDesc* __restrict__ descs, int count, int64_t total, PfHead* head) {
+    constexpr int NW = 2 * NWN;
+    constexpr int BM = 32 * IT;
+    constexpr int BN = 64 * NWN;
+    constexpr int kX = BM * kStepBytes;           // activation tile of one step
+    constexpr int kXI = kX / 1024 / NW;           // its dwordx4 DMA instructions per wave
+    static_assert(kXI >= 1 && kXI * NW * 1024 == kX, "activation tile split over the waves");
+    constexpr int kChunk = 4 * kPairBytes;        // a weight row's bytes for four steps
+    constexpr int kW = BN * kChunk;               // weight slot
+    constexpr int kWPieces = kW / 16;             // 9 per row
+    constexpr int kWFull = kWPieces / (NW * 64);  // weight DMA instructions of every wave (4)
+    static_assert(kWPieces - kWFull * NW * 64 == NW * 32, "the rest is one instruction of half the waves");
+    constexpr int kXS = 2 * (XD + 1);             // activation slots: XD step pairs ahead of the one computed
+    constexpr int kLds = kXS * kX + 2 * kW;       // activation ring, weight ring of two chunks
+    constexpr int kHalf = IT / 2;                 // activation tiles each wave of a slice stores
+    static_assert(IT % 2 == 0 && NW * 64 * 32 * 4 <= kLds, "exchange rounds fit the ring space");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
+
+    const int lane = threadIdx.x & 63;
+    const int li = lane & 31;
+    const int g = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int wh = wave / NWN;  // block of each step's pair this wave takes
+    const int wsl = wave % NWN; // weight slice
+    const int nw_mine = kWFull + (wave < NW / 2 ? 1 : 0);
+    const uint32_t lds0 = lds_addr(lds);
+
+    // A-operand offsets: chunk 2 ks + g of activation row 32 i + li, ks = 2 wh + hk.
+    uint32_t aoff[2];
+#pragma unroll
+    for (int hk = 0; hk < 2; ++hk) aoff[hk] = 16u * (uint32_t)(8 * li + ((2 * (2 * wh + hk) + g) ^ swz(li)));
+    // Weight dwords of rows 64 wsl + 32 j + li (144-byte pitch in a slot): block 0
+    // codes 8g .. 8g+7 sit in dwords 2g .. 2g+2 and its scale in dword 0; block 1
+    // codes in dwords 5+2g, 6+2g and its scale in the high half of dword 4.
+    const uint32_t wrow = (uint32_t)((64 * wsl + li) * kChunk);
+    const uint32_t wcode = wrow + 4u * (uint32_t)(wh ? 5 + 2 * g : 2 * g);
+    const uint32_t wscale = wrow + 4u * (uint32_t)(wh ? 4 : 0);
+
+    auto tile = [&](const PfArgs& a, int64_t m0, int64_t n0) {
+    const int64_t rb = (int64_t)a.np * kPairBytes;
+    const int nsup = a.np / 4;
+    const uint8_t* wbase = a.w + n0 * rb;
+    const uint8_t* xbase = (const uint8_t*)(a.x + m0 * (int64_t)a.k);
+    const int64_t n_last = a.n - 1 - n0;
+    const int64_t m_last = a.m - 1 - m0;
+    // Source offsets, fixed for the K loop (rows past N or M read the last row):
+    //  * weight piece P = 64 (NW q + wave) + lane of a slot is piece P % 9 of
+    //    row P / 9 and lands at byte 16 P of the slot;
+    //  * activation slot S = 64 (kXI wave + q) + lane holds chunk (S % 8) ^ swz
+    //    of row S / 8, as in the other kernel.
+    uint32_t woff[kWFull + 1], xoff[kXI];
+#pragma unroll
+    for (int q = 0; q <= kWFull; ++q) {
+        const int P = min(64 * (NW * q + wave) + lane, kWPieces - 1);
+        const int64_t row = min((int64_t)(P / 9), n_last);
+        woff[q] = (uint32_t)(row * rb + 16 * (P % 9));
+    }
+#pragma unroll
+    for (int q = 0; q < kXI; ++q) {
+        const int slot = 64 * (wave * kXI + q) + lane;
+        const int i = slot >> 3;
+        const int c = (slot & 7) ^ swz(i);
+        const int64_t row = min((int64_t)i, m_last);
+        xoff[q] = (uint32_t)((row * a.k + 8 * c) * 2);
+    }
+    auto issue_x = [&](int s) {
+        const uint8_t* xb = xbase + (int64_t)s * kStepBytes;
+        const uint32_t dst = lds0 + (uint32_t)((s % kXS) * kX) + 1024u * (uint32_t)(wave * kXI);
+#pragma unroll
+        for (int q = 0; q < kXI; ++q) dma_x4(xb + xoff[q], dst + 1024u * q);
+    };
+    auto issue_w = [&](int u) {
+        const uint8_t* wb = wbase + (int64_t)u * kChunk;
+        const uint32_t dst = lds0 + (uint32_t)(kXS * kX + (u & 1) * kW) + 1024u * (uint32_t)wave;
+#pragma unroll
+        for (int q = 0; q < kWFull; ++q) dma_x4(wb + woff[q], dst + 1024u * (uint32_t)(NW * q));
+        if (wave < NW / 2) dma_x4(wb + woff[kWFull], dst + 1024u * (uint32_t)(NW * kWFull));
+    };
+
+    f16v acc[IT][2];
+#pragma unroll
+    for (int i = 0; i < IT; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    auto compute = [&](int s) {
+        const uint8_t* xt = lds + (s % kXS) * kX;
+        const uint8_t* wt = lds + kXS * kX + ((s >> 2) & 1) * kW + kPairBytes * (s & 3);
+        uint32_t C[2][3], S[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint8_t* r = wt + 32 * kChunk * j;
+            C[j][0] = *(const uint32_t*)(r + wcode);
+            C[j][1] = *(const uint32_t*)(r + wcode + 4);
+            C[j][2] = wh == 0 ? *(const uint32_t*)(r + wcode + 8) : 0u;  // block 0 spans three dwords
+            S[j] = *(const uint32_t*)(r + wscale);
+        }
+        h8 av[2][IT];
+#pragma unroll
+        for (int hk = 0; hk < 2; ++hk)
+#pragma unroll
+            for (int i = 0; i < IT; ++i) av[hk][i] = *(const h8*)(xt + aoff[hk] + 4096 * i);
+        uint32_t P[2][4];
+        h2 sc[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            uint32_t e0, e1;
+            _Float16 d;
+            if (wh == 0) {
+                e0 = __builtin_amdgcn_perm(C[j][1], C[j][0], 0x05040302u);
+                e1 = __builtin_amdgcn_perm(C[j][2], C[j][1], 0x05040302u);
+                d = as_h2(S[j]).x;
+            } else {
+                e0 = C[j][0];
+                e1 = C[j][1];
+                d = as_h2(S[j]).y;
+            }
+            spread(e0, e1, P[j]);
+            sc[j] = h2{d, d};
+        }
+#pragma unroll
+        for (int hk = 0; hk < 2; ++hk) {
+            u4 bw[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) bw[j] = hk ? expand8<true>(P[j], sc[j]) : expand8<false>(P[j], sc[j]);
+#pragma unroll
+            for (int i = 0; i < IT; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[hk][i], __builtin_bit_cast(h8, bw[j]),
+                                                                       acc[i][j], 0, 0, 0);
+        }
+    };
+
+    // Steps go in pairs between barriers (k % 256 == 0: the step count is a
+    // multiple of four; weight chunk u serves pairs 2u and 2u + 1).  Issue
+    // order: W(0), then the activations of pairs 0 .. XD - 1; after the
+    // barrier of pair t, the activations of pair t + XD, then W(t / 2 + 1)
+    // when t is even.  At the barrier of pair t (XD = 1 or 2) the loads that
+    // may stay out are the activations of pairs t + 1 .. t + XD - 1 and, at
+    // odd t, W(t / 2 + 1) issued at pair t - 1; every other earlier load is
+    // needed now (for XD = 2 and even t, W(t / 2) comes after the pair's own
+    // activations).
+    static_assert(XD == 1 || XD == 2, "lookahead of one or two step pairs");
+    const int npairs = a.np >> 1;
+    issue_w(0);
+    for (int t = 0; t < XD && t < npairs; ++t) {
+        issue_x(2 * t);
+        issue_x(2 * t + 1);
+    }
+    for (int t = 0; t < npairs; ++t) {
+        const int x_out = min(XD - 1, npairs - 1 - t);
+        const int w_out = (t & 1) && (t >> 1) + 1 < nsup;
+        const int out = 2 * kXI * x_out + nw_mine * w_out;
+        if (wave < NW / 2)
+            wait_vm_upto<2 * kXI * (XD - 1), kWFull + 1, 2 * kXI * (XD - 1) + kWFull + 1>(out);
+        else
+            wait_vm_upto<2 * kXI * (XD - 1), kWFull, 2 * kXI * (XD - 1) + kWFull>(out);
+        step_barrier();  // every wave's loads of the pair are in LDS; the slots refilled next are free
+        if (t + XD < npairs) {
+            issue_x(2 * (t + XD));
+            issue_x(2 * (t + XD) + 1);
+        }
+        if (!(t & 1) && (t >> 1) + 1 < nsup) issue_w((t >> 1) + 1);
+        compute(2 * t);
+        compute(2 * t + 1);
+    }
+
+    // The slice's two partial sums meet: round r, wave h = 0 hands over tile
+    // kHalf + r and keeps tile r; wave h = 1 the other way round.  Each lane's
+    // 32 floats go to (slot e4, lane) of the wave's 8 KiB region.
+#pragma unroll
+    for (int r = 0; r < kHalf; ++r) {
+        __syncthreads();  // the last step's (or the previous round's) LDS reads are done
+        float4* mine = (float4*)(lds + 8192 * wave);
+        if (wh == 0) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4)
+                    mine[(4 * j + e4) * 64 + lane] = float4{acc[kHalf + r][j][4 * e4], acc[kHalf + r][j][4 * e4 + 1],
+                                                             acc[kHalf + r][j][4 * e4 + 2], acc[kHalf + r][j][4 * e4 + 3]};
+        } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4)
+                    mine[(4 * j + e4) * 64 + lane] =
+                        float4{acc[r][j][4 * e4], acc[r][j][4 * e4 + 1], acc[r][j][4 * e4 + 2], acc[r][j][4 * e4 + 3]};
+        }
+        __syncthreads();
+        const float4* theirs = (const float4*)(lds + 8192 * (wh ? wave - NWN : wave + NWN));
+        if (wh == 0) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const float4 v = theirs[(4 * j + e4) * 64 + lane];
+                    acc[r][j][4 * e4] += v.x;
+                    acc[r][j][4 * e4 + 1] += v.y;
+                    acc[r][j][4 * e4 + 2] += v.z;
+                    acc[r][j][4 * e4 + 3] += v.w;
+                }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const float4 v = theirs[(4 * j + e4) * 64 + lane];
+                    acc[kHalf + r][j][4 * e4] += v.x;
+                    acc[kHalf + r][j][4 * e4 + 1] += v.y;
+                    acc[kHalf + r][j][4 * e4 + 2] += v.z;
+                    acc[kHalf + r][j][4 * e4 + 3] += v.w;
+                }
+        }
+    }
+
+    // D layout of the 32x32 product: lane (li, g), element e -> row 8*(e/4) + 4*g + e%4, column li
+    auto store = [&](int i, int j) {
+        const int64_t col = n0 + 64 * wsl + 32 * j + li;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int64_t row = m0 + 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
+            if (row < a.m && col < a.n) ((g_f32*)a.y)[row * a.n + col] = acc[i][j][e];
+        }
+    };
+    if (wh == 0) {
+#pragma unroll
+        for (int i = 0; i < kHalf; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) store(i, j);
+    } else {
+#pragma unroll
+        for (int i = kHalf; i < IT; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) store(i, j);
+    }
+    };
+
+    if (!BATCH) {
+        // XCD-aware tile order, as in the other kernel
+        const int b = blockIdx.x;
+        const int xcd = b % kXcd;
+        const int local = b / kXcd;
+        const int m_tile = local % one.mt;
+        const int n_tile = (local / one.mt) * kXcd + xcd;
+        if (n_tile >= one.nt) return;
+        tile(one, (int64_t)m_tile * BM, (int64_t)n_tile * BN);
+        return;
+    }
+    __shared__ uint32_t ticket;
+    if (threadIdx.x == 0) ticket = atomicAdd(&head->next, 1u);
+    __syncthreads();
+    uint32_t t = __builtin_amdgcn_readfirstlane(ticket);
+    int d = 0;
+    while ((int64_t)t < total) {
+        while (d + 1 < count && descs[d + 1].tile_begin <= (int64_t)t) ++d;
+        const PfDesc D = descs[d];
+        const int64_t local = (int64_t)t - D.tile_begin;
+        uint32_t following = 0;
+        if (threadIdx.x == 0) following = atomicAdd(&head->next, 1u);
+        tile(D, (local % D.mt) * BM, (local / D.mt) * BN);
+        __syncthreads();  // every wave is done with this tile's LDS and has read `ticket`
+        if (threadIdx.x == 0) ticket = following;
+        __syncthreads();
+        t = __builtin_amdgcn_readfirstlane(ticket);
+    }
+    if (threadIdx.x == 0) {
+        __threadfence();
+        if (atomicAdd(&head->done, 1u) == gridDim.x - 1) {
+            atomicExch(&head->next, 0u);
+            atomicExch(&head->done, 0u);
+        }
     }
 }
 
@@ -298,19 +652,41 @@ template <int IT, int NW>
 hipError_t launch(PfArgs a, hipStream_t s) {
     a.mt = (int)((a.m + 32 * IT - 1) / (32 * IT));
     a.nt = (int)((a.n + 64 * NW - 1) / (64 * NW));
-    a.cost_begin = 0;
+    a.tile_begin = 0;
     const int64_t ngroups = (a.nt + kXcd - 1) / kXcd;
     const int64_t grid = ngroups * kXcd * a.mt;
     hipLaunchKernelGGL((k_prefill<IT, NW, false>), dim3((unsigned)grid), dim3(NW * 64), 0, s, a, nullptr, 0,
-                       (int64_t)0);
+                       (int64_t)0, nullptr);
     return hipGetLastError();
 }
 
 template <int IT, int NW>
-hipError_t launch_batch(const PfDesc* descs, int count, int64_t total, hipStream_t s) {
-    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(total, 2 * (int64_t)device_cu_count()));
+hipError_t launch_batch(PfHead* head, const PfDesc* descs, int count, int64_t tiles, hipStream_t s) {
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(tiles, 2 * (int64_t)device_cu_count()));
     PfArgs none = {};
-    hipLaunchKernelGGL((k_prefill<IT, NW, true>), dim3(grid), dim3(NW * 64), 0, s, none, descs, count, total);
+    hipLaunchKernelGGL((k_prefill<IT, NW, true>), dim3(grid), dim3(NW * 64), 0, s, none, descs, count, tiles, head);
+    return hipGetLastError();
+}
+
+template <int IT, int NWN>
+hipError_t launch_q(PfArgs a, hipStream_t s) {
+    a.mt = (int)((a.m + 32 * IT - 1) / (32 * IT));
+    a.nt = (int)((a.n + 64 * NWN - 1) / (64 * NWN));
+    a.tile_begin = 0;
+    const int64_t ngroups = (a.nt + kXcd - 1) / kXcd;
+    const int64_t grid = ngroups * kXcd * a.mt;
+    hipLaunchKernelGGL((k_prefill_q<IT, NWN, 1, false>), dim3((unsigned)grid), dim3(NWN * 128), 0, s, a, nullptr, 0,
+                       (int64_t)0, nullptr);
+    return hipGetLastError();
+}
+
+template <int IT, int NWN>
+hipError_t launch_batch_q(PfHead* head, const PfDesc* descs, int count, int64_t tiles, hipStream_t s) {
+    // one workgroup of 2 NWN waves per CU (the LDS ring takes most of a CU's 160 KiB)
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(tiles, (int64_t)device_cu_count()));
+    PfArgs none = {};
+    hipLaunchKernelGGL((k_prefill_q<IT, NWN, 1, true>), dim3(grid), dim3(NWN * 128), 0, s, none, descs, count, tiles,
+                       head);
     return hipGetLastError();
 }
 
@@ -331,6 +707,11 @@ hipError_t launch_gemm_prefill(const uint8_t* w, const uint16_t* x, float* y, in
     a.np = (int)(k / 64);
     const int64_t cus = device_cu_count();
     auto tiles = [&](int it, int nw) { return ((m + 32 * it - 1) / (32 * it)) * ((n + 64 * nw - 1) / (64 * nw)); };
+    if (k % 256 == 0) {
+        if (m > 96 && tiles(4, 4) >= cus) return launch_q<4, 4>(a, s);
+        if (tiles(2, 4) >= cus) return launch_q<2, 4>(a, s);
+        return launch_q<2, 2>(a, s);
+    }
     if (m > 96 && tiles(4, 4) >= cus) return launch<4, 4>(a, s);
     if (tiles(2, 4) >= cus) return launch<2, 4>(a, s);
     return launch<2, 2>(a, s);
@@ -343,17 +724,27 @@ int prefill_batch_tile_m(int64_t m) {
     return (double)p128 <= 1.15 * (double)p64 ? 128 : 64;
 }
 
-// Fills mt, nt, np and cost_begin for the batch tile shape; returns the cost.
-int64_t prefill_fill(PfDesc* d, int tile_m, int64_t cost_begin) {
+// Fills mt, nt, np and tile_begin for the batch tile shape; returns the tiles.
+int64_t prefill_fill(PfDesc* d, int tile_m, int64_t tile_begin) {
     d->np = d->k / 64;
     d->mt = (int)((d->m + tile_m - 1) / tile_m);
     d->nt = (int)((d->n + 255) / 256);
-    d->cost_begin = cost_begin;
-    return (int64_t)d->mt * d->nt * d->np;
+    d->tile_begin = tile_begin;
+    return (int64_t)d->mt * d->nt;
 }
 
-hipError_t launch_gemm_prefill_batch(const PfDesc* descs, int count, int tile_m, int64_t total, hipStream_t s) {
-    return tile_m == 128 ? launch_batch<4, 4>(descs, count, total, s) : launch_batch<2, 4>(descs, count, total, s);
+hipError_t launch_gemm_prefill_batch(void* plan, int n_chunked, int64_t tiles_chunked, int n_other,
+                                     int64_t tiles_other, int tile_m, hipStream_t s) {
+    PfHead* head = static_cast<PfHead*>(plan);
+    const PfDesc* descs = reinterpret_cast<const PfDesc*>(head + 2);
+    hipError_t e = hipSuccess;
+    if (n_chunked > 0)
+        e = tile_m == 128 ? launch_batch_q<4, 4>(head, descs, n_chunked, tiles_chunked, s)
+                          : launch_batch_q<2, 4>(head, descs, n_chunked, tiles_chunked, s);
+    if (e == hipSuccess && n_other > 0)
+        e = tile_m == 128 ? launch_batch<4, 4>(head + 1, descs + n_chunked, n_other, tiles_other, s)
+                          : launch_batch<2, 4>(head + 1, descs + n_chunked, n_other, tiles_other, s);
+    return e;
 }
 
 }  // namespace q4

@@ -101,11 +101,23 @@ struct PfDesc {
     int k;
     int np;             // pairs per weight row (k / 64)
     int mt, nt;         // tiles along M and N
-    int64_t cost_begin; // steps of the earlier tiles of the list
+    int64_t tile_begin; // tiles of the earlier descriptors of the list
+};
+// Work counter of a prefill batch plan (first 16 bytes of the plan buffer):
+// workgroups take tile numbers from `next`; the last one to finish a launch
+// sets both fields back to zero, so the plan is ready for the next launch.
+struct PfHead {
+    uint32_t next;
+    uint32_t done;
+    uint32_t reserved[2];
 };
 int prefill_batch_tile_m(int64_t m);
-int64_t prefill_fill(PfDesc* d, int tile_m, int64_t cost_begin);
-hipError_t launch_gemm_prefill_batch(const PfDesc* descs, int count, int tile_m, int64_t total, hipStream_t s);
+int64_t prefill_fill(PfDesc* d, int tile_m, int64_t tile_begin);
+// `plan`: two PfHead, then the `n_chunked` descriptors with k % 256 == 0
+// (the kernel that moves weights in 144-byte chunks; tile numbers from 0),
+// then the `n_other` others (tile numbers from 0).
+hipError_t launch_gemm_prefill_batch(void* plan, int n_chunked, int64_t tiles_chunked, int n_other,
+                                     int64_t tiles_other, int tile_m, hipStream_t s);
 int argmax_blocks(int64_t n, int64_t k);
 hipError_t launch_lm_head(const uint8_t* w, const uint16_t* h, float* logits, int32_t* token,
                           int64_t n, int64_t k, uint64_t* keys, hipStream_t s);
