@@ -52,6 +52,7 @@
 #include "q4_launch.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace q4 {
 
@@ -457,41 +458,35 @@ k_prefill_q(PfArgs one, const PfDesc* __restrict__ descs, int count, int64_t tot
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    auto compute = [&](int s) {
-        const uint8_t* xt = lds + (s % kXS) * kX;
+    // B operands of step s for rows j = 0, 1: block H of the step's pair, as
+    // the code pairs P (spread) and the scale sc; H is this wave's block half
+    // (a template constant, so no per-lane select between the two layouts).
+    auto weights = [&](int s, auto Hc, uint32_t (&P)[2][4], h2 (&sc)[2]) {
+        constexpr int H = decltype(Hc)::value;
         const uint8_t* wt = lds + kXS * kX + ((s >> 2) & 1) * kW + kPairBytes * (s & 3);
-        uint32_t C[2][3], S[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const uint8_t* r = wt + 32 * kChunk * j;
-            C[j][0] = *(const uint32_t*)(r + wcode);
-            C[j][1] = *(const uint32_t*)(r + wcode + 4);
-            C[j][2] = wh == 0 ? *(const uint32_t*)(r + wcode + 8) : 0u;  // block 0 spans three dwords
-            S[j] = *(const uint32_t*)(r + wscale);
-        }
-        h8 av[2][IT];
-#pragma unroll
-        for (int hk = 0; hk < 2; ++hk)
-#pragma unroll
-            for (int i = 0; i < IT; ++i) av[hk][i] = *(const h8*)(xt + aoff[hk] + 4096 * i);
-        uint32_t P[2][4];
-        h2 sc[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
+            const uint32_t c0 = *(const uint32_t*)(r + wcode);
+            const uint32_t c1 = *(const uint32_t*)(r + wcode + 4);
+            const uint32_t sd = *(const uint32_t*)(r + wscale);
             uint32_t e0, e1;
             _Float16 d;
-            if (wh == 0) {
-                e0 = __builtin_amdgcn_perm(C[j][1], C[j][0], 0x05040302u);
-                e1 = __builtin_amdgcn_perm(C[j][2], C[j][1], 0x05040302u);
-                d = as_h2(S[j]).x;
+            if constexpr (H == 0) {  // block 0 codes start at byte 2: three dwords
+                const uint32_t c2 = *(const uint32_t*)(r + wcode + 8);
+                e0 = __builtin_amdgcn_perm(c1, c0, 0x05040302u);
+                e1 = __builtin_amdgcn_perm(c2, c1, 0x05040302u);
+                d = as_h2(sd).x;
             } else {
-                e0 = C[j][0];
-                e1 = C[j][1];
-                d = as_h2(S[j]).y;
+                e0 = c0;
+                e1 = c1;
+                d = as_h2(sd).y;
             }
             spread(e0, e1, P[j]);
             sc[j] = h2{d, d};
         }
+    };
+    auto products = [&](const h8 (&av)[2][IT], const uint32_t (&P)[2][4], const h2 (&sc)[2]) {
 #pragma unroll
         for (int hk = 0; hk < 2; ++hk) {
             u4 bw[2];
@@ -504,6 +499,24 @@ k_prefill_q(PfArgs one, const PfDesc* __restrict__ descs, int count, int64_t tot
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[hk][i], __builtin_bit_cast(h8, bw[j]),
                                                                        acc[i][j], 0, 0, 0);
         }
+    };
+    // One step: its A operands (two k-substeps of IT activation tiles), its
+    // B operands, then the products.
+    auto compute = [&](int s, auto Hc) {
+        h8 av[2][IT];
+        const uint8_t* xt = lds + (s % kXS) * kX;
+#pragma unroll
+        for (int hk = 0; hk < 2; ++hk)
+#pragma unroll
+            for (int i = 0; i < IT; ++i) av[hk][i] = *(const h8*)(xt + aoff[hk] + 4096 * i);
+        uint32_t P[2][4];
+        h2 sc[2];
+        weights(s, Hc, P, sc);
+        products(av, P, sc);
+    };
+    auto compute_pair = [&](int t, auto Hc) {
+        compute(2 * t, Hc);
+        compute(2 * t + 1, Hc);
     };
 
     // Steps go in pairs between barriers (k % 256 == 0: the step count is a
@@ -522,6 +535,7 @@ k_prefill_q(PfArgs one, const PfDesc* __restrict__ descs, int count, int64_t tot
         issue_x(2 * t);
         issue_x(2 * t + 1);
     }
+    auto kloop = [&](auto Hc) {
     for (int t = 0; t < npairs; ++t) {
         const int x_out = min(XD - 1, npairs - 1 - t);
         const int w_out = (t & 1) && (t >> 1) + 1 < nsup;
@@ -536,9 +550,13 @@ k_prefill_q(PfArgs one, const PfDesc* __restrict__ descs, int count, int64_t tot
             issue_x(2 * (t + XD) + 1);
         }
         if (!(t & 1) && (t >> 1) + 1 < nsup) issue_w((t >> 1) + 1);
-        compute(2 * t);
-        compute(2 * t + 1);
+        compute_pair(t, Hc);
     }
+    };
+    if (wh == 0)
+        kloop(std::integral_constant<int, 0>{});
+    else
+        kloop(std::integral_constant<int, 1>{});
 
     // The slice's two partial sums meet: round r, wave h = 0 hands over tile
     // kHalf + r and keeps tile r; wave h = 1 the other way round.  Each lane's
