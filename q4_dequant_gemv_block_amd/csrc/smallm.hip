@@ -17,7 +17,7 @@
 // Work: a workgroup of 16 waves owns a tile of 256 weight rows (16 per wave)
 // and one K-range of its GEMM; the K-range is the longest run of 16-pair
 // segments whose activations for all M rows fit kXBytes of LDS, so K is split
-// only for large M and K (M = 16: 4096 columns).  Items (GEMM, K-range, tile)
+// only for large M and K (M = 16: 5120 columns).  Items (GEMM, K-range, tile)
 // are ordered GEMM, K-range, tile, and every workgroup takes a byte-balanced
 // contiguous run of them, so the activations of a K-range are staged once and
 // serve many tiles.  When a GEMM has several K-ranges each range writes its
@@ -53,7 +53,7 @@ constexpr int kSmWaves = 16;
 constexpr int kSmThreads = kSmWaves * 64;
 constexpr int kTileRows = 16 * kSmWaves;  // 256
 constexpr int kPairsPerLane = 4;          // pairs g, g+4, g+8, g+12 of a segment
-constexpr int kXBytes = 144 * 1024;       // activations of one K-range, all M rows
+constexpr int kXBytes = 160 * 1024;       // activations of one K-range, all M rows (the whole LDS)
 
 __device__ __forceinline__ int64_t uniform64(int64_t v) {
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
@@ -75,12 +75,24 @@ struct SmCursor {
     int d, c, t, jb;
 };
 
-// Row stride of the staged activations, in 16-byte chunks: odd, so the 16
-// activation rows that a wave reads at once fall on different LDS banks.
-__device__ __forceinline__ int x_stride(const SmDesc& D) { return 8 * D.P + 1; }
+// Staged activations, two layouts.  Padded (SWZ = false): row r holds its P
+// pairs x 8 chunks (16 bytes each) from chunk r (8P + 1) on, chunk c of pair
+// pl at 8 pl + c; the odd row stride puts the 16 rows a wave reads at once on
+// different LDS banks.  Swizzled (SWZ = true, when the padding does not fit:
+// M = 16 rows of 5120 columns take exactly 160 KiB): row stride 8P, chunk c of
+// pair pl at 8 (pl ^ ((r >> 3) & 1)) + (c ^ (r & 7)), which spreads the 16
+// rows over the banks without extra space (P is even, so pl ^ 1 stays in the
+// range); it costs per-lane read offsets, so it is used only there.
+template <bool SWZ>
+__device__ __forceinline__ int x_stride(const SmDesc& D) { return SWZ ? 8 * D.P : 8 * D.P + 1; }
+template <bool SWZ>
+__device__ __forceinline__ int x_slot(int r, int pl, int c) {
+    return SWZ ? 8 * (pl ^ ((r >> 3) & 1)) + (c ^ (r & 7)) : 8 * pl + c;
+}
 
-// Activations of pairs [c*P, c*P + 16*segs) of all M rows into
-// xs[row * x_stride + pl * 8 + chunk]; pairs past K/64 are zero.
+// Activations of pairs [c*P, c*P + 16*segs) of all M rows into their slots;
+// pairs past K/64 are zero.
+template <bool SWZ>
 __device__ void stage_range(const SmDesc& D, int c, int m, u4* __restrict__ xs) {
     const int p0 = c * D.P;
     const int npairs = 16 * segs_of(D, c);
@@ -113,7 +125,7 @@ __device__ void stage_range(const SmDesc& D, int c, int m, u4* __restrict__ xs) 
             ent.y = xe(a + 16) | (xe(cq + 16) << 16);
             ent.z = xe(bb) | (xe(e) << 16);
             ent.w = xe(bb + 16) | (xe(e + 16) << 16);
-            xs[mm * x_stride(D) + (b >> 1) * 8 + 4 * half + cc] = ent;
+            xs[mm * x_stride<SWZ>(D) + x_slot<SWZ>(mm, b >> 1, 4 * half + cc)] = ent;
         }
     }
 }
@@ -122,6 +134,7 @@ struct SmBuf {
     uint32_t d[kPairsPerLane][9];
 };
 
+template <bool SWZ>
 __global__ void __launch_bounds__(kSmThreads) k_smallm(const SmDesc* __restrict__ descs, int count, SmDesc one,
                                                        int m, int64_t total, float* __restrict__ ws) {
     extern __shared__ u4 xs[];
@@ -209,14 +222,17 @@ __global__ void __launch_bounds__(kSmThreads) k_smallm(const SmDesc* __restrict_
         }
         if (r.d != staged_d || r.c != staged_c) {
             __syncthreads();
-            stage_range(Dc, r.c, m, xs);
+            stage_range<SWZ>(Dc, r.c, m, xs);
             __syncthreads();
             staged_d = r.d;
             staged_c = r.c;
         }
         // A operand rows m >= M only produce product rows that are never
         // stored, so those lanes read activation row M - 1 (an LDS broadcast).
-        const u4* xu = xs + min(l16, m - 1) * x_stride(Dc) + (16 * r.jb + g) * 8;
+        // Pair 16 jb + g + 4 jj: 16 jb + 4 jj is even, so its slot is
+        // 8 (16 jb + 4 jj) + slot(row, g, c) in both layouts.
+        const int xr = min(l16, m - 1);
+        const u4* xu = xs + xr * x_stride<SWZ>(Dc) + 128 * r.jb;
 #pragma unroll
         for (int jj = 0; jj < kPairsPerLane; ++jj) {
             const _Float16 d0 = as_h2(b.d[jj][0]).x, d1 = as_h2(b.d[jj][4]).y;
@@ -231,7 +247,7 @@ __global__ void __launch_bounds__(kSmThreads) k_smallm(const SmDesc* __restrict_
                 bw.y = as_u32(q.q1 * s);
                 bw.z = as_u32(q.q2 * s);
                 bw.w = as_u32(q.q3 * s);
-                const u4 ax = xu[32 * jj + c];
+                const u4 ax = xu[32 * jj + x_slot<SWZ>(xr, g, c)];
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, ax), __builtin_bit_cast(h8, bw),
                                                              acc, 0, 0, 0);
             }
@@ -295,12 +311,17 @@ __global__ void __launch_bounds__(256) k_sum_ranges(const SmDesc* __restrict__ d
 
 }  // namespace
 
-// Pairs per K-range for m activation rows: the longest run of whole
-// 16-pair segments whose activations fit kXBytes.
+// Pairs per K-range for m activation rows: the longest run of whole 16-pair
+// segments whose activations fit kXBytes in the padded layout, or in the
+// swizzled one (no padding, a little longer) when that takes fewer ranges.
 static int smallm_range_pairs(int64_t k, int64_t m) {
     const int np = (int)(k / 64);
-    const int fit = std::max(16, (int)(kXBytes / (kChunksPerPair * 16 * m)) / 16 * 16);
-    return std::min(fit, (np + 15) / 16 * 16);
+    const int np16 = (np + 15) / 16 * 16;
+    const int row_chunks = (int)(kXBytes / (16 * m));  // 16-byte chunks per activation row
+    const int fit_pad = std::max(16, (row_chunks - 1) / kChunksPerPair / 16 * 16);
+    const int fit_swz = std::max(16, row_chunks / kChunksPerPair / 16 * 16);
+    if ((np + fit_swz - 1) / fit_swz < (np + fit_pad - 1) / fit_pad) return std::min(fit_swz, np16);
+    return std::min(fit_pad, np16);
 }
 
 // Fills the derived fields of a descriptor; returns its workspace floats.
@@ -332,22 +353,29 @@ static int smallm_grid(int64_t total) {
     return (int)std::max<int64_t>(1, std::min<int64_t>(total, (int64_t)device_cu_count()));
 }
 
-// Staged activations: m rows of max_range_pairs * 8 chunks plus one chunk of
-// padding (at most 16 * 16 bytes beyond kXBytes).
+// Staged activations: m rows of max_range_pairs * 8 chunks, plus one chunk of
+// padding per row when that still fits the LDS (then the padded layout).
+static bool smallm_swizzle(int64_t max_range_pairs, int64_t m) {
+    return (max_range_pairs * kChunksPerPair + 1) * m * (int64_t)sizeof(u4) > kXBytes;
+}
 static size_t smallm_lds(int64_t max_range_pairs, int64_t m) {
-    return (size_t)(max_range_pairs * kChunksPerPair + 1) * m * sizeof(u4);
+    return (size_t)(max_range_pairs * kChunksPerPair + (smallm_swizzle(max_range_pairs, m) ? 0 : 1)) * m * sizeof(u4);
 }
 
 static hipError_t launch_sm(const SmDesc* descs, int count, const SmDesc& one, int64_t m, int64_t total,
                             int max_p, float* ws, hipStream_t s) {
     const size_t lds = smallm_lds(max_p, m);
+    const void* kern = smallm_swizzle(max_p, m) ? (const void*)k_smallm<true> : (const void*)k_smallm<false>;
     if (lds > 65536) {
-        const hipError_t e =
-            hipFuncSetAttribute((const void*)k_smallm, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_smallm, dim3(smallm_grid(total)), dim3(kSmThreads), lds, s, descs, count, one, (int)m,
-                       total, ws);
+    if (smallm_swizzle(max_p, m))
+        hipLaunchKernelGGL(k_smallm<true>, dim3(smallm_grid(total)), dim3(kSmThreads), lds, s, descs, count, one,
+                           (int)m, total, ws);
+    else
+        hipLaunchKernelGGL(k_smallm<false>, dim3(smallm_grid(total)), dim3(kSmThreads), lds, s, descs, count, one,
+                           (int)m, total, ws);
     return hipGetLastError();
 }
 

@@ -52,25 +52,32 @@ def test_abi_version(lib):
 def test_workspace_bytes(lib):
     assert lib.q4_workspace_bytes(q4.Q4_OP_GEMV, 1, 5120, 5120) == 0
     assert lib.q4_workspace_bytes(q4.Q4_OP_GEMM_SMALLM, 1, 5120, 5120) == 0
-    assert lib.q4_workspace_bytes(q4.Q4_OP_GEMM_SMALLM, 16, 5120, 5120) > 0
+    assert lib.q4_workspace_bytes(q4.Q4_OP_GEMM_SMALLM, 16, 5120, 5120) == 0  # 16 rows of 5120 fit LDS
+    assert lib.q4_workspace_bytes(q4.Q4_OP_GEMM_SMALLM, 16, 5120, 17408) > 0
     ws = lib.q4_workspace_bytes(q4.Q4_OP_LM_HEAD_ARGMAX, 1, 151936, 5120)
     assert ws >= 8 and ws % 8 == 0
     assert lib.q4_workspace_bytes(99, 1, 1, 32) == 0
 
 
 def test_smallm_k_range_workspace_rule(lib):
-    # The activations of one K-range (all M rows) live in 144 KiB of LDS, in
-    # whole 16-pair segments: 128 bytes per pair and row.  A GEMM needs partial
-    # sums (nranges x M x N floats) only when its K does not fit one range.
+    # The activations of one K-range (all M rows) live in 160 KiB of LDS, in
+    # whole 16-pair segments: 128 bytes per pair and row, plus 16 bytes per row
+    # of padding unless dropping it (the swizzled layout) takes fewer ranges.
+    # A GEMM needs partial sums (nranges x M x N floats) only when its K does
+    # not fit one range.
     def expect(m, n, k):
         np_ = k // 64
-        fit = max(16, (144 * 1024 // (128 * m)) // 16 * 16)
+        row_chunks = 160 * 1024 // (16 * m)
+        fit_pad = max(16, (row_chunks - 1) // 8 // 16 * 16)
+        fit_swz = max(16, row_chunks // 8 // 16 * 16)
+        fit = fit_swz if -(-np_ // fit_swz) < -(-np_ // fit_pad) else fit_pad
         p = min(fit, (np_ + 15) // 16 * 16)
         nr = -(-np_ // p)
         return nr * m * n * 4 if nr > 1 else 0
 
     op = q4.Q4_OP_GEMM_SMALLM
-    assert lib.q4_workspace_bytes(op, 16, 5120, 5120) == 2 * 16 * 5120 * 4
+    assert lib.q4_workspace_bytes(op, 16, 5120, 5120) == 0  # 16 x 80 pairs x 128 bytes: exactly 160 KiB
+    assert lib.q4_workspace_bytes(op, 16, 5120, 17408) == 4 * 16 * 5120 * 4  # 80 + 80 + 80 + 32 pairs
     assert lib.q4_workspace_bytes(op, 16, 5120, 4096) == 0
     assert lib.q4_workspace_bytes(op, 8, 5120, 5120) == 0
     assert lib.q4_workspace_bytes(op, 2, 5120, 5120) == 0
@@ -116,13 +123,13 @@ def test_smallm_validation(lib):
     assert lib.q4_0_gemm_smallm(FAKE, FAKE * 2, FAKE * 8, 17, 8, 64, None, 0, None) == q4.Q4_ERR_INVALID_ARG
     assert b"m = 17" in lib.q4_last_error()
     assert lib.q4_0_gemm_smallm(FAKE, FAKE * 2, FAKE * 8, 0, 8, 64, None, 0, None) == q4.Q4_ERR_INVALID_ARG
-    need = lib.q4_workspace_bytes(q4.Q4_OP_GEMM_SMALLM, 16, 5120, 5120)
+    need = lib.q4_workspace_bytes(q4.Q4_OP_GEMM_SMALLM, 16, 5120, 17408)  # K split in four ranges
     assert need > 0 and need % 4 == 0
     w, x, y = FAKE * 64, FAKE * 4096, FAKE * 8192
-    assert lib.q4_0_gemm_smallm(w, x, y, 16, 5120, 5120, None, 0, None) == q4.Q4_ERR_WORKSPACE
-    assert lib.q4_0_gemm_smallm(w, x, y, 16, 5120, 5120, FAKE * 16384, need - 4, None) == q4.Q4_ERR_WORKSPACE
+    assert lib.q4_0_gemm_smallm(w, x, y, 16, 5120, 17408, None, 0, None) == q4.Q4_ERR_WORKSPACE
+    assert lib.q4_0_gemm_smallm(w, x, y, 16, 5120, 17408, FAKE * 16384, need - 4, None) == q4.Q4_ERR_WORKSPACE
     # workspace overlapping the output
-    assert lib.q4_0_gemm_smallm(w, x, y, 16, 5120, 5120, y + 64, need, None) == q4.Q4_ERR_INVALID_ARG
+    assert lib.q4_0_gemm_smallm(w, x, y, 16, 5120, 17408, y + 64, need, None) == q4.Q4_ERR_INVALID_ARG
 
 
 def test_prefill_validation(lib):
