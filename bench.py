@@ -41,13 +41,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """Hash of the kernel sources and build flags, comments and blank space
-    left out (so an edited comment does not invalidate a measurement)."""
+# Kernel source of each workload's dominant kernel (besides the shared device
+# and launch headers, the host-side C ABI and the build script).
+KERNEL_SOURCE = {"sweep": "gemv.hip", "gemv": "gemv.hip", "lmhead": "gemv.hip", "smallm": "smallm.hip",
+                 "prefill": "prefill.hip"}
+
+
+def kernel_source_hash(workload: str) -> str:
+    """Hash of the sources that build `workload`'s kernel and of the build
+    flags, comments and blank space left out (so an edited comment, or a
+    change to another workload's kernel, does not invalidate a measurement)."""
     import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "q4_dequant_gemv_block_amd", "csrc")
-    files = [os.path.join(csrc, n) for n in sorted(os.listdir(csrc))]
+    names = [KERNEL_SOURCE[workload.split("_m")[0]], "q4_device.h", "q4_launch.h", "api.cpp"]
+    files = [os.path.join(csrc, n) for n in sorted(names)]
     files.append(os.path.join(ROOT, "q4_dequant_gemv_block_amd", "build.py"))
     for path in files:
         with open(path) as f:
@@ -70,7 +78,7 @@ def counter_traffic(workload: str):
     with open(path) as f:
         table = json.load(f)
     e = table.get(workload)
-    if not e or e.get("source_hash") != kernel_source_hash():
+    if not e or e.get("source_hash") != kernel_source_hash(workload):
         return None
     return e.get("bytes_per_launch")
 
@@ -326,7 +334,7 @@ def record_traffic(workload: str, kernel: str, fetch_csv: str, write_csv: str, c
     write = _counter_mean(write_csv, kernel, "WRITE_SIZE") * 1024.0 * w_scale
     path = os.path.join(PROFILE_DIR, "traffic.json")
     table = json.load(open(path)) if os.path.exists(path) else {}
-    table[workload] = {"kernel": kernel, "source_hash": kernel_source_hash(),
+    table[workload] = {"kernel": kernel, "source_hash": kernel_source_hash(workload),
                        "bytes_per_launch": int(round(fetch + write)),
                        "fetch_bytes": int(round(fetch)), "write_bytes": int(round(write)),
                        "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}
