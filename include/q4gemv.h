@@ -269,15 +269,16 @@ Q4_API size_t q4_0_gemm_prefill_batch_plan_bytes(int count);
  * each filling only part of it.  Descriptor i names w (n rows of k/32 Q4_0
  * blocks, 16-byte aligned), x (m x k binary16, 16-byte aligned) and y (m x n
  * binary32, written); every k % 64 == 0, m*n <= 2^40, |d| <= 8188.  Each
- * result is that of q4_0_gemm_prefill on the same operands within the same
- * bound (the tile shape may differ, so the f32 summation order may too).
+ * result equals that of q4_0_gemm_prefill on the same operands bit for bit
+ * (each GEMM runs in the same kernel with the same f32 summation order; the
+ * tile shape may differ, which does not change that order).
  * Validates the list, writes its device form into `plan_buf`
  * (q4_0_gemm_prefill_batch_plan_bytes(count) bytes, 16-byte aligned) and
  * fills `*plan`; the copy has completed when this returns.  No output may
  * overlap another output, an input or the plan.  The plan buffer also holds
- * the launch's work counter, which every launch returns to its initial state
- * when it completes: run one launch of a plan at a time (launches on one
- * stream are fine; the same plan on two streams at once is not).
+ * the work counters of its launches, which every launch returns to their
+ * initial state when it completes: run one call of a plan at a time (calls on
+ * one stream are fine; the same plan on two streams at once is not).
  */
 Q4_API q4_status q4_0_gemm_prefill_batch_plan(const q4_gemv_desc* descs, int count, int64_t m, void* plan_buf,
                                               size_t plan_bytes, q4_prefill_plan* plan, void* stream);

@@ -137,6 +137,15 @@ def test_prefill_validation(lib):
     assert lib.q4_0_gemm_prefill(FAKE, FAKE * 2, FAKE * 8, 4, 8, 40, None, 0, None) == q4.Q4_ERR_INVALID_ARG
 
 
+def test_prefill_plan_bytes_layout(lib):
+    # two 16-byte work-counter heads (the k % 256 == 0 part and the rest), then
+    # one 64-byte descriptor per GEMM
+    for count in (1, 2, 7, 448):
+        assert lib.q4_0_gemm_prefill_batch_plan_bytes(count) == 2 * 16 + 64 * count
+    assert lib.q4_0_gemm_prefill_batch_plan_bytes(0) == 0
+    assert lib.q4_0_gemm_prefill_batch_plan_bytes((1 << 20) + 1) == 0
+
+
 def test_lm_head_validation(lib):
     w, h, lg, tok = FAKE, FAKE * 2, FAKE * 4, FAKE * 8
     need = lib.q4_workspace_bytes(q4.Q4_OP_LM_HEAD_ARGMAX, 1, 1000, 64)
