@@ -53,6 +53,8 @@ class Oracle:
         lib.q4o_gemm_rows.argtypes = [vp, i64, i64, vp, i64, vp, vp]
         lib.q4o_argmax.argtypes = [vp, i64]
         lib.q4o_argmax.restype = i64
+        lib.q4o_accepted_prefix.argtypes = [vp, vp, i64]
+        lib.q4o_accepted_prefix.restype = i64
         self.lib = lib
         self.path = path
 
@@ -97,6 +99,22 @@ class Oracle:
         return int(self.lib.q4o_argmax(v.ctypes.data, v.size))
 
 
+    def accepted_prefix(self, tokens, draft) -> int:
+        """Leading positions where tokens[i] == draft[i] (stops at the first mismatch)."""
+        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64)).ravel()
+        d = np.ascontiguousarray(np.asarray(draft, dtype=np.int64)).ravel()
+        assert t.size == d.size
+        return int(self.lib.q4o_accepted_prefix(t.ctypes.data, d.ctypes.data, t.size))
+
+    def verify(self, w_rows: np.ndarray, k: int, h, draft):
+        """Greedy verify of a draft: (y, a, tokens, accepted) for hidden states h [M, K]
+        (f16) and the draft's M tokens: y, a as gemm_rows, tokens[i] = argmax(y[i]),
+        accepted = accepted_prefix(tokens, draft)."""
+        y, a = self.gemm_rows(w_rows, k, np.asarray(h).reshape(-1, k))
+        tokens = np.array([self.argmax(y[i]) for i in range(y.shape[0])], dtype=np.int64)
+        return y, a, tokens, self.accepted_prefix(tokens, draft)
+
+
 def default() -> Oracle:
     global _default
     with _lock:
@@ -121,6 +139,14 @@ def gemm_rows(w_rows: np.ndarray, k: int, x) -> tuple[np.ndarray, np.ndarray]:
 
 def argmax(y) -> int:
     return default().argmax(y)
+
+
+def accepted_prefix(tokens, draft) -> int:
+    return default().accepted_prefix(tokens, draft)
+
+
+def verify(w_rows: np.ndarray, k: int, h, draft):
+    return default().verify(w_rows, k, h, draft)
 
 
 def _u8(a) -> np.ndarray:

@@ -26,6 +26,11 @@
  * (d has 11 significant bits, code-8 has 4, x has 11), so y differs from the
  * exact real sum only by the rounding of the additions.
  * The greedy token is the lowest index among the maxima of y.
+ * Greedy verify of a speculative draft (the trunk checks the tokens a draft
+ * proposed in one batched pass: aipolix.com SwarmLLM page, section
+ * "Speculation is used to amortize network round trips"): the greedy token of
+ * every row, and the number of leading rows whose greedy token equals the
+ * draft's token for that row (the prefix ends at the first mismatch).
  * Parallelism: OpenMP over independent outputs only; each sum is sequential.
  */
 #include <math.h>
@@ -100,4 +105,12 @@ int64_t q4o_argmax(const double* y, int64_t n) {
         if (y[i] > y[best]) best = i;
     }
     return best;
+}
+
+/* Leading positions i = 0, 1, ... at which tokens[i] == draft[i]; stops at
+ * the first mismatch (m >= 0). */
+int64_t q4o_accepted_prefix(const int64_t* tokens, const int64_t* draft, int64_t m) {
+    int64_t i = 0;
+    while (i < m && tokens[i] == draft[i]) ++i;
+    return i;
 }

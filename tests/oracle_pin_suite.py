@@ -14,6 +14,11 @@ instance disagrees with a fact fixed by the pages' reading or by mathematics:
   argmax_golden     hand-worked argmax cases (tests/golden/argmax.txt)
   argmax_invariants y[r] >= y[i] for all i, y[r] > y[i] for i < r; numpy.argmax
                     (first occurrence) on random vectors; planted ties
+  verify_prefix     hand-worked accepted-prefix cases (first mismatch ends it,
+                    later matches do not count)
+  verify_brute      greedy verify on tiny shapes: tokens = numpy.argmax of the
+                    numpy float64 product of a dense matrix built from the
+                    chosen numbers, drafts with a mismatch planted at each row
 
 ``tests/test_oracle_pins.py`` runs them on the oracle; ``tests/test_oracle_mutants.py``
 plants plausible mistakes into copies of the oracle's source and checks that
@@ -137,8 +142,32 @@ def argmax_invariants(o):
                 assert o.argmax(z) == i
 
 
+def verify_prefix(o):
+    cases = [([5, 3, 9, 9], [5, 3, 9, 9], 4), ([5, 3, 9, 9], [5, 3, 1, 9], 2), ([5, 3, 9, 9], [0, 3, 9, 9], 0),
+             ([5, 3, 9, 9], [5, 3, 9, 8], 3), ([7], [7], 1), ([7], [6], 0), ([1, 2, 3], [1, 0, 3], 1),
+             ([2, 2, 2, 2, 2], [2, 2, 2, 2, 2], 5), ([4, 4], [5, 4], 0)]
+    for tokens, draft, want in cases:
+        assert o.accepted_prefix(tokens, draft) == want, (tokens, draft)
+
+
+def verify_brute(o):
+    rng = np.random.default_rng(17)
+    for m, n, k in ((1, 5, 32), (3, 40, 64), (6, 33, 96), (16, 70, 128)):
+        codes, d, w = q4_encode.random_case(rng, n, k, signed_d=True)
+        dense = q4_encode.weights_from_numbers(codes, d)  # float64 [n, k] from the chosen numbers
+        h = rng.standard_normal((m, k)).astype(np.float16)
+        want = np.argmax(h.astype(np.float64) @ dense.T, axis=1)
+        for j in range(m + 1):  # mismatch planted at row j (j == m: none)
+            draft = want.copy()
+            if j < m:
+                draft[j] = (draft[j] + 1) % n
+            y, a, tokens, accepted = o.verify(w, k, h, draft)
+            assert np.array_equal(tokens, want), (m, n, k)
+            assert accepted == j, (m, n, k, j)
+
+
 ALL = [golden_blocks, f16_exhaustive, basis_columns, all_ones, integer_exact,
-       brute_force, multi_row_layout, argmax_golden, argmax_invariants]
+       brute_force, multi_row_layout, argmax_golden, argmax_invariants, verify_prefix, verify_brute]
 
 
 def failures(o):

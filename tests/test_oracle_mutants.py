@@ -27,6 +27,10 @@ MUTANTS = {
     "argmax_last_tie": ("if (y[i] > y[best])", "if (y[i] >= y[best])"),
     "scale_dropped": ("return (double)(code - 8) * d;", "return (double)(code - 8);"),
     "x_ignored_sign": ("* q4o_f16_to_f64(xr[i]);", "* fabs(q4o_f16_to_f64(xr[i]));"),
+    "prefix_counts_all_matches": ("while (i < m && tokens[i] == draft[i]) ++i;",
+                                  "for (int64_t j = 0; j < m; ++j) i += tokens[j] == draft[j];"),
+    "prefix_past_mismatch": ("while (i < m && tokens[i] == draft[i]) ++i;",
+                             "while (i < m && tokens[i] == draft[i]) ++i;\n    if (i < m) ++i;"),
 }
 
 
