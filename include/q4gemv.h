@@ -64,6 +64,7 @@ typedef int q4_status;
 #define Q4_OP_GEMM_SMALLM 1
 #define Q4_OP_GEMM_PREFILL 2
 #define Q4_OP_LM_HEAD_ARGMAX 3
+#define Q4_OP_LM_HEAD_VERIFY 4
 
 /* Version of this interface (Q4_ABI_VERSION of the library that was built). */
 Q4_API int q4_abi_version(void);
@@ -151,6 +152,35 @@ Q4_API q4_status q4_0_gemm_prefill(const void* w, const void* x, float* y,
 Q4_API q4_status lm_head_argmax(const void* w, const void* h, float* logits, int32_t* token,
                          int64_t n_vocab, int64_t k,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * logits[i][n] = sum_k w[n][k] * h[i][k];  tokens[i] = lowest n with the
+ * largest logits[i][n];  *accepted = the number of leading i (from 0) with
+ * tokens[i] == draft[i]
+ *
+ * Greedy verify of a speculative draft: the trunk checks every token a draft
+ * proposed in one batched pass over the LM head's weights (aipolix.com
+ * SwarmLLM page, section "Speculation is used to amortize network round
+ * trips"; greedy decoding: taozi.news, section "基准成绩").  Row i of h is the
+ * trunk's hidden state at the position the draft filled with draft[i]; the
+ * caller keeps draft[0 .. accepted) and, when accepted < m, takes
+ * tokens[accepted] in place of the rejected one.  The logits of row i satisfy
+ * the bound of q4_0_gemm_smallm (q4_0_gemv for m == 1); tokens[i] is the
+ * lowest index among the maxima of the returned logits[i] (-0 and +0 equal).
+ *   w        : n_vocab rows of k/32 Q4_0 blocks
+ *   h        : m x k binary16, row-major
+ *   logits   : m x n_vocab binary32 (written)
+ *   tokens   : m int32 (written);  draft : m int32 (read);  accepted : 1 int32
+ *              (written); all in device memory, 4-byte aligned
+ *   workspace : q4_workspace_bytes(Q4_OP_LM_HEAD_VERIFY, m, n_vocab, k) bytes
+ *               of device memory, 16-byte aligned; contents on entry do not
+ *               matter.
+ *   1 <= m <= 16, n_vocab >= 1, k % 64 == 0, w and h 16-byte aligned.  Inputs
+ *   finite.  No output may overlap another output or an input.
+ */
+Q4_API q4_status lm_head_verify(const void* w, const void* h, float* logits, int32_t* tokens,
+                                const int32_t* draft, int32_t* accepted, int64_t m, int64_t n_vocab, int64_t k,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * A list of independent GEMVs run as ONE launch ("one command submit per

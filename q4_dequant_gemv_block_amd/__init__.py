@@ -31,11 +31,12 @@ Q4_OP_GEMV = 0
 Q4_OP_GEMM_SMALLM = 1
 Q4_OP_GEMM_PREFILL = 2
 Q4_OP_LM_HEAD_ARGMAX = 3
+Q4_OP_LM_HEAD_VERIFY = 4
 
 # Every symbol include/q4gemv.h declares.
 EXPORTS = (
     "q4_abi_version", "q4_last_error", "q4_workspace_bytes", "q4_0_gemv", "q4_0_gemm_smallm",
-    "q4_0_gemm_prefill", "lm_head_argmax", "q4_0_gemv_batch_plan_bytes", "q4_0_gemv_batch_plan",
+    "q4_0_gemm_prefill", "lm_head_argmax", "lm_head_verify", "q4_0_gemv_batch_plan_bytes", "q4_0_gemv_batch_plan",
     "q4_0_gemm_smallm_batch_plan_bytes", "q4_0_gemm_smallm_batch_plan", "q4_0_gemm_smallm_batch",
     "q4_0_gemm_prefill_batch_plan_bytes", "q4_0_gemm_prefill_batch_plan", "q4_0_gemm_prefill_batch",
     "q4_0_gemv_batch",
@@ -84,6 +85,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.q4_0_gemm_prefill.argtypes = [vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t, vp]
     lib.lm_head_argmax.restype = st
     lib.lm_head_argmax.argtypes = [vp, vp, vp, vp, i64, i64, vp, ctypes.c_size_t, vp]
+    lib.lm_head_verify.restype = st
+    lib.lm_head_verify.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t, vp]
     lib.q4_0_gemv_batch_plan_bytes.restype = ctypes.c_size_t
     lib.q4_0_gemv_batch_plan_bytes.argtypes = [ctypes.POINTER(GemvDesc), ctypes.c_int]
     lib.q4_0_gemv_batch_plan.restype = st
@@ -236,6 +239,35 @@ def lm_head_argmax(w: torch.Tensor, h: torch.Tensor, logits: torch.Tensor | None
                                          n, k, _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
                                          _stream(stream)))
     return logits, token
+
+
+def lm_head_verify(w: torch.Tensor, h: torch.Tensor, draft: torch.Tensor, logits: torch.Tensor | None = None,
+                   tokens: torch.Tensor | None = None, accepted: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None, stream=None):
+    """(logits float32 [M, V], tokens int32 [M], accepted int32 [1]) for the LM head W
+    (uint8 [V, K/32*18]), the trunk's hidden states h (float16 [M, K], M <= 16) and the
+    draft's tokens for the same positions (int32 [M])."""
+    if h.dim() != 2:
+        raise ValueError("h must be float16 [M, K]")
+    m, k = h.shape
+    n = _weights(w, k)
+    if draft.dim() != 1 or draft.shape[0] != m:
+        raise ValueError("draft must be int32 [M]")
+    if logits is None:
+        logits = torch.empty((m, n), dtype=torch.float32, device=h.device)
+    if tokens is None:
+        tokens = torch.empty(m, dtype=torch.int32, device=h.device)
+    if accepted is None:
+        accepted = torch.empty(1, dtype=torch.int32, device=h.device)
+    need = workspace_bytes(Q4_OP_LM_HEAD_VERIFY, m, n, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=h.device)
+    _check(load_library().lm_head_verify(_ptr(w, torch.uint8, "w"), _ptr(h, torch.float16, "h"),
+                                         _ptr(logits, torch.float32, "logits"), _ptr(tokens, torch.int32, "tokens"),
+                                         _ptr(draft, torch.int32, "draft"), _ptr(accepted, torch.int32, "accepted"),
+                                         m, n, k, _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                         _stream(stream)))
+    return logits, tokens, accepted
 
 
 class GemmPlan(ctypes.Structure):

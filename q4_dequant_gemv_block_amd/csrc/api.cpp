@@ -98,6 +98,9 @@ size_t q4_workspace_bytes(int op, int64_t m, int64_t n, int64_t k) {
         case Q4_OP_LM_HEAD_ARGMAX:
             if (n < 1 || k < 32) return 0;
             return (size_t)q4::argmax_blocks(n, k) * sizeof(uint64_t);
+        case Q4_OP_LM_HEAD_VERIFY:
+            if (m < 1 || m > 16 || n < 1 || n > kMaxN || k < 64 || k % 64 != 0 || k > kMaxK) return 0;
+            return q4::verify_workspace_bytes(m, n, k);
         default:
             return 0;
     }
@@ -191,6 +194,39 @@ q4_status lm_head_argmax(const void* w, const void* h, float* logits, int32_t* t
                                             token, n_vocab, k, static_cast<uint64_t*>(workspace),
                                             static_cast<hipStream_t>(stream));
     return hip_status(e, "lm_head_argmax launch");
+}
+
+q4_status lm_head_verify(const void* w, const void* h, float* logits, int32_t* tokens, const int32_t* draft,
+                         int32_t* accepted, int64_t m, int64_t n_vocab, int64_t k, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    const char* fn = "lm_head_verify";
+    q4_status st = check_shape(fn, m, 16, n_vocab, k);
+    if (st) return st;
+    st = check_tensors(fn, w, h, logits, m, n_vocab, k, (size_t)(m * n_vocab) * 4);
+    if (st) return st;
+    if (!tokens || !draft || !accepted) return fail(Q4_ERR_INVALID_ARG, "%s: null tokens, draft or accepted", fn);
+    if (!aligned(tokens, 4) || !aligned(draft, 4) || !aligned(accepted, 4))
+        return fail(Q4_ERR_MISALIGNED, "%s: tokens, draft and accepted must be 4-byte aligned", fn);
+    if (!fast_path(w, k))
+        return fail(Q4_ERR_INVALID_ARG, "%s: needs k %% 64 == 0 and k <= %lld", fn, (long long)q4::kFastMaxK);
+    const size_t need = q4_workspace_bytes(Q4_OP_LM_HEAD_VERIFY, m, n_vocab, k);
+    if (!workspace || workspace_bytes < need)
+        return fail(Q4_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
+    if (!aligned(workspace, 16)) return fail(Q4_ERR_MISALIGNED, "%s: workspace must be 16-byte aligned", fn);
+    const Range rw = range(w, (size_t)(n_vocab * row_bytes(k))), rh = range(h, (size_t)(m * k) * 2),
+                rl = range(logits, (size_t)(m * n_vocab) * 4), rt = range(tokens, (size_t)m * 4),
+                rd = range(draft, (size_t)m * 4), ra = range(accepted, 4), rws = range(workspace, need);
+    const Range outs[4] = {rl, rt, ra, rws}, ins[3] = {rw, rh, rd};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j])) return fail(Q4_ERR_INVALID_ARG, "%s: outputs must not overlap", fn);
+        for (int j = 0; j < 3; ++j)
+            if (overlap(outs[i], ins[j])) return fail(Q4_ERR_INVALID_ARG, "%s: an output overlaps an input", fn);
+    }
+    const hipError_t e = q4::launch_lm_head_verify(static_cast<const uint8_t*>(w), static_cast<const uint16_t*>(h),
+                                                   logits, tokens, draft, accepted, m, n_vocab, k, workspace,
+                                                   static_cast<hipStream_t>(stream));
+    return hip_status(e, "lm_head_verify launch");
 }
 
 }  // extern "C"

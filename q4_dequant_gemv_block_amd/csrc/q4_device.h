@@ -143,4 +143,35 @@ __host__ __device__ inline void chunk_positions(int c, int (&pos)[4]) {
     }
 }
 
+// Greedy pick: the maximum of these keys over a set of (logit, index) is the
+// lowest index among the largest logits.
+// Order-preserving key: larger logit first, then lower index; -0 counts as +0.
+__device__ __forceinline__ uint64_t argmax_key(float v, int64_t idx) {
+    uint32_t u = __builtin_bit_cast(uint32_t, v);
+    if ((u << 1) == 0u) u = 0u;  // -0 -> +0
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, o);
+        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), o);
+        const uint64_t t = ((uint64_t)hi << 32) | lo;
+        v = t > v ? t : v;
+    }
+    return v;
+}
+
+// Maximum over the workgroup; sh holds one entry per wave.
+__device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* sh) {
+    v = wave_max_u64(v);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+    __syncthreads();
+    uint64_t r = 0;
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) r = sh[i] > r ? sh[i] : r;
+    return r;
+}
+
 }  // namespace q4

@@ -119,6 +119,12 @@ int64_t prefill_fill(PfDesc* d, int tile_m, int64_t tile_begin);
 hipError_t launch_gemm_prefill_batch(void* plan, int n_chunked, int64_t tiles_chunked, int n_other,
                                      int64_t tiles_other, int tile_m, hipStream_t s);
 int argmax_blocks(int64_t n, int64_t k);
+// Greedy verify of a draft (verify.hip): small-M logits (the GEMV for m = 1),
+// row argmax keys, tokens and the accepted prefix; workspace as below.
+size_t verify_workspace_bytes(int64_t m, int64_t n, int64_t k);
+hipError_t launch_lm_head_verify(const uint8_t* w, const uint16_t* h, float* logits, int32_t* tokens,
+                                 const int32_t* draft, int32_t* accepted, int64_t m, int64_t n, int64_t k,
+                                 void* workspace, hipStream_t s);
 hipError_t launch_lm_head(const uint8_t* w, const uint16_t* h, float* logits, int32_t* token,
                           int64_t n, int64_t k, uint64_t* keys, hipStream_t s);
 // `plan`: SchedHead, then `count` PlanDesc, then `nchunks` SchedChunk.

@@ -1,0 +1,90 @@
+// Greedy verify of a speculative draft: logits[i][n] = sum_k w[n][k] h[i][k]
+// for the m <= 16 rows of h (the trunk's hidden states at the draft's
+// positions), tokens[i] = lowest n among the largest logits[i][n], and
+// accepted = the number of leading rows i with tokens[i] == draft[i].
+//
+// The trunk checks all the tokens a draft proposed in one batched pass
+// (aipolix.com SwarmLLM page, section "Speculation is used to amortize network
+// round trips"); decoding is greedy (taozi.news, section "基准成绩").  The
+// logits come from the small-M GEMM (one pass over the vocabulary's weights
+// for all m rows; the GEMV for m = 1); then every row's slices are reduced to
+// 64-bit keys (argmax_key: larger logit first, then lower index) and one
+// workgroup picks each row's token and counts the accepted prefix.
+#include "q4_device.h"
+#include "q4_launch.h"
+
+#include <algorithm>
+
+namespace q4 {
+
+namespace {
+
+constexpr int kRowThreads = 256;
+
+// keys[i * B + b] = max key over slice b of row i (blockIdx.x = b, blockIdx.y = i).
+__global__ void __launch_bounds__(kRowThreads) k_argmax_rows(const float* __restrict__ logits, int64_t n,
+                                                            uint64_t* __restrict__ keys) {
+    __shared__ uint64_t sh[kRowThreads / 64];
+    const int64_t B = gridDim.x;
+    const int64_t lo = n * blockIdx.x / B, hi = n * (blockIdx.x + 1) / B;
+    const float* row = logits + (int64_t)blockIdx.y * n;
+    uint64_t best = 0;
+    for (int64_t j = lo + threadIdx.x; j < hi; j += kRowThreads) {
+        const uint64_t kk = argmax_key(row[j], j);
+        best = kk > best ? kk : best;
+    }
+    const uint64_t b = block_max_u64(best, sh);
+    if (threadIdx.x == 0) keys[(int64_t)blockIdx.y * B + blockIdx.x] = b;
+}
+
+// One workgroup: tokens[i] from row i's B keys, then the accepted prefix.
+__global__ void __launch_bounds__(kRowThreads) k_verify_final(const uint64_t* __restrict__ keys, int B, int m,
+                                                             const int32_t* __restrict__ draft,
+                                                             int32_t* __restrict__ tokens,
+                                                             int32_t* __restrict__ accepted) {
+    __shared__ uint64_t sh[kRowThreads / 64];
+    __shared__ int32_t tok[16];
+    for (int i = 0; i < m; ++i) {
+        uint64_t best = 0;
+        for (int b = threadIdx.x; b < B; b += kRowThreads) best = keys[(int64_t)i * B + b] > best ? keys[(int64_t)i * B + b] : best;
+        const uint64_t r = block_max_u64(best, sh);
+        if (threadIdx.x == 0) {
+            tok[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)(r & 0xFFFFFFFFu));
+            tokens[i] = tok[i];
+        }
+        __syncthreads();  // sh is reused by the next row
+    }
+    if (threadIdx.x == 0) {
+        int a = 0;
+        while (a < m && tok[a] == draft[a]) ++a;
+        accepted[0] = a;
+    }
+}
+
+// Slices per row: about 2,048 logits each, at most 256.
+int verify_slices(int64_t n) { return (int)std::max<int64_t>(1, std::min<int64_t>(256, (n + 2047) / 2048)); }
+
+}  // namespace
+
+size_t verify_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+    const size_t gemm = m >= 2 ? (smallm_workspace_bytes(m, n, k) + 255) / 256 * 256 : 0;
+    return gemm + (size_t)m * verify_slices(n) * sizeof(uint64_t);
+}
+
+hipError_t launch_lm_head_verify(const uint8_t* w, const uint16_t* h, float* logits, int32_t* tokens,
+                                 const int32_t* draft, int32_t* accepted, int64_t m, int64_t n, int64_t k,
+                                 void* workspace, hipStream_t s) {
+    const size_t gemm = m >= 2 ? (smallm_workspace_bytes(m, n, k) + 255) / 256 * 256 : 0;
+    uint64_t* keys = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) + gemm);
+    hipError_t e = m >= 2 ? launch_gemm_smallm(w, h, logits, m, n, k, static_cast<float*>(workspace), s)
+                          : launch_gemv(w, h, logits, n, k, s);
+    if (e != hipSuccess) return e;
+    const int B = verify_slices(n);
+    hipLaunchKernelGGL(k_argmax_rows, dim3(B, (unsigned)m), dim3(kRowThreads), 0, s, logits, n, keys);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_verify_final, dim3(1), dim3(kRowThreads), 0, s, keys, B, (int)m, draft, tokens, accepted);
+    return hipGetLastError();
+}
+
+}  // namespace q4

@@ -159,6 +159,30 @@ def test_lm_head_validation(lib):
     assert lib.lm_head_argmax(w, h, lg, tok, 1000, 96, FAKE * 16, need, None) == q4.Q4_ERR_INVALID_ARG
 
 
+def test_verify_validation(lib):
+    w, h, lg = FAKE * 64, FAKE * 4096, FAKE * 8192
+    tok, dr, acc, ws = FAKE * 12288, FAKE * 12289, FAKE * 12290, FAKE * 16384
+    n, k = 151936, 5120
+    need = lib.q4_workspace_bytes(q4.Q4_OP_LM_HEAD_VERIFY, 4, n, k)
+    assert need >= 4 * 8 and need % 8 == 0
+    assert lib.q4_workspace_bytes(q4.Q4_OP_LM_HEAD_VERIFY, 17, n, k) == 0
+    ok = (w, h, lg, tok, dr, acc)
+    assert lib.lm_head_verify(*ok, 0, n, k, ws, need, None) == q4.Q4_ERR_INVALID_ARG
+    assert lib.lm_head_verify(*ok, 17, n, k, ws, need, None) == q4.Q4_ERR_INVALID_ARG
+    assert b"m = 17" in lib.q4_last_error()
+    assert lib.lm_head_verify(w, h, lg, tok, None, acc, 4, n, k, ws, need, None) == q4.Q4_ERR_INVALID_ARG
+    assert lib.lm_head_verify(w, h, lg, tok + 2, dr, acc, 4, n, k, ws, need, None) == q4.Q4_ERR_MISALIGNED
+    assert lib.lm_head_verify(*ok, 4, n, k, None, 0, None) == q4.Q4_ERR_WORKSPACE
+    assert lib.lm_head_verify(*ok, 4, n, k, ws, need - 8, None) == q4.Q4_ERR_WORKSPACE
+    assert lib.lm_head_verify(*ok, 4, n, k, ws + 8, need, None) == q4.Q4_ERR_MISALIGNED
+    # accepted inside the tokens, tokens inside the logits, workspace over the draft
+    assert lib.lm_head_verify(w, h, lg, tok, dr, tok + 4, 4, n, k, ws, need, None) == q4.Q4_ERR_INVALID_ARG
+    assert lib.lm_head_verify(w, h, lg, lg + 64, dr, acc, 4, n, k, ws, need, None) == q4.Q4_ERR_INVALID_ARG
+    assert lib.lm_head_verify(w, h, lg, tok, dr, acc, 4, n, k, dr, need, None) == q4.Q4_ERR_INVALID_ARG
+    # k % 64 != 0 is not supported here
+    assert lib.lm_head_verify(*ok, 4, n, 96, ws, need, None) == q4.Q4_ERR_INVALID_ARG
+
+
 def test_batch_plan_validation(lib):
     D = q4.GemvDesc
     plan = q4.GemvPlan()
