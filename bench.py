@@ -255,6 +255,36 @@ def bench_lmhead(args):
                          "kernel": "q4::k_sweep<QuadEngine<12,2,2,288>,ARGMAX> + q4::k_argmax_final"}}
 
 
+def bench_verify(args):
+    """Greedy verify of an M-token draft against the LM head (151,936 x 5,120):
+    the M rows' logits, their greedy tokens and the accepted prefix, per call."""
+    import torch
+    import synth
+    q4 = load_q4()
+    m = args.m or 4
+    n, k = synth.VOCAB, synth.HIDDEN
+    w = torch.from_numpy(synth.q4_0(SEED, synth.stream_id(2, 0, 0, synth.T_W), n, k)).cuda()
+    h = torch.from_numpy(synth.f16_normal(SEED, synth.stream_id(2, 0, 1, synth.T_X), m * k).reshape(m, k)).cuda()
+    draft = torch.zeros(m, dtype=torch.int32, device="cuda")
+    lg = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    tok = torch.empty(m, dtype=torch.int32, device="cuda")
+    acc = torch.empty(1, dtype=torch.int32, device="cuda")
+    wsp = torch.empty(max(16, q4.workspace_bytes(q4.Q4_OP_LM_HEAD_VERIFY, m, n, k)), dtype=torch.uint8, device="cuda")
+    ms = time_steps(lambda: q4.lm_head_verify(w, h, draft, lg, tok, acc, wsp), args.steps * 10, args.warmup)
+    bytes_ = n * k // 32 * 18 + m * k * 2 + m * n * 4 + 2 * m * 4 + 4
+    gbs = bytes_ / (ms * 1e-3) / 1e9
+    return {"metric": "greedy verify of an M-token draft: LM head GB/s (151936x5120 Q4_0, M=%d)" % m,
+            "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps * 10, "warmup": args.warmup,
+            "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f16->f32", "data": "synthetic",
+            "config": {"workload": "verify M=%d draft rows against the LM head 151936x5120" % m},
+            "draft_tokens_per_s": round(m / (ms * 1e-3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "kernel": ("q4::k_sweep (GEMV)" if m == 1 else "q4::k_smallm") +
+                                   " + k_argmax_rows + k_verify_final"}}
+
+
 def bench_gemm(args, prefill: bool):
     import torch
     q4 = load_q4()
@@ -351,7 +381,8 @@ def main():
     # the first launches after the inputs are written run slower (about 40 %
     # on the first one, settling within about ten launches of the sweep)
     ap.add_argument("--warmup", type=int, default=25)
-    ap.add_argument("--workload", default="sweep", choices=["sweep", "gemv", "lmhead", "smallm", "prefill", "copy"])
+    ap.add_argument("--workload", default="sweep",
+                    choices=["sweep", "gemv", "lmhead", "verify", "smallm", "prefill", "copy"])
     ap.add_argument("--m", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--record-traffic", nargs=6, metavar=("WORKLOAD", "KERNEL", "FETCH_CSV", "WRITE_CSV",
@@ -368,7 +399,7 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    fn = {"sweep": bench_sweep, "gemv": bench_gemv, "lmhead": bench_lmhead, "copy": bench_copy,
+    fn = {"sweep": bench_sweep, "gemv": bench_gemv, "lmhead": bench_lmhead, "verify": bench_verify, "copy": bench_copy,
           "smallm": lambda a: bench_gemm(a, False), "prefill": lambda a: bench_gemm(a, True)}[args.workload]
     out = fn(args)
     print(json.dumps(out), flush=True)
