@@ -43,8 +43,8 @@ def log(*a):
 
 # Kernel source of each workload's dominant kernel (besides the shared device
 # and launch headers, the host-side C ABI and the build script).
-KERNEL_SOURCE = {"sweep": "gemv.hip", "gemv": "gemv.hip", "lmhead": "gemv.hip", "smallm": "smallm.hip",
-                 "prefill": "prefill.hip"}
+KERNEL_SOURCE = {"sweep": ["gemv.hip"], "gemv": ["gemv.hip"], "lmhead": ["gemv.hip"], "smallm": ["smallm.hip"],
+                 "prefill": ["prefill.hip"], "verify": ["smallm.hip", "gemv.hip", "verify.hip"]}
 
 
 def kernel_source_hash(workload: str) -> str:
@@ -54,7 +54,7 @@ def kernel_source_hash(workload: str) -> str:
     import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "q4_dequant_gemv_block_amd", "csrc")
-    names = [KERNEL_SOURCE[workload.split("_m")[0]], "q4_device.h", "q4_launch.h", "api.cpp"]
+    names = KERNEL_SOURCE[workload.split("_m")[0]] + ["q4_device.h", "q4_launch.h", "api.cpp"]
     files = [os.path.join(csrc, n) for n in sorted(names)]
     files.append(os.path.join(ROOT, "q4_dequant_gemv_block_amd", "build.py"))
     for path in files:
@@ -280,7 +280,7 @@ def bench_verify(args):
             "config": {"workload": "verify M=%d draft rows against the LM head 151936x5120" % m},
             "draft_tokens_per_s": round(m / (ms * 1e-3), 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counter_traffic("verify_m%d" % m),
                          "kernel": ("q4::k_sweep (GEMV)" if m == 1 else "q4::k_smallm") +
                                    " + k_argmax_rows + k_verify_final"}}
 
