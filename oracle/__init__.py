@@ -6,9 +6,10 @@ it and shares no code with it.  The arithmetic lives in ``q4_oracle.c`` (the
 definition it follows is written out in that file's header); this module only
 compiles it with gcc and marshals numpy arrays.
 
-Pinned by ``tests/test_oracle_pins.py`` (hand-computed blocks in
-``tests/golden/``, exhaustive binary16 decode against numpy, closed forms,
-exact integer products, brute force on tiny shapes, argmax invariants).
+Pinned by ``tests/test_oracle_pins.py`` (hand-computed blocks and final-norm
+cases in ``tests/golden/``, exhaustive binary16 decode and binary16 rounding
+against numpy, closed forms, exact integer products, brute force on tiny
+shapes, argmax invariants).
 """
 from __future__ import annotations
 
@@ -55,6 +56,10 @@ class Oracle:
         lib.q4o_argmax.restype = i64
         lib.q4o_accepted_prefix.argtypes = [vp, vp, i64]
         lib.q4o_accepted_prefix.restype = i64
+        lib.q4o_f64_to_f16.argtypes = [ctypes.c_double]
+        lib.q4o_f64_to_f16.restype = ctypes.c_uint16
+        lib.q4o_f64_to_f16_array.argtypes = [vp, i64, vp]
+        lib.q4o_rms_norm.argtypes = [vp, vp, i64, ctypes.c_double, vp, vp]
         self.lib = lib
         self.path = path
 
@@ -114,6 +119,31 @@ class Oracle:
         tokens = np.array([self.argmax(y[i]) for i in range(y.shape[0])], dtype=np.int64)
         return y, a, tokens, self.accepted_prefix(tokens, draft)
 
+    def f64_to_f16(self, v) -> np.ndarray:
+        """binary64 -> binary16 bit patterns (uint16), nearest, ties to even."""
+        a = np.ascontiguousarray(np.asarray(v, dtype=np.float64))
+        out = np.empty(a.shape, dtype=np.uint16)
+        self.lib.q4o_f64_to_f16_array(a.ctypes.data, a.size, out.ctypes.data)
+        return out
+
+    def rms_norm(self, h, g, eps: float) -> tuple[np.ndarray, np.ndarray]:
+        """The final norm of one hidden state: (x, v) for f16 h and gain g [K];
+        v = h * g / sqrt(mean(h^2) + eps) in binary64, x its binary16 bit patterns."""
+        hb = np.ascontiguousarray(_f16bits(np.asarray(h)).ravel())
+        gb = np.ascontiguousarray(_f16bits(np.asarray(g)).ravel())
+        assert hb.size == gb.size >= 1
+        v = np.empty(hb.size, dtype=np.float64)
+        x = np.empty(hb.size, dtype=np.uint16)
+        self.lib.q4o_rms_norm(hb.ctypes.data, gb.ctypes.data, hb.size, float(eps), v.ctypes.data, x.ctypes.data)
+        return x, v
+
+    def lm_head_norm(self, w_rows: np.ndarray, k: int, h, g, eps: float):
+        """Final norm, then the LM head: (y, a, token, x) for f16 h and g [K]; x is the
+        normed activation (binary16 bits), y, a as gemm_rows on x, token = argmax(y)."""
+        x, _ = self.rms_norm(h, g, eps)
+        y, a = self.gemm_rows(w_rows, k, x)
+        return y, a, self.argmax(y), x
+
 
 def default() -> Oracle:
     global _default
@@ -147,6 +177,18 @@ def accepted_prefix(tokens, draft) -> int:
 
 def verify(w_rows: np.ndarray, k: int, h, draft):
     return default().verify(w_rows, k, h, draft)
+
+
+def f64_to_f16(v) -> np.ndarray:
+    return default().f64_to_f16(v)
+
+
+def rms_norm(h, g, eps: float):
+    return default().rms_norm(h, g, eps)
+
+
+def lm_head_norm(w_rows: np.ndarray, k: int, h, g, eps: float):
+    return default().lm_head_norm(w_rows, k, h, g, eps)
 
 
 def _u8(a) -> np.ndarray:

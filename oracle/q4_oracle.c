@@ -31,6 +31,16 @@
  * "Speculation is used to amortize network round trips"): the greedy token of
  * every row, and the number of leading rows whose greedy token equals the
  * draft's token for that row (the prefix ends at the first mismatch).
+ * The final norm before the LM head (the host applies it to the hidden state
+ * the last stage returns, then the LM head and sampling: originshq.com page,
+ * section "The Architecture: Layers Distributed, Activations in Flight";
+ * taozi.news, section "技术架构").  The pages name the step only; the reading
+ * used here is RMS normalisation with a learned per-element gain g and a
+ * small constant eps:
+ *   r   = 1 / sqrt( (sum over i = 0..K-1, in increasing i, of h_i^2) / K + eps )
+ *   v_i = h_i * g_i * r                       (binary64)
+ *   x_i = v_i rounded to binary16, nearest, ties to even
+ * and x is the activation the LM head multiplies.
  * Parallelism: OpenMP over independent outputs only; each sum is sequential.
  */
 #include <math.h>
@@ -113,4 +123,52 @@ int64_t q4o_accepted_prefix(const int64_t* tokens, const int64_t* draft, int64_t
     int64_t i = 0;
     while (i < m && tokens[i] == draft[i]) ++i;
     return i;
+}
+
+/* binary64 -> binary16, round to nearest, ties to even (IEEE 754
+ * roundTiesToEven).  The result's quantum is 2^(E-10) for |v| in the binade
+ * [2^E, 2^(E+1)), E >= -14, and 2^-24 below 2^-14 (subnormals); |v| >= 65520
+ * (the midpoint above the largest finite value 65504, whose last fraction bit
+ * is odd) rounds to infinity; NaN gives the quiet NaN 0x7E00. */
+uint16_t q4o_f64_to_f16(double v) {
+    if (isnan(v)) return 0x7E00;
+    const uint16_t sign = signbit(v) ? 0x8000 : 0;
+    const double a = fabs(v);
+    if (a >= 65520.0) return sign | 0x7C00;
+    if (a == 0.0) return sign;
+    int e2;
+    frexp(a, &e2);           /* a in [2^(e2-1), 2^e2) */
+    int E = e2 - 1;
+    if (E < -14) E = -14;    /* subnormals share the smallest binade's quantum */
+    const double t = ldexp(a, 10 - E);  /* a in quanta: exact (power-of-two scaling) */
+    double q = floor(t);
+    const double rem = t - q;           /* exact */
+    if (rem > 0.5 || (rem == 0.5 && fmod(q, 2.0) != 0.0)) q += 1.0;
+    /* value = q * 2^(E-10), 0 <= q <= 2048 */
+    if (q >= 2048.0) {  /* carried into the next binade */
+        q = 1024.0;
+        E += 1;
+    }
+    if (q < 1024.0) return sign | (uint16_t)q;  /* subnormal (only when E == -14) or zero */
+    return sign | (uint16_t)(((E + 15) << 10) | ((int)q - 1024));
+}
+
+void q4o_f64_to_f16_array(const double* v, int64_t n, uint16_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = q4o_f64_to_f16(v[i]);
+}
+
+/* The final norm: h and g binary16 [K], eps >= 0; v (binary64 [K], may be
+ * NULL) receives h_i g_i r, x (binary16 [K]) its rounding. */
+void q4o_rms_norm(const uint16_t* h, const uint16_t* g, int64_t k, double eps, double* v, uint16_t* x) {
+    double ss = 0.0;
+    for (int64_t i = 0; i < k; ++i) {
+        const double hi = q4o_f16_to_f64(h[i]);
+        ss += hi * hi;
+    }
+    const double r = 1.0 / sqrt(ss / (double)k + eps);
+    for (int64_t i = 0; i < k; ++i) {
+        const double vi = q4o_f16_to_f64(h[i]) * q4o_f16_to_f64(g[i]) * r;
+        if (v) v[i] = vi;
+        x[i] = q4o_f64_to_f16(vi);
+    }
 }

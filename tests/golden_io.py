@@ -59,3 +59,21 @@ def argmax_cases():
         ys = [v for key, v in c["_lines"] if key == "y"][0]
         out.append(dict(name=c["name"], y=np.array([float(t) for t in ys]), r=c["r"]))
     return out
+
+
+def rms_norm_cases():
+    """Hand-worked final-norm cases: dict(name, h float16[K], g float16[K], eps float32, x float16[K])."""
+    out = []
+    for c in _cases("rms_norm.txt"):
+        f = {key: v for key, v in c["_lines"]}
+        h = np.array([float(t) for t in f["h"]], dtype=np.float64)
+        g = np.array([float(t) for t in f["g"]], dtype=np.float64)
+        x = np.array([float(t) for t in f["x"]], dtype=np.float64)
+        eps = float(f["eps"][0])
+        for name, v in (("h", h), ("g", g), ("x", x)):
+            assert np.array_equal(v.astype(np.float16).astype(np.float64), v), (c["name"], name)
+        assert float(np.float32(eps)) == eps, c["name"]
+        assert h.size == g.size == x.size, c["name"]
+        out.append(dict(name=c["name"], h=h.astype(np.float16), g=g.astype(np.float16), eps=eps,
+                        x=x.astype(np.float16)))
+    return out

@@ -19,6 +19,18 @@ instance disagrees with a fact fixed by the pages' reading or by mathematics:
   verify_brute      greedy verify on tiny shapes: tokens = numpy.argmax of the
                     numpy float64 product of a dense matrix built from the
                     chosen numbers, drafts with a mismatch planted at each row
+  f16_round         binary64 -> binary16 against numpy's float16 conversion on
+                    every binary16 value, every midpoint between neighbours
+                    (ties), one binary64 step either side of each, the
+                    overflow threshold and random values across the range
+  norm_golden       hand-worked final-norm cases (tests/golden/rms_norm.txt)
+  norm_closed_forms constant vectors normalise to +-1; sum of v^2 = K with
+                    unit gain; power-of-two scaling of h leaves x unchanged
+                    and of g scales v; eps dominates a tiny h
+  norm_brute        random h, g, eps against numpy float64 (pairwise mean,
+                    numpy sqrt, numpy float16 rounding), lengths 1 to 5120
+  lm_head_norm_brute final norm then LM head on tiny shapes: token = numpy.argmax
+                    of the dense product with numpy's normed activation
 
 ``tests/test_oracle_pins.py`` runs them on the oracle; ``tests/test_oracle_mutants.py``
 plants plausible mistakes into copies of the oracle's source and checks that
@@ -166,8 +178,94 @@ def verify_brute(o):
             assert accepted == j, (m, n, k, j)
 
 
+def f16_round(o):
+    pos = np.arange(0, 0x7C00, dtype=np.uint32).astype(np.uint16)  # +0 .. 65504
+    vals = pos.view(np.float16).astype(np.float64)
+    mids = (vals[:-1] + vals[1:]) / 2  # exact in binary64
+    top = np.array([65504.0 + 8.0, 65520.0, np.nextafter(65520.0, 0.0), 1e9])  # ties at the top: 65520 -> inf
+    rng = np.random.default_rng(23)
+    rnd = np.exp2(rng.uniform(-30.0, 17.0, 200000)) * rng.choice([-1.0, 1.0], 200000)
+    cand = np.concatenate([vals, -vals, mids, -mids, np.nextafter(mids, 0.0), np.nextafter(mids, np.inf),
+                           top, -top, rnd, [0.0, -0.0, np.inf, -np.inf]])
+    got = o.f64_to_f16(cand)
+    with np.errstate(over="ignore"):
+        want = cand.astype(np.float16).view(np.uint16)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(cand[i], got[i], want[i]) for i in bad[:5]]
+    assert np.isnan(o.f64_to_f16(np.array([np.nan])).view(np.float16)[0])
+
+
+def norm_golden(o):
+    for c in golden_io.rms_norm_cases():
+        x, v = o.rms_norm(c["h"], c["g"], c["eps"])
+        assert np.array_equal(x, c["x"].view(np.uint16)), (c["name"], x.view(np.float16), c["x"])
+
+
+def norm_closed_forms(o):
+    k = 96
+    ones = np.ones(k, dtype=np.float16)
+    for c in (1.0, -3.0, 0.0078125, 2.0 ** -20, 60000.0):
+        h = np.full(k, c, dtype=np.float16)
+        x, v = o.rms_norm(h, ones, 0.0)
+        assert np.all(v == np.sign(c)) and np.all(x.view(np.float16) == np.sign(c)), c
+    rng = np.random.default_rng(29)
+    for k in (1, 5, 64, 1000):
+        h = rng.standard_normal(k).astype(np.float16)
+        h[0] = 1.5  # not all zero
+        g = (1.0 + 0.25 * rng.standard_normal(k)).astype(np.float16)
+        x, v = o.rms_norm(h, np.ones(k, dtype=np.float16), 0.0)
+        assert abs(np.sum(v * v) / k - 1.0) < 1e-12, k
+        for s in (0.5, 2.0, 8.0):  # h stays exact in binary16 when scaled by these
+            x2, v2 = o.rms_norm((h.astype(np.float64) * s).astype(np.float16), np.ones(k, dtype=np.float16), 0.0)
+            assert np.array_equal(x2, x) and np.allclose(v2, v, rtol=1e-15, atol=0), (k, s)
+        _, vg = o.rms_norm(h, g, 0.0)
+        _, vg2 = o.rms_norm(h, (g.astype(np.float64) * 4).astype(np.float16), 0.0)
+        assert np.array_equal(vg2, 4 * vg), k
+        tiny = np.full(k, 2.0 ** -12, dtype=np.float16)
+        _, vt = o.rms_norm(tiny, g, 1.0)  # r = 1 / sqrt(2^-24 + 1)
+        assert np.allclose(vt, 2.0 ** -12 * g.astype(np.float64) / np.sqrt(1.0 + 2.0 ** -24), rtol=1e-15), k
+
+
+def _numpy_norm(h, g, eps):
+    h64, g64 = h.astype(np.float64), g.astype(np.float64)
+    return h64 * g64 / np.sqrt(np.mean(h64 * h64) + eps)
+
+
+def norm_brute(o):
+    rng = np.random.default_rng(31)
+    for k in (1, 2, 7, 64, 333, 5120):
+        for eps in (float(np.float32(1e-6)), 0.0, 1.0):
+            for scale in (1.0, 1e-3, 200.0):
+                h = (scale * rng.standard_normal(k)).astype(np.float16)
+                h[rng.integers(k)] = np.float16(scale)
+                g = (1.0 + 0.25 * rng.standard_normal(k)).astype(np.float16)
+                x, v = o.rms_norm(h, g, eps)
+                want_v = _numpy_norm(h, g, eps)
+                assert np.allclose(v, want_v, rtol=1e-13, atol=0), (k, eps, scale)
+                # the two sides sum in different orders, so v may differ in its last
+                # bits; none of these seeds puts a v that close to a rounding midpoint
+                assert np.array_equal(x, want_v.astype(np.float16).view(np.uint16)), (k, eps, scale)
+
+
+def lm_head_norm_brute(o):
+    rng = np.random.default_rng(37)
+    for n, k in ((5, 32), (40, 64), (33, 96), (70, 128)):
+        codes, d, w = q4_encode.random_case(rng, n, k, signed_d=True)
+        dense = q4_encode.weights_from_numbers(codes, d)
+        h = (4.0 * rng.standard_normal(k)).astype(np.float16)
+        g = (1.0 + 0.25 * rng.standard_normal(k)).astype(np.float16)
+        eps = float(np.float32(1e-6))
+        x_np = _numpy_norm(h, g, eps).astype(np.float16)
+        y_np = dense @ x_np.astype(np.float64)
+        y, a, token, x = o.lm_head_norm(w, k, h, g, eps)
+        assert np.array_equal(x, x_np.view(np.uint16)), (n, k)
+        assert np.allclose(y, y_np, rtol=1e-12, atol=1e-12), (n, k)
+        assert token == int(np.argmax(y_np)), (n, k)
+
+
 ALL = [golden_blocks, f16_exhaustive, basis_columns, all_ones, integer_exact,
-       brute_force, multi_row_layout, argmax_golden, argmax_invariants, verify_prefix, verify_brute]
+       brute_force, multi_row_layout, argmax_golden, argmax_invariants, verify_prefix, verify_brute,
+       f16_round, norm_golden, norm_closed_forms, norm_brute, lm_head_norm_brute]
 
 
 def failures(o):

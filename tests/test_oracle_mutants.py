@@ -29,6 +29,19 @@ MUTANTS = {
     "x_ignored_sign": ("* q4o_f16_to_f64(xr[i]);", "* fabs(q4o_f16_to_f64(xr[i]));"),
     "prefix_counts_all_matches": ("while (i < m && tokens[i] == draft[i]) ++i;",
                                   "for (int64_t j = 0; j < m; ++j) i += tokens[j] == draft[j];"),
+    "norm_sum_not_mean": ("sqrt(ss / (double)k + eps)", "sqrt(ss + eps)"),
+    "norm_eps_outside_root": ("1.0 / sqrt(ss / (double)k + eps)", "1.0 / (sqrt(ss / (double)k) + eps)"),
+    "norm_root_missing": ("1.0 / sqrt(ss / (double)k + eps)", "1.0 / (ss / (double)k + eps)"),
+    "norm_gain_ignored": ("q4o_f16_to_f64(h[i]) * q4o_f16_to_f64(g[i]) * r", "q4o_f16_to_f64(h[i]) * r"),
+    "norm_gain_reversed": ("q4o_f16_to_f64(g[i]) * r", "q4o_f16_to_f64(g[k - 1 - i]) * r"),
+    "norm_sum_of_abs": ("ss += hi * hi;", "ss += fabs(hi);"),
+    "f16_ties_away_from_zero": ("(rem == 0.5 && fmod(q, 2.0) != 0.0)", "(rem == 0.5)"),
+    "f16_truncates": ("if (rem > 0.5 || (rem == 0.5 && fmod(q, 2.0) != 0.0)) q += 1.0;", ""),
+    "f16_overflow_saturates": ("if (a >= 65520.0) return sign | 0x7C00;", "if (a >= 65520.0) return sign | 0x7BFF;"),
+    "f16_overflow_threshold_65504": ("if (a >= 65520.0)", "if (a > 65504.0)"),
+    "f16_subnormal_quantum": ("if (E < -14) E = -14;", "if (E < -15) E = -15;"),
+    "f16_carry_lost": ("q = 1024.0;\n        E += 1;", "q = 2047.0;"),
+    "f16_sign_dropped": ("const uint16_t sign = signbit(v) ? 0x8000 : 0;", "const uint16_t sign = 0;"),
     "prefix_past_mismatch": ("while (i < m && tokens[i] == draft[i]) ++i;",
                              "while (i < m && tokens[i] == draft[i]) ++i;\n    if (i < m) ++i;"),
 }
