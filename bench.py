@@ -1,6 +1,7 @@
 """Benchmark of the Q4_0 dequantize-and-multiply path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sweep|gemv|lmhead|smallm|prefill]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload sweep|gemv|lmhead|lmhead_norm|verify|smallm|prefill|copy] [--m M]
 
 Default workload ("sweep"): the 27B-shaped decode weight sweep, 64 layers x
 (q, k, v, o 5120x5120; gate, up 17408x5120; down 5120x17408) = 448 Q4_0 GEMVs
@@ -15,7 +16,8 @@ on a bounded sample of the same workload on this host's cores).
 
 Other workloads print the same kind of line for the single 5120x5120 GEMV
 (rotating weight copies so the 256 MB last-level cache does not serve them),
-the LM head with argmax, small-M (--m) and prefill (--m) over the sweep.
+the LM head with argmax (with the final norm fused: lmhead_norm), the greedy
+verify of an M-row draft, small-M (--m) and prefill (--m) over the sweep.
 """
 from __future__ import annotations
 
@@ -43,7 +45,8 @@ def log(*a):
 
 # Kernel source of each workload's dominant kernel (besides the shared device
 # and launch headers, the host-side C ABI and the build script).
-KERNEL_SOURCE = {"sweep": ["gemv.hip"], "gemv": ["gemv.hip"], "lmhead": ["gemv.hip"], "smallm": ["smallm.hip"],
+KERNEL_SOURCE = {"sweep": ["gemv.hip"], "gemv": ["gemv.hip"], "lmhead": ["gemv.hip"], "lmhead_norm": ["gemv.hip"],
+                 "smallm": ["smallm.hip"],
                  "prefill": ["prefill.hip"], "verify": ["smallm.hip", "gemv.hip", "verify.hip"]}
 
 
@@ -171,14 +174,15 @@ def bench_sweep(args):
     batch = q4.GemvBatch(list(zip(ws, xs, ys)))
     ms = time_steps(batch, args.steps, args.warmup)
     gbs = SWEEP_BYTES / (ms * 1e-3) / 1e9
-    # LM head (151,936 x 5,120 + argmax) for the implied tokens/s
+    # the host's step after the sweep: final norm + LM head (151,936 x 5,120) + argmax, for the implied tokens/s
     import synth
-    wl = torch.from_numpy(synth.q4_0(SEED, synth.stream_id(2, 0, 0, synth.T_W), synth.VOCAB, synth.HIDDEN)).cuda()
-    hl = torch.from_numpy(synth.f16_normal(SEED, synth.stream_id(2, 0, 0, synth.T_X), synth.HIDDEN)).cuda()
+    wl, hl, gl = lmhead_inputs()
     lg = torch.empty(synth.VOCAB, dtype=torch.float32, device="cuda")
     tok = torch.empty(1, dtype=torch.int32, device="cuda")
-    wsp = torch.empty(q4.workspace_bytes(q4.Q4_OP_LM_HEAD_ARGMAX, 1, synth.VOCAB, synth.HIDDEN), dtype=torch.uint8, device="cuda")
-    lm_ms = time_steps(lambda: q4.lm_head_argmax(wl, hl, lg, tok, wsp), max(args.steps, 20), args.warmup)
+    wsp = torch.empty(q4.workspace_bytes(q4.Q4_OP_LM_HEAD_NORM_ARGMAX, 1, synth.VOCAB, synth.HIDDEN),
+                      dtype=torch.uint8, device="cuda")
+    lm_ms = time_steps(lambda: q4.lm_head_norm_argmax(wl, hl, gl, NORM_EPS, lg, tok, workspace=wsp),
+                       max(args.steps, 20), args.warmup)
     out = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -190,7 +194,7 @@ def bench_sweep(args):
                    "seed": SEED},
         "sweeps_per_s": round(1000.0 / ms, 2),
         "pct_of_8TBps": round(100.0 * gbs / PEAK_HBM_GBS, 2),
-        "lm_head_argmax_us": round(lm_ms * 1000.0, 2),
+        "lm_head_norm_argmax_us": round(lm_ms * 1000.0, 2),
         "implied_tok_s": round(1000.0 / (ms + lm_ms), 2),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4),
@@ -253,6 +257,57 @@ def bench_lmhead(args):
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counter_traffic("lmhead"),
                          "kernel": "q4::k_sweep<QuadEngine<12,2,2,288>,ARGMAX> + q4::k_argmax_final"}}
+
+
+NORM_EPS = 1e-6
+
+
+def lmhead_inputs():
+    """The LM head's weights (151,936 x 5,120), a hidden state (4 z, z ~ N(0,1)) and the final norm's gain."""
+    import torch
+    import synth
+    w = torch.from_numpy(synth.q4_0(SEED, synth.stream_id(2, 0, 0, synth.T_W), synth.VOCAB, synth.HIDDEN)).cuda()
+    h = torch.from_numpy(synth.f16_scaled_normal(SEED, synth.stream_id(2, 0, 0, synth.T_X), synth.HIDDEN, 4.0)).cuda()
+    g = torch.from_numpy(synth.norm_gain(SEED, synth.stream_id(2, 0, 1, synth.T_X), synth.HIDDEN)).cuda()
+    return w, h, g
+
+
+def bench_lmhead_norm(args):
+    """The final norm fused into the LM head (151,936 x 5,120) with the greedy
+    pick; the plain LM head on the same weights is timed beside it."""
+    import torch
+    import synth
+    q4 = load_q4()
+    n, k = synth.VOCAB, synth.HIDDEN
+    w, h, g = lmhead_inputs()
+    lg = torch.empty(n, dtype=torch.float32, device="cuda")
+    tok = torch.empty(1, dtype=torch.int32, device="cuda")
+    wsp = torch.empty(q4.workspace_bytes(q4.Q4_OP_LM_HEAD_NORM_ARGMAX, 1, n, k), dtype=torch.uint8, device="cuda")
+    steps = args.steps * 10
+    fused = lambda: q4.lm_head_norm_argmax(w, h, g, NORM_EPS, lg, tok, workspace=wsp)  # noqa: E731
+    plain = lambda: q4.lm_head_argmax(w, h, lg, tok, wsp)  # noqa: E731
+    # both warmed, then timed in alternating blocks (the first blocks after the
+    # inputs are written run slower, which would otherwise land on one side)
+    for f in (fused, plain):
+        time_steps(f, 1, args.warmup)
+    blocks = {"fused": [], "plain": []}
+    for r in range(4):
+        for name in (("fused", "plain") if r % 2 == 0 else ("plain", "fused")):
+            blocks[name].append(time_steps(fused if name == "fused" else plain, steps, 0))
+    ms = float(np.median(blocks["fused"]))
+    plain_ms = float(np.median(blocks["plain"]))
+    steps *= 4
+    bytes_ = n * k // 32 * 18 + 2 * k * 2 + n * 4 + 4
+    gbs = bytes_ / (ms * 1e-3) / 1e9
+    return {"metric": "final norm + LM head + greedy argmax HBM GB/s (151936x5120 Q4_0)", "value": round(gbs, 2),
+            "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16->f32",
+            "data": "synthetic", "config": {"workload": "RMS norm of h (k=5120) fused into LM head 151936x5120 + argmax"},
+            "tokens_per_s": round(1.0 / (ms * 1e-3), 1), "plain_lm_head_ms": round(plain_ms, 5),
+            "norm_overhead_us": round((ms - plain_ms) * 1000.0, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counter_traffic("lmhead_norm"),
+                         "kernel": "q4::k_sweep<QuadEngine<12,2,2,288>,ARGMAX,NORM> + q4::k_argmax_final"}}
 
 
 def bench_verify(args):
@@ -382,7 +437,7 @@ def main():
     # on the first one, settling within about ten launches of the sweep)
     ap.add_argument("--warmup", type=int, default=25)
     ap.add_argument("--workload", default="sweep",
-                    choices=["sweep", "gemv", "lmhead", "verify", "smallm", "prefill", "copy"])
+                    choices=["sweep", "gemv", "lmhead", "lmhead_norm", "verify", "smallm", "prefill", "copy"])
     ap.add_argument("--m", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--record-traffic", nargs=6, metavar=("WORKLOAD", "KERNEL", "FETCH_CSV", "WRITE_CSV",
@@ -399,7 +454,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    fn = {"sweep": bench_sweep, "gemv": bench_gemv, "lmhead": bench_lmhead, "verify": bench_verify, "copy": bench_copy,
+    fn = {"sweep": bench_sweep, "gemv": bench_gemv, "lmhead": bench_lmhead, "lmhead_norm": bench_lmhead_norm,
+          "verify": bench_verify, "copy": bench_copy,
           "smallm": lambda a: bench_gemm(a, False), "prefill": lambda a: bench_gemm(a, True)}[args.workload]
     out = fn(args)
     print(json.dumps(out), flush=True)

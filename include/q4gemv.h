@@ -65,6 +65,7 @@ typedef int q4_status;
 #define Q4_OP_GEMM_PREFILL 2
 #define Q4_OP_LM_HEAD_ARGMAX 3
 #define Q4_OP_LM_HEAD_VERIFY 4
+#define Q4_OP_LM_HEAD_NORM_ARGMAX 5
 
 /* Version of this interface (Q4_ABI_VERSION of the library that was built). */
 Q4_API int q4_abi_version(void);
@@ -146,12 +147,48 @@ Q4_API q4_status q4_0_gemm_prefill(const void* w, const void* x, float* y,
  *   logits : n_vocab binary32 values (written)
  *   token  : one int32 in device memory (written)
  *   workspace : q4_workspace_bytes(Q4_OP_LM_HEAD_ARGMAX, 1, n_vocab, k) bytes
- *               of device memory; its contents on entry do not matter.
- *   n_vocab >= 1, k >= 32, k % 32 == 0.  Inputs must be finite.
+ *               of device memory, 8-byte aligned; its contents on entry do not
+ *               matter.
+ *   n_vocab >= 1, k % 64 == 0, 64 <= k <= 32768, w 16-byte aligned (other k:
+ *   Q4_ERR_INVALID_ARG).  Inputs must be finite.
  */
 Q4_API q4_status lm_head_argmax(const void* w, const void* h, float* logits, int32_t* token,
                          int64_t n_vocab, int64_t k,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * x = final_norm(h);  logits[n] = sum_k w[n][k] * x[k];  token = lowest n
+ * with the largest logit
+ *
+ * The host normalises the hidden state the last stage returns, then applies
+ * the LM head and the greedy pick (originshq.com page, section "The
+ * Architecture: Layers Distributed, Activations in Flight"; taozi.news,
+ * section "技术架构").  The norm is read as RMS normalisation with a gain:
+ *   r = 1 / sqrt(mean over k of h[k]^2 + eps),  x[k] = binary16(h[k] r gamma[k])
+ * rounded to nearest, ties to even; the statistics are taken in binary32.  It
+ * runs inside the LM head's kernel (each workgroup normalises the 10 KB
+ * hidden state while staging it; there is no separate pass).  Each x[k] is
+ * the binary16 nearest to the binary64 value or, when that value lies within
+ * about 2^-20 of a rounding midpoint, its other neighbour; the logits then
+ * satisfy the bound of q4_0_gemv with x as the activation.
+ *   w      : n_vocab rows of k/32 Q4_0 blocks
+ *   h      : k binary16 values (the hidden state)
+ *   gamma  : k binary16 values (the norm's gain), 16-byte aligned
+ *   eps    : finite, > 0
+ *   logits : n_vocab binary32 values (written)
+ *   token  : one int32 in device memory (written)
+ *   x_out  : NULL, or k binary16 in device memory, 16-byte aligned, that
+ *            receive x (written)
+ *   workspace : q4_workspace_bytes(Q4_OP_LM_HEAD_NORM_ARGMAX, 1, n_vocab, k)
+ *               bytes of device memory, 8-byte aligned; contents on entry do
+ *               not matter.
+ *   n_vocab >= 1, k % 64 == 0, 64 <= k <= 32768, w 16-byte aligned.  Inputs
+ *   finite, and |h[k] r gamma[k]| below 65520 (else x[k] is infinite).  No
+ *   output may overlap another output or an input.
+ */
+Q4_API q4_status lm_head_norm_argmax(const void* w, const void* h, const void* gamma, float eps, float* logits,
+                                     int32_t* token, void* x_out, int64_t n_vocab, int64_t k,
+                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * logits[i][n] = sum_k w[n][k] * h[i][k];  tokens[i] = lowest n with the

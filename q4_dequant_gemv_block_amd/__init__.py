@@ -32,11 +32,13 @@ Q4_OP_GEMM_SMALLM = 1
 Q4_OP_GEMM_PREFILL = 2
 Q4_OP_LM_HEAD_ARGMAX = 3
 Q4_OP_LM_HEAD_VERIFY = 4
+Q4_OP_LM_HEAD_NORM_ARGMAX = 5
 
 # Every symbol include/q4gemv.h declares.
 EXPORTS = (
     "q4_abi_version", "q4_last_error", "q4_workspace_bytes", "q4_0_gemv", "q4_0_gemm_smallm",
-    "q4_0_gemm_prefill", "lm_head_argmax", "lm_head_verify", "q4_0_gemv_batch_plan_bytes", "q4_0_gemv_batch_plan",
+    "q4_0_gemm_prefill", "lm_head_argmax", "lm_head_norm_argmax", "lm_head_verify", "q4_0_gemv_batch_plan_bytes",
+    "q4_0_gemv_batch_plan",
     "q4_0_gemm_smallm_batch_plan_bytes", "q4_0_gemm_smallm_batch_plan", "q4_0_gemm_smallm_batch",
     "q4_0_gemm_prefill_batch_plan_bytes", "q4_0_gemm_prefill_batch_plan", "q4_0_gemm_prefill_batch",
     "q4_0_gemv_batch",
@@ -86,6 +88,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lm_head_argmax.restype = st
     lib.lm_head_argmax.argtypes = [vp, vp, vp, vp, i64, i64, vp, ctypes.c_size_t, vp]
     lib.lm_head_verify.restype = st
+    lib.lm_head_norm_argmax.argtypes = [vp, vp, vp, ctypes.c_float, vp, vp, vp, i64, i64, vp, ctypes.c_size_t, vp]
+    lib.lm_head_norm_argmax.restype = ctypes.c_int
     lib.lm_head_verify.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t, vp]
     lib.q4_0_gemv_batch_plan_bytes.restype = ctypes.c_size_t
     lib.q4_0_gemv_batch_plan_bytes.argtypes = [ctypes.POINTER(GemvDesc), ctypes.c_int]
@@ -238,6 +242,38 @@ def lm_head_argmax(w: torch.Tensor, h: torch.Tensor, logits: torch.Tensor | None
                                          _ptr(logits, torch.float32, "logits"), _ptr(token, torch.int32, "token"),
                                          n, k, _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
                                          _stream(stream)))
+    return logits, token
+
+
+def lm_head_norm_argmax(w: torch.Tensor, h: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,
+                        logits: torch.Tensor | None = None, token: torch.Tensor | None = None,
+                        x_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                        stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Final norm of h, then the LM head: (logits float32 [V], token int32 [1]) for W
+    (uint8 [V, K/32*18]), the hidden state h and the norm's gain gamma (float16 [K]).
+    x_out (float16 [K], optional) receives the normed activation."""
+    if h.dim() != 1 or gamma.dim() != 1 or gamma.shape[0] != h.shape[0]:
+        raise ValueError("h and gamma must be float16 [K]")
+    k = h.shape[0]
+    n = _weights(w, k)
+    if logits is None:
+        logits = torch.empty(n, dtype=torch.float32, device=h.device)
+    if token is None:
+        token = torch.empty(1, dtype=torch.int32, device=h.device)
+    need = workspace_bytes(Q4_OP_LM_HEAD_NORM_ARGMAX, 1, n, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=h.device)
+    xo = 0
+    if x_out is not None:
+        if x_out.dim() != 1 or x_out.shape[0] != k:
+            raise ValueError("x_out must be float16 [K]")
+        xo = _ptr(x_out, torch.float16, "x_out")
+    _check(load_library().lm_head_norm_argmax(_ptr(w, torch.uint8, "w"), _ptr(h, torch.float16, "h"),
+                                              _ptr(gamma, torch.float16, "gamma"), float(eps),
+                                              _ptr(logits, torch.float32, "logits"),
+                                              _ptr(token, torch.int32, "token"), xo, n, k,
+                                              _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                              _stream(stream)))
     return logits, token
 
 

@@ -96,6 +96,7 @@ size_t q4_workspace_bytes(int op, int64_t m, int64_t n, int64_t k) {
             // (with w not 4-byte aligned the call takes the generic kernel and ignores the workspace)
             return q4::smallm_workspace_bytes(m, n, k);
         case Q4_OP_LM_HEAD_ARGMAX:
+        case Q4_OP_LM_HEAD_NORM_ARGMAX:
             if (n < 1 || k < 32) return 0;
             return (size_t)q4::argmax_blocks(n, k) * sizeof(uint64_t);
         case Q4_OP_LM_HEAD_VERIFY:
@@ -194,6 +195,43 @@ q4_status lm_head_argmax(const void* w, const void* h, float* logits, int32_t* t
                                             token, n_vocab, k, static_cast<uint64_t*>(workspace),
                                             static_cast<hipStream_t>(stream));
     return hip_status(e, "lm_head_argmax launch");
+}
+
+q4_status lm_head_norm_argmax(const void* w, const void* h, const void* gamma, float eps, float* logits,
+                              int32_t* token, void* x_out, int64_t n_vocab, int64_t k, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    const char* fn = "lm_head_norm_argmax";
+    q4_status st = check_shape(fn, 1, 1, n_vocab, k);
+    if (st) return st;
+    st = check_tensors(fn, w, h, logits, 1, n_vocab, k, (size_t)n_vocab * 4);
+    if (st) return st;
+    if (!token || !gamma) return fail(Q4_ERR_INVALID_ARG, "%s: null token or gamma pointer", fn);
+    if (!aligned(token, 4)) return fail(Q4_ERR_MISALIGNED, "%s: token must be 4-byte aligned", fn);
+    if (!aligned(gamma, 16)) return fail(Q4_ERR_MISALIGNED, "%s: gamma must be 16-byte aligned", fn);
+    if (x_out && !aligned(x_out, 16)) return fail(Q4_ERR_MISALIGNED, "%s: x_out must be 16-byte aligned", fn);
+    if (!(eps > 0.0f) || !(eps <= 3.4e38f)) return fail(Q4_ERR_INVALID_ARG, "%s: eps must be finite and > 0", fn);
+    if (!fast_path(w, k))
+        return fail(Q4_ERR_INVALID_ARG, "%s: needs k %% 64 == 0 and k <= %lld", fn, (long long)q4::kFastMaxK);
+    const size_t need = q4_workspace_bytes(Q4_OP_LM_HEAD_NORM_ARGMAX, 1, n_vocab, k);
+    if (!workspace || workspace_bytes < need) return fail(Q4_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
+    if (!aligned(workspace, 8)) return fail(Q4_ERR_MISALIGNED, "%s: workspace must be 8-byte aligned", fn);
+    const Range rw = range(w, (size_t)(n_vocab * row_bytes(k))), rh = range(h, (size_t)k * 2),
+                rg = range(gamma, (size_t)k * 2);
+    const Range outs[4] = {range(logits, (size_t)n_vocab * 4), range(token, 4), range(workspace, need),
+                           x_out ? range(x_out, (size_t)k * 2) : Range{0, 0}};
+    for (int i = 0; i < 4; ++i) {
+        if (outs[i].lo == outs[i].hi) continue;
+        if (overlap(outs[i], rw) || overlap(outs[i], rh) || overlap(outs[i], rg))
+            return fail(Q4_ERR_INVALID_ARG, "%s: an output or the workspace overlaps an input", fn);
+        for (int j = i + 1; j < 4; ++j)
+            if (outs[j].lo != outs[j].hi && overlap(outs[i], outs[j]))
+                return fail(Q4_ERR_INVALID_ARG, "%s: outputs and workspace must not overlap", fn);
+    }
+    const hipError_t e = q4::launch_lm_head_norm(
+        static_cast<const uint8_t*>(w), static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(gamma), eps,
+        static_cast<uint16_t*>(x_out), logits, token, n_vocab, k, static_cast<uint64_t*>(workspace),
+        static_cast<hipStream_t>(stream));
+    return hip_status(e, "lm_head_norm_argmax launch");
 }
 
 q4_status lm_head_verify(const void* w, const void* h, float* logits, int32_t* tokens, const int32_t* draft,

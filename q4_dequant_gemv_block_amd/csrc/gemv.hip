@@ -133,6 +133,118 @@ __device__ void stage_x(const uint16_t* __restrict__ x, int nblocks, int npairs_
     }
 }
 
+// The final norm before the LM head, applied while the activations are staged
+// (the host normalises the hidden state the last stage returns before the LM
+// head: "Every Device Brings a Slice", originshq.com, section "The
+// Architecture: Layers Distributed, Activations in Flight").  Read as RMS
+// normalisation with a per-element gain g: r = 1/sqrt(mean(h^2) + eps),
+// x_i = binary16(h_i r g_i), nearest-even.  Every workgroup reads the k values
+// of h (L2-resident after the first) and reduces their squares in one fixed
+// order (thread t takes blocks t, t + blockDim, ...; butterfly within the
+// wave; the waves' partials summed in wave order), so all workgroups stage the
+// same x; workgroup 0 also writes x to x_out when that is set.
+struct NormArgs {
+    const uint16_t* gamma;  // g [k], binary16; unused without the norm
+    uint16_t* x_out;        // x [k], binary16, or null
+    float eps;
+};
+
+__device__ __forceinline__ float half_lo(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu)); }
+__device__ __forceinline__ float half_hi(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); }
+__device__ __forceinline__ uint32_t half_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+// Block threadIdx.x of h and of g, loaded once: the sum of squares and the
+// scaling both read them from registers.
+struct NormHeld {
+    uint32_t h[16], g[16];
+};
+
+__device__ __forceinline__ void load_block16(const uint16_t* __restrict__ p, int64_t b, uint32_t (&v)[16]) {
+    g_u4* src = (g_u4*)(p + 32 * b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const u4 t = src[i];
+        v[4 * i + 0] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+    }
+}
+
+__device__ __forceinline__ void norm_prefetch(const uint16_t* __restrict__ h, const NormArgs& nm, int k,
+                                              NormHeld& held) {
+    if ((int)threadIdx.x < (k >> 5)) {
+        load_block16(h, threadIdx.x, held.h);
+        load_block16(nm.gamma, threadIdx.x, held.g);
+    }
+}
+
+__device__ __forceinline__ float sum_squares16(const uint32_t (&v)[16], float ss) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const float lo = half_lo(v[j]), hi = half_hi(v[j]);
+        ss = __builtin_fmaf(lo, lo, ss);
+        ss = __builtin_fmaf(hi, hi, ss);
+    }
+    return ss;
+}
+
+// The caller has synchronised the workgroup: xs holds nothing still to be read.
+template <int WAVES>
+__device__ void stage_x_norm(const uint16_t* __restrict__ h, const NormArgs& nm, const NormHeld& held, int k,
+                             int npairs_pad, int stride, u4* __restrict__ xs) {
+    const int nblocks = k >> 5;
+    float ss = 0.0f;
+    if ((int)threadIdx.x < nblocks) ss = sum_squares16(held.h, ss);
+    for (int b = threadIdx.x + blockDim.x; b < nblocks; b += blockDim.x) {  // k beyond 32 values per thread
+        uint32_t v[16];
+        load_block16(h, b, v);
+        ss = sum_squares16(v, ss);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    float* part = reinterpret_cast<float*>(xs);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float tot = 0.0f;
+#pragma unroll
+    for (int wv = 0; wv < WAVES; ++wv) tot += part[wv];
+    __syncthreads();  // every wave has its total before xs is overwritten
+    const float r = 1.0f / __builtin_sqrtf(tot / (float)k + nm.eps);
+    const bool write_out = nm.x_out != nullptr && blockIdx.x == 0;
+
+    const int nb_pad = 2 * npairs_pad;
+    for (int b = threadIdx.x; b < nb_pad; b += blockDim.x) {
+        uint32_t v[16];  // the 32 binary16 values of x in block b, two per dword
+        if (b < nblocks) {
+            uint32_t hv[16], gv[16];
+            if (b == (int)threadIdx.x) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    hv[j] = held.h[j];
+                    gv[j] = held.g[j];
+                }
+            } else {
+                load_block16(h, b, hv);
+                load_block16(nm.gamma, b, gv);
+            }
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                v[j] = half_bits(half_lo(hv[j]) * r * half_lo(gv[j])) |
+                       (half_bits(half_hi(hv[j]) * r * half_hi(gv[j])) << 16);
+            if (write_out) {
+                u4* dst = reinterpret_cast<u4*>(nm.x_out + 32 * (int64_t)b);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[i] = u4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] = 0u;
+        }
+        if (b & 1)
+            stage_block<1>(v, b >> 1, stride, xs);
+        else
+            stage_block<0>(v, b >> 1, stride, xs);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // GEMV engines.  Both keep one contract with the sweep kernel below: a row
 // step of a GEMV gives every wave kRowsPerWave consecutive rows, which the
@@ -585,10 +697,10 @@ __device__ __forceinline__ Live live_of(const PlanDesc& p) {
 // the barriers of chunk changes and activation staging are reached by all.
 // The NB-slot ring of each wave: the slot of the unit being computed is
 // refilled once its pairs are read, so NB units are in flight during the math.
-template <class E, int XS, bool BATCH, bool ARGMAX>
+template <class E, int XS, bool BATCH, bool ARGMAX, bool NORM>
 __global__ void __launch_bounds__(E::kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
 k_sweep(const PlanDesc* __restrict__ descs, int count, SchedHead* head, const SchedChunk* __restrict__ chunks,
-        PlanDesc one, int xs_bytes, uint64_t* __restrict__ keys) {
+        PlanDesc one, int xs_bytes, uint64_t* __restrict__ keys, NormArgs nrm) {
     constexpr int NB = E::kNB;
     extern __shared__ u4 xs[];
     __shared__ int q_next[2];  // ids of this workgroup's coming chunks (batch schedule)
@@ -710,7 +822,7 @@ k_sweep(const PlanDesc* __restrict__ descs, int count, SchedHead* head, const Sc
                 Dc = get(u.d);
                 dc = u.d;
             }
-            if (u.d != staged) {
+            if (!NORM && u.d != staged) {  // (with the norm, staged before the first step)
                 __syncthreads();
                 stage_x(Dc.x, Dc.k >> 5, Dc.npl * 16, XS > 0 ? XS : Dc.npl * 16, xs);
                 __syncthreads();
@@ -744,6 +856,15 @@ k_sweep(const PlanDesc* __restrict__ descs, int count, SchedHead* head, const Sc
                 issue_next(RR[i], i);
             else
                 RR[i].d = -1;
+        }
+        if constexpr (NORM) {
+            // h and g are loaded behind the first weight units, so their wait
+            // overlaps the one the first step makes anyway; then the norm is
+            // staged once for the whole launch.
+            NormHeld held;
+            norm_prefetch(one.x, nrm, one.k, held);
+            stage_x_norm<E::kWaves>(one.x, nrm, held, one.k, one.npl * 16, XS > 0 ? XS : one.npl * 16, xs);
+            __syncthreads();
         }
         bool go = true;
         while (go) {
@@ -868,52 +989,55 @@ static PlanDesc single_desc(const uint8_t* w, const uint16_t* x, float* y, int64
 
 static bool quad_ok(int64_t k) { return k % 1024 == 0 && k >= 4096; }
 
-template <class E, int XS, bool BATCH, bool AM>
+template <class E, int XS, bool BATCH, bool AM, bool NORM>
 static hipError_t launch_sweep(const PlanDesc* descs, int count, SchedHead* head, const SchedChunk* chunks,
-                               const PlanDesc& one, int64_t max_k, int grid, uint64_t* keys, hipStream_t s) {
+                               const PlanDesc& one, int64_t max_k, int grid, uint64_t* keys, const NormArgs& nrm,
+                               hipStream_t s) {
     const size_t xsb = x_lds_bytes(max_k);
     const size_t lds = xsb + (size_t)E::kWaves * E::kWaveLds;
-    auto kern = k_sweep<E, XS, BATCH, AM>;
+    auto kern = k_sweep<E, XS, BATCH, AM, NORM>;
     if (lds > 65536) {
         const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3(grid), dim3(E::kWaves * 64), lds, s, descs, count, head, chunks, one, (int)xsb,
-                       keys);
+                       keys, nrm);
     return hipGetLastError();
 }
 
 // The kernel of a shape, for the activation stride max_k needs.
-template <class E, class EV, bool BATCH, bool AM>
+template <class E, class EV, bool BATCH, bool AM, bool NORM>
 static hipError_t launch_stride(const PlanDesc* descs, int count, SchedHead* head, const SchedChunk* chunks,
-                                const PlanDesc& one, int64_t max_k, int grid, uint64_t* keys, hipStream_t s) {
+                                const PlanDesc& one, int64_t max_k, int grid, uint64_t* keys, const NormArgs& nrm,
+                                hipStream_t s) {
     return fixed_stride(max_k)
-               ? launch_sweep<E, kXStride, BATCH, AM>(descs, count, head, chunks, one, max_k, grid, keys, s)
-               : launch_sweep<EV, 0, BATCH, AM>(descs, count, head, chunks, one, max_k, grid, keys, s);
+               ? launch_sweep<E, kXStride, BATCH, AM, NORM>(descs, count, head, chunks, one, max_k, grid, keys, nrm, s)
+               : launch_sweep<EV, 0, BATCH, AM, NORM>(descs, count, head, chunks, one, max_k, grid, keys, nrm, s);
 }
 
 // A batch (descs, head, chunks) runs on a wide shape; a single GEMV passes
 // its descriptor in `one`.
-template <bool BATCH, bool AM>
+template <bool BATCH, bool AM, bool NORM = false>
 static hipError_t launch_any(const Shape& sh, const PlanDesc* descs, int count, SchedHead* head,
                              const SchedChunk* chunks, const PlanDesc& one, int64_t max_k, int grid, uint64_t* keys,
-                             hipStream_t s) {
+                             hipStream_t s, const NormArgs& nrm = NormArgs{nullptr, nullptr, 0.0f}) {
     constexpr int W = kWide.waves, WN = kNarrow.waves, R = kWide.r;
+    static_assert(!(BATCH && NORM), "the norm prologue belongs to a single LM head");
     if constexpr (!BATCH) {
         if (sh.waves == WN && sh.quad)
-            return launch_stride<QuadEngine<WN, 1, 4, kXStride>, QuadEngine<WN, 1, 4, 0>, BATCH, AM>(
-                descs, count, head, chunks, one, max_k, grid, keys, s);
+            return launch_stride<QuadEngine<WN, 1, 4, kXStride>, QuadEngine<WN, 1, 4, 0>, BATCH, AM, NORM>(
+                descs, count, head, chunks, one, max_k, grid, keys, nrm, s);
         if (sh.waves == WN)
-            return launch_stride<DmaEngine<WN, kNarrow.r, kXStride>, DmaEngine<WN, kNarrow.r, 0>, BATCH, AM>(
-                descs, count, head, chunks, one, max_k, grid, keys, s);
+            return launch_stride<DmaEngine<WN, kNarrow.r, kXStride>, DmaEngine<WN, kNarrow.r, 0>, BATCH, AM, NORM>(
+                descs, count, head, chunks, one, max_k, grid, keys, nrm, s);
     }
     if (sh.quad)
         return launch_stride<QuadEngine<kQuadWide.waves, kQuadWide.r, kQuadNB, kXStride>,
                              QuadEngine<kQuadWide.waves, kQuadWide.r, kQuadNB, 0>,
-                             BATCH, AM>(
-            descs, count, head, chunks, one, max_k, grid, keys, s);
-    return launch_stride<DmaEngine<W, R, kXStride>, DmaEngine<W, R, 0>, BATCH, AM>(descs, count, head, chunks, one,
-                                                                                  max_k, grid, keys, s);
+                             BATCH, AM, NORM>(
+            descs, count, head, chunks, one, max_k, grid, keys, nrm, s);
+    return launch_stride<DmaEngine<W, R, kXStride>, DmaEngine<W, R, 0>, BATCH, AM, NORM>(
+        descs, count, head, chunks, one, max_k, grid, keys, nrm, s);
 }
 
 // Workgroups for a static split of `steps` row steps.
@@ -951,6 +1075,19 @@ hipError_t launch_lm_head(const uint8_t* w, const uint16_t* h, float* logits, in
     const PlanDesc d = single_desc(w, h, logits, n, k, sh);
     const int grid = argmax_blocks(n, k);
     hipError_t e = launch_any<false, true>(sh, nullptr, 1, nullptr, nullptr, d, k, grid, keys, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_argmax_final, dim3(1), dim3(kFinalThreads), 0, s, keys, grid, token);
+    return hipGetLastError();
+}
+
+hipError_t launch_lm_head_norm(const uint8_t* w, const uint16_t* h, const uint16_t* gamma, float eps,
+                               uint16_t* x_out, float* logits, int32_t* token, int64_t n, int64_t k, uint64_t* keys,
+                               hipStream_t s) {
+    const Shape& sh = single_shape(n, k);
+    const PlanDesc d = single_desc(w, h, logits, n, k, sh);
+    const int grid = argmax_blocks(n, k);
+    hipError_t e = launch_any<false, true, true>(sh, nullptr, 1, nullptr, nullptr, d, k, grid, keys, s,
+                                                 NormArgs{gamma, x_out, eps});
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_argmax_final, dim3(1), dim3(kFinalThreads), 0, s, keys, grid, token);
     return hipGetLastError();

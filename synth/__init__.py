@@ -136,6 +136,18 @@ def f16_normal(seed: int, stream: int, count: int, begin: int = 0) -> np.ndarray
     return out.view(np.float16)
 
 
+def f16_scaled_normal(seed: int, stream: int, count: int, scale: float, begin: int = 0) -> np.ndarray:
+    """count values scale * z rounded to f16 (z the f16 N(0,1) stream), as numpy float16."""
+    z = f16_normal(seed, stream, count, begin).astype(np.float64)
+    return f64_to_f16_bits(scale * z).view(np.float16)
+
+
+def norm_gain(seed: int, stream: int, count: int) -> np.ndarray:
+    """count gains of a final norm, 1 + 0.25 z rounded to f16 (z the f16 N(0,1) stream)."""
+    z = f16_normal(seed, stream, count).astype(np.float64)
+    return f64_to_f16_bits(1.0 + 0.25 * z).view(np.float16)
+
+
 def decode_sweep():
     """The 448 (layer, proj, N, K) GEMVs of one 64-layer weight sweep, in order."""
     return [(l, p, n, k) for l in range(LAYERS) for p, (_, n, k) in enumerate(PROJ)]

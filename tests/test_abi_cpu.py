@@ -159,6 +159,39 @@ def test_lm_head_validation(lib):
     assert lib.lm_head_argmax(w, h, lg, tok, 1000, 96, FAKE * 16, need, None) == q4.Q4_ERR_INVALID_ARG
 
 
+def test_lm_head_norm_validation(lib):
+    w, h, g, lg, tok, xo, ws = FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 8, FAKE * 9, FAKE * 16
+    n, k = 1000, 64
+    need = lib.q4_workspace_bytes(q4.Q4_OP_LM_HEAD_NORM_ARGMAX, 1, n, k)
+    assert need == lib.q4_workspace_bytes(q4.Q4_OP_LM_HEAD_ARGMAX, 1, n, k) > 0
+
+    def call(w=w, h=h, g=g, eps=1e-6, lg=lg, tok=tok, xo=xo, n=n, k=k, ws=ws, nb=need):
+        return lib.lm_head_norm_argmax(w, h, g, eps, lg, tok, xo, n, k, ws, nb, None)
+
+    assert call(ws=None, nb=0) == q4.Q4_ERR_WORKSPACE
+    assert call(nb=need - 8) == q4.Q4_ERR_WORKSPACE
+    assert call(ws=ws + 4) == q4.Q4_ERR_MISALIGNED
+    assert call(g=None) == q4.Q4_ERR_INVALID_ARG
+    assert call(tok=None) == q4.Q4_ERR_INVALID_ARG
+    assert call(g=g + 2) == q4.Q4_ERR_MISALIGNED
+    assert call(xo=xo + 2) == q4.Q4_ERR_MISALIGNED
+    assert call(tok=tok + 2) == q4.Q4_ERR_MISALIGNED
+    for bad in (0.0, -1e-6, float("inf"), float("nan")):
+        assert call(eps=bad) == q4.Q4_ERR_INVALID_ARG, bad
+    assert b"eps" in lib.q4_last_error()
+    # x_out over the logits, over gamma, over the token; workspace over gamma; token in the logits
+    assert call(xo=lg + 16) == q4.Q4_ERR_INVALID_ARG
+    assert call(xo=g) == q4.Q4_ERR_INVALID_ARG
+    assert call(tok=xo + 4) == q4.Q4_ERR_INVALID_ARG
+    assert call(ws=g) == q4.Q4_ERR_INVALID_ARG
+    assert call(tok=lg + 8) == q4.Q4_ERR_INVALID_ARG
+    # logits over h
+    assert call(lg=h) == q4.Q4_ERR_INVALID_ARG
+    # k % 64 != 0 is not supported here; k not a multiple of 32 at all
+    assert call(k=96) == q4.Q4_ERR_INVALID_ARG
+    assert call(k=80) == q4.Q4_ERR_INVALID_ARG
+
+
 def test_verify_validation(lib):
     w, h, lg = FAKE * 64, FAKE * 4096, FAKE * 8192
     tok, dr, acc, ws = FAKE * 12288, FAKE * 12289, FAKE * 12290, FAKE * 16384
