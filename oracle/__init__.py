@@ -60,6 +60,7 @@ class Oracle:
         lib.q4o_f64_to_f16.restype = ctypes.c_uint16
         lib.q4o_f64_to_f16_array.argtypes = [vp, i64, vp]
         lib.q4o_rms_norm.argtypes = [vp, vp, i64, ctypes.c_double, vp, vp]
+        lib.q4o_gemv_handoff.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
         self.lib = lib
         self.path = path
 
@@ -144,14 +145,30 @@ class Oracle:
         y, a = self.gemm_rows(w_rows, k, x)
         return y, a, self.argmax(y), x
 
+    def gemv_handoff(self, w_rows: np.ndarray, k: int, x, residual=None):
+        """The stage hand-off: (h16, y, a) for packed rows [n], f16 x [K] and an optional
+        float32 residual [n]: y, a as gemm_rows, h16 = binary16 bits of residual + y."""
+        w = _u8(w_rows).reshape(-1, k // 32 * 18)
+        xb = np.ascontiguousarray(_f16bits(np.asarray(x)).ravel())
+        assert xb.size == k
+        n = w.shape[0]
+        r = None
+        if residual is not None:
+            r = np.ascontiguousarray(np.asarray(residual, dtype=np.float32).ravel())
+            assert r.size == n
+        h16 = np.empty(n, dtype=np.uint16)
+        y = np.empty(n, dtype=np.float64)
+        a = np.empty(n, dtype=np.float64)
+        self.lib.q4o_gemv_handoff(w.ctypes.data, n, k, xb.ctypes.data, None if r is None else r.ctypes.data,
+                                  h16.ctypes.data, y.ctypes.data, a.ctypes.data)
+        return h16, y, a
+
 
 def default() -> Oracle:
     global _default
     with _lock:
         if _default is None:
-            if not os.path.exists(_LIB):
-                build()
-            _default = Oracle(_LIB)
+            _default = Oracle(build())  # rebuilt when the source is newer than the library
     return _default
 
 
@@ -189,6 +206,10 @@ def rms_norm(h, g, eps: float):
 
 def lm_head_norm(w_rows: np.ndarray, k: int, h, g, eps: float):
     return default().lm_head_norm(w_rows, k, h, g, eps)
+
+
+def gemv_handoff(w_rows: np.ndarray, k: int, x, residual=None):
+    return default().gemv_handoff(w_rows, k, x, residual)
 
 
 def _u8(a) -> np.ndarray:

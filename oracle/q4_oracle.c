@@ -41,6 +41,14 @@
  *   v_i = h_i * g_i * r                       (binary64)
  *   x_i = v_i rounded to binary16, nearest, ties to even
  * and x is the activation the LM head multiplies.
+ * The hand-off at the end of a stage's layer range (each device converts the
+ * hidden state it produced to f16 and sends it to the next participant:
+ * aipolix.com en-us page, section "A model can be larger than any one browser
+ * can hold"; its pt-pt page, section "O modelo pode ser maior do que a
+ * memória de cada dispositivo").  Read as the epilogue of the range's last
+ * GEMV with the residual stream added first:
+ *   h16[n] = binary16 rounding (nearest, ties to even) of r[n] + y[n]
+ * with y[n] the binary64 sum above and r an optional binary32 residual.
  * Parallelism: OpenMP over independent outputs only; each sum is sequential.
  */
 #include <math.h>
@@ -171,4 +179,13 @@ void q4o_rms_norm(const uint16_t* h, const uint16_t* g, int64_t k, double eps, d
         if (v) v[i] = vi;
         x[i] = q4o_f64_to_f16(vi);
     }
+}
+
+/* The stage hand-off: out16[n] = binary16(r[n] + y[n]) for one activation x
+ * (binary16 [K]) and rows w_rows [nrows]; r (binary32 [nrows]) may be NULL
+ * (zero); y and a (binary64 [nrows], a may be NULL) as q4o_gemm_rows. */
+void q4o_gemv_handoff(const uint8_t* w_rows, int64_t nrows, int64_t k, const uint16_t* x, const float* r,
+                      uint16_t* out16, double* y, double* a) {
+    q4o_gemm_rows(w_rows, nrows, k, x, 1, y, a);
+    for (int64_t n = 0; n < nrows; ++n) out16[n] = q4o_f64_to_f16((r ? (double)r[n] : 0.0) + y[n]);
 }

@@ -31,6 +31,11 @@ instance disagrees with a fact fixed by the pages' reading or by mathematics:
                     numpy sqrt, numpy float16 rounding), lengths 1 to 5120
   lm_head_norm_brute final norm then LM head on tiny shapes: token = numpy.argmax
                     of the dense product with numpy's normed activation
+  handoff_exact     the stage hand-off with d = 1, integer x and an integer
+                    residual: h16 = the exact integer (|value| <= 2048 is exact
+                    in binary16), and large sums round to even
+  handoff_brute     tiny shapes: h16 = numpy float16 of the numpy float64 dense
+                    product plus the float32 residual
 
 ``tests/test_oracle_pins.py`` runs them on the oracle; ``tests/test_oracle_mutants.py``
 plants plausible mistakes into copies of the oracle's source and checks that
@@ -263,9 +268,45 @@ def lm_head_norm_brute(o):
         assert token == int(np.argmax(y_np)), (n, k)
 
 
+def handoff_exact(o):
+    rng = np.random.default_rng(41)
+    for n, k in ((7, 32), (33, 96)):
+        codes = rng.integers(0, 16, size=(n, k))
+        w = q4_encode.encode(codes, np.full((n, k // 32), 0x3C00, dtype=np.uint16))  # d = 1
+        x = rng.integers(-3, 4, size=k).astype(np.float16)
+        exact = (codes - 8) @ x.astype(np.int64)
+        res = rng.integers(-500, 500, size=n).astype(np.float32)
+        h16, y, a = o.gemv_handoff(w, k, x, res)
+        assert np.array_equal(y, exact.astype(np.float64)), (n, k)
+        want = exact + res.astype(np.int64)
+        assert np.all(np.abs(want) <= 2048)
+        assert np.array_equal(h16.view(np.float16).astype(np.float64), want.astype(np.float64)), (n, k)
+        h0, _, _ = o.gemv_handoff(w, k, x)
+        assert np.array_equal(h0.view(np.float16).astype(np.float64), exact.astype(np.float64)), (n, k)
+    # one row, K = 32, every code 15 (weight 7), d = 1, x = 1: y = 224; residual 2048 - 224 + 1 -> 2049,
+    # a tie between 2048 and 2050 in binary16 (spacing 2 above 2048): even mantissa -> 2048
+    w = q4_encode.encode(np.full((1, 32), 15), np.full((1, 1), 0x3C00, dtype=np.uint16))
+    h16, y, _ = o.gemv_handoff(w, 32, np.ones(32, dtype=np.float16), np.array([1825.0], dtype=np.float32))
+    assert y[0] == 224.0 and h16.view(np.float16)[0] == 2048.0
+    h16, _, _ = o.gemv_handoff(w, 32, np.ones(32, dtype=np.float16), np.array([1827.0], dtype=np.float32))
+    assert h16.view(np.float16)[0] == 2052.0  # 2051: tie between 2050 and 2052 -> 2052 (even)
+
+
+def handoff_brute(o):
+    rng = np.random.default_rng(43)
+    for n, k in ((5, 32), (40, 64), (70, 128)):
+        codes, d, w = q4_encode.random_case(rng, n, k, signed_d=True)
+        dense = q4_encode.weights_from_numbers(codes, d)
+        x = rng.standard_normal(k).astype(np.float16)
+        res = (3.0 * rng.standard_normal(n)).astype(np.float32)
+        want = (dense @ x.astype(np.float64) + res.astype(np.float64)).astype(np.float16)
+        h16, y, a = o.gemv_handoff(w, k, x, res)
+        assert np.array_equal(h16, want.view(np.uint16)), (n, k)
+
+
 ALL = [golden_blocks, f16_exhaustive, basis_columns, all_ones, integer_exact,
        brute_force, multi_row_layout, argmax_golden, argmax_invariants, verify_prefix, verify_brute,
-       f16_round, norm_golden, norm_closed_forms, norm_brute, lm_head_norm_brute]
+       f16_round, norm_golden, norm_closed_forms, norm_brute, lm_head_norm_brute, handoff_exact, handoff_brute]
 
 
 def failures(o):

@@ -42,6 +42,11 @@ MUTANTS = {
     "f16_subnormal_quantum": ("if (E < -14) E = -14;", "if (E < -15) E = -15;"),
     "f16_carry_lost": ("q = 1024.0;\n        E += 1;", "q = 2047.0;"),
     "f16_sign_dropped": ("const uint16_t sign = signbit(v) ? 0x8000 : 0;", "const uint16_t sign = 0;"),
+    "handoff_residual_dropped": ("q4o_f64_to_f16((r ? (double)r[n] : 0.0) + y[n])", "q4o_f64_to_f16(y[n])"),
+    "handoff_residual_subtracted": ("q4o_f64_to_f16((r ? (double)r[n] : 0.0) + y[n])",
+                                    "q4o_f64_to_f16(y[n] - (r ? (double)r[n] : 0.0))"),
+    "handoff_rounded_before_residual": ("q4o_f64_to_f16((r ? (double)r[n] : 0.0) + y[n])",
+                                        "q4o_f64_to_f16((r ? (double)r[n] : 0.0) + q4o_f16_to_f64(q4o_f64_to_f16(y[n])))"),
     "prefix_past_mismatch": ("while (i < m && tokens[i] == draft[i]) ++i;",
                              "while (i < m && tokens[i] == draft[i]) ++i;\n    if (i < m) ++i;"),
 }
