@@ -1,7 +1,7 @@
 """Benchmark of the Q4_0 dequantize-and-multiply path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload sweep|gemv|lmhead|lmhead_norm|verify|smallm|prefill|copy] [--m M]
+                    [--workload sweep|gemv|lmhead|lmhead_norm|handoff|verify|smallm|prefill|copy] [--m M]
 
 Default workload ("sweep"): the 27B-shaped decode weight sweep, 64 layers x
 (q, k, v, o 5120x5120; gate, up 17408x5120; down 5120x17408) = 448 Q4_0 GEMVs
@@ -16,7 +16,8 @@ on a bounded sample of the same workload on this host's cores).
 
 Other workloads print the same kind of line for the single 5120x5120 GEMV
 (rotating weight copies so the 256 MB last-level cache does not serve them),
-the LM head with argmax (with the final norm fused: lmhead_norm), the greedy
+the LM head with argmax (with the final norm fused: lmhead_norm), the stage
+hand-off GEMV with its binary16 epilogue (handoff), the greedy
 verify of an M-row draft, small-M (--m) and prefill (--m) over the sweep.
 """
 from __future__ import annotations
@@ -46,6 +47,7 @@ def log(*a):
 # Kernel source of each workload's dominant kernel (besides the shared device
 # and launch headers, the host-side C ABI and the build script).
 KERNEL_SOURCE = {"sweep": ["gemv.hip"], "gemv": ["gemv.hip"], "lmhead": ["gemv.hip"], "lmhead_norm": ["gemv.hip"],
+                 "handoff": ["gemv.hip"],
                  "smallm": ["smallm.hip"],
                  "prefill": ["prefill.hip"], "verify": ["smallm.hip", "gemv.hip", "verify.hip"]}
 
@@ -235,6 +237,53 @@ def bench_gemv(args):
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counter_traffic("gemv"),
                          "kernel": "q4::k_sweep<QuadEngine<4,1,4,288>>"}}
+
+
+def bench_handoff(args):
+    """The stage hand-off: the range's last GEMV (down projection, 5,120 x 17,408)
+    with the binary16 epilogue (residual + y), cycling through weight copies so
+    the last-level cache does not serve them; the plain f32 GEMV timed beside it."""
+    import torch
+    import synth
+    q4 = load_q4()
+    n, k = synth.HIDDEN, synth.FFN
+    copies = 16  # 16 x 50 MB > 256 MB
+    w0 = synth.q4_0(SEED, synth.stream_id(1, 63, 6, synth.T_W), n, k)
+    ws = [torch.from_numpy(w0).cuda() for _ in range(copies)]
+    x = torch.from_numpy(synth.f16_normal(SEED, synth.stream_id(5, 63, 6, synth.T_X), k)).cuda()
+    r = torch.from_numpy(4.0 * synth.f16_normal(SEED, synth.stream_id(5, 63, 6, synth.T_R), n).astype(np.float32)).cuda()
+    h16 = torch.empty(n, dtype=torch.float16, device="cuda")
+    y = torch.empty(n, dtype=torch.float32, device="cuda")
+    it = [0]
+
+    def handoff():
+        q4.q4_0_gemv_handoff(ws[it[0] % copies], x, r, h16)
+        it[0] += 1
+
+    def plain():
+        q4.q4_0_gemv(ws[it[0] % copies], x, y)
+        it[0] += 1
+    steps = max(args.steps, 1) * copies
+    for f in (handoff, plain):
+        time_steps(f, 1, args.warmup * copies)
+    blocks = {"handoff": [], "plain": []}
+    for rr in range(4):
+        for name in (("handoff", "plain") if rr % 2 == 0 else ("plain", "handoff")):
+            blocks[name].append(time_steps(handoff if name == "handoff" else plain, steps, 0))
+    ms = float(np.median(blocks["handoff"]))
+    plain_ms = float(np.median(blocks["plain"]))
+    bytes_ = n * k // 32 * 18 + k * 2 + n * 4 + n * 2
+    gbs = bytes_ / (ms * 1e-3) / 1e9
+    return {"metric": "stage hand-off GEMV HBM GB/s (5120x17408 Q4_0, binary16 residual + y epilogue)",
+            "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": 4 * steps, "warmup": args.warmup,
+            "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f16->f32->f16", "data": "synthetic",
+            "config": {"workload": "down projection 5120x17408 + residual, binary16 hand-off, %d rotating weight copies"
+                                   % copies},
+            "plain_f32_gemv_ms": round(plain_ms, 5), "epilogue_overhead_us": round((ms - plain_ms) * 1000.0, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counter_traffic("handoff"),
+                         "kernel": "q4::k_sweep<QuadEngine<4,1,4,288>,H16>"}}
 
 
 def bench_lmhead(args):
@@ -437,7 +486,8 @@ def main():
     # on the first one, settling within about ten launches of the sweep)
     ap.add_argument("--warmup", type=int, default=25)
     ap.add_argument("--workload", default="sweep",
-                    choices=["sweep", "gemv", "lmhead", "lmhead_norm", "verify", "smallm", "prefill", "copy"])
+                    choices=["sweep", "gemv", "lmhead", "lmhead_norm", "handoff", "verify", "smallm", "prefill",
+                             "copy"])
     ap.add_argument("--m", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--record-traffic", nargs=6, metavar=("WORKLOAD", "KERNEL", "FETCH_CSV", "WRITE_CSV",
@@ -455,6 +505,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     fn = {"sweep": bench_sweep, "gemv": bench_gemv, "lmhead": bench_lmhead, "lmhead_norm": bench_lmhead_norm,
+          "handoff": bench_handoff,
           "verify": bench_verify, "copy": bench_copy,
           "smallm": lambda a: bench_gemm(a, False), "prefill": lambda a: bench_gemm(a, True)}[args.workload]
     out = fn(args)

@@ -157,6 +157,29 @@ Q4_API q4_status lm_head_argmax(const void* w, const void* h, float* logits, int
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * h16[n] = binary16(residual[n] + sum_k w[n][k] * x[k]), rounded to nearest,
+ * ties to even
+ *
+ * The hand-off at the end of a stage's layer range: the device converts the
+ * hidden state it produced to f16 and sends it to the next participant
+ * (aipolix.com en-us page, section "A model can be larger than any one
+ * browser can hold"; 5,120 values, about 10 KB per hop).  Read as the
+ * epilogue of the range's last GEMV (the down projection) with the residual
+ * stream added first: the binary32 sum of q4_0_gemv (same kernel, same
+ * association, so h16 equals the rounding of q4_0_gemv's y plus the residual
+ * bit for bit) plus residual[n] in binary32, then one rounding to binary16.
+ *   w        : n rows of k/32 Q4_0 blocks, 16-byte aligned
+ *   x        : k binary16 values, 16-byte aligned
+ *   residual : NULL (zero) or n binary32 values, 4-byte aligned
+ *   h16      : n binary16 values (written), 2-byte aligned
+ *   n >= 1, k % 64 == 0, 64 <= k <= 32768 (other k: Q4_ERR_INVALID_ARG).
+ *   Inputs finite; |residual + y| >= 65520 gives an infinite h16.  h16 must
+ *   not overlap an input.
+ */
+Q4_API q4_status q4_0_gemv_handoff(const void* w, const void* x, const float* residual, void* h16, int64_t n,
+                                   int64_t k, void* stream);
+
+/*
  * x = final_norm(h);  logits[n] = sum_k w[n][k] * x[k];  token = lowest n
  * with the largest logit
  *

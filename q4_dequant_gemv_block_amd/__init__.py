@@ -37,8 +37,8 @@ Q4_OP_LM_HEAD_NORM_ARGMAX = 5
 # Every symbol include/q4gemv.h declares.
 EXPORTS = (
     "q4_abi_version", "q4_last_error", "q4_workspace_bytes", "q4_0_gemv", "q4_0_gemm_smallm",
-    "q4_0_gemm_prefill", "lm_head_argmax", "lm_head_norm_argmax", "lm_head_verify", "q4_0_gemv_batch_plan_bytes",
-    "q4_0_gemv_batch_plan",
+    "q4_0_gemm_prefill", "lm_head_argmax", "lm_head_norm_argmax", "lm_head_verify", "q4_0_gemv_handoff",
+    "q4_0_gemv_batch_plan_bytes", "q4_0_gemv_batch_plan",
     "q4_0_gemm_smallm_batch_plan_bytes", "q4_0_gemm_smallm_batch_plan", "q4_0_gemm_smallm_batch",
     "q4_0_gemm_prefill_batch_plan_bytes", "q4_0_gemm_prefill_batch_plan", "q4_0_gemm_prefill_batch",
     "q4_0_gemv_batch",
@@ -88,6 +88,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lm_head_argmax.restype = st
     lib.lm_head_argmax.argtypes = [vp, vp, vp, vp, i64, i64, vp, ctypes.c_size_t, vp]
     lib.lm_head_verify.restype = st
+    lib.q4_0_gemv_handoff.argtypes = [vp, vp, vp, vp, i64, i64, vp]
+    lib.q4_0_gemv_handoff.restype = ctypes.c_int
     lib.lm_head_norm_argmax.argtypes = [vp, vp, vp, ctypes.c_float, vp, vp, vp, i64, i64, vp, ctypes.c_size_t, vp]
     lib.lm_head_norm_argmax.restype = ctypes.c_int
     lib.lm_head_verify.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t, vp]
@@ -243,6 +245,26 @@ def lm_head_argmax(w: torch.Tensor, h: torch.Tensor, logits: torch.Tensor | None
                                          n, k, _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
                                          _stream(stream)))
     return logits, token
+
+
+def q4_0_gemv_handoff(w: torch.Tensor, x: torch.Tensor, residual: torch.Tensor | None = None,
+                      out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The stage hand-off: float16 [N] = binary16(residual + W x) for W (uint8 [N, K/32*18]),
+    x (float16 [K]) and an optional float32 residual [N]."""
+    if x.dim() != 1:
+        raise ValueError("x must be float16 [K]")
+    k = x.shape[0]
+    n = _weights(w, k)
+    if out is None:
+        out = torch.empty(n, dtype=torch.float16, device=x.device)
+    rp = 0
+    if residual is not None:
+        if residual.dim() != 1 or residual.shape[0] != n:
+            raise ValueError("residual must be float32 [N]")
+        rp = _ptr(residual, torch.float32, "residual")
+    _check(load_library().q4_0_gemv_handoff(_ptr(w, torch.uint8, "w"), _ptr(x, torch.float16, "x"), rp,
+                                            _ptr(out, torch.float16, "out"), n, k, _stream(stream)))
+    return out
 
 
 def lm_head_norm_argmax(w: torch.Tensor, h: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,

@@ -197,6 +197,27 @@ q4_status lm_head_argmax(const void* w, const void* h, float* logits, int32_t* t
     return hip_status(e, "lm_head_argmax launch");
 }
 
+q4_status q4_0_gemv_handoff(const void* w, const void* x, const float* residual, void* h16, int64_t n, int64_t k,
+                            void* stream) {
+    const char* fn = "q4_0_gemv_handoff";
+    q4_status st = check_shape(fn, 1, 1, n, k);
+    if (st) return st;
+    if (!w || !x || !h16) return fail(Q4_ERR_INVALID_ARG, "%s: null tensor pointer", fn);
+    if (!aligned(w, 16) || !aligned(x, 16)) return fail(Q4_ERR_MISALIGNED, "%s: w and x must be 16-byte aligned", fn);
+    if (!aligned(h16, 2)) return fail(Q4_ERR_MISALIGNED, "%s: h16 must be 2-byte aligned", fn);
+    if (residual && !aligned(residual, 4)) return fail(Q4_ERR_MISALIGNED, "%s: residual must be 4-byte aligned", fn);
+    if (!fast_path(w, k))
+        return fail(Q4_ERR_INVALID_ARG, "%s: needs k %% 64 == 0 and k <= %lld", fn, (long long)q4::kFastMaxK);
+    const Range rh = range(h16, (size_t)n * 2);
+    if (overlap(rh, range(w, (size_t)(n * row_bytes(k)))) || overlap(rh, range(x, (size_t)k * 2)) ||
+        (residual && overlap(rh, range(residual, (size_t)n * 4))))
+        return fail(Q4_ERR_INVALID_ARG, "%s: h16 overlaps an input", fn);
+    const hipError_t e = q4::launch_gemv_handoff(static_cast<const uint8_t*>(w), static_cast<const uint16_t*>(x),
+                                                 residual, static_cast<uint16_t*>(h16), n, k,
+                                                 static_cast<hipStream_t>(stream));
+    return hip_status(e, "q4_0_gemv_handoff launch");
+}
+
 q4_status lm_head_norm_argmax(const void* w, const void* h, const void* gamma, float eps, float* logits,
                               int32_t* token, void* x_out, int64_t n_vocab, int64_t k, void* workspace,
                               size_t workspace_bytes, void* stream) {

@@ -143,10 +143,13 @@ __device__ void stage_x(const uint16_t* __restrict__ x, int nblocks, int npairs_
 // order (thread t takes blocks t, t + blockDim, ...; butterfly within the
 // wave; the waves' partials summed in wave order), so all workgroups stage the
 // same x; workgroup 0 also writes x to x_out when that is set.
+// The same struct carries the stage hand-off's residual (the epilogue that
+// writes binary16(residual + y) in place of y; see k_sweep).
 struct NormArgs {
     const uint16_t* gamma;  // g [k], binary16; unused without the norm
     uint16_t* x_out;        // x [k], binary16, or null
     float eps;
+    const float* residual;  // hand-off: r [n], binary32, or null (zero)
 };
 
 __device__ __forceinline__ float half_lo(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu)); }
@@ -697,7 +700,7 @@ __device__ __forceinline__ Live live_of(const PlanDesc& p) {
 // the barriers of chunk changes and activation staging are reached by all.
 // The NB-slot ring of each wave: the slot of the unit being computed is
 // refilled once its pairs are read, so NB units are in flight during the math.
-template <class E, int XS, bool BATCH, bool ARGMAX, bool NORM>
+template <class E, int XS, bool BATCH, bool ARGMAX, bool NORM, bool H16>
 __global__ void __launch_bounds__(E::kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
 k_sweep(const PlanDesc* __restrict__ descs, int count, SchedHead* head, const SchedChunk* __restrict__ chunks,
         PlanDesc one, int xs_bytes, uint64_t* __restrict__ keys, NormArgs nrm) {
@@ -839,6 +842,12 @@ k_sweep(const PlanDesc* __restrict__ descs, int count, SchedHead* head, const Sc
             if (u.jb + 1 >= Dc.npl) {  // last unit of the wave's rows in this step
                 eng.finish(u.s, acc, [&](int64_t row, float v) {
                     if (row < Dc.n) {
+                        if constexpr (H16) {
+                            // stage hand-off: binary16 (nearest-even) of residual + y, into y's place
+                            const float t = nrm.residual ? v + nrm.residual[row] : v;
+                            reinterpret_cast<uint16_t*>(Dc.y)[row] = (uint16_t)half_bits(t);
+                            return;
+                        }
                         ((g_f32*)Dc.y)[row] = v;
                         if (ARGMAX) {
                             const uint64_t kk = argmax_key(v, row);
@@ -989,13 +998,13 @@ static PlanDesc single_desc(const uint8_t* w, const uint16_t* x, float* y, int64
 
 static bool quad_ok(int64_t k) { return k % 1024 == 0 && k >= 4096; }
 
-template <class E, int XS, bool BATCH, bool AM, bool NORM>
+template <class E, int XS, bool BATCH, bool AM, bool NORM, bool H16>
 static hipError_t launch_sweep(const PlanDesc* descs, int count, SchedHead* head, const SchedChunk* chunks,
                                const PlanDesc& one, int64_t max_k, int grid, uint64_t* keys, const NormArgs& nrm,
                                hipStream_t s) {
     const size_t xsb = x_lds_bytes(max_k);
     const size_t lds = xsb + (size_t)E::kWaves * E::kWaveLds;
-    auto kern = k_sweep<E, XS, BATCH, AM, NORM>;
+    auto kern = k_sweep<E, XS, BATCH, AM, NORM, H16>;
     if (lds > 65536) {
         const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -1006,37 +1015,39 @@ static hipError_t launch_sweep(const PlanDesc* descs, int count, SchedHead* head
 }
 
 // The kernel of a shape, for the activation stride max_k needs.
-template <class E, class EV, bool BATCH, bool AM, bool NORM>
+template <class E, class EV, bool BATCH, bool AM, bool NORM, bool H16>
 static hipError_t launch_stride(const PlanDesc* descs, int count, SchedHead* head, const SchedChunk* chunks,
                                 const PlanDesc& one, int64_t max_k, int grid, uint64_t* keys, const NormArgs& nrm,
                                 hipStream_t s) {
     return fixed_stride(max_k)
-               ? launch_sweep<E, kXStride, BATCH, AM, NORM>(descs, count, head, chunks, one, max_k, grid, keys, nrm, s)
-               : launch_sweep<EV, 0, BATCH, AM, NORM>(descs, count, head, chunks, one, max_k, grid, keys, nrm, s);
+               ? launch_sweep<E, kXStride, BATCH, AM, NORM, H16>(descs, count, head, chunks, one, max_k, grid, keys,
+                                                                  nrm, s)
+               : launch_sweep<EV, 0, BATCH, AM, NORM, H16>(descs, count, head, chunks, one, max_k, grid, keys, nrm, s);
 }
 
 // A batch (descs, head, chunks) runs on a wide shape; a single GEMV passes
 // its descriptor in `one`.
-template <bool BATCH, bool AM, bool NORM = false>
+template <bool BATCH, bool AM, bool NORM = false, bool H16 = false>
 static hipError_t launch_any(const Shape& sh, const PlanDesc* descs, int count, SchedHead* head,
                              const SchedChunk* chunks, const PlanDesc& one, int64_t max_k, int grid, uint64_t* keys,
-                             hipStream_t s, const NormArgs& nrm = NormArgs{nullptr, nullptr, 0.0f}) {
+                             hipStream_t s, const NormArgs& nrm = NormArgs{nullptr, nullptr, 0.0f, nullptr}) {
     constexpr int W = kWide.waves, WN = kNarrow.waves, R = kWide.r;
     static_assert(!(BATCH && NORM), "the norm prologue belongs to a single LM head");
+    static_assert(!(H16 && (BATCH || AM || NORM)), "the hand-off epilogue belongs to a single GEMV");
     if constexpr (!BATCH) {
         if (sh.waves == WN && sh.quad)
-            return launch_stride<QuadEngine<WN, 1, 4, kXStride>, QuadEngine<WN, 1, 4, 0>, BATCH, AM, NORM>(
+            return launch_stride<QuadEngine<WN, 1, 4, kXStride>, QuadEngine<WN, 1, 4, 0>, BATCH, AM, NORM, H16>(
                 descs, count, head, chunks, one, max_k, grid, keys, nrm, s);
         if (sh.waves == WN)
-            return launch_stride<DmaEngine<WN, kNarrow.r, kXStride>, DmaEngine<WN, kNarrow.r, 0>, BATCH, AM, NORM>(
+            return launch_stride<DmaEngine<WN, kNarrow.r, kXStride>, DmaEngine<WN, kNarrow.r, 0>, BATCH, AM, NORM, H16>(
                 descs, count, head, chunks, one, max_k, grid, keys, nrm, s);
     }
     if (sh.quad)
         return launch_stride<QuadEngine<kQuadWide.waves, kQuadWide.r, kQuadNB, kXStride>,
                              QuadEngine<kQuadWide.waves, kQuadWide.r, kQuadNB, 0>,
-                             BATCH, AM, NORM>(
+                             BATCH, AM, NORM, H16>(
             descs, count, head, chunks, one, max_k, grid, keys, nrm, s);
-    return launch_stride<DmaEngine<W, R, kXStride>, DmaEngine<W, R, 0>, BATCH, AM, NORM>(
+    return launch_stride<DmaEngine<W, R, kXStride>, DmaEngine<W, R, 0>, BATCH, AM, NORM, H16>(
         descs, count, head, chunks, one, max_k, grid, keys, nrm, s);
 }
 
@@ -1087,10 +1098,19 @@ hipError_t launch_lm_head_norm(const uint8_t* w, const uint16_t* h, const uint16
     const PlanDesc d = single_desc(w, h, logits, n, k, sh);
     const int grid = argmax_blocks(n, k);
     hipError_t e = launch_any<false, true, true>(sh, nullptr, 1, nullptr, nullptr, d, k, grid, keys, s,
-                                                 NormArgs{gamma, x_out, eps});
+                                                 NormArgs{gamma, x_out, eps, nullptr});
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_argmax_final, dim3(1), dim3(kFinalThreads), 0, s, keys, grid, token);
     return hipGetLastError();
+}
+
+hipError_t launch_gemv_handoff(const uint8_t* w, const uint16_t* x, const float* residual, uint16_t* h16,
+                               int64_t n, int64_t k, hipStream_t s) {
+    const Shape& sh = single_shape(n, k);
+    const PlanDesc d = single_desc(w, x, reinterpret_cast<float*>(h16), n, k, sh);
+    return launch_any<false, false, false, true>(sh, nullptr, 1, nullptr, nullptr, d, k,
+                                                 static_grid(d.steps, sh, INT32_MAX), nullptr, s,
+                                                 NormArgs{nullptr, nullptr, 0.0f, residual});
 }
 
 hipError_t launch_gemm_generic(const uint8_t* w, const uint16_t* x, float* y, int64_t m,

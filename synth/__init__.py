@@ -48,7 +48,7 @@ PROJ = (
 VOCAB = 151936
 
 # Tensor kinds inside a stream id.
-T_W, T_X = 0, 1
+T_W, T_X, T_R = 0, 1, 2  # weights, activations, residual stream
 
 
 def stream_id(workload: int, layer: int, proj: int, tensor: int) -> int:

@@ -159,6 +159,27 @@ def test_lm_head_validation(lib):
     assert lib.lm_head_argmax(w, h, lg, tok, 1000, 96, FAKE * 16, need, None) == q4.Q4_ERR_INVALID_ARG
 
 
+def test_gemv_handoff_validation(lib):
+    w, x, r, out = FAKE, FAKE * 2, FAKE * 3, FAKE * 4
+    n, k = 1000, 64
+
+    def call(w=w, x=x, r=r, out=out, n=n, k=k):
+        return lib.q4_0_gemv_handoff(w, x, r, out, n, k, None)
+
+    assert call(w=None) == q4.Q4_ERR_INVALID_ARG
+    assert call(out=None) == q4.Q4_ERR_INVALID_ARG
+    assert call(x=x + 8) == q4.Q4_ERR_MISALIGNED
+    assert call(out=out + 1) == q4.Q4_ERR_MISALIGNED
+    assert call(r=r + 2) == q4.Q4_ERR_MISALIGNED
+    assert call(k=96) == q4.Q4_ERR_INVALID_ARG
+    assert call(n=0) == q4.Q4_ERR_INVALID_ARG
+    # the output over the weights, over x, over the residual
+    assert call(out=w + 64) == q4.Q4_ERR_INVALID_ARG
+    assert call(out=x) == q4.Q4_ERR_INVALID_ARG
+    assert call(out=r + 8) == q4.Q4_ERR_INVALID_ARG
+    assert b"overlaps" in lib.q4_last_error()
+
+
 def test_lm_head_norm_validation(lib):
     w, h, g, lg, tok, xo, ws = FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 8, FAKE * 9, FAKE * 16
     n, k = 1000, 64
