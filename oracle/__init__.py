@@ -61,6 +61,7 @@ class Oracle:
         lib.q4o_f64_to_f16_array.argtypes = [vp, i64, vp]
         lib.q4o_rms_norm.argtypes = [vp, vp, i64, ctypes.c_double, vp, vp]
         lib.q4o_gemv_handoff.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
+        lib.q4o_q8_gemm_rows.argtypes = [vp, i64, i64, vp, i64, vp, vp]
         self.lib = lib
         self.path = path
 
@@ -145,6 +146,21 @@ class Oracle:
         y, a = self.gemm_rows(w_rows, k, x)
         return y, a, self.argmax(y), x
 
+    def q8_gemm_rows(self, w_rows: np.ndarray, k: int, x) -> tuple[np.ndarray, np.ndarray]:
+        """(y, a) as gemm_rows, for packed Q8_0 rows uint8[n, K/32*34]."""
+        assert k % 32 == 0
+        w = _u8(w_rows).reshape(-1, k // 32 * 34)
+        xb = _f16bits(np.asarray(x))
+        one_d = xb.ndim == 1
+        xb = np.ascontiguousarray(xb.reshape(-1, k))
+        m, n = xb.shape[0], w.shape[0]
+        y = np.empty((m, n), dtype=np.float64)
+        a = np.empty((m, n), dtype=np.float64)
+        self.lib.q4o_q8_gemm_rows(w.ctypes.data, n, k, xb.ctypes.data, m, y.ctypes.data, a.ctypes.data)
+        if one_d:
+            return y[0], a[0]
+        return y, a
+
     def gemv_handoff(self, w_rows: np.ndarray, k: int, x, residual=None):
         """The stage hand-off: (h16, y, a) for packed rows [n], f16 x [K] and an optional
         float32 residual [n]: y, a as gemm_rows, h16 = binary16 bits of residual + y."""
@@ -210,6 +226,10 @@ def lm_head_norm(w_rows: np.ndarray, k: int, h, g, eps: float):
 
 def gemv_handoff(w_rows: np.ndarray, k: int, x, residual=None):
     return default().gemv_handoff(w_rows, k, x, residual)
+
+
+def q8_gemm_rows(w_rows: np.ndarray, k: int, x) -> tuple[np.ndarray, np.ndarray]:
+    return default().q8_gemm_rows(w_rows, k, x)
 
 
 def _u8(a) -> np.ndarray:

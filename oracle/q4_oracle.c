@@ -41,6 +41,14 @@
  *   v_i = h_i * g_i * r                       (binary64)
  *   x_i = v_i rounded to binary16, nearest, ties to even
  * and x is the activation the LM head multiplies.
+ * The pages' other weight format, "GGUF Q8_0", used by the small dense Qwen3
+ * models (taozi.news, section "支持模型与限制"), is named but not defined
+ * either; the reading used here:
+ *   - a row of K weights is K/32 blocks of 34 bytes, blocks contiguous along K;
+ *   - bytes 0..1 of a block: the scale d, IEEE binary16, little-endian;
+ *   - byte 2 + j (j = 0..31): code j, a two's-complement signed byte;
+ *   - weight j of the block = code_j * d.
+ * Its products are exact in binary64 as well (8-bit codes, 11-bit d and x).
  * The hand-off at the end of a stage's layer range (each device converts the
  * hidden state it produced to f16 and sends it to the next participant:
  * aipolix.com en-us page, section "A model can be larger than any one browser
@@ -188,4 +196,32 @@ void q4o_gemv_handoff(const uint8_t* w_rows, int64_t nrows, int64_t k, const uin
                       uint16_t* out16, double* y, double* a) {
     q4o_gemm_rows(w_rows, nrows, k, x, 1, y, a);
     for (int64_t n = 0; n < nrows; ++n) out16[n] = q4o_f64_to_f16((r ? (double)r[n] : 0.0) + y[n]);
+}
+
+/* Weight kk (0..31) of a Q8_0 block. */
+static double q8_block_weight(const uint8_t* blk, int kk) {
+    const double d = q4o_f16_to_f64((uint16_t)(blk[0] | ((uint16_t)blk[1] << 8)));
+    const int code = (int)(int8_t)blk[2 + kk];
+    return (double)code * d;
+}
+
+/* y[m][n] and a[m][n] as q4o_gemm_rows, for Q8_0 rows (34-byte blocks). */
+void q4o_q8_gemm_rows(const uint8_t* w_rows, int64_t nrows, int64_t k,
+                      const uint16_t* x, int64_t m, double* y, double* a) {
+    const int64_t rb = (k / 32) * 34;
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t n = 0; n < nrows; ++n) {
+        const uint8_t* row = w_rows + n * rb;
+        for (int64_t mm = 0; mm < m; ++mm) {
+            const uint16_t* xr = x + mm * k;
+            double acc = 0.0, mag = 0.0;
+            for (int64_t i = 0; i < k; ++i) {
+                double p = q8_block_weight(row + (i / 32) * 34, (int)(i % 32)) * q4o_f16_to_f64(xr[i]);
+                acc += p;
+                mag += fabs(p);
+            }
+            y[mm * nrows + n] = acc;
+            if (a) a[mm * nrows + n] = mag;
+        }
+    }
 }

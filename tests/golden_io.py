@@ -33,12 +33,13 @@ def _cases(name):
                     case["r"] = int(rest)
 
 
-def q4_0_block_cases():
-    """Hand-computed Q4_0 cases: dict(name, k, w uint8[n, k/32*18], x float16[k], y, a)."""
+def q4_0_block_cases(fixture="q4_0_blocks.txt", block_bytes=18):
+    """Hand-computed Q4_0 cases: dict(name, k, w uint8[n, k/32*18], x float16[k], y, a)
+    (Q8_0 cases with fixture q8_0_blocks.txt and 34-byte blocks)."""
     out = []
-    for c in _cases("q4_0_blocks.txt"):
+    for c in _cases(fixture):
         k = c["k"]
-        rb = k // 32 * 18
+        rb = k // 32 * block_bytes
         for r in c["rows"]:
             assert len(r) == rb, (c["name"], len(r), rb)
         w = np.frombuffer(b"".join(c["rows"]), dtype=np.uint8).reshape(len(c["rows"]), rb).copy()
@@ -77,3 +78,8 @@ def rms_norm_cases():
         out.append(dict(name=c["name"], h=h.astype(np.float16), g=g.astype(np.float16), eps=eps,
                         x=x.astype(np.float16)))
     return out
+
+
+def q8_0_block_cases():
+    """Hand-computed Q8_0 cases, as q4_0_block_cases with 34-byte blocks."""
+    return q4_0_block_cases("q8_0_blocks.txt", 34)

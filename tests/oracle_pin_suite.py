@@ -31,6 +31,11 @@ instance disagrees with a fact fixed by the pages' reading or by mathematics:
                     numpy sqrt, numpy float16 rounding), lengths 1 to 5120
   lm_head_norm_brute final norm then LM head on tiny shapes: token = numpy.argmax
                     of the dense product with numpy's normed activation
+  q8_golden         hand-computed Q8_0 blocks (tests/golden/q8_0_blocks.txt)
+  q8_basis_columns  x = e_k returns column k of a Q8_0 matrix (chosen codes)
+  q8_integer_exact  Q8_0 with d = 1 and integer x: the exact int64 product
+  q8_brute          tiny Q8_0 shapes vs numpy float64 matmul of the dense
+                    matrix built from the chosen numbers
   handoff_exact     the stage hand-off with d = 1, integer x and an integer
                     residual: h16 = the exact integer (|value| <= 2048 is exact
                     in binary16), and large sums round to even
@@ -268,6 +273,50 @@ def lm_head_norm_brute(o):
         assert token == int(np.argmax(y_np)), (n, k)
 
 
+def q8_golden(o):
+    for c in golden_io.q8_0_block_cases():
+        y, a = o.q8_gemm_rows(c["w"], c["k"], c["x"])
+        assert np.array_equal(y, c["y"]), (c["name"], y, c["y"])
+        assert np.array_equal(a, c["a"]), (c["name"], a, c["a"])
+
+
+def q8_basis_columns(o):
+    rng = np.random.default_rng(47)
+    n, k = 5, 96
+    codes, d, w = q4_encode.random_case_q8(rng, n, k)
+    for col in (0, 1, 2, 31, 32, 33, 63, 64, 95):
+        x = np.zeros(k, dtype=np.float16)
+        x[col] = 1.0
+        y, a = o.q8_gemm_rows(w, k, x)
+        want = codes[:, col].astype(np.float64) * d[:, col // 32]
+        assert np.array_equal(y, want), (col, y, want)
+        assert np.array_equal(a, np.abs(want)), col
+
+
+def q8_integer_exact(o):
+    rng = np.random.default_rng(53)
+    for n, k in ((3, 32), (17, 160), (4, 1024)):
+        codes = rng.integers(-128, 128, size=(n, k))
+        w = q4_encode.encode_q8(codes, np.full((n, k // 32), 0x3C00, dtype=np.uint16))  # d = 1
+        x = rng.integers(-16, 17, size=k).astype(np.float16)
+        y, a = o.q8_gemm_rows(w, k, x)
+        want = codes @ x.astype(np.int64)
+        assert np.array_equal(y, want.astype(np.float64)), (n, k)
+        assert np.array_equal(a, (np.abs(codes) @ np.abs(x.astype(np.int64))).astype(np.float64)), (n, k)
+
+
+def q8_brute(o):
+    rng = np.random.default_rng(59)
+    for m, n, k in ((1, 5, 32), (3, 40, 64), (2, 33, 96), (4, 70, 128)):
+        codes, d, w = q4_encode.random_case_q8(rng, n, k)
+        dense = q4_encode.weights_from_numbers_q8(codes, d)
+        x = rng.standard_normal((m, k)).astype(np.float16)
+        y, a = o.q8_gemm_rows(w, k, x)
+        want = x.astype(np.float64) @ dense.T
+        assert np.allclose(y, want, rtol=1e-12, atol=1e-12), (m, n, k)
+        assert np.allclose(a, np.abs(x.astype(np.float64)) @ np.abs(dense).T, rtol=1e-12, atol=0), (m, n, k)
+
+
 def handoff_exact(o):
     rng = np.random.default_rng(41)
     for n, k in ((7, 32), (33, 96)):
@@ -306,7 +355,8 @@ def handoff_brute(o):
 
 ALL = [golden_blocks, f16_exhaustive, basis_columns, all_ones, integer_exact,
        brute_force, multi_row_layout, argmax_golden, argmax_invariants, verify_prefix, verify_brute,
-       f16_round, norm_golden, norm_closed_forms, norm_brute, lm_head_norm_brute, handoff_exact, handoff_brute]
+       f16_round, norm_golden, norm_closed_forms, norm_brute, lm_head_norm_brute, handoff_exact, handoff_brute,
+       q8_golden, q8_basis_columns, q8_integer_exact, q8_brute]
 
 
 def failures(o):

@@ -39,3 +39,32 @@ def weights_from_numbers(codes: np.ndarray, d: np.ndarray) -> np.ndarray:
     """Dense float64 weights (code - 8) * d from the numbers a test chose (not from bytes)."""
     n, k = codes.shape
     return (codes.astype(np.float64) - 8.0) * np.repeat(d, 32, axis=1).reshape(n, k)
+
+
+def encode_q8(codes: np.ndarray, d_bits: np.ndarray) -> np.ndarray:
+    """Q8_0: codes int8[n, K] in -128..127, d_bits uint16[n, K/32] -> uint8[n, K/32*34]
+    (bytes 0-1 = f16 scale bits, little-endian; byte 2+j = code j as a two's-complement byte)."""
+    codes = np.asarray(codes)
+    n, k = codes.shape
+    assert k % 32 == 0 and codes.min(initial=0) >= -128 and codes.max(initial=0) <= 127
+    nb = k // 32
+    d_bits = np.asarray(d_bits, dtype=np.uint16).reshape(n, nb)
+    out = np.zeros((n, nb, 34), dtype=np.uint8)
+    out[:, :, 0] = (d_bits & 0xFF).astype(np.uint8)
+    out[:, :, 1] = (d_bits >> 8).astype(np.uint8)
+    out[:, :, 2:] = codes.astype(np.int8).view(np.uint8).reshape(n, nb, 32)
+    return out.reshape(n, nb * 34)
+
+
+def random_case_q8(rng: np.random.Generator, n: int, k: int, d_lo=0.0005, d_hi=0.005):
+    """Random Q8_0 codes (-128..127), signed scales (exact f16) and packed rows; (codes, d, packed)."""
+    codes = rng.integers(-128, 128, size=(n, k))
+    d = rng.uniform(d_lo, d_hi, size=(n, k // 32)) * rng.choice([-1.0, 1.0], size=(n, k // 32))
+    d16 = d.astype(np.float16)
+    return codes, d16.astype(np.float64), encode_q8(codes, d16.view(np.uint16))
+
+
+def weights_from_numbers_q8(codes: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """Dense float64 Q8_0 weights code * d from the numbers a test chose."""
+    n, k = codes.shape
+    return codes.astype(np.float64) * np.repeat(d, 32, axis=1).reshape(n, k)

@@ -47,6 +47,12 @@ MUTANTS = {
                                     "q4o_f64_to_f16(y[n] - (r ? (double)r[n] : 0.0))"),
     "handoff_rounded_before_residual": ("q4o_f64_to_f16((r ? (double)r[n] : 0.0) + y[n])",
                                         "q4o_f64_to_f16((r ? (double)r[n] : 0.0) + q4o_f16_to_f64(q4o_f64_to_f16(y[n])))"),
+    "q8_codes_unsigned": ("const int code = (int)(int8_t)blk[2 + kk];", "const int code = (int)blk[2 + kk];"),
+    "q8_codes_offset_128": ("const int code = (int)(int8_t)blk[2 + kk];", "const int code = (int)blk[2 + kk] - 128;"),
+    "q8_scale_big_endian": ("q4o_f16_to_f64((uint16_t)(blk[0] | ((uint16_t)blk[1] << 8)));\n    const int code",
+                            "q4o_f16_to_f64((uint16_t)(blk[1] | ((uint16_t)blk[0] << 8)));\n    const int code"),
+    "q8_block_stride_32": ("row + (i / 32) * 34, (int)(i % 32)", "row + (i / 32) * 32, (int)(i % 32)"),
+    "q8_codes_shifted": ("const int code = (int)(int8_t)blk[2 + kk];", "const int code = (int)(int8_t)blk[1 + kk];"),
     "prefix_past_mismatch": ("while (i < m && tokens[i] == draft[i]) ++i;",
                              "while (i < m && tokens[i] == draft[i]) ++i;\n    if (i < m) ++i;"),
 }
