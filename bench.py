@@ -1,7 +1,8 @@
 """Benchmark of the Q4_0 dequantize-and-multiply path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload sweep|gemv|lmhead|lmhead_norm|handoff|verify|smallm|prefill|copy] [--m M]
+                    [--workload sweep|gemv|lmhead|lmhead_norm|handoff|q8|verify|smallm|prefill|copy]
+                    [--m M]
 
 Default workload ("sweep"): the 27B-shaped decode weight sweep, 64 layers x
 (q, k, v, o 5120x5120; gate, up 17408x5120; down 5120x17408) = 448 Q4_0 GEMVs
@@ -17,7 +18,8 @@ on a bounded sample of the same workload on this host's cores).
 Other workloads print the same kind of line for the single 5120x5120 GEMV
 (rotating weight copies so the 256 MB last-level cache does not serve them),
 the LM head with argmax (with the final norm fused: lmhead_norm), the stage
-hand-off GEMV with its binary16 epilogue (handoff), the greedy
+hand-off GEMV with its binary16 epilogue (handoff), the Q8_0 GEMV over a
+small dense model's layers (q8), the greedy
 verify of an M-row draft, small-M (--m) and prefill (--m) over the sweep.
 """
 from __future__ import annotations
@@ -47,7 +49,7 @@ def log(*a):
 # Kernel source of each workload's dominant kernel (besides the shared device
 # and launch headers, the host-side C ABI and the build script).
 KERNEL_SOURCE = {"sweep": ["gemv.hip"], "gemv": ["gemv.hip"], "lmhead": ["gemv.hip"], "lmhead_norm": ["gemv.hip"],
-                 "handoff": ["gemv.hip"],
+                 "handoff": ["gemv.hip"], "q8": ["q8.hip"],
                  "smallm": ["smallm.hip"],
                  "prefill": ["prefill.hip"], "verify": ["smallm.hip", "gemv.hip", "verify.hip"]}
 
@@ -237,6 +239,53 @@ def bench_gemv(args):
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counter_traffic("gemv"),
                          "kernel": "q4::k_sweep<QuadEngine<4,1,4,288>>"}}
+
+
+def bench_q8(args):
+    """Q8_0 GEMVs over the layers of a small dense model shaped like Qwen3 4B
+    (36 layers x q 4096x2560, k and v 1024x2560, o 2560x4096, gate and up
+    9728x2560, down 2560x9728: 252 GEMVs, 3.86 GB of Q8_0 weights), each with
+    its own f16 input; one step = the 252 launches replayed from a HIP graph."""
+    import torch
+    import synth
+    q4 = load_q4()
+    log("uploading the Q8_0 layers ...")
+    ws, xs, ys = [], [], []
+    wbytes = io = 0
+    for layer in range(synth.Q8_LAYERS):
+        for p, (_, n, k) in enumerate(synth.Q8_PROJ):
+            w = synth.q8_0(SEED, synth.stream_id(6, layer, p, synth.T_W), n, k)
+            ws.append(torch.from_numpy(w).cuda())
+            xs.append(torch.from_numpy(synth.f16_normal(SEED, synth.stream_id(6, layer, p, synth.T_X), k)).cuda())
+            ys.append(torch.empty(n, dtype=torch.float32, device="cuda"))
+            wbytes += w.nbytes
+            io += 2 * k + 4 * n
+
+    def eager():
+        for w, x, y in zip(ws, xs, ys):
+            q4.q8_0_gemv(w, x, y)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        eager()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        eager()
+    ms = time_steps(g.replay, args.steps, args.warmup)
+    eager_ms = time_steps(eager, max(2, args.steps // 5), 2)
+    gbs = (wbytes + io) / (ms * 1e-3) / 1e9
+    return {"metric": "Q8_0 GEMV HBM GB/s over a small dense model's layers (Qwen3-4B shapes)",
+            "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f16->f32", "data": "synthetic",
+            "config": {"workload": "36 layers x 7 Q8_0 GEMVs (q 4096x2560, k,v 1024x2560, o 2560x4096, gate,up "
+                                   "9728x2560, down 2560x9728), 252 launches in one HIP graph",
+                       "weight_bytes": wbytes, "algorithmic_bytes_per_step": wbytes + io},
+            "eager_ms_per_step": round(eager_ms, 4),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counter_traffic("q8"),
+                         "kernel": "q4::k_q8_gemv", "launches_per_step": len(ws)}}
 
 
 def bench_handoff(args):
@@ -486,8 +535,8 @@ def main():
     # on the first one, settling within about ten launches of the sweep)
     ap.add_argument("--warmup", type=int, default=25)
     ap.add_argument("--workload", default="sweep",
-                    choices=["sweep", "gemv", "lmhead", "lmhead_norm", "handoff", "verify", "smallm", "prefill",
-                             "copy"])
+                    choices=["sweep", "gemv", "lmhead", "lmhead_norm", "handoff", "q8", "verify", "smallm",
+                             "prefill", "copy"])
     ap.add_argument("--m", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--record-traffic", nargs=6, metavar=("WORKLOAD", "KERNEL", "FETCH_CSV", "WRITE_CSV",
@@ -505,7 +554,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     fn = {"sweep": bench_sweep, "gemv": bench_gemv, "lmhead": bench_lmhead, "lmhead_norm": bench_lmhead_norm,
-          "handoff": bench_handoff,
+          "handoff": bench_handoff, "q8": bench_q8,
           "verify": bench_verify, "copy": bench_copy,
           "smallm": lambda a: bench_gemm(a, False), "prefill": lambda a: bench_gemm(a, True)}[args.workload]
     out = fn(args)

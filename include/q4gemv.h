@@ -157,6 +157,24 @@ Q4_API q4_status lm_head_argmax(const void* w, const void* h, float* logits, int
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * y[n] = sum_k w[n][k] * x[k]  with w in Q8_0 blocks
+ *
+ * The pages' other weight format, "GGUF Q8_0", used by the small dense Qwen3
+ * models (taozi.news, section "支持模型与限制"); the pages name it only.
+ * Read as: a row of k weights is k/32 blocks of 34 bytes; bytes 0..1 of a
+ * block are the scale d (binary16, little-endian), bytes 2..33 the 32 codes
+ * as two's-complement signed bytes; weight j = code_j * d.  Same boundary
+ * and bound as q4_0_gemv: |y - y_exact| <= 1e-3 * sum_k |w x| per row
+ * (binary32 sums, one fixed association per row).
+ *   w : n rows of k/32 Q8_0 blocks, 4-byte aligned (rows follow each other;
+ *       a row starts 2 bytes into a dword when k/32 is odd)
+ *   x : k binary16 values, 16-byte aligned;  y : n binary32 (written)
+ *   n >= 1, k % 32 == 0, 32 <= k <= 32768.  Inputs finite.  y must not
+ *   overlap w or x.
+ */
+Q4_API q4_status q8_0_gemv(const void* w, const void* x, float* y, int64_t n, int64_t k, void* stream);
+
+/*
  * h16[n] = binary16(residual[n] + sum_k w[n][k] * x[k]), rounded to nearest,
  * ties to even
  *

@@ -37,7 +37,7 @@ Q4_OP_LM_HEAD_NORM_ARGMAX = 5
 # Every symbol include/q4gemv.h declares.
 EXPORTS = (
     "q4_abi_version", "q4_last_error", "q4_workspace_bytes", "q4_0_gemv", "q4_0_gemm_smallm",
-    "q4_0_gemm_prefill", "lm_head_argmax", "lm_head_norm_argmax", "lm_head_verify", "q4_0_gemv_handoff",
+    "q4_0_gemm_prefill", "lm_head_argmax", "lm_head_norm_argmax", "lm_head_verify", "q4_0_gemv_handoff", "q8_0_gemv",
     "q4_0_gemv_batch_plan_bytes", "q4_0_gemv_batch_plan",
     "q4_0_gemm_smallm_batch_plan_bytes", "q4_0_gemm_smallm_batch_plan", "q4_0_gemm_smallm_batch",
     "q4_0_gemm_prefill_batch_plan_bytes", "q4_0_gemm_prefill_batch_plan", "q4_0_gemm_prefill_batch",
@@ -88,6 +88,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lm_head_argmax.restype = st
     lib.lm_head_argmax.argtypes = [vp, vp, vp, vp, i64, i64, vp, ctypes.c_size_t, vp]
     lib.lm_head_verify.restype = st
+    lib.q8_0_gemv.argtypes = [vp, vp, vp, i64, i64, vp]
+    lib.q8_0_gemv.restype = ctypes.c_int
     lib.q4_0_gemv_handoff.argtypes = [vp, vp, vp, vp, i64, i64, vp]
     lib.q4_0_gemv_handoff.restype = ctypes.c_int
     lib.lm_head_norm_argmax.argtypes = [vp, vp, vp, ctypes.c_float, vp, vp, vp, i64, i64, vp, ctypes.c_size_t, vp]
@@ -245,6 +247,28 @@ def lm_head_argmax(w: torch.Tensor, h: torch.Tensor, logits: torch.Tensor | None
                                          n, k, _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
                                          _stream(stream)))
     return logits, token
+
+
+def q8_row_bytes(k: int) -> int:
+    """Bytes of one Q8_0 row of K weights (K/32 blocks of 34 bytes)."""
+    if k % 32:
+        raise ValueError("K must be a multiple of 32")
+    return k // 32 * 34
+
+
+def q8_0_gemv(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y float32 [N] = W x for Q8_0 weights W (uint8 [N, K/32*34]) and x (float16 [K])."""
+    if x.dim() != 1:
+        raise ValueError("x must be float16 [K]")
+    k = x.shape[0]
+    if w.dim() != 2 or w.shape[1] != q8_row_bytes(k):
+        raise ValueError("w must be uint8 [N, K/32*34]")
+    n = w.shape[0]
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=x.device)
+    _check(load_library().q8_0_gemv(_ptr(w, torch.uint8, "w"), _ptr(x, torch.float16, "x"),
+                                    _ptr(out, torch.float32, "out"), n, k, _stream(stream)))
+    return out
 
 
 def q4_0_gemv_handoff(w: torch.Tensor, x: torch.Tensor, residual: torch.Tensor | None = None,

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libq4gemv.so")
-SOURCES = ["gemv.hip", "smallm.hip", "prefill.hip", "verify.hip", "api.cpp"]
+SOURCES = ["gemv.hip", "smallm.hip", "prefill.hip", "verify.hip", "q8.hip", "api.cpp"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -197,6 +197,23 @@ q4_status lm_head_argmax(const void* w, const void* h, float* logits, int32_t* t
     return hip_status(e, "lm_head_argmax launch");
 }
 
+q4_status q8_0_gemv(const void* w, const void* x, float* y, int64_t n, int64_t k, void* stream) {
+    const char* fn = "q8_0_gemv";
+    q4_status st = check_shape(fn, 1, 1, n, k);
+    if (st) return st;
+    if (!w || !x || !y) return fail(Q4_ERR_INVALID_ARG, "%s: null tensor pointer", fn);
+    if (!aligned(w, 4)) return fail(Q4_ERR_MISALIGNED, "%s: w must be 4-byte aligned", fn);
+    if (!aligned(x, 16)) return fail(Q4_ERR_MISALIGNED, "%s: x must be 16-byte aligned", fn);
+    if (!aligned(y, 4)) return fail(Q4_ERR_MISALIGNED, "%s: y must be 4-byte aligned", fn);
+    if (k > q4::kFastMaxK) return fail(Q4_ERR_INVALID_ARG, "%s: k = %lld above %lld", fn, (long long)k, (long long)q4::kFastMaxK);
+    const Range ry = range(y, (size_t)n * 4);
+    if (overlap(ry, range(w, (size_t)(n * (k / 32) * 34))) || overlap(ry, range(x, (size_t)k * 2)))
+        return fail(Q4_ERR_INVALID_ARG, "%s: output overlaps an input", fn);
+    const hipError_t e = q4::launch_q8_gemv(static_cast<const uint8_t*>(w), static_cast<const uint16_t*>(x), y, n, k,
+                                            static_cast<hipStream_t>(stream));
+    return hip_status(e, "q8_0_gemv launch");
+}
+
 q4_status q4_0_gemv_handoff(const void* w, const void* x, const float* residual, void* h16, int64_t n, int64_t k,
                             void* stream) {
     const char* fn = "q4_0_gemv_handoff";

@@ -127,6 +127,8 @@ hipError_t launch_lm_head_verify(const uint8_t* w, const uint16_t* h, float* log
                                  void* workspace, hipStream_t s);
 hipError_t launch_lm_head(const uint8_t* w, const uint16_t* h, float* logits, int32_t* token,
                           int64_t n, int64_t k, uint64_t* keys, hipStream_t s);
+// Q8_0 GEMV (q8.hip): any k % 32 == 0 up to kFastMaxK, w 4-byte aligned, x 16-byte aligned.
+hipError_t launch_q8_gemv(const uint8_t* w, const uint16_t* x, float* y, int64_t n, int64_t k, hipStream_t s);
 // A GEMV whose epilogue writes binary16(residual + y) (residual may be null).
 hipError_t launch_gemv_handoff(const uint8_t* w, const uint16_t* x, const float* residual, uint16_t* h16,
                                int64_t n, int64_t k, hipStream_t s);

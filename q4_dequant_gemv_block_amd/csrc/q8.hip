@@ -1,0 +1,121 @@
+// Q8_0 matrix-vector product: y[n] = sum_k w[n][k] x[k], w in Q8_0 blocks.
+//
+// The pages' other weight format, used by the small dense Qwen3 models
+// (taozi.news, section "支持模型与限制"), read as: 34-byte blocks of 32
+// weights, an f16 scale d (little-endian) then 32 two's-complement code bytes,
+// weight j = code_j * d; a row of K weights is K/32 consecutive blocks.
+//
+// The kernel streams rows from HBM: one wave per row at a time, lane l takes
+// blocks l, l + 64, ... of the row, so the 64 lanes of one load instruction
+// cover 64 consecutive blocks (2,176 contiguous bytes).  A block sits at an
+// even byte offset; a lane reads the 36-byte dword-aligned window around it
+// (two dwordx4 and one dword) and realigns the codes with v_alignbyte when the
+// block starts 2 bytes into a dword.  Codes become f16 exactly (byte xor 0x80
+// under the exponent of 1024 via v_perm, minus 1152), products and sums go
+// through v_dot2_f32_f16 against x staged once per workgroup in LDS, and the
+// block's sum is scaled by d with one FMA.  The row's lanes are summed by a
+// fixed butterfly, so every row has one association wherever it runs.
+#include "q4_device.h"
+#include "q4_launch.h"
+
+#include <algorithm>
+
+namespace q4 {
+
+namespace {
+
+constexpr int kQ8BlockBytes = 34;
+constexpr int kQ8Waves = 8;   // waves per workgroup
+constexpr int kQ8Unroll = 2;  // blocks per lane loaded before their math
+
+typedef __attribute__((address_space(1))) const uint16_t g_u16;
+
+// One block in registers: its 32 codes (code 4j + i in byte i of c[j]) and d.
+struct Q8Block {
+    uint32_t c[8];
+    float d;
+};
+
+// `end`: one past the matrix's last byte.  Only the matrix's last block can
+// have a window that reaches past it (when that block starts on a dword).
+__device__ __forceinline__ void load_q8(const uint8_t* blk, const uint8_t* end, Q8Block& B) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(blk);
+    const bool odd = (a & 2u) != 0;  // the block starts 2 bytes into a dword
+    const uint8_t* al = reinterpret_cast<const uint8_t*>(a & ~(uintptr_t)3);
+    const u4a4 p = *(g_u4a4*)al;
+    const u4a4 q = *(g_u4a4*)(al + 16);
+    uint32_t t;
+    if (odd || al + 36 <= end)
+        t = *(g_u32*)(al + 32);
+    else
+        t = (uint32_t)*(g_u16*)(al + 32);
+    const uint32_t D[9] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w, t};
+    B.d = odd ? f16_hi(D[0]) : f16_lo(D[0]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) B.c[j] = odd ? D[j + 1] : __builtin_amdgcn_alignbyte(D[j + 1], D[j], 2);
+}
+
+// sum_j code_j x_j over one block (binary32 through v_dot2_f32_f16), codes
+// exact in f16: byte ^ 0x80 = code + 128, placed under 0x64 it reads as
+// 1024 + code + 128, and subtracting 1152 leaves the code.
+__device__ __forceinline__ float q8_dot(const Q8Block& B, const u4 (&xv)[4]) {
+    const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t u = B.c[j] ^ 0x80808080u;
+        const h2 lo = as_h2(__builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) - bias;  // codes 4j, 4j+1
+        const h2 hi = as_h2(__builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) - bias;  // codes 4j+2, 4j+3
+        const u4 xc = xv[j >> 1];
+        const uint32_t x0 = (j & 1) ? xc.z : xc.x;
+        const uint32_t x1 = (j & 1) ? xc.w : xc.y;
+        s = __builtin_amdgcn_fdot2(lo, as_h2(x0), s, false);
+        s = __builtin_amdgcn_fdot2(hi, as_h2(x1), s, false);
+    }
+    return s;
+}
+
+__global__ void __launch_bounds__(kQ8Waves * 64) k_q8_gemv(const uint8_t* __restrict__ w,
+                                                          const uint16_t* __restrict__ x, float* __restrict__ y,
+                                                          int64_t n, int k) {
+    extern __shared__ u4 xs[];  // x, k binary16
+    for (int i = threadIdx.x; i < (k >> 3); i += blockDim.x) xs[i] = ((g_u4*)x)[i];
+    __syncthreads();
+    const int nb = k >> 5;
+    const int lane = threadIdx.x & 63;
+    const int64_t rb = (int64_t)nb * kQ8BlockBytes;
+    const uint8_t* end = w + n * rb;
+    const int64_t nwaves = (int64_t)gridDim.x * kQ8Waves;
+    for (int64_t row = (int64_t)blockIdx.x * kQ8Waves + (threadIdx.x >> 6); row < n; row += nwaves) {
+        const uint8_t* wr = w + row * rb;
+        float acc = 0.0f;
+        for (int b0 = lane; b0 < nb; b0 += 64 * kQ8Unroll) {
+            Q8Block B[kQ8Unroll];
+#pragma unroll
+            for (int u = 0; u < kQ8Unroll; ++u)
+                if (b0 + 64 * u < nb) load_q8(wr + (int64_t)(b0 + 64 * u) * kQ8BlockBytes, end, B[u]);
+#pragma unroll
+            for (int u = 0; u < kQ8Unroll; ++u) {
+                const int b = b0 + 64 * u;
+                if (b < nb) {
+                    const u4 xv[4] = {xs[4 * b], xs[4 * b + 1], xs[4 * b + 2], xs[4 * b + 3]};
+                    acc = __builtin_fmaf(B[u].d, q8_dot(B[u], xv), acc);
+                }
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+        if (lane == 0) y[row] = acc;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_q8_gemv(const uint8_t* w, const uint16_t* x, float* y, int64_t n, int64_t k, hipStream_t s) {
+    const int64_t wgs = (n + kQ8Waves - 1) / kQ8Waves;
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(wgs, 2 * (int64_t)device_cu_count()));
+    hipLaunchKernelGGL(k_q8_gemv, dim3(grid), dim3(kQ8Waves * 64), (size_t)k * 2, s, w, x, y, n, (int)k);
+    return hipGetLastError();
+}
+
+}  // namespace q4

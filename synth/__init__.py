@@ -46,6 +46,19 @@ PROJ = (
     ("down", HIDDEN, FFN),
 )
 VOCAB = 151936
+# The small dense model the Q8_0 workload is shaped after (Qwen3 4B: hidden
+# 2,560, 32 query and 8 key/value heads of 128, MLP 9,728, 36 layers; from
+# that model's public configuration, which the pages do not give).
+Q8_LAYERS = 36
+Q8_PROJ = (
+    ("q", 4096, 2560),
+    ("k", 1024, 2560),
+    ("v", 1024, 2560),
+    ("o", 2560, 4096),
+    ("gate", 9728, 2560),
+    ("up", 9728, 2560),
+    ("down", 2560, 9728),
+)
 
 # Tensor kinds inside a stream id.
 T_W, T_X, T_R = 0, 1, 2  # weights, activations, residual stream
@@ -71,9 +84,7 @@ def _load():
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_LIB):
-                build()
-            lib = ctypes.CDLL(_LIB)
+            lib = ctypes.CDLL(build())  # rebuilt when gen.c is newer than the library
             u64, i64, vp = ctypes.c_uint64, ctypes.c_int64, ctypes.c_void_p
             lib.synth_f64_to_f16.argtypes = [ctypes.c_double]
             lib.synth_f64_to_f16.restype = ctypes.c_uint16
@@ -83,6 +94,7 @@ def _load():
             lib.synth_q4_0_rows.argtypes = [u64, u64, i64, i64, i64, vp]
             lib.synth_q4_0_row_list.argtypes = [u64, u64, i64, vp, i64, vp]
             lib.synth_f16_normal.argtypes = [u64, u64, i64, i64, vp]
+            lib.synth_q8_0_rows.argtypes = [u64, u64, i64, i64, i64, vp]
             _lib = lib
     return _lib
 
@@ -127,6 +139,19 @@ def q4_0_row_list(seed: int, stream: int, k: int, rows) -> np.ndarray:
     out = np.empty((r.size, row_bytes(k)), dtype=np.uint8)
     _load().synth_q4_0_row_list(seed, stream, k, r.ctypes.data, r.size, out.ctypes.data)
     return out
+
+
+def q8_0_rows(seed: int, stream: int, k: int, row_begin: int, row_count: int) -> np.ndarray:
+    """Packed Q8_0 rows [row_begin, row_begin+row_count) of a K-column matrix, uint8[rows, K/32*34]."""
+    assert k % 32 == 0
+    out = np.empty((row_count, k // 32 * 34), dtype=np.uint8)
+    _load().synth_q8_0_rows(seed, stream, k, row_begin, row_count, out.ctypes.data)
+    return out
+
+
+def q8_0(seed: int, stream: int, n: int, k: int) -> np.ndarray:
+    """A whole packed Q8_0 matrix of N rows and K columns, uint8[N, K/32*34]."""
+    return q8_0_rows(seed, stream, k, 0, n)
 
 
 def f16_normal(seed: int, stream: int, count: int, begin: int = 0) -> np.ndarray:

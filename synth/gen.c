@@ -26,6 +26,14 @@
  *       (so d is U[0.001, 0.02] rounded to the nearest f16),
  *     stored little-endian in bytes 0..1 of the block.
  *
+ * Q8_0 weights (34-byte blocks: an f16 scale, then 32 signed code bytes):
+ *   block g uses outputs 5g .. 5g+4 of the stream:
+ *     code bytes 0..31 = little-endian bytes of outputs 5g .. 5g+3
+ *       (every code uniform on -128..127, independently),
+ *     scale d = f16_rne(0.0001 + 0.0019 * u), u = (output(5g+4) >> 11) * 2^-53
+ *       (d uniform on [0.0001, 0.002], so code * d spans about +-0.25 like
+ *       the Q4_0 weights), stored little-endian in bytes 0..1.
+ *
  * f16 activations ~ N(0,1): element i uses the Box-Muller pair built from
  * outputs 2*(i/2) and 2*(i/2)+1:
  *     u1 = ((o0 >> 11) + 1) * 2^-53  in (0, 1]
@@ -112,6 +120,31 @@ void synth_q4_0_rows(uint64_t seed, uint64_t stream, int64_t k,
         for (int64_t b = 0; b < bpr; ++b) {
             uint64_t g = (uint64_t)((row_begin + r) * bpr + b);
             q4_0_block(s0, g, out + (r * bpr + b) * 18);
+        }
+    }
+}
+
+static void q8_0_block(uint64_t s0, uint64_t g, uint8_t* blk) {
+    for (int w = 0; w < 4; ++w) {
+        const uint64_t o = stream_at(s0, 5 * g + (uint64_t)w);
+        for (int i = 0; i < 8; ++i) blk[2 + 8 * w + i] = (uint8_t)(o >> (8 * i));
+    }
+    const double u = (double)(stream_at(s0, 5 * g + 4) >> 11) * 0x1.0p-53;
+    const uint16_t d = synth_f64_to_f16(0.0001 + 0.0019 * u);
+    blk[0] = (uint8_t)(d & 0xFF);
+    blk[1] = (uint8_t)(d >> 8);
+}
+
+/* Rows [row_begin, row_begin + row_count) of a K-column Q8_0 matrix. */
+void synth_q8_0_rows(uint64_t seed, uint64_t stream, int64_t k,
+                     int64_t row_begin, int64_t row_count, uint8_t* out) {
+    const uint64_t s0 = stream_state(seed, stream);
+    const int64_t bpr = k / 32;
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < row_count; ++r) {
+        for (int64_t b = 0; b < bpr; ++b) {
+            uint64_t g = (uint64_t)((row_begin + r) * bpr + b);
+            q8_0_block(s0, g, out + (r * bpr + b) * 34);
         }
     }
 }

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
         assert name in exported, name
         assert getattr(lib, name) is not None
     # nothing else of ours leaks out with default visibility
-    ours = {n for n in exported if n.startswith(("q4", "lm_head"))}
+    ours = {n for n in exported if n.startswith(("q4", "q8", "lm_head"))}
     assert ours == set(declared_symbols())
 
 
@@ -157,6 +157,25 @@ def test_lm_head_validation(lib):
     assert lib.lm_head_argmax(w, h, lg, lg + 8, 1000, 64, FAKE * 16, need, None) == q4.Q4_ERR_INVALID_ARG
     # k % 64 != 0 is not supported here
     assert lib.lm_head_argmax(w, h, lg, tok, 1000, 96, FAKE * 16, need, None) == q4.Q4_ERR_INVALID_ARG
+
+
+def test_q8_gemv_validation(lib):
+    w, x, y = FAKE, FAKE * 2, FAKE * 3
+    n, k = 1000, 96
+
+    def call(w=w, x=x, y=y, n=n, k=k):
+        return lib.q8_0_gemv(w, x, y, n, k, None)
+
+    assert call(w=None) == q4.Q4_ERR_INVALID_ARG
+    assert call(w=w + 2) == q4.Q4_ERR_MISALIGNED
+    assert call(x=x + 4) == q4.Q4_ERR_MISALIGNED
+    assert call(y=y + 2) == q4.Q4_ERR_MISALIGNED
+    assert call(k=80) == q4.Q4_ERR_INVALID_ARG
+    assert call(k=32768 + 32) == q4.Q4_ERR_INVALID_ARG
+    assert call(n=0) == q4.Q4_ERR_INVALID_ARG
+    # y over the weights (1000 rows x 102 bytes) or over x
+    assert call(y=w + 100000) == q4.Q4_ERR_INVALID_ARG
+    assert call(y=x) == q4.Q4_ERR_INVALID_ARG
 
 
 def test_gemv_handoff_validation(lib):

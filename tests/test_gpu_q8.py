@@ -1,0 +1,103 @@
+"""q8_0_gemv: the Q8_0 GEMV against the oracle, element by element within the
+bound, over shapes that cover odd block counts per row (rows that start 2 bytes
+into a dword), a single block, the largest K, ragged row counts, the matrix's
+last block on a dword boundary, and the Qwen3-4B-shaped projections."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import assert_parity, dev_f16, dev_u8, lib, say
+
+pytestmark = pytest.mark.gpu
+SEED = synth.DEFAULT_SEED
+
+
+def run(w_np, x_np):
+    q4 = lib()
+    y = q4.q8_0_gemv(dev_u8(w_np), dev_f16(x_np))
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("n,k", [(1, 32), (7, 32), (65, 96), (300, 160), (1000, 1024), (513, 2080),
+                                 (4096, 2560), (2560, 9728), (200, 32768), (9728, 2560)])
+def test_q8_parity(n, k):
+    w = synth.q8_0(SEED, 9300 + k % 1000, n, k)
+    x = synth.f16_normal(SEED, 9400 + n % 1000, k)
+    y = run(w, x)
+    y_ref, a_ref = oracle.q8_gemm_rows(w, k, x)
+    r = assert_parity(y, y_ref, a_ref, "q8 n=%d k=%d" % (n, k))
+    say("q8 n=%d k=%d max err/a %.3g" % (n, k, r))
+
+
+def test_q8_last_block_ends_the_allocation():
+    """The matrix copied to the end of a larger buffer's exact length: the last
+    block starts on a dword, so its 36-byte window would pass the end."""
+    n, k = 33, 96  # 99 blocks: the last one starts at 98 * 34, a multiple of 4
+    w = synth.q8_0(SEED, 9501, n, k)
+    assert ((n * (k // 32) - 1) * 34) % 4 == 0
+    x = synth.f16_normal(SEED, 9502, k)
+    buf = torch.empty(w.size, dtype=torch.uint8, device="cuda")
+    buf.copy_(torch.from_numpy(w.ravel()))
+    q4 = lib()
+    y = q4.q8_0_gemv(buf.view(n, -1), dev_f16(x))
+    torch.cuda.synchronize()
+    y_ref, a_ref = oracle.q8_gemm_rows(w, k, x)
+    assert_parity(y.cpu().numpy(), y_ref, a_ref, "q8 tail")
+
+
+def test_q8_rows_are_position_independent():
+    """A row's output does not depend on where it sits: the same rows shuffled give the same bits."""
+    n, k = 777, 2560
+    w = synth.q8_0(SEED, 9601, n, k)
+    x = synth.f16_normal(SEED, 9602, k)
+    perm = np.random.default_rng(5).permutation(n)
+    y1 = run(w, x)
+    y2 = run(np.ascontiguousarray(w[perm]), x)
+    assert np.array_equal(y1[perm], y2)
+
+
+def test_q8_extreme_codes_and_scales():
+    """Every code -128 or +127 with large scales: the f16 decode of the codes stays exact."""
+    n, k = 64, 512
+    rng = np.random.default_rng(7)
+    codes = rng.choice([-128, 127], size=(n, k))
+    d = rng.choice([-8.0, 4.0, 0.5], size=(n, k // 32)).astype(np.float16)
+    import q4_encode
+    w = q4_encode.encode_q8(codes, d.view(np.uint16))
+    x = synth.f16_normal(SEED, 9701, k)
+    y = run(w, x)
+    y_ref, a_ref = oracle.q8_gemm_rows(w, k, x)
+    assert_parity(y, y_ref, a_ref, "q8 extremes")
+
+
+def test_q8_graph_replay_matches_eager():
+    """Three Q8_0 GEMVs captured in a HIP graph: every replay (with eager work
+    and synchronisations between them) gives the eager bits."""
+    q4 = lib()
+    shapes = [(1024, 2560), (2560, 4096), (333, 96)]
+    ws = [dev_u8(synth.q8_0(SEED, 9800 + i, n, k)) for i, (n, k) in enumerate(shapes)]
+    xs = [dev_f16(synth.f16_normal(SEED, 9900 + i, k)) for i, (n, k) in enumerate(shapes)]
+    ys = [torch.empty(n, dtype=torch.float32, device="cuda") for n, _ in shapes]
+    eager = [q4.q8_0_gemv(w, x).clone() for w, x in zip(ws, xs)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for w, x, y in zip(ws, xs, ys):
+            q4.q8_0_gemv(w, x, y)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for w, x, y in zip(ws, xs, ys):
+            q4.q8_0_gemv(w, x, y)
+    for rep in range(3):
+        for y in ys:
+            y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for y, e in zip(ys, eager):
+            assert torch.equal(y, e), rep
+        q4.q8_0_gemv(ws[0], xs[1][:2560].contiguous())  # eager work between replays
+        torch.cuda.synchronize()

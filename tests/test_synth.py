@@ -62,3 +62,16 @@ def test_sweep_shapes():
     assert len(sw) == 448
     assert synth.sweep_weight_bytes() == 13_400_801_280
     assert synth.row_bytes(5120) == 2880 and synth.row_bytes(17408) == 9792
+
+
+def test_q8_0_rows():
+    """Q8_0 bytes: addressable rows, codes over the whole signed byte range, d in [1e-4, 2e-3]."""
+    full = synth.q8_0(synth.DEFAULT_SEED, 77, 40, 256)
+    assert full.shape == (40, 8 * 34)
+    assert np.array_equal(synth.q8_0_rows(synth.DEFAULT_SEED, 77, 256, 13, 5), full[13:18])
+    blocks = full.reshape(-1, 34)
+    d = blocks[:, :2].copy().view(np.float16).astype(np.float64).ravel()
+    assert d.min() >= 0.0001 - 1e-7 and d.max() <= 0.002 + 1e-6
+    codes = blocks[:, 2:].view(np.int8).ravel().astype(np.int64)
+    assert codes.min() == -128 and codes.max() == 127
+    assert abs(codes.mean()) < 3.0
