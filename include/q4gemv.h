@@ -316,6 +316,39 @@ Q4_API q4_status q4_0_gemv_batch_plan(const q4_gemv_desc* descs, int count, void
  * results do not depend on how the chunks were handed out. */
 Q4_API q4_status q4_0_gemv_batch(const q4_gemv_plan* plan, void* stream);
 
+/* Host-side handle of a Q8_0 GEMV list plan.  Filled by q8_0_gemv_batch_plan;
+ * plain data, may be copied. */
+typedef struct q8_gemv_plan {
+    void* device;  /* the caller's device buffer holding the plan */
+    int count;     /* number of GEMVs */
+    int max_k;     /* largest k in the list */
+    int grid;      /* workgroups of one launch */
+    int reserved;
+} q8_gemv_plan;
+
+/* Device bytes q8_0_gemv_batch_plan needs for `count` descriptors on the
+ * current device (0 when count is outside [1, 1<<20]). */
+Q4_API size_t q8_0_gemv_batch_plan_bytes(int count);
+
+/*
+ * A list of Q8_0 GEMVs (descriptors as q4_gemv_desc, with w holding n rows of
+ * k/32 Q8_0 blocks) run as one launch, for the layers of a small dense model
+ * in one submission.  Validate `count` host-side descriptors (each as
+ * q8_0_gemv requires; no output may overlap another output, an input or the
+ * plan), lay the rows out in units of 16 rows of one GEMV, cut them into one
+ * contiguous byte-balanced range per workgroup, and copy descriptors and
+ * ranges into the caller's device buffer `plan_buf` (16-byte aligned, at least
+ * q8_0_gemv_batch_plan_bytes(count) bytes).  The copy is enqueued on `stream`
+ * and has completed when this call returns.  The plan holds no counters: its
+ * launches may be captured in a HIP graph and may overlap in time when their
+ * outputs do not.  Every row's result equals q8_0_gemv's bit for bit.
+ */
+Q4_API q4_status q8_0_gemv_batch_plan(const q4_gemv_desc* descs, int count, void* plan_buf, size_t plan_bytes,
+                                      q8_gemv_plan* plan, void* stream);
+
+/* Run every GEMV of a Q8_0 plan in one launch on `stream`. */
+Q4_API q4_status q8_0_gemv_batch(const q8_gemv_plan* plan, void* stream);
+
 /* Host-side handle of a small-M batch plan.  Filled by
  * q4_0_gemm_smallm_batch_plan; plain data, may be copied. */
 typedef struct q4_gemm_plan {

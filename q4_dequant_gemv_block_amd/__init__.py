@@ -37,7 +37,8 @@ Q4_OP_LM_HEAD_NORM_ARGMAX = 5
 # Every symbol include/q4gemv.h declares.
 EXPORTS = (
     "q4_abi_version", "q4_last_error", "q4_workspace_bytes", "q4_0_gemv", "q4_0_gemm_smallm",
-    "q4_0_gemm_prefill", "lm_head_argmax", "lm_head_norm_argmax", "lm_head_verify", "q4_0_gemv_handoff", "q8_0_gemv",
+    "q4_0_gemm_prefill", "lm_head_argmax", "lm_head_norm_argmax", "lm_head_verify", "q4_0_gemv_handoff", "q8_0_gemv", "q8_0_gemv_batch_plan_bytes",
+    "q8_0_gemv_batch_plan", "q8_0_gemv_batch",
     "q4_0_gemv_batch_plan_bytes", "q4_0_gemv_batch_plan",
     "q4_0_gemm_smallm_batch_plan_bytes", "q4_0_gemm_smallm_batch_plan", "q4_0_gemm_smallm_batch",
     "q4_0_gemm_prefill_batch_plan_bytes", "q4_0_gemm_prefill_batch_plan", "q4_0_gemm_prefill_batch",
@@ -59,6 +60,11 @@ class GemvDesc(ctypes.Structure):
 class GemvPlan(ctypes.Structure):
     _fields_ = [("device", ctypes.c_void_p), ("count", ctypes.c_int), ("max_k", ctypes.c_int),
                 ("grid", ctypes.c_int), ("nchunks", ctypes.c_int), ("flags", ctypes.c_int)]
+
+
+class Q8Plan(ctypes.Structure):
+    _fields_ = [("device", ctypes.c_void_p), ("count", ctypes.c_int), ("max_k", ctypes.c_int),
+                ("grid", ctypes.c_int), ("reserved", ctypes.c_int)]
 
 
 _lib = None
@@ -90,6 +96,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lm_head_verify.restype = st
     lib.q8_0_gemv.argtypes = [vp, vp, vp, i64, i64, vp]
     lib.q8_0_gemv.restype = ctypes.c_int
+    lib.q8_0_gemv_batch_plan_bytes.argtypes = [ctypes.c_int]
+    lib.q8_0_gemv_batch_plan_bytes.restype = ctypes.c_size_t
+    lib.q8_0_gemv_batch_plan.argtypes = [ctypes.POINTER(GemvDesc), ctypes.c_int, vp, ctypes.c_size_t,
+                                         ctypes.POINTER(Q8Plan), vp]
+    lib.q8_0_gemv_batch_plan.restype = ctypes.c_int
+    lib.q8_0_gemv_batch.argtypes = [ctypes.POINTER(Q8Plan), vp]
+    lib.q8_0_gemv_batch.restype = ctypes.c_int
     lib.q4_0_gemv_handoff.argtypes = [vp, vp, vp, vp, i64, i64, vp]
     lib.q4_0_gemv_handoff.restype = ctypes.c_int
     lib.lm_head_norm_argmax.argtypes = [vp, vp, vp, ctypes.c_float, vp, vp, vp, i64, i64, vp, ctypes.c_size_t, vp]
@@ -392,6 +405,39 @@ class GemvBatch:
 
     def __call__(self, stream=None):
         _check(load_library().q4_0_gemv_batch(ctypes.byref(self.plan), _stream(stream)))
+
+
+class Q8Batch:
+    """A list of Q8_0 GEMVs (w, x, y), w uint8 [N, K/32*34], planned once and run as
+    one launch per call."""
+
+    def __init__(self, items, stream=None):
+        items = list(items)
+        descs = (GemvDesc * len(items))()
+        self._keep = []
+        for i, (w, x, y) in enumerate(items):
+            k = x.shape[-1]
+            if w.dim() != 2 or w.shape[1] != q8_row_bytes(k):
+                raise ValueError("descriptor %d: w must be uint8 [N, K/32*34]" % i)
+            n = w.shape[0]
+            if y.numel() != n:
+                raise ValueError("descriptor %d: y must hold N=%d floats" % (i, n))
+            descs[i] = GemvDesc(_ptr(w, torch.uint8, "w"), _ptr(x, torch.float16, "x"),
+                                _ptr(y, torch.float32, "y"), n, k)
+            self._keep.append((w, x, y))
+        lib = load_library()
+        dev = items[0][0].device if items else torch.device("cuda")
+        self.plan = Q8Plan()
+        with torch.cuda.device(dev):  # the ranges are cut for this device's compute units
+            nbytes = int(lib.q8_0_gemv_batch_plan_bytes(len(items)))
+            if nbytes == 0:
+                _check(Q4_ERR_INVALID_ARG)
+            self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+            _check(lib.q8_0_gemv_batch_plan(descs, len(items), self.buffer.data_ptr(), self.buffer.numel(),
+                                            ctypes.byref(self.plan), _stream(stream)))
+
+    def __call__(self, stream=None):
+        _check(load_library().q8_0_gemv_batch(ctypes.byref(self.plan), _stream(stream)))
 
 
 class SmallMBatch:

@@ -436,6 +436,75 @@ q4_status q4_0_gemv_batch(const q4_gemv_plan* plan, void* stream) {
     return hip_status(e, "q4_0_gemv_batch launch");
 }
 
+size_t q8_0_gemv_batch_plan_bytes(int count) {
+    if (count < 1 || count > (1 << 20)) return 0;
+    const int64_t grid_max = 2 * (int64_t)q4::device_cu_count();
+    return (size_t)count * sizeof(q4::Q8Desc) + (size_t)(grid_max + 1) * sizeof(int64_t);
+}
+
+q4_status q8_0_gemv_batch_plan(const q4_gemv_desc* descs, int count, void* plan_buf, size_t plan_bytes,
+                               q8_gemv_plan* plan, void* stream) {
+    const char* fn = "q8_0_gemv_batch_plan";
+    if (!plan || !plan_buf || !descs) return fail(Q4_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (count < 1 || count > (1 << 20)) return fail(Q4_ERR_INVALID_ARG, "%s: count = %d outside [1, 1<<20]", fn, count);
+    std::vector<Range> outs, ins;
+    std::vector<q4::Q8Desc> dev(count);
+    int max_k = 0;
+    for (int i = 0; i < count; ++i) {
+        const q4_gemv_desc& d = descs[i];
+        q4_status st = check_shape(fn, 1, 1, d.n, d.k);
+        if (st) return fail(st, "%s: descriptor %d: %s", fn, i, std::string(g_err).c_str());
+        if (d.k > q4::kFastMaxK) return fail(Q4_ERR_INVALID_ARG, "%s: descriptor %d: k above %lld", fn, i, (long long)q4::kFastMaxK);
+        if (!d.w || !d.x || !d.y) return fail(Q4_ERR_INVALID_ARG, "%s: descriptor %d: null tensor pointer", fn, i);
+        if (!aligned(d.w, 4) || !aligned(d.x, 16) || !aligned(d.y, 4))
+            return fail(Q4_ERR_MISALIGNED, "%s: descriptor %d: w must be 4-, x 16-, y 4-byte aligned", fn, i);
+        outs.push_back(range(d.y, (size_t)d.n * 4));
+        ins.push_back(range(d.w, (size_t)(d.n * (d.k / 32) * 34)));
+        ins.push_back(range(d.x, (size_t)d.k * 2));
+        dev[i] = q4::Q8Desc{static_cast<const uint8_t*>(d.w), static_cast<const uint16_t*>(d.x), d.y, d.n,
+                            (int32_t)d.k, 0, 0};
+        max_k = std::max<int>(max_k, (int)d.k);
+    }
+    std::sort(outs.begin(), outs.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+    for (size_t i = 1; i < outs.size(); ++i)
+        if (outs[i].lo < outs[i - 1].hi) return fail(Q4_ERR_INVALID_ARG, "%s: two outputs overlap", fn);
+    for (const Range& r : ins)
+        for (const Range& o : outs)  // (lists of a model's layers: a few hundred entries)
+            if (overlap(o, r)) return fail(Q4_ERR_INVALID_ARG, "%s: an output overlaps an input", fn);
+    std::vector<int64_t> wg_begin;
+    const int grid = q4::q8_batch_layout(dev.data(), count, &wg_begin);
+    const size_t need = (size_t)count * sizeof(q4::Q8Desc) + wg_begin.size() * sizeof(int64_t);
+    if (plan_bytes < need) return fail(Q4_ERR_WORKSPACE, "%s: plan buffer of %zu bytes needed", fn, need);
+    if (!aligned(plan_buf, 16)) return fail(Q4_ERR_MISALIGNED, "%s: plan buffer must be 16-byte aligned", fn);
+    const Range rp = range(plan_buf, need);
+    for (const Range& r : outs)
+        if (overlap(rp, r)) return fail(Q4_ERR_INVALID_ARG, "%s: the plan buffer overlaps a tensor", fn);
+    for (const Range& r : ins)
+        if (overlap(rp, r)) return fail(Q4_ERR_INVALID_ARG, "%s: the plan buffer overlaps a tensor", fn);
+    std::vector<uint8_t> host(need);
+    std::memcpy(host.data(), dev.data(), dev.size() * sizeof(q4::Q8Desc));
+    std::memcpy(host.data() + dev.size() * sizeof(q4::Q8Desc), wg_begin.data(), wg_begin.size() * sizeof(int64_t));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(plan_buf, host.data(), need, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_status(e, "q8_0_gemv_batch_plan copy");
+    plan->device = plan_buf;
+    plan->count = count;
+    plan->max_k = max_k;
+    plan->grid = grid;
+    plan->reserved = 0;
+    return ok();
+}
+
+q4_status q8_0_gemv_batch(const q8_gemv_plan* plan, void* stream) {
+    if (!plan || !plan->device) return fail(Q4_ERR_INVALID_ARG, "q8_0_gemv_batch: null plan");
+    if (plan->count < 1 || plan->max_k < 32 || plan->max_k > q4::kFastMaxK || plan->max_k % 32 != 0 || plan->grid < 1)
+        return fail(Q4_ERR_INVALID_ARG, "q8_0_gemv_batch: plan was not filled by q8_0_gemv_batch_plan");
+    const hipError_t e = q4::launch_q8_batch(plan->device, plan->count, plan->grid, plan->max_k,
+                                             static_cast<hipStream_t>(stream));
+    return hip_status(e, "q8_0_gemv_batch launch");
+}
+
 size_t q4_0_gemm_smallm_batch_plan_bytes(int count) {
     if (count < 1 || count > (1 << 20)) return 0;
     return (size_t)count * sizeof(q4::SmDesc);

@@ -19,6 +19,8 @@
 #include "q4_launch.h"
 
 #include <algorithm>
+#include <climits>
+#include <vector>
 
 namespace q4 {
 
@@ -109,7 +111,119 @@ __global__ void __launch_bounds__(kQ8Waves * 64) k_q8_gemv(const uint8_t* __rest
     }
 }
 
+// Rows r0 and r0 + 1 (when has1) of one GEMV by one wave: the loads of both
+// rows' blocks go out before their math, so each lane has up to four blocks
+// in flight.  Each row keeps the association of k_q8_gemv (blocks in lane
+// order, the same butterfly), so its bits equal the single call's.
+__device__ __forceinline__ void q8_two_rows(const Q8Desc& D, int64_t r0, bool has1, const u4* __restrict__ xs,
+                                            int lane) {
+    const int nb = D.k >> 5;
+    const int64_t rb = (int64_t)nb * kQ8BlockBytes;
+    const uint8_t* end = D.w + D.n * rb;
+    const uint8_t* w0 = D.w + r0 * rb;
+    const uint8_t* w1 = w0 + rb;
+    float a0 = 0.0f, a1 = 0.0f;
+    for (int b0 = lane; b0 < nb; b0 += 64 * kQ8Unroll) {
+        Q8Block B0[kQ8Unroll], B1[kQ8Unroll];
+#pragma unroll
+        for (int u = 0; u < kQ8Unroll; ++u) {
+            const int b = b0 + 64 * u;
+            if (b < nb) {
+                load_q8(w0 + (int64_t)b * kQ8BlockBytes, end, B0[u]);
+                if (has1) load_q8(w1 + (int64_t)b * kQ8BlockBytes, end, B1[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kQ8Unroll; ++u) {
+            const int b = b0 + 64 * u;
+            if (b < nb) {
+                const u4 xv[4] = {xs[4 * b], xs[4 * b + 1], xs[4 * b + 2], xs[4 * b + 3]};
+                a0 = __builtin_fmaf(B0[u].d, q8_dot(B0[u], xv), a0);
+                if (has1) a1 = __builtin_fmaf(B1[u].d, q8_dot(B1[u], xv), a1);
+            }
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        a0 += __shfl_xor(a0, o, 64);
+        a1 += __shfl_xor(a1, o, 64);
+    }
+    if (lane == 0) {
+        D.y[r0] = a0;
+        if (has1) D.y[r0 + 1] = a1;
+    }
+}
+
+// A GEMV list: workgroup g takes units [wg_begin[g], wg_begin[g+1]) in list
+// order (a unit: kQ8UnitRows rows of one GEMV, two per wave), staging a
+// GEMV's x into LDS when its first unit comes up.
+__global__ void __launch_bounds__(kQ8Waves * 64) k_q8_batch(const Q8Desc* __restrict__ descs, int count,
+                                                           const int64_t* __restrict__ wg_begin) {
+    static_assert(kQ8UnitRows == 2 * kQ8Waves, "two rows per wave per unit");
+    extern __shared__ u4 xs[];
+    const int64_t u_lo = wg_begin[blockIdx.x], u_hi = wg_begin[blockIdx.x + 1];
+    if (u_lo >= u_hi) return;  // the whole workgroup: no barrier is reached
+    int lo = 0, hi = count - 1;  // the GEMV holding unit u_lo: last d with unit_begin <= u_lo
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (descs[mid].unit_begin <= u_lo)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    int d = lo;
+    Q8Desc D = descs[d];
+    int64_t next = d + 1 < count ? descs[d + 1].unit_begin : INT64_MAX;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < (D.k >> 3); i += blockDim.x) xs[i] = ((g_u4*)D.x)[i];
+    __syncthreads();
+    for (int64_t u = u_lo; u < u_hi; ++u) {
+        if (u >= next) {  // the next GEMV (every GEMV has at least one unit)
+            ++d;
+            D = descs[d];
+            next = d + 1 < count ? descs[d + 1].unit_begin : INT64_MAX;
+            __syncthreads();  // every wave is done with the previous x
+            for (int i = threadIdx.x; i < (D.k >> 3); i += blockDim.x) xs[i] = ((g_u4*)D.x)[i];
+            __syncthreads();
+        }
+        const int64_t r0 = (u - D.unit_begin) * kQ8UnitRows + 2 * wave;
+        if (r0 < D.n) q8_two_rows(D, r0, r0 + 1 < D.n, xs, lane);
+    }
+}
+
 }  // namespace
+
+int q8_batch_layout(Q8Desc* descs, int count, std::vector<int64_t>* wg_begin) {
+    int64_t units = 0;
+    double total = 0.0;
+    for (int i = 0; i < count; ++i) {
+        descs[i].unit_begin = units;
+        units += (descs[i].n + kQ8UnitRows - 1) / kQ8UnitRows;
+        total += (double)descs[i].n * (descs[i].k / 32) * kQ8BlockBytes;
+    }
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(units, 2 * (int64_t)device_cu_count()));
+    // workgroup g starts at the first unit whose bytes-before reach total * g / grid
+    wg_begin->assign(grid + 1, units);
+    (*wg_begin)[0] = 0;
+    int g = 1;
+    double before = 0.0;
+    for (int i = 0; i < count && g < grid; ++i) {
+        const double row = (double)(descs[i].k / 32) * kQ8BlockBytes;
+        const int64_t nu = (descs[i].n + kQ8UnitRows - 1) / kQ8UnitRows;
+        for (int64_t j = 0; j < nu && g < grid; ++j) {
+            while (g < grid && before >= total * g / grid) (*wg_begin)[g++] = descs[i].unit_begin + j;
+            before += row * (double)std::min<int64_t>(kQ8UnitRows, descs[i].n - j * kQ8UnitRows);
+        }
+    }
+    return grid;
+}
+
+hipError_t launch_q8_batch(const void* plan, int count, int grid, int max_k, hipStream_t s) {
+    const Q8Desc* descs = static_cast<const Q8Desc*>(plan);
+    const int64_t* wg_begin = reinterpret_cast<const int64_t*>(descs + count);
+    hipLaunchKernelGGL(k_q8_batch, dim3(grid), dim3(kQ8Waves * 64), (size_t)max_k * 2, s, descs, count, wg_begin);
+    return hipGetLastError();
+}
 
 hipError_t launch_q8_gemv(const uint8_t* w, const uint16_t* x, float* y, int64_t n, int64_t k, hipStream_t s) {
     const int64_t wgs = (n + kQ8Waves - 1) / kQ8Waves;

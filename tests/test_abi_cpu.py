@@ -178,6 +178,33 @@ def test_q8_gemv_validation(lib):
     assert call(y=x) == q4.Q4_ERR_INVALID_ARG
 
 
+def test_q8_batch_validation(lib):
+    D = q4.GemvDesc
+    plan = q4.Q8Plan()
+    assert lib.q8_0_gemv_batch_plan_bytes(0) == 0
+    nbytes = lib.q8_0_gemv_batch_plan_bytes(2)
+    assert nbytes >= 2 * 48 + 16
+    buf = FAKE * 64
+    good = (D * 2)(D(FAKE, FAKE * 2, FAKE * 4, 8, 96), D(FAKE * 8, FAKE * 2, FAKE * 6, 8, 64))
+    # the two outputs overlap
+    arr = (D * 2)(D(FAKE, FAKE * 2, FAKE * 4, 8, 96), D(FAKE * 8, FAKE * 2, FAKE * 4 + 16, 8, 64))
+    assert lib.q8_0_gemv_batch_plan(arr, 2, buf, nbytes, ctypes.byref(plan), None) == q4.Q4_ERR_INVALID_ARG
+    # an output over another descriptor's weights
+    arr = (D * 2)(D(FAKE, FAKE * 2, FAKE * 8 + 64, 8, 96), D(FAKE * 8, FAKE * 2, FAKE * 6, 8, 64))
+    assert lib.q8_0_gemv_batch_plan(arr, 2, buf, nbytes, ctypes.byref(plan), None) == q4.Q4_ERR_INVALID_ARG
+    # k not a multiple of 32, k too large, w misaligned
+    for bad in (D(FAKE, FAKE * 2, FAKE * 4, 8, 80), D(FAKE, FAKE * 2, FAKE * 4, 8, 32768 + 32),
+                D(FAKE + 2, FAKE * 2, FAKE * 4, 8, 96)):
+        arr = (D * 1)(bad)
+        assert lib.q8_0_gemv_batch_plan(arr, 1, buf, nbytes, ctypes.byref(plan), None) != q4.Q4_OK
+    # plan buffer too small, misaligned, over a tensor; null plan at launch
+    assert lib.q8_0_gemv_batch_plan(good, 2, buf, 16, ctypes.byref(plan), None) == q4.Q4_ERR_WORKSPACE
+    assert lib.q8_0_gemv_batch_plan(good, 2, buf + 8, nbytes, ctypes.byref(plan), None) == q4.Q4_ERR_MISALIGNED
+    assert lib.q8_0_gemv_batch_plan(good, 2, FAKE * 4, nbytes, ctypes.byref(plan), None) == q4.Q4_ERR_INVALID_ARG
+    assert lib.q8_0_gemv_batch(None, None) == q4.Q4_ERR_INVALID_ARG
+    assert lib.q8_0_gemv_batch(ctypes.byref(q4.Q8Plan()), None) == q4.Q4_ERR_INVALID_ARG
+
+
 def test_gemv_handoff_validation(lib):
     w, x, r, out = FAKE, FAKE * 2, FAKE * 3, FAKE * 4
     n, k = 1000, 64

@@ -101,3 +101,69 @@ def test_q8_graph_replay_matches_eager():
             assert torch.equal(y, e), rep
         q4.q8_0_gemv(ws[0], xs[1][:2560].contiguous())  # eager work between replays
         torch.cuda.synchronize()
+
+
+def _batch_items(shapes, base):
+    ws = [synth.q8_0(SEED, base + i, n, k) for i, (n, k) in enumerate(shapes)]
+    xs = [synth.f16_normal(SEED, base + 500 + i, k) for i, (n, k) in enumerate(shapes)]
+    items = [(dev_u8(w), dev_f16(x), torch.full((n,), float("nan"), dtype=torch.float32, device="cuda"))
+             for w, x, (n, k) in zip(ws, xs, shapes)]
+    return ws, xs, items
+
+
+def test_q8_batch_equals_single_calls():
+    """A mixed list in one launch: every row bit-equal to q8_0_gemv's, every row within the bound."""
+    q4 = lib()
+    shapes = [(1, 32), (15, 96), (16, 160), (17, 2080), (300, 2560), (1024, 2560), (33, 32768), (2560, 9728),
+              (5, 64), (4096, 2560)]
+    ws, xs, items = _batch_items(shapes, 10100)
+    q4.Q8Batch(items)()
+    torch.cuda.synchronize()
+    for i, ((w_d, x_d, y), w, x, (n, k)) in enumerate(zip(items, ws, xs, shapes)):
+        single = q4.q8_0_gemv(w_d, x_d)
+        torch.cuda.synchronize()
+        assert torch.equal(y, single), (i, n, k)
+        y_ref, a_ref = oracle.q8_gemm_rows(w, k, x)
+        assert_parity(y.cpu().numpy(), y_ref, a_ref, "q8 batch %d" % i)
+
+
+def test_q8_batch_model_layers():
+    """Two layers of the Qwen3-4B-shaped projections (14 GEMVs) as one launch, against the oracle."""
+    q4 = lib()
+    shapes = [(n, k) for _ in range(2) for (_, n, k) in synth.Q8_PROJ]
+    ws, xs, items = _batch_items(shapes, 10300)
+    batch = q4.Q8Batch(items)
+    say("q8 batch grid %d over %d GEMVs" % (batch.plan.grid, len(items)))
+    batch()
+    torch.cuda.synchronize()
+    for i, ((_, _, y), w, x, (n, k)) in enumerate(zip(items, ws, xs, shapes)):
+        y_ref, a_ref = oracle.q8_gemm_rows(w, k, x)
+        assert_parity(y.cpu().numpy(), y_ref, a_ref, "q8 layers %d" % i)
+
+
+def test_q8_batch_graph_replay():
+    """The batch launch captured in a HIP graph: every replay gives the eager bits."""
+    q4 = lib()
+    shapes = [(1024, 2560), (2560, 4096), (97, 1056)]
+    _, _, items = _batch_items(shapes, 10500)
+    batch = q4.Q8Batch(items)
+    batch()
+    torch.cuda.synchronize()
+    eager = [y.clone() for _, _, y in items]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        batch()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        batch()
+    for rep in range(3):
+        for _, _, y in items:
+            y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for (_, _, y), e in zip(items, eager):
+            assert torch.equal(y, e), rep
+        batch()  # eager work between replays
+        torch.cuda.synchronize()
