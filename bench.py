@@ -185,8 +185,9 @@ def bench_sweep(args):
     tok = torch.empty(1, dtype=torch.int32, device="cuda")
     wsp = torch.empty(q4.workspace_bytes(q4.Q4_OP_LM_HEAD_NORM_ARGMAX, 1, synth.VOCAB, synth.HIDDEN),
                       dtype=torch.uint8, device="cuda")
+    # (the first launches after the sweep's run settle slowly: warm up with 200)
     lm_ms = time_steps(lambda: q4.lm_head_norm_argmax(wl, hl, gl, NORM_EPS, lg, tok, workspace=wsp),
-                       max(args.steps, 20), args.warmup)
+                       max(args.steps, 20) * 10, 200)
     out = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),

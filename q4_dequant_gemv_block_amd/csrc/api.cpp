@@ -438,7 +438,7 @@ q4_status q4_0_gemv_batch(const q4_gemv_plan* plan, void* stream) {
 
 size_t q8_0_gemv_batch_plan_bytes(int count) {
     if (count < 1 || count > (1 << 20)) return 0;
-    const int64_t grid_max = 2 * (int64_t)q4::device_cu_count();
+    const int64_t grid_max = q4::kQ8WgPerCu * (int64_t)q4::device_cu_count();
     return (size_t)count * sizeof(q4::Q8Desc) + (size_t)(grid_max + 1) * sizeof(int64_t);
 }
 

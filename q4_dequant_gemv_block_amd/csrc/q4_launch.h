@@ -142,6 +142,7 @@ struct Q8Desc {
     int64_t unit_begin;  // index of this GEMV's first unit in the list
 };
 constexpr int kQ8UnitRows = 16;
+constexpr int kQ8WgPerCu = 2;  // the launch grid is at most this many workgroups per compute unit
 // Fills unit_begin and the workgroups' unit ranges (contiguous, byte-balanced); returns the grid.
 int q8_batch_layout(Q8Desc* descs, int count, std::vector<int64_t>* wg_begin);
 hipError_t launch_q8_batch(const void* plan, int count, int grid, int max_k, hipStream_t s);

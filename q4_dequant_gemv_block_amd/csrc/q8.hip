@@ -201,7 +201,7 @@ int q8_batch_layout(Q8Desc* descs, int count, std::vector<int64_t>* wg_begin) {
         units += (descs[i].n + kQ8UnitRows - 1) / kQ8UnitRows;
         total += (double)descs[i].n * (descs[i].k / 32) * kQ8BlockBytes;
     }
-    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(units, 2 * (int64_t)device_cu_count()));
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(units, kQ8WgPerCu * (int64_t)device_cu_count()));
     // workgroup g starts at the first unit whose bytes-before reach total * g / grid
     wg_begin->assign(grid + 1, units);
     (*wg_begin)[0] = 0;
