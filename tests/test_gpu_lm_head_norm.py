@@ -74,7 +74,7 @@ def full_check(w, h, g, eps=EPS, what=""):
 # shapes across the kernel's variants: narrow and wide, the four-row engine
 # (k % 1024 == 0, k >= 4096) and the other, fixed and per-k activation stride
 @pytest.mark.parametrize("n,k", [(70, 64), (3001, 1024), (4099, 4096), (1000, 960), (20000, 5120),
-                                 (2500, 17408), (1200, 20480)])
+                                 (2500, 17408), (1200, 20480), (300, 32768)])
 def test_norm_parity(n, k):
     w = synth.q4_0(SEED, 8100 + k, n, k)
     h = synth.f16_scaled_normal(SEED, 8200 + k, k, 4.0)

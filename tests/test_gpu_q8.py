@@ -167,3 +167,18 @@ def test_q8_batch_graph_replay():
             assert torch.equal(y, e), rep
         batch()  # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_q8_vocabulary_sized_rows_sampled():
+    """151,936 rows x 2,560 (a Q8_0 LM head of the small dense model's width):
+    sampled rows, the first and the last included, against the oracle."""
+    n, k = synth.VOCAB, 2560
+    q4 = lib()
+    w = synth.q8_0(SEED, 10701, n, k)
+    x = synth.f16_normal(SEED, 10702, k)
+    y = q4.q8_0_gemv(dev_u8(w), dev_f16(x))
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    rows = np.unique(np.concatenate([[0, 1, n - 2, n - 1], np.random.default_rng(11).integers(0, n, 3000)]))
+    y_ref, a_ref = oracle.q8_gemm_rows(np.ascontiguousarray(w[rows]), k, x)
+    assert_parity(y[rows], y_ref, a_ref, "q8 vocabulary rows")
