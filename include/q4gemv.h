@@ -316,6 +316,29 @@ Q4_API q4_status q4_0_gemv_batch_plan(const q4_gemv_desc* descs, int count, void
  * results do not depend on how the chunks were handed out. */
 Q4_API q4_status q4_0_gemv_batch(const q4_gemv_plan* plan, void* stream);
 
+/*
+ * Make the GEMV of a planned list whose descriptor named the output `y` the
+ * stage hand-off (the end of a
+ * device's layer range, whose hidden state goes to the next participant as
+ * f16: aipolix.com en-us page, section "A model can be larger than any one
+ * browser can hold"): from the next q4_0_gemv_batch launch on, that GEMV
+ * writes h16[n] = binary16(residual[n] + y[n]) (nearest-even; the binary32 y
+ * of the same kernel and association, residual added in binary32) instead of
+ * its binary32 y, which is no longer written.  So a stage's whole layer range,
+ * ending in the hand-off, is one launch.
+ *   residual : NULL (zero) or n binary32, 4-byte aligned
+ *   h16      : n binary16, 2-byte aligned; must not overlap any tensor of the
+ *              list (other than that GEMV's own former y), the residual or the
+ *              plan
+ * (The plan keeps its own order of the list, so the GEMV is named by its
+ * output.)  Reads the plan's descriptors back, checks, and writes the changed
+ * one; the copies are enqueued on `stream` and complete before the call
+ * returns.  No GEMV with output y in the plan: Q4_ERR_INVALID_ARG.
+ * Launches of the plan must not be running meanwhile.
+ */
+Q4_API q4_status q4_0_gemv_batch_handoff(const q4_gemv_plan* plan, const float* y, const float* residual,
+                                         void* h16, void* stream);
+
 /* Host-side handle of a Q8_0 GEMV list plan.  Filled by q8_0_gemv_batch_plan;
  * plain data, may be copied. */
 typedef struct q8_gemv_plan {

@@ -42,7 +42,7 @@ EXPORTS = (
     "q4_0_gemv_batch_plan_bytes", "q4_0_gemv_batch_plan",
     "q4_0_gemm_smallm_batch_plan_bytes", "q4_0_gemm_smallm_batch_plan", "q4_0_gemm_smallm_batch",
     "q4_0_gemm_prefill_batch_plan_bytes", "q4_0_gemm_prefill_batch_plan", "q4_0_gemm_prefill_batch",
-    "q4_0_gemv_batch",
+    "q4_0_gemv_batch", "q4_0_gemv_batch_handoff",
 )
 
 
@@ -96,6 +96,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lm_head_verify.restype = st
     lib.q8_0_gemv.argtypes = [vp, vp, vp, i64, i64, vp]
     lib.q8_0_gemv.restype = ctypes.c_int
+    lib.q4_0_gemv_batch_handoff.argtypes = [ctypes.POINTER(GemvPlan), vp, vp, vp, vp]
+    lib.q4_0_gemv_batch_handoff.restype = ctypes.c_int
     lib.q8_0_gemv_batch_plan_bytes.argtypes = [ctypes.c_int]
     lib.q8_0_gemv_batch_plan_bytes.restype = ctypes.c_size_t
     lib.q8_0_gemv_batch_plan.argtypes = [ctypes.POINTER(GemvDesc), ctypes.c_int, vp, ctypes.c_size_t,
@@ -402,6 +404,22 @@ class GemvBatch:
             self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=dev)
             _check(lib.q4_0_gemv_batch_plan(descs, len(items), self.buffer.data_ptr(), self.buffer.numel(),
                                             ctypes.byref(self.plan), _stream(stream)))
+
+    def set_handoff(self, index: int, h16: torch.Tensor, residual: torch.Tensor | None = None, stream=None):
+        """Make item `index` of the list the stage hand-off: it writes float16 h16 [N] =
+        residual + W x (rounded once) instead of its float32 y."""
+        n = self._keep[index][2].numel()
+        if h16.numel() != n:
+            raise ValueError("h16 must hold N=%d float16 values" % n)
+        rp = 0
+        if residual is not None:
+            if residual.numel() != n:
+                raise ValueError("residual must hold N=%d float32 values" % n)
+            rp = _ptr(residual, torch.float32, "residual")
+        y = self._keep[index][2]
+        _check(load_library().q4_0_gemv_batch_handoff(ctypes.byref(self.plan), _ptr(y, torch.float32, "y"), rp,
+                                                      _ptr(h16, torch.float16, "h16"), _stream(stream)))
+        self._keep.append((h16, residual))
 
     def __call__(self, stream=None):
         _check(load_library().q4_0_gemv_batch(ctypes.byref(self.plan), _stream(stream)))

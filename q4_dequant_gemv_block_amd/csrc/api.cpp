@@ -436,6 +436,51 @@ q4_status q4_0_gemv_batch(const q4_gemv_plan* plan, void* stream) {
     return hip_status(e, "q4_0_gemv_batch launch");
 }
 
+q4_status q4_0_gemv_batch_handoff(const q4_gemv_plan* plan, const float* y, const float* residual, void* h16,
+                                  void* stream) {
+    const char* fn = "q4_0_gemv_batch_handoff";
+    if (!plan || !plan->device) return fail(Q4_ERR_INVALID_ARG, "%s: null plan", fn);
+    if (plan->count < 1 || plan->max_k < 64 || plan->max_k > q4::kFastMaxK || plan->grid < 1 ||
+        plan->nchunks < plan->grid || (plan->flags & ~q4::kPlanQuad) != 0)
+        return fail(Q4_ERR_INVALID_ARG, "%s: plan was not filled by q4_0_gemv_batch_plan", fn);
+    if (!y || !h16) return fail(Q4_ERR_INVALID_ARG, "%s: null y or h16", fn);
+    if (!aligned(h16, 2)) return fail(Q4_ERR_MISALIGNED, "%s: h16 must be 2-byte aligned", fn);
+    if (residual && !aligned(residual, 4)) return fail(Q4_ERR_MISALIGNED, "%s: residual must be 4-byte aligned", fn);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    std::vector<q4::PlanDesc> dev(plan->count);
+    uint8_t* table = static_cast<uint8_t*>(plan->device) + sizeof(q4::SchedHead);
+    hipError_t e = hipMemcpyAsync(dev.data(), table, dev.size() * sizeof(q4::PlanDesc), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_status(e, "q4_0_gemv_batch_handoff read-back");
+    int index = -1;
+    for (int i = 0; i < plan->count; ++i)
+        if (dev[i].y == y) index = i;
+    if (index < 0) return fail(Q4_ERR_INVALID_ARG, "%s: no GEMV of the plan writes that y", fn);
+    q4::PlanDesc& d = dev[index];
+    const Range rh = range(h16, (size_t)d.n * 2);
+    const Range rr = residual ? range(residual, (size_t)d.n * 4) : Range{0, 0};
+    const Range rp = range(plan->device, sizeof(q4::SchedHead) + dev.size() * sizeof(q4::PlanDesc));
+    if (overlap(rh, rp) || (residual && (overlap(rh, rr) || overlap(rr, rp))))
+        return fail(Q4_ERR_INVALID_ARG, "%s: h16, the residual and the plan must not overlap", fn);
+    for (int i = 0; i < plan->count; ++i) {
+        const q4::PlanDesc& o = dev[i];
+        const Range rw = range(o.w, (size_t)(o.n * row_bytes(o.k))), rx = range(o.x, (size_t)o.k * 2);
+        if (overlap(rh, rw) || overlap(rh, rx))
+            return fail(Q4_ERR_INVALID_ARG, "%s: h16 overlaps an input of descriptor %d", fn, i);
+        if (i != index) {
+            const Range ry = o.h16 ? range(o.y, (size_t)o.n * 2) : range(o.y, (size_t)o.n * 4);
+            if (overlap(rh, ry) || (residual && overlap(rr, ry)))
+                return fail(Q4_ERR_INVALID_ARG, "%s: h16 or the residual overlaps the output of descriptor %d", fn, i);
+        }
+    }
+    d.y = static_cast<float*>(h16);
+    d.residual = residual;
+    d.h16 = 1;
+    e = hipMemcpyAsync(table + (size_t)index * sizeof(q4::PlanDesc), &d, sizeof(d), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    return hip_status(e, "q4_0_gemv_batch_handoff copy");
+}
+
 size_t q8_0_gemv_batch_plan_bytes(int count) {
     if (count < 1 || count > (1 << 20)) return 0;
     const int64_t grid_max = q4::kQ8WgPerCu * (int64_t)q4::device_cu_count();

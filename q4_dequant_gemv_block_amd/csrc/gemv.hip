@@ -664,8 +664,10 @@ struct Live {
     const uint8_t* w;
     const uint16_t* x;
     float* y;
+    const float* residual;
     int32_t n, k, npl, steps;
     int64_t cost_begin;
+    bool h16;
 };
 
 __device__ __forceinline__ Live live_of(const PlanDesc& p) {
@@ -678,6 +680,8 @@ __device__ __forceinline__ Live live_of(const PlanDesc& p) {
     l.npl = p.npl;
     l.steps = (int32_t)p.steps;
     l.cost_begin = p.cost_begin;
+    l.residual = p.residual;
+    l.h16 = p.h16 != 0;
     return l;
 }
 
@@ -842,9 +846,10 @@ k_sweep(const PlanDesc* __restrict__ descs, int count, SchedHead* head, const Sc
             if (u.jb + 1 >= Dc.npl) {  // last unit of the wave's rows in this step
                 eng.finish(u.s, acc, [&](int64_t row, float v) {
                     if (row < Dc.n) {
-                        if constexpr (H16) {
+                        if (H16 || (BATCH && Dc.h16)) {
                             // stage hand-off: binary16 (nearest-even) of residual + y, into y's place
-                            const float t = nrm.residual ? v + nrm.residual[row] : v;
+                            const float* res = H16 ? nrm.residual : Dc.residual;
+                            const float t = res ? v + res[row] : v;
                             reinterpret_cast<uint16_t*>(Dc.y)[row] = (uint16_t)half_bits(t);
                             return;
                         }
@@ -993,6 +998,9 @@ static PlanDesc single_desc(const uint8_t* w, const uint16_t* x, float* y, int64
     d.npl = npl_of(k);
     d.steps = (n + sh.rows_per_step() - 1) / sh.rows_per_step();
     d.cost_begin = 0;
+    d.residual = nullptr;
+    d.h16 = 0;
+    d.reserved = 0;
     return d;
 }
 

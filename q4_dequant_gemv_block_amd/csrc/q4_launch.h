@@ -20,6 +20,9 @@ struct PlanDesc {
     int32_t npl;         // pairs per lane: ceil(k/64 / 16)
     int64_t steps;       // row steps of the engine's rows per step
     int64_t cost_begin;  // sum of steps*npl over the earlier descriptors
+    const float* residual;  // stage hand-off (batch): r [n] or null
+    int32_t h16;            // 1: this GEMV is the stage hand-off, y holds binary16(r + y) [n]
+    int32_t reserved;
 };
 
 // Head of a batch plan's schedule (device memory, first bytes of the plan).

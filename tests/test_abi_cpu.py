@@ -348,3 +348,15 @@ def test_prefill_batch_plan_validation(lib):
     assert lib.q4_0_gemm_prefill_batch_plan(good, 2, 2, buf, 8, ctypes.byref(plan), None) == q4.Q4_ERR_WORKSPACE
     assert lib.q4_0_gemm_prefill_batch_plan(good, 2, 2, FAKE * 8, nbytes, ctypes.byref(plan), None) == q4.Q4_ERR_INVALID_ARG
     assert lib.q4_0_gemm_prefill_batch(ctypes.byref(q4.PrefillPlan()), None) == q4.Q4_ERR_INVALID_ARG
+
+
+def test_batch_handoff_validation(lib):
+    plan = q4.GemvPlan()
+    y = FAKE * 4
+    assert lib.q4_0_gemv_batch_handoff(None, y, None, FAKE, None) == q4.Q4_ERR_INVALID_ARG
+    assert lib.q4_0_gemv_batch_handoff(ctypes.byref(plan), y, None, FAKE, None) == q4.Q4_ERR_INVALID_ARG
+    plan.device, plan.count, plan.max_k, plan.grid, plan.nchunks, plan.flags = FAKE * 64, 3, 5120, 256, 300, 0
+    assert lib.q4_0_gemv_batch_handoff(ctypes.byref(plan), None, None, FAKE, None) == q4.Q4_ERR_INVALID_ARG
+    assert lib.q4_0_gemv_batch_handoff(ctypes.byref(plan), y, None, None, None) == q4.Q4_ERR_INVALID_ARG
+    assert lib.q4_0_gemv_batch_handoff(ctypes.byref(plan), y, None, FAKE + 1, None) == q4.Q4_ERR_MISALIGNED
+    assert lib.q4_0_gemv_batch_handoff(ctypes.byref(plan), y, FAKE + 2, FAKE, None) == q4.Q4_ERR_MISALIGNED

@@ -45,7 +45,8 @@ def _read_plan(batch):
     nxt, done, nchunks, grid = np.frombuffer(raw[:16].tobytes(), dtype=np.int32)
     count = batch.plan.count
     desc_t = np.dtype([("w", "<u8"), ("x", "<u8"), ("y", "<u8"), ("n", "<i8"), ("k", "<i4"), ("npl", "<i4"),
-                       ("steps", "<i8"), ("cost_begin", "<i8")])
+                       ("steps", "<i8"), ("cost_begin", "<i8"), ("residual", "<u8"), ("h16", "<i4"),
+                       ("reserved", "<i4")])
     chunk_t = np.dtype([("d0", "<i4"), ("s0", "<i4"), ("c_end", "<i8")])
     descs = np.frombuffer(raw[16:16 + count * desc_t.itemsize].tobytes(), dtype=desc_t)
     off = 16 + count * desc_t.itemsize
@@ -133,3 +134,40 @@ def test_full_decode_sweep_sampled():
         y_ref, a_ref = oracle.gemm_rows(w_rows, k, x)
         worst = max(worst, assert_parity(y, y_ref, a_ref, "sweep stream %d" % sw))
     say("sweep worst err/a", worst)
+
+
+def test_stage_handoff_in_the_batch():
+    """One layer of the sweep shapes as a stage whose last GEMV (the down
+    projection) is the hand-off: the other outputs equal the plain batch's bit
+    for bit, the hand-off writes binary16(y + residual) of the plain batch's y
+    (numpy's float32 add and float16 rounding) and leaves its old y alone; the
+    plain GEMV of a second plan is unaffected."""
+    q4 = lib()
+    seed = synth.DEFAULT_SEED
+    shapes = [(n, k) for (_, n, k) in synth.PROJ]
+    ws = [dev_u8(synth.q4_0(seed, 11000 + i, n, k)) for i, (n, k) in enumerate(shapes)]
+    xs = [dev_f16(synth.f16_normal(seed, 11100 + i, k)) for i, (n, k) in enumerate(shapes)]
+    ys_plain = [torch.empty(n, dtype=torch.float32, device="cuda") for n, _ in shapes]
+    ys_stage = [torch.empty(n, dtype=torch.float32, device="cuda") for n, _ in shapes]
+    last = len(shapes) - 1
+    n_last = shapes[last][0]
+    r = torch.from_numpy(4.0 * synth.f16_normal(seed, 11200, n_last).astype(np.float32)).cuda()
+    h16 = torch.full((n_last,), float("nan"), dtype=torch.float16, device="cuda")
+    plain = q4.GemvBatch(list(zip(ws, xs, ys_plain)))
+    stage = q4.GemvBatch(list(zip(ws, xs, ys_stage)))
+    ys_stage[last].fill_(float("nan"))
+    stage.set_handoff(last, h16, r)
+    say("stage hand-off: %d GEMVs, hand-off n=%d" % (len(shapes), n_last))
+    for _ in range(2):  # a second launch of each: the plans stay as they are
+        plain()
+        stage()
+    torch.cuda.synchronize()
+    for i in range(last):
+        assert torch.equal(ys_plain[i], ys_stage[i]), i
+    assert torch.isnan(ys_stage[last]).all()
+    want = (ys_plain[last].cpu().numpy() + r.cpu().numpy()).astype(np.float16)
+    assert np.array_equal(h16.cpu().numpy().view(np.uint16), want.view(np.uint16))
+    # the same as the single hand-off call
+    single = q4.q4_0_gemv_handoff(ws[last], xs[last], r)
+    torch.cuda.synchronize()
+    assert torch.equal(single.view(torch.int16), h16.view(torch.int16))
