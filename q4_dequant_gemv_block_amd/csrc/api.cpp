@@ -513,9 +513,11 @@ q4_status q8_0_gemv_batch_plan(const q4_gemv_desc* descs, int count, void* plan_
     std::sort(outs.begin(), outs.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
     for (size_t i = 1; i < outs.size(); ++i)
         if (outs[i].lo < outs[i - 1].hi) return fail(Q4_ERR_INVALID_ARG, "%s: two outputs overlap", fn);
-    for (const Range& r : ins)
-        for (const Range& o : outs)  // (lists of a model's layers: a few hundred entries)
-            if (overlap(o, r)) return fail(Q4_ERR_INVALID_ARG, "%s: an output overlaps an input", fn);
+    for (const Range& r : ins) {  // outputs are sorted and disjoint: only the neighbours of r.lo can overlap r
+        auto it = std::upper_bound(outs.begin(), outs.end(), r.lo, [](uintptr_t v, const Range& o) { return v < o.lo; });
+        if ((it != outs.end() && overlap(*it, r)) || (it != outs.begin() && overlap(*(it - 1), r)))
+            return fail(Q4_ERR_INVALID_ARG, "%s: an output overlaps an input", fn);
+    }
     std::vector<int64_t> wg_begin;
     const int grid = q4::q8_batch_layout(dev.data(), count, &wg_begin);
     const size_t need = (size_t)count * sizeof(q4::Q8Desc) + wg_begin.size() * sizeof(int64_t);
