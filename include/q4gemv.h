@@ -358,13 +358,16 @@ Q4_API size_t q8_0_gemv_batch_plan_bytes(int count);
  * k/32 Q8_0 blocks) run as one launch, for the layers of a small dense model
  * in one submission.  Validate `count` host-side descriptors (each as
  * q8_0_gemv requires; no output may overlap another output, an input or the
- * plan), lay the rows out in units of 16 rows of one GEMV, cut them into one
- * contiguous byte-balanced range per workgroup, and copy descriptors and
- * ranges into the caller's device buffer `plan_buf` (16-byte aligned, at least
- * q8_0_gemv_batch_plan_bytes(count) bytes).  The copy is enqueued on `stream`
- * and has completed when this call returns.  The plan holds no counters: its
- * launches may be captured in a HIP graph and may overlap in time when their
- * outputs do not.  Every row's result equals q8_0_gemv's bit for bit.
+ * plan), lay the rows out in units of 16 rows of one GEMV, give every
+ * workgroup one contiguous byte-balanced range of the first 85 % of the bytes
+ * and hand the remaining units out in chunks through a counter, and copy the
+ * counters (zero), descriptors and ranges into the caller's device buffer
+ * `plan_buf` (16-byte aligned, at least q8_0_gemv_batch_plan_bytes(count)
+ * bytes).  The copy is enqueued on `stream` and has completed when this call
+ * returns.  Launches of one plan must not overlap in time (they share its
+ * counters; the last workgroup of a launch sets them back to zero, which also
+ * makes the launch safe to capture in a HIP graph).  Every row's result
+ * equals q8_0_gemv's bit for bit.
  */
 Q4_API q4_status q8_0_gemv_batch_plan(const q4_gemv_desc* descs, int count, void* plan_buf, size_t plan_bytes,
                                       q8_gemv_plan* plan, void* stream);

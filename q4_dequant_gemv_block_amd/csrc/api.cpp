@@ -484,7 +484,7 @@ q4_status q4_0_gemv_batch_handoff(const q4_gemv_plan* plan, const float* y, cons
 size_t q8_0_gemv_batch_plan_bytes(int count) {
     if (count < 1 || count > (1 << 20)) return 0;
     const int64_t grid_max = q4::kQ8WgPerCu * (int64_t)q4::device_cu_count();
-    return (size_t)count * sizeof(q4::Q8Desc) + (size_t)(grid_max + 1) * sizeof(int64_t);
+    return sizeof(q4::Q8Head) + (size_t)count * sizeof(q4::Q8Desc) + (size_t)(grid_max + 1) * sizeof(int64_t);
 }
 
 q4_status q8_0_gemv_batch_plan(const q4_gemv_desc* descs, int count, void* plan_buf, size_t plan_bytes,
@@ -519,8 +519,9 @@ q4_status q8_0_gemv_batch_plan(const q4_gemv_desc* descs, int count, void* plan_
             return fail(Q4_ERR_INVALID_ARG, "%s: an output overlaps an input", fn);
     }
     std::vector<int64_t> wg_begin;
-    const int grid = q4::q8_batch_layout(dev.data(), count, &wg_begin);
-    const size_t need = (size_t)count * sizeof(q4::Q8Desc) + wg_begin.size() * sizeof(int64_t);
+    q4::Q8Head head{};
+    const int grid = q4::q8_batch_layout(dev.data(), count, &wg_begin, &head);
+    const size_t need = sizeof(head) + (size_t)count * sizeof(q4::Q8Desc) + wg_begin.size() * sizeof(int64_t);
     if (plan_bytes < need) return fail(Q4_ERR_WORKSPACE, "%s: plan buffer of %zu bytes needed", fn, need);
     if (!aligned(plan_buf, 16)) return fail(Q4_ERR_MISALIGNED, "%s: plan buffer must be 16-byte aligned", fn);
     const Range rp = range(plan_buf, need);
@@ -529,8 +530,10 @@ q4_status q8_0_gemv_batch_plan(const q4_gemv_desc* descs, int count, void* plan_
     for (const Range& r : ins)
         if (overlap(rp, r)) return fail(Q4_ERR_INVALID_ARG, "%s: the plan buffer overlaps a tensor", fn);
     std::vector<uint8_t> host(need);
-    std::memcpy(host.data(), dev.data(), dev.size() * sizeof(q4::Q8Desc));
-    std::memcpy(host.data() + dev.size() * sizeof(q4::Q8Desc), wg_begin.data(), wg_begin.size() * sizeof(int64_t));
+    std::memcpy(host.data(), &head, sizeof(head));
+    std::memcpy(host.data() + sizeof(head), dev.data(), dev.size() * sizeof(q4::Q8Desc));
+    std::memcpy(host.data() + sizeof(head) + dev.size() * sizeof(q4::Q8Desc), wg_begin.data(),
+                wg_begin.size() * sizeof(int64_t));
     const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipMemcpyAsync(plan_buf, host.data(), need, hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);

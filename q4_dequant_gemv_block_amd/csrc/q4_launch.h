@@ -132,9 +132,16 @@ hipError_t launch_lm_head(const uint8_t* w, const uint16_t* h, float* logits, in
                           int64_t n, int64_t k, uint64_t* keys, hipStream_t s);
 // Q8_0 GEMV (q8.hip): any k % 32 == 0 up to kFastMaxK, w 4-byte aligned, x 16-byte aligned.
 hipError_t launch_q8_gemv(const uint8_t* w, const uint16_t* x, float* y, int64_t n, int64_t k, hipStream_t s);
-// A Q8_0 GEMV list in one launch.  The plan in device memory: `count` Q8Desc,
-// then grid + 1 int64 unit indices (workgroup g takes units [b[g], b[g+1]));
-// a unit is kQ8UnitRows consecutive rows of one GEMV.
+// A Q8_0 GEMV list in one launch.  The plan in device memory: a Q8Head, then
+// `count` Q8Desc, then grid + 1 int64 unit indices (workgroup g first takes
+// units [b[g], b[g+1])); a unit is kQ8UnitRows consecutive rows of one GEMV.
+// Units from dyn_begin on are handed out `chunk` at a time through `next`;
+// `done` counts finished workgroups, the last one sets both back to zero.
+struct Q8Head {
+    uint32_t next, done;
+    int32_t chunk, reserved;
+    int64_t dyn_begin, dyn_end;
+};
 struct Q8Desc {
     const uint8_t* w;
     const uint16_t* x;
@@ -146,9 +153,10 @@ struct Q8Desc {
 };
 constexpr int kQ8UnitRows = 16;
 constexpr int kQ8WgPerCu = 2;  // the launch grid is at most this many workgroups per compute unit
-// Fills unit_begin and the workgroups' unit ranges (contiguous, byte-balanced); returns the grid.
-int q8_batch_layout(Q8Desc* descs, int count, std::vector<int64_t>* wg_begin);
-hipError_t launch_q8_batch(const void* plan, int count, int grid, int max_k, hipStream_t s);
+// Fills unit_begin, the head's dynamic part and the workgroups' first unit
+// ranges (contiguous, byte-balanced); returns the grid.
+int q8_batch_layout(Q8Desc* descs, int count, std::vector<int64_t>* wg_begin, Q8Head* head);
+hipError_t launch_q8_batch(void* plan, int count, int grid, int max_k, hipStream_t s);
 // A GEMV whose epilogue writes binary16(residual + y) (residual may be null).
 hipError_t launch_gemv_handoff(const uint8_t* w, const uint16_t* x, const float* residual, uint16_t* h16,
                                int64_t n, int64_t k, hipStream_t s);

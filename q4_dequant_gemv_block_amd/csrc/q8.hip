@@ -29,6 +29,7 @@ namespace {
 constexpr int kQ8BlockBytes = 34;
 constexpr int kQ8Waves = 8;   // waves per workgroup
 constexpr int kQ8Unroll = 2;  // blocks per lane loaded before their math
+constexpr double kQ8StaticShare = 0.85;  // of a list's bytes, split statically before the chunks
 
 typedef __attribute__((address_space(1))) const uint16_t g_u16;
 
@@ -154,46 +155,65 @@ __device__ __forceinline__ void q8_two_rows(const Q8Desc& D, int64_t r0, bool ha
     }
 }
 
-// A GEMV list: workgroup g takes units [wg_begin[g], wg_begin[g+1]) in list
-// order (a unit: kQ8UnitRows rows of one GEMV, two per wave), staging a
-// GEMV's x into LDS when its first unit comes up.
-__global__ void __launch_bounds__(kQ8Waves * 64) k_q8_batch(const Q8Desc* __restrict__ descs, int count,
-                                                           const int64_t* __restrict__ wg_begin) {
+// A GEMV list: workgroup g first takes units [wg_begin[g], wg_begin[g+1]) in
+// list order (a unit: kQ8UnitRows rows of one GEMV, two per wave), then
+// chunks of the remaining units from the counter as it runs out of work, so
+// that workgroups that stream faster take more.  A GEMV's x is staged into
+// LDS when a unit of it comes up after a unit of another GEMV.
+__global__ void __launch_bounds__(kQ8Waves * 64) k_q8_batch(Q8Head* head, const Q8Desc* __restrict__ descs,
+                                                           int count, const int64_t* __restrict__ wg_begin) {
     static_assert(kQ8UnitRows == 2 * kQ8Waves, "two rows per wave per unit");
     extern __shared__ u4 xs[];
-    const int64_t u_lo = wg_begin[blockIdx.x], u_hi = wg_begin[blockIdx.x + 1];
-    if (u_lo >= u_hi) return;  // the whole workgroup: no barrier is reached
-    int lo = 0, hi = count - 1;  // the GEMV holding unit u_lo: last d with unit_begin <= u_lo
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (descs[mid].unit_begin <= u_lo)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    int d = lo;
-    Q8Desc D = descs[d];
-    int64_t next = d + 1 < count ? descs[d + 1].unit_begin : INT64_MAX;
+    __shared__ uint32_t ticket;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int i = threadIdx.x; i < (D.k >> 3); i += blockDim.x) xs[i] = ((g_u4*)D.x)[i];
-    __syncthreads();
-    for (int64_t u = u_lo; u < u_hi; ++u) {
-        if (u >= next) {  // the next GEMV (every GEMV has at least one unit)
-            ++d;
-            D = descs[d];
-            next = d + 1 < count ? descs[d + 1].unit_begin : INT64_MAX;
-            __syncthreads();  // every wave is done with the previous x
-            for (int i = threadIdx.x; i < (D.k >> 3); i += blockDim.x) xs[i] = ((g_u4*)D.x)[i];
-            __syncthreads();
+    int d = -1;  // the GEMV whose x is in LDS
+    Q8Desc D;
+    int64_t d_end = 0;  // one past its last unit
+    auto run = [&](int64_t u_lo, int64_t u_hi) {
+        for (int64_t u = u_lo; u < u_hi; ++u) {
+            if (d < 0 || u < D.unit_begin || u >= d_end) {
+                int lo = 0, hi = count - 1;  // last GEMV with unit_begin <= u
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (descs[mid].unit_begin <= u)
+                        lo = mid;
+                    else
+                        hi = mid - 1;
+                }
+                d = lo;
+                D = descs[d];
+                d_end = d + 1 < count ? descs[d + 1].unit_begin : INT64_MAX;
+                __syncthreads();  // every wave is done with the previous x
+                for (int i = threadIdx.x; i < (D.k >> 3); i += blockDim.x) xs[i] = ((g_u4*)D.x)[i];
+                __syncthreads();
+            }
+            const int64_t r0 = (u - D.unit_begin) * kQ8UnitRows + 2 * wave;
+            if (r0 < D.n) q8_two_rows(D, r0, r0 + 1 < D.n, xs, lane);
         }
-        const int64_t r0 = (u - D.unit_begin) * kQ8UnitRows + 2 * wave;
-        if (r0 < D.n) q8_two_rows(D, r0, r0 + 1 < D.n, xs, lane);
+    };
+    run(wg_begin[blockIdx.x], wg_begin[blockIdx.x + 1]);
+    const int64_t dyn_begin = head->dyn_begin, dyn_end = head->dyn_end;
+    const int chunk = head->chunk;
+    for (;;) {  // ends when the counter passes the last chunk: every workgroup gets there
+        if (threadIdx.x == 0) ticket = atomicAdd(&head->next, 1u);
+        __syncthreads();
+        const int64_t u0 = dyn_begin + (int64_t)__builtin_amdgcn_readfirstlane(ticket) * chunk;
+        __syncthreads();  // every wave has read the ticket before the next one is taken
+        if (u0 >= dyn_end) break;
+        run(u0, std::min<int64_t>(u0 + chunk, dyn_end));
+    }
+    if (threadIdx.x == 0) {
+        __threadfence();  // this workgroup's tickets come first
+        if (atomicAdd(&head->done, 1u) == gridDim.x - 1) {
+            atomicExch(&head->next, 0u);
+            atomicExch(&head->done, 0u);
+        }
     }
 }
 
 }  // namespace
 
-int q8_batch_layout(Q8Desc* descs, int count, std::vector<int64_t>* wg_begin) {
+int q8_batch_layout(Q8Desc* descs, int count, std::vector<int64_t>* wg_begin, Q8Head* head) {
     int64_t units = 0;
     double total = 0.0;
     for (int i = 0; i < count; ++i) {
@@ -202,26 +222,54 @@ int q8_batch_layout(Q8Desc* descs, int count, std::vector<int64_t>* wg_begin) {
         total += (double)descs[i].n * (descs[i].k / 32) * kQ8BlockBytes;
     }
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(units, kQ8WgPerCu * (int64_t)device_cu_count()));
-    // workgroup g starts at the first unit whose bytes-before reach total * g / grid
-    wg_begin->assign(grid + 1, units);
+    // the first kQ8StaticShare of the bytes go out as one contiguous range per
+    // workgroup (workgroup g from the first unit whose bytes-before reach
+    // static * g / grid); the units after them go out in chunks
+    const double share = total * kQ8StaticShare;
+    int64_t dyn_begin = units;
+    double static_bytes = total;
+    {
+        double before = 0.0;
+        for (int i = 0; i < count && dyn_begin == units; ++i) {
+            const double row = (double)(descs[i].k / 32) * kQ8BlockBytes;
+            const int64_t nu = (descs[i].n + kQ8UnitRows - 1) / kQ8UnitRows;
+            for (int64_t j = 0; j < nu; ++j) {
+                if (before >= share) {
+                    dyn_begin = descs[i].unit_begin + j;
+                    static_bytes = before;
+                    break;
+                }
+                before += row * (double)std::min<int64_t>(kQ8UnitRows, descs[i].n - j * kQ8UnitRows);
+            }
+        }
+    }
+    wg_begin->assign(grid + 1, dyn_begin);
     (*wg_begin)[0] = 0;
     int g = 1;
     double before = 0.0;
     for (int i = 0; i < count && g < grid; ++i) {
         const double row = (double)(descs[i].k / 32) * kQ8BlockBytes;
         const int64_t nu = (descs[i].n + kQ8UnitRows - 1) / kQ8UnitRows;
-        for (int64_t j = 0; j < nu && g < grid; ++j) {
-            while (g < grid && before >= total * g / grid) (*wg_begin)[g++] = descs[i].unit_begin + j;
+        for (int64_t j = 0; j < nu && g < grid && descs[i].unit_begin + j < dyn_begin; ++j) {
+            while (g < grid && before >= static_bytes * g / grid) (*wg_begin)[g++] = descs[i].unit_begin + j;
             before += row * (double)std::min<int64_t>(kQ8UnitRows, descs[i].n - j * kQ8UnitRows);
         }
     }
+    head->next = 0;
+    head->done = 0;
+    head->chunk = (int32_t)std::max<int64_t>(1, (units - dyn_begin) / (4 * (int64_t)grid));
+    head->reserved = 0;
+    head->dyn_begin = dyn_begin;
+    head->dyn_end = units;
     return grid;
 }
 
-hipError_t launch_q8_batch(const void* plan, int count, int grid, int max_k, hipStream_t s) {
-    const Q8Desc* descs = static_cast<const Q8Desc*>(plan);
+hipError_t launch_q8_batch(void* plan, int count, int grid, int max_k, hipStream_t s) {
+    Q8Head* head = static_cast<Q8Head*>(plan);
+    const Q8Desc* descs = reinterpret_cast<const Q8Desc*>(head + 1);
     const int64_t* wg_begin = reinterpret_cast<const int64_t*>(descs + count);
-    hipLaunchKernelGGL(k_q8_batch, dim3(grid), dim3(kQ8Waves * 64), (size_t)max_k * 2, s, descs, count, wg_begin);
+    hipLaunchKernelGGL(k_q8_batch, dim3(grid), dim3(kQ8Waves * 64), (size_t)max_k * 2, s, head, descs, count,
+                       wg_begin);
     return hipGetLastError();
 }
 
