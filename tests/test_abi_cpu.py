@@ -360,3 +360,11 @@ def test_batch_handoff_validation(lib):
     assert lib.q4_0_gemv_batch_handoff(ctypes.byref(plan), y, None, None, None) == q4.Q4_ERR_INVALID_ARG
     assert lib.q4_0_gemv_batch_handoff(ctypes.byref(plan), y, None, FAKE + 1, None) == q4.Q4_ERR_MISALIGNED
     assert lib.q4_0_gemv_batch_handoff(ctypes.byref(plan), y, FAKE + 2, FAKE, None) == q4.Q4_ERR_MISALIGNED
+
+
+def test_header_is_plain_c(tmp_path):
+    """The boundary header compiles as C99 (pedantic), with no C++ or HIP types."""
+    src = tmp_path / "use.c"
+    src.write_text('#include "q4gemv.h"\nint main(void) { return q4_abi_version() == Q4_ABI_VERSION ? 0 : 1; }\n')
+    subprocess.check_call(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only",
+                           "-I", os.path.dirname(HEADER), str(src)])
