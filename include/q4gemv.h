@@ -25,7 +25,8 @@
  *     the call returns.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
  *     void*; NULL means the null stream).  No call synchronizes the host,
- *     except q4_0_gemv_batch_plan (see there).
+ *     except the four ..._batch_plan calls and q4_0_gemv_batch_handoff (see
+ *     there).
  *   - Outputs are overwritten.  Outputs must not overlap any input.
  *   - Arguments are validated on the host before anything is enqueued; on an
  *     error nothing has been launched and the output is untouched.
