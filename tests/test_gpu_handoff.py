@@ -72,3 +72,20 @@ def test_handoff_out_of_place_and_into_preallocated():
     q4.q4_0_gemv_handoff(w, x, r, out=out)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), out.view(torch.int16))
+
+
+@pytest.mark.parametrize("n,k,scale", [(1, 64, 4.0), (3, 1024, 3.0e4), (129, 4096, 1.0e-6)])
+def test_handoff_edges(n, k, scale):
+    """A single row; residuals near the top of binary16's range; residuals far
+    below the outputs."""
+    q4 = lib()
+    w = synth.q4_0(SEED, 9300 + n, n, k)
+    x = synth.f16_normal(SEED, 9301, k)
+    r = (scale * synth.f16_normal(SEED, 9302, n)).astype(np.float32)
+    r = np.clip(r, -60000.0, 60000.0).astype(np.float32)
+    w_d, x_d = dev_u8(w), dev_f16(x)
+    h16 = q4.q4_0_gemv_handoff(w_d, x_d, torch.from_numpy(r).cuda())
+    y = q4.q4_0_gemv(w_d, x_d)
+    torch.cuda.synchronize()
+    want = (y.cpu().numpy() + r).astype(np.float16)
+    assert np.array_equal(h16.cpu().numpy().view(np.uint16), want.view(np.uint16))

@@ -121,3 +121,22 @@ def test_full_vocab_norm():
     g = synth.norm_gain(SEED, 8702, k)
     say("lm_head_norm full vocab")
     full_check(w, h, g, what="full vocab")
+
+
+@pytest.mark.parametrize("case", ["one_row", "large_eps", "single_nonzero"])
+def test_norm_degenerate_cases(case):
+    """One vocabulary row; eps far above mean(h^2) (x scaled down by it); a hidden
+    state with one nonzero element (x there = +-sqrt(k) g, zero elsewhere)."""
+    n, k = (1, 1024) if case == "one_row" else (700, 2048)
+    w = synth.q4_0(SEED, 8801, n, k)
+    h = synth.f16_scaled_normal(SEED, 8802, k, 4.0)
+    eps = EPS
+    if case == "large_eps":
+        eps = 1.0e4
+    if case == "single_nonzero":
+        h = np.zeros(k, np.float16)
+        h[123] = np.float16(-3.0)
+    g = synth.norm_gain(SEED, 8803, k)
+    logits, token, x = full_check(w, h, g, eps, what=case)
+    if case == "single_nonzero":
+        assert np.count_nonzero(x & 0x7FFF) == 1

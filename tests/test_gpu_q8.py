@@ -182,3 +182,13 @@ def test_q8_vocabulary_sized_rows_sampled():
     rows = np.unique(np.concatenate([[0, 1, n - 2, n - 1], np.random.default_rng(11).integers(0, n, 3000)]))
     y_ref, a_ref = oracle.q8_gemm_rows(np.ascontiguousarray(w[rows]), k, x)
     assert_parity(y[rows], y_ref, a_ref, "q8 vocabulary rows")
+
+
+@pytest.mark.parametrize("n,k", [(1, 32768), (1, 32), (2, 33 * 32)])
+def test_q8_single_rows(n, k):
+    """One or two rows: the largest K, a single block, an odd block count."""
+    w = synth.q8_0(SEED, 10800 + n, n, k)
+    x = synth.f16_normal(SEED, 10801, k)
+    y = run(w, x)
+    y_ref, a_ref = oracle.q8_gemm_rows(w, k, x)
+    assert_parity(y, y_ref, a_ref, "q8 n=%d k=%d" % (n, k))
