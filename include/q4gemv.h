@@ -394,9 +394,11 @@ Q4_API size_t q4_0_gemm_smallm_batch_plan_bytes(int count);
 
 /*
  * A list of small-M GEMMs with the same m, run as one launch: the verify pass
- * of a speculative draft over a whole layer stack, one submit per token
- * (aipolix.com en-us page, sections "Speculation is used to amortize network
- * round trips" and "One submit per token").  Descriptor i names w (n rows of
+ * of a speculative draft over a whole layer stack (aipolix.com en-us page,
+ * section "Speculation is used to amortize network round trips"), issued as
+ * one submission per token as the decode engine does ("Every Device Brings a
+ * Slice: How SwarmLLM Runs a 27B Model Across Browser Tabs", originshq.com,
+ * section "The Engine: ~50 WGSL Kernels Written From Scratch").  Descriptor i names w (n rows of
  * k/32 Q4_0 blocks, 4-byte aligned), x (m x k binary16, 16-byte aligned) and
  * y (m x n binary32, written); every k % 64 == 0, 2 <= m <= 16, |d| <= 8188.
  * Each GEMM's result is bit-identical to q4_0_gemm_smallm on the same

@@ -32,10 +32,10 @@ TOL = 1e-3
 
 
 def build(force: bool = False) -> str:
-    """Compile q4_oracle.c (gcc -O2, OpenMP over outputs, no fast-math, no FMA contraction)."""
+    """Compile q4_oracle.c (gcc -O3, OpenMP over outputs, no fast-math, no FMA contraction)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-fno-fast-math",
+        subprocess.check_call(["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-fno-fast-math",
                                "-ffp-contract=off", "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
@@ -50,8 +50,8 @@ class Oracle:
         lib.q4o_f16_to_f64.argtypes = [ctypes.c_uint16]
         lib.q4o_f16_to_f64.restype = ctypes.c_double
         lib.q4o_f16_to_f64_array.argtypes = [vp, i64, vp]
-        lib.q4o_dequant_row.argtypes = [vp, i64, vp]
         lib.q4o_gemm_rows.argtypes = [vp, i64, i64, vp, i64, vp, vp]
+        lib.q4o_gemm_rows.restype = ctypes.c_int
         lib.q4o_argmax.argtypes = [vp, i64]
         lib.q4o_argmax.restype = i64
         lib.q4o_accepted_prefix.argtypes = [vp, vp, i64]
@@ -61,6 +61,7 @@ class Oracle:
         lib.q4o_f64_to_f16_array.argtypes = [vp, i64, vp]
         lib.q4o_rms_norm.argtypes = [vp, vp, i64, ctypes.c_double, vp, vp]
         lib.q4o_gemv_handoff.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
+        lib.q4o_gemv_handoff.restype = ctypes.c_int
         lib.q4o_q8_gemm_rows.argtypes = [vp, i64, i64, vp, i64, vp, vp]
         self.lib = lib
         self.path = path
@@ -70,14 +71,6 @@ class Oracle:
         b = _f16bits(np.asarray(bits))
         out = np.empty(b.shape, dtype=np.float64)
         self.lib.q4o_f16_to_f64_array(b.ctypes.data, b.size, out.ctypes.data)
-        return out
-
-    def dequant_rows(self, w_rows: np.ndarray, k: int) -> np.ndarray:
-        """The binary64 weights of packed rows uint8[n, K/32*18] -> float64[n, K]."""
-        w = _u8(w_rows).reshape(-1, k // 32 * 18)
-        out = np.empty((w.shape[0], k), dtype=np.float64)
-        for i in range(w.shape[0]):
-            self.lib.q4o_dequant_row(w[i].ctypes.data, k, out[i].ctypes.data)
         return out
 
     def gemm_rows(self, w_rows: np.ndarray, k: int, x) -> tuple[np.ndarray, np.ndarray]:
@@ -94,7 +87,8 @@ class Oracle:
         m, n = xb.shape[0], w.shape[0]
         y = np.empty((m, n), dtype=np.float64)
         a = np.empty((m, n), dtype=np.float64)
-        self.lib.q4o_gemm_rows(w.ctypes.data, n, k, xb.ctypes.data, m, y.ctypes.data, a.ctypes.data)
+        if self.lib.q4o_gemm_rows(w.ctypes.data, n, k, xb.ctypes.data, m, y.ctypes.data, a.ctypes.data):
+            raise MemoryError("oracle: no memory for the decoded activations")
         if one_d:
             return y[0], a[0]
         return y, a
@@ -175,8 +169,9 @@ class Oracle:
         h16 = np.empty(n, dtype=np.uint16)
         y = np.empty(n, dtype=np.float64)
         a = np.empty(n, dtype=np.float64)
-        self.lib.q4o_gemv_handoff(w.ctypes.data, n, k, xb.ctypes.data, None if r is None else r.ctypes.data,
-                                  h16.ctypes.data, y.ctypes.data, a.ctypes.data)
+        if self.lib.q4o_gemv_handoff(w.ctypes.data, n, k, xb.ctypes.data, None if r is None else r.ctypes.data,
+                                     h16.ctypes.data, y.ctypes.data, a.ctypes.data):
+            raise MemoryError("oracle: no memory for the decoded activations")
         return h16, y, a
 
 
@@ -190,10 +185,6 @@ def default() -> Oracle:
 
 def f16_to_f64(bits) -> np.ndarray:
     return default().f16_to_f64(bits)
-
-
-def dequant_rows(w_rows: np.ndarray, k: int) -> np.ndarray:
-    return default().dequant_rows(w_rows, k)
 
 
 def gemm_rows(w_rows: np.ndarray, k: int, x) -> tuple[np.ndarray, np.ndarray]:

@@ -61,6 +61,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 /* IEEE 754 binary16 -> binary64, exact: sign, 5-bit exponent (bias 15),
  * 10-bit fraction; exponent 0 = subnormal (fraction * 2^-24), exponent 31 =
@@ -93,35 +94,57 @@ static double block_weight(const uint8_t* blk, int k) {
     return (double)(code - 8) * d;
 }
 
-/* The K weights of one packed row, as binary64. */
-void q4o_dequant_row(const uint8_t* row, int64_t k, double* out) {
-    for (int64_t i = 0; i < k; ++i) out[i] = block_weight(row + (i / 32) * 18, (int)(i % 32));
-}
-
 /*
  * y = X * W^T over the given packed rows.
  *   w_rows : nrows packed rows, each K/32*18 bytes, consecutive
  *   x      : M x K binary16 bit patterns, row-major
  *   y, a   : M x nrows binary64, row-major (a may be NULL)
+ * Each weight is decoded once and meets the M activations of its column; the
+ * M sums of a row advance together, each still taken in increasing k.
+ * Returns 0, or -1 when the scratch copy of x cannot be allocated.
  */
-void q4o_gemm_rows(const uint8_t* w_rows, int64_t nrows, int64_t k,
-                   const uint16_t* x, int64_t m, double* y, double* a) {
+int q4o_gemm_rows(const uint8_t* w_rows, int64_t nrows, int64_t k,
+                  const uint16_t* x, int64_t m, double* y, double* a) {
     const int64_t rb = (k / 32) * 18;
-    #pragma omp parallel for schedule(dynamic, 16)
-    for (int64_t n = 0; n < nrows; ++n) {
-        const uint8_t* row = w_rows + n * rb;
-        for (int64_t mm = 0; mm < m; ++mm) {
-            const uint16_t* xr = x + mm * k;
-            double acc = 0.0, mag = 0.0;
-            for (int64_t i = 0; i < k; ++i) {
-                double p = block_weight(row + (i / 32) * 18, (int)(i % 32)) * q4o_f16_to_f64(xr[i]);
-                acc += p;
-                mag += fabs(p);
-            }
-            y[mm * nrows + n] = acc;
-            if (a) a[mm * nrows + n] = mag;
-        }
+    /* x decoded once, column-major: xt[i * m + mm] = x[mm][i] */
+    double* xt = (double*)malloc((size_t)(k * m) * sizeof(double));
+    if (!xt) return -1;
+    for (int64_t mm = 0; mm < m; ++mm) {
+        const uint16_t* xr = x + mm * k;
+        for (int64_t i = 0; i < k; ++i) xt[i * m + mm] = q4o_f16_to_f64(xr[i]);
     }
+    int failed = 0;
+    #pragma omp parallel
+    {
+        double* acc = (double*)malloc((size_t)(2 * m) * sizeof(double));
+        double* mag = acc ? acc + m : NULL;
+        if (!acc) {
+            #pragma omp atomic write
+            failed = 1;
+        }
+        #pragma omp for schedule(dynamic, 4)
+        for (int64_t n = 0; n < nrows; ++n) {
+            if (!acc) continue;
+            const uint8_t* row = w_rows + n * rb;
+            for (int64_t mm = 0; mm < m; ++mm) acc[mm] = mag[mm] = 0.0;
+            for (int64_t i = 0; i < k; ++i) {
+                const double wv = block_weight(row + (i / 32) * 18, (int)(i % 32));
+                const double* xi = xt + i * m;
+                for (int64_t mm = 0; mm < m; ++mm) {
+                    const double p = wv * xi[mm];
+                    acc[mm] += p;
+                    mag[mm] += fabs(p);
+                }
+            }
+            for (int64_t mm = 0; mm < m; ++mm) {
+                y[mm * nrows + n] = acc[mm];
+                if (a) a[mm * nrows + n] = mag[mm];
+            }
+        }
+        free(acc);
+    }
+    free(xt);
+    return failed ? -1 : 0;
 }
 
 /* Lowest index i with y[i] equal to the maximum of y (n >= 1, no NaN). */
@@ -192,10 +215,11 @@ void q4o_rms_norm(const uint16_t* h, const uint16_t* g, int64_t k, double eps, d
 /* The stage hand-off: out16[n] = binary16(r[n] + y[n]) for one activation x
  * (binary16 [K]) and rows w_rows [nrows]; r (binary32 [nrows]) may be NULL
  * (zero); y and a (binary64 [nrows], a may be NULL) as q4o_gemm_rows. */
-void q4o_gemv_handoff(const uint8_t* w_rows, int64_t nrows, int64_t k, const uint16_t* x, const float* r,
-                      uint16_t* out16, double* y, double* a) {
-    q4o_gemm_rows(w_rows, nrows, k, x, 1, y, a);
+int q4o_gemv_handoff(const uint8_t* w_rows, int64_t nrows, int64_t k, const uint16_t* x, const float* r,
+                     uint16_t* out16, double* y, double* a) {
+    if (q4o_gemm_rows(w_rows, nrows, k, x, 1, y, a)) return -1;
     for (int64_t n = 0; n < nrows; ++n) out16[n] = q4o_f64_to_f16((r ? (double)r[n] : 0.0) + y[n]);
+    return 0;
 }
 
 /* Weight kk (0..31) of a Q8_0 block. */

@@ -459,7 +459,8 @@ q4_status q4_0_gemv_batch_handoff(const q4_gemv_plan* plan, const float* y, cons
     q4::PlanDesc& d = dev[index];
     const Range rh = range(h16, (size_t)d.n * 2);
     const Range rr = residual ? range(residual, (size_t)d.n * 4) : Range{0, 0};
-    const Range rp = range(plan->device, sizeof(q4::SchedHead) + dev.size() * sizeof(q4::PlanDesc));
+    // the whole plan: head, descriptors and the chunk table the kernel reads during a launch
+    const Range rp = range(plan->device, plan_size(plan->count, (size_t)plan->nchunks));
     if (overlap(rh, rp) || (residual && (overlap(rh, rr) || overlap(rr, rp))))
         return fail(Q4_ERR_INVALID_ARG, "%s: h16, the residual and the plan must not overlap", fn);
     for (int i = 0; i < plan->count; ++i) {

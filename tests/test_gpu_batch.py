@@ -1,5 +1,7 @@
 """q4_0_gemv_batch: a list of GEMVs in one launch, against single GEMVs and the
 oracle; the full 64-layer decode weight sweep on sampled rows."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -171,3 +173,34 @@ def test_stage_handoff_in_the_batch():
     single = q4.q4_0_gemv_handoff(ws[last], xs[last], r)
     torch.cuda.synchronize()
     assert torch.equal(single.view(torch.int16), h16.view(torch.int16))
+
+
+def test_batch_handoff_refuses_an_h16_over_the_plan():
+    """h16 may not overlap any part of the plan the kernel reads during a
+    launch: the head, the descriptors, or the chunk table at the plan's end
+    (an h16 lying wholly inside the chunk table is refused).  A refused call
+    leaves the plan as it was."""
+    q4 = lib()
+    shapes = [(5120, 5120), (17408, 5120), (512, 5120)]
+    ws = [dev_u8(synth.q4_0(SEED, 11300 + i, n, k)) for i, (n, k) in enumerate(shapes)]
+    xs = [dev_f16(synth.f16_normal(SEED, 11400 + i, k)) for i, (n, k) in enumerate(shapes)]
+    ys = [torch.empty(n, dtype=torch.float32, device="cuda") for n, _ in shapes]
+    batch = q4.GemvBatch(list(zip(ws, xs, ys)))
+    batch()
+    torch.cuda.synchronize()
+    want = [y.clone() for y in ys]
+    lb = q4.load_library()
+    base, nbytes = batch.buffer.data_ptr(), batch.buffer.numel()
+    n_last = shapes[-1][0]
+    chunk_table = nbytes - 16 * batch.plan.nchunks
+    assert chunk_table > 0 and 16 * batch.plan.nchunks >= 2 * n_last + 16
+    for off in (0, 16, chunk_table, chunk_table + 16, nbytes - 2 * n_last):
+        st = lb.q4_0_gemv_batch_handoff(ctypes.byref(batch.plan), ys[-1].data_ptr(), None, base + off, None)
+        assert st == q4.Q4_ERR_INVALID_ARG, (off, st)
+    # the plan is intact
+    for y in ys:
+        y.fill_(float("nan"))
+    batch()
+    torch.cuda.synchronize()
+    for a, b in zip(ys, want):
+        assert torch.equal(a, b)

@@ -25,8 +25,19 @@ def test_parity(m, n, k):
     assert_parity(y.cpu().numpy(), y_ref, a_ref, "prefill %dx%dx%d" % (m, n, k))
 
 
+def sampled_rows(rng, n, count=1024):
+    """`count` distinct rows of n (all of them when n <= count), first and last included."""
+    if n <= count:
+        return np.arange(n)
+    inner = rng.choice(np.arange(1, n - 1), size=count - 2, replace=False)
+    return np.unique(np.concatenate([[0, n - 1], inner]))
+
+
 @pytest.mark.parametrize("m", [169, 512])
 def test_prompt_sizes_sampled(m):
+    """Single q4_0_gemm_prefill calls at the prompt sizes on three projection
+    shapes, 1,024 sampled output rows each (first and last included), every
+    one of the m activation rows."""
     q4 = lib()
     rng = np.random.default_rng(m)
     for proj in (0, 4, 6):
@@ -37,16 +48,19 @@ def test_prompt_sizes_sampled(m):
         say("prefill", m, n, k)
         y = q4.q4_0_gemm_prefill(dev_u8(w), dev_f16(x))
         torch.cuda.synchronize()
-        rows = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, 14)]))
+        rows = sampled_rows(rng, n)
+        assert len(rows) == min(n, 1024) and rows[0] == 0 and rows[-1] == n - 1
         y_ref, a_ref = oracle.gemm_rows(w[rows], k, x)
         assert_parity(y.cpu().numpy()[:, rows], y_ref, a_ref, "prefill m=%d %dx%d" % (m, n, k))
 
 
-@pytest.mark.parametrize("m", [37, 169])
+@pytest.mark.parametrize("m", [37, 100, 169, 512])
 def test_batch_parity_and_single_calls(m):
     """A mixed prefill list in one launch: every GEMM within the bound of the
     oracle and equal to its own q4_0_gemm_prefill call, with ragged M, N
-    (rows past a tile) and K (1088: 17 pairs)."""
+    (rows past a tile) and K (1088: 17 pairs).  M = 37 and 169 run on 64-row
+    tiles, M = 100 (ragged) and 512 on 128-row tiles, on both batch kernels
+    (k % 256 == 0 and the others)."""
     q4 = lib()
     shapes = [(300, 1024), (64, 2048), (257, 1088), (31, 4096), (512, 64)]
     host, items = [], []
@@ -57,6 +71,7 @@ def test_batch_parity_and_single_calls(m):
         items.append((dev_u8(w), dev_f16(x), torch.full((m, n), float("nan"), device="cuda")))
     say("prefill batch m=%d of %d GEMMs" % (m, len(items)))
     batch = q4.PrefillBatch(items)
+    assert batch.plan.tile_m == (128 if m in (100, 512) else 64), batch.plan.tile_m
     batch()
     torch.cuda.synchronize()
     for (w, x), (wd, xd, yd), (n, k) in zip(host, items, shapes):
@@ -73,25 +88,33 @@ def test_batch_parity_and_single_calls(m):
         assert torch.equal(b, it[2])
 
 
-def test_batch_layer_sampled():
-    """One layer's seven projections at M = 169 as one batch, sampled rows
-    against the oracle."""
+@pytest.mark.parametrize("m", [169, 512])
+def test_batch_full_layers(m):
+    """Layers 0 and 63 of the prefill workload the benchmark times (the
+    sweep's weights, the prefill activations, the same batch kernel and tile
+    shape: 64-row tiles at M = 169, 128-row tiles at M = 512) as one batch of
+    14 GEMMs: every output of every GEMM against the oracle, and each GEMM bit
+    for bit equal to its own q4_0_gemm_prefill call."""
     q4 = lib()
-    m = 169
-    rng = np.random.default_rng(1690)
-    items, checks = [], []
-    for proj in range(7):
-        _, n, k = synth.PROJ[proj]
-        sw = synth.stream_id(4, 1, proj, synth.T_W)
-        x = synth.f16_normal(SEED, synth.stream_id(4, 1000 + m, proj, synth.T_X), m * k).reshape(m, k)
-        w = synth.q4_0(SEED, sw, n, k)
-        items.append((dev_u8(w), dev_f16(x), torch.empty((m, n), dtype=torch.float32, device="cuda")))
-        rows = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, 6)]))
-        checks.append((w[rows], x, k, rows))
-        del w
+    items, host = [], []
+    for layer in (0, 63):
+        for proj in range(7):
+            _, n, k = synth.PROJ[proj]
+            w = synth.q4_0(SEED, synth.stream_id(1, layer, proj, synth.T_W), n, k)
+            x = synth.f16_normal(SEED, synth.stream_id(4, layer, proj, synth.T_X), m * k).reshape(m, k)
+            items.append((dev_u8(w), dev_f16(x), torch.full((m, n), float("nan"), device="cuda")))
+            host.append((layer, proj, w, x))
     batch = q4.PrefillBatch(items)
+    assert batch.plan.tile_m == (128 if m == 512 else 64)
+    say("prefill full layers 0 and 63, m=%d, tile_m=%d" % (m, batch.plan.tile_m))
     batch()
     torch.cuda.synchronize()
-    for (wr, x, k, rows), it in zip(checks, items):
-        y_ref, a_ref = oracle.gemm_rows(wr, k, x)
-        assert_parity(it[2].cpu().numpy()[:, rows], y_ref, a_ref, "prefill layer batch")
+    worst = 0.0
+    for (layer, proj, w, x), (wd, xd, yd) in zip(host, items):
+        _, n, k = synth.PROJ[proj]
+        y = yd.cpu().numpy()
+        single = q4.q4_0_gemm_prefill(wd, xd).cpu().numpy()
+        assert np.array_equal(y, single), (m, layer, proj)
+        y_ref, a_ref = oracle.gemm_rows(w, k, x)
+        worst = max(worst, assert_parity(y, y_ref, a_ref, "prefill m=%d layer %d proj %d" % (m, layer, proj)))
+    say("prefill full layers m=%d: worst err/a %.3g" % (m, worst))

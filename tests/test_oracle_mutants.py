@@ -19,14 +19,16 @@ MUTANTS = {
     "nibbles_swapped": ("(k < 16) ? (byte & 0x0F) : (byte >> 4)", "(k < 16) ? (byte >> 4) : (byte & 0x0F)"),
     "sequential_nibbles": ("blk[2 + (k & 15)]", "blk[2 + (k >> 1)]"),
     "scale_big_endian": ("blk[0] | ((uint16_t)blk[1] << 8)", "blk[1] | ((uint16_t)blk[0] << 8)"),
-    "magnitude_without_abs": ("mag += fabs(p);", "mag += p;"),
+    "magnitude_without_abs": ("mag[mm] += fabs(p);", "mag[mm] += p;"),
     "f16_bias_off_by_one": ("e - 25", "e - 24"),
     "f16_subnormal_scale": ("ldexp((double)f, -24)", "ldexp((double)f, -25)"),
     "block_stride_16": ("(i / 32) * 18", "(i / 32) * 16"),
-    "output_transposed": ("y[mm * nrows + n] = acc;", "y[n * m + mm] = acc;"),
+    "output_transposed": ("y[mm * nrows + n] = acc[mm];", "y[n * m + mm] = acc[mm];"),
     "argmax_last_tie": ("if (y[i] > y[best])", "if (y[i] >= y[best])"),
     "scale_dropped": ("return (double)(code - 8) * d;", "return (double)(code - 8);"),
-    "x_ignored_sign": ("* q4o_f16_to_f64(xr[i]);", "* fabs(q4o_f16_to_f64(xr[i]));"),
+    "x_ignored_sign": ("xt[i * m + mm] = q4o_f16_to_f64(xr[i]);", "xt[i * m + mm] = fabs(q4o_f16_to_f64(xr[i]));"),
+    "activation_row_stride": ("xt[i * m + mm] = q4o_f16_to_f64(xr[i]);", "xt[i * m + mm] = q4o_f16_to_f64(xr[i ^ 1]);"),
+    "weight_column_shifted": ("const double* xi = xt + i * m;", "const double* xi = xt + ((i + 1) % k) * m;"),
     "prefix_counts_all_matches": ("while (i < m && tokens[i] == draft[i]) ++i;",
                                   "for (int64_t j = 0; j < m; ++j) i += tokens[j] == draft[j];"),
     "norm_sum_not_mean": ("sqrt(ss / (double)k + eps)", "sqrt(ss + eps)"),
@@ -67,7 +69,7 @@ def test_mutant_is_caught(name, tmp_path):
     c = tmp_path / "mutant.c"
     so = tmp_path / "libmutant.so"
     c.write_text(mutated)
-    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+    subprocess.check_call(["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
                            "-o", str(so), str(c), "-lm"])
     bad = suite.failures(oracle.Oracle(str(so)))
     assert bad, "mutant %s passed every pin" % name
@@ -75,6 +77,6 @@ def test_mutant_is_caught(name, tmp_path):
 
 def test_unmutated_copy_passes(tmp_path):
     so = tmp_path / "libcopy.so"
-    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+    subprocess.check_call(["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
                            "-o", str(so), SRC, "-lm"])
     assert suite.failures(oracle.Oracle(str(so))) == []
