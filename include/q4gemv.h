@@ -158,6 +158,25 @@ Q4_API q4_status lm_head_argmax(const void* w, const void* h, float* logits, int
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * lm_head_argmax without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same operation, kernels and results as lm_head_argmax
+ * (logits and token bit-identical); w, h, logits, token, n_vocab and k as
+ * there.  The per-workgroup keys live in an array the library holds on each
+ * device until the process ends (2048 keys, 16 KiB per device); every grid
+ * this call launches fits it, so no size is refused for it.  The call
+ * allocates nothing: no hipMalloc, no hipFree, no library routine that
+ * allocates.  Its first call on a device looks the array's address up there
+ * (Q4_ERR_HIP if that fails).  All calls on one device share that array, so
+ * calls that overlap in time on one device (on different streams, or from
+ * different host threads without ordering) race and may return a wrong
+ * token; calls ordered on one stream do not.  Nothing in the array needs
+ * clearing: each call writes the keys it reads.
+ */
+Q4_API q4_status lm_head_argmax_noalloc(const void* w, const void* h, float* logits, int32_t* token,
+                                        int64_t n_vocab, int64_t k, void* stream);
+
+/*
  * y[n] = sum_k w[n][k] * x[k]  with w in Q8_0 blocks
  *
  * The pages' other weight format, "GGUF Q8_0", used by the small dense Qwen3

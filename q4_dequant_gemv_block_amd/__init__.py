@@ -37,7 +37,8 @@ Q4_OP_LM_HEAD_NORM_ARGMAX = 5
 # Every symbol include/q4gemv.h declares.
 EXPORTS = (
     "q4_abi_version", "q4_last_error", "q4_workspace_bytes", "q4_0_gemv", "q4_0_gemm_smallm",
-    "q4_0_gemm_prefill", "lm_head_argmax", "lm_head_norm_argmax", "lm_head_verify", "q4_0_gemv_handoff", "q8_0_gemv", "q8_0_gemv_batch_plan_bytes",
+    "q4_0_gemm_prefill", "lm_head_argmax", "lm_head_argmax_noalloc", "lm_head_norm_argmax", "lm_head_verify",
+    "q4_0_gemv_handoff", "q8_0_gemv", "q8_0_gemv_batch_plan_bytes",
     "q8_0_gemv_batch_plan", "q8_0_gemv_batch",
     "q4_0_gemv_batch_plan_bytes", "q4_0_gemv_batch_plan",
     "q4_0_gemm_smallm_batch_plan_bytes", "q4_0_gemm_smallm_batch_plan", "q4_0_gemm_smallm_batch",
@@ -93,6 +94,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.q4_0_gemm_prefill.argtypes = [vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t, vp]
     lib.lm_head_argmax.restype = st
     lib.lm_head_argmax.argtypes = [vp, vp, vp, vp, i64, i64, vp, ctypes.c_size_t, vp]
+    lib.lm_head_argmax_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, vp]
+    lib.lm_head_argmax_noalloc.restype = st
     lib.lm_head_verify.restype = st
     lib.q8_0_gemv.argtypes = [vp, vp, vp, i64, i64, vp]
     lib.q8_0_gemv.restype = ctypes.c_int
@@ -261,6 +264,24 @@ def lm_head_argmax(w: torch.Tensor, h: torch.Tensor, logits: torch.Tensor | None
                                          _ptr(logits, torch.float32, "logits"), _ptr(token, torch.int32, "token"),
                                          n, k, _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
                                          _stream(stream)))
+    return logits, token
+
+
+def lm_head_argmax_noalloc(w: torch.Tensor, h: torch.Tensor, logits: torch.Tensor | None = None,
+                           token: torch.Tensor | None = None, stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """lm_head_argmax with the per-workgroup keys in the library's own per-device
+    array: the C call allocates nothing (pass logits and token to allocate nothing here either)."""
+    if h.dim() != 1:
+        raise ValueError("h must be float16 [K]")
+    k = h.shape[0]
+    n = _weights(w, k)
+    if logits is None:
+        logits = torch.empty(n, dtype=torch.float32, device=h.device)
+    if token is None:
+        token = torch.empty(1, dtype=torch.int32, device=h.device)
+    _check(load_library().lm_head_argmax_noalloc(_ptr(w, torch.uint8, "w"), _ptr(h, torch.float16, "h"),
+                                                 _ptr(logits, torch.float32, "logits"),
+                                                 _ptr(token, torch.int32, "token"), n, k, _stream(stream)))
     return logits, token
 
 

@@ -197,6 +197,32 @@ q4_status lm_head_argmax(const void* w, const void* h, float* logits, int32_t* t
     return hip_status(e, "lm_head_argmax launch");
 }
 
+q4_status lm_head_argmax_noalloc(const void* w, const void* h, float* logits, int32_t* token, int64_t n_vocab,
+                                 int64_t k, void* stream) {
+    const char* fn = "lm_head_argmax_noalloc";
+    q4_status st = check_shape(fn, 1, 1, n_vocab, k);
+    if (st) return st;
+    st = check_tensors(fn, w, h, logits, 1, n_vocab, k, (size_t)n_vocab * 4);
+    if (st) return st;
+    if (!token) return fail(Q4_ERR_INVALID_ARG, "%s: null token pointer", fn);
+    if (!aligned(token, 4)) return fail(Q4_ERR_MISALIGNED, "%s: token must be 4-byte aligned", fn);
+    if (!fast_path(w, k))
+        return fail(Q4_ERR_INVALID_ARG, "%s: needs k %% 64 == 0 and k <= %lld", fn, (long long)q4::kFastMaxK);
+    const Range rt = range(token, 4), rl = range(logits, (size_t)n_vocab * 4);
+    if (overlap(rt, rl) || overlap(rt, range(w, (size_t)(n_vocab * row_bytes(k)))) || overlap(rt, range(h, (size_t)k * 2)))
+        return fail(Q4_ERR_INVALID_ARG, "%s: token must not overlap the tensors", fn);
+    const int keys = q4::argmax_blocks(n_vocab, k);
+    if (keys > q4::kLmHeadScratchKeys)
+        return fail(Q4_ERR_INVALID_ARG, "%s: %d workgroup keys exceed the library's array of %d", fn, keys,
+                    q4::kLmHeadScratchKeys);
+    uint64_t* scratch = nullptr;
+    hipError_t e = q4::lm_head_scratch(&scratch);
+    if (e != hipSuccess) return hip_status(e, "lm_head_argmax_noalloc: scratch address");
+    e = q4::launch_lm_head(static_cast<const uint8_t*>(w), static_cast<const uint16_t*>(h), logits, token, n_vocab, k,
+                           scratch, static_cast<hipStream_t>(stream));
+    return hip_status(e, "lm_head_argmax_noalloc launch");
+}
+
 q4_status q8_0_gemv(const void* w, const void* x, float* y, int64_t n, int64_t k, void* stream) {
     const char* fn = "q8_0_gemv";
     q4_status st = check_shape(fn, 1, 1, n, k);

@@ -37,6 +37,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <vector>
 
 namespace q4 {
@@ -1097,6 +1098,37 @@ hipError_t launch_lm_head(const uint8_t* w, const uint16_t* h, float* logits, in
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_argmax_final, dim3(1), dim3(kFinalThreads), 0, s, keys, grid, token);
     return hipGetLastError();
+}
+
+// The LM head's per-workgroup keys for callers that cannot allocate device
+// memory: one fixed array per device, held until the process ends and shared
+// by every such call on that device.  Host code never passes the array's name
+// to a kernel (on the host it is a stand-in, not a device address); it uses
+// the device address looked up once per device below.
+static __device__ __align__(256) uint64_t scratch[kLmHeadScratchKeys];
+
+hipError_t lm_head_scratch(uint64_t** keys) {
+    static std::atomic<uint64_t*> addr[64];
+    static std::mutex mu;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    uint64_t* p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(mu);
+        p = addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            void* sym = nullptr;
+            e = hipGetSymbolAddress(&sym, HIP_SYMBOL(scratch));  // with `dev` current
+            if (e != hipSuccess) return e;
+            if (!sym) return hipErrorInvalidSymbol;
+            p = static_cast<uint64_t*>(sym);
+            addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *keys = p;
+    return hipSuccess;
 }
 
 hipError_t launch_lm_head_norm(const uint8_t* w, const uint16_t* h, const uint16_t* gamma, float eps,

@@ -59,6 +59,12 @@ constexpr int64_t kFastMaxK = 32768;
 // Largest grid (and partial-key count) of the LM-head kernel.
 constexpr int kArgmaxMaxBlocks = 2048;
 
+// Keys held in the library's own per-device array for the LM head entry
+// point that allocates nothing; *keys receives its device address on the
+// current device (looked up on the first call per device).
+constexpr int kLmHeadScratchKeys = kArgmaxMaxBlocks;
+hipError_t lm_head_scratch(uint64_t** keys);
+
 int device_cu_count();
 
 hipError_t launch_gemv(const uint8_t* w, const uint16_t* x, float* y, int64_t n, int64_t k,

@@ -159,6 +159,26 @@ def test_lm_head_validation(lib):
     assert lib.lm_head_argmax(w, h, lg, tok, 1000, 96, FAKE * 16, need, None) == q4.Q4_ERR_INVALID_ARG
 
 
+def test_lm_head_noalloc_validation(lib):
+    """The entry point without a workspace refuses bad arguments before it
+    looks up its array or launches anything."""
+    w, h, lg, tok = FAKE, FAKE * 2, FAKE * 4, FAKE * 8
+
+    def call(w=w, h=h, lg=lg, tok=tok, n=1000, k=64):
+        return lib.lm_head_argmax_noalloc(w, h, lg, tok, n, k, None)
+
+    assert call(w=None) == q4.Q4_ERR_INVALID_ARG
+    assert call(tok=None) == q4.Q4_ERR_INVALID_ARG
+    assert call(tok=tok + 2) == q4.Q4_ERR_MISALIGNED
+    assert call(w=w + 4) == q4.Q4_ERR_MISALIGNED
+    assert call(tok=lg + 8) == q4.Q4_ERR_INVALID_ARG  # token inside the logits
+    assert call(lg=h) == q4.Q4_ERR_INVALID_ARG  # logits over the hidden state
+    assert call(k=96) == q4.Q4_ERR_INVALID_ARG
+    assert call(k=32768 + 64) == q4.Q4_ERR_INVALID_ARG
+    assert call(n=0) == q4.Q4_ERR_INVALID_ARG
+    assert b"lm_head_argmax_noalloc" in lib.q4_last_error()
+
+
 def test_q8_gemv_validation(lib):
     w, x, y = FAKE, FAKE * 2, FAKE * 3
     n, k = 1000, 96
