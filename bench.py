@@ -1,8 +1,8 @@
 """Benchmark of the Q4_0 dequantize-and-multiply path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload sweep|gemv|lmhead|lmhead_norm|handoff|q8|verify|smallm|prefill|copy]
-                    [--m M]
+                    [--workload sweep|gemv|lmhead|lmhead_norm|handoff|q8|verify|smallm|prefill|copy|stream]
+                    [--m M] [--pattern P --wg-per-cu W]
 
 Default workload ("sweep"): the 27B-shaped decode weight sweep, 64 layers x
 (q, k, v, o 5120x5120; gate, up 17408x5120; down 5120x17408) = 448 Q4_0 GEMVs
@@ -133,8 +133,33 @@ SEED = 0x51A40000
 SWEEP_BYTES = 13_422_428_160  # weights 13,400,801,280 + x 6,160,384 + y 15,466,496
 
 
-def time_steps(fn, steps: int, warmup: int):
+# After an idle period the GPU's power management lets the first launch of a
+# memory-bound kernel run at full speed, slows the next ones by up to 45 % and
+# recovers over about 50 ms (measured on the 448-GEMV sweep: 2.25, 3.13, 2.78,
+# 2.61, ... 2.15 ms, the same after 0.2 s and after 2 s of idle).  A decode
+# loop runs in that steady state, so every workload first launches its step
+# for SETTLE_S seconds of wall time, untimed, before its warm-up steps.
+SETTLE_S = 0.25
+
+
+def settle(fn, seconds: float = SETTLE_S) -> int:
+    """Launch fn until `seconds` of wall time have passed (synchronizing every few
+    launches so the queue stays short); returns the number of launches."""
     import torch
+    if seconds <= 0:
+        return 0
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            fn()
+        n += 4
+        torch.cuda.synchronize()
+    return n
+
+
+def time_steps(fn, steps: int, warmup: int, settle_s: float = 0.0):
+    import torch
+    settle(fn, settle_s)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -176,18 +201,9 @@ def bench_sweep(args):
     ws, xs, ys, ids = sweep_inputs(q4, 1)
     log("  %.1f s" % (time.time() - t0))
     batch = q4.GemvBatch(list(zip(ws, xs, ys)))
+    n_settle = settle(batch)
     ms = time_steps(batch, args.steps, args.warmup)
     gbs = SWEEP_BYTES / (ms * 1e-3) / 1e9
-    # the host's step after the sweep: final norm + LM head (151,936 x 5,120) + argmax, for the implied tokens/s
-    import synth
-    wl, hl, gl = lmhead_inputs()
-    lg = torch.empty(synth.VOCAB, dtype=torch.float32, device="cuda")
-    tok = torch.empty(1, dtype=torch.int32, device="cuda")
-    wsp = torch.empty(q4.workspace_bytes(q4.Q4_OP_LM_HEAD_NORM_ARGMAX, 1, synth.VOCAB, synth.HIDDEN),
-                      dtype=torch.uint8, device="cuda")
-    # (the first launches after the sweep's run settle slowly: warm up with 200)
-    lm_ms = time_steps(lambda: q4.lm_head_norm_argmax(wl, hl, gl, NORM_EPS, lg, tok, workspace=wsp),
-                       max(args.steps, 20) * 10, 200)
     out = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -197,15 +213,33 @@ def bench_sweep(args):
                                "gate,up 17408x5120; down 5120x17408), 448 Q4_0 GEMVs, M=1, one launch",
                    "weight_bytes": 13_400_801_280, "algorithmic_bytes_per_step": SWEEP_BYTES,
                    "seed": SEED},
+        "settle_s": SETTLE_S, "settle_launches": n_settle,
         "sweeps_per_s": round(1000.0 / ms, 2),
         "pct_of_8TBps": round(100.0 * gbs / PEAK_HBM_GBS, 2),
-        "lm_head_norm_argmax_us": round(lm_ms * 1000.0, 2),
-        "implied_tok_s": round(1000.0 / (ms + lm_ms), 2),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": counter_traffic("sweep"),
                      "kernel": "q4::k_sweep<QuadEngine<12,2,2,288>> (batch)", "launches_per_step": 1},
     }
+    if args.sweep_only:  # (profiling runs: the sweep kernel alone)
+        return out
+    # the host's step after the sweep: final norm + LM head (151,936 x 5,120) + argmax, for the implied tokens/s
+    import synth
+    wl, hl, gl = lmhead_inputs()
+    lg = torch.empty(synth.VOCAB, dtype=torch.float32, device="cuda")
+    tok = torch.empty(1, dtype=torch.int32, device="cuda")
+    wsp = torch.empty(q4.workspace_bytes(q4.Q4_OP_LM_HEAD_NORM_ARGMAX, 1, synth.VOCAB, synth.HIDDEN),
+                      dtype=torch.uint8, device="cuda")
+    lm_ms = time_steps(lambda: q4.lm_head_norm_argmax(wl, hl, gl, NORM_EPS, lg, tok, workspace=wsp),
+                       max(args.steps, 20) * 10, args.warmup, settle_s=SETTLE_S)
+    del wl, hl, gl, lg
+    ceiling = stream_ceiling()
+    out.update({
+        "stream_ceiling_GBps": ceiling["GBps"], "stream_ceiling_pattern": ceiling["pattern"],
+        "pct_of_stream_ceiling": round(100.0 * gbs / ceiling["GBps"], 2),
+        "lm_head_norm_argmax_us": round(lm_ms * 1000.0, 2),
+        "implied_tok_s": round(1000.0 / (ms + lm_ms), 2),
+    })
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(ids)
     return out
@@ -228,7 +262,7 @@ def bench_gemv(args):
         q4.q4_0_gemv(ws[it[0] % copies], x, y)
         it[0] += 1
     steps = max(args.steps, 1) * copies
-    ms = time_steps(step, steps, args.warmup * copies)
+    ms = time_steps(step, steps, args.warmup * copies, settle_s=SETTLE_S)
     hot_ms = time_steps(lambda: q4.q4_0_gemv(ws[0], x, y), steps, args.warmup)
     bytes_ = n * k // 32 * 18 + k * 2 + n * 4
     gbs = bytes_ / (ms * 1e-3) / 1e9
@@ -264,7 +298,7 @@ def bench_q8(args):
             io += 2 * k + 4 * n
 
     batch = q4.Q8Batch(list(zip(ws, xs, ys)))
-    ms = time_steps(batch, args.steps, args.warmup)
+    ms = time_steps(batch, args.steps, args.warmup, settle_s=SETTLE_S)
 
     def singles():
         for w, x, y in zip(ws, xs, ys):
@@ -325,7 +359,7 @@ def bench_handoff(args):
     wbytes = sum(w.numel() for w in ws)
     stage_bytes = wbytes + io - 4 * n_last + 2 * n_last + 4 * n_last  # last y: binary16 out, residual in
     for f in (stage, plain):
-        time_steps(f, 1, args.warmup)
+        time_steps(f, 1, args.warmup, settle_s=SETTLE_S)
     blocks = {"stage": [], "plain": []}
     for rr in range(4):
         for name in (("stage", "plain") if rr % 2 == 0 else ("plain", "stage")):
@@ -370,7 +404,7 @@ def bench_lmhead(args):
     lg = torch.empty(n, dtype=torch.float32, device="cuda")
     tok = torch.empty(1, dtype=torch.int32, device="cuda")
     wsp = torch.empty(q4.workspace_bytes(q4.Q4_OP_LM_HEAD_ARGMAX, 1, n, k), dtype=torch.uint8, device="cuda")
-    ms = time_steps(lambda: q4.lm_head_argmax(w, h, lg, tok, wsp), args.steps * 10, args.warmup)
+    ms = time_steps(lambda: q4.lm_head_argmax(w, h, lg, tok, wsp), args.steps * 10, args.warmup, settle_s=SETTLE_S)
     bytes_ = n * k // 32 * 18 + k * 2 + n * 4 + 4
     gbs = bytes_ / (ms * 1e-3) / 1e9
     return {"metric": "LM head + greedy argmax HBM GB/s (151936x5120 Q4_0)", "value": round(gbs, 2), "unit": "GB/s",
@@ -412,7 +446,7 @@ def bench_lmhead_norm(args):
     # both warmed, then timed in alternating blocks (the first blocks after the
     # inputs are written run slower, which would otherwise land on one side)
     for f in (fused, plain):
-        time_steps(f, 1, args.warmup)
+        time_steps(f, 1, args.warmup, settle_s=SETTLE_S)
     blocks = {"fused": [], "plain": []}
     for r in range(4):
         for name in (("fused", "plain") if r % 2 == 0 else ("plain", "fused")):
@@ -448,7 +482,8 @@ def bench_verify(args):
     tok = torch.empty(m, dtype=torch.int32, device="cuda")
     acc = torch.empty(1, dtype=torch.int32, device="cuda")
     wsp = torch.empty(max(16, q4.workspace_bytes(q4.Q4_OP_LM_HEAD_VERIFY, m, n, k)), dtype=torch.uint8, device="cuda")
-    ms = time_steps(lambda: q4.lm_head_verify(w, h, draft, lg, tok, acc, wsp), args.steps * 10, args.warmup)
+    ms = time_steps(lambda: q4.lm_head_verify(w, h, draft, lg, tok, acc, wsp), args.steps * 10, args.warmup,
+                    settle_s=SETTLE_S)
     bytes_ = n * k // 32 * 18 + m * k * 2 + m * n * 4 + 2 * m * 4 + 4
     gbs = bytes_ / (ms * 1e-3) / 1e9
     return {"metric": "greedy verify of an M-token draft: LM head GB/s (151936x5120 Q4_0, M=%d)" % m,
@@ -471,7 +506,7 @@ def bench_gemm(args, prefill: bool):
     if prefill:
         # the 448 GEMMs as one prefill batch: one launch
         batch = q4.PrefillBatch(list(zip(ws, xs, ys)))
-        ms = time_steps(batch, args.steps, args.warmup)
+        ms = time_steps(batch, args.steps, args.warmup, settle_s=SETTLE_S)
 
         def step():
             for w, x, y in zip(ws, xs, ys):
@@ -481,7 +516,7 @@ def bench_gemm(args, prefill: bool):
     else:
         # the 448 GEMMs as one small-M batch: one launch (plus the K-range sum when K is split)
         batch = q4.SmallMBatch(list(zip(ws, xs, ys)))
-        ms = time_steps(batch, args.steps, args.warmup)
+        ms = time_steps(batch, args.steps, args.warmup, settle_s=SETTLE_S)
         eager_ms = ms
         how = "one batched launch"
     wbytes = 13_400_801_280
@@ -503,6 +538,74 @@ def bench_gemm(args, prefill: bool):
             "tflops": round(tf, 3), "GBps": round(gbs, 2), "eager_ms_per_step": round(eager_ms, 4), "roofline": rl}
 
 
+STREAM_BYTES = 16 << 30
+# (pattern, workgroups of 256 threads per CU) of the read-ceiling probe: 0/1
+# grid-stride cached / non-temporal loads, 2/3 one contiguous range per
+# workgroup cached / non-temporal, 4 non-temporal buffer loads into an LDS ring
+STREAM_PATTERNS = {0: "grid-stride, cached", 1: "grid-stride, non-temporal", 2: "range per workgroup, cached",
+                   3: "range per workgroup, non-temporal", 4: "range per workgroup, non-temporal into LDS"}
+STREAM_CONFIGS = [(p, w) for p in range(4) for w in (1, 2, 4, 8)] + [(4, 1), (4, 2), (4, 3)]
+STREAM_BEST = [(1, 1), (3, 2), (4, 2), (4, 3)]  # the fastest configurations on MI355X
+
+
+def load_stream():
+    import ctypes
+    from q4_dequant_gemv_block_amd import build
+    if not os.path.exists(build.STREAM_LIB):
+        build.build()
+    lib = ctypes.CDLL(build.STREAM_LIB)
+    lib.q4_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p]
+    lib.q4_stream_read.restype = ctypes.c_int
+    return lib
+
+
+def stream_rates(configs, steps: int, warmup: int, nbytes: int = STREAM_BYTES) -> list:
+    """Read rate of a fresh nbytes buffer for each (pattern, wg_per_cu)."""
+    import torch
+    lib = load_stream()
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.view(torch.int32).fill_(0x5A5A5A5A)
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    res = []
+    for i, (p, w) in enumerate(configs):
+        def step(p=p, w=w):
+            st = lib.q4_stream_read(buf.data_ptr(), nbytes, out.data_ptr(), p, w, stream)
+            if st != 0:
+                raise RuntimeError("q4_stream_read(%d, %d): %d" % (p, w, st))
+        ms = time_steps(step, steps, warmup, settle_s=SETTLE_S if i == 0 else 0.05)
+        res.append({"pattern": p, "wg_per_cu": w, "what": STREAM_PATTERNS[p], "ms": round(ms, 4),
+                    "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)})
+    del buf
+    return res
+
+
+def stream_ceiling() -> dict:
+    """The best read rate over the fastest probe configurations (16 GiB read once)."""
+    best = max(stream_rates(STREAM_BEST, 10, 2), key=lambda r: r["GBps"])
+    return {"GBps": best["GBps"], "pattern": "%s, %d workgroups/CU" % (best["what"], best["wg_per_cu"])}
+
+
+def bench_stream(args):
+    """The device's read-bandwidth ceiling: a 16 GiB buffer read once and folded
+    into one word (libq4stream), for every probe configuration, or the one
+    --pattern/--wg-per-cu names.  value = the best rate."""
+    configs = STREAM_CONFIGS if args.pattern < 0 else [(args.pattern, args.wg_per_cu)]
+    res = stream_rates(configs, args.steps, args.warmup)
+    best = max(res, key=lambda r: r["GBps"])
+    return {"metric": "HBM read ceiling GB/s (16 GiB read once, read-reduce)", "value": best["GBps"],
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": best["ms"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32", "data": "synthetic",
+            "config": {"workload": "read-reduce of %d bytes" % STREAM_BYTES, "best": "%s, %d workgroups/CU" % (
+                best["what"], best["wg_per_cu"])},
+            "pct_of_8TBps": round(100.0 * best["GBps"] / PEAK_HBM_GBS, 2), "settle_s": SETTLE_S,
+            "configs": res,
+            "roofline": {"bound": "hbm", "achieved": best["GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(best["GBps"] / PEAK_HBM_GBS, 4), "traffic": None,
+                         "kernel": "libq4stream pattern %d" % best["pattern"]}}
+
+
 COPY_BYTES = 1 << 30
 
 
@@ -512,7 +615,7 @@ def bench_copy(args):
     import torch
     a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
-    ms = time_steps(lambda: b.copy_(a), args.steps, args.warmup)
+    ms = time_steps(lambda: b.copy_(a), args.steps, args.warmup, settle_s=SETTLE_S)
     return {"metric": "device copy GB/s (counter calibration)", "value": round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 2),
             "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
@@ -556,14 +659,17 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
-    # the first launches after the inputs are written run slower (about 40 %
-    # on the first one, settling within about ten launches of the sweep)
-    ap.add_argument("--warmup", type=int, default=25)
+    # (before these, every workload settles for SETTLE_S seconds: see there)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="sweep",
                     choices=["sweep", "gemv", "lmhead", "lmhead_norm", "handoff", "q8", "verify", "smallm",
-                             "prefill", "copy"])
+                             "prefill", "copy", "stream"])
     ap.add_argument("--m", type=int, default=0)
+    ap.add_argument("--pattern", type=int, default=-1, help="stream: one probe pattern (0..4) instead of all")
+    ap.add_argument("--wg-per-cu", type=int, default=2, help="stream: workgroups per CU with --pattern")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep-only", action="store_true",
+                    help="sweep: time the sweep alone (no LM head, read ceiling or CPU baseline), for profiling")
     ap.add_argument("--record-traffic", nargs=6, metavar=("WORKLOAD", "KERNEL", "FETCH_CSV", "WRITE_CSV",
                                                           "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write profiles/traffic.json from rocprofv3 counter CSVs and exit (no GPU needed)")
@@ -580,7 +686,7 @@ def main():
         sys.exit(1)
     fn = {"sweep": bench_sweep, "gemv": bench_gemv, "lmhead": bench_lmhead, "lmhead_norm": bench_lmhead_norm,
           "handoff": bench_handoff, "q8": bench_q8,
-          "verify": bench_verify, "copy": bench_copy,
+          "verify": bench_verify, "copy": bench_copy, "stream": bench_stream,
           "smallm": lambda a: bench_gemm(a, False), "prefill": lambda a: bench_gemm(a, True)}[args.workload]
     out = fn(args)
     print(json.dumps(out), flush=True)

@@ -13,6 +13,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libq4gemv.so")
+# the read-bandwidth probe the benchmark quotes the GEMV against (not part of the GEMV library)
+STREAM_SRC = "stream.hip"
+STREAM_LIB = os.path.join(HERE, "libq4stream.so")
 SOURCES = ["gemv.hip", "smallm.hip", "prefill.hip", "verify.hip", "q8.hip", "api.cpp"]
 ARCH = "gfx950"
 
@@ -100,6 +103,16 @@ def build(verbose: bool = False, defines=()) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
     os.replace(tmp, LIB)
+    tmp = STREAM_LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc()] + FLAGS + ["-shared", os.path.join(CSRC, STREAM_SRC), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stderr=subprocess.PIPE, text=True)
+    if r.returncode != 0:
+        print(r.stderr, file=sys.stderr, flush=True)
+        raise subprocess.CalledProcessError(r.returncode, cmd)
+    check_resources(r.stderr, STREAM_SRC)
+    os.replace(tmp, STREAM_LIB)
     return LIB
 
 

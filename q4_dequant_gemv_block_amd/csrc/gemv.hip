@@ -68,6 +68,13 @@ constexpr int kWavesPerEu = Q4_SWEEP_WPE;   // register budget: waves per SIMD t
 #define Q4_QUAD_NB 2
 #endif
 constexpr int kQuadNB = Q4_QUAD_NB;  // units per wave in the quad engine's LDS ring
+#ifndef Q4_QUAD_TAIL_X4
+#define Q4_QUAD_TAIL_X4 0
+#endif
+#ifndef Q4_SWEEP_FAIR
+#define Q4_SWEEP_FAIR 1
+#endif
+constexpr bool kFairPriority = Q4_SWEEP_FAIR != 0;  // waves behind the workgroup's leader get a higher priority
 
 struct Shape {
     int waves, r, wg_per_cu;
@@ -111,6 +118,14 @@ __device__ __forceinline__ void stage_block(const uint32_t (&v)[16], int p, int 
     }
 }
 
+// Every load of the staging has returned when its loop ends (each value is
+// consumed), but the compiler also considers the path on which both branches
+// of the chunk layout are skipped and would keep those loads pending into the
+// GEMV loop, where it then waited for every outstanding load (the ring's
+// included) before each step's LDS reads.  An explicit vmcnt(0) here costs
+// nothing and clears that.
+__device__ __forceinline__ void staged_loads_done() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ void stage_x(const uint16_t* __restrict__ x, int nblocks, int npairs_pad, int stride,
                         u4* __restrict__ xs) {
     const int nb_pad = 2 * npairs_pad;
@@ -132,6 +147,7 @@ __device__ void stage_x(const uint16_t* __restrict__ x, int nblocks, int npairs_
         else
             stage_block<0>(v, b >> 1, stride, xs);
     }
+    staged_loads_done();
 }
 
 // The final norm before the LM head, applied while the activations are staged
@@ -247,6 +263,7 @@ __device__ void stage_x_norm(const uint16_t* __restrict__ h, const NormArgs& nm,
         else
             stage_block<0>(v, b >> 1, stride, xs);
     }
+    staged_loads_done();
 }
 
 // ---------------------------------------------------------------------------
@@ -299,12 +316,24 @@ __device__ __forceinline__ float pair_acc(float a, float d0, float s0, float d1,
 // 16 lane slots by row16_sum.  Every row's result thus depends only on its
 // own bytes and the activations, not on its position or on the engine.
 
-// s_waitcnt vmcnt(n) with the other counters left free (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14).
+// s_waitcnt vmcnt(n), the other counters left free.  As asm with a memory
+// clobber it is also a compiler barrier: no LDS read of a ring slot moves
+// above the wait for that slot's loads.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until this wave's LDS reads have returned (before a slot they read is refilled).
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier for LDS hand-overs only: this wave's LDS accesses are
+// complete, then s_barrier.  __syncthreads' release fence would also wait for
+// every outstanding load of the wave, the ring's included, and drain it.
+__device__ __forceinline__ void lds_barrier() {
+    wait_lgkm0();
+    asm volatile("s_barrier" ::: "memory");
 }
 
 // Wait until a unit's loads are done, given the units issued after it (each
@@ -323,20 +352,52 @@ __device__ __forceinline__ void wait_unit(uint32_t after) {
         wait_vmcnt<0>();
 }
 
-typedef __attribute__((address_space(1))) void g_void;
-typedef __attribute__((address_space(3))) void l_void;
-
 // Fourth dword of a raw buffer descriptor on gfx9 (32-bit data format, no
 // swizzle); loads past the descriptor's size return zero.
 constexpr int kBufferWord3 = 0x00020000;
 
-// 16 (4) bytes per lane from global memory straight into LDS (lane i's bytes
-// land at dst + 16 i (4 i)), non-temporal.  `dst` must be wave-uniform.
+// Loads from global memory straight into LDS, non-temporal: lane i's 16 (4)
+// bytes land at M0 + 16 i (4 i), M0 being the wave-uniform LDS address of the
+// destination.  They are issued through asm, so the compiler does not track
+// them: it cannot tell the ring slot being refilled from the one being read,
+// and for the builtins it waited for every outstanding load before each
+// step's first LDS read, which left one unit per wave in flight instead of
+// the ring's NB.  The engines wait for their own loads (explicit vmcnt before
+// reading a slot, lgkmcnt(0) after reading it and before refilling it).  The
+// loads write no register; the s_nop covers the M0 write just before.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
 __device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* dst) {
-    __builtin_amdgcn_global_load_lds((g_void*)src, (l_void*)dst, 16, 0, 2);
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "{m0}"(lds_addr(dst)) : "memory");
 }
 __device__ __forceinline__ void dma4(const uint8_t* src, uint8_t* dst) {
-    __builtin_amdgcn_global_load_lds((g_void*)src, (l_void*)dst, 4, 0, 2);
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off nt" ::"v"(src), "{m0}"(lds_addr(dst)) : "memory");
+}
+
+// Buffer resource of a raw byte buffer (gfx9: base, stride 0, size in bytes,
+// 32-bit data format); loads at offsets at or past `bytes` return zeros.
+// Every field is wave-uniform.
+struct Rsrc {
+    u4 w;
+};
+__device__ __forceinline__ Rsrc make_rsrc(const uint8_t* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    Rsrc r;
+    r.w.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    r.w.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xFFFFu);
+    r.w.z = __builtin_amdgcn_readfirstlane(bytes);
+    r.w.w = (uint32_t)kBufferWord3;
+    return r;
+}
+// 16 (4) bytes per lane at byte offset voff of the buffer into LDS at M0 + 16 i (4 i).
+__device__ __forceinline__ void dma16(const Rsrc& r, uint32_t voff, uint8_t* dst) {
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(r.w), "{m0}"(lds_addr(dst))
+                 : "memory");
+}
+__device__ __forceinline__ void dma4(const Rsrc& r, uint32_t voff, uint8_t* dst) {
+    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen nt lds" ::"v"(voff), "s"(r.w), "{m0}"(lds_addr(dst))
+                 : "memory");
 }
 
 // Segment engine, for any k % 64 == 0.  A wave's unit is 4R consecutive rows
@@ -416,9 +477,7 @@ struct DmaEngine {
                 const uint32_t rr = (uint32_t)min((int)row0 + r, last_row);
                 const uint8_t* row = D.w + (uint64_t)rr * rb + seg;
                 if ((uint32_t)lane < full) dma16(row + 16 * lane, dst + r * kPitch);
-                if ((uint32_t)lane < (rem >> 2))
-                    __builtin_amdgcn_global_load_lds((g_void*)(row + 16 * full + 4 * lane),
-                                                     (l_void*)(dst + r * kPitch + 16 * full), 4, 0, 2);
+                if ((uint32_t)lane < (rem >> 2)) dma4(row + 16 * full + 4 * lane, dst + r * kPitch + 16 * full);
             }
         }
     }
@@ -434,7 +493,7 @@ struct DmaEngine {
         for (int i = 0; i < R; ++i)
 #pragma unroll
             for (int c = 0; c < 9; ++c) W.d[i][c] = p[i * (kPitch / 4) + c];
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the reads are done before the slot is reloaded
+        wait_lgkm0();  // the reads are done before the slot is reloaded
         if (edge(Dp, s) && 16 * jb + l16 >= (Dp.k >> 6)) {
 #pragma unroll
             for (int i = 0; i < R; ++i) {
@@ -476,7 +535,7 @@ struct DmaEngine {
         for (int i = 0; i < R; ++i) {
             const float v = row16_sum((acc.c0[i] + acc.c2[i]) + (acc.c1[i] + acc.c3[i]));
             acc.c0[i] = acc.c1[i] = acc.c2[i] = acc.c3[i] = 0.0f;
-            if (l16 == 0) store(r0 + i, v);
+            if (l16 == 0) store(i, r0 + i, v);
         }
     }
 };
@@ -555,14 +614,17 @@ struct QuadEngine {
             const int64_t left = (int64_t)(end - off);
             const int32_t hi = (int32_t)((uint64_t)left >> 32);
             const uint32_t nrec = hi < 0 ? 0u : (hi > 0 ? 0xFFFFFFFFu : (uint32_t)left);
-            const __amdgpu_buffer_rsrc_t rs =
-                __builtin_amdgcn_make_buffer_rsrc((void*)(D.w + off), (short)0, (int)nrec, kBufferWord3);
+            const Rsrc rs = make_rsrc(D.w + off, nrec);
             // The piece offsets ride in the per-lane offset: an instruction
             // offset would move the LDS destination as well.
             uint8_t* dst = wl + slot * kSlot + i * kSlab;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (l_void*)dst, 16, 16 * lane, 0, 0, 2);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (l_void*)(dst + 1024), 16, 1024 + 16 * lane, 0, 0, 2);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (l_void*)(dst + 2048), 4, 2048 + 4 * lane, 0, 0, 2);
+            dma16(rs, 16 * lane, dst);
+            dma16(rs, 1024 + 16 * lane, dst + 1024);
+            if (Q4_QUAD_TAIL_X4) {  // the last 256 bytes as 16 lanes x 16 bytes (same LDS layout)
+                if (lane < 16) dma16(rs, 2048 + 16 * lane, dst + 2048);
+            } else {
+                dma4(rs, 2048 + 4 * lane, dst + 2048);
+            }
         }
     }
 
@@ -576,7 +638,7 @@ struct QuadEngine {
         for (int i = 0; i < R; ++i)
 #pragma unroll
             for (int c = 0; c < 9; ++c) W.d[i][c] = rd[slot][i][c];
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the reads are done before the slot is reloaded
+        wait_lgkm0();  // the reads are done before the slot is reloaded
     }
 
     template <class DS>
@@ -654,7 +716,7 @@ struct QuadEngine {
             const float e = row16_sum((g ? b23 : b01) + sw);
             acc.a0[i] = acc.a1[i] = acc.a2[i] = acc.a3[i] = 0.0f;
             if ((lane & 15) == 0)
-                store((int64_t)s * (WAVES * 4 * R) + wrow0 + 4 * i + (g ? 2 : 0) + (h ? 1 : 0), e);
+                store(i, (int64_t)s * (WAVES * 4 * R) + wrow0 + 4 * i + (g ? 2 : 0) + (h ? 1 : 0), e);
         }
     }
 };
@@ -712,6 +774,8 @@ k_sweep(const PlanDesc* __restrict__ descs, int count, SchedHead* head, const Sc
     constexpr int NB = E::kNB;
     extern __shared__ u4 xs[];
     __shared__ int q_next[2];  // ids of this workgroup's coming chunks (batch schedule)
+    __shared__ uint32_t lead;  // most units any wave of the workgroup has started (wave priority)
+    if (threadIdx.x == 0) lead = 0;  // (a barrier follows before the first use: chunk setup or staging)
     E eng;
     eng.init(reinterpret_cast<uint8_t*>(xs) + xs_bytes +
              __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) * E::kWaveLds);
@@ -789,7 +853,7 @@ k_sweep(const PlanDesc* __restrict__ descs, int count, SchedHead* head, const Sc
         hl = nx.c_end;
         Dl = get(cl_d);
         ++trans;
-        __syncthreads();  // q_next[(trans+1)&1] is written and q_next[trans&1] read by every wave
+        lds_barrier();  // q_next[(trans+1)&1] is written and q_next[trans&1] read by every wave
         const int id = __builtin_amdgcn_readfirstlane(q_next[(trans + 1) & 1]);
         nx_ok = id < n_chunks;
         if (nx_ok) nx = chunks[id];
@@ -831,12 +895,30 @@ k_sweep(const PlanDesc* __restrict__ descs, int count, SchedHead* head, const Sc
                 dc = u.d;
             }
             if (!NORM && u.d != staged) {  // (with the norm, staged before the first step)
-                __syncthreads();
+                lds_barrier();  // every wave is done with the previous activations
                 stage_x(Dc.x, Dc.k >> 5, Dc.npl * 16, XS > 0 ? XS : Dc.npl * 16, xs);
-                __syncthreads();
+                lds_barrier();
                 staged = u.d;
             }
             typename E::Regs W;
+            if (kFairPriority) {
+                // Among waves of equal priority a SIMD issues the oldest first, so
+                // the youngest wave of each SIMD falls behind, and the workgroup's
+                // barriers (chunk changes, activation staging) then hold the others,
+                // whose rings drain meanwhile.  A wave behind the leader raises its
+                // priority by how far it lags.
+                if ((threadIdx.x & 63) == 0) atomicMax(&lead, n_done);
+                const uint32_t behind =
+                    (uint32_t)__builtin_amdgcn_readfirstlane((int)(__hip_atomic_load(&lead, __ATOMIC_RELAXED,
+                                                                                    __HIP_MEMORY_SCOPE_WORKGROUP) -
+                                                                  n_done));
+                if ((int32_t)behind >= 2)
+                    __builtin_amdgcn_s_setprio(3);
+                else if ((int32_t)behind >= 1)
+                    __builtin_amdgcn_s_setprio(2);
+                else
+                    __builtin_amdgcn_s_setprio(0);
+            }
             eng.fetch(Dc, u.s, u.jb, slot, n_issued - 1u - n_done, W);
             ++n_done;
             if (have_l)
@@ -845,7 +927,7 @@ k_sweep(const PlanDesc* __restrict__ descs, int count, SchedHead* head, const Sc
                 r.d = -1;
             eng.math(Dc, u.jb, xs, W, acc);
             if (u.jb + 1 >= Dc.npl) {  // last unit of the wave's rows in this step
-                eng.finish(u.s, acc, [&](int64_t row, float v) {
+                eng.finish(u.s, acc, [&](int, int64_t row, float v) {
                     if (row < Dc.n) {
                         if (H16 || (BATCH && Dc.h16)) {
                             // stage hand-off: binary16 (nearest-even) of residual + y, into y's place
@@ -1171,7 +1253,14 @@ hipError_t launch_gemm_generic(const uint8_t* w, const uint16_t* x, float* y, in
 // (guided self-scheduling), at least one atom each, which workgroups take
 // from the shared counter as they run out of work.  Depends only on the
 // shapes and the device's CU count.
-static constexpr double kStaticShare = 0.6;
+#ifndef Q4_SCHED_STATIC
+#define Q4_SCHED_STATIC 0.6
+#endif
+#ifndef Q4_SCHED_DIV
+#define Q4_SCHED_DIV 3
+#endif
+static constexpr double kStaticShare = Q4_SCHED_STATIC;
+static constexpr int kGuidedDiv = Q4_SCHED_DIV;  // dynamic chunks: remaining / (kGuidedDiv * grid)
 
 void build_schedule(PlanDesc* descs, int count, std::vector<SchedChunk>* out, int* grid_out, int* flags_out) {
     // GEMVs with more units per row step first: the chunks handed out last
@@ -1217,7 +1306,8 @@ void build_schedule(PlanDesc* descs, int count, std::vector<SchedChunk>* out, in
     }
     while (a < n_atoms) {
         out->push_back(SchedChunk{atoms[a].d, atoms[a].s, 0});
-        const int64_t size = std::max<int64_t>(1, (total - cost_at(a) + 3 * grid - 1) / (3 * grid));
+        const int64_t size =
+            std::max<int64_t>(1, (total - cost_at(a) + kGuidedDiv * grid - 1) / (kGuidedDiv * (int64_t)grid));
         const int64_t end = cost_at(a) + size;
         ++a;
         while (a < n_atoms && cost_at(a) < end) ++a;
