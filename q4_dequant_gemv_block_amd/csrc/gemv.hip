@@ -75,6 +75,17 @@ constexpr int kQuadNB = Q4_QUAD_NB;  // units per wave in the quad engine's LDS 
 #define Q4_SWEEP_FAIR 1
 #endif
 constexpr bool kFairPriority = Q4_SWEEP_FAIR != 0;  // waves behind the workgroup's leader get a higher priority
+#ifndef Q4_FAIR_BEFORE_FETCH
+#define Q4_FAIR_BEFORE_FETCH 1
+#endif
+#ifndef Q4_FAIR_HIGH
+#define Q4_FAIR_HIGH 4
+#endif
+#ifndef Q4_FAIR_MID
+#define Q4_FAIR_MID 2
+#endif
+constexpr bool kFairBeforeFetch = Q4_FAIR_BEFORE_FETCH != 0;  // priority set before the wait for the unit
+constexpr int kFairHigh = Q4_FAIR_HIGH, kFairMid = Q4_FAIR_MID;  // lag (units) for priority 3 and 2
 
 struct Shape {
     int waves, r, wg_per_cu;
@@ -390,6 +401,14 @@ __device__ __forceinline__ Rsrc make_rsrc(const uint8_t* base, uint32_t bytes) {
     r.w.w = (uint32_t)kBufferWord3;
     return r;
 }
+// The same buffer moved `step` bytes on (base + step, size - step, at least 0).
+__device__ __forceinline__ Rsrc rsrc_advance(Rsrc r, uint32_t step) {
+    const uint64_t a = (((uint64_t)(r.w.y & 0xFFFFu)) << 32 | r.w.x) + step;
+    r.w.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    r.w.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xFFFFu);
+    r.w.z = __builtin_amdgcn_readfirstlane(r.w.z > step ? r.w.z - step : 0u);
+    return r;
+}
 // 16 (4) bytes per lane at byte offset voff of the buffer into LDS at M0 + 16 i (4 i).
 __device__ __forceinline__ void dma16(const Rsrc& r, uint32_t voff, uint8_t* dst) {
     asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(r.w), "{m0}"(lds_addr(dst))
@@ -455,8 +474,29 @@ struct DmaEngine {
         return !((int64_t)s * (WAVES * 4 * R) + wrow0 + 4 * R <= D.n && ((D.k >> 6) & 15) == 0);
     }
 
+    // Row step being loaded and its next segment.
+    const uint8_t* cw;
+    int64_t cn;
+    int32_t ck, cs, cjb;
     template <class DS>
-    __device__ __forceinline__ void issue(const DS& D, int s, int jb, int slot) {
+    __device__ __forceinline__ void begin(const DS& D, int s) {
+        cw = D.w;
+        cn = D.n;
+        ck = D.k;
+        cs = s;
+        cjb = 0;
+    }
+    struct Cursor {
+        const uint8_t* w;
+        int64_t n;
+        int32_t k;
+    };
+    __device__ __forceinline__ void issue(int slot) {
+        issue_at(Cursor{cw, cn, ck}, cs, cjb, slot);
+        ++cjb;
+    }
+    template <class DS>
+    __device__ __forceinline__ void issue_at(const DS& D, int s, int jb, int slot) const {
         const int np = D.k >> 6;
         const uint32_t rb = (uint32_t)np * kPairBytes;
         const int64_t row0 = (int64_t)s * (WAVES * 4 * R) + wrow0;
@@ -602,29 +642,41 @@ struct QuadEngine {
     // whose base is the slab and whose size ends at the matrix end: the
     // hardware returns zeros past the end (rows past N, never stored), every
     // lane is active, and the per-lane offsets are fixed.
+    // Descriptors of each quad's next slab.  A row step computes them once
+    // (begin); each issued unit moves them one slab on, so a unit costs a few
+    // scalar instructions.  (Scalar work between a unit's arrival and the
+    // next loads delays them: 128 dependent scalar instructions per unit cost
+    // 2 % of the read rate in a load-only probe of this access pattern.)
+    Rsrc cur[R];
     template <class DS>
-    __device__ __forceinline__ void issue(const DS& D, int s, int jb, int slot) const {
+    __device__ __forceinline__ void begin(const DS& D, int s) {
         const uint64_t rb = (uint32_t)(D.k >> 6) * kPairBytes;
         const uint64_t row0 = (uint64_t)s * (WAVES * 4 * R) + wrow0;
         const uint64_t end = (uint64_t)(uint32_t)D.n * rb;
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-            const uint64_t off = (row0 + 4 * i) * rb + (uint32_t)jb * kSlab;
+            const uint64_t off = (row0 + 4 * i) * rb;
             // bytes left after `off`, clamped to [0, 2^32 - 1] with 32-bit compares
             const int64_t left = (int64_t)(end - off);
             const int32_t hi = (int32_t)((uint64_t)left >> 32);
             const uint32_t nrec = hi < 0 ? 0u : (hi > 0 ? 0xFFFFFFFFu : (uint32_t)left);
-            const Rsrc rs = make_rsrc(D.w + off, nrec);
+            cur[i] = make_rsrc(D.w + off, nrec);
+        }
+    }
+    __device__ __forceinline__ void issue(int slot) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
             // The piece offsets ride in the per-lane offset: an instruction
             // offset would move the LDS destination as well.
             uint8_t* dst = wl + slot * kSlot + i * kSlab;
-            dma16(rs, 16 * lane, dst);
-            dma16(rs, 1024 + 16 * lane, dst + 1024);
+            dma16(cur[i], 16 * lane, dst);
+            dma16(cur[i], 1024 + 16 * lane, dst + 1024);
             if (Q4_QUAD_TAIL_X4) {  // the last 256 bytes as 16 lanes x 16 bytes (same LDS layout)
-                if (lane < 16) dma16(rs, 2048 + 16 * lane, dst + 2048);
+                if (lane < 16) dma16(cur[i], 2048 + 16 * lane, dst + 2048);
             } else {
-                dma4(rs, 2048 + 4 * lane, dst + 2048);
+                dma4(cur[i], 2048 + 4 * lane, dst + 2048);
             }
+            cur[i] = rsrc_advance(cur[i], kSlab);
         }
     }
 
@@ -826,6 +878,10 @@ k_sweep(const PlanDesc* __restrict__ descs, int count, SchedHead* head, const Sc
     // Move the load cursor one unit on; at the end of a chunk go to the next
     // one (batch) or stop.
     auto advance_l = [&]() {
+        if (cl_jb + 1 < Dl.npl) {  // the next unit of the same row step
+            ++cl_jb;
+            return;
+        }
         int d2 = cl_d, s2 = cl_s, jb2 = cl_jb + 1;
         if (jb2 >= Dl.npl) {
             jb2 = 0;
@@ -877,9 +933,29 @@ k_sweep(const PlanDesc* __restrict__ descs, int count, SchedHead* head, const Sc
             r.d = cl_d;
             r.s = cl_s;
             r.jb = cl_jb;
-            eng.issue(Dl, cl_s, cl_jb, slot);
+            if (cl_jb == 0) eng.begin(Dl, cl_s);  // (every row step starts at unit 0)
+            eng.issue(slot);
             ++n_issued;
             advance_l();
+        };
+        // Among waves of equal priority a SIMD issues the oldest first, so the
+        // youngest wave of each SIMD falls behind, and the workgroup's barriers
+        // (chunk changes, activation staging) then hold the others, whose rings
+        // drain meanwhile.  A wave behind the leader raises its priority by how
+        // far it lags.
+        auto update_priority = [&]() {
+            if (!kFairPriority) return;
+            if ((threadIdx.x & 63) == 0) atomicMax(&lead, n_done);
+            const int32_t behind = __builtin_amdgcn_readfirstlane(
+                (int)(__hip_atomic_load(&lead, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) - n_done));
+            if (behind >= kFairHigh)
+                __builtin_amdgcn_s_setprio(3);
+            else if (behind >= kFairMid)
+                __builtin_amdgcn_s_setprio(2);
+            else if (behind >= 1)
+                __builtin_amdgcn_s_setprio(1);
+            else
+                __builtin_amdgcn_s_setprio(0);
         };
         // One step on the unit in (r, slot): take a chunk id if one is owed,
         // stage the activations if the GEMV changed, read the unit's pairs,
@@ -901,30 +977,14 @@ k_sweep(const PlanDesc* __restrict__ descs, int count, SchedHead* head, const Sc
                 staged = u.d;
             }
             typename E::Regs W;
-            if (kFairPriority) {
-                // Among waves of equal priority a SIMD issues the oldest first, so
-                // the youngest wave of each SIMD falls behind, and the workgroup's
-                // barriers (chunk changes, activation staging) then hold the others,
-                // whose rings drain meanwhile.  A wave behind the leader raises its
-                // priority by how far it lags.
-                if ((threadIdx.x & 63) == 0) atomicMax(&lead, n_done);
-                const uint32_t behind =
-                    (uint32_t)__builtin_amdgcn_readfirstlane((int)(__hip_atomic_load(&lead, __ATOMIC_RELAXED,
-                                                                                    __HIP_MEMORY_SCOPE_WORKGROUP) -
-                                                                  n_done));
-                if ((int32_t)behind >= 2)
-                    __builtin_amdgcn_s_setprio(3);
-                else if ((int32_t)behind >= 1)
-                    __builtin_amdgcn_s_setprio(2);
-                else
-                    __builtin_amdgcn_s_setprio(0);
-            }
+            if (kFairBeforeFetch) update_priority();
             eng.fetch(Dc, u.s, u.jb, slot, n_issued - 1u - n_done, W);
             ++n_done;
             if (have_l)
                 issue_next(r, slot);
             else
                 r.d = -1;
+            if (!kFairBeforeFetch) update_priority();
             eng.math(Dc, u.jb, xs, W, acc);
             if (u.jb + 1 >= Dc.npl) {  // last unit of the wave's rows in this step
                 eng.finish(u.s, acc, [&](int, int64_t row, float v) {
