@@ -453,6 +453,7 @@ struct DmaEngine {
     int lane, l16;
     uint32_t rr0;    // row of this lane's first row within a step
     uint32_t wrow0;  // first row of this wave within a step
+    int64_t rbase = 0;  // first row of row step 0 (a single GEMV's workgroup range)
     uint8_t* wl;     // this wave's window
 
     __device__ __forceinline__ void init(uint8_t* window) {
@@ -471,7 +472,7 @@ struct DmaEngine {
     // Whether the unit reads clamped rows or a short segment (uniform).
     template <class DS>
     __device__ __forceinline__ bool edge(const DS& D, int s) const {
-        return !((int64_t)s * (WAVES * 4 * R) + wrow0 + 4 * R <= D.n && ((D.k >> 6) & 15) == 0);
+        return !(rbase + (int64_t)s * (WAVES * 4 * R) + wrow0 + 4 * R <= D.n && ((D.k >> 6) & 15) == 0);
     }
 
     // Row step being loaded and its next segment.
@@ -499,7 +500,7 @@ struct DmaEngine {
     __device__ __forceinline__ void issue_at(const DS& D, int s, int jb, int slot) const {
         const int np = D.k >> 6;
         const uint32_t rb = (uint32_t)np * kPairBytes;
-        const int64_t row0 = (int64_t)s * (WAVES * 4 * R) + wrow0;
+        const int64_t row0 = rbase + (int64_t)s * (WAVES * 4 * R) + wrow0;
         const uint32_t seg = (uint32_t)jb * kSeg;
         uint8_t* dst = wl + slot * kSlot;
         if (!edge(D, s)) {
@@ -570,7 +571,7 @@ struct DmaEngine {
     // After the last unit of row step s: row sums, in a fixed order.
     template <class F>
     __device__ __forceinline__ void finish(int s, Acc& acc, F&& store) const {
-        const int64_t r0 = (int64_t)s * (WAVES * 4 * R) + rr0;
+        const int64_t r0 = rbase + (int64_t)s * (WAVES * 4 * R) + rr0;
 #pragma unroll
         for (int i = 0; i < R; ++i) {
             const float v = row16_sum((acc.c0[i] + acc.c2[i]) + (acc.c1[i] + acc.c3[i]));
@@ -616,6 +617,7 @@ struct QuadEngine {
     int lane;
     uint32_t lane16;  // 16 * lane: this lane's byte offset in a chunk row of the activations
     uint32_t wrow0;   // first row of this wave within a step
+    int64_t rbase = 0;  // first row of row step 0 (a single GEMV's workgroup range)
     uint8_t* wl;      // this wave's ring
     lds_u32 rd[NB][R];  // this lane's pair in each slot and quad
 
@@ -651,7 +653,7 @@ struct QuadEngine {
     template <class DS>
     __device__ __forceinline__ void begin(const DS& D, int s) {
         const uint64_t rb = (uint32_t)(D.k >> 6) * kPairBytes;
-        const uint64_t row0 = (uint64_t)s * (WAVES * 4 * R) + wrow0;
+        const uint64_t row0 = (uint64_t)rbase + (uint64_t)s * (WAVES * 4 * R) + wrow0;
         const uint64_t end = (uint64_t)(uint32_t)D.n * rb;
 #pragma unroll
         for (int i = 0; i < R; ++i) {
@@ -768,7 +770,7 @@ struct QuadEngine {
             const float e = row16_sum((g ? b23 : b01) + sw);
             acc.a0[i] = acc.a1[i] = acc.a2[i] = acc.a3[i] = 0.0f;
             if ((lane & 15) == 0)
-                store(i, (int64_t)s * (WAVES * 4 * R) + wrow0 + 4 * i + (g ? 2 : 0) + (h ? 1 : 0), e);
+                store(i, rbase + (int64_t)s * (WAVES * 4 * R) + wrow0 + 4 * i + (g ? 2 : 0) + (h ? 1 : 0), e);
         }
     }
 };
@@ -832,7 +834,8 @@ k_sweep(const PlanDesc* __restrict__ descs, int count, SchedHead* head, const Sc
     eng.init(reinterpret_cast<uint8_t*>(xs) + xs_bytes +
              __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) * E::kWaveLds);
     const int n_desc = BATCH ? count : 1;
-    auto get = [&](int d) -> Live { return live_of(BATCH ? descs[d] : one); };
+    PlanDesc one_wg = one;  // a single GEMV: this workgroup's rows (below)
+    auto get = [&](int d) -> Live { return live_of(BATCH ? descs[d] : one_wg); };
 
     // The workgroup's first chunk.
     int cl_d, cl_s, cl_jb;  // next unit to load: descriptor, row step, unit within the step
@@ -846,13 +849,24 @@ k_sweep(const PlanDesc* __restrict__ descs, int count, SchedHead* head, const Sc
         hl = ch.c_end;
         have_l = true;
     } else {
-        const int64_t total = (int64_t)one.steps * one.npl;
+        // A single GEMV: workgroup g takes the rows of wave-row groups
+        // [groups * g / G, groups * (g + 1) / G) (groups of one wave's rows
+        // per step), its row steps counted from its first row; rows past its
+        // range are neither loaded nor stored.  Whole row steps per
+        // workgroup would leave some with one step more than others.
+        constexpr int64_t kGroup = E::kRowsPerWave;
+        constexpr int64_t kStep = (int64_t)E::kWaves * E::kRowsPerWave;
+        const int64_t groups = (one.n + kGroup - 1) / kGroup;
         const int64_t G = gridDim.x;
-        const int64_t c_lo = uniform64((total / G) * blockIdx.x + ((total % G) * blockIdx.x) / G);
-        hl = uniform64((total / G) * (blockIdx.x + 1) + ((total % G) * ((int64_t)blockIdx.x + 1)) / G);
+        const int64_t r0 = uniform64(groups * blockIdx.x / G * kGroup);
+        const int64_t r1 = uniform64(min(one.n, groups * ((int64_t)blockIdx.x + 1) / G * kGroup));
+        eng.rbase = r0;
+        one_wg.n = r1;
+        one_wg.steps = (r1 - r0 + kStep - 1) / kStep;
+        hl = one_wg.steps * one.npl;
         cl_d = 0;
-        cl_s = (int)uniform64((c_lo + one.npl - 1) / one.npl);
-        have_l = cl_s < one.steps && (int64_t)cl_s * one.npl < hl;
+        cl_s = 0;
+        have_l = r1 > r0;
     }
     cl_jb = 0;
     if (have_l) Dl = get(cl_d);
@@ -1122,6 +1136,25 @@ int device_cu_count() {
     return cus;
 }
 
+hipError_t allow_dynamic_lds(const void* kern, size_t bytes) {
+    struct Entry {
+        const void* kern;
+        int dev;
+        size_t bytes;
+    };
+    static std::mutex mu;
+    static std::vector<Entry> done;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    for (const Entry& x : done)
+        if (x.kern == kern && x.dev == dev && x.bytes >= bytes) return hipSuccess;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess) done.push_back(Entry{kern, dev, bytes});
+    return e;
+}
+
 static int npl_of(int64_t k) { return (int)(((k / 64) + 15) / 16); }
 
 // LDS of the staged activations: the fixed stride when k fits it, else k's own padding.
@@ -1157,7 +1190,7 @@ static hipError_t launch_sweep(const PlanDesc* descs, int count, SchedHead* head
     const size_t lds = xsb + (size_t)E::kWaves * E::kWaveLds;
     auto kern = k_sweep<E, XS, BATCH, AM, NORM, H16>;
     if (lds > 65536) {
-        const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        const hipError_t e = allow_dynamic_lds((const void*)kern, lds);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3(grid), dim3(E::kWaves * 64), lds, s, descs, count, head, chunks, one, (int)xsb,

@@ -67,6 +67,10 @@ hipError_t lm_head_scratch(uint64_t** keys);
 
 int device_cu_count();
 
+// Lets `kern` take `bytes` of dynamic LDS on the current device.  The runtime
+// call is made once per kernel, device and larger size, not per launch.
+hipError_t allow_dynamic_lds(const void* kern, size_t bytes);
+
 hipError_t launch_gemv(const uint8_t* w, const uint16_t* x, float* y, int64_t n, int64_t k,
                        hipStream_t s);
 hipError_t launch_gemm_generic(const uint8_t* w, const uint16_t* x, float* y, int64_t m,

@@ -367,7 +367,7 @@ static hipError_t launch_sm(const SmDesc* descs, int count, const SmDesc& one, i
     const size_t lds = smallm_lds(max_p, m);
     const void* kern = smallm_swizzle(max_p, m) ? (const void*)k_smallm<true> : (const void*)k_smallm<false>;
     if (lds > 65536) {
-        const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        const hipError_t e = allow_dynamic_lds((const void*)kern, lds);
         if (e != hipSuccess) return e;
     }
     if (smallm_swizzle(max_p, m))

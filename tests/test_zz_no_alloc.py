@@ -1,8 +1,9 @@
 """lm_head_argmax_noalloc (the LM head entry point that allocates nothing)
 against lm_head_argmax, the entry point with a caller's workspace: logits bit
-for bit, the same token, the oracle's bound and argmax rule; two calls in a
-row, the second with a smaller input (its keys array then still holds the
-first call's keys beyond the second call's grid)."""
+for bit, the same token, the oracle's bound and argmax rule; calls in a row,
+the second with a smaller input (its keys array then still holds the first
+call's keys beyond the second call's grid), the third the first size again
+(the one-launch counter must be back at zero)."""
 import numpy as np
 import pytest
 import torch
@@ -18,7 +19,8 @@ SEED = synth.DEFAULT_SEED
 def test_noalloc_equals_workspace_entry_point():
     q4 = lib()
     rng = np.random.default_rng(77)
-    cases = [(synth.VOCAB, synth.HIDDEN, 1500), (3001, 1024, 1501)]  # the second smaller
+    # the second smaller; the third the first again (the one-launch counter is back at zero after each call)
+    cases = [(synth.VOCAB, synth.HIDDEN, 1500), (3001, 1024, 1501), (synth.VOCAB, synth.HIDDEN, 1502)]
     for n, k, stream in cases:
         w = synth.q4_0(SEED, stream, n, k)
         h = synth.f16_normal(SEED, stream + 10, k)
