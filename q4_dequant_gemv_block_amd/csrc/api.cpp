@@ -670,14 +670,16 @@ q4_status q4_0_gemm_prefill_batch_plan(const q4_gemv_desc* descs, int count, int
     if (!aligned(plan_buf, 16)) return fail(Q4_ERR_MISALIGNED, "%s: plan buffer must be 16-byte aligned", fn);
     if (check_buffer(fn, "plan buffer", plan_buf, need, descs, count, m)) return Q4_ERR_INVALID_ARG;
     const int tile_m = q4::prefill_batch_tile_m(m);
-    // Two zeroed work counters, then the descriptors with k % 256 == 0 (run by
-    // the kernel that moves weights in 144-byte chunks), then the others, each
-    // part in list order and numbering its tiles from 0.
+    // Two work heads (per-XCD tile ranges, counters zero), then the
+    // descriptors with k % 256 == 0 (run by the kernel that moves weights in
+    // 144-byte chunks), then the others, each part in list order and numbering
+    // its tiles from 0.
     std::vector<uint8_t> host(need, 0);
     q4::PfDesc* dev = reinterpret_cast<q4::PfDesc*>(host.data() + 2 * sizeof(q4::PfHead));
     int64_t tiles[2] = {0, 0};
     int placed = 0;
-    for (int part = 0; part < 2; ++part)
+    for (int part = 0; part < 2; ++part) {
+        const int part_first = placed;
         for (int i = 0; i < count; ++i) {
             if ((descs[i].k % 256 == 0) != (part == 0)) continue;
             q4::PfDesc d = {};
@@ -691,6 +693,12 @@ q4_status q4_0_gemm_prefill_batch_plan(const q4_gemv_desc* descs, int count, int
             if (tiles[part] >= (int64_t(1) << 31)) return fail(Q4_ERR_INVALID_ARG, "%s: more than 2^31 tiles", fn);
             std::memcpy(&dev[placed++], &d, sizeof(d));
         }
+        // the part's tile ranges per XCD (descriptor indices relative to the part)
+        q4::PfHead head;
+        if (placed > part_first) q4::prefill_queues(dev + part_first, placed - part_first, tiles[part], &head);
+        else head = q4::PfHead{};
+        std::memcpy(host.data() + part * sizeof(q4::PfHead), &head, sizeof(head));
+    }
     const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipMemcpyAsync(plan_buf, host.data(), need, hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);

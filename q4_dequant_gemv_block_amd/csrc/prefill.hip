@@ -45,14 +45,17 @@
 // all M-tiles of one N-tile go to consecutive workgroups of the same XCD, so
 // a weight tile is read from HBM once and served from that XCD's L2 to the
 // others.  A list of GEMMs (the batch entry point) numbers its tiles in list
-// order (GEMM, N-tile, M-tile) and hands them out one at a time from a
-// counter in the plan, so the workgroups running at once share a few GEMMs
-// and their weight and activation tiles are re-read from the caches, not HBM.
+// order (GEMM, N-tile, M-tile), cuts that order into one range per XCD and
+// hands each range's tiles out one at a time to the workgroups of its XCD
+// (run_batch), so the M-tiles of a weight tile meet in one L2 and an
+// activation matrix is read by one XCD.
 #include "q4_device.h"
 #include "q4_launch.h"
 
 #include <algorithm>
+#include <cmath>
 #include <type_traits>
+#include <utility>
 
 namespace q4 {
 
@@ -122,9 +125,68 @@ __device__ __forceinline__ void dma_x1(const void* src, uint32_t m0) {
 // step; the asm is a compiler memory barrier, so no LDS access moves across.
 __device__ __forceinline__ void step_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// Instruction order of one pipeline phase for the scheduler: each MFMA is
+// followed by one LDS read (for the first NR MFMAs) and NV vector ALU ops,
+// so the reads and the expansion for the next phase run under the MFMAs.
+template <int M, int NR, int NV>
+__device__ __forceinline__ void sched_one() {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if constexpr (M < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // VALU
+}
+template <int NR, int NV, int... M>
+__device__ __forceinline__ void sched_phase(std::integer_sequence<int, M...>) {
+    (sched_one<M, NR, NV>(), ...);
+}
+
+// The batch schedule of both kernels.  The plan cuts the list's tiles
+// (numbered GEMM, N-tile, M-tile; M-tile fastest) into one contiguous range
+// per XCD.  Workgroup b runs on XCD b % 8 (the dispatcher deals workgroups
+// to the XCDs in turn) and takes that XCD's tiles one at a time, so the
+// M-tiles of a weight tile run side by side on one XCD: the weight tile is
+// fetched into that XCD's L2 once and read from there by the others, and an
+// activation matrix is read by one XCD (two at a range's ends), not by all
+// eight.  A workgroup whose range is used up helps the next XCD's range, and
+// so on round the eight.  The next tile number is fetched while the current
+// tile runs.  tile(D, t) computes tile t of descriptor D.
+template <typename Tile>
+__device__ __forceinline__ void run_batch(const PfDesc* __restrict__ descs, int count, PfHead* head, Tile&& tile) {
+    __shared__ uint32_t ticket;
+    const int home = (int)(blockIdx.x % kPfQueues);
+    for (int v = 0; v < kPfQueues; ++v) {
+        PfQueue* q = &head->q[(home + v) % kPfQueues];
+        const int64_t begin = q->begin, end = q->end;
+        if (begin >= end) continue;
+        int d = q->d_first;
+        if (threadIdx.x == 0) ticket = atomicAdd(&q->next, 1u);
+        __syncthreads();
+        uint32_t t = __builtin_amdgcn_readfirstlane(ticket);
+        while (begin + (int64_t)t < end) {
+            const int64_t gt = begin + (int64_t)t;
+            while (d + 1 < count && descs[d + 1].tile_begin <= gt) ++d;
+            const PfDesc D = descs[d];
+            uint32_t following = 0;
+            if (threadIdx.x == 0) following = atomicAdd(&q->next, 1u);
+            tile(D, gt - D.tile_begin);
+            __syncthreads();  // every wave is done with this tile's LDS and has read `ticket`
+            if (threadIdx.x == 0) ticket = following;
+            __syncthreads();
+            t = __builtin_amdgcn_readfirstlane(ticket);
+        }
+        __syncthreads();  // every wave has read `ticket` before the next range's first number lands in it
+    }
+    if (threadIdx.x == 0) {
+        __threadfence();  // this workgroup's counter updates come first
+        if (atomicAdd(&head->done, 1u) == gridDim.x - 1) {  // last workgroup of the launch
+            for (int i = 0; i < kPfQueues; ++i) atomicExch(&head->q[i].next, 0u);
+            atomicExch(&head->done, 0u);
+        }
+    }
+}
+
 template <int IT, int NW, bool BATCH>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
-k_prefill(PfArgs one, const PfDesc* __restrict__ descs, int count, int64_t total, PfHead* head) {
+k_prefill(PfArgs one, const PfDesc* __restrict__ descs, int count, PfHead* head) {
     constexpr int BM = 32 * IT;
     constexpr int kTile = BM * kStepBytes;           // bytes of one activation tile
     constexpr int kInstr = kTile / (64 * 16) / NW;   // DMA instructions per wave per tile
@@ -303,51 +365,9 @@ k_prefill(PfArgs one, const PfDesc* __restrict__ descs, int count, int64_t total
         tile(one, (int64_t)m_tile * BM, (int64_t)n_tile * (64 * NW));
         return;
     }
-    // Batch: tiles are numbered in list order (GEMM, N-tile, M-tile; M-tile
-    // fastest) and handed out one at a time from the plan's counter, so the
-    // workgroups running at any moment share a few GEMMs: the M-tiles of an
-    // N-tile read the same weight rows close together in time, and an
-    // activation matrix is read by all N-tiles of its GEMM while it is hot in
-    // the caches.  The next number is fetched while the current tile runs.
-    __shared__ uint32_t ticket;
-    if (threadIdx.x == 0) ticket = atomicAdd(&head->next, 1u);
-    __syncthreads();
-    uint32_t t = __builtin_amdgcn_readfirstlane(ticket);
-    int d = 0;
-    while ((int64_t)t < total) {
-        while (d + 1 < count && descs[d + 1].tile_begin <= (int64_t)t) ++d;
-        const PfDesc D = descs[d];
-        const int64_t local = (int64_t)t - D.tile_begin;
-        uint32_t following = 0;
-        if (threadIdx.x == 0) following = atomicAdd(&head->next, 1u);
+    run_batch(descs, count, head, [&](const PfDesc& D, int64_t local) {
         tile(D, (local % D.mt) * BM, (local / D.mt) * (64 * NW));
-        __syncthreads();  // every wave is done with this tile's buffers and has read `ticket`
-        if (threadIdx.x == 0) ticket = following;
-        __syncthreads();
-        t = __builtin_amdgcn_readfirstlane(ticket);
-    }
-    if (threadIdx.x == 0) {
-        __threadfence();  // this workgroup's counter updates come first
-        if (atomicAdd(&head->done, 1u) == gridDim.x - 1) {  // last workgroup of the launch
-            atomicExch(&head->next, 0u);
-            atomicExch(&head->done, 0u);
-        }
-    }
-}
-
-// Wait until at most `n` of this wave's loads are outstanding (n is one of
-// the few values the step schedule produces; the count is an immediate).
-template <int A, int B, int C>
-__device__ __forceinline__ void wait_vm_upto(int n) {
-    static_assert(A < 16 && B < 16 && C < 16, "vmcnt values below 16");
-    if (n == 0)
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-    else if (n == A)
-        __builtin_amdgcn_s_waitcnt(0x0F70 | A);
-    else if (n == B)
-        __builtin_amdgcn_s_waitcnt(0x0F70 | B);
-    else
-        __builtin_amdgcn_s_waitcnt(0x0F70 | C);
+    });
 }
 
 // Prefill for k % 256 == 0: weights move in 144-byte row chunks.
@@ -368,10 +388,25 @@ __device__ __forceinline__ void wait_vm_upto(int n) {
 // same outputs, which meet once per tile: in rounds of one activation tile,
 // each wave hands the partner the tile the partner stores, through LDS, and
 // adds what it receives (own + partner; the sum is the same either way).
-// Activation tiles move per step as in the other kernel (ring of three).
-template <int IT, int NWN, int XD, bool BATCH>
-__global__ void __launch_bounds__(128 * NWN) __attribute__((amdgpu_waves_per_eu(2)))
-k_prefill_q(PfArgs one, const PfDesc* __restrict__ descs, int count, int64_t total, PfHead* head) {
+//
+// The K loop is software-pipelined.  A step's work for a wave is two phases
+// (its two k-substeps), each 2 IT MFMAs from one set of A registers and two B
+// operands.  While a phase's MFMAs run, the wave reads the next phase's A
+// operands from LDS and expands the next B operands, so the matrix cores are
+// not left waiting for LDS latency or the dequantization:
+//   phase (s, 0): MFMAs of substep 0; read A(s, 1) and the raw weights of
+//                 step s + 1; expand B(s, 1)
+//   phase (s, 1): MFMAs of substep 1; read A(s + 1, 0); spread the weights of
+//                 step s + 1 and expand B(s + 1, 0)
+// Steps go in pairs between workgroup barriers, and the last phase of pair t
+// already reads step 2t + 2, so the barrier of pair t guarantees steps up to
+// 2t + 2: activations live in a ring of five step slots, and the loads
+// issued after the barrier of pair t (steps 2t + 3, 2t + 4, and weight chunk
+// t / 2 + 1 at even t) refill the slots of pair t - 1.  Every wave waits for
+// all of its loads before each barrier.
+template <int IT, int NWN, bool BATCH>
+__global__ void __launch_bounds__(128 * NWN) __attribute__((amdgpu_waves_per_eu(2, 2)))
+k_prefill_q(PfArgs one, const PfDesc* __restrict__ descs, int count, PfHead* head) {
     constexpr int NW = 2 * NWN;
     constexpr int BM = 32 * IT;
     constexpr int BN = 64 * NWN;
@@ -383,7 +418,7 @@ k_prefill_q(PfArgs one, const PfDesc* __restrict__ descs, int count, int64_t tot
     constexpr int kWPieces = kW / 16;             // 9 per row
     constexpr int kWFull = kWPieces / (NW * 64);  // weight DMA instructions of every wave (4)
     static_assert(kWPieces - kWFull * NW * 64 == NW * 32, "the rest is one instruction of half the waves");
-    constexpr int kXS = 2 * (XD + 1);             // activation slots: XD step pairs ahead of the one computed
+    constexpr int kXS = 5;                        // activation step slots
     constexpr int kLds = kXS * kX + 2 * kW;       // activation ring, weight ring of two chunks
     constexpr int kHalf = IT / 2;                 // activation tiles each wave of a slice stores
     static_assert(IT % 2 == 0 && NW * 64 * 32 * 4 <= kLds, "exchange rounds fit the ring space");
@@ -395,7 +430,6 @@ k_prefill_q(PfArgs one, const PfDesc* __restrict__ descs, int count, int64_t tot
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int wh = wave / NWN;  // block of each step's pair this wave takes
     const int wsl = wave % NWN; // weight slice
-    const int nw_mine = kWFull + (wave < NW / 2 ? 1 : 0);
     const uint32_t lds0 = lds_addr(lds);
 
     // A-operand offsets: chunk 2 ks + g of activation row 32 i + li, ks = 2 wh + hk.
@@ -458,105 +492,126 @@ k_prefill_q(PfArgs one, const PfDesc* __restrict__ descs, int count, int64_t tot
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    // B operands of step s for rows j = 0, 1: block H of the step's pair, as
-    // the code pairs P (spread) and the scale sc; H is this wave's block half
-    // (a template constant, so no per-lane select between the two layouts).
-    auto weights = [&](int s, auto Hc, uint32_t (&P)[2][4], h2 (&sc)[2]) {
+    // A operands of substep hk of step s: IT activation tiles.
+    auto read_a = [&](int s, int hk, h8 (&A)[IT]) {
+        const uint8_t* xt = lds + (s % kXS) * kX;
+#pragma unroll
+        for (int i = 0; i < IT; ++i) A[i] = *(const h8*)(xt + aoff[hk] + 4096 * i);
+    };
+    // Raw weight dwords of step s for rows j = 0, 1: block H of the step's pair
+    // (H is this wave's block half, a template constant, so no per-lane select
+    // between the two layouts): code dwords c[j][0..2] and the scale dword.
+    auto read_w = [&](int s, auto Hc, uint32_t (&c)[2][3], uint32_t (&sd)[2]) {
         constexpr int H = decltype(Hc)::value;
         const uint8_t* wt = lds + kXS * kX + ((s >> 2) & 1) * kW + kPairBytes * (s & 3);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const uint8_t* r = wt + 32 * kChunk * j;
-            const uint32_t c0 = *(const uint32_t*)(r + wcode);
-            const uint32_t c1 = *(const uint32_t*)(r + wcode + 4);
-            const uint32_t sd = *(const uint32_t*)(r + wscale);
+            c[j][0] = *(const uint32_t*)(r + wcode);
+            c[j][1] = *(const uint32_t*)(r + wcode + 4);
+            if constexpr (H == 0) c[j][2] = *(const uint32_t*)(r + wcode + 8);  // block 0 codes start at byte 2
+            sd[j] = *(const uint32_t*)(r + wscale);
+        }
+    };
+    // Code pairs P (spread) and scales of the raw dwords.
+    auto spread_w = [&](auto Hc, const uint32_t (&c)[2][3], const uint32_t (&sd)[2], uint32_t (&P)[2][4],
+                        h2 (&sc)[2]) {
+        constexpr int H = decltype(Hc)::value;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
             uint32_t e0, e1;
             _Float16 d;
-            if constexpr (H == 0) {  // block 0 codes start at byte 2: three dwords
-                const uint32_t c2 = *(const uint32_t*)(r + wcode + 8);
-                e0 = __builtin_amdgcn_perm(c1, c0, 0x05040302u);
-                e1 = __builtin_amdgcn_perm(c2, c1, 0x05040302u);
-                d = as_h2(sd).x;
+            if constexpr (H == 0) {
+                e0 = __builtin_amdgcn_perm(c[j][1], c[j][0], 0x05040302u);
+                e1 = __builtin_amdgcn_perm(c[j][2], c[j][1], 0x05040302u);
+                d = as_h2(sd[j]).x;
             } else {
-                e0 = c0;
-                e1 = c1;
-                d = as_h2(sd).y;
+                e0 = c[j][0];
+                e1 = c[j][1];
+                d = as_h2(sd[j]).y;
             }
             spread(e0, e1, P[j]);
             sc[j] = h2{d, d};
         }
     };
-    auto products = [&](const h8 (&av)[2][IT], const uint32_t (&P)[2][4], const h2 (&sc)[2]) {
+    auto expand = [&](auto HKc, const uint32_t (&P)[2][4], const h2 (&sc)[2], u4 (&bw)[2]) {
 #pragma unroll
-        for (int hk = 0; hk < 2; ++hk) {
-            u4 bw[2];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) bw[j] = hk ? expand8<true>(P[j], sc[j]) : expand8<false>(P[j], sc[j]);
-#pragma unroll
-            for (int i = 0; i < IT; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[hk][i], __builtin_bit_cast(h8, bw[j]),
-                                                                       acc[i][j], 0, 0, 0);
-        }
+        for (int j = 0; j < 2; ++j) bw[j] = decltype(HKc)::value ? expand8<true>(P[j], sc[j]) : expand8<false>(P[j], sc[j]);
     };
-    // One step: its A operands (two k-substeps of IT activation tiles), its
-    // B operands, then the products.
-    auto compute = [&](int s, auto Hc) {
-        h8 av[2][IT];
-        const uint8_t* xt = lds + (s % kXS) * kX;
+    auto mfma = [&](const h8 (&A)[IT], const u4 (&bw)[2]) {
 #pragma unroll
-        for (int hk = 0; hk < 2; ++hk)
+        for (int i = 0; i < IT; ++i)
 #pragma unroll
-            for (int i = 0; i < IT; ++i) av[hk][i] = *(const h8*)(xt + aoff[hk] + 4096 * i);
-        uint32_t P[2][4];
-        h2 sc[2];
-        weights(s, Hc, P, sc);
-        products(av, P, sc);
+            for (int j = 0; j < 2; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i], __builtin_bit_cast(h8, bw[j]), acc[i][j], 0, 0, 0);
     };
-    auto compute_pair = [&](int t, auto Hc) {
-        compute(2 * t, Hc);
-        compute(2 * t + 1, Hc);
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+
+    // Pipeline registers: A0/bw0 feed substep 0, A1/bw1 substep 1; Pc/scc are
+    // the spread weights of the current step, cn/sdn the raw ones of the next.
+    h8 A0[IT], A1[IT];
+    u4 bw0[2], bw1[2];
+    uint32_t Pc[2][4], cn[2][3], sdn[2];
+    h2 scc[2];
+
+    // One step s (its two phases); sn is the step whose operands are read
+    // ahead (s + 1, clamped to the last step: reads past the end are unused).
+    auto step = [&](int s, int sn, auto Hc) {
+        // phase (s, 0)
+        mfma(A0, bw0);
+        read_a(s, 1, A1);
+        read_w(sn, Hc, cn, sdn);
+        expand(I1{}, Pc, scc, bw1);
+        sched_phase<IT + 4, 3>(std::make_integer_sequence<int, 2 * IT>{});
+        __builtin_amdgcn_sched_barrier(0);
+        // phase (s, 1)
+        mfma(A1, bw1);
+        read_a(sn, 0, A0);
+        spread_w(Hc, cn, sdn, Pc, scc);
+        expand(I0{}, Pc, scc, bw0);
+        sched_phase<IT, 5>(std::make_integer_sequence<int, 2 * IT>{});
+        __builtin_amdgcn_sched_barrier(0);
     };
 
-    // Steps go in pairs between barriers (k % 256 == 0: the step count is a
-    // multiple of four; weight chunk u serves pairs 2u and 2u + 1).  Issue
-    // order: W(0), then the activations of pairs 0 .. XD - 1; after the
-    // barrier of pair t, the activations of pair t + XD, then W(t / 2 + 1)
-    // when t is even.  At the barrier of pair t (XD = 1 or 2) the loads that
-    // may stay out are the activations of pairs t + 1 .. t + XD - 1 and, at
-    // odd t, W(t / 2 + 1) issued at pair t - 1; every other earlier load is
-    // needed now (for XD = 2 and even t, W(t / 2) comes after the pair's own
-    // activations).
-    static_assert(XD == 1 || XD == 2, "lookahead of one or two step pairs");
-    const int npairs = a.np >> 1;
+    const int np = a.np;
+    const int npairs = np >> 1;
+    // Prologue: weight chunk 0 and steps 0 .. 2, then the barrier of pair 0
+    // and the first step's operands.
     issue_w(0);
-    for (int t = 0; t < XD && t < npairs; ++t) {
-        issue_x(2 * t);
-        issue_x(2 * t + 1);
-    }
+    issue_x(0);
+    issue_x(1);
+    issue_x(2);  // np >= 4
     auto kloop = [&](auto Hc) {
-    for (int t = 0; t < npairs; ++t) {
-        const int x_out = min(XD - 1, npairs - 1 - t);
-        const int w_out = (t & 1) && (t >> 1) + 1 < nsup;
-        const int out = 2 * kXI * x_out + nw_mine * w_out;
-        if (wave < NW / 2)
-            wait_vm_upto<2 * kXI * (XD - 1), kWFull + 1, 2 * kXI * (XD - 1) + kWFull + 1>(out);
-        else
-            wait_vm_upto<2 * kXI * (XD - 1), kWFull, 2 * kXI * (XD - 1) + kWFull>(out);
-        step_barrier();  // every wave's loads of the pair are in LDS; the slots refilled next are free
-        if (t + XD < npairs) {
-            issue_x(2 * (t + XD));
-            issue_x(2 * (t + XD) + 1);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        step_barrier();
+        if (3 < np) issue_x(3);
+        if (4 < np) issue_x(4);
+        if (1 < nsup) issue_w(1);
+        read_a(0, 0, A0);
+        {
+            uint32_t c[2][3], sd[2];
+            read_w(0, Hc, c, sd);
+            spread_w(Hc, c, sd, Pc, scc);
         }
-        if (!(t & 1) && (t >> 1) + 1 < nsup) issue_w((t >> 1) + 1);
-        compute_pair(t, Hc);
-    }
+        expand(I0{}, Pc, scc, bw0);
+        for (int t = 0; t < npairs; ++t) {
+            const int s0 = 2 * t;
+            step(s0, s0 + 1, Hc);
+            step(s0 + 1, min(s0 + 2, np - 1), Hc);
+            if (t + 1 == npairs) break;
+            // barrier of pair t + 1: steps up to 2t + 4 and their weight chunk are in LDS
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            step_barrier();
+            if (s0 + 5 < np) issue_x(s0 + 5);
+            if (s0 + 6 < np) issue_x(s0 + 6);
+            if (!((t + 1) & 1) && ((t + 1) >> 1) + 1 < nsup) issue_w(((t + 1) >> 1) + 1);
+        }
     };
     if (wh == 0)
-        kloop(std::integral_constant<int, 0>{});
+        kloop(I0{});
     else
-        kloop(std::integral_constant<int, 1>{});
+        kloop(I1{});
 
     // The slice's two partial sums meet: round r, wave h = 0 hands over tile
     // kHalf + r and keeps tile r; wave h = 1 the other way round.  Each lane's
@@ -640,30 +695,9 @@ k_prefill_q(PfArgs one, const PfDesc* __restrict__ descs, int count, int64_t tot
         tile(one, (int64_t)m_tile * BM, (int64_t)n_tile * BN);
         return;
     }
-    __shared__ uint32_t ticket;
-    if (threadIdx.x == 0) ticket = atomicAdd(&head->next, 1u);
-    __syncthreads();
-    uint32_t t = __builtin_amdgcn_readfirstlane(ticket);
-    int d = 0;
-    while ((int64_t)t < total) {
-        while (d + 1 < count && descs[d + 1].tile_begin <= (int64_t)t) ++d;
-        const PfDesc D = descs[d];
-        const int64_t local = (int64_t)t - D.tile_begin;
-        uint32_t following = 0;
-        if (threadIdx.x == 0) following = atomicAdd(&head->next, 1u);
+    run_batch(descs, count, head, [&](const PfDesc& D, int64_t local) {
         tile(D, (local % D.mt) * BM, (local / D.mt) * BN);
-        __syncthreads();  // every wave is done with this tile's LDS and has read `ticket`
-        if (threadIdx.x == 0) ticket = following;
-        __syncthreads();
-        t = __builtin_amdgcn_readfirstlane(ticket);
-    }
-    if (threadIdx.x == 0) {
-        __threadfence();
-        if (atomicAdd(&head->done, 1u) == gridDim.x - 1) {
-            atomicExch(&head->next, 0u);
-            atomicExch(&head->done, 0u);
-        }
-    }
+    });
 }
 
 template <int IT, int NW>
@@ -674,7 +708,7 @@ hipError_t launch(PfArgs a, hipStream_t s) {
     const int64_t ngroups = (a.nt + kXcd - 1) / kXcd;
     const int64_t grid = ngroups * kXcd * a.mt;
     hipLaunchKernelGGL((k_prefill<IT, NW, false>), dim3((unsigned)grid), dim3(NW * 64), 0, s, a, nullptr, 0,
-                       (int64_t)0, nullptr);
+                       nullptr);
     return hipGetLastError();
 }
 
@@ -682,7 +716,7 @@ template <int IT, int NW>
 hipError_t launch_batch(PfHead* head, const PfDesc* descs, int count, int64_t tiles, hipStream_t s) {
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(tiles, 2 * (int64_t)device_cu_count()));
     PfArgs none = {};
-    hipLaunchKernelGGL((k_prefill<IT, NW, true>), dim3(grid), dim3(NW * 64), 0, s, none, descs, count, tiles, head);
+    hipLaunchKernelGGL((k_prefill<IT, NW, true>), dim3(grid), dim3(NW * 64), 0, s, none, descs, count, head);
     return hipGetLastError();
 }
 
@@ -693,8 +727,8 @@ hipError_t launch_q(PfArgs a, hipStream_t s) {
     a.tile_begin = 0;
     const int64_t ngroups = (a.nt + kXcd - 1) / kXcd;
     const int64_t grid = ngroups * kXcd * a.mt;
-    hipLaunchKernelGGL((k_prefill_q<IT, NWN, 1, false>), dim3((unsigned)grid), dim3(NWN * 128), 0, s, a, nullptr, 0,
-                       (int64_t)0, nullptr);
+    hipLaunchKernelGGL((k_prefill_q<IT, NWN, false>), dim3((unsigned)grid), dim3(NWN * 128), 0, s, a, nullptr, 0,
+                       nullptr);
     return hipGetLastError();
 }
 
@@ -703,8 +737,7 @@ hipError_t launch_batch_q(PfHead* head, const PfDesc* descs, int count, int64_t 
     // one workgroup of 2 NWN waves per CU (the LDS ring takes most of a CU's 160 KiB)
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(tiles, (int64_t)device_cu_count()));
     PfArgs none = {};
-    hipLaunchKernelGGL((k_prefill_q<IT, NWN, 1, true>), dim3(grid), dim3(NWN * 128), 0, s, none, descs, count, tiles,
-                       head);
+    hipLaunchKernelGGL((k_prefill_q<IT, NWN, true>), dim3(grid), dim3(NWN * 128), 0, s, none, descs, count, head);
     return hipGetLastError();
 }
 
@@ -749,6 +782,41 @@ int64_t prefill_fill(PfDesc* d, int tile_m, int64_t tile_begin) {
     d->nt = (int)((d->n + 255) / 256);
     d->tile_begin = tile_begin;
     return (int64_t)d->mt * d->nt;
+}
+
+void prefill_queues(const PfDesc* descs, int count, int64_t tiles, PfHead* head) {
+    // Work of a tile ~ its K (block pairs); the cut points fall on N-tile
+    // boundaries, at the first one where the work before reaches x/8 of all.
+    double total = 0.0;
+    for (int i = 0; i < count; ++i) total += (double)descs[i].mt * descs[i].nt * descs[i].np;
+    int64_t cut[kPfQueues + 1];
+    cut[0] = 0;
+    cut[kPfQueues] = tiles;
+    int d = 0;
+    double before = 0.0;  // work of the descriptors before d
+    for (int x = 1; x < kPfQueues; ++x) {
+        const double target = total * x / kPfQueues;
+        while (d < count && before + (double)descs[d].mt * descs[d].nt * descs[d].np < target) {
+            before += (double)descs[d].mt * descs[d].nt * descs[d].np;
+            ++d;
+        }
+        if (d == count) {
+            cut[x] = tiles;
+            continue;
+        }
+        const double group = (double)descs[d].mt * descs[d].np;  // one N-tile's M-tiles
+        int64_t groups = (int64_t)std::ceil((target - before) / group);
+        groups = std::min<int64_t>(std::max<int64_t>(groups, 0), descs[d].nt);
+        cut[x] = std::max(cut[x - 1], descs[d].tile_begin + groups * descs[d].mt);
+    }
+    *head = PfHead{};
+    int first = 0;
+    for (int x = 0; x < kPfQueues; ++x) {
+        while (first + 1 < count && descs[first + 1].tile_begin <= cut[x]) ++first;
+        head->q[x].begin = cut[x];
+        head->q[x].end = cut[x + 1];
+        head->q[x].d_first = first;
+    }
 }
 
 hipError_t launch_gemm_prefill_batch(void* plan, int n_chunked, int64_t tiles_chunked, int n_other,

@@ -116,16 +116,32 @@ struct PfDesc {
     int mt, nt;         // tiles along M and N
     int64_t tile_begin; // tiles of the earlier descriptors of the list
 };
-// Work counter of a prefill batch plan (first 16 bytes of the plan buffer):
-// workgroups take tile numbers from `next`; the last one to finish a launch
-// sets both fields back to zero, so the plan is ready for the next launch.
-struct PfHead {
+// One XCD's share of a prefill batch: tiles [begin, end) of the list's
+// numbering, handed out one at a time through `next`; d_first is the
+// descriptor that holds tile `begin`.
+struct PfQueue {
     uint32_t next;
+    int32_t d_first;
+    int64_t begin, end;
+    int64_t reserved;
+};
+constexpr int kPfQueues = 8;  // one per XCD
+// Work counters of one kernel's part of a prefill batch plan.  Workgroups on
+// XCD x take tiles from q[x] and, once it is empty, from the others in turn;
+// `done` counts finished workgroups, and the last one of a launch sets every
+// `next` and `done` back to zero, so the plan is ready for the next launch.
+struct PfHead {
     uint32_t done;
-    uint32_t reserved[2];
+    uint32_t reserved[7];
+    PfQueue q[kPfQueues];
 };
 int prefill_batch_tile_m(int64_t m);
 int64_t prefill_fill(PfDesc* d, int tile_m, int64_t tile_begin);
+// Cuts tiles [0, tiles) of `count` filled descriptors into the kPfQueues
+// queues of *head: contiguous ranges of about equal work (tiles weighted by
+// k), each starting at an N-tile, so every M-tile of a weight tile is run on
+// one XCD.  `next` and `done` are left zero.
+void prefill_queues(const PfDesc* descs, int count, int64_t tiles, PfHead* head);
 // `plan`: two PfHead, then the `n_chunked` descriptors with k % 256 == 0
 // (the kernel that moves weights in 144-byte chunks; tile numbers from 0),
 // then the `n_other` others (tile numbers from 0).

@@ -138,10 +138,11 @@ def test_prefill_validation(lib):
 
 
 def test_prefill_plan_bytes_layout(lib):
-    # two 16-byte work-counter heads (the k % 256 == 0 part and the rest), then
-    # one 64-byte descriptor per GEMM
+    # two 288-byte work heads (the k % 256 == 0 part and the rest: a 32-byte
+    # counter block and eight 32-byte per-XCD tile ranges), then one 64-byte
+    # descriptor per GEMM
     for count in (1, 2, 7, 448):
-        assert lib.q4_0_gemm_prefill_batch_plan_bytes(count) == 2 * 16 + 64 * count
+        assert lib.q4_0_gemm_prefill_batch_plan_bytes(count) == 2 * 288 + 64 * count
     assert lib.q4_0_gemm_prefill_batch_plan_bytes(0) == 0
     assert lib.q4_0_gemm_prefill_batch_plan_bytes((1 << 20) + 1) == 0
 
