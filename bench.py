@@ -100,15 +100,28 @@ def load_q4():
 
 
 def cpu_cores() -> int:
+    """Threads the oracle runs with: OMP_NUM_THREADS when set, else the CPUs
+    this process may run on."""
     env = os.environ.get("OMP_NUM_THREADS")
-    if env and env.isdigit():
+    if env and env.isdigit() and int(env) > 0:
         return int(env)
     return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(items, budget_s: float = 12.0) -> dict:
-    """Time the oracle over the sweep's GEMVs in order until about budget_s of
-    CPU work; report algorithmic GB/s (and the sweeps/s it implies)."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_rate(items, budget_s: float):
+    """Run the oracle over the sweep's GEMVs in order until about budget_s of
+    wall time; returns (algorithmic bytes, GEMVs, seconds)."""
     import oracle
     import synth
     done_bytes, done, t_total = 0, 0, 0.0
@@ -122,10 +135,27 @@ def cpu_baseline(items, budget_s: float = 12.0) -> dict:
         done += 1
         if t_total >= budget_s:
             break
+    return done_bytes, done, t_total
+
+
+def cpu_baseline(items, budget_s: float = 12.0, one_core_s: float = 4.0) -> dict:
+    """Time the oracle over the sweep's GEMVs in order until about budget_s of
+    CPU work with the thread count set explicitly (cpu_cores), then about
+    one_core_s on one thread; report algorithmic GB/s (and the sweeps/s it
+    implies)."""
+    import oracle
+    o = oracle.default()
+    threads = o.set_threads(cpu_cores())
+    done_bytes, done, t_total = _oracle_rate(items, budget_s)
+    o.set_threads(1)
+    b1, d1, t1 = _oracle_rate(items, one_core_s)
+    o.set_threads(threads)
     gbs = done_bytes / t_total / 1e9
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": cpu_cores(), "kind": "oracle",
-            "sample": "first %d of the sweep's GEMVs (%.2f GB of weights), binary64, %.1f s" % (
-                done, done_bytes / 1e9, t_total),
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "first %d of the sweep's GEMVs (%.2f GB of weights), binary64, %.1f s, %d threads" % (
+                done, done_bytes / 1e9, t_total, threads),
+            "cpu_model": cpu_model(), "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "one_core_gbps": round(b1 / t1 / 1e9, 4), "one_core_sample": "first %d GEMVs, %.1f s" % (d1, t1),
             "sweeps_per_s": round(gbs * 1e9 / SWEEP_BYTES, 6)}
 
 

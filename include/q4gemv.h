@@ -442,7 +442,7 @@ typedef struct q4_prefill_plan {
     void* device;          /* the caller's device buffer holding the descriptors */
     int count;             /* number of GEMMs */
     int m;                 /* token rows of every GEMM */
-    int tile_m;            /* internal: activation rows per tile (64 or 128) */
+    int tile_m;            /* internal: activation rows per tile (64, 96 or 128) */
     int count_chunked;     /* internal: GEMMs with k % 256 == 0 (first in the device list) */
     int64_t tiles_chunked; /* internal: their tiles */
     int64_t tiles_other;   /* internal: tiles of the other GEMMs */

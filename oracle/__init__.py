@@ -63,8 +63,19 @@ class Oracle:
         lib.q4o_gemv_handoff.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
         lib.q4o_gemv_handoff.restype = ctypes.c_int
         lib.q4o_q8_gemm_rows.argtypes = [vp, i64, i64, vp, i64, vp, vp]
+        lib.q4o_set_threads.argtypes = [ctypes.c_int]
+        lib.q4o_threads.restype = ctypes.c_int
         self.lib = lib
         self.path = path
+
+    def set_threads(self, n: int) -> int:
+        """Team size of the oracle's parallel loops from now on (timing only);
+        returns the size in effect."""
+        self.lib.q4o_set_threads(int(n))
+        return int(self.lib.q4o_threads())
+
+    def threads(self) -> int:
+        return int(self.lib.q4o_threads())
 
     def f16_to_f64(self, bits) -> np.ndarray:
         """Exact binary16 -> binary64 of uint16 bit patterns."""

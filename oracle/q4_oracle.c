@@ -60,6 +60,7 @@
  * Parallelism: OpenMP over independent outputs only; each sum is sequential.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 
@@ -249,3 +250,8 @@ void q4o_q8_gemm_rows(const uint8_t* w_rows, int64_t nrows, int64_t k,
         }
     }
 }
+
+/* Team size of the parallel loops above (timing only; what is computed does
+ * not depend on it): set, and read back. */
+void q4o_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int q4o_threads(void) { return omp_get_max_threads(); }

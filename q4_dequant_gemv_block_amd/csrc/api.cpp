@@ -689,7 +689,7 @@ q4_status q4_0_gemm_prefill_batch_plan(const q4_gemv_desc* descs, int count, int
             d.m = m;
             d.n = descs[i].n;
             d.k = (int)descs[i].k;
-            tiles[part] += q4::prefill_fill(&d, tile_m, tiles[part]);
+            tiles[part] += q4::prefill_fill(&d, part == 0 ? tile_m : q4::prefill_other_tile_m(tile_m), tiles[part]);
             if (tiles[part] >= (int64_t(1) << 31)) return fail(Q4_ERR_INVALID_ARG, "%s: more than 2^31 tiles", fn);
             std::memcpy(&dev[placed++], &d, sizeof(d));
         }
@@ -719,7 +719,7 @@ q4_status q4_0_gemm_prefill_batch(const q4_prefill_plan* plan, void* stream) {
     const char* fn = "q4_0_gemm_prefill_batch";
     if (!plan || !plan->device) return fail(Q4_ERR_INVALID_ARG, "%s: null plan", fn);
     const int n_other = plan->count - plan->count_chunked;
-    if (plan->count < 1 || plan->m < 1 || (plan->tile_m != 64 && plan->tile_m != 128) || plan->count_chunked < 0 ||
+    if (plan->count < 1 || plan->m < 1 || (plan->tile_m != 64 && plan->tile_m != 96 && plan->tile_m != 128) || plan->count_chunked < 0 ||
         n_other < 0 || (plan->count_chunked > 0) != (plan->tiles_chunked > 0) || (n_other > 0) != (plan->tiles_other > 0))
         return fail(Q4_ERR_INVALID_ARG, "%s: plan was not filled by q4_0_gemm_prefill_batch_plan", fn);
     const hipError_t e =

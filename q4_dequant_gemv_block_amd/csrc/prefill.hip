@@ -411,8 +411,10 @@ k_prefill_q(PfArgs one, const PfDesc* __restrict__ descs, int count, PfHead* hea
     constexpr int BM = 32 * IT;
     constexpr int BN = 64 * NWN;
     constexpr int kX = BM * kStepBytes;           // activation tile of one step
-    constexpr int kXI = kX / 1024 / NW;           // its dwordx4 DMA instructions per wave
-    static_assert(kXI >= 1 && kXI * NW * 1024 == kX, "activation tile split over the waves");
+    constexpr int kXTot = kX / 1024;              // its dwordx4 DMA instructions
+    constexpr int kXFull = kXTot / NW;            // ... of every wave
+    constexpr int kXRem = kXTot % NW;             // waves below this one issue one more
+    static_assert(kXFull >= 1 && kXTot * 1024 == kX, "activation tile split over the waves");
     constexpr int kChunk = 4 * kPairBytes;        // a weight row's bytes for four steps
     constexpr int kW = BN * kChunk;               // weight slot
     constexpr int kWPieces = kW / 16;             // 9 per row
@@ -420,8 +422,8 @@ k_prefill_q(PfArgs one, const PfDesc* __restrict__ descs, int count, PfHead* hea
     static_assert(kWPieces - kWFull * NW * 64 == NW * 32, "the rest is one instruction of half the waves");
     constexpr int kXS = 5;                        // activation step slots
     constexpr int kLds = kXS * kX + 2 * kW;       // activation ring, weight ring of two chunks
-    constexpr int kHalf = IT / 2;                 // activation tiles each wave of a slice stores
-    static_assert(IT % 2 == 0 && NW * 64 * 32 * 4 <= kLds, "exchange rounds fit the ring space");
+    constexpr int kLo = (IT + 1) / 2;             // wave h = 0 of a slice stores tiles [0, kLo), h = 1 the rest
+    static_assert(NW * 64 * 32 * 4 <= kLds, "exchange rounds fit the ring space");
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
 
     const int lane = threadIdx.x & 63;
@@ -453,9 +455,9 @@ k_prefill_q(PfArgs one, const PfDesc* __restrict__ descs, int count, PfHead* hea
     // Source offsets, fixed for the K loop (rows past N or M read the last row):
     //  * weight piece P = 64 (NW q + wave) + lane of a slot is piece P % 9 of
     //    row P / 9 and lands at byte 16 P of the slot;
-    //  * activation slot S = 64 (kXI wave + q) + lane holds chunk (S % 8) ^ swz
+    //  * activation slot S = 64 (NW q + wave) + lane holds chunk (S % 8) ^ swz
     //    of row S / 8, as in the other kernel.
-    uint32_t woff[kWFull + 1], xoff[kXI];
+    uint32_t woff[kWFull + 1], xoff[kXFull + 1];
 #pragma unroll
     for (int q = 0; q <= kWFull; ++q) {
         const int P = min(64 * (NW * q + wave) + lane, kWPieces - 1);
@@ -463,8 +465,8 @@ k_prefill_q(PfArgs one, const PfDesc* __restrict__ descs, int count, PfHead* hea
         woff[q] = (uint32_t)(row * rb + 16 * (P % 9));
     }
 #pragma unroll
-    for (int q = 0; q < kXI; ++q) {
-        const int slot = 64 * (wave * kXI + q) + lane;
+    for (int q = 0; q <= kXFull; ++q) {
+        const int slot = min(64 * (NW * q + wave) + lane, 64 * kXTot - 1);
         const int i = slot >> 3;
         const int c = (slot & 7) ^ swz(i);
         const int64_t row = min((int64_t)i, m_last);
@@ -472,9 +474,10 @@ k_prefill_q(PfArgs one, const PfDesc* __restrict__ descs, int count, PfHead* hea
     }
     auto issue_x = [&](int s) {
         const uint8_t* xb = xbase + (int64_t)s * kStepBytes;
-        const uint32_t dst = lds0 + (uint32_t)((s % kXS) * kX) + 1024u * (uint32_t)(wave * kXI);
+        const uint32_t dst = lds0 + (uint32_t)((s % kXS) * kX) + 1024u * (uint32_t)wave;
 #pragma unroll
-        for (int q = 0; q < kXI; ++q) dma_x4(xb + xoff[q], dst + 1024u * q);
+        for (int q = 0; q < kXFull; ++q) dma_x4(xb + xoff[q], dst + 1024u * (uint32_t)(NW * q));
+        if (kXRem > 0 && wave < kXRem) dma_x4(xb + xoff[kXFull], dst + 1024u * (uint32_t)(NW * kXFull));
     };
     auto issue_w = [&](int u) {
         const uint8_t* wb = wbase + (int64_t)u * kChunk;
@@ -613,53 +616,46 @@ k_prefill_q(PfArgs one, const PfDesc* __restrict__ descs, int count, PfHead* hea
     else
         kloop(I1{});
 
-    // The slice's two partial sums meet: round r, wave h = 0 hands over tile
-    // kHalf + r and keeps tile r; wave h = 1 the other way round.  Each lane's
-    // 32 floats go to (slot e4, lane) of the wave's 8 KiB region.
-#pragma unroll
-    for (int r = 0; r < kHalf; ++r) {
-        __syncthreads();  // the last step's (or the previous round's) LDS reads are done
+    // The slice's two partial sums meet: in round r, wave h = 0 hands over
+    // tile kLo + r (when there is one) and receives tile r, wave h = 1 hands
+    // over tile r and receives tile kLo + r.  Each lane's 32 floats go to
+    // (slot e4, lane) of the wave's 8 KiB region.  The sum is partner's plus
+    // own, the same value whichever wave stores it.
+    auto put = [&](int i) {
         float4* mine = (float4*)(lds + 8192 * wave);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4)
+                mine[(4 * j + e4) * 64 + lane] =
+                    float4{acc[i][j][4 * e4], acc[i][j][4 * e4 + 1], acc[i][j][4 * e4 + 2], acc[i][j][4 * e4 + 3]};
+    };
+    auto take = [&](int i) {
+        const float4* theirs = (const float4*)(lds + 8192 * (wh ? wave - NWN : wave + NWN));
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const float4 v = theirs[(4 * j + e4) * 64 + lane];
+                acc[i][j][4 * e4] += v.x;
+                acc[i][j][4 * e4 + 1] += v.y;
+                acc[i][j][4 * e4 + 2] += v.z;
+                acc[i][j][4 * e4 + 3] += v.w;
+            }
+    };
+#pragma unroll
+    for (int r = 0; r < kLo; ++r) {
+        __syncthreads();  // the last step's (or the previous round's) LDS reads are done
         if (wh == 0) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4)
-                    mine[(4 * j + e4) * 64 + lane] = float4{acc[kHalf + r][j][4 * e4], acc[kHalf + r][j][4 * e4 + 1],
-                                                             acc[kHalf + r][j][4 * e4 + 2], acc[kHalf + r][j][4 * e4 + 3]};
+            if (kLo + r < IT) put(kLo + r);
         } else {
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4)
-                    mine[(4 * j + e4) * 64 + lane] =
-                        float4{acc[r][j][4 * e4], acc[r][j][4 * e4 + 1], acc[r][j][4 * e4 + 2], acc[r][j][4 * e4 + 3]};
+            put(r);
         }
         __syncthreads();
-        const float4* theirs = (const float4*)(lds + 8192 * (wh ? wave - NWN : wave + NWN));
-        if (wh == 0) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) {
-                    const float4 v = theirs[(4 * j + e4) * 64 + lane];
-                    acc[r][j][4 * e4] += v.x;
-                    acc[r][j][4 * e4 + 1] += v.y;
-                    acc[r][j][4 * e4 + 2] += v.z;
-                    acc[r][j][4 * e4 + 3] += v.w;
-                }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) {
-                    const float4 v = theirs[(4 * j + e4) * 64 + lane];
-                    acc[kHalf + r][j][4 * e4] += v.x;
-                    acc[kHalf + r][j][4 * e4 + 1] += v.y;
-                    acc[kHalf + r][j][4 * e4 + 2] += v.z;
-                    acc[kHalf + r][j][4 * e4 + 3] += v.w;
-                }
-        }
+        if (wh == 0)
+            take(r);
+        else if (kLo + r < IT)
+            take(kLo + r);
     }
 
     // D layout of the 32x32 product: lane (li, g), element e -> row 8*(e/4) + 4*g + e%4, column li
@@ -673,12 +669,12 @@ k_prefill_q(PfArgs one, const PfDesc* __restrict__ descs, int count, PfHead* hea
     };
     if (wh == 0) {
 #pragma unroll
-        for (int i = 0; i < kHalf; ++i)
+        for (int i = 0; i < kLo; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j) store(i, j);
     } else {
 #pragma unroll
-        for (int i = kHalf; i < IT; ++i)
+        for (int i = kLo; i < IT; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j) store(i, j);
     }
@@ -743,9 +739,9 @@ hipError_t launch_batch_q(PfHead* head, const PfDesc* descs, int count, int64_t 
 
 }  // namespace
 
-// Tile shape by size: the largest tile (activation rows 32 IT x weight rows
-// 64 NW) that still gives every CU a workgroup, else the smallest.  (128 x
-// 128 is left out: it needs more than 256 registers, one wave per SIMD.)
+// Tile shape by size: the batch rule's activation rows (128, 96 or 64 x 256
+// weight rows) when that still gives every CU a workgroup, else 64 x 256,
+// else 64 x 128.
 hipError_t launch_gemm_prefill(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
                                int64_t k, hipStream_t s) {
     PfArgs a;
@@ -758,12 +754,16 @@ hipError_t launch_gemm_prefill(const uint8_t* w, const uint16_t* x, float* y, in
     a.np = (int)(k / 64);
     const int64_t cus = device_cu_count();
     auto tiles = [&](int it, int nw) { return ((m + 32 * it - 1) / (32 * it)) * ((n + 64 * nw - 1) / (64 * nw)); };
+    // the batch tile when it still gives every CU a workgroup, else the smallest
+    const int tm = prefill_batch_tile_m(m);
     if (k % 256 == 0) {
-        if (m > 96 && tiles(4, 4) >= cus) return launch_q<4, 4>(a, s);
+        if (tm == 128 && tiles(4, 4) >= cus) return launch_q<4, 4>(a, s);
+        if (tm == 96 && tiles(3, 4) >= cus) return launch_q<3, 4>(a, s);
         if (tiles(2, 4) >= cus) return launch_q<2, 4>(a, s);
         return launch_q<2, 2>(a, s);
     }
-    if (m > 96 && tiles(4, 4) >= cus) return launch<4, 4>(a, s);
+    if (tm == 128 && tiles(4, 4) >= cus) return launch<4, 4>(a, s);
+    if (tm == 96 && tiles(3, 4) >= cus) return launch<3, 4>(a, s);
     if (tiles(2, 4) >= cus) return launch<2, 4>(a, s);
     return launch<2, 2>(a, s);
 }
@@ -771,9 +771,18 @@ hipError_t launch_gemm_prefill(const uint8_t* w, const uint16_t* x, float* y, in
 // Tile rows for a batch of M-row GEMMs: 128 unless 64-row tiles pad M by
 // clearly less (M = 169: 192 rows against 256).
 int prefill_batch_tile_m(int64_t m) {
-    const int64_t p128 = (m + 127) / 128 * 128, p64 = (m + 63) / 64 * 64;
-    return (double)p128 <= 1.15 * (double)p64 ? 128 : 64;
+    // the largest of 128, 96 and 64 rows whose padded M is within 15 % of the
+    // least padded M (a larger tile re-reads weights and expands them less often)
+    const int64_t p128 = (m + 127) / 128 * 128, p96 = (m + 95) / 96 * 96, p64 = (m + 63) / 64 * 64;
+    const double least = (double)std::min(p128, std::min(p96, p64));
+    if ((double)p128 <= 1.15 * least) return 128;
+    if ((double)p96 <= 1.15 * least) return 96;
+    return 64;
 }
+
+// The other kernel's batched form has no 96-row tile (it would spill
+// registers); it runs 64-row tiles instead.
+int prefill_other_tile_m(int tile_m) { return tile_m == 96 ? 64 : tile_m; }
 
 // Fills mt, nt, np and tile_begin for the batch tile shape; returns the tiles.
 int64_t prefill_fill(PfDesc* d, int tile_m, int64_t tile_begin) {
@@ -825,11 +834,12 @@ hipError_t launch_gemm_prefill_batch(void* plan, int n_chunked, int64_t tiles_ch
     const PfDesc* descs = reinterpret_cast<const PfDesc*>(head + 2);
     hipError_t e = hipSuccess;
     if (n_chunked > 0)
-        e = tile_m == 128 ? launch_batch_q<4, 4>(head, descs, n_chunked, tiles_chunked, s)
-                          : launch_batch_q<2, 4>(head, descs, n_chunked, tiles_chunked, s);
+        e = tile_m == 128  ? launch_batch_q<4, 4>(head, descs, n_chunked, tiles_chunked, s)
+            : tile_m == 96 ? launch_batch_q<3, 4>(head, descs, n_chunked, tiles_chunked, s)
+                           : launch_batch_q<2, 4>(head, descs, n_chunked, tiles_chunked, s);
     if (e == hipSuccess && n_other > 0)
-        e = tile_m == 128 ? launch_batch<4, 4>(head + 1, descs + n_chunked, n_other, tiles_other, s)
-                          : launch_batch<2, 4>(head + 1, descs + n_chunked, n_other, tiles_other, s);
+        e = prefill_other_tile_m(tile_m) == 128 ? launch_batch<4, 4>(head + 1, descs + n_chunked, n_other, tiles_other, s)
+                                                : launch_batch<2, 4>(head + 1, descs + n_chunked, n_other, tiles_other, s);
     return e;
 }
 

@@ -136,6 +136,8 @@ struct PfHead {
     PfQueue q[kPfQueues];
 };
 int prefill_batch_tile_m(int64_t m);
+// Tile rows of the k % 256 != 0 part of a batch whose k % 256 == 0 part uses tile_m.
+int prefill_other_tile_m(int tile_m);
 int64_t prefill_fill(PfDesc* d, int tile_m, int64_t tile_begin);
 // Cuts tiles [0, tiles) of `count` filled descriptors into the kPfQueues
 // queues of *head: contiguous ranges of about equal work (tiles weighted by

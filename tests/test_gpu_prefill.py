@@ -54,12 +54,16 @@ def test_prompt_sizes_sampled(m):
         assert_parity(y.cpu().numpy()[:, rows], y_ref, a_ref, "prefill m=%d %dx%d" % (m, n, k))
 
 
-@pytest.mark.parametrize("m", [37, 100, 169, 512])
+TILE_M = {37: 64, 96: 96, 100: 128, 169: 96, 512: 128}
+
+
+@pytest.mark.parametrize("m", [37, 96, 100, 169, 512])
 def test_batch_parity_and_single_calls(m):
     """A mixed prefill list in one launch: every GEMM within the bound of the
     oracle and equal to its own q4_0_gemm_prefill call, with ragged M, N
-    (rows past a tile) and K (1088: 17 pairs).  M = 37 and 169 run on 64-row
-    tiles, M = 100 (ragged) and 512 on 128-row tiles, on both batch kernels
+    (rows past a tile) and K (1088: 17 pairs).  M = 37 runs on 64-row tiles,
+    M = 96 and 169 (ragged) on 96-row tiles (the k % 256 != 0 GEMMs on 64-row
+    ones), M = 100 (ragged) and 512 on 128-row tiles, on both batch kernels
     (k % 256 == 0 and the others)."""
     q4 = lib()
     shapes = [(300, 1024), (64, 2048), (257, 1088), (31, 4096), (512, 64)]
@@ -71,7 +75,7 @@ def test_batch_parity_and_single_calls(m):
         items.append((dev_u8(w), dev_f16(x), torch.full((m, n), float("nan"), device="cuda")))
     say("prefill batch m=%d of %d GEMMs" % (m, len(items)))
     batch = q4.PrefillBatch(items)
-    assert batch.plan.tile_m == (128 if m in (100, 512) else 64), batch.plan.tile_m
+    assert batch.plan.tile_m == TILE_M[m], batch.plan.tile_m
     batch()
     torch.cuda.synchronize()
     for (w, x), (wd, xd, yd), (n, k) in zip(host, items, shapes):
@@ -92,7 +96,7 @@ def test_batch_parity_and_single_calls(m):
 def test_batch_full_layers(m):
     """Layers 0 and 63 of the prefill workload the benchmark times (the
     sweep's weights, the prefill activations, the same batch kernel and tile
-    shape: 64-row tiles at M = 169, 128-row tiles at M = 512) as one batch of
+    shape: 96-row tiles at M = 169, 128-row tiles at M = 512) as one batch of
     14 GEMMs: every output of every GEMM against the oracle, and each GEMM bit
     for bit equal to its own q4_0_gemm_prefill call."""
     q4 = lib()
@@ -105,7 +109,7 @@ def test_batch_full_layers(m):
             items.append((dev_u8(w), dev_f16(x), torch.full((m, n), float("nan"), device="cuda")))
             host.append((layer, proj, w, x))
     batch = q4.PrefillBatch(items)
-    assert batch.plan.tile_m == (128 if m == 512 else 64)
+    assert batch.plan.tile_m == TILE_M[m]
     say("prefill full layers 0 and 63, m=%d, tile_m=%d" % (m, batch.plan.tile_m))
     batch()
     torch.cuda.synchronize()
