@@ -102,12 +102,12 @@ def test_metamorphic_bit_exact():
     y = run_gemv(w, x)
     # two runs are identical
     assert np.array_equal(y, run_gemv(w, x))
-    # negating x negates y, to the tolerance only: the hardware's f16 dot
-    # product rounds a few sums differently when every input changes sign
-    # (about 1 in 30,000 chains of 16 steps on MI355X), so the last bit of a
-    # row may differ
+    # negating x negates y up to the rounding of the f16 dot product, which
+    # is not symmetric in sign on MI355X (test_negation_dot2_rounding)
     y_ref, a_ref = oracle.gemm_rows(w, k, x)
-    assert_parity(-run_gemv(w, -x), y_ref, a_ref, "negated x")
+    yn = run_gemv(w, -x)
+    assert_parity(-yn, y_ref, a_ref, "negated x")
+    assert np.all(np.abs(y.astype(np.float64) + yn.astype(np.float64)) <= NEG_BOUND * a_ref)
     # doubling every scale doubles y (scales are normal f16: add one to the exponent)
     w2 = w.copy().reshape(n, k // 32, 18)
     d = (w2[:, :, 0].astype(np.uint16) | (w2[:, :, 1].astype(np.uint16) << 8)) + 0x0400
@@ -120,6 +120,39 @@ def test_metamorphic_bit_exact():
     dup = np.concatenate([np.arange(n), [5, 5, 700, 1023]])
     yd = run_gemv(w[dup], x)
     assert np.array_equal(yd, y[dup])
+
+
+# |y(x) + y(-x)| <= NEG_BOUND * a.  Binary32 additions, multiplications and
+# FMAs round to nearest-even, which commutes with negation; only the f16 dot
+# product steps may round a block's partial sum one unit in the last place
+# the other way, and the later exact-sign operations carry that difference
+# on.  Measured on MI355X: at most 16 units of the result, 2^-28 of a; the
+# bound is 256 times that, far below the 1e-3 parity tolerance.
+NEG_BOUND = 2.0 ** -20
+
+
+def test_negation_dot2_rounding():
+    """Negating x negates y exactly except where v_dot2_f32_f16 rounds a
+    chain step differently for the negated inputs.  On MI355X its rounding
+    is not symmetric in sign: a probe of 2^20 chains of 16 steps with
+    integer weights in [-8, 7] and normal f16 activations found 206 chains
+    whose -x result was not the bit negation of the +x one (one step each,
+    one unit in the last place).  Here: 65,536 rows x 5,120 columns; every
+    row within NEG_BOUND * a of the negation, and the rows that differ at
+    all a small fraction, which is recorded."""
+    n, k = 65536, 5120
+    w = synth.q4_0(SEED, 12002, n, k)
+    x = synth.f16_normal(SEED, 12003, k)
+    y = run_gemv(w, x).astype(np.float64)
+    yn = run_gemv(w, -x).astype(np.float64)
+    diff = np.nonzero(y != -yn)[0]
+    say("negation: %d of %d rows not bit-negated; first %s" % (diff.size, n, diff[:8].tolist()))
+    assert diff.size <= n // 100
+    if diff.size:
+        _, a_ref = oracle.gemm_rows(w[diff], k, x)
+        ratio = np.abs(y[diff] + yn[diff]) / a_ref
+        say("negation: largest |y(x) + y(-x)| / a = %.3g" % ratio.max())
+        assert np.all(ratio <= NEG_BOUND)
 
 
 def test_alignment_errors():
