@@ -87,7 +87,7 @@ struct SmDesc {
     int32_t P;           // pairs per K-range (a multiple of 16)
     int32_t nranges;     // K-ranges
     int32_t tiles;       // tiles of 256 rows
-    int32_t pad;
+    int32_t m;           // activation rows (the engine and its unit size depend on it)
     int64_t ws_off;      // first partial-sum float in the workspace (nranges > 1)
     int64_t cost_begin;  // units of the earlier descriptors
 };

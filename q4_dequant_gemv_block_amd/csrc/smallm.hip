@@ -14,28 +14,50 @@
 // activation row was measured at 1.8 TB/s for M = 2 down to 0.4 TB/s for
 // M = 16, bound by its LDS reads.)
 //
-// Work: a workgroup of 16 waves owns a tile of 256 weight rows (16 per wave)
-// and one K-range of its GEMM; the K-range is the longest run of 16-pair
-// segments whose activations for all M rows fit kXBytes of LDS, so K is split
-// only for large M and K (M = 16: 5120 columns).  Items (GEMM, K-range, tile)
-// are ordered GEMM, K-range, tile, and every workgroup takes a byte-balanced
-// contiguous run of them, so the activations of a K-range are staged once and
-// serve many tiles.  When a GEMM has several K-ranges each range writes its
-// partial product to the workspace and a second kernel adds the partials in
-// range order, so results are deterministic.
+// Work: a workgroup owns tiles of 16 weight rows per wave and one K-range of
+// its GEMM; the K-range is the longest run of 16-pair spans whose activations
+// for all M rows fit the LDS the weights leave free.  Items (GEMM, K-range,
+// tile) are ordered GEMM, K-range, tile, and every workgroup takes a
+// byte-balanced contiguous run of them, so the activations of a K-range are
+// staged once and serve many tiles.  When a GEMM has several K-ranges each
+// range writes its partial product to the workspace and a second kernel adds
+// the partials in range order, so results are deterministic.
 //
-// A wave's unit is its 16 rows x one 16-pair segment.  Lane (g, n) = (lane /
-// 16, lane % 16) loads pairs g, g+4, g+8, g+12 of the segment of weight row n
-// (the four lanes of a row cover its 576 contiguous bytes) into registers; the
-// loads of the next unit are issued before the current one is computed, also
-// across tiles, K-ranges and GEMMs.  Each pair expands to 8 chunks of 8 halves
-// ((code - 8) * d rounded once to f16: error <= 2^-11 of each weight, inside
-// the 1e-3 bound); chunk c of lane (g, n) is the B operand for weight row n,
-// and the A operand of lane (g, m) is chunk c of the same pair of activation
-// row m, read from LDS (rows m >= M are zero).  The 32 k of one MFMA are 8 k
-// from each of 4 pairs; both operands use the same assignment, so the sum is
-// the full dot product.  Rows beyond N and pairs beyond K/64 read clamped
-// in-range addresses and meet zero activations.
+// Each pair expands to 8 chunks of 8 halves ((code - 8) * d rounded once to
+// f16: error <= 2^-11 of each weight, inside the 1e-3 bound); chunk c of lane
+// (g, n) = (lane / 16, lane % 16) is the B operand for weight row n, and the A
+// operand of lane (g, m) is chunk c of the same pair of activation row m,
+// read from LDS (rows m >= M read row M - 1; those products are never
+// stored).  The 32 k of one MFMA are 8 k from each of 4 pairs; both operands
+// use the same assignment, so the sum is the full dot product.  Pairs beyond
+// K/64 meet zero activations.
+//
+// Two engines move the weights:
+//  * LDS ring (k_smallm_lds, M <= 7).  Weights move from HBM straight into
+//    LDS in whole lines, as in the M = 1 engine.  A workgroup of 8 waves owns
+//    128-row tiles; a wave's unit is its 16 rows x one 8-pair segment (288
+//    bytes per row), six buffer loads of 16 bytes per lane straight to LDS
+//    into a ring of two unit slots per wave (86 KiB in all, the activations
+//    get the other 76 KiB: K = 17,408 splits from M = 4 on), waited for
+//    with explicit vmcnt counts; a unit is read into registers and its slot
+//    refilled before it is computed.  The loads are cached: a segment shares
+//    its end lines with the row's next segment, which the same wave loads
+//    next (with the non-temporal hint those lines were fetched twice, 1.24x
+//    the bytes).  In a slot, row n's segment is four 80-byte groups, one per
+//    lane group g (bytes 72 g .. 72 g + 63 in four 16-byte pieces, then bytes
+//    72 g + 56 .. 72 g + 71), so the pairs 2g, 2g+1 of lane (g, n) start on a
+//    16-byte boundary; rows are 21 pieces apart (one pad piece), so the 16
+//    rows of one ds_read_b128 fall on distinct banks; the lane reads its pairs
+//    with five ds_read_b128.  Rows beyond N and bytes past the matrix end
+//    load zeros (the buffer descriptor ends at the matrix end).
+//  * Register loads (k_smallm_reg, M > 7), when the activations need the
+//    whole LDS (M = 16: 5,120 columns in one K-range).  A workgroup of 16
+//    waves owns 256-row tiles; lane (g, n) loads pairs g, g+4, g+8, g+12 of
+//    its row's 16-pair segment (the four lanes of a row cover its 576
+//    contiguous bytes) into registers, the next unit's loads issued before
+//    the current one is computed.  These loads touch about 32 lines per
+//    instruction and bind the L1's tag lookups; rows beyond N and pairs
+//    beyond K/64 read clamped in-range addresses.
 #include "q4_device.h"
 #include "q4_launch.h"
 
@@ -49,11 +71,31 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) float g_f32;
 
-constexpr int kSmWaves = 16;
-constexpr int kSmThreads = kSmWaves * 64;
-constexpr int kTileRows = 16 * kSmWaves;  // 256
-constexpr int kPairsPerLane = 4;          // pairs g, g+4, g+8, g+12 of a segment
-constexpr int kXBytes = 160 * 1024;       // activations of one K-range, all M rows (the whole LDS)
+// Two ways to move the weights (see above): ENG = 0 register loads, 1 LDS
+// ring.  Waves per workgroup, rows per tile, pairs per unit and row, the LDS
+// the weight rings take and the LDS left for the staged activations.
+template <int ENG>
+struct Geo;
+template <>
+struct Geo<0> {
+    static constexpr int kWaves = 16, kTileRows = 256, kSegPairs = 16, kXBytes = 160 * 1024;
+};
+template <>
+struct Geo<1> {
+    static constexpr int kWaves = 8, kTileRows = 128, kSegPairs = 8;
+    static constexpr int kPieces = 21;               // 16-byte pieces per row in a slot: 4 lane groups x 5, one pad
+    static constexpr int kPitch = 16 * kPieces;      // 336
+    static constexpr int kSlot = 16 * kPitch;        // 5376 bytes: one unit of one wave
+    static constexpr int kNB = 2;                    // unit slots per wave
+    static constexpr int kRing = kWaves * kNB * kSlot;      // 86016 bytes at the start of LDS
+    static constexpr int kLoads = (16 * kPieces + 63) / 64;  // 6 load instructions per unit
+    static constexpr int kXBytes = 160 * 1024 - kRing;       // 77824
+};
+// M up to this uses the LDS ring; larger M the register loads, whose
+// activations may take the whole LDS (measured on the 448-GEMM sweep: the
+// ring is 5-7 % faster at M = 2..5, 2 % slower at M = 8).
+constexpr int kLdsMaxM = 7;
+__host__ __device__ constexpr int engine_of(int64_t m) { return m <= kLdsMaxM ? 1 : 0; }
 
 __device__ __forceinline__ int64_t uniform64(int64_t v) {
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
@@ -61,14 +103,47 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Segments (16 pairs) of K-range c of a descriptor.
+// Segments (SEG pairs) of K-range c of a descriptor.
+template <int SEG>
 __device__ __forceinline__ int segs_of(const SmDesc& D, int c) {
-    return (min(D.P, D.np - c * D.P) + 15) >> 4;
+    return (min(D.P, D.np - c * D.P) + SEG - 1) / SEG;
 }
 
 // First unit (cost) of item (c, t): ranges before c are full.
+template <int SEG>
 __device__ __forceinline__ int64_t item_start(const SmDesc& D, int c, int t) {
-    return D.cost_begin + (int64_t)c * D.tiles * (D.P >> 4) + (int64_t)t * segs_of(D, c);
+    return D.cost_begin + (int64_t)c * D.tiles * (D.P / SEG) + (int64_t)t * segs_of<SEG>(D, c);
+}
+
+// Direct-to-LDS loads through asm (the compiler does not track them; the
+// kernel waits with explicit vmcnt counts): 16 bytes per lane at byte offset
+// voff of the buffer into LDS at M0 + 16 * lane.  They write no register; the
+// s_nop covers the M0 write just before.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+struct Rsrc {
+    u4 w;
+};
+// Raw buffer of `bytes` bytes at base (gfx9: stride 0, 32-bit data format);
+// loads at or past `bytes` return zeros.  Every field is wave-uniform.
+__device__ __forceinline__ Rsrc make_rsrc(const uint8_t* base, uint64_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    Rsrc r;
+    r.w.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    r.w.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xFFFFu);
+    r.w.z = __builtin_amdgcn_readfirstlane((uint32_t)min(bytes, (uint64_t)0xFFFFFFFFu));
+    r.w.w = 0x00020000u;
+    return r;
+}
+__device__ __forceinline__ void dma16(const Rsrc& r, uint32_t voff, uint32_t m0) {
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r.w), "{m0}"(m0) : "memory");
+}
+// s_waitcnt vmcnt(N) (a compiler barrier too: no LDS read of a slot moves above it).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 struct SmCursor {
@@ -90,13 +165,13 @@ __device__ __forceinline__ int x_slot(int r, int pl, int c) {
     return SWZ ? 8 * (pl ^ ((r >> 3) & 1)) + (c ^ (r & 7)) : 8 * pl + c;
 }
 
-// Activations of pairs [c*P, c*P + 16*segs) of all M rows into their slots;
-// pairs past K/64 are zero.
-template <bool SWZ>
+// Activations of pairs [c*P, c*P + SEG*segs) of all M rows into their slots
+// (THREADS threads); pairs past K/64 are zero.
+template <bool SWZ, int SEG, int THREADS>
 __device__ void stage_range(const SmDesc& D, int c, int m, u4* __restrict__ xs) {
     const int p0 = c * D.P;
-    const int npairs = 16 * segs_of(D, c);
-    for (int it = threadIdx.x; it < 2 * npairs * m; it += kSmThreads) {
+    const int npairs = SEG * segs_of<SEG>(D, c);
+    for (int it = threadIdx.x; it < 2 * npairs * m; it += THREADS) {
         const int mm = it % m;
         const int b = it / m;  // block within the range
         const int p = p0 + (b >> 1);
@@ -130,13 +205,232 @@ __device__ void stage_range(const SmDesc& D, int c, int m, u4* __restrict__ xs) 
     }
 }
 
+// The LDS-ring engine (M <= kLdsMaxM).
+template <bool SWZ>
+__global__ void __launch_bounds__(Geo<1>::kWaves * 64) k_smallm_lds(const SmDesc* __restrict__ descs, int count,
+                                                                     SmDesc one, int m, int64_t total,
+                                                                     float* __restrict__ ws) {
+    using E = Geo<1>;
+    constexpr int kSegPairs = E::kSegPairs, kTileRows = E::kTileRows, kPieces = E::kPieces, kPitch = E::kPitch;
+    constexpr int kSlot = E::kSlot, kNB = E::kNB, kRing = E::kRing, kLoads = E::kLoads;
+    extern __shared__ u4 lds_u4[];
+    uint8_t* lds = reinterpret_cast<uint8_t*>(lds_u4);
+    u4* xs = reinterpret_cast<u4*>(lds + kRing);  // staged activations after the weight rings
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4;
+    const int l16 = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int n_desc = descs ? count : 1;
+    auto get = [&](int d) -> SmDesc { return descs ? descs[d] : one; };
+    const uint32_t ring0 = lds_addr(lds) + (uint32_t)(wave * kNB * kSlot);
+
+    const int64_t G = gridDim.x;
+    const int64_t c_lo = uniform64((total / G) * blockIdx.x + ((total % G) * blockIdx.x) / G);
+    const int64_t c_hi = uniform64((total / G) * (blockIdx.x + 1) + ((total % G) * ((int64_t)blockIdx.x + 1)) / G);
+    if (c_lo >= c_hi) return;  // whole workgroup leaves together
+
+    // First item starting at or after c_lo.
+    int lo = 0, hi = n_desc - 1;  // last descriptor starting at or before c_lo
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (get(mid).cost_begin <= c_lo) lo = mid; else hi = mid - 1;
+    }
+    SmCursor cl;
+    cl.d = lo;
+    cl.jb = 0;
+    SmDesc Dl = get(lo);
+    {
+        const int64_t full = (int64_t)Dl.tiles * (Dl.P / kSegPairs);  // units of a full K-range
+        const int64_t o = c_lo - Dl.cost_begin;
+        int c = (int)(o / full < Dl.nranges - 1 ? o / full : Dl.nranges - 1);
+        const int64_t r = o - c * full;
+        const int sg = segs_of<kSegPairs>(Dl, c);
+        int64_t t = (r + sg - 1) / sg;
+        if (t >= Dl.tiles) {
+            t = 0;
+            if (++c == Dl.nranges) {
+                c = 0;
+                if (++cl.d < n_desc) Dl = get(cl.d);
+            }
+        }
+        cl.c = c;
+        cl.t = (int)t;
+    }
+    bool have_l = cl.d < n_desc && item_start<kSegPairs>(Dl, cl.c, cl.t) < c_hi;
+    if (!have_l) return;
+
+    auto advance_l = [&]() {
+        if (++cl.jb < segs_of<kSegPairs>(Dl, cl.c)) return;
+        cl.jb = 0;
+        if (++cl.t == Dl.tiles) {
+            cl.t = 0;
+            if (++cl.c == Dl.nranges) {
+                cl.c = 0;
+                if (++cl.d >= n_desc) {
+                    have_l = false;
+                    return;
+                }
+                Dl = get(cl.d);
+            }
+        }
+        have_l = item_start<kSegPairs>(Dl, cl.c, cl.t) < c_hi;
+    };
+
+    // This lane's piece of load q of a unit: slot piece L = 64 q + lane is
+    // piece L % 21 of row L / 21; piece 5 gg + i (gg < 4) holds bytes
+    // 72 gg + 16 i of the row's segment for i < 4 and 72 gg + 56 for i = 4;
+    // piece 20 is padding (loaded with a copy of piece 19).  Lanes past the
+    // slot's 336 pieces do not load.
+    int prow[kLoads], poff[kLoads];
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) {
+        const int L = min(64 * q + lane, 16 * kPieces - 1);
+        const int pc = min(L % kPieces, 4 * 5 - 1);
+        const int gg = pc / 5, i = pc % 5;
+        prow[q] = L / kPieces;
+        poff[q] = 72 * gg + (i < 4 ? 16 * i : 56);
+    }
+    const bool last_live = 64 * (kLoads - 1) + lane < 16 * kPieces;
+
+    // Loads of the unit at the cursor into slot `slot`: rows t*128 + 16*wave + n,
+    // pairs c*P + 8*jb ..; the descriptor ends at the matrix end.
+    auto issue = [&](int slot) {
+        const int64_t rb = (int64_t)Dl.np * kPairBytes;
+        const int64_t row0 = (int64_t)cl.t * kTileRows + 16 * wave;
+        const int64_t off0 = row0 * rb + (int64_t)(cl.c * Dl.P + kSegPairs * cl.jb) * kPairBytes;
+        const int64_t bytes = Dl.n * rb;
+        const Rsrc rs = make_rsrc(Dl.w + min(off0, bytes), (uint64_t)max(bytes - off0, (int64_t)0));
+        const uint32_t dst = ring0 + (uint32_t)(slot * kSlot);
+#pragma unroll
+        for (int q = 0; q < kLoads - 1; ++q) dma16(rs, (uint32_t)(prow[q] * rb + poff[q]), dst + 1024u * q);
+        if (last_live)
+            dma16(rs, (uint32_t)(prow[kLoads - 1] * rb + poff[kLoads - 1]), dst + 1024u * (kLoads - 1));
+    };
+
+    struct Rec {
+        int d, c, t, jb;
+    };
+    f4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    int dc = -1, staged_d = -1, staged_c = -1;
+    SmDesc Dc;
+
+    // Lane (g, n)'s pairs 2g, 2g+1 of the unit in `slot`, as 20 dwords (pair 0
+    // is dwords 0..8, pair 1 dwords 9..15, 18, 19), once the unit's loads are
+    // done (`after`: one later unit's loads were issued behind it).  The reads
+    // have returned when this returns, so the slot may be refilled.
+    auto fetch = [&](int slot, bool after, uint32_t (&D)[20]) {
+        if (after)
+            wait_vmcnt<kLoads>();
+        else
+            wait_vmcnt<0>();
+        const u4* src = reinterpret_cast<const u4*>(lds + wave * kNB * kSlot + slot * kSlot + l16 * kPitch + 80 * g);
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            const u4 v = src[i];
+            D[4 * i] = v.x; D[4 * i + 1] = v.y; D[4 * i + 2] = v.z; D[4 * i + 3] = v.w;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    };
+
+    auto process = [&](const Rec& r, const uint32_t (&D)[20]) {
+        if (r.d != dc) {
+            Dc = get(r.d);
+            dc = r.d;
+        }
+        if (r.d != staged_d || r.c != staged_c) {
+            __syncthreads();
+            stage_range<SWZ, kSegPairs, E::kWaves * 64>(Dc, r.c, m, xs);
+            __syncthreads();
+            staged_d = r.d;
+            staged_c = r.c;
+        }
+        // A operand rows m >= M only produce product rows that are never
+        // stored, so those lanes read activation row M - 1 (an LDS broadcast).
+        // Pair 8 jb + 2 g + pp: 8 jb + 2 g is even, so its slot is
+        // 8 (8 jb + 2 g) + slot(row, pp, c) in both layouts.
+        const int xr = min(l16, m - 1);
+        const u4* xu = xs + xr * x_stride<SWZ>(Dc) + 64 * r.jb + 16 * g;
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+            uint32_t P[9];
+#pragma unroll
+            for (int i = 0; i < 9; ++i) P[i] = pp == 0 ? D[i] : D[i < 7 ? 9 + i : 11 + i];
+            const _Float16 d0 = as_h2(P[0]).x, d1 = as_h2(P[4]).y;
+            const h2 s0 = {d0, d0}, s1 = {d1, d1};
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const uint32_t code = (c == 0) ? realign_block0(P[0], P[4]) : P[c < 4 ? c : c + 1];
+                const Codes4 q = expand(code);
+                const h2 sc = c < 4 ? s0 : s1;
+                u4 bw;
+                bw.x = as_u32(q.q0 * sc);
+                bw.y = as_u32(q.q1 * sc);
+                bw.z = as_u32(q.q2 * sc);
+                bw.w = as_u32(q.q3 * sc);
+                const u4 ax = xu[x_slot<SWZ>(xr, pp, c)];
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, ax), __builtin_bit_cast(h8, bw),
+                                                             acc, 0, 0, 0);
+            }
+        }
+        if (r.jb + 1 == segs_of<kSegPairs>(Dc, r.c)) {  // last segment of the item: store the tile
+            // D layout of the 16x16 product: lane (g, l16), element e -> activation row 4g + e, weight row l16
+            const int64_t row = (int64_t)r.t * kTileRows + 16 * wave + l16;
+            if (row < Dc.n) {
+                float* out = Dc.nranges > 1 ? ws + Dc.ws_off + (int64_t)r.c * m * Dc.n : Dc.y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int mm = 4 * g + e;
+                    if (mm < m) ((g_f32*)out)[(int64_t)mm * Dc.n + row] = acc[e];
+                }
+            }
+            acc = f4v{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+    };
+
+    // Ring of two slots, two units in flight while a unit is computed: a
+    // unit's pairs are read into registers, its slot is refilled with the unit
+    // two ahead, and then the unit is computed from the registers.
+    Rec cur = Rec{cl.d, cl.c, cl.t, cl.jb};
+    issue(0);
+    advance_l();
+    bool have1 = have_l;
+    Rec nxt = cur;
+    if (have1) {
+        nxt = Rec{cl.d, cl.c, cl.t, cl.jb};
+        issue(1);
+        advance_l();
+    }
+    int slot = 0;
+    for (;;) {
+        uint32_t D[20];
+        fetch(slot, have1, D);
+        const bool have2 = have_l;
+        Rec nn = nxt;
+        if (have2) {
+            nn = Rec{cl.d, cl.c, cl.t, cl.jb};
+            issue(slot);
+            advance_l();
+        }
+        process(cur, D);
+        if (!have1) break;
+        cur = nxt;
+        nxt = nn;
+        have1 = have2;
+        slot ^= 1;
+    }
+}
+
 struct SmBuf {
-    uint32_t d[kPairsPerLane][9];
+    uint32_t d[4][9];  // pairs g, g+4, g+8, g+12 of a 16-pair segment
 };
 
+// The register-load engine (M > kLdsMaxM).
 template <bool SWZ>
-__global__ void __launch_bounds__(kSmThreads) k_smallm(const SmDesc* __restrict__ descs, int count, SmDesc one,
-                                                       int m, int64_t total, float* __restrict__ ws) {
+__global__ void __launch_bounds__(Geo<0>::kWaves * 64) k_smallm_reg(const SmDesc* __restrict__ descs, int count,
+                                                                     SmDesc one, int m, int64_t total,
+                                                                     float* __restrict__ ws) {
+    using E = Geo<0>;
+    constexpr int kSegPairs = E::kSegPairs, kTileRows = E::kTileRows;
     extern __shared__ u4 xs[];
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4;
@@ -161,11 +455,11 @@ __global__ void __launch_bounds__(kSmThreads) k_smallm(const SmDesc* __restrict_
     cl.jb = 0;
     SmDesc Dl = get(lo);
     {
-        const int64_t full = (int64_t)Dl.tiles * (Dl.P >> 4);  // units of a full K-range
+        const int64_t full = (int64_t)Dl.tiles * (Dl.P / kSegPairs);  // units of a full K-range
         const int64_t o = c_lo - Dl.cost_begin;
         int c = (int)(o / full < Dl.nranges - 1 ? o / full : Dl.nranges - 1);
         const int64_t r = o - c * full;
-        const int sg = segs_of(Dl, c);
+        const int sg = segs_of<kSegPairs>(Dl, c);
         int64_t t = (r + sg - 1) / sg;
         if (t >= Dl.tiles) {
             t = 0;
@@ -177,11 +471,11 @@ __global__ void __launch_bounds__(kSmThreads) k_smallm(const SmDesc* __restrict_
         cl.c = c;
         cl.t = (int)t;
     }
-    bool have_l = cl.d < n_desc && item_start(Dl, cl.c, cl.t) < c_hi;
+    bool have_l = cl.d < n_desc && item_start<kSegPairs>(Dl, cl.c, cl.t) < c_hi;
     if (!have_l) return;
 
     auto advance_l = [&]() {
-        if (++cl.jb < segs_of(Dl, cl.c)) return;
+        if (++cl.jb < segs_of<kSegPairs>(Dl, cl.c)) return;
         cl.jb = 0;
         if (++cl.t == Dl.tiles) {
             cl.t = 0;
@@ -194,7 +488,7 @@ __global__ void __launch_bounds__(kSmThreads) k_smallm(const SmDesc* __restrict_
                 Dl = get(cl.d);
             }
         }
-        have_l = item_start(Dl, cl.c, cl.t) < c_hi;
+        have_l = item_start<kSegPairs>(Dl, cl.c, cl.t) < c_hi;
     };
 
     auto issue = [&](SmBuf& b) {
@@ -202,7 +496,7 @@ __global__ void __launch_bounds__(kSmThreads) k_smallm(const SmDesc* __restrict_
         const uint8_t* wrow = Dl.w + row * (int64_t)Dl.np * kPairBytes;
         const int p0 = cl.c * Dl.P + 16 * cl.jb + g;
 #pragma unroll
-        for (int jj = 0; jj < kPairsPerLane; ++jj) {
+        for (int jj = 0; jj < 4; ++jj) {
             const int p = min(p0 + 4 * jj, Dl.np - 1);
             load_pair(wrow + (int64_t)p * kPairBytes, b.d[jj]);
         }
@@ -222,7 +516,7 @@ __global__ void __launch_bounds__(kSmThreads) k_smallm(const SmDesc* __restrict_
         }
         if (r.d != staged_d || r.c != staged_c) {
             __syncthreads();
-            stage_range<SWZ>(Dc, r.c, m, xs);
+            stage_range<SWZ, kSegPairs, E::kWaves * 64>(Dc, r.c, m, xs);
             __syncthreads();
             staged_d = r.d;
             staged_c = r.c;
@@ -234,7 +528,7 @@ __global__ void __launch_bounds__(kSmThreads) k_smallm(const SmDesc* __restrict_
         const int xr = min(l16, m - 1);
         const u4* xu = xs + xr * x_stride<SWZ>(Dc) + 128 * r.jb;
 #pragma unroll
-        for (int jj = 0; jj < kPairsPerLane; ++jj) {
+        for (int jj = 0; jj < 4; ++jj) {
             const _Float16 d0 = as_h2(b.d[jj][0]).x, d1 = as_h2(b.d[jj][4]).y;
             const h2 s0 = {d0, d0}, s1 = {d1, d1};
 #pragma unroll
@@ -252,7 +546,7 @@ __global__ void __launch_bounds__(kSmThreads) k_smallm(const SmDesc* __restrict_
                                                              acc, 0, 0, 0);
             }
         }
-        if (r.jb + 1 == segs_of(Dc, r.c)) {  // last segment of the item: store the tile
+        if (r.jb + 1 == segs_of<kSegPairs>(Dc, r.c)) {  // last segment of the item: store the tile
             // D layout of the 16x16 product: lane (g, l16), element e -> activation row 4g + e, weight row l16
             const int64_t row = (int64_t)r.t * kTileRows + 16 * wave + l16;
             if (row < Dc.n) {
@@ -311,13 +605,19 @@ __global__ void __launch_bounds__(256) k_sum_ranges(const SmDesc* __restrict__ d
 
 }  // namespace
 
+// LDS left for the staged activations, rows per tile and pairs per unit of
+// the engine that runs m activation rows.
+static int sm_xbytes(int64_t m) { return engine_of(m) ? Geo<1>::kXBytes : Geo<0>::kXBytes; }
+static int sm_tile_rows(int64_t m) { return engine_of(m) ? Geo<1>::kTileRows : Geo<0>::kTileRows; }
+static int sm_seg(int64_t m) { return engine_of(m) ? Geo<1>::kSegPairs : Geo<0>::kSegPairs; }
+
 // Pairs per K-range for m activation rows: the longest run of whole 16-pair
-// segments whose activations fit kXBytes in the padded layout, or in the
-// swizzled one (no padding, a little longer) when that takes fewer ranges.
+// spans whose activations fit the engine's LDS in the padded layout, or in
+// the swizzled one (no padding, a little longer) when that takes fewer ranges.
 static int smallm_range_pairs(int64_t k, int64_t m) {
     const int np = (int)(k / 64);
     const int np16 = (np + 15) / 16 * 16;
-    const int row_chunks = (int)(kXBytes / (16 * m));  // 16-byte chunks per activation row
+    const int row_chunks = (int)(sm_xbytes(m) / (16 * m));  // 16-byte chunks per activation row
     const int fit_pad = std::max(16, (row_chunks - 1) / kChunksPerPair / 16 * 16);
     const int fit_swz = std::max(16, row_chunks / kChunksPerPair / 16 * 16);
     if ((np + fit_swz - 1) / fit_swz < (np + fit_pad - 1) / fit_pad) return std::min(fit_swz, np16);
@@ -329,16 +629,18 @@ int64_t smallm_fill(SmDesc* d, int64_t m, int64_t ws_off, int64_t cost_begin) {
     d->np = (int32_t)(d->k / 64);
     d->P = smallm_range_pairs(d->k, m);
     d->nranges = (d->np + d->P - 1) / d->P;
-    d->tiles = (int32_t)((d->n + kTileRows - 1) / kTileRows);
+    d->tiles = (int32_t)((d->n + sm_tile_rows(m) - 1) / sm_tile_rows(m));
     d->cost_begin = cost_begin;
+    d->m = (int32_t)m;
     const int64_t floats = d->nranges > 1 ? (int64_t)d->nranges * m * d->n : 0;
     d->ws_off = floats ? ws_off : 0;
     return floats;
 }
 
 int64_t smallm_cost(const SmDesc& d) {
+    const int seg = sm_seg(d.m);
     int64_t c = 0;
-    for (int r = 0; r < d.nranges; ++r) c += (int64_t)d.tiles * ((std::min(d.P, d.np - r * d.P) + 15) / 16);
+    for (int r = 0; r < d.nranges; ++r) c += (int64_t)d.tiles * ((std::min(d.P, d.np - r * d.P) + seg - 1) / seg);
     return c;
 }
 
@@ -354,29 +656,39 @@ static int smallm_grid(int64_t total) {
 }
 
 // Staged activations: m rows of max_range_pairs * 8 chunks, plus one chunk of
-// padding per row when that still fits the LDS (then the padded layout).
+// padding per row when that still fits the LDS (then the padded layout); the
+// LDS-ring engine's rings come first.
 static bool smallm_swizzle(int64_t max_range_pairs, int64_t m) {
-    return (max_range_pairs * kChunksPerPair + 1) * m * (int64_t)sizeof(u4) > kXBytes;
+    return (max_range_pairs * kChunksPerPair + 1) * m * (int64_t)sizeof(u4) > sm_xbytes(m);
 }
 static size_t smallm_lds(int64_t max_range_pairs, int64_t m) {
-    return (size_t)(max_range_pairs * kChunksPerPair + (smallm_swizzle(max_range_pairs, m) ? 0 : 1)) * m * sizeof(u4);
+    return (size_t)(engine_of(m) ? Geo<1>::kRing : 0) +
+           (size_t)(max_range_pairs * kChunksPerPair + (smallm_swizzle(max_range_pairs, m) ? 0 : 1)) * m * sizeof(u4);
+}
+
+template <class K>
+static hipError_t launch_k(K kern, int threads, const SmDesc* descs, int count, const SmDesc& one, int64_t m,
+                           int64_t total, size_t lds, float* ws, hipStream_t s) {
+    if (lds > 65536) {
+        const hipError_t e = allow_dynamic_lds((const void*)kern, lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(smallm_grid(total)), dim3(threads), lds, s, descs, count, one, (int)m, total, ws);
+    return hipGetLastError();
 }
 
 static hipError_t launch_sm(const SmDesc* descs, int count, const SmDesc& one, int64_t m, int64_t total,
                             int max_p, float* ws, hipStream_t s) {
     const size_t lds = smallm_lds(max_p, m);
-    const void* kern = smallm_swizzle(max_p, m) ? (const void*)k_smallm<true> : (const void*)k_smallm<false>;
-    if (lds > 65536) {
-        const hipError_t e = allow_dynamic_lds((const void*)kern, lds);
-        if (e != hipSuccess) return e;
+    const bool swz = smallm_swizzle(max_p, m);
+    if (engine_of(m)) {
+        constexpr int t = Geo<1>::kWaves * 64;
+        return swz ? launch_k(k_smallm_lds<true>, t, descs, count, one, m, total, lds, ws, s)
+                   : launch_k(k_smallm_lds<false>, t, descs, count, one, m, total, lds, ws, s);
     }
-    if (smallm_swizzle(max_p, m))
-        hipLaunchKernelGGL(k_smallm<true>, dim3(smallm_grid(total)), dim3(kSmThreads), lds, s, descs, count, one,
-                           (int)m, total, ws);
-    else
-        hipLaunchKernelGGL(k_smallm<false>, dim3(smallm_grid(total)), dim3(kSmThreads), lds, s, descs, count, one,
-                           (int)m, total, ws);
-    return hipGetLastError();
+    constexpr int t = Geo<0>::kWaves * 64;
+    return swz ? launch_k(k_smallm_reg<true>, t, descs, count, one, m, total, lds, ws, s)
+               : launch_k(k_smallm_reg<false>, t, descs, count, one, m, total, lds, ws, s);
 }
 
 hipError_t launch_gemm_smallm(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n, int64_t k,

@@ -60,14 +60,16 @@ def test_workspace_bytes(lib):
 
 
 def test_smallm_k_range_workspace_rule(lib):
-    # The activations of one K-range (all M rows) live in 160 KiB of LDS, in
-    # whole 16-pair segments: 128 bytes per pair and row, plus 16 bytes per row
-    # of padding unless dropping it (the swizzled layout) takes fewer ranges.
-    # A GEMM needs partial sums (nranges x M x N floats) only when its K does
-    # not fit one range.
+    # The activations of one K-range (all M rows) live in the LDS the weights
+    # leave free (M <= 7: 160 KiB - 8 waves x 2 slots x 5,376 bytes of weight
+    # rings; M > 7: all 160 KiB), in whole 16-pair spans: 128 bytes per pair and row, plus 16
+    # bytes per row of padding unless dropping it (the swizzled layout) takes
+    # fewer ranges.  A GEMM needs partial sums (nranges x M x N floats) only
+    # when its K does not fit one range.
     def expect(m, n, k):
         np_ = k // 64
-        row_chunks = 160 * 1024 // (16 * m)
+        # M <= 7: the LDS-ring engine (8 waves x 2 slots x 5,376 bytes of weights)
+        row_chunks = (160 * 1024 - (8 * 2 * 5376 if m <= 7 else 0)) // (16 * m)
         fit_pad = max(16, (row_chunks - 1) // 8 // 16 * 16)
         fit_swz = max(16, row_chunks // 8 // 16 * 16)
         fit = fit_swz if -(-np_ // fit_swz) < -(-np_ // fit_pad) else fit_pad
@@ -78,9 +80,9 @@ def test_smallm_k_range_workspace_rule(lib):
     op = q4.Q4_OP_GEMM_SMALLM
     assert lib.q4_workspace_bytes(op, 16, 5120, 5120) == 0  # 16 x 80 pairs x 128 bytes: exactly 160 KiB
     assert lib.q4_workspace_bytes(op, 16, 5120, 17408) == 4 * 16 * 5120 * 4  # 80 + 80 + 80 + 32 pairs
-    assert lib.q4_workspace_bytes(op, 16, 5120, 4096) == 0
+    assert lib.q4_workspace_bytes(op, 4, 5120, 17408) == 2 * 4 * 5120 * 4  # 144 + 128 pairs
     assert lib.q4_workspace_bytes(op, 8, 5120, 5120) == 0
-    assert lib.q4_workspace_bytes(op, 2, 5120, 5120) == 0
+    assert lib.q4_workspace_bytes(op, 2, 5120, 17408) == 0
     for m in (2, 3, 5, 8, 9, 12, 16):
         for k in (64, 1024, 4096, 5120, 13824, 17408, 32768):
             assert lib.q4_workspace_bytes(op, m, 4608, k) == expect(m, 4608, k), (m, k)

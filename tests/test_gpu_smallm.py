@@ -1,5 +1,7 @@
 """q4_0_gemm_smallm (M <= 16): against the oracle, and row m against the M=1
-GEMV of X[m] (the batched verify pass agrees with plain decode)."""
+GEMV of X[m] (the batched verify pass agrees with plain decode).  M <= 7 runs
+the LDS-ring engine, larger M the register-load one; both are covered, each
+with a K split into ranges (M = 4, 7, 16 at K = 17,408)."""
 import numpy as np
 import pytest
 import torch
@@ -14,7 +16,7 @@ SEED = synth.DEFAULT_SEED
 SHAPES = [(1, 64), (37, 128), (100, 5120), (64, 1088), (31, 17408), (7, 96), (513, 2048)]
 
 
-@pytest.mark.parametrize("m", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 7, 8, 16])
 @pytest.mark.parametrize("n,k", SHAPES, ids=["%dx%d" % s for s in SHAPES])
 def test_parity(m, n, k):
     q4 = lib()
@@ -31,15 +33,17 @@ def test_parity(m, n, k):
         assert_parity(yi, y_ref[i], a_ref[i])
 
 
-def test_layer_shapes_sampled():
-    """M = 16 against one full layer of the sweep shapes (q, gate, down)."""
+@pytest.mark.parametrize("m", [4, 16])
+def test_layer_shapes_sampled(m):
+    """M = 4 (LDS ring) and 16 (register loads) against one full layer of the
+    sweep shapes (q, gate, down)."""
     q4 = lib()
     rng = np.random.default_rng(9)
     for proj in (0, 4, 6):
         _, n, k = synth.PROJ[proj]
         sw = synth.stream_id(3, 0, proj, synth.T_W)
         w = synth.q4_0(SEED, sw, n, k)
-        x = synth.f16_normal(SEED, synth.stream_id(3, 0, proj, synth.T_X), 16 * k).reshape(16, k)
+        x = synth.f16_normal(SEED, synth.stream_id(3, 0, proj, synth.T_X), m * k).reshape(m, k)
         say("smallm layer shape", n, k)
         y = q4.q4_0_gemm_smallm(dev_u8(w), dev_f16(x))
         torch.cuda.synchronize()
@@ -48,7 +52,7 @@ def test_layer_shapes_sampled():
         assert_parity(y.cpu().numpy()[:, rows], y_ref, a_ref)
 
 
-@pytest.mark.parametrize("m", [2, 5, 16])
+@pytest.mark.parametrize("m", [2, 5, 7, 16])
 def test_batch_matches_single_calls_and_oracle(m):
     """A mixed small-M list in one launch: every GEMM bit-identical to its own
     q4_0_gemm_smallm call and within the bound of the oracle, including GEMMs
