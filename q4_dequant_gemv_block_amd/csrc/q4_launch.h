@@ -99,6 +99,13 @@ int64_t smallm_cost(const SmDesc& d);
 size_t smallm_workspace_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm_smallm(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n,
                               int64_t k, float* workspace, hipStream_t s);
+// A single small-M GEMM (m <= 7) whose K fits one K-range, which also writes row mm's
+// greedy-pick key of each workgroup b to keys[mm * G + b] (argmax_key: larger
+// logit, then lower index; 0 when the workgroup stored none of that row), G =
+// smallm_key_slices(m, n, k); that is 0 when m > 7 or K does not fit one range.
+int smallm_key_slices(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemm_smallm_keys(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n, int64_t k,
+                                   uint64_t* keys, hipStream_t s);
 // descs: `count` filled descriptors in device memory; total: sum of their costs.
 hipError_t launch_gemm_smallm_batch(const SmDesc* descs, int count, int64_t m, int64_t total, int max_p,
                                     int64_t max_mn, bool any_split, float* workspace, hipStream_t s);

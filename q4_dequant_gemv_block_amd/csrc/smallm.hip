@@ -146,6 +146,35 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Greedy-pick epilogue (keys != null): each lane keeps, for its four
+// activation rows, the largest argmax key over the outputs it stored; at the
+// end the workgroup reduces them and writes row mm's key to
+// keys[mm * gridDim.x + blockIdx.x] (0 when it stored none of that row).
+// `scratch` is LDS no wave still reads (2 KiB).
+template <int WAVES>
+__device__ __forceinline__ void write_keys(uint64_t (&best)[4], int m, uint64_t* __restrict__ keys, void* scratch) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) {  // over the 16 lanes of the group
+            const uint64_t v = __shfl_xor(best[e], o, 64);
+            best[e] = v > best[e] ? v : best[e];
+        }
+    uint64_t* sh = static_cast<uint64_t*>(scratch);
+    __syncthreads();  // every wave is done with the LDS
+    if ((lane & 15) == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sh[wave * 16 + 4 * g + e] = best[e];
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < m) {
+        uint64_t r = 0;
+        for (int w = 0; w < WAVES; ++w) r = sh[w * 16 + threadIdx.x] > r ? sh[w * 16 + threadIdx.x] : r;
+        keys[(int64_t)threadIdx.x * gridDim.x + blockIdx.x] = r;
+    }
+}
+
 struct SmCursor {
     int d, c, t, jb;
 };
@@ -209,7 +238,7 @@ __device__ void stage_range(const SmDesc& D, int c, int m, u4* __restrict__ xs) 
 template <bool SWZ>
 __global__ void __launch_bounds__(Geo<1>::kWaves * 64) k_smallm_lds(const SmDesc* __restrict__ descs, int count,
                                                                      SmDesc one, int m, int64_t total,
-                                                                     float* __restrict__ ws) {
+                                                                     float* __restrict__ ws, uint64_t* __restrict__ keys) {
     using E = Geo<1>;
     constexpr int kSegPairs = E::kSegPairs, kTileRows = E::kTileRows, kPieces = E::kPieces, kPitch = E::kPitch;
     constexpr int kSlot = E::kSlot, kNB = E::kNB, kRing = E::kRing, kLoads = E::kLoads;
@@ -227,7 +256,10 @@ __global__ void __launch_bounds__(Geo<1>::kWaves * 64) k_smallm_lds(const SmDesc
     const int64_t G = gridDim.x;
     const int64_t c_lo = uniform64((total / G) * blockIdx.x + ((total % G) * blockIdx.x) / G);
     const int64_t c_hi = uniform64((total / G) * (blockIdx.x + 1) + ((total % G) * ((int64_t)blockIdx.x + 1)) / G);
-    if (c_lo >= c_hi) return;  // whole workgroup leaves together
+    if (c_lo >= c_hi) {  // whole workgroup leaves together
+        if (keys && (int)threadIdx.x < m) keys[(int64_t)threadIdx.x * gridDim.x + blockIdx.x] = 0;
+        return;
+    }
 
     // First item starting at or after c_lo.
     int lo = 0, hi = n_desc - 1;  // last descriptor starting at or before c_lo
@@ -257,7 +289,10 @@ __global__ void __launch_bounds__(Geo<1>::kWaves * 64) k_smallm_lds(const SmDesc
         cl.t = (int)t;
     }
     bool have_l = cl.d < n_desc && item_start<kSegPairs>(Dl, cl.c, cl.t) < c_hi;
-    if (!have_l) return;
+    if (!have_l) {
+        if (keys && (int)threadIdx.x < m) keys[(int64_t)threadIdx.x * gridDim.x + blockIdx.x] = 0;
+        return;
+    }
 
     auto advance_l = [&]() {
         if (++cl.jb < segs_of<kSegPairs>(Dl, cl.c)) return;
@@ -311,6 +346,7 @@ __global__ void __launch_bounds__(Geo<1>::kWaves * 64) k_smallm_lds(const SmDesc
         int d, c, t, jb;
     };
     f4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    uint64_t best[4] = {0, 0, 0, 0};
     int dc = -1, staged_d = -1, staged_c = -1;
     SmDesc Dc;
 
@@ -380,7 +416,13 @@ __global__ void __launch_bounds__(Geo<1>::kWaves * 64) k_smallm_lds(const SmDesc
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int mm = 4 * g + e;
-                    if (mm < m) ((g_f32*)out)[(int64_t)mm * Dc.n + row] = acc[e];
+                    if (mm < m) {
+                        ((g_f32*)out)[(int64_t)mm * Dc.n + row] = acc[e];
+                        if (keys) {
+                            const uint64_t kk = argmax_key(acc[e], row);
+                            best[e] = kk > best[e] ? kk : best[e];
+                        }
+                    }
                 }
             }
             acc = f4v{0.0f, 0.0f, 0.0f, 0.0f};
@@ -418,6 +460,7 @@ __global__ void __launch_bounds__(Geo<1>::kWaves * 64) k_smallm_lds(const SmDesc
         have1 = have2;
         slot ^= 1;
     }
+    if (keys) write_keys<Geo<1>::kWaves>(best, m, keys, lds);
 }
 
 struct SmBuf {
@@ -428,7 +471,7 @@ struct SmBuf {
 template <bool SWZ>
 __global__ void __launch_bounds__(Geo<0>::kWaves * 64) k_smallm_reg(const SmDesc* __restrict__ descs, int count,
                                                                      SmDesc one, int m, int64_t total,
-                                                                     float* __restrict__ ws) {
+                                                                     float* __restrict__ ws, uint64_t* /*keys: M <= 7 only*/) {
     using E = Geo<0>;
     constexpr int kSegPairs = E::kSegPairs, kTileRows = E::kTileRows;
     extern __shared__ u4 xs[];
@@ -668,27 +711,49 @@ static size_t smallm_lds(int64_t max_range_pairs, int64_t m) {
 
 template <class K>
 static hipError_t launch_k(K kern, int threads, const SmDesc* descs, int count, const SmDesc& one, int64_t m,
-                           int64_t total, size_t lds, float* ws, hipStream_t s) {
+                           int64_t total, size_t lds, float* ws, uint64_t* keys, hipStream_t s) {
     if (lds > 65536) {
         const hipError_t e = allow_dynamic_lds((const void*)kern, lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3(smallm_grid(total)), dim3(threads), lds, s, descs, count, one, (int)m, total, ws);
+    hipLaunchKernelGGL(kern, dim3(smallm_grid(total)), dim3(threads), lds, s, descs, count, one, (int)m, total, ws,
+                       keys);
     return hipGetLastError();
 }
 
 static hipError_t launch_sm(const SmDesc* descs, int count, const SmDesc& one, int64_t m, int64_t total,
-                            int max_p, float* ws, hipStream_t s) {
+                            int max_p, float* ws, uint64_t* keys, hipStream_t s) {
     const size_t lds = smallm_lds(max_p, m);
     const bool swz = smallm_swizzle(max_p, m);
     if (engine_of(m)) {
         constexpr int t = Geo<1>::kWaves * 64;
-        return swz ? launch_k(k_smallm_lds<true>, t, descs, count, one, m, total, lds, ws, s)
-                   : launch_k(k_smallm_lds<false>, t, descs, count, one, m, total, lds, ws, s);
+        return swz ? launch_k(k_smallm_lds<true>, t, descs, count, one, m, total, lds, ws, keys, s)
+                   : launch_k(k_smallm_lds<false>, t, descs, count, one, m, total, lds, ws, keys, s);
     }
     constexpr int t = Geo<0>::kWaves * 64;
-    return swz ? launch_k(k_smallm_reg<true>, t, descs, count, one, m, total, lds, ws, s)
-               : launch_k(k_smallm_reg<false>, t, descs, count, one, m, total, lds, ws, s);
+    return swz ? launch_k(k_smallm_reg<true>, t, descs, count, one, m, total, lds, ws, keys, s)
+               : launch_k(k_smallm_reg<false>, t, descs, count, one, m, total, lds, ws, keys, s);
+}
+
+int smallm_key_slices(int64_t m, int64_t n, int64_t k) {
+    SmDesc d = {};
+    d.n = n;
+    d.k = (int32_t)k;
+    smallm_fill(&d, m, 0, 0);
+    return d.nranges == 1 && engine_of(m) ? smallm_grid(smallm_cost(d)) : 0;  // the LDS-ring engine only
+}
+
+hipError_t launch_gemm_smallm_keys(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n, int64_t k,
+                                   uint64_t* keys, hipStream_t s) {
+    SmDesc d = {};
+    d.w = w;
+    d.x = x;
+    d.y = y;
+    d.n = n;
+    d.k = (int32_t)k;
+    smallm_fill(&d, m, 0, 0);
+    if (d.nranges != 1 || !engine_of(m)) return hipErrorInvalidValue;
+    return launch_sm(nullptr, 1, d, m, smallm_cost(d), d.P, nullptr, keys, s);
 }
 
 hipError_t launch_gemm_smallm(const uint8_t* w, const uint16_t* x, float* y, int64_t m, int64_t n, int64_t k,
@@ -701,7 +766,7 @@ hipError_t launch_gemm_smallm(const uint8_t* w, const uint16_t* x, float* y, int
     d.k = (int32_t)k;
     smallm_fill(&d, m, 0, 0);
     const int64_t total = smallm_cost(d);
-    hipError_t e = launch_sm(nullptr, 1, d, m, total, d.P, workspace, s);
+    hipError_t e = launch_sm(nullptr, 1, d, m, total, d.P, workspace, nullptr, s);
     if (e != hipSuccess || d.nranges < 2) return e;
     const int grid = (int)std::min<int64_t>((m * n + 255) / 256, (int64_t)device_cu_count() * 4);
     hipLaunchKernelGGL(k_sum_ranges, dim3(grid, 1), dim3(256), 0, s, nullptr, 1, d, (int)m, workspace);
@@ -711,7 +776,7 @@ hipError_t launch_gemm_smallm(const uint8_t* w, const uint16_t* x, float* y, int
 hipError_t launch_gemm_smallm_batch(const SmDesc* descs, int count, int64_t m, int64_t total, int max_p,
                                     int64_t max_mn, bool any_split, float* workspace, hipStream_t s) {
     SmDesc none = {};
-    hipError_t e = launch_sm(descs, count, none, m, total, max_p, workspace, s);
+    hipError_t e = launch_sm(descs, count, none, m, total, max_p, workspace, nullptr, s);
     if (e != hipSuccess || !any_split) return e;
     const int gx = (int)std::max<int64_t>(1, std::min<int64_t>((max_mn + 255) / 256, 64));
     const int gy = std::min(count, 65535);

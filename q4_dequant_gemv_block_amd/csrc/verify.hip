@@ -7,8 +7,10 @@
 // (aipolix.com SwarmLLM page, section "Speculation is used to amortize network
 // round trips"); decoding is greedy (taozi.news, section "基准成绩").  The
 // logits come from the small-M GEMM (one pass over the vocabulary's weights
-// for all m rows; the GEMV for m = 1); then every row's slices are reduced to
-// 64-bit keys (argmax_key: larger logit first, then lower index) and one
+// for all m rows; the GEMV for m = 1); each row's logits are reduced to
+// 64-bit keys (argmax_key: larger logit first, then lower index), by the
+// small-M kernel itself as it stores them (one key per workgroup and row)
+// when K fits one K-range, else by a pass over row slices; then one
 // workgroup picks each row's token and counts the accepted prefix.
 #include "q4_device.h"
 #include "q4_launch.h"
@@ -66,9 +68,13 @@ int verify_slices(int64_t n) { return (int)std::max<int64_t>(1, std::min<int64_t
 
 }  // namespace
 
+// Keys per row: the separate pass's slices, or the small-M kernel's
+// workgroups when it writes them itself (at most kArgmaxMaxBlocks).
+static int key_slots(int64_t n) { return std::max(verify_slices(n), kArgmaxMaxBlocks); }
+
 size_t verify_workspace_bytes(int64_t m, int64_t n, int64_t k) {
     const size_t gemm = m >= 2 ? (smallm_workspace_bytes(m, n, k) + 255) / 256 * 256 : 0;
-    return gemm + (size_t)m * verify_slices(n) * sizeof(uint64_t);
+    return gemm + (size_t)m * key_slots(n) * sizeof(uint64_t);
 }
 
 hipError_t launch_lm_head_verify(const uint8_t* w, const uint16_t* h, float* logits, int32_t* tokens,
@@ -76,12 +82,22 @@ hipError_t launch_lm_head_verify(const uint8_t* w, const uint16_t* h, float* log
                                  void* workspace, hipStream_t s) {
     const size_t gemm = m >= 2 ? (smallm_workspace_bytes(m, n, k) + 255) / 256 * 256 : 0;
     uint64_t* keys = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) + gemm);
-    hipError_t e = m >= 2 ? launch_gemm_smallm(w, h, logits, m, n, k, static_cast<float*>(workspace), s)
-                          : launch_gemv(w, h, logits, n, k, s);
-    if (e != hipSuccess) return e;
-    const int B = verify_slices(n);
-    hipLaunchKernelGGL(k_argmax_rows, dim3(B, (unsigned)m), dim3(kRowThreads), 0, s, logits, n, keys);
-    e = hipGetLastError();
+    // m >= 2 with K in one range (the LM head's): the small-M kernel writes the
+    // keys of the logits it stores, one per workgroup and row.
+    const int fused = m >= 2 ? smallm_key_slices(m, n, k) : 0;
+    int B;
+    hipError_t e;
+    if (fused > 0 && fused <= key_slots(n)) {
+        e = launch_gemm_smallm_keys(w, h, logits, m, n, k, keys, s);
+        B = fused;
+    } else {
+        e = m >= 2 ? launch_gemm_smallm(w, h, logits, m, n, k, static_cast<float*>(workspace), s)
+                   : launch_gemv(w, h, logits, n, k, s);
+        if (e != hipSuccess) return e;
+        B = verify_slices(n);
+        hipLaunchKernelGGL(k_argmax_rows, dim3(B, (unsigned)m), dim3(kRowThreads), 0, s, logits, n, keys);
+        e = hipGetLastError();
+    }
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_verify_final, dim3(1), dim3(kRowThreads), 0, s, keys, B, (int)m, draft, tokens, accepted);
     return hipGetLastError();
