@@ -147,7 +147,8 @@ def test_negation_dot2_rounding():
     yn = run_gemv(w, -x).astype(np.float64)
     diff = np.nonzero(y != -yn)[0]
     say("negation: %d of %d rows not bit-negated; first %s" % (diff.size, n, diff[:8].tolist()))
-    assert diff.size <= n // 100
+    # the asymmetry is there (this input shows it on MI355X: 70 rows), and rare
+    assert 1 <= diff.size <= n // 100
     if diff.size:
         _, a_ref = oracle.gemm_rows(w[diff], k, x)
         ratio = np.abs(y[diff] + yn[diff]) / a_ref
