@@ -524,8 +524,9 @@ def bench_verify(args):
             "draft_tokens_per_s": round(m / (ms * 1e-3), 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counter_traffic("verify_m%d" % m),
-                         "kernel": ("q4::k_sweep (GEMV)" if m == 1 else "q4::k_smallm") +
-                                   " + k_argmax_rows + k_verify_final"}}
+                         "kernel": ("q4::k_sweep (GEMV) + k_argmax_rows" if m == 1 else
+                                    "q4::k_smallm_lds (row keys fused)" if m <= 7 else
+                                    "q4::k_smallm_reg + k_argmax_rows") + " + k_verify_final"}}
 
 
 def bench_gemm(args, prefill: bool):
@@ -560,12 +561,24 @@ def bench_gemm(args, prefill: bool):
           {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
            "frac": round(gbs / PEAK_HBM_GBS, 4)})
     rl["traffic"] = counter_traffic("prefill_m%d" % m if prefill else "smallm_m%d" % m)
-    return {"metric": "%s Q4_0 GEMM over the 64-layer sweep (M=%d)" % (name, m),
+    if prefill:
+        tm = batch.plan.tile_m
+        rl["kernel"] = "q4::k_prefill_q<%d,4> (batch, %d-row tiles)" % (tm // 32, tm)
+    else:
+        rl["kernel"] = ("q4::k_smallm_lds" if m <= 7 else "q4::k_smallm_reg") + " (batch)"
+    extra = {}
+    if not prefill and m >= 8:
+        # beside the HBM roofline: the matrix cores (every MFMA covers 16 activation rows whatever M is)
+        extra["roofline_mfma"] = {"bound": "mfma", "achieved": round(tf, 3), "peak": PEAK_F16_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": round(tf / PEAK_F16_TFLOPS, 5),
+                                  "issued_16_rows": round(tf * 16 / m, 3)}
+    return {**{"metric": "%s Q4_0 GEMM over the 64-layer sweep (M=%d)" % (name, m),
             "value": round(tf if prefill else gbs, 3), "unit": "TFLOP/s" if prefill else "GB/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16->f32",
             "data": "synthetic", "config": {"workload": "%s M=%d x 448 sweep GEMMs, %s" % (name, m, how)},
-            "tflops": round(tf, 3), "GBps": round(gbs, 2), "eager_ms_per_step": round(eager_ms, 4), "roofline": rl}
+            "tflops": round(tf, 3), "GBps": round(gbs, 2), "eager_ms_per_step": round(eager_ms, 4), "roofline": rl},
+            **extra}
 
 
 STREAM_BYTES = 16 << 30
