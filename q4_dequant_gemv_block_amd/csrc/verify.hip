@@ -39,23 +39,28 @@ __global__ void __launch_bounds__(kRowThreads) k_argmax_rows(const float* __rest
     if (threadIdx.x == 0) keys[(int64_t)blockIdx.y * B + blockIdx.x] = b;
 }
 
-// One workgroup: tokens[i] from row i's B keys, then the accepted prefix.
-__global__ void __launch_bounds__(kRowThreads) k_verify_final(const uint64_t* __restrict__ keys, int B, int m,
-                                                             const int32_t* __restrict__ draft,
-                                                             int32_t* __restrict__ tokens,
-                                                             int32_t* __restrict__ accepted) {
-    __shared__ uint64_t sh[kRowThreads / 64];
-    __shared__ int32_t tok[16];
-    for (int i = 0; i < m; ++i) {
+// One workgroup of 16 waves: wave i reduces row i's B keys to tokens[i]
+// (rows run side by side), then one thread counts the accepted prefix.
+constexpr int kFinalWaves = 16;
+__global__ void __launch_bounds__(kFinalWaves * 64) k_verify_final(const uint64_t* __restrict__ keys, int B, int m,
+                                                                  const int32_t* __restrict__ draft,
+                                                                  int32_t* __restrict__ tokens,
+                                                                  int32_t* __restrict__ accepted) {
+    __shared__ int32_t tok[kFinalWaves];
+    const int i = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (i < m) {
         uint64_t best = 0;
-        for (int b = threadIdx.x; b < B; b += kRowThreads) best = keys[(int64_t)i * B + b] > best ? keys[(int64_t)i * B + b] : best;
-        const uint64_t r = block_max_u64(best, sh);
-        if (threadIdx.x == 0) {
-            tok[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)(r & 0xFFFFFFFFu));
+        for (int b = lane; b < B; b += 64) {
+            const uint64_t v = keys[(int64_t)i * B + b];
+            best = v > best ? v : best;
+        }
+        best = wave_max_u64(best);
+        if (lane == 0) {
+            tok[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
             tokens[i] = tok[i];
         }
-        __syncthreads();  // sh is reused by the next row
     }
+    __syncthreads();
     if (threadIdx.x == 0) {
         int a = 0;
         while (a < m && tok[a] == draft[a]) ++a;
@@ -99,7 +104,7 @@ hipError_t launch_lm_head_verify(const uint8_t* w, const uint16_t* h, float* log
         e = hipGetLastError();
     }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_verify_final, dim3(1), dim3(kRowThreads), 0, s, keys, B, (int)m, draft, tokens, accepted);
+    hipLaunchKernelGGL(k_verify_final, dim3(1), dim3(kFinalWaves * 64), 0, s, keys, B, (int)m, draft, tokens, accepted);
     return hipGetLastError();
 }
 
