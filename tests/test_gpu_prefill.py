@@ -122,3 +122,30 @@ def test_batch_full_layers(m):
         y_ref, a_ref = oracle.gemm_rows(w, k, x)
         worst = max(worst, assert_parity(y, y_ref, a_ref, "prefill m=%d layer %d proj %d" % (m, layer, proj)))
     say("prefill full layers m=%d: worst err/a %.3g" % (m, worst))
+
+
+@pytest.mark.parametrize("k", [1024, 1088])
+def test_single_call_96_row_tiles(k):
+    """A single q4_0_gemm_prefill call wide enough to run 96-row tiles (M =
+    169, N = 33,000: 258 tiles of 96 x 256, more than the CUs), on both
+    kernels (k % 256 == 0 and not): 1,024 sampled rows against the oracle,
+    and bit-equal to the same GEMM in a batch (whose k % 256 != 0 part runs
+    64-row tiles: the tile shape does not change any output's summation
+    order)."""
+    q4 = lib()
+    m, n = 169, 33000
+    w = synth.q4_0(SEED, 9900 + k, n, k)
+    x = synth.f16_normal(SEED, 9950 + k, m * k).reshape(m, k)
+    wd, xd = dev_u8(w), dev_f16(x)
+    say("prefill single 96-row tiles", m, n, k)
+    y = q4.q4_0_gemm_prefill(wd, xd)
+    yb = torch.full((m, n), float("nan"), device="cuda")
+    batch = q4.PrefillBatch([(wd, xd, yb)])
+    assert batch.plan.tile_m == 96
+    batch()
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    assert np.array_equal(y, yb.cpu().numpy())
+    rows = sampled_rows(np.random.default_rng(k), n)
+    y_ref, a_ref = oracle.gemm_rows(w[rows], k, x)
+    assert_parity(y[:, rows], y_ref, a_ref, "prefill 96-row single m=%d n=%d k=%d" % (m, n, k))
