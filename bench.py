@@ -49,7 +49,7 @@ def log(*a):
 # Kernel source of each workload's dominant kernel (besides the shared device
 # and launch headers, the host-side C ABI and the build script).
 KERNEL_SOURCE = {"sweep": ["gemv.hip"], "gemv": ["gemv.hip"], "lmhead": ["gemv.hip"], "lmhead_norm": ["gemv.hip"],
-                 "handoff": ["gemv.hip"], "q8": ["q8.hip"],
+                 "handoff": ["gemv.hip"], "q8": ["gemv.hip", "q8.hip"],
                  "smallm": ["smallm.hip"],
                  "prefill": ["prefill.hip"], "verify": ["smallm.hip", "gemv.hip", "verify.hip"]}
 
@@ -328,6 +328,9 @@ def bench_q8(args):
             io += 2 * k + 4 * n
 
     batch = q4.Q8Batch(list(zip(ws, xs, ys)))
+    n_slab, n_all = batch.plan.n_slab, batch.plan.count
+    kernels = ([] if n_slab == 0 else ["q4::k_sweep<Q8Engine<12,2,448>> (%d GEMVs)" % n_slab]) + \
+        ([] if n_slab == n_all else ["q4::k_q8_batch (%d GEMVs)" % (n_all - n_slab)])
     ms = time_steps(batch, args.steps, args.warmup, settle_s=SETTLE_S)
 
     def singles():
@@ -348,12 +351,12 @@ def bench_q8(args):
             "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "f16->f32", "data": "synthetic",
             "config": {"workload": "36 layers x 7 Q8_0 GEMVs (q 4096x2560, k,v 1024x2560, o 2560x4096, gate,up "
-                                   "9728x2560, down 2560x9728), one q8_0_gemv_batch launch",
+                                   "9728x2560, down 2560x9728), one q8_0_gemv_batch call",
                        "weight_bytes": wbytes, "algorithmic_bytes_per_step": wbytes + io},
             "graph_of_single_launches_ms": round(graph_ms, 4),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counter_traffic("q8"),
-                         "kernel": "q4::k_q8_batch", "launches_per_step": 1}}
+                         "kernel": " + ".join(kernels), "launches_per_step": len(kernels)}}
 
 
 STAGE_LAYERS = 22  # a stage of layers 0..21, the pages' example of one peer's range

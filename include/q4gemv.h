@@ -191,6 +191,11 @@ Q4_API q4_status lm_head_argmax_noalloc(const void* w, const void* h, float* log
  *   x : k binary16 values, 16-byte aligned;  y : n binary32 (written)
  *   n >= 1, k % 32 == 0, 32 <= k <= 32768.  Inputs finite.  y must not
  *   overlap w or x.
+ * Two kernels, chosen by shape alone: k % 512 == 0 with 2048 <= k <= 28672
+ * and w 16-byte aligned streams whole 64-pair slabs of 8-row groups through
+ * LDS; any other shape reads each block through its own lane.  The two sum
+ * a row in different orders (both within the bound); a row's result depends
+ * only on its bytes, x and which kernel its shape selects.
  */
 Q4_API q4_status q8_0_gemv(const void* w, const void* x, float* y, int64_t n, int64_t k, void* stream);
 
@@ -362,28 +367,34 @@ Q4_API q4_status q4_0_gemv_batch_handoff(const q4_gemv_plan* plan, const float* 
 /* Host-side handle of a Q8_0 GEMV list plan.  Filled by q8_0_gemv_batch_plan;
  * plain data, may be copied. */
 typedef struct q8_gemv_plan {
-    void* device;  /* the caller's device buffer holding the plan */
-    int count;     /* number of GEMVs */
-    int max_k;     /* largest k in the list */
-    int grid;      /* workgroups of one launch */
-    int reserved;
+    void* device;        /* the caller's device buffer holding the plan */
+    int count;           /* number of GEMVs */
+    int n_slab;          /* internal: GEMVs on the slab kernel (the plan's first part) */
+    int grid_slab;       /* internal: workgroups of their launch */
+    int nchunks_slab;    /* internal: chunks of their schedule */
+    int max_k;           /* internal: largest k of the other GEMVs */
+    int grid;            /* internal: workgroups of the other GEMVs' launch */
+    size_t offset_other; /* internal: byte offset of the other GEMVs' part in the plan */
 } q8_gemv_plan;
 
-/* Device bytes q8_0_gemv_batch_plan needs for `count` descriptors on the
- * current device (0 when count is outside [1, 1<<20]). */
-Q4_API size_t q8_0_gemv_batch_plan_bytes(int count);
+/* Device bytes q8_0_gemv_batch_plan needs for this list on the current device
+ * (0, with the error text set, when the list is invalid). */
+Q4_API size_t q8_0_gemv_batch_plan_bytes(const q4_gemv_desc* descs, int count);
 
 /*
  * A list of Q8_0 GEMVs (descriptors as q4_gemv_desc, with w holding n rows of
- * k/32 Q8_0 blocks) run as one launch, for the layers of a small dense model
- * in one submission.  Validate `count` host-side descriptors (each as
- * q8_0_gemv requires; no output may overlap another output, an input or the
- * plan), lay the rows out in units of 16 rows of one GEMV, give every
- * workgroup one contiguous byte-balanced range of the first 85 % of the bytes
- * and hand the remaining units out in chunks through a counter, and copy the
- * counters (zero), descriptors and ranges into the caller's device buffer
- * `plan_buf` (16-byte aligned, at least q8_0_gemv_batch_plan_bytes(count)
- * bytes).  The copy is enqueued on `stream` and has completed when this call
+ * k/32 Q8_0 blocks) run as one launch per kernel (at most two), for the
+ * layers of a small dense model in one submission.  Validate `count`
+ * host-side descriptors (each as q8_0_gemv requires; no output may overlap
+ * another output, an input or the plan) and split them by the kernel
+ * q8_0_gemv would choose.  The slab kernel's GEMVs get the schedule of
+ * q4_0_gemv_batch_plan (row steps of 96 rows, a static first chunk per
+ * workgroup, then chunks from a counter); the others are laid out in units of
+ * 16 rows of one GEMV, every workgroup taking one contiguous byte-balanced
+ * range of the first 85 % of the bytes and then units in chunks from a
+ * counter.  Copy the counters (zero), descriptors, chunks and ranges into the
+ * caller's device buffer `plan_buf` (16-byte aligned, at least
+ * q8_0_gemv_batch_plan_bytes bytes).  The copy is enqueued on `stream` and has completed when this call
  * returns.  Launches of one plan must not overlap in time (they share its
  * counters; the last workgroup of a launch sets them back to zero, which also
  * makes the launch safe to capture in a HIP graph).  Every row's result
@@ -392,7 +403,7 @@ Q4_API size_t q8_0_gemv_batch_plan_bytes(int count);
 Q4_API q4_status q8_0_gemv_batch_plan(const q4_gemv_desc* descs, int count, void* plan_buf, size_t plan_bytes,
                                       q8_gemv_plan* plan, void* stream);
 
-/* Run every GEMV of a Q8_0 plan in one launch on `stream`. */
+/* Run every GEMV of a Q8_0 plan on `stream` (one launch per kernel the list uses). */
 Q4_API q4_status q8_0_gemv_batch(const q8_gemv_plan* plan, void* stream);
 
 /* Host-side handle of a small-M batch plan.  Filled by

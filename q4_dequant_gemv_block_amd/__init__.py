@@ -64,8 +64,9 @@ class GemvPlan(ctypes.Structure):
 
 
 class Q8Plan(ctypes.Structure):
-    _fields_ = [("device", ctypes.c_void_p), ("count", ctypes.c_int), ("max_k", ctypes.c_int),
-                ("grid", ctypes.c_int), ("reserved", ctypes.c_int)]
+    _fields_ = [("device", ctypes.c_void_p), ("count", ctypes.c_int), ("n_slab", ctypes.c_int),
+                ("grid_slab", ctypes.c_int), ("nchunks_slab", ctypes.c_int), ("max_k", ctypes.c_int),
+                ("grid", ctypes.c_int), ("offset_other", ctypes.c_size_t)]
 
 
 _lib = None
@@ -101,7 +102,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.q8_0_gemv.restype = ctypes.c_int
     lib.q4_0_gemv_batch_handoff.argtypes = [ctypes.POINTER(GemvPlan), vp, vp, vp, vp]
     lib.q4_0_gemv_batch_handoff.restype = ctypes.c_int
-    lib.q8_0_gemv_batch_plan_bytes.argtypes = [ctypes.c_int]
+    lib.q8_0_gemv_batch_plan_bytes.argtypes = [ctypes.POINTER(GemvDesc), ctypes.c_int]
     lib.q8_0_gemv_batch_plan_bytes.restype = ctypes.c_size_t
     lib.q8_0_gemv_batch_plan.argtypes = [ctypes.POINTER(GemvDesc), ctypes.c_int, vp, ctypes.c_size_t,
                                          ctypes.POINTER(Q8Plan), vp]
@@ -468,7 +469,7 @@ class Q8Batch:
         dev = items[0][0].device if items else torch.device("cuda")
         self.plan = Q8Plan()
         with torch.cuda.device(dev):  # the ranges are cut for this device's compute units
-            nbytes = int(lib.q8_0_gemv_batch_plan_bytes(len(items)))
+            nbytes = int(lib.q8_0_gemv_batch_plan_bytes(descs, len(items)))
             if nbytes == 0:
                 _check(Q4_ERR_INVALID_ARG)
             self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=dev)

@@ -36,6 +36,8 @@ q4_status hip_status(hipError_t e, const char* what) {
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+// The Q8_0 GEMVs that run on the slab engine (single calls and lists alike).
+bool q8_on_slabs(const void* w, int64_t k) { return q4::q8_slab_ok(k) && aligned(w, 16); }
 
 struct Range {
     uintptr_t lo, hi;  // [lo, hi)
@@ -235,8 +237,10 @@ q4_status q8_0_gemv(const void* w, const void* x, float* y, int64_t n, int64_t k
     const Range ry = range(y, (size_t)n * 4);
     if (overlap(ry, range(w, (size_t)(n * (k / 32) * 34))) || overlap(ry, range(x, (size_t)k * 2)))
         return fail(Q4_ERR_INVALID_ARG, "%s: output overlaps an input", fn);
-    const hipError_t e = q4::launch_q8_gemv(static_cast<const uint8_t*>(w), static_cast<const uint16_t*>(x), y, n, k,
-                                            static_cast<hipStream_t>(stream));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = q8_on_slabs(w, k)
+                             ? q4::launch_q8_slab_gemv(static_cast<const uint8_t*>(w), static_cast<const uint16_t*>(x), y, n, k, s)
+                             : q4::launch_q8_gemv(static_cast<const uint8_t*>(w), static_cast<const uint16_t*>(x), y, n, k, s);
     return hip_status(e, "q8_0_gemv launch");
 }
 
@@ -407,6 +411,69 @@ size_t plan_size(int count, size_t nchunks) {
     return sizeof(q4::SchedHead) + (size_t)count * sizeof(q4::PlanDesc) + nchunks * sizeof(q4::SchedChunk);
 }
 
+// A Q8_0 list: the GEMVs the slab engine takes (the same rule as a single
+// call, so a GEMV gives the same bits either way) form the plan's first part
+// (SchedHead, descriptors, chunks), the others its second part (Q8Head,
+// descriptors, workgroup ranges), each run by its own launch.
+struct Q8Layout {
+    std::vector<q4::PlanDesc> slab;
+    std::vector<q4::SchedChunk> chunks;
+    int grid_slab = 0;
+    std::vector<q4::Q8Desc> other;
+    std::vector<int64_t> wg_begin;
+    q4::Q8Head head{};
+    int grid_other = 0, max_k_other = 0;
+    size_t off_other = 0, bytes = 0;
+    std::vector<Range> outs, ins;
+};
+
+q4_status q8_layout(const char* fn, const q4_gemv_desc* descs, int count, Q8Layout* L) {
+    if (!descs) return fail(Q4_ERR_INVALID_ARG, "%s: null descriptor list", fn);
+    if (count < 1 || count > (1 << 20)) return fail(Q4_ERR_INVALID_ARG, "%s: count = %d outside [1, 1<<20]", fn, count);
+    for (int i = 0; i < count; ++i) {
+        const q4_gemv_desc& d = descs[i];
+        q4_status st = check_shape(fn, 1, 1, d.n, d.k);
+        if (st) return fail(st, "%s: descriptor %d: %s", fn, i, std::string(g_err).c_str());
+        if (d.k > q4::kFastMaxK) return fail(Q4_ERR_INVALID_ARG, "%s: descriptor %d: k above %lld", fn, i, (long long)q4::kFastMaxK);
+        if (!d.w || !d.x || !d.y) return fail(Q4_ERR_INVALID_ARG, "%s: descriptor %d: null tensor pointer", fn, i);
+        if (!aligned(d.w, 4) || !aligned(d.x, 16) || !aligned(d.y, 4))
+            return fail(Q4_ERR_MISALIGNED, "%s: descriptor %d: w must be 4-, x 16-, y 4-byte aligned", fn, i);
+        L->outs.push_back(range(d.y, (size_t)d.n * 4));
+        L->ins.push_back(range(d.w, (size_t)(d.n * (d.k / 32) * 34)));
+        L->ins.push_back(range(d.x, (size_t)d.k * 2));
+        if (q8_on_slabs(d.w, d.k)) {
+            q4::PlanDesc p = {};
+            p.w = static_cast<const uint8_t*>(d.w);
+            p.x = static_cast<const uint16_t*>(d.x);
+            p.y = d.y;
+            p.n = d.n;
+            p.k = (int32_t)d.k;
+            L->slab.push_back(p);
+        } else {
+            L->other.push_back(q4::Q8Desc{static_cast<const uint8_t*>(d.w), static_cast<const uint16_t*>(d.x), d.y, d.n,
+                                          (int32_t)d.k, 0, 0});
+            L->max_k_other = std::max<int>(L->max_k_other, (int)d.k);
+        }
+    }
+    std::sort(L->outs.begin(), L->outs.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+    for (size_t i = 1; i < L->outs.size(); ++i)
+        if (L->outs[i].lo < L->outs[i - 1].hi) return fail(Q4_ERR_INVALID_ARG, "%s: two outputs overlap", fn);
+    for (const Range& r : L->ins) {  // outputs are sorted and disjoint: only the neighbours of r.lo can overlap r
+        auto it = std::upper_bound(L->outs.begin(), L->outs.end(), r.lo, [](uintptr_t v, const Range& o) { return v < o.lo; });
+        if ((it != L->outs.end() && overlap(*it, r)) || (it != L->outs.begin() && overlap(*(it - 1), r)))
+            return fail(Q4_ERR_INVALID_ARG, "%s: an output overlaps an input", fn);
+    }
+    if (!L->slab.empty()) L->grid_slab = q4::build_schedule_q8(L->slab.data(), (int)L->slab.size(), &L->chunks);
+    if (!L->other.empty())
+        L->grid_other = q4::q8_batch_layout(L->other.data(), (int)L->other.size(), &L->wg_begin, &L->head);
+    const size_t first = L->slab.empty() ? 0 : plan_size((int)L->slab.size(), L->chunks.size());
+    L->off_other = (first + 15) / 16 * 16;
+    L->bytes = L->off_other + (L->other.empty() ? 0
+                                                : sizeof(q4::Q8Head) + L->other.size() * sizeof(q4::Q8Desc) +
+                                                      L->wg_begin.size() * sizeof(int64_t));
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -508,77 +575,74 @@ q4_status q4_0_gemv_batch_handoff(const q4_gemv_plan* plan, const float* y, cons
     return hip_status(e, "q4_0_gemv_batch_handoff copy");
 }
 
-size_t q8_0_gemv_batch_plan_bytes(int count) {
-    if (count < 1 || count > (1 << 20)) return 0;
-    const int64_t grid_max = q4::kQ8WgPerCu * (int64_t)q4::device_cu_count();
-    return sizeof(q4::Q8Head) + (size_t)count * sizeof(q4::Q8Desc) + (size_t)(grid_max + 1) * sizeof(int64_t);
+size_t q8_0_gemv_batch_plan_bytes(const q4_gemv_desc* descs, int count) {
+    Q8Layout L;
+    if (q8_layout("q8_0_gemv_batch_plan_bytes", descs, count, &L)) return 0;
+    ok();
+    return L.bytes;
 }
 
 q4_status q8_0_gemv_batch_plan(const q4_gemv_desc* descs, int count, void* plan_buf, size_t plan_bytes,
                                q8_gemv_plan* plan, void* stream) {
     const char* fn = "q8_0_gemv_batch_plan";
-    if (!plan || !plan_buf || !descs) return fail(Q4_ERR_INVALID_ARG, "%s: null pointer", fn);
-    if (count < 1 || count > (1 << 20)) return fail(Q4_ERR_INVALID_ARG, "%s: count = %d outside [1, 1<<20]", fn, count);
-    std::vector<Range> outs, ins;
-    std::vector<q4::Q8Desc> dev(count);
-    int max_k = 0;
-    for (int i = 0; i < count; ++i) {
-        const q4_gemv_desc& d = descs[i];
-        q4_status st = check_shape(fn, 1, 1, d.n, d.k);
-        if (st) return fail(st, "%s: descriptor %d: %s", fn, i, std::string(g_err).c_str());
-        if (d.k > q4::kFastMaxK) return fail(Q4_ERR_INVALID_ARG, "%s: descriptor %d: k above %lld", fn, i, (long long)q4::kFastMaxK);
-        if (!d.w || !d.x || !d.y) return fail(Q4_ERR_INVALID_ARG, "%s: descriptor %d: null tensor pointer", fn, i);
-        if (!aligned(d.w, 4) || !aligned(d.x, 16) || !aligned(d.y, 4))
-            return fail(Q4_ERR_MISALIGNED, "%s: descriptor %d: w must be 4-, x 16-, y 4-byte aligned", fn, i);
-        outs.push_back(range(d.y, (size_t)d.n * 4));
-        ins.push_back(range(d.w, (size_t)(d.n * (d.k / 32) * 34)));
-        ins.push_back(range(d.x, (size_t)d.k * 2));
-        dev[i] = q4::Q8Desc{static_cast<const uint8_t*>(d.w), static_cast<const uint16_t*>(d.x), d.y, d.n,
-                            (int32_t)d.k, 0, 0};
-        max_k = std::max<int>(max_k, (int)d.k);
-    }
-    std::sort(outs.begin(), outs.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
-    for (size_t i = 1; i < outs.size(); ++i)
-        if (outs[i].lo < outs[i - 1].hi) return fail(Q4_ERR_INVALID_ARG, "%s: two outputs overlap", fn);
-    for (const Range& r : ins) {  // outputs are sorted and disjoint: only the neighbours of r.lo can overlap r
-        auto it = std::upper_bound(outs.begin(), outs.end(), r.lo, [](uintptr_t v, const Range& o) { return v < o.lo; });
-        if ((it != outs.end() && overlap(*it, r)) || (it != outs.begin() && overlap(*(it - 1), r)))
-            return fail(Q4_ERR_INVALID_ARG, "%s: an output overlaps an input", fn);
-    }
-    std::vector<int64_t> wg_begin;
-    q4::Q8Head head{};
-    const int grid = q4::q8_batch_layout(dev.data(), count, &wg_begin, &head);
-    const size_t need = sizeof(head) + (size_t)count * sizeof(q4::Q8Desc) + wg_begin.size() * sizeof(int64_t);
-    if (plan_bytes < need) return fail(Q4_ERR_WORKSPACE, "%s: plan buffer of %zu bytes needed", fn, need);
+    if (!plan || !plan_buf) return fail(Q4_ERR_INVALID_ARG, "%s: null pointer", fn);
+    Q8Layout L;
+    const q4_status st = q8_layout(fn, descs, count, &L);
+    if (st) return st;
+    if (plan_bytes < L.bytes) return fail(Q4_ERR_WORKSPACE, "%s: plan buffer of %zu bytes needed", fn, L.bytes);
     if (!aligned(plan_buf, 16)) return fail(Q4_ERR_MISALIGNED, "%s: plan buffer must be 16-byte aligned", fn);
-    const Range rp = range(plan_buf, need);
-    for (const Range& r : outs)
+    const Range rp = range(plan_buf, L.bytes);
+    for (const Range& r : L.outs)
         if (overlap(rp, r)) return fail(Q4_ERR_INVALID_ARG, "%s: the plan buffer overlaps a tensor", fn);
-    for (const Range& r : ins)
+    for (const Range& r : L.ins)
         if (overlap(rp, r)) return fail(Q4_ERR_INVALID_ARG, "%s: the plan buffer overlaps a tensor", fn);
-    std::vector<uint8_t> host(need);
-    std::memcpy(host.data(), &head, sizeof(head));
-    std::memcpy(host.data() + sizeof(head), dev.data(), dev.size() * sizeof(q4::Q8Desc));
-    std::memcpy(host.data() + sizeof(head) + dev.size() * sizeof(q4::Q8Desc), wg_begin.data(),
-                wg_begin.size() * sizeof(int64_t));
+    std::vector<uint8_t> host(L.bytes, 0);
+    if (!L.slab.empty()) {
+        const q4::SchedHead sh = {0u, 0u, (int32_t)L.chunks.size(), (int32_t)L.grid_slab};
+        std::memcpy(host.data(), &sh, sizeof(sh));
+        std::memcpy(host.data() + sizeof(sh), L.slab.data(), L.slab.size() * sizeof(q4::PlanDesc));
+        std::memcpy(host.data() + sizeof(sh) + L.slab.size() * sizeof(q4::PlanDesc), L.chunks.data(),
+                    L.chunks.size() * sizeof(q4::SchedChunk));
+    }
+    if (!L.other.empty()) {
+        uint8_t* o = host.data() + L.off_other;
+        std::memcpy(o, &L.head, sizeof(L.head));
+        std::memcpy(o + sizeof(L.head), L.other.data(), L.other.size() * sizeof(q4::Q8Desc));
+        std::memcpy(o + sizeof(L.head) + L.other.size() * sizeof(q4::Q8Desc), L.wg_begin.data(),
+                    L.wg_begin.size() * sizeof(int64_t));
+    }
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = hipMemcpyAsync(plan_buf, host.data(), need, hipMemcpyHostToDevice, s);
+    hipError_t e = hipMemcpyAsync(plan_buf, host.data(), L.bytes, hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return hip_status(e, "q8_0_gemv_batch_plan copy");
     plan->device = plan_buf;
     plan->count = count;
-    plan->max_k = max_k;
-    plan->grid = grid;
-    plan->reserved = 0;
+    plan->n_slab = (int)L.slab.size();
+    plan->grid_slab = L.grid_slab;
+    plan->nchunks_slab = (int)L.chunks.size();
+    plan->max_k = L.max_k_other;
+    plan->grid = L.grid_other;
+    plan->offset_other = L.off_other;
     return ok();
 }
 
 q4_status q8_0_gemv_batch(const q8_gemv_plan* plan, void* stream) {
-    if (!plan || !plan->device) return fail(Q4_ERR_INVALID_ARG, "q8_0_gemv_batch: null plan");
-    if (plan->count < 1 || plan->max_k < 32 || plan->max_k > q4::kFastMaxK || plan->max_k % 32 != 0 || plan->grid < 1)
-        return fail(Q4_ERR_INVALID_ARG, "q8_0_gemv_batch: plan was not filled by q8_0_gemv_batch_plan");
-    const hipError_t e = q4::launch_q8_batch(plan->device, plan->count, plan->grid, plan->max_k,
-                                             static_cast<hipStream_t>(stream));
+    const char* fn = "q8_0_gemv_batch";
+    if (!plan || !plan->device) return fail(Q4_ERR_INVALID_ARG, "%s: null plan", fn);
+    const int n_other = plan->count - plan->n_slab;
+    const bool slab_ok = plan->n_slab == 0 ? plan->grid_slab == 0
+                                           : plan->grid_slab >= 1 && plan->nchunks_slab >= plan->grid_slab;
+    const bool other_ok = n_other == 0 ? plan->grid == 0
+                                       : plan->grid >= 1 && plan->max_k >= 32 && plan->max_k <= q4::kFastMaxK &&
+                                             plan->max_k % 32 == 0 && plan->offset_other % 16 == 0;
+    if (plan->count < 1 || plan->n_slab < 0 || n_other < 0 || !slab_ok || !other_ok)
+        return fail(Q4_ERR_INVALID_ARG, "%s: plan was not filled by q8_0_gemv_batch_plan", fn);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    if (plan->n_slab > 0) e = q4::launch_q8_slab_batch(plan->device, plan->n_slab, plan->grid_slab, s);
+    if (e == hipSuccess && n_other > 0)
+        e = q4::launch_q8_batch(static_cast<uint8_t*>(plan->device) + plan->offset_other, n_other, plan->grid,
+                                plan->max_k, s);
     return hip_status(e, "q8_0_gemv_batch launch");
 }
 

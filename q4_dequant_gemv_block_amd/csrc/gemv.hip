@@ -38,6 +38,7 @@
 #include <algorithm>
 #include <atomic>
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 namespace q4 {
@@ -456,6 +457,11 @@ struct DmaEngine {
     int64_t rbase = 0;  // first row of row step 0 (a single GEMV's workgroup range)
     uint8_t* wl;     // this wave's window
 
+    // Activations of GEMV D into xs (chunk order of q4_device.h).
+    template <class L>
+    __device__ static void stage(const L& D, u4* __restrict__ xs) {
+        stage_x(D.x, D.k >> 5, D.npl * 16, XS > 0 ? XS : D.npl * 16, xs);
+    }
     __device__ __forceinline__ void init(uint8_t* window) {
         lane = threadIdx.x & 63;
         l16 = lane & 15;
@@ -621,6 +627,11 @@ struct QuadEngine {
     uint8_t* wl;      // this wave's ring
     lds_u32 rd[NB][R];  // this lane's pair in each slot and quad
 
+    // Activations of GEMV D into xs (chunk order of q4_device.h).
+    template <class L>
+    __device__ static void stage(const L& D, u4* __restrict__ xs) {
+        stage_x(D.x, D.k >> 5, D.npl * 16, XS > 0 ? XS : D.npl * 16, xs);
+    }
     __device__ __forceinline__ void init(uint8_t* window) {
         lane = threadIdx.x & 63;
         lane16 = (uint32_t)lane * 16u;
@@ -775,6 +786,223 @@ struct QuadEngine {
     }
 };
 
+
+// Q8_0 slab engine.  A Q8_0 block is an f16 scale then 32 two's-complement
+// code bytes (34 bytes; taozi.news, section "支持模型与限制", for the small
+// dense models that carry this format); a pair of blocks is 68 bytes, 17
+// dwords.  A wave's rows of a row step are 8 consecutive rows (an oct) whose
+// 8 np pairs (np = k/64, a multiple of 8) are 8 np / 64 whole slabs of 64
+// pairs (4,352 bytes: four 1 KiB loads and one of 256 bytes); lane l holds
+// pair 64 jb + l of the oct in slab jb, which belongs to oct row
+// (64 jb + l) / np.  With np >= 32 a slab holds pairs of at most three rows.
+//  * Codes become exact f16 pairs: byte xor 0x80 is code + 128, placed under
+//    the exponent byte 0x64 it reads 1024 + code + 128, and 1152 is taken off.
+//    Block 0's codes start two bytes into the pair: its first and last two
+//    codes share one dword (one v_perm), the others are read as they lie, so
+//    no code dword is realigned; the activations are paired to match.
+//  * Each lane accumulates its pairs of a row in pair order, block 0 then
+//    block 1, each block's dot product chained from zero and scaled by one
+//    FMA.  A row's pairs sit in lanes (r np + p) mod 64, a rotation of the
+//    row's pair order by a multiple of 8 lanes; the row sum adds lanes l and
+//    l + 32, then l and l + 16, then l and l + 8 (pairs of classes that a
+//    rotation by 8 lanes maps onto each other), then the 8 lanes of a class
+//    slot p % 8 in a fixed tree, so a row's result depends on its own bytes
+//    only, wherever it sits.
+//  * The activations are staged in natural order: chunk c (halves 8c..8c+7)
+//    of pair p at xs[c * stride + p].
+// Code dword u (four codes) against x dwords (xa: codes 0,1; xb: codes 2,3).
+__device__ __forceinline__ float q8_dot4(uint32_t u, uint32_t xa, uint32_t xb, float s) {
+    const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+    const uint32_t v = u ^ 0x80808080u;
+    const h2 lo = as_h2(__builtin_amdgcn_perm(0x64646464u, v, 0x04010400u)) - bias;
+    const h2 hi = as_h2(__builtin_amdgcn_perm(0x64646464u, v, 0x04030402u)) - bias;
+    s = __builtin_amdgcn_fdot2(lo, as_h2(xa), s, false);
+    return __builtin_amdgcn_fdot2(hi, as_h2(xb), s, false);
+}
+
+// One Q8_0 pair (17 dwords D) against its 64 activations (X[c]: halves
+// 8c..8c+7): the two blocks' dot products s0, s1, each chained from zero.
+// Block 0's codes start two bytes into the pair: its last and first two
+// codes share one dword (one v_perm), the others are taken as they lie
+// (codes 4d-2 .. 4d+1 in dword d), and each code pair meets the activation
+// dword of the same two columns.
+__device__ __forceinline__ void q8_pair_sums(const uint32_t (&D)[17], const u4 (&X)[8], float& s0_out,
+                                             float& s1_out) {
+    float s0 = q8_dot4(__builtin_amdgcn_perm(D[0], D[8], 0x07060100u), X[3].w, X[0].x, 0.0f);
+#pragma unroll
+    for (int d = 1; d < 8; ++d) {  // x dwords 2d-1 and 2d (halves 4d-2 .. 4d+1)
+        const int m0 = 2 * d - 1, m1 = 2 * d;
+        s0 = q8_dot4(D[d], X[m0 >> 2][m0 & 3], X[m1 >> 2][m1 & 3], s0);
+    }
+    float s1 = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d)  // block 1: codes 4d .. 4d+3 in dword 9 + d
+        s1 = q8_dot4(D[9 + d], X[4 + (d >> 1)][2 * (d & 1)], X[4 + (d >> 1)][2 * (d & 1) + 1], s1);
+    s0_out = s0;
+    s1_out = s1;
+}
+// The pair into a row accumulator: a = d1 s1 + (d0 s0 + a).
+__device__ __forceinline__ float q8_pair_acc(const uint32_t (&D)[17], float s0, float s1, float a) {
+    return __builtin_fmaf(f16_hi(D[8]), s1, __builtin_fmaf(f16_lo(D[0]), s0, a));
+}
+
+// The last steps of a Q8_0 row sum: w holds, in each lane l, the row's
+// partial over lanes l, l^8, l^16, ... (classes), for class slot l % 8; the 8
+// slots of each group of 8 lanes are summed in a fixed tree, the total landing
+// in the group's first lane.
+__device__ __forceinline__ float q8_slot_tree(float w) {
+    float t = w + dpp_mov<0xB1>(w);  // quad_perm [1,0,3,2]
+    t = t + dpp_mov<0x4E>(t);        // quad_perm [2,3,0,1]
+    return t + dpp_mov<0x104>(t);    // row_shl:4
+}
+
+template <int WAVES, int NB, int XS>
+struct Q8Engine {
+    static constexpr int kWaves = WAVES;
+    static constexpr int kNB = NB;
+    static constexpr int kRowsPerWave = 8;
+    static constexpr int kPair = 68;                 // two 34-byte blocks
+    static constexpr int kSlab = 64 * kPair;        // 4352
+    static constexpr int kLoads = 5;
+    static constexpr int kWaveLds = NB * kSlab;
+    struct Regs {
+        uint32_t d[17];
+    };
+    // One accumulator per oct row, as separate variables (compile-time indices only).
+    struct Acc {
+        float a[8];
+        int rc;  // oct row of the slab's first pair (uniform)
+        int nb;  // first pair of oct row rc + 1, counted from the oct start (uniform)
+    };
+    int lane;
+    uint32_t wrow0;     // first row of this wave within a step
+    int64_t rbase = 0;  // first row of row step 0 (a single GEMV's workgroup range)
+    uint8_t* wl;        // this wave's ring
+    Rsrc cur;           // the oct's next slab
+
+    __device__ __forceinline__ void init(uint8_t* window) {
+        lane = threadIdx.x & 63;
+        const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+        wrow0 = (uint32_t)(wave * 8);
+        wl = window;
+    }
+    __device__ __forceinline__ void init_acc(Acc& a) const {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a.a[i] = 0.0f;
+        a.rc = 0;
+        a.nb = 0;
+    }
+    template <class L>
+    __device__ static void stage(const L& D, u4* __restrict__ xs) {
+        const int stride = XS > 0 ? XS : D.npl * 8;
+        const int n = D.k >> 3;  // chunks of 8 halves
+        for (int i = threadIdx.x; i < n; i += WAVES * 64) xs[(i & 7) * stride + (i >> 3)] = ((g_u4*)D.x)[i];
+        staged_loads_done();
+    }
+    template <class DS>
+    __device__ __forceinline__ void begin(const DS& D, int s) {
+        const uint64_t rb = (uint32_t)(D.k >> 6) * (uint64_t)kPair;
+        const uint64_t row0 = (uint64_t)rbase + (uint64_t)s * (WAVES * 8) + wrow0;
+        const uint64_t end = (uint64_t)(uint32_t)D.n * rb;
+        const uint64_t off = row0 * rb;
+        const int64_t left = (int64_t)(end - off);
+        const int32_t hi = (int32_t)((uint64_t)left >> 32);
+        const uint32_t nrec = hi < 0 ? 0u : (hi > 0 ? 0xFFFFFFFFu : (uint32_t)left);
+        cur = make_rsrc(D.w + off, nrec);
+    }
+    __device__ __forceinline__ void issue(int slot) {
+        uint8_t* dst = wl + slot * kSlab;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dma16(cur, 1024 * q + 16 * lane, dst + 1024 * q);
+        dma4(cur, 4096 + 4 * lane, dst + 4096);
+        cur = rsrc_advance(cur, kSlab);
+    }
+    template <class DS>
+    __device__ __forceinline__ void fetch(const DS& Dp, int s, int jb, int slot, uint32_t after, Regs& W) const {
+        (void)Dp;
+        (void)s;
+        (void)jb;
+        wait_unit<kLoads, kNB>(after);
+        typedef const __attribute__((address_space(3))) uint32_t* lds_u32;
+        const lds_u32 src = (lds_u32)(wl + slot * kSlab + kPair * lane);
+#pragma unroll
+        for (int c = 0; c < 17; ++c) W.d[c] = src[c];
+        wait_lgkm0();  // the reads are done before the slot is reloaded
+    }
+
+    template <class DS>
+    __device__ __forceinline__ void math(const DS& Dp, int jb, const u4* __restrict__ xs, const Regs& W,
+                                         Acc& acc) const {
+        const int np = Dp.k >> 6;
+        const int o = 64 * jb;  // first pair of the slab within the oct
+        if (jb == 0) {
+            acc.rc = 0;
+            acc.nb = np;
+        }
+        const int b1 = acc.nb - o;  // lanes >= b1 hold pairs of row rc + 1 (b1 >= 64: none)
+        const int b2 = b1 + np;     // lanes >= b2 hold pairs of row rc + 2
+        const int j = (lane >= b1 ? 1 : 0) + (lane >= b2 ? 1 : 0);
+        const int p = o + lane - (acc.nb - np) - j * np;  // pair within its row
+        const int stride = XS > 0 ? XS : Dp.npl * 8;
+        const u4* xb = xs + p;
+        u4 X[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) X[c] = xb[c * stride];
+        float s0, s1;
+        q8_pair_sums(W.d, X, s0, s1);
+        auto upd = [&](auto R) {
+            constexpr int r = decltype(R)::value;
+            if (b1 >= 64) {
+                acc.a[r] = q8_pair_acc(W.d, s0, s1, acc.a[r]);
+                return;
+            }
+            float t = acc.a[r];
+            if constexpr (r + 1 < 8) t = j == 1 ? acc.a[r + 1] : t;
+            if constexpr (r + 2 < 8) t = j == 2 ? acc.a[r + 2] : t;
+            t = q8_pair_acc(W.d, s0, s1, t);
+            acc.a[r] = j == 0 ? t : acc.a[r];
+            if constexpr (r + 1 < 8) acc.a[r + 1] = j == 1 ? t : acc.a[r + 1];
+            if constexpr (r + 2 < 8) acc.a[r + 2] = j == 2 ? t : acc.a[r + 2];
+        };
+        switch (acc.rc) {
+            case 0: upd(std::integral_constant<int, 0>{}); break;
+            case 1: upd(std::integral_constant<int, 1>{}); break;
+            case 2: upd(std::integral_constant<int, 2>{}); break;
+            case 3: upd(std::integral_constant<int, 3>{}); break;
+            case 4: upd(std::integral_constant<int, 4>{}); break;
+            case 5: upd(std::integral_constant<int, 5>{}); break;
+            case 6: upd(std::integral_constant<int, 6>{}); break;
+            default: upd(std::integral_constant<int, 7>{}); break;
+        }
+        while (acc.nb <= o + 64) {  // the next slab's first row
+            ++acc.rc;
+            acc.nb += np;
+        }
+    }
+
+    // After the oct's last slab: row r of the oct ends in lane 8r.
+    template <class F>
+    __device__ __forceinline__ void finish(int s, Acc& acc, F&& store) const {
+        // Each level keeps half of the rows a lane holds and adds the partner's
+        // value of them: lanes 0..31 keep rows 0..3, lanes 32..63 rows 4..7;
+        // then, within each half, lanes with bit 4 clear keep the half's rows
+        // 0, 1, the others 2, 3.
+        const bool b5 = (lane & 32) != 0, b4 = (lane & 16) != 0;
+        float u[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] = (b5 ? acc.a[i + 4] : acc.a[i]) + __shfl_xor(b5 ? acc.a[i] : acc.a[i + 4], 32, 64);
+        float v[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) v[i] = (b4 ? u[i + 2] : u[i]) + __shfl_xor(b4 ? u[i] : u[i + 2], 16, 64);
+        // bit 3 picks one of the two; the partner is 8 lanes away
+        const bool b3 = (lane & 8) != 0;
+        const float w = (b3 ? v[1] : v[0]) + dpp_mov<0x128>(b3 ? v[0] : v[1]);  // row_ror:8
+        const float t = q8_slot_tree(w);  // lane 8r: the total of row r
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc.a[i] = 0.0f;
+        if ((lane & 7) == 0) store(0, rbase + (int64_t)s * (WAVES * 8) + wrow0 + (lane >> 3), t);
+    }
+};
 
 // The fields of a GEMV the sweep kernel keeps in scalar registers.
 struct Live {
@@ -986,7 +1214,7 @@ k_sweep(const PlanDesc* __restrict__ descs, int count, SchedHead* head, const Sc
             }
             if (!NORM && u.d != staged) {  // (with the norm, staged before the first step)
                 lds_barrier();  // every wave is done with the previous activations
-                stage_x(Dc.x, Dc.k >> 5, Dc.npl * 16, XS > 0 ? XS : Dc.npl * 16, xs);
+                E::stage(Dc, xs);
                 lds_barrier();
                 staged = u.d;
             }
@@ -1355,14 +1583,14 @@ hipError_t launch_gemm_generic(const uint8_t* w, const uint16_t* x, float* y, in
 static constexpr double kStaticShare = Q4_SCHED_STATIC;
 static constexpr int kGuidedDiv = Q4_SCHED_DIV;  // dynamic chunks: remaining / (kGuidedDiv * grid)
 
-void build_schedule(PlanDesc* descs, int count, std::vector<SchedChunk>* out, int* grid_out, int* flags_out) {
+// The schedule of a list whose row steps have `rows_per_step` rows and whose
+// GEMV of width k takes npl(k) units per wave and row step; returns the grid.
+static int schedule_list(PlanDesc* descs, int count, int rows_per_step, int wg_per_cu, int (*npl)(int64_t),
+                         std::vector<SchedChunk>* out) {
     // GEMVs with more units per row step first: the chunks handed out last
     // are then the shortest, and so is the wait for the last workgroup.
     std::stable_sort(descs, descs + count,
-                     [](const PlanDesc& a, const PlanDesc& b) { return npl_of(a.k) > npl_of(b.k); });
-    bool quad = true;
-    for (int i = 0; i < count; ++i) quad = quad && quad_ok(descs[i].k);
-    const Shape& sh = quad ? kQuadWide : kWide;
+                     [npl](const PlanDesc& a, const PlanDesc& b) { return npl(a.k) > npl(b.k); });
     struct Atom {
         int32_t d, s;
         int64_t cost;  // start cost of its first step
@@ -1372,8 +1600,8 @@ void build_schedule(PlanDesc* descs, int count, std::vector<SchedChunk>* out, in
     int open_units = 2;  // units of the last atom
     for (int i = 0; i < count; ++i) {
         PlanDesc& p = descs[i];
-        p.npl = npl_of(p.k);
-        p.steps = (p.n + sh.rows_per_step() - 1) / sh.rows_per_step();
+        p.npl = npl(p.k);
+        p.steps = (p.n + rows_per_step - 1) / rows_per_step;
         p.cost_begin = total;
         const int units = p.npl;  // one unit per 16 pairs of a row
         for (int64_t st = 0; st < p.steps; ++st) {
@@ -1387,7 +1615,7 @@ void build_schedule(PlanDesc* descs, int count, std::vector<SchedChunk>* out, in
     }
     if (open_units < 2 && atoms.size() > 1) atoms.pop_back();  // a lone one-unit step joins the atom before it
     const int64_t n_atoms = (int64_t)atoms.size();
-    const int grid = static_grid(n_atoms, sh, INT32_MAX);
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(n_atoms, (int64_t)device_cu_count() * wg_per_cu));
     out->clear();
     int64_t a = 0;
     auto cost_at = [&](int64_t i) { return i < n_atoms ? atoms[i].cost : total; };
@@ -1410,7 +1638,14 @@ void build_schedule(PlanDesc* descs, int count, std::vector<SchedChunk>* out, in
         (*out)[i].c_end = descs[nx.d0].cost_begin + (int64_t)nx.s0 * descs[nx.d0].npl;
     }
     out->back().c_end = total;
-    *grid_out = grid;
+    return grid;
+}
+
+void build_schedule(PlanDesc* descs, int count, std::vector<SchedChunk>* out, int* grid_out, int* flags_out) {
+    bool quad = true;
+    for (int i = 0; i < count; ++i) quad = quad && quad_ok(descs[i].k);
+    const Shape& sh = quad ? kQuadWide : kWide;
+    *grid_out = schedule_list(descs, count, sh.rows_per_step(), sh.wg_per_cu, npl_of, out);
     *flags_out = quad ? kPlanQuad : 0;
 }
 
@@ -1424,6 +1659,124 @@ hipError_t launch_gemv_batch(const void* plan, int count, int nchunks, int grid,
     PlanDesc none = {};
     return launch_any<true, false>((flags & kPlanQuad) ? kQuadWide : kWide, descs, count, head, chunks, none, max_k,
                                    grid, nullptr, s);
+}
+
+// Q8_0 rows kernel, for single GEMVs too small to fill the slab engine
+// (whose parallelism is one 8-row group per wave): one wave per row at a
+// time, lane l takes pairs l, l + 64, ... of the row, two pairs' loads in
+// flight, the activations staged in LDS as the slab engine stages them.  A
+// row gets the slab engine's association exactly: lane p mod 64 holds pair p
+// (the engine's lanes are the same up to a rotation by a multiple of 8, which
+// the tree below does not see), the same per-pair arithmetic in pair order,
+// the same lane tree.  Either kernel gives a row the same bits.
+constexpr int kQ8RowWaves = 8;
+
+__device__ __forceinline__ void load_q8_pair(const uint8_t* p, uint32_t (&D)[17]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const u4a4 v = *(g_u4a4*)(p + 16 * i);
+        D[4 * i] = v.x; D[4 * i + 1] = v.y; D[4 * i + 2] = v.z; D[4 * i + 3] = v.w;
+    }
+    D[16] = *(g_u32*)(p + 64);
+}
+
+__global__ void __launch_bounds__(kQ8RowWaves * 64) k_q8_rows(const uint8_t* __restrict__ w,
+                                                            const uint16_t* __restrict__ x, float* __restrict__ y,
+                                                            int64_t n, int k) {
+    extern __shared__ u4 xs[];  // chunk c of pair p at xs[c * np + p]
+    const int np = k >> 6;
+    for (int i = threadIdx.x; i < (k >> 3); i += blockDim.x) xs[(i & 7) * np + (i >> 3)] = ((g_u4*)x)[i];
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int64_t rb = (int64_t)np * 68;
+    const int64_t nwaves = (int64_t)gridDim.x * kQ8RowWaves;
+    for (int64_t row = (int64_t)blockIdx.x * kQ8RowWaves + (threadIdx.x >> 6); row < n; row += nwaves) {
+        const uint8_t* wr = w + row * rb;
+        float a = 0.0f;
+        for (int p0 = lane; p0 < np; p0 += 128) {
+            uint32_t D[2][17];
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                if (p0 + 64 * u < np) load_q8_pair(wr + 68 * (int64_t)(p0 + 64 * u), D[u]);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int p = p0 + 64 * u;
+                if (p < np) {
+                    u4 X[8];
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) X[c] = xs[c * np + p];
+                    float s0, s1;
+                    q8_pair_sums(D[u], X, s0, s1);
+                    a = q8_pair_acc(D[u], s0, s1, a);
+                }
+            }
+        }
+        a = a + __shfl_xor(a, 32, 64);
+        a = a + __shfl_xor(a, 16, 64);
+        a = a + __shfl_xor(a, 8, 64);
+        const float t = q8_slot_tree(a);
+        if (lane == 0) y[row] = t;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Q8_0 on the sweep kernel (Q8Engine): a single GEMV and a list.
+// ---------------------------------------------------------------------------
+constexpr int kQ8XStride = 448;  // activation chunk stride in pairs: k <= 28672 (56 KiB of LDS)
+using Q8Wide = Q8Engine<12, 2, kQ8XStride>;
+constexpr int kQ8WideRows = Q8Wide::kWaves * 8;  // 96 rows per row step
+
+bool q8_slab_ok(int64_t k) { return k % 512 == 0 && k >= 2048 && k <= 64 * (int64_t)kQ8XStride; }
+static int q8_npl(int64_t k) { return (int)(k / 512); }  // slabs of a wave's 8 rows
+
+template <class E, int XS, bool BATCH>
+static hipError_t launch_q8_sweep(const PlanDesc* descs, int count, SchedHead* head, const SchedChunk* chunks,
+                                  const PlanDesc& one, int64_t max_k, int grid, hipStream_t s) {
+    const size_t xsb = (size_t)(XS > 0 ? XS : max_k / 64) * kChunksPerPair * sizeof(u4);
+    const size_t lds = xsb + (size_t)E::kWaves * E::kWaveLds;
+    auto kern = k_sweep<E, XS, BATCH, false, false, false>;
+    if (lds > 65536) {
+        const hipError_t e = allow_dynamic_lds((const void*)kern, lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(E::kWaves * 64), lds, s, descs, count, head, chunks, one, (int)xsb,
+                       nullptr, NormArgs{nullptr, nullptr, 0.0f, nullptr});
+    return hipGetLastError();
+}
+
+// A single GEMV: the slab engine when it gives every CU two workgroups' row
+// steps, else the rows kernel (the same bits either way).
+hipError_t launch_q8_slab_gemv(const uint8_t* w, const uint16_t* x, float* y, int64_t n, int64_t k, hipStream_t s) {
+    const int cus = device_cu_count();
+    if ((n + kQ8WideRows - 1) / kQ8WideRows >= 2 * (int64_t)cus) {
+        PlanDesc d = {};
+        d.w = w;
+        d.x = x;
+        d.y = y;
+        d.n = n;
+        d.k = (int32_t)k;
+        d.npl = q8_npl(k);
+        d.steps = (n + kQ8WideRows - 1) / kQ8WideRows;
+        const int grid = (int)std::min<int64_t>(d.steps, cus);
+        return launch_q8_sweep<Q8Wide, kQ8XStride, false>(nullptr, 1, nullptr, nullptr, d, k, grid, s);
+    }
+    const int64_t wgs = (n + kQ8RowWaves - 1) / kQ8RowWaves;
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(wgs, 2 * (int64_t)cus));
+    hipLaunchKernelGGL(k_q8_rows, dim3(grid), dim3(kQ8RowWaves * 64), (size_t)k * 2, s, w, x, y, n, (int)k);
+    return hipGetLastError();
+}
+
+int build_schedule_q8(PlanDesc* descs, int count, std::vector<SchedChunk>* out) {
+    return schedule_list(descs, count, kQ8WideRows, 1, q8_npl, out);
+}
+
+hipError_t launch_q8_slab_batch(const void* plan, int count, int grid, hipStream_t s) {
+    const uint8_t* base = static_cast<const uint8_t*>(plan);
+    SchedHead* head = (SchedHead*)base;
+    const PlanDesc* descs = (const PlanDesc*)(base + sizeof(SchedHead));
+    const SchedChunk* chunks = (const SchedChunk*)(base + sizeof(SchedHead) + (size_t)count * sizeof(PlanDesc));
+    PlanDesc none = {};
+    return launch_q8_sweep<Q8Wide, kQ8XStride, true>(descs, count, head, chunks, none, 64 * kQ8XStride, grid, s);
 }
 
 }  // namespace q4

@@ -86,7 +86,7 @@ struct SmDesc {
     int32_t np;          // pairs per row (k / 64)
     int32_t P;           // pairs per K-range (a multiple of 16)
     int32_t nranges;     // K-ranges
-    int32_t tiles;       // tiles of 256 rows
+    int32_t tiles;       // row tiles (256 rows when m > 7, 128 when m <= 7)
     int32_t m;           // activation rows (the engine and its unit size depend on it)
     int64_t ws_off;      // first partial-sum float in the workspace (nranges > 1)
     int64_t cost_begin;  // units of the earlier descriptors
@@ -167,6 +167,17 @@ hipError_t launch_lm_head(const uint8_t* w, const uint16_t* h, float* logits, in
                           int64_t n, int64_t k, uint64_t* keys, hipStream_t s);
 // Q8_0 GEMV (q8.hip): any k % 32 == 0 up to kFastMaxK, w 4-byte aligned, x 16-byte aligned.
 hipError_t launch_q8_gemv(const uint8_t* w, const uint16_t* x, float* y, int64_t n, int64_t k, hipStream_t s);
+// Q8_0 on the sweep kernel's slab engine (gemv.hip): k % 512 == 0, 2048 <= k <= 28672,
+// w 16-byte aligned, x 16-byte aligned.  The library routes a GEMV there exactly
+// when q8_slab_ok(k) holds and w is 16-byte aligned, single calls and lists alike.
+bool q8_slab_ok(int64_t k);
+hipError_t launch_q8_slab_gemv(const uint8_t* w, const uint16_t* x, float* y, int64_t n, int64_t k, hipStream_t s);
+// A list on the slab engine: orders descs[0..count) (npl, steps and cost_begin
+// filled as for the Q4_0 list, in units of 64-pair slabs) and cuts the
+// schedule; returns the grid.  The plan in device memory: SchedHead, the
+// `count` PlanDesc, the chunks.
+int build_schedule_q8(PlanDesc* descs, int count, std::vector<SchedChunk>* out);
+hipError_t launch_q8_slab_batch(const void* plan, int count, int grid, hipStream_t s);
 // A Q8_0 GEMV list in one launch.  The plan in device memory: a Q8Head, then
 // `count` Q8Desc, then grid + 1 int64 unit indices (workgroup g first takes
 // units [b[g], b[g+1])); a unit is kQ8UnitRows consecutive rows of one GEMV.

@@ -204,11 +204,11 @@ def test_q8_gemv_validation(lib):
 def test_q8_batch_validation(lib):
     D = q4.GemvDesc
     plan = q4.Q8Plan()
-    assert lib.q8_0_gemv_batch_plan_bytes(0) == 0
-    nbytes = lib.q8_0_gemv_batch_plan_bytes(2)
-    assert nbytes >= 2 * 48 + 16
+    assert lib.q8_0_gemv_batch_plan_bytes(None, 0) == 0
     buf = FAKE * 64
     good = (D * 2)(D(FAKE, FAKE * 2, FAKE * 4, 8, 96), D(FAKE * 8, FAKE * 2, FAKE * 6, 8, 64))
+    nbytes = lib.q8_0_gemv_batch_plan_bytes(good, 2)
+    assert nbytes >= 2 * 48 + 32
     # the two outputs overlap
     arr = (D * 2)(D(FAKE, FAKE * 2, FAKE * 4, 8, 96), D(FAKE * 8, FAKE * 2, FAKE * 4 + 16, 8, 64))
     assert lib.q8_0_gemv_batch_plan(arr, 2, buf, nbytes, ctypes.byref(plan), None) == q4.Q4_ERR_INVALID_ARG
@@ -226,6 +226,33 @@ def test_q8_batch_validation(lib):
     assert lib.q8_0_gemv_batch_plan(good, 2, FAKE * 4, nbytes, ctypes.byref(plan), None) == q4.Q4_ERR_INVALID_ARG
     assert lib.q8_0_gemv_batch(None, None) == q4.Q4_ERR_INVALID_ARG
     assert lib.q8_0_gemv_batch(ctypes.byref(q4.Q8Plan()), None) == q4.Q4_ERR_INVALID_ARG
+
+
+def test_q8_batch_splits_by_kernel(lib):
+    """A Q8_0 list is split by the kernel a single call would take: k % 512 == 0
+    in [2048, 28672] with w 16-byte aligned goes to the slab kernel (the plan's
+    first part: a 16-byte head, 72-byte descriptors and 16-byte chunks, its
+    size rounded up to 16), the rest to the per-block kernel (second part)."""
+    D = q4.GemvDesc
+    W, X, Y, W2, X2, Y2 = (FAKE << 12) * 1, (FAKE << 12) * 2, (FAKE << 12) * 3, (FAKE << 12) * 4, (FAKE << 12) * 5, \
+        (FAKE << 12) * 6
+    slab = D(W, X, Y, 1000, 2560)
+    other = [D(W2, X2, Y2, 1000, 96),      # k not a multiple of 512
+             D(W2 + 4, X2, Y2, 1000, 2560),  # w 4- but not 16-byte aligned
+             D(W2, X2, Y2, 1000, 1536),    # k below 2048
+             D(W2, X2, Y2, 10, 29184)]     # k above 28672
+
+    def nbytes(*ds):
+        return lib.q8_0_gemv_batch_plan_bytes((D * len(ds))(*ds), len(ds))
+
+    s1 = nbytes(slab)
+    assert s1 >= 16 + 72 + 16 and s1 % 16 == 0 and s1 - 16 - 72 - 16 < 16 * 1000  # head, descriptor, chunks; rounded to 16
+    for o in other:
+        o1 = nbytes(o)
+        assert o1 >= 32 + 48 + 16 and (o1 - 32 - 48) % 8 == 0, o1  # head, one descriptor, grid + 1 ranges
+        assert nbytes(slab, o) == s1 + o1
+    assert nbytes(D(W, X, Y, 1000, 28672)) % 16 == 0  # the largest k on the slab kernel
+    assert lib.q4_last_error().decode() == ""
 
 
 def test_gemv_handoff_validation(lib):

@@ -117,7 +117,9 @@ def test_q8_batch_equals_single_calls():
     shapes = [(1, 32), (15, 96), (16, 160), (17, 2080), (300, 2560), (1024, 2560), (33, 32768), (2560, 9728),
               (5, 64), (4096, 2560)]
     ws, xs, items = _batch_items(shapes, 10100)
-    q4.Q8Batch(items)()
+    batch = q4.Q8Batch(items)
+    assert batch.plan.n_slab == 4  # (300, 2560), (1024, 2560), (2560, 9728), (4096, 2560)
+    batch()
     torch.cuda.synchronize()
     for i, ((w_d, x_d, y), w, x, (n, k)) in enumerate(zip(items, ws, xs, shapes)):
         single = q4.q8_0_gemv(w_d, x_d)
@@ -182,6 +184,79 @@ def test_q8_vocabulary_sized_rows_sampled():
     rows = np.unique(np.concatenate([[0, 1, n - 2, n - 1], np.random.default_rng(11).integers(0, n, 3000)]))
     y_ref, a_ref = oracle.q8_gemm_rows(np.ascontiguousarray(w[rows]), k, x)
     assert_parity(y[rows], y_ref, a_ref, "q8 vocabulary rows")
+
+
+# Shapes of the slab kernel (k % 512 == 0, 2048 <= k <= 28672, w 16-byte
+# aligned): fewer rows than one 8-row group, ragged row counts, slabs that
+# hold pairs of three rows (k = 2048: 32 pairs per row), rows that span many
+# slabs, the largest k; and the first k above it, which takes the per-block
+# kernel.  Single calls with fewer than 49,152 rows run on the rows kernel
+# (the slab engine's association), larger ones (50000 x 2048) on the slab engine.
+SLAB_SHAPES = [(1, 2048), (7, 2048), (9, 3072), (95, 2560), (97, 4096), (1000, 2048), (333, 9728),
+               (100, 28672), (50000, 2048), (64, 29184)]
+
+
+@pytest.mark.parametrize("n,k", SLAB_SHAPES, ids=["%dx%d" % s for s in SLAB_SHAPES])
+def test_q8_slab_shapes(n, k):
+    w = synth.q8_0(SEED, 11000 + k % 997, n, k)
+    x = synth.f16_normal(SEED, 11100 + n % 997, k)
+    say("q8 slab n=%d k=%d" % (n, k))
+    y = run(w, x)
+    y_ref, a_ref = oracle.q8_gemm_rows(w, k, x)
+    r = assert_parity(y, y_ref, a_ref, "q8 slab n=%d k=%d" % (n, k))
+    say("q8 slab n=%d k=%d max err/a %.3g" % (n, k, r))
+
+
+def test_q8_slab_rows_position_independent_long_rows():
+    """Rows of 152 pairs (k = 9728) span two or three slabs and start at every
+    multiple of 8 lanes: a shuffle of the rows gives the same bits."""
+    n, k = 515, 9728
+    w = synth.q8_0(SEED, 11201, n, k)
+    x = synth.f16_normal(SEED, 11202, k)
+    perm = np.random.default_rng(9).permutation(n)
+    y1 = run(w, x)
+    y2 = run(np.ascontiguousarray(w[perm]), x)
+    assert np.array_equal(y1[perm], y2)
+
+
+def test_q8_rows_kernel_equals_slab_engine():
+    """The same rows through the slab engine (a 49,200-row single call) and
+    through the rows kernel (single calls on slices of it): equal bits."""
+    n, k = 49200, 2560
+    q4 = lib()
+    w = synth.q8_0(SEED, 11401, n, k)
+    x = dev_f16(synth.f16_normal(SEED, 11402, k))
+    wd = dev_u8(w)
+    y = q4.q8_0_gemv(wd, x)
+    for lo, hi in [(0, 1000), (48001, 49200), (20000, 20037)]:
+        ys = q4.q8_0_gemv(wd[lo:hi], x)
+        torch.cuda.synchronize()
+        assert torch.equal(y[lo:hi], ys), (lo, hi)
+    y_ref, a_ref = oracle.q8_gemm_rows(np.ascontiguousarray(w[:2000]), k, x.cpu().numpy())
+    assert_parity(y[:2000].cpu().numpy(), y_ref, a_ref, "q8 slab engine rows")
+
+
+def test_q8_misaligned_weights_take_the_block_kernel():
+    """w 4- but not 16-byte aligned at a slab shape: the per-block kernel runs,
+    within the bound, and a list holding the same descriptor gives its bits."""
+    n, k = 300, 2560
+    w = synth.q8_0(SEED, 11301, n, k)
+    x = synth.f16_normal(SEED, 11302, k)
+    buf = torch.empty(w.size + 4, dtype=torch.uint8, device="cuda")
+    wd = buf[4:].view(n, -1)
+    wd.copy_(torch.from_numpy(w))
+    assert wd.data_ptr() % 16 == 4
+    q4 = lib()
+    xd = dev_f16(x)
+    y = q4.q8_0_gemv(wd, xd)
+    yb = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    batch = q4.Q8Batch([(wd, xd, yb)])
+    assert batch.plan.n_slab == 0
+    batch()
+    torch.cuda.synchronize()
+    assert torch.equal(y, yb)
+    y_ref, a_ref = oracle.q8_gemm_rows(w, k, x)
+    assert_parity(y.cpu().numpy(), y_ref, a_ref, "q8 misaligned")
 
 
 @pytest.mark.parametrize("n,k", [(1, 32768), (1, 32), (2, 33 * 32)])
