@@ -329,7 +329,7 @@ def bench_q8(args):
 
     batch = q4.Q8Batch(list(zip(ws, xs, ys)))
     n_slab, n_all = batch.plan.n_slab, batch.plan.count
-    kernels = ([] if n_slab == 0 else ["q4::k_sweep<Q8Engine<12,2,448>> (%d GEMVs)" % n_slab]) + \
+    kernels = ([] if n_slab == 0 else ["q4::k_sweep<Q8Engine<8,3,448>> (%d GEMVs)" % n_slab]) + \
         ([] if n_slab == n_all else ["q4::k_q8_batch (%d GEMVs)" % (n_all - n_slab)])
     ms = time_steps(batch, args.steps, args.warmup, settle_s=SETTLE_S)
 

@@ -388,7 +388,7 @@ Q4_API size_t q8_0_gemv_batch_plan_bytes(const q4_gemv_desc* descs, int count);
  * host-side descriptors (each as q8_0_gemv requires; no output may overlap
  * another output, an input or the plan) and split them by the kernel
  * q8_0_gemv would choose.  The slab kernel's GEMVs get the schedule of
- * q4_0_gemv_batch_plan (row steps of 96 rows, a static first chunk per
+ * q4_0_gemv_batch_plan (row steps of 64 rows, a static first chunk per
  * workgroup, then chunks from a counter); the others are laid out in units of
  * 16 rows of one GEMV, every workgroup taking one contiguous byte-balanced
  * range of the first 85 % of the bytes and then units in chunks from a

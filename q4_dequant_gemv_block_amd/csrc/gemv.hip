@@ -1722,9 +1722,21 @@ __global__ void __launch_bounds__(kQ8RowWaves * 64) k_q8_rows(const uint8_t* __r
 // ---------------------------------------------------------------------------
 // Q8_0 on the sweep kernel (Q8Engine): a single GEMV and a list.
 // ---------------------------------------------------------------------------
-constexpr int kQ8XStride = 448;  // activation chunk stride in pairs: k <= 28672 (56 KiB of LDS)
-using Q8Wide = Q8Engine<12, 2, kQ8XStride>;
-constexpr int kQ8WideRows = Q8Wide::kWaves * 8;  // 96 rows per row step
+#ifndef Q4_Q8_XS
+#define Q4_Q8_XS 448
+#endif
+constexpr int kQ8XStride = Q4_Q8_XS;  // activation chunk stride in pairs: k <= 64 * stride
+// 8 waves with three slabs in flight each (measured over the Qwen3-4B-shaped
+// list: 12 x 2 slots 0.78, 8 x 3 0.82-0.83, 9 x 3 and 10 x 3 with a smaller
+// activation stride 0.78, 6 x 4 0.74 of 8 TB/s).
+#ifndef Q4_Q8_WAVES
+#define Q4_Q8_WAVES 8
+#endif
+#ifndef Q4_Q8_NB
+#define Q4_Q8_NB 3
+#endif
+using Q8Wide = Q8Engine<Q4_Q8_WAVES, Q4_Q8_NB, kQ8XStride>;
+constexpr int kQ8WideRows = Q8Wide::kWaves * 8;  // rows per row step
 
 bool q8_slab_ok(int64_t k) { return k % 512 == 0 && k >= 2048 && k <= 64 * (int64_t)kQ8XStride; }
 static int q8_npl(int64_t k) { return (int)(k / 512); }  // slabs of a wave's 8 rows

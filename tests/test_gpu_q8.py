@@ -190,7 +190,7 @@ def test_q8_vocabulary_sized_rows_sampled():
 # aligned): fewer rows than one 8-row group, ragged row counts, slabs that
 # hold pairs of three rows (k = 2048: 32 pairs per row), rows that span many
 # slabs, the largest k; and the first k above it, which takes the per-block
-# kernel.  Single calls with fewer than 49,152 rows run on the rows kernel
+# kernel.  Single calls with fewer than 32,768 rows run on the rows kernel
 # (the slab engine's association), larger ones (50000 x 2048) on the slab engine.
 SLAB_SHAPES = [(1, 2048), (7, 2048), (9, 3072), (95, 2560), (97, 4096), (1000, 2048), (333, 9728),
                (100, 28672), (50000, 2048), (64, 29184)]
