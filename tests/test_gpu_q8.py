@@ -115,10 +115,12 @@ def test_q8_batch_equals_single_calls():
     """A mixed list in one launch: every row bit-equal to q8_0_gemv's, every row within the bound."""
     q4 = lib()
     shapes = [(1, 32), (15, 96), (16, 160), (17, 2080), (300, 2560), (1024, 2560), (33, 32768), (2560, 9728),
-              (5, 64), (4096, 2560)]
+              (5, 64), (4096, 2560), (3, 2048), (1, 4096), (9, 28672)]
     ws, xs, items = _batch_items(shapes, 10100)
     batch = q4.Q8Batch(items)
-    assert batch.plan.n_slab == 4  # (300, 2560), (1024, 2560), (2560, 9728), (4096, 2560)
+    # on the slab engine: (300, 2560), (1024, 2560), (2560, 9728), (4096, 2560), and the groups of
+    # fewer than 8 rows (3, 2048), (1, 4096) and (9, 28672)
+    assert batch.plan.n_slab == 7
     batch()
     torch.cuda.synchronize()
     for i, ((w_d, x_d, y), w, x, (n, k)) in enumerate(zip(items, ws, xs, shapes)):
