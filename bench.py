@@ -303,7 +303,7 @@ def bench_gemv(args):
             "hot_cache_GBps": round(bytes_ / (hot_ms * 1e-3) / 1e9, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counter_traffic("gemv"),
-                         "kernel": "q4::k_sweep<QuadEngine<4,1,4,288>>"}}
+                         "kernel": "q4::k_gemv_rows<288, false>"}}
 
 
 def bench_q8(args):

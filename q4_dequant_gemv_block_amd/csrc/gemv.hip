@@ -1005,6 +1005,61 @@ struct Q8Engine {
     }
 };
 
+// Rows kernel for single GEMVs too small to fill the engines (whose unit of
+// parallelism is a wave's 4R rows of a row step): one wave per row at a time,
+// lane l takes pairs l, l + 64, ... of the row (cached 36-byte loads, two
+// pairs in flight), the activations staged in LDS as the engines stage them.
+// A row gets the engines' association exactly: lane l holds lane slot l % 16
+// of class l / 16 (the engines' lanes differ by a rotation of whole 16-lane
+// classes, or keep the classes in separate accumulators), its pairs in pair
+// order through pair_acc; then lanes l and l + 32 (classes c and c + 2), l and
+// l + 16, and the 16 slots by row16_sum.  So a row has the same bits on
+// either path, and a single call equals a list's.  With H16 the row is
+// written as binary16(residual + y) (the stage hand-off) in place of y.
+constexpr int kRowWaves = 8;
+
+template <int XS, bool H16>
+__global__ void __launch_bounds__(kRowWaves * 64) k_gemv_rows(const uint8_t* __restrict__ w,
+                                                            const uint16_t* __restrict__ x, float* __restrict__ y,
+                                                            const float* __restrict__ residual, int64_t n, int k) {
+    extern __shared__ u4 xs[];
+    const int np = k >> 6;
+    const int npl16 = (np + 15) / 16 * 16;
+    const int stride = XS > 0 ? XS : npl16;
+    stage_x(x, k >> 5, npl16, stride, xs);
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int64_t rb = (int64_t)np * kPairBytes;
+    const int64_t nwaves = (int64_t)gridDim.x * kRowWaves;
+    for (int64_t row = (int64_t)blockIdx.x * kRowWaves + (threadIdx.x >> 6); row < n; row += nwaves) {
+        const uint8_t* wr = w + row * rb;
+        float a = 0.0f;
+        for (int p0 = lane; p0 < np; p0 += 128) {
+            uint32_t D[2][1][9];
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                if (p0 + 64 * u < np) load_pair(wr + (int64_t)(p0 + 64 * u) * kPairBytes, D[u][0]);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int p = p0 + 64 * u;
+                if (p < np) {
+                    float s0[1], s1[1];
+                    block_sums<1>(D[u], xs + p, stride, s0, s1);
+                    a = pair_acc(a, f16_lo(D[u][0][0]), s0[0], f16_hi(D[u][0][4]), s1[0]);
+                }
+            }
+        }
+        const float b = a + __shfl_xor(a, 32, 64);
+        const float e = row16_sum(b + __shfl_xor(b, 16, 64));
+        if (lane == 0) {
+            if (H16)
+                reinterpret_cast<uint16_t*>(y)[row] = (uint16_t)half_bits(residual ? e + residual[row] : e);
+            else
+                y[row] = e;
+        }
+    }
+}
+
 // The fields of a GEMV the sweep kernel keeps in scalar registers.
 struct Live {
     const uint8_t* w;
@@ -1480,8 +1535,29 @@ static const Shape& single_shape(int64_t n, int64_t k) {
     return quad ? kQuadNarrow : kNarrow;
 }
 
+// Single GEMVs the narrow engine shape would take run on the rows kernel
+// (measured per call, cold weights: 17408 x 5120 15.5 against 20.2 us,
+// 5120 x 17408 16.7 against 21.3, 5120 x 5120 8.6-9.5 against 9.6).
+static bool rows_single(int64_t n, int64_t k) { return &single_shape(n, k) == &kQuadNarrow || &single_shape(n, k) == &kNarrow; }
+
+template <bool H16>
+static hipError_t launch_rows(const uint8_t* w, const uint16_t* x, float* y, const float* residual, int64_t n,
+                              int64_t k, hipStream_t s) {
+    const int64_t wgs = (n + kRowWaves - 1) / kRowWaves;
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(wgs, 4 * (int64_t)device_cu_count()));
+    const size_t xsb = x_lds_bytes(k);
+    if (fixed_stride(k))
+        hipLaunchKernelGGL((k_gemv_rows<kXStride, H16>), dim3(grid), dim3(kRowWaves * 64), xsb, s, w, x, y, residual,
+                           n, (int)k);
+    else
+        hipLaunchKernelGGL((k_gemv_rows<0, H16>), dim3(grid), dim3(kRowWaves * 64), xsb, s, w, x, y, residual, n,
+                           (int)k);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemv(const uint8_t* w, const uint16_t* x, float* y, int64_t n, int64_t k,
                        hipStream_t s) {
+    if (rows_single(n, k)) return launch_rows<false>(w, x, y, nullptr, n, k, s);
     const Shape& sh = single_shape(n, k);
     const PlanDesc d = single_desc(w, x, y, n, k, sh);
     return launch_any<false, false>(sh, nullptr, 1, nullptr, nullptr, d, k, static_grid(d.steps, sh, INT32_MAX),
@@ -1550,6 +1626,7 @@ hipError_t launch_lm_head_norm(const uint8_t* w, const uint16_t* h, const uint16
 
 hipError_t launch_gemv_handoff(const uint8_t* w, const uint16_t* x, const float* residual, uint16_t* h16,
                                int64_t n, int64_t k, hipStream_t s) {
+    if (rows_single(n, k)) return launch_rows<true>(w, x, reinterpret_cast<float*>(h16), residual, n, k, s);
     const Shape& sh = single_shape(n, k);
     const PlanDesc d = single_desc(w, x, reinterpret_cast<float*>(h16), n, k, sh);
     return launch_any<false, false, false, true>(sh, nullptr, 1, nullptr, nullptr, d, k,
