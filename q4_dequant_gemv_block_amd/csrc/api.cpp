@@ -522,7 +522,7 @@ q4_status q4_0_gemv_batch_plan(const q4_gemv_desc* descs, int count, void* plan_
 q4_status q4_0_gemv_batch(const q4_gemv_plan* plan, void* stream) {
     if (!plan || !plan->device) return fail(Q4_ERR_INVALID_ARG, "q4_0_gemv_batch: null plan");
     if (plan->count < 1 || plan->max_k < 64 || plan->max_k > q4::kFastMaxK || plan->grid < 1 ||
-        plan->nchunks < plan->grid || (plan->flags & ~q4::kPlanQuad) != 0)
+        plan->nchunks < plan->grid || (plan->flags & ~(q4::kPlanQuad | q4::kPlanWide8)) != 0)
         return fail(Q4_ERR_INVALID_ARG, "q4_0_gemv_batch: plan was not filled by q4_0_gemv_batch_plan");
     const hipError_t e = q4::launch_gemv_batch(plan->device, plan->count, plan->nchunks, plan->grid, plan->max_k,
                                                plan->flags, static_cast<hipStream_t>(stream));
@@ -534,7 +534,7 @@ q4_status q4_0_gemv_batch_handoff(const q4_gemv_plan* plan, const float* y, cons
     const char* fn = "q4_0_gemv_batch_handoff";
     if (!plan || !plan->device) return fail(Q4_ERR_INVALID_ARG, "%s: null plan", fn);
     if (plan->count < 1 || plan->max_k < 64 || plan->max_k > q4::kFastMaxK || plan->grid < 1 ||
-        plan->nchunks < plan->grid || (plan->flags & ~q4::kPlanQuad) != 0)
+        plan->nchunks < plan->grid || (plan->flags & ~(q4::kPlanQuad | q4::kPlanWide8)) != 0)
         return fail(Q4_ERR_INVALID_ARG, "%s: plan was not filled by q4_0_gemv_batch_plan", fn);
     if (!y || !h16) return fail(Q4_ERR_INVALID_ARG, "%s: null y or h16", fn);
     if (!aligned(h16, 2)) return fail(Q4_ERR_MISALIGNED, "%s: h16 must be 2-byte aligned", fn);

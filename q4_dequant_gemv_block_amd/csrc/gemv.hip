@@ -103,6 +103,10 @@ constexpr Shape kNarrow = {4, 1, 2, false};
 #endif
 constexpr Shape kQuadWide = {Q4_QUAD_WAVES, Q4_QUAD_R, 1, true};
 constexpr Shape kQuadNarrow = {4, 1, 2, true};
+// Wide shapes with 8 waves, for lists and GEMVs whose staged activations (k
+// above 24,576) leave too little LDS for the rings of 12 waves.
+constexpr Shape kWide8 = {8, Q4_SWEEP_R, 1, false};
+constexpr Shape kQuadWide8 = {8, Q4_QUAD_R, 1, true};
 constexpr int kXStride = 288;  // activation chunk stride in pairs: k <= 18432 (36 KiB of LDS)
 
 
@@ -1448,6 +1452,16 @@ static size_t x_lds_bytes(int64_t max_k) {
     return (size_t)pairs * kChunksPerPair * sizeof(u4);
 }
 
+// The wide shape for activations of up to max_k columns: 12 waves when their
+// rings fit beside the staged activations in LDS, else 8.
+static const Shape& wide_shape(bool quad, int64_t max_k) {
+    const size_t ring = quad ? (size_t)QuadEngine<kQuadWide.waves, kQuadWide.r, kQuadNB, 0>::kWaveLds
+                             : (size_t)DmaEngine<kWide.waves, kWide.r, 0>::kWaveLds;
+    const Shape& w = quad ? kQuadWide : kWide;
+    if (x_lds_bytes(max_k) + (size_t)w.waves * ring + 1024 <= 160 * 1024) return w;
+    return quad ? kQuadWide8 : kWide8;
+}
+
 static PlanDesc single_desc(const uint8_t* w, const uint16_t* x, float* y, int64_t n, int64_t k, const Shape& sh) {
     PlanDesc d;
     d.w = w;
@@ -1510,6 +1524,12 @@ static hipError_t launch_any(const Shape& sh, const PlanDesc* descs, int count, 
             return launch_stride<DmaEngine<WN, kNarrow.r, kXStride>, DmaEngine<WN, kNarrow.r, 0>, BATCH, AM, NORM, H16>(
                 descs, count, head, chunks, one, max_k, grid, keys, nrm, s);
     }
+    if (sh.waves == kQuadWide8.waves && sh.quad)  // k above 24,576: the unfixed stride only
+        return launch_sweep<QuadEngine<kQuadWide8.waves, kQuadWide8.r, kQuadNB, 0>, 0, BATCH, AM, NORM, H16>(
+            descs, count, head, chunks, one, max_k, grid, keys, nrm, s);
+    if (sh.waves == kWide8.waves)
+        return launch_sweep<DmaEngine<kWide8.waves, kWide8.r, 0>, 0, BATCH, AM, NORM, H16>(
+            descs, count, head, chunks, one, max_k, grid, keys, nrm, s);
     if (sh.quad)
         return launch_stride<QuadEngine<kQuadWide.waves, kQuadWide.r, kQuadNB, kXStride>,
                              QuadEngine<kQuadWide.waves, kQuadWide.r, kQuadNB, 0>,
@@ -1529,7 +1549,7 @@ static int static_grid(int64_t steps, const Shape& sh, int cap) {
 // workgroups of work, else the narrow one.
 static const Shape& single_shape(int64_t n, int64_t k) {
     const bool quad = quad_ok(k);
-    const Shape& wide = quad ? kQuadWide : kWide;
+    const Shape& wide = wide_shape(quad, k);
     const int64_t wide_steps = (n + wide.rows_per_step() - 1) / wide.rows_per_step();
     if (wide_steps >= 2 * (int64_t)device_cu_count()) return wide;
     return quad ? kQuadNarrow : kNarrow;
@@ -1721,10 +1741,14 @@ static int schedule_list(PlanDesc* descs, int count, int rows_per_step, int wg_p
 
 void build_schedule(PlanDesc* descs, int count, std::vector<SchedChunk>* out, int* grid_out, int* flags_out) {
     bool quad = true;
-    for (int i = 0; i < count; ++i) quad = quad && quad_ok(descs[i].k);
-    const Shape& sh = quad ? kQuadWide : kWide;
+    int64_t max_k = 0;
+    for (int i = 0; i < count; ++i) {
+        quad = quad && quad_ok(descs[i].k);
+        max_k = std::max<int64_t>(max_k, descs[i].k);
+    }
+    const Shape& sh = wide_shape(quad, max_k);
     *grid_out = schedule_list(descs, count, sh.rows_per_step(), sh.wg_per_cu, npl_of, out);
-    *flags_out = quad ? kPlanQuad : 0;
+    *flags_out = (quad ? kPlanQuad : 0) | (sh.waves == kWide8.waves ? kPlanWide8 : 0);
 }
 
 hipError_t launch_gemv_batch(const void* plan, int count, int nchunks, int grid, int max_k, int flags,
@@ -1735,7 +1759,9 @@ hipError_t launch_gemv_batch(const void* plan, int count, int nchunks, int grid,
     const PlanDesc* descs = (const PlanDesc*)(base + sizeof(SchedHead));
     const SchedChunk* chunks = (const SchedChunk*)(base + sizeof(SchedHead) + (size_t)count * sizeof(PlanDesc));
     PlanDesc none = {};
-    return launch_any<true, false>((flags & kPlanQuad) ? kQuadWide : kWide, descs, count, head, chunks, none, max_k,
+    const Shape& sh = (flags & kPlanWide8) ? ((flags & kPlanQuad) ? kQuadWide8 : kWide8)
+                                           : ((flags & kPlanQuad) ? kQuadWide : kWide);
+    return launch_any<true, false>(sh, descs, count, head, chunks, none, max_k,
                                    grid, nullptr, s);
 }
 

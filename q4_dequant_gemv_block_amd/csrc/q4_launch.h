@@ -44,8 +44,11 @@ struct SchedChunk {
     int64_t c_end;
 };
 
-// Plan flag: the list runs on the quad engine (every k a multiple of 1024, at least 4096).
+// Plan flags: the list runs on the quad engine (every k a multiple of 1024, at
+// least 4096); the list runs with 8-wave workgroups (its largest k leaves too
+// little LDS for 12 waves' rings).
 constexpr int kPlanQuad = 1;
+constexpr int kPlanWide8 = 2;
 
 // Orders descs[0..count) by row-step size (largest first, stable), fills
 // npl, steps and cost_begin and cuts the list into

@@ -16,7 +16,9 @@ SEED = synth.DEFAULT_SEED
 
 def test_mixed_list_matches_single_gemv_and_oracle():
     q4 = lib()
-    shapes = [(5, 64), (100, 5120), (33, 1088), (1, 17408), (257, 2048), (64, 1024), (31, 17408), (2000, 320)]
+    # single calls of these run on the rows kernel; (40, 32768) and (70, 20544) stage x past the fixed stride
+    shapes = [(5, 64), (100, 5120), (33, 1088), (1, 17408), (257, 2048), (64, 1024), (31, 17408), (2000, 320),
+              (40, 32768), (70, 20544)]
     items, host = [], []
     for i, (n, k) in enumerate(shapes):
         w = synth.q4_0(SEED, 5000 + i, n, k)
@@ -204,3 +206,38 @@ def test_batch_handoff_refuses_an_h16_over_the_plan():
     torch.cuda.synchronize()
     for a, b in zip(ys, want):
         assert torch.equal(a, b)
+
+
+def test_widest_k_runs_on_eight_wave_workgroups():
+    """k above 24,576 stages more activations than leave room for 12 waves'
+    rings: a quad-engine list (k % 1024 == 0) and a wide single call run with
+    8-wave workgroups.  Every output equals the single call's (rows kernel for
+    the slices) bit for bit and lies within the bound on sampled rows."""
+    q4 = lib()
+    shapes = [(300, 32768), (100, 28672), (2, 25600)]
+    items, host = [], []
+    for i, (n, k) in enumerate(shapes):
+        w = synth.q4_0(SEED, 7600 + i, n, k)
+        x = synth.f16_normal(SEED, 7700 + i, k)
+        host.append((w, x))
+        items.append((dev_u8(w), dev_f16(x), torch.full((n,), float("nan"), device=device())))
+    batch = q4.GemvBatch(items)
+    assert batch.plan.flags == 3  # quad engine, 8-wave workgroups
+    batch()
+    torch.cuda.synchronize()
+    for (w, x), (wd, xd, yd), (n, k) in zip(host, items, shapes):
+        assert torch.equal(yd, q4.q4_0_gemv(wd, xd)), (n, k)
+        y_ref, a_ref = oracle.gemm_rows(w, k, x)
+        assert_parity(yd.cpu().numpy(), y_ref, a_ref, "8-wave list %dx%d" % (n, k))
+    # a single call wide enough for the wide shape: 40,000 rows x 32,768 (737 MB)
+    n, k = 40000, 32768
+    w = synth.q4_0(SEED, 7800, n, k)
+    x = synth.f16_normal(SEED, 7801, k)
+    wd, xd = dev_u8(w), dev_f16(x)
+    say("wide single 40000 x 32768")
+    y = q4.q4_0_gemv(wd, xd)
+    for lo, hi in [(0, 64), (39936, 40000), (20011, 20100)]:
+        assert torch.equal(y[lo:hi], q4.q4_0_gemv(wd[lo:hi], xd)), (lo, hi)
+    rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(3).integers(0, n, 254)]))
+    y_ref, a_ref = oracle.gemm_rows(np.ascontiguousarray(w[rows]), k, x)
+    assert_parity(y[rows].cpu().numpy(), y_ref, a_ref, "wide single k = 32768")

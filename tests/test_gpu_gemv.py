@@ -43,7 +43,8 @@ def test_golden_blocks_on_fast_path():
 
 
 SHAPES = [(1, 64), (5, 64), (17, 128), (33, 1088), (64, 1024), (100, 5184), (257, 2048),
-          (31, 17408), (1000, 320), (7, 96), (3, 32), (40, 5120 + 32)]
+          (31, 17408), (1000, 320), (7, 96), (3, 32), (40, 5120 + 32),
+          (64, 32768), (333, 20544)]  # activations past the fixed LDS stride (k > 18,432)
 
 
 @pytest.mark.parametrize("n,k", SHAPES, ids=["%dx%d" % s for s in SHAPES])
