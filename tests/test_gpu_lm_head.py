@@ -80,3 +80,31 @@ def test_full_lm_head():
     blk[:, 1] = (d >> 8).astype(np.uint8)
     l4, t4 = run(w4, h)
     assert t4 == 17 and l4[17] == 2 * logits[g]
+
+
+def test_widest_k_on_eight_wave_workgroups():
+    """k = 32,768 with a vocabulary wide enough for the wide shape: the LM head
+    (and its final-norm form) runs with 8-wave workgroups.  The logits equal
+    q4_0_gemv's bit for bit, the token is their lowest-index maximum, and
+    sampled rows lie within the bound."""
+    q4 = lib()
+    n, k = 33000, 32768
+    w = synth.q4_0(SEED, 7900, n, k)
+    h = synth.f16_normal(SEED, 7901, k)
+    wd, hd = dev_u8(w), dev_f16(h)
+    logits, token = q4.lm_head_argmax(wd, hd)
+    y = q4.q4_0_gemv(wd, hd)
+    torch.cuda.synchronize()
+    assert torch.equal(logits, y)
+    lg = logits.cpu().numpy()
+    assert int(token.cpu().numpy()[0]) == int(np.argmax(lg))
+    rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(4).integers(0, n, 126)]))
+    y_ref, a_ref = oracle.gemm_rows(np.ascontiguousarray(w[rows]), k, h)
+    assert_parity(lg[rows], y_ref, a_ref, "LM head k = 32768")
+    # the final norm form: its x_out through the plain LM head gives the same logits and token
+    g = dev_f16(synth.norm_gain(SEED, 7902, k))
+    x_out = torch.empty(k, dtype=torch.float16, device="cuda")
+    logits_n, token_n = q4.lm_head_norm_argmax(wd, hd, g, 1e-6, x_out=x_out)
+    logits_p, token_p = q4.lm_head_argmax(wd, x_out)
+    torch.cuda.synchronize()
+    assert torch.equal(logits_n, logits_p) and int(token_n.item()) == int(token_p.item())
