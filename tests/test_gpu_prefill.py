@@ -11,7 +11,8 @@ from gpu_util import assert_parity, dev_f16, dev_u8, lib, say
 pytestmark = pytest.mark.gpu
 SEED = synth.DEFAULT_SEED
 
-CASES = [(1, 64, 64), (17, 100, 1024), (33, 257, 2048), (64, 128, 5120), (5, 31, 96), (169, 200, 1088)]
+CASES = [(1, 64, 64), (17, 100, 1024), (33, 257, 2048), (64, 128, 5120), (5, 31, 96), (169, 200, 1088),
+         (37, 100, 32768), (70, 90, 20544)]  # the largest k on both kernels (k % 256 == 0 and not)
 
 
 @pytest.mark.parametrize("m,n,k", CASES, ids=["%dx%dx%d" % c for c in CASES])

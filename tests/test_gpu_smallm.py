@@ -13,7 +13,7 @@ from gpu_util import assert_parity, dev_f16, dev_u8, lib, say
 pytestmark = pytest.mark.gpu
 SEED = synth.DEFAULT_SEED
 
-SHAPES = [(1, 64), (37, 128), (100, 5120), (64, 1088), (31, 17408), (7, 96), (513, 2048)]
+SHAPES = [(1, 64), (37, 128), (100, 5120), (64, 1088), (31, 17408), (7, 96), (513, 2048), (50, 32768)]
 
 
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 7, 8, 16])
