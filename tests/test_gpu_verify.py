@@ -32,7 +32,8 @@ def check_tokens(logits, tokens, y_ref, a_ref):
             assert y_ref[i, r] - y_ref[i, tokens[i]] < TOL * max(a_ref[i, r], a_ref[i, tokens[i]]), (i, tokens[i], r)
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 3001, 1024), (2, 4099, 1024), (5, 257, 2048), (16, 3000, 5120), (16, 70, 64)])
+@pytest.mark.parametrize("m,n,k", [(1, 3001, 1024), (2, 4099, 1024), (5, 257, 2048), (16, 3000, 5120), (16, 70, 64),
+                                   (4, 1500, 32768), (1, 700, 32768)])  # k split into ranges; M = 1 at the largest k
 def test_verify_parity_and_prefix(m, n, k):
     w = synth.q4_0(SEED, 7100 + m, n, k)
     h = synth.f16_normal(SEED, 7200 + m * 7 + k, m * k).reshape(m, k)
