@@ -107,6 +107,9 @@ constexpr Shape kQuadNarrow = {4, 1, 2, true};
 // above 24,576) leave too little LDS for the rings of 12 waves.
 constexpr Shape kWide8 = {8, Q4_SWEEP_R, 1, false};
 constexpr Shape kQuadWide8 = {8, Q4_QUAD_R, 1, true};
+// The quad engine with 11 waves, for single wide GEMVs whose 8-row groups
+// spread more evenly over 11 waves per workgroup than over 12.
+constexpr Shape kQuadWide11 = {11, Q4_QUAD_R, 1, true};
 constexpr int kXStride = 288;  // activation chunk stride in pairs: k <= 18432 (36 KiB of LDS)
 
 
@@ -1524,6 +1527,12 @@ static hipError_t launch_any(const Shape& sh, const PlanDesc* descs, int count, 
             return launch_stride<DmaEngine<WN, kNarrow.r, kXStride>, DmaEngine<WN, kNarrow.r, 0>, BATCH, AM, NORM, H16>(
                 descs, count, head, chunks, one, max_k, grid, keys, nrm, s);
     }
+    if constexpr (!BATCH) {
+        if (sh.waves == kQuadWide11.waves && sh.quad)
+            return launch_stride<QuadEngine<kQuadWide11.waves, kQuadWide11.r, kQuadNB, kXStride>,
+                                 QuadEngine<kQuadWide11.waves, kQuadWide11.r, kQuadNB, 0>, BATCH, AM, NORM, H16>(
+                descs, count, head, chunks, one, max_k, grid, keys, nrm, s);
+    }
     if (sh.waves == kQuadWide8.waves && sh.quad)  // k above 24,576: the unfixed stride only
         return launch_sweep<QuadEngine<kQuadWide8.waves, kQuadWide8.r, kQuadNB, 0>, 0, BATCH, AM, NORM, H16>(
             descs, count, head, chunks, one, max_k, grid, keys, nrm, s);
@@ -1550,12 +1559,29 @@ static int static_grid(int64_t steps, const Shape& sh, int cap) {
 // against 20.3 on the rows kernel, 45,000 x 5,120 28.1 against 31.9; at half
 // that, 12,288 rows, 13.7 against 11.6), else the narrow one (which single
 // calls replace by the rows kernel).
+// The longest wave's share of a single wide GEMV's 8-row groups over the
+// average: workgroup g of G takes groups [groups g / G, groups (g + 1) / G)
+// and its waves the groups of each row step in turn, so the launch lasts as
+// long as the waves with the most groups.
+static double wave_imbalance(int64_t n, const Shape& sh) {
+    const int64_t steps = (n + sh.rows_per_step() - 1) / sh.rows_per_step();
+    const int64_t G = std::max<int64_t>(1, std::min<int64_t>(steps, device_cu_count()));
+    const int64_t groups = (n + 4 * sh.r - 1) / (4 * sh.r);
+    const int64_t most = ((groups + G - 1) / G + sh.waves - 1) / sh.waves;
+    return (double)most * (double)(G * sh.waves) / (double)groups;
+}
+
 static const Shape& single_shape(int64_t n, int64_t k) {
     const bool quad = quad_ok(k);
     const Shape& wide = wide_shape(quad, k);
     const int64_t wide_steps = (n + wide.rows_per_step() - 1) / wide.rows_per_step();
-    if (wide_steps >= (int64_t)device_cu_count()) return wide;
-    return quad ? kQuadNarrow : kNarrow;
+    if (wide_steps < (int64_t)device_cu_count()) return quad ? kQuadNarrow : kNarrow;
+    // 11 waves when that spreads the groups clearly more evenly (the LM head,
+    // 151,936 rows: the busiest wave 1.13 x the average with 12 waves, 1.04
+    // with 11; measured 78.6-79.2 against 75.3-75.6 us per call)
+    if (&wide == &kQuadWide && wave_imbalance(n, kQuadWide11) < wave_imbalance(n, kQuadWide) - 0.03)
+        return kQuadWide11;
+    return wide;
 }
 
 // Single GEMVs the narrow engine shape would take run on the rows kernel
