@@ -81,11 +81,15 @@ __device__ __forceinline__ u4 expand8(const uint32_t (&P)[4], h2 s) {
     const uint32_t mask = HI ? 0x00F000F0u : 0x000F000Fu;
     const uint32_t bias = HI ? 0x54005400u : 0x64006400u;
     const h2 off = HI ? h2{(_Float16)72.0f, (_Float16)72.0f} : h2{(_Float16)1032.0f, (_Float16)1032.0f};
+    // in stages, so that no instruction reads the result of the one before it
+    const uint32_t t0 = and_or(P[0], mask, bias), t1 = and_or(P[1], mask, bias);
+    const uint32_t t2 = and_or(P[2], mask, bias), t3 = and_or(P[3], mask, bias);
+    const h2 q0 = as_h2(t0) - off, q1 = as_h2(t1) - off, q2 = as_h2(t2) - off, q3 = as_h2(t3) - off;
     u4 r;
-    r.x = as_u32((as_h2(and_or(P[0], mask, bias)) - off) * s);
-    r.y = as_u32((as_h2(and_or(P[1], mask, bias)) - off) * s);
-    r.z = as_u32((as_h2(and_or(P[2], mask, bias)) - off) * s);
-    r.w = as_u32((as_h2(and_or(P[3], mask, bias)) - off) * s);
+    r.x = as_u32(q0 * s);
+    r.y = as_u32(q1 * s);
+    r.z = as_u32(q2 * s);
+    r.w = as_u32(q3 * s);
     return r;
 }
 
