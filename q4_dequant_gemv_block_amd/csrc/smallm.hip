@@ -62,6 +62,7 @@
 #include "q4_launch.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace q4 {
 
@@ -223,21 +224,34 @@ __device__ void stage_range(const SmDesc& D, int c, int m, u4* __restrict__ xs) 
             for (int i = 0; i < 16; ++i) v[i] = 0u;
         }
         auto xe = [&](int j) -> uint32_t { return (v[j >> 1] >> (16 * (j & 1))) & 0xFFFFu; };
-        const int half = b & 1;
+        // The block half as a compile-time constant, so that every position
+        // below is one too (with a run-time half each half-word extraction
+        // was a select over the 16 registers: twice the kernel's code).
+        auto put = [&](auto H) {
+            constexpr int half = decltype(H)::value;
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-            int pos[4];
-            chunk_positions(4 * half + cc, pos);
-            const int off = 32 * half;
-            const int a = pos[0] - off, bb = pos[1] - off, cq = pos[2] - off, e = pos[3] - off;
-            u4 ent;
-            ent.x = xe(a) | (xe(cq) << 16);
-            ent.y = xe(a + 16) | (xe(cq + 16) << 16);
-            ent.z = xe(bb) | (xe(e) << 16);
-            ent.w = xe(bb + 16) | (xe(e + 16) << 16);
-            xs[mm * x_stride<SWZ>(D) + x_slot<SWZ>(mm, b >> 1, 4 * half + cc)] = ent;
-        }
+            for (int cc = 0; cc < 4; ++cc) {
+                int pos[4];
+                chunk_positions(4 * half + cc, pos);
+                const int off = 32 * half;
+                const int a = pos[0] - off, bb = pos[1] - off, cq = pos[2] - off, e = pos[3] - off;
+                u4 ent;
+                ent.x = xe(a) | (xe(cq) << 16);
+                ent.y = xe(a + 16) | (xe(cq + 16) << 16);
+                ent.z = xe(bb) | (xe(e) << 16);
+                ent.w = xe(bb + 16) | (xe(e + 16) << 16);
+                xs[mm * x_stride<SWZ>(D) + x_slot<SWZ>(mm, b >> 1, 4 * half + cc)] = ent;
+            }
+        };
+        if (b & 1)
+            put(std::integral_constant<int, 1>{});
+        else
+            put(std::integral_constant<int, 0>{});
     }
+    // Every staging load has been consumed, but on the path that skips both
+    // halves the compiler would keep one pending into the GEMM loop and wait
+    // there for every outstanding load, the ring's included, at each unit.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 }
 
 // The LDS-ring engine (M <= kLdsMaxM).
