@@ -646,6 +646,11 @@ __global__ void __launch_bounds__(Geo<0>::kWaves * 64) k_smallm_reg(const SmDesc
         }
     };
 
+    // The other buffer's loads are issued before each unit is computed, also
+    // when no unit is left (they then re-read clamped in-range addresses and
+    // go unused): with a conditional issue the compiler's wait after the
+    // join of the two paths covered the other buffer's loads as well, and a
+    // wave then computed each unit with nothing in flight.
     SmBuf A, B;
     Rec ra, rb;
     ra = Rec{cl.d, cl.c, cl.t, cl.jb};
@@ -653,19 +658,15 @@ __global__ void __launch_bounds__(Geo<0>::kWaves * 64) k_smallm_reg(const SmDesc
     advance_l();
     for (;;) {
         bool more = have_l;
-        if (more) {
-            rb = Rec{cl.d, cl.c, cl.t, cl.jb};
-            issue(B);
-            advance_l();
-        }
+        rb = Rec{cl.d, cl.c, cl.t, cl.jb};
+        issue(B);
+        if (more) advance_l();
         process(ra, A);
         if (!more) break;
         more = have_l;
-        if (more) {
-            ra = Rec{cl.d, cl.c, cl.t, cl.jb};
-            issue(A);
-            advance_l();
-        }
+        ra = Rec{cl.d, cl.c, cl.t, cl.jb};
+        issue(A);
+        if (more) advance_l();
         process(rb, B);
         if (!more) break;
     }
