@@ -446,7 +446,7 @@ def bench_lmhead(args):
             "data": "synthetic", "config": {"workload": "LM head 151936x5120 + argmax"},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counter_traffic("lmhead"),
-                         "kernel": "q4::k_sweep<QuadEngine<12,2,2,288>,ARGMAX> + q4::k_argmax_final"}}
+                         "kernel": "q4::k_sweep<QuadEngine<11,2,2,288>,ARGMAX> + q4::k_argmax_final"}}
 
 
 NORM_EPS = 1e-6
@@ -497,7 +497,7 @@ def bench_lmhead_norm(args):
             "norm_overhead_us": round((ms - plain_ms) * 1000.0, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": counter_traffic("lmhead_norm"),
-                         "kernel": "q4::k_sweep<QuadEngine<12,2,2,288>,ARGMAX,NORM> + q4::k_argmax_final"}}
+                         "kernel": "q4::k_sweep<QuadEngine<11,2,2,288>,ARGMAX,NORM> + q4::k_argmax_final"}}
 
 
 def bench_verify(args):
