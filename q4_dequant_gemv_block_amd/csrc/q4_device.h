@@ -16,15 +16,21 @@
 //
 // A code dword V with bytes (codes a, b, c, e in the low nibbles and a+16,
 // b+16, c+16, e+16 in the high nibbles) expands to four f16 pairs with exact
-// values code - 8:
-//   (a, c)        : (V      & 0x000F000F) | 0x6400 6400 -> 1024 + q, minus 1032
-//   (a+16, c+16)  : (V      & 0x00F000F0) | 0x5400 5400 -> 64 + q,   minus 72
-//   (b, e)        : (V >> 8 & 0x000F000F) | 0x6400 6400
-//   (b+16, e+16)  : (V >> 8 & 0x00F000F0) | 0x5400 5400
-// (0x6400 is 1024.0 with unit spacing, 0x5400 is 64.0 with spacing 1/16, so a
-// nibble OR-ed into bits 0-3 or 4-7 adds exactly q).  Each pair then meets the
-// matching pair of activations in one v_dot2 (f16 x f16 products are exact in
-// f32; sums round in f32), and the block sum is scaled once by d.
+// values code - 8, in eight operations and no shift:
+//   L02 = (V & 0x00FF00FF) | 0x6400 6400       -> 1024 + byte, bytes 0 and 2
+//   L13 = byte permute [V.1, 0x64, V.3, 0x64]  -> 1024 + byte, bytes 1 and 3
+//   H   = (L & 0x00F000F0) | 0x5408 5408       -> 64.5 + high nibble
+//   low  - 8 = L - 16 H   (one packed f16 fma)
+//   high - 8 = H - 72.5   (one packed f16 add)
+// (0x6400 is 1024.0 with unit spacing, so a byte under it adds exactly its
+// value; 0x5400 is 64.0 with spacing 1/16, so a nibble in bits 4-7 adds
+// exactly its value and bit 3 adds 0.5.  Every intermediate is a multiple of
+// 1/2 below 2048 in magnitude and every result an integer in [-8, 7], all
+// exact in f16.)  The pairs come out as
+//   (a, c), (a+16, c+16), (b, e), (b+16, e+16).
+// Each pair then meets the matching pair of activations in one v_dot2 (f16 x
+// f16 products are exact in f32; sums round in f32), and the block sum is
+// scaled once by d.
 //
 // The activations are therefore stored, per code dword, as the four f16
 // pairs (x_a, x_c), (x_a+16, x_c+16), (x_b, x_e), (x_b+16, x_e+16): one 16-byte
@@ -71,14 +77,19 @@ struct Codes4 {
 };
 
 __device__ __forceinline__ Codes4 expand(uint32_t v) {
-    const uint32_t u = v >> 8;
-    const h2 c1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
-    const h2 c72 = {(_Float16)72.0f, (_Float16)72.0f};
+    const h2 m16 = {(_Float16)-16.0f, (_Float16)-16.0f};
+    const h2 c72h = {(_Float16)72.5f, (_Float16)72.5f};
+    // the four bit-level steps first, then the four packed f16 steps: a packed
+    // read right after the VALU write of its operand costs a wait state
+    const uint32_t l02 = and_or(v, 0x00FF00FFu, 0x64006400u);
+    const uint32_t l13 = __builtin_amdgcn_perm(0x64646464u, v, 0x04030401u);
+    const uint32_t h02 = and_or(v, 0x00F000F0u, 0x54085408u);
+    const uint32_t h13 = and_or(l13, 0x00F000F0u, 0x54085408u);
     Codes4 r;
-    r.q0 = as_h2(and_or(v, 0x000F000Fu, 0x64006400u)) - c1032;
-    r.q1 = as_h2(and_or(v, 0x00F000F0u, 0x54005400u)) - c72;
-    r.q2 = as_h2(and_or(u, 0x000F000Fu, 0x64006400u)) - c1032;
-    r.q3 = as_h2(and_or(u, 0x00F000F0u, 0x54005400u)) - c72;
+    r.q0 = __builtin_elementwise_fma(as_h2(h02), m16, as_h2(l02));
+    r.q2 = __builtin_elementwise_fma(as_h2(h13), m16, as_h2(l13));
+    r.q1 = as_h2(h02) - c72h;
+    r.q3 = as_h2(h13) - c72h;
     return r;
 }
 
