@@ -309,24 +309,24 @@ template <int R>
 __device__ __forceinline__ void block_sums(const uint32_t (&D)[R][9], const u4* __restrict__ xb, int stride,
                                            float (&s0)[R], float (&s1)[R]) {
 #pragma unroll
-    for (int i = 0; i < R; ++i) s0[i] = s1[i] = 0.0f;
-#pragma unroll
     for (int ch = 0; ch < 8; ++ch) {
         const u4 X = xb[ch * stride];
 #pragma unroll
         for (int i = 0; i < R; ++i) {
             const uint32_t code = ch == 0 ? realign_block0(D[i][0], D[i][4]) : D[i][ch < 4 ? ch : ch + 1];
             if (ch < 4)
-                s0[i] = dot_chunk(expand(code), X, s0[i]);
+                s0[i] = dot_chunk(expand(code), X, ch == 0 ? 0.0f : s0[i]);
             else
-                s1[i] = dot_chunk(expand(code), X, s1[i]);
+                s1[i] = dot_chunk(expand(code), X, ch == 4 ? 0.0f : s1[i]);
         }
     }
 }
 
-// One pair into a row accumulator: a = d1 * s1 + (d0 * s0 + a), two roundings.
-__device__ __forceinline__ float pair_acc(float a, float d0, float s0, float d1, float s1) {
-    return __builtin_fmaf(d1, s1, __builtin_fmaf(d0, s0, a));
+// One pair into a row accumulator: a = d1 * s1 + (d0 * s0 + a), two roundings,
+// with d0 the f16 in the low half of w0 (the pair's first dword) and d1 the
+// f16 in the high half of w4 (its fifth).
+__device__ __forceinline__ float pair_acc(float a, uint32_t w0, float s0, uint32_t w4, float s1) {
+    return fma_hi(w4, s1, fma_lo(w0, s0, a));
 }
 
 // Row sums in a fixed association that both engines share.  Pair p of a row
@@ -563,15 +563,9 @@ struct DmaEngine {
         const int stride = XS > 0 ? XS : Dp.npl * 16;
         float s0[R], s1[R];
         block_sums<R>(W.d, xs + (l16 + 16 * jb), stride, s0, s1);
-        float d0[R], d1[R];
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-            d0[i] = f16_lo(W.d[i][0]);
-            d1[i] = f16_hi(W.d[i][4]);
-        }
         auto add = [&](float(&a)[R]) {
 #pragma unroll
-            for (int i = 0; i < R; ++i) a[i] = pair_acc(a[i], d0[i], s0[i], d1[i], s1[i]);
+            for (int i = 0; i < R; ++i) a[i] = pair_acc(a[i], W.d[i][0], s0[i], W.d[i][4], s1[i]);
         };
         switch (jb & 3) {  // the pairs' class (uniform)
             case 0: add(acc.c0); break;
@@ -733,7 +727,7 @@ struct QuadEngine {
         // one row: A = pair_acc(A, ...) in place, the f16 scales read as they are
         auto one = [&](float(&A)[R]) {
 #pragma unroll
-            for (int i = 0; i < R; ++i) A[i] = pair_acc(A[i], f16_lo(W.d[i][0]), s0[i], f16_hi(W.d[i][4]), s1[i]);
+            for (int i = 0; i < R; ++i) A[i] = pair_acc(A[i], W.d[i][0], s0[i], W.d[i][4], s1[i]);
         };
         // two rows: lanes < b into A, the others into B (a zero scale leaves
         // the other accumulator as it is)
@@ -742,8 +736,8 @@ struct QuadEngine {
             for (int i = 0; i < R; ++i) {
                 const uint32_t w0 = W.d[i][0], w4 = W.d[i][4];
                 const uint32_t z0 = w0 & 0xFFFF0000u, z4 = w4 & 0x0000FFFFu;  // scale zeroed
-                A[i] = pair_acc(A[i], f16_lo(next ? z0 : w0), s0[i], f16_hi(next ? z4 : w4), s1[i]);
-                B[i] = pair_acc(B[i], f16_lo(next ? w0 : z0), s0[i], f16_hi(next ? w4 : z4), s1[i]);
+                A[i] = pair_acc(A[i], next ? z0 : w0, s0[i], next ? z4 : w4, s1[i]);
+                B[i] = pair_acc(B[i], next ? w0 : z0, s0[i], next ? w4 : z4, s1[i]);
             }
         };
         if (b >= 64) {
@@ -851,7 +845,7 @@ __device__ __forceinline__ void q8_pair_sums(const uint32_t (&D)[17], const u4 (
 }
 // The pair into a row accumulator: a = d1 s1 + (d0 s0 + a).
 __device__ __forceinline__ float q8_pair_acc(const uint32_t (&D)[17], float s0, float s1, float a) {
-    return __builtin_fmaf(f16_hi(D[8]), s1, __builtin_fmaf(f16_lo(D[0]), s0, a));
+    return fma_hi(D[8], s1, fma_lo(D[0], s0, a));
 }
 
 // The last steps of a Q8_0 row sum: w holds, in each lane l, the row's
@@ -1052,7 +1046,7 @@ __global__ void __launch_bounds__(kRowWaves * 64) k_gemv_rows(const uint8_t* __r
                 if (p < np) {
                     float s0[1], s1[1];
                     block_sums<1>(D[u], xs + p, stride, s0, s1);
-                    a = pair_acc(a, f16_lo(D[u][0][0]), s0[0], f16_hi(D[u][0][4]), s1[0]);
+                    a = pair_acc(a, D[u][0][0], s0[0], D[u][0][4], s1[0]);
                 }
             }
         }

@@ -73,23 +73,37 @@ constexpr int kStepBytes = 64 * 2;  // one activation row of one step (64 halves
 
 typedef PfDesc PfArgs;
 
-// The four f16 pairs of natural-order weights from 8 code bytes (two dwords,
-// byte j = codes j (low nibble) and j + 16 (high nibble) of the block):
-// HI selects the high nibbles.  Exact (code - 8), then times the scale.
+// The four f16 pairs of natural-order weights from 8 code bytes, given as
+// four dwords [b, 0x64, b', 0x64] (spread below): as f16 halves they read
+// 1024 + b and 1024 + b', b = low nibble + 16 * high nibble.  The low
+// nibbles come first (HI = false): H = (P & 0x00F000F0) | 0x5408 5408 reads
+// 64.5 + high nibble (0x5400 is 64.0 with spacing 1/16; bit 3 adds 0.5), and
+// P - 16 H is exactly low nibble - 8 (one packed fma); H then replaces P.
+// The high nibbles (HI = true) are H - 72.5 = high nibble - 8.  Every
+// intermediate is exact in f16; the product with the scale rounds once.
 template <bool HI>
-__device__ __forceinline__ u4 expand8(const uint32_t (&P)[4], h2 s) {
-    const uint32_t mask = HI ? 0x00F000F0u : 0x000F000Fu;
-    const uint32_t bias = HI ? 0x54005400u : 0x64006400u;
-    const h2 off = HI ? h2{(_Float16)72.0f, (_Float16)72.0f} : h2{(_Float16)1032.0f, (_Float16)1032.0f};
-    // in stages, so that no instruction reads the result of the one before it
-    const uint32_t t0 = and_or(P[0], mask, bias), t1 = and_or(P[1], mask, bias);
-    const uint32_t t2 = and_or(P[2], mask, bias), t3 = and_or(P[3], mask, bias);
-    const h2 q0 = as_h2(t0) - off, q1 = as_h2(t1) - off, q2 = as_h2(t2) - off, q3 = as_h2(t3) - off;
+__device__ __forceinline__ u4 expand8(uint32_t (&P)[4], h2 s) {
+    uint32_t q[4];
+    if (HI) {
+        const h2 off = {(_Float16)72.5f, (_Float16)72.5f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = as_u32(as_h2(P[i]) - off);
+    } else {
+        const h2 m16 = {(_Float16)-16.0f, (_Float16)-16.0f};
+        // in stages, so that no instruction reads the result of the one before it
+        uint32_t h[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = and_or(P[i], 0x00F000F0u, 0x54085408u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = as_u32(__builtin_elementwise_fma(as_h2(h[i]), m16, as_h2(P[i])));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) P[i] = h[i];
+    }
     u4 r;
-    r.x = as_u32(q0 * s);
-    r.y = as_u32(q1 * s);
-    r.z = as_u32(q2 * s);
-    r.w = as_u32(q3 * s);
+    r.x = as_u32(as_h2(q[0]) * s);
+    r.y = as_u32(as_h2(q[1]) * s);
+    r.z = as_u32(as_h2(q[2]) * s);
+    r.w = as_u32(as_h2(q[3]) * s);
     return r;
 }
 
@@ -99,13 +113,14 @@ __device__ __forceinline__ u4 expand8(const uint32_t (&P)[4], h2 s) {
 // rows distinct (row parity, slot) pairs (no conflict with 64 banks).
 __device__ __forceinline__ int swz(int i) { return (i & 7) ^ ((i >> 3) & 1); }
 
-// Code bytes 8g .. 8g+7 of a block as four dwords [b, 0, b', 0] (consecutive
-// byte pairs spread to the two halves), from the block's code dwords E0, E1.
+// Code bytes 8g .. 8g+7 of a block as four dwords [b, 0x64, b', 0x64]
+// (consecutive byte pairs spread to the two halves under the exponent byte of
+// 1024.0), from the block's code dwords E0, E1.
 __device__ __forceinline__ void spread(uint32_t e0, uint32_t e1, uint32_t (&P)[4]) {
-    P[0] = __builtin_amdgcn_perm(e0, e0, 0x0C010C00u);
-    P[1] = __builtin_amdgcn_perm(e0, e0, 0x0C030C02u);
-    P[2] = __builtin_amdgcn_perm(e1, e1, 0x0C010C00u);
-    P[3] = __builtin_amdgcn_perm(e1, e1, 0x0C030C02u);
+    P[0] = __builtin_amdgcn_perm(0x64646464u, e0, 0x04010400u);
+    P[1] = __builtin_amdgcn_perm(0x64646464u, e0, 0x04030402u);
+    P[2] = __builtin_amdgcn_perm(0x64646464u, e1, 0x04010400u);
+    P[3] = __builtin_amdgcn_perm(0x64646464u, e1, 0x04030402u);
 }
 
 // Direct-to-LDS loads (lane i's bytes land at M0 + size * i) issued through
@@ -541,7 +556,7 @@ k_prefill_q(PfArgs one, const PfDesc* __restrict__ descs, int count, PfHead* hea
             sc[j] = h2{d, d};
         }
     };
-    auto expand = [&](auto HKc, const uint32_t (&P)[2][4], const h2 (&sc)[2], u4 (&bw)[2]) {
+    auto expand = [&](auto HKc, uint32_t (&P)[2][4], const h2 (&sc)[2], u4 (&bw)[2]) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) bw[j] = decltype(HKc)::value ? expand8<true>(P[j], sc[j]) : expand8<false>(P[j], sc[j]);
     };

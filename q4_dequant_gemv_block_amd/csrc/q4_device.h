@@ -101,6 +101,15 @@ __device__ __forceinline__ float dot_chunk(const Codes4& q, u4 x, float s) {
     return s;
 }
 
+// a + d * s with d the f16 in the low (fma_lo) or high (fma_hi) half of w, one
+// rounding (the f16 widens exactly).
+__device__ __forceinline__ float fma_lo(uint32_t w, float s, float a) {
+    return __builtin_fmaf((float)as_h2(w).x, s, a);
+}
+__device__ __forceinline__ float fma_hi(uint32_t w, float s, float a) {
+    return __builtin_fmaf((float)as_h2(w).y, s, a);
+}
+
 __device__ __forceinline__ float f16_lo(uint32_t v) { return (float)as_h2(v).x; }
 __device__ __forceinline__ float f16_hi(uint32_t v) { return (float)as_h2(v).y; }
 
