@@ -612,11 +612,14 @@ struct QuadEngine {
     struct Regs {
         uint32_t d[R][9];
     };
-    // Per quad, one accumulator per quad row, as separate variables: every
-    // index is a compile-time constant (a run-time row index would move the
-    // accumulators to memory).
+    // Per quad, the partial sums of the quad's four rows, as separate
+    // variables (every index a compile-time constant: a run-time row index
+    // would move them to memory).  The slabs add into cur (the row rc) and,
+    // in lanes past a row end, nxt (row rc + 1); when row rc is complete its
+    // sum moves to its named slot, once per row rather than once per slab.
     struct Acc {
         float a0[R], a1[R], a2[R], a3[R];
+        float cur[R], nxt[R];
         int rc;  // quad row of the slab's first pair (uniform)
         int nb;  // first pair of quad row rc + 1, from the quad start (uniform)
     };
@@ -646,7 +649,7 @@ struct QuadEngine {
     }
     __device__ __forceinline__ void init_acc(Acc& a) const {
 #pragma unroll
-        for (int i = 0; i < R; ++i) a.a0[i] = a.a1[i] = a.a2[i] = a.a3[i] = 0.0f;
+        for (int i = 0; i < R; ++i) a.a0[i] = a.a1[i] = a.a2[i] = a.a3[i] = a.cur[i] = a.nxt[i] = 0.0f;
         a.rc = 0;
         a.nb = 0;
     }
@@ -724,37 +727,33 @@ struct QuadEngine {
         const int stride = XS > 0 ? XS : Dp.npl * 16;
         float s0[R], s1[R];
         block_sums<R>(W.d, (const u4*)((const uint8_t*)xs + px), stride, s0, s1);
-        // one row: A = pair_acc(A, ...) in place, the f16 scales read as they are
-        auto one = [&](float(&A)[R]) {
+        if (b >= 64) {  // one row: cur = pair_acc(cur, ...) in place
 #pragma unroll
-            for (int i = 0; i < R; ++i) A[i] = pair_acc(A[i], W.d[i][0], s0[i], W.d[i][4], s1[i]);
-        };
-        // two rows: lanes < b into A, the others into B (a zero scale leaves
-        // the other accumulator as it is)
-        auto two = [&](float(&A)[R], float(&B)[R]) {
+            for (int i = 0; i < R; ++i) acc.cur[i] = pair_acc(acc.cur[i], W.d[i][0], s0[i], W.d[i][4], s1[i]);
+        } else {  // two rows: each lane takes its row's sum, adds the pair, puts it back
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                const uint32_t w0 = W.d[i][0], w4 = W.d[i][4];
-                const uint32_t z0 = w0 & 0xFFFF0000u, z4 = w4 & 0x0000FFFFu;  // scale zeroed
-                A[i] = pair_acc(A[i], next ? z0 : w0, s0[i], next ? z4 : w4, s1[i]);
-                B[i] = pair_acc(B[i], next ? w0 : z0, s0[i], next ? w4 : z4, s1[i]);
-            }
-        };
-        if (b >= 64) {
-            switch (acc.rc) {
-                case 0: one(acc.a0); break;
-                case 1: one(acc.a1); break;
-                case 2: one(acc.a2); break;
-                default: one(acc.a3); break;
-            }
-        } else {
-            switch (acc.rc) {
-                case 0: two(acc.a0, acc.a1); break;
-                case 1: two(acc.a1, acc.a2); break;
-                default: two(acc.a2, acc.a3); break;
+                const float t = pair_acc(next ? acc.nxt[i] : acc.cur[i], W.d[i][0], s0[i], W.d[i][4], s1[i]);
+                acc.cur[i] = next ? acc.cur[i] : t;
+                acc.nxt[i] = next ? t : acc.nxt[i];
             }
         }
-        if (o + 64 >= acc.nb) {
+        if (o + 64 >= acc.nb) {  // row rc is complete (a slab ends at most one row)
+            auto put = [&](float(&A)[R]) {
+#pragma unroll
+                for (int i = 0; i < R; ++i) A[i] = acc.cur[i];
+            };
+            switch (acc.rc) {
+                case 0: put(acc.a0); break;
+                case 1: put(acc.a1); break;
+                case 2: put(acc.a2); break;
+                default: put(acc.a3); break;
+            }
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                acc.cur[i] = acc.nxt[i];
+                acc.nxt[i] = 0.0f;
+            }
             ++acc.rc;
             acc.nb += np;
         }
@@ -780,7 +779,6 @@ struct QuadEngine {
             const float sw =
                 __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, t), 0x401F));
             const float e = row16_sum((g ? b23 : b01) + sw);
-            acc.a0[i] = acc.a1[i] = acc.a2[i] = acc.a3[i] = 0.0f;
             if ((lane & 15) == 0)
                 store(i, rbase + (int64_t)s * (WAVES * 4 * R) + wrow0 + 4 * i + (g ? 2 : 0) + (h ? 1 : 0), e);
         }
