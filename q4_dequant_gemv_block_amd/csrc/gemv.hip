@@ -645,7 +645,14 @@ struct QuadEngine {
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int i = 0; i < R; ++i) rd[b][i] = (lds_u32)(window + b * kSlot + i * kSlab + kPairBytes * lane);
+            for (int i = 0; i < R; ++i) {
+                // held in a register of its own: recomputed from one base at
+                // every read, the offsets past the paired reads' reach cost
+                // vector adds on every unit
+                uint32_t a = (uint32_t)(uintptr_t)(window + b * kSlot + i * kSlab + kPairBytes * lane);
+                asm volatile("" : "+v"(a));
+                rd[b][i] = (lds_u32)(uintptr_t)a;
+            }
     }
     __device__ __forceinline__ void init_acc(Acc& a) const {
 #pragma unroll
