@@ -734,16 +734,15 @@ struct QuadEngine {
         const int stride = XS > 0 ? XS : Dp.npl * 16;
         float s0[R], s1[R];
         block_sums<R>(W.d, (const u4*)((const uint8_t*)xs + px), stride, s0, s1);
-        if (b >= 64) {  // one row: cur = pair_acc(cur, ...) in place
+        // each lane takes its row's sum, adds the pair and puts it back; one
+        // form for slabs inside a row (no lane is past a row end) and slabs
+        // across one: a branch between the two left the compiler copying the
+        // sums between registers at the join, on every slab
 #pragma unroll
-            for (int i = 0; i < R; ++i) acc.cur[i] = pair_acc(acc.cur[i], W.d[i][0], s0[i], W.d[i][4], s1[i]);
-        } else {  // two rows: each lane takes its row's sum, adds the pair, puts it back
-#pragma unroll
-            for (int i = 0; i < R; ++i) {
-                const float t = pair_acc(next ? acc.nxt[i] : acc.cur[i], W.d[i][0], s0[i], W.d[i][4], s1[i]);
-                acc.cur[i] = next ? acc.cur[i] : t;
-                acc.nxt[i] = next ? t : acc.nxt[i];
-            }
+        for (int i = 0; i < R; ++i) {
+            const float t = pair_acc(next ? acc.nxt[i] : acc.cur[i], W.d[i][0], s0[i], W.d[i][4], s1[i]);
+            acc.cur[i] = next ? acc.cur[i] : t;
+            acc.nxt[i] = next ? t : acc.nxt[i];
         }
         if (o + 64 >= acc.nb) {  // row rc is complete (a slab ends at most one row)
             auto put = [&](float(&A)[R]) {
