@@ -79,6 +79,9 @@ constexpr bool kFairPriority = Q4_SWEEP_FAIR != 0;  // waves behind the workgrou
 #ifndef Q4_FAIR_BEFORE_FETCH
 #define Q4_FAIR_BEFORE_FETCH 1
 #endif
+#ifndef Q4_FAIR_EVERY
+#define Q4_FAIR_EVERY 4  // units between priority updates (a power of two)
+#endif
 #ifndef Q4_FAIR_HIGH
 #define Q4_FAIR_HIGH 4
 #endif
@@ -1248,6 +1251,7 @@ k_sweep(const PlanDesc* __restrict__ descs, int count, SchedHead* head, const Sc
         // far it lags.
         auto update_priority = [&]() {
             if (!kFairPriority) return;
+            if ((n_done & (Q4_FAIR_EVERY - 1)) != 0) return;
             if ((threadIdx.x & 63) == 0) atomicMax(&lead, n_done);
             const int32_t behind = __builtin_amdgcn_readfirstlane(
                 (int)(__hip_atomic_load(&lead, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) - n_done));
